@@ -1,0 +1,90 @@
+"""DSA-style top-k sparse decode over an MLA latent cache, float64.
+
+Test infrastructure only (see the package docstring).
+
+The chain is o = Attn(q, KV[TopK(ReLU(K_I . q_I))]) ([稀疏注意力] "改进一：DSA",
+the selection-chain figure), with the single-head, unweighted indexer.
+
+Readings where the pages leave a step open:
+
+* Indexer precision: a score is the exact dot product of the bf16 inputs,
+  rounded once to float32, then ReLU.  The float64 dot below is exact for
+  these inputs in all but vanishingly rare exponent spreads (each product of
+  two bf16 values has 16 significant bits; 128 of them fit in float64's 53
+  unless their magnitudes span more than ~30 binades).  Selection compares
+  the float32 scores.
+* Ties (including the ReLU zeros) go to the lower index; k_eff = min(k, L);
+  the selected indices are returned in ascending order and padded with -1.
+* Attention over the selected rows equals the pages' -inf index mask followed
+  by softmax ([attention] DSA ③ Token-wise Mask), so the oracle attends to the
+  gathered rows directly.
+* The query is given already absorbed into the latent space (weight
+  absorption, [attention] "乘法结合律" 的变换) with its RoPE part already
+  rotated; V is the first Dv dims of each latent row.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import softmax
+
+
+def indexer_scores(q_index, k_index, seq_len: int) -> np.ndarray:
+    """score_j = ReLU(q_I . k_I,j) for j < seq_len, as float32.
+
+    [transformer架构] §2.2(1) Lightning Indexer (one head, weight 1) and
+    [稀疏注意力] DSA chain ReLU(K_I . q_I).
+    """
+    k = np.asarray(k_index, dtype=np.float64)[:seq_len]
+    s = (k @ np.asarray(q_index, dtype=np.float64)).astype(np.float32)
+    return np.maximum(s, np.float32(0.0))
+
+
+def topk_select(scores, k: int) -> np.ndarray:
+    """Indices of the min(k, len) largest scores, ties to the lower index,
+    ascending, padded with -1 to length k.
+
+    [transformer架构] §2.2(2) Top-k 稀疏选择; [attention] DSA ① (Top-K of the
+    indexer scores).
+    """
+    scores = np.asarray(scores, dtype=np.float32)
+    n = scores.shape[0]
+    order = np.lexsort((np.arange(n), -scores.astype(np.float64)))
+    keff = min(k, n)
+    sel = np.sort(order[:keff]).astype(np.int32)
+    out = np.full(k, -1, dtype=np.int32)
+    out[:keff] = sel
+    return out
+
+
+def sparse_attention_one(q_vec, latent, idx, scale: float, Dv: int) -> np.ndarray:
+    """softmax(scale * q . c_j) over the selected rows j, times c_j[:Dv].
+
+    [attention] DSA ② MQA 等价变换 (every head reads the one latent row) and
+    ③ (unselected rows are -inf before the softmax).
+    """
+    idx = np.asarray(idx)
+    idx = idx[idx >= 0]
+    rows = np.asarray(latent, dtype=np.float64)[idx]
+    p = softmax((rows @ np.asarray(q_vec, dtype=np.float64)) * scale)
+    return p @ rows[:, :Dv]
+
+
+def topk_sparse_decode(q, latent, q_index, k_index, seq_lens, top_k: int, scale: float,
+                       Dv: int, batches=None, heads=None):
+    """Whole chain per batch row.  Returns (topk_idx [B, k] int32, out [B, H, Dv]).
+
+    ``batches``/``heads`` restrict the attention output to a sample (NaN
+    elsewhere); indices are computed for every selected batch row.
+    """
+    B, H, _ = q.shape
+    batches = range(B) if batches is None else batches
+    heads = range(H) if heads is None else heads
+    idx = np.full((B, top_k), -1, dtype=np.int32)
+    out = np.full((B, H, Dv), np.nan)
+    for b in batches:
+        s = indexer_scores(q_index[b], k_index[b], int(seq_lens[b]))
+        idx[b] = topk_select(s, top_k)
+        for h in heads:
+            out[b, h] = sparse_attention_one(q[b, h], latent[b], idx[b], scale, Dv)
+    return idx, out

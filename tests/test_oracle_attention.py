@@ -1,0 +1,145 @@
+"""Pins of the oracle's dense attention (prefill and decode), CPU only."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import golden_rows
+from oracle import attention as att
+from oracle import rope
+from workloads import TINY, ROPE_NONE, ROPE_PLAIN, ROPE_YARN, rope_settings, tiny_inputs
+
+NO_ROPE = rope_settings(ROPE_NONE)
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def test_softmax_rows_sum_to_one():
+    s = _rand((50, 300), 0) * np.array([[1.0], [30.0], [300.0], [1e-3], [700.0]] * 10)
+    p = att.softmax(s)
+    assert np.all(np.abs(p.sum(-1) - 1.0) < 1e-12)
+    assert np.all(p >= 0)
+    assert np.allclose(att.softmax(s + 123.0), p, rtol=1e-12, atol=1e-15)
+
+
+def test_two_key_closed_form():
+    """Two visible keys: weights are the logistic of the score gap."""
+    rng = np.random.default_rng(1)
+    q, k0, k1, v0, v1 = (rng.standard_normal(16) for _ in range(5))
+    scale = 0.25
+    w0 = 1.0 / (1.0 + math.exp(scale * (q @ k1 - q @ k0)))
+    out = att.attend(q, np.stack([k0, k1]), np.stack([v0, v1]), scale)
+    assert np.allclose(out, w0 * v0 + (1 - w0) * v1, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("hkv", [8, 2, 1])
+def test_gqa_equals_mha_on_repeated_kv(hkv):
+    """[注意力变体与MoE] "MQA 与 GQA": GQA is MHA after repeating each K/V head
+    g times along the head axis (repeat_interleave)."""
+    B, Hq, T, D = 2, 8, 9, 16
+    q, k, v = _rand((B, Hq, T, D), 1), _rand((B, hkv, T, D), 2), _rand((B, hkv, T, D), 3)
+    g = Hq // hkv
+    out = att.causal_attention(q, k, v, 0.3)
+    ref = att.causal_attention(q, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1), 0.3)
+    assert np.allclose(out, ref, rtol=1e-13, atol=1e-14)
+    # decode too
+    L = np.array([9, 4])
+    od = att.decode(q[:, :, 0], k, v, L, 0.3, None)
+    rd = att.decode(q[:, :, 0], np.repeat(k, g, axis=1), np.repeat(v, g, axis=1), L, 0.3, None)
+    assert np.allclose(od, rd, rtol=1e-13, atol=1e-14)
+
+
+def test_mqa_every_head_reads_kv_head_zero():
+    B, Hq, T, D = 1, 4, 6, 8
+    q, k, v = _rand((B, Hq, T, D), 4), _rand((B, 1, T, D), 5), _rand((B, 1, T, D), 6)
+    out = att.causal_attention(q, k, v, 0.5)
+    for h in range(Hq):
+        one = att.causal_attention(q[:, h:h + 1], k, v, 0.5)
+        assert np.allclose(out[:, h], one[:, 0])
+
+
+def test_matches_torch_sdpa_library_routine():
+    """Causal GQA attention equals torch's scaled_dot_product_attention (CPU,
+    float64, is_causal, enable_gqa) -- an independent library routine."""
+    B, Hq, Hkv, T, D = 2, 8, 2, 37, 32
+    q, k, v = _rand((B, Hq, T, D), 7), _rand((B, Hkv, T, D), 8), _rand((B, Hkv, T, D), 9)
+    scale = 1 / math.sqrt(D)
+    ours = att.causal_attention(q, k, v, scale)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        is_causal=True, scale=scale, enable_gqa=True).numpy()
+    assert np.allclose(ours, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_structured_invariants():
+    B, Hq, Hkv, T, D = 1, 4, 2, 12, 16
+    q, k, v = _rand((B, Hq, T, D), 10), _rand((B, Hkv, T, D), 11), _rand((B, Hkv, T, D), 12)
+    out = att.causal_attention(q, k, v, 0.7)
+    # row 0 sees only key 0
+    for h in range(Hq):
+        assert np.allclose(out[0, h, 0], v[0, h // 2, 0], rtol=1e-14)
+    # q = 0: uniform weights -> prefix means
+    z = att.causal_attention(np.zeros_like(q), k, v, 0.7)
+    pm = np.cumsum(v, axis=2) / np.arange(1, T + 1)[None, None, :, None]
+    for h in range(Hq):
+        assert np.allclose(z[0, h], pm[0, h // 2], rtol=1e-13, atol=1e-14)
+    # V == 1 -> output 1
+    ones = att.causal_attention(q, k, np.ones_like(v), 0.7)
+    assert np.allclose(ones, 1.0, rtol=1e-14)
+    # planted needle: one key aligned with a large q dominates
+    qn = np.zeros((1, 1, T, D)); qn[0, 0, -1, 0] = 40.0
+    kn = np.zeros((1, 1, T, D)); kn[0, 0, 5, 0] = 1.0
+    vn = _rand((1, 1, T, D), 13)
+    o = att.causal_attention(qn, kn, vn, 1.0, rows=[T - 1])
+    assert np.allclose(o[0, 0, -1], vn[0, 0, 5], atol=1e-15 + 1e-12)
+
+
+def test_decode_of_last_token_equals_prefill_last_row():
+    """Decode against a cache of rope(K) reproduces prefill's last row."""
+    B, Hq, Hkv, T, D = 2, 8, 2, 23, 32
+    q, k, v = _rand((B, Hq, T, D), 14), _rand((B, Hkv, T, D), 15), _rand((B, Hkv, T, D), 16)
+    p = rope_settings(ROPE_YARN, base=1e4, factor=4.0, original_max_position=8)
+    pre = att.prefill_causal(q, k, v, 0.2, p, rows=[T - 1])
+    kc = rope.rotate_rows(k.transpose(2, 0, 1, 3), np.arange(T), p).transpose(1, 2, 0, 3)
+    dec = att.decode(q[:, :, T - 1], kc, v, np.array([T, T]), 0.2, p)
+    assert np.allclose(dec, pre[:, :, T - 1], rtol=1e-12, atol=1e-13)
+    # a shorter context sees only its prefix: seq_len 7 decode == prefill row 6
+    pre6 = att.prefill_causal(q, k, v, 0.2, p, rows=[6])
+    dec6 = att.decode(q[:, :, 6], kc, v, np.array([7, 7]), 0.2, p)
+    assert np.allclose(dec6, pre6[:, :, 6], rtol=1e-12, atol=1e-13)
+
+
+def test_tiny_demo_shapes_and_param_counts():
+    """[注意力变体与MoE] "MQA 与 GQA": the demo's printed output shape and K/V
+    parameter counts for n_kv_head = 8, 2, 1."""
+    for n_kv, ob, ot, oc, params in golden_rows("tiny_attention_demo.txt"):
+        d = tiny_inputs(int(n_kv))
+        y = att.page_attention(d["x"], d["wq"], d["wk"], d["wv"], TINY.n_head, int(n_kv))
+        assert y.shape == (int(ob), int(ot), int(oc))
+        assert d["wk"].size + d["wv"].size == int(params)
+        # the page function (K/V repeated) equals the oracle's head-mapped attention
+        x = d["x"].astype(np.float64)
+        hd = TINY.head_dim
+
+        def split(w, n):
+            return (x @ w.astype(np.float64)).reshape(2, 10, n, hd).transpose(0, 2, 1, 3)
+
+        o2 = att.causal_attention(split(d["wq"], 8), split(d["wk"], int(n_kv)),
+                                  split(d["wv"], int(n_kv)), 1 / math.sqrt(hd))
+        assert np.allclose(o2.transpose(0, 2, 1, 3).reshape(2, 10, 64), y, rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_rope_is_relative():
+    """Shifting every position by the same amount leaves prefill unchanged
+    (RoPE scores depend only on n - m)."""
+    B, Hq, Hkv, T, D = 1, 2, 1, 8, 16
+    q, k, v = _rand((B, Hq, T, D), 17), _rand((B, Hkv, T, D), 18), _rand((B, Hkv, T, D), 19)
+    p = rope_settings(ROPE_PLAIN, base=1e4)
+    out = att.prefill_causal(q, k, v, 0.25, p)
+    sh = 1000
+    qr = rope.rotate_rows(q.transpose(2, 0, 1, 3), np.arange(T) + sh, p).transpose(1, 2, 0, 3)
+    kr = rope.rotate_rows(k.transpose(2, 0, 1, 3), np.arange(T) + sh, p).transpose(1, 2, 0, 3)
+    assert np.allclose(att.causal_attention(qr, kr, v, 0.25), out, rtol=1e-10, atol=1e-12)

@@ -1,0 +1,107 @@
+"""Pins of the oracle's indexer, top-k selection and sparse attention (CPU)."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import attention as att
+from oracle import sparse
+from workloads import bf16_bits_to_f64, randn_bf16
+
+
+def _fraction_to_f32(fr: Fraction) -> np.float32:
+    """Correctly rounded (nearest, ties to even) float32 of an exact rational."""
+    if fr == 0:
+        return np.float32(0.0)
+    d = np.float32(float(fr))            # candidate (possibly double-rounded)
+    # neighbours of the candidate in float32
+    lo = np.nextafter(d, np.float32(-np.inf))
+    hi = np.nextafter(d, np.float32(np.inf))
+    best = min((lo, d, hi), key=lambda c: (abs(Fraction(float(c)) - fr),
+                                             int(np.asarray(c).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+def test_indexer_scores_are_exact_dot_rounded_once_then_relu():
+    rng = np.random.default_rng(0)
+    q = bf16_bits_to_f64(randn_bf16(rng, (128,)))
+    k = bf16_bits_to_f64(randn_bf16(rng, (400, 128)))
+    s = sparse.indexer_scores(q, k, 400)
+    assert s.dtype == np.float32
+    for j in range(400):
+        exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(q, k[j]))
+        want = max(_fraction_to_f32(exact), np.float32(0.0))
+        assert s[j] == want, j
+    # seq_len cuts the scan
+    assert sparse.indexer_scores(q, k, 17).shape == (17,)
+
+
+def _brute_topk(scores, k):
+    order = sorted(range(len(scores)), key=lambda j: (-float(scores[j]), j))
+    sel = sorted(order[:min(k, len(scores))])
+    return sel + [-1] * (k - len(sel))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_against_brute_force_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 60))
+    k = int(rng.integers(1, 70))
+    # few distinct values -> many ties, including zeros
+    scores = rng.integers(0, 5, size=n).astype(np.float32)
+    got = sparse.topk_select(scores, k)
+    assert list(got) == _brute_topk(scores, k)
+    keff = min(k, n)
+    sel = got[:keff]
+    assert np.all(np.diff(sel) > 0)
+    uns = np.setdiff1d(np.arange(n), sel)
+    if len(uns) and keff:
+        assert scores[sel].min() >= scores[uns].max()
+        # at the boundary value, every selected index precedes every unselected one
+        t = scores[sel].min()
+        if np.any(scores[uns] == t):
+            assert sel[scores[sel] == t].max() < uns[scores[uns] == t].min()
+
+
+def test_short_context_selects_everything():
+    s = np.array([3.0, 0.0, 1.0], dtype=np.float32)
+    assert list(sparse.topk_select(s, 5)) == [0, 1, 2, -1, -1]
+
+
+def test_full_selection_reduces_to_dense_mqa():
+    """k >= L: sparse attention over all rows equals dense MQA decode over the
+    latent rows (K = latent, V = its first Dv dims)."""
+    rng = np.random.default_rng(3)
+    B, H, L, Dqk, Dv, Di = 2, 4, 50, 24, 16, 8
+    q = rng.standard_normal((B, H, Dqk))
+    lat = rng.standard_normal((B, L, Dqk))
+    qi = rng.standard_normal((B, Di))
+    ki = rng.standard_normal((B, L, Di))
+    seq = np.array([50, 31])
+    idx, out = sparse.topk_sparse_decode(q, lat, qi, ki, seq, top_k=64, scale=0.3, Dv=Dv)
+    dense = att.decode(q, lat[:, None], lat[:, None, :, :Dv], seq, 0.3, None)
+    assert np.allclose(out, dense, rtol=1e-12, atol=1e-14)
+    assert list(idx[1][:31]) == list(range(31)) and np.all(idx[1][31:] == -1)
+
+
+def test_selection_equals_minus_inf_mask():
+    """[attention] DSA ③: adding a -inf mask to unselected scores then softmax
+    equals attending to the selected rows only."""
+    rng = np.random.default_rng(4)
+    L, D = 40, 12
+    q = rng.standard_normal(D)
+    lat = rng.standard_normal((L, D))
+    idx = np.array([1, 5, 6, 20, 39])
+    got = sparse.sparse_attention_one(q, lat, np.concatenate([idx, [-1, -1]]), 0.5, 8)
+    s = lat @ q * 0.5
+    mask = np.full(L, -np.inf)
+    mask[idx] = 0.0
+    p = att.softmax(s + mask)
+    assert np.allclose(got, p @ lat[:, :8], rtol=1e-13)
+
+
+def test_relu_zeroes_negative_scores():
+    q = np.ones(4)
+    k = np.array([[1, 1, 1, 1], [-1, -1, -1, -1], [0.5, -0.5, 0, 0]], dtype=np.float64)
+    assert list(sparse.indexer_scores(q, k, 3)) == [4.0, 0.0, 0.0]
