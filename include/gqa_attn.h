@@ -1,0 +1,221 @@
+/*
+ * gqa_attn.h -- grouped-query attention over a bf16 KV cache on AMD MI355X
+ * (gfx950).  C ABI of libgqa_attn.so.
+ *
+ * Pages cited (by title):
+ *   [transformer架构]  "Agentic RL入门3：transformer架构" (xiaored5.github.io)
+ *   [注意力变体与MoE]  "注意力变体与 MoE" (notes.cassieliang.com)
+ *   [attention]        "attention" (my-site-6ix.pages.dev, posts/attention)
+ *   [稀疏注意力]        "稀疏注意力：省了什么，没省什么" (geekvape-learning, C11 lesson 5)
+ *   [注意力机制进化史]  "注意力机制进化史：从MHA、MQA、GQA、MLA到NSA、MoBA！" (CSDN)
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are plain device pointers to dense, row-major arrays; bf16 is the
+ *     IEEE-754 binary16-brain format (1-8-7), stored as 16-bit words.
+ *   - MHA, GQA and MQA are one operation: n_kv_head = n_head, n_head / g and 1.
+ *     q head h reads kv head floor(h / g) with g = n_head / n_kv_head, the map
+ *     the pages' GQA code builds by repeating each K/V head g times along the
+ *     head axis ([注意力变体与MoE] "MQA 与 GQA"; [attention] GQA).  No K/V is
+ *     ever copied: the g heads of a group read the same bytes.
+ *   - Arithmetic: bf16 inputs, fp32 accumulation, bf16 outputs rounded once
+ *     (round to nearest even).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *     asynchronous on it; results are ready when the stream is synchronized.
+ *   - Ownership: the caller allocates and owns every buffer, including the
+ *     workspace.  The library allocates no device memory and holds no mutable
+ *     global state; calls on different streams with disjoint buffers may run
+ *     concurrently.
+ *   - Errors: arguments are validated on the host before anything is launched.
+ *     On GQA_ERR_INVALID_ARGUMENT, GQA_ERR_UNSUPPORTED or
+ *     GQA_ERR_WORKSPACE_TOO_SMALL nothing is launched and nothing is written.
+ *     GQA_ERR_DEVICE reports a failed launch (hipGetLastError); faults inside
+ *     a kernel surface at the caller's next synchronization.  Values read
+ *     from device memory (seq_lens, positions) cannot be checked on the host:
+ *     seq_lens outside [1, S_max] is undefined behaviour (loads are still
+ *     clamped to the cache so no access leaves the buffers).
+ *   - Pointers must be 16-byte aligned; head_dim must be a multiple of 8.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GQA_OK = 0,
+    GQA_ERR_INVALID_ARGUMENT = 1,     /* bad size, null or misaligned pointer, bad RoPE setting */
+    GQA_ERR_UNSUPPORTED = 2,          /* valid but not instantiated (head_dim, rotary_dim, ...) */
+    GQA_ERR_WORKSPACE_TOO_SMALL = 3,
+    GQA_ERR_DEVICE = 4
+} gqa_status;
+
+/* RoPE frequency scalings, [transformer架构] §1.1 (plain) and §1.2 ①-③. */
+typedef enum {
+    GQA_ROPE_NONE = 0,   /* no rotation */
+    GQA_ROPE_PLAIN = 1,  /* theta_i = base^(-2i/d), angle m*theta_i                     (§1.1) */
+    GQA_ROPE_PI = 2,     /* position interpolation: angle (m/s)*theta_i                    (§1.2 ①) */
+    GQA_ROPE_NTK = 3,    /* NTK-aware: base' = base * s^(d/(d-2))                          (§1.2 ②) */
+    GQA_ROPE_YARN = 4    /* NTK-by-parts ramp gamma(r_i), r_i = L_train*theta_i/(2 pi),
+                            theta_i' = (1-gamma) theta_i/s + gamma theta_i, and cos/sin
+                            multiplied by 0.1 ln s + 1 when yarn_mscale != 0            (§1.2 ③) */
+} gqa_rope_scaling;
+
+/* All fields explicit; the library applies no hidden defaults. */
+typedef struct {
+    int32_t scaling;               /* gqa_rope_scaling */
+    int32_t rotary_dim;            /* even, multiple of 8, <= head_dim and <= 256; 0 means head_dim.
+                                      Pairs are adjacent dims (2i, 2i+1) of the first rotary_dim dims;
+                                      later dims pass through unchanged. */
+    double  base;                  /* > 1, e.g. 1e4, 5e5, 1e6 */
+    double  factor;                /* s >= 1 for PI / NTK / YaRN; must be 1 for PLAIN */
+    int32_t original_max_position; /* L_train (YaRN only), > 0 */
+    int32_t yarn_mscale;           /* YaRN only: nonzero folds the temperature into cos/sin */
+    double  yarn_alpha;            /* YaRN ramp lower edge (page default 1) */
+    double  yarn_beta;             /* YaRN ramp upper edge (page default 32), > alpha */
+} gqa_rope_params;
+
+/*
+ * rope_apply -- rotate the adjacent pairs of the first rotary_dim dims of
+ * every (token, head) row by its token's position:
+ *     (x_2i, x_2i+1) <- (x_2i cos a - x_2i+1 sin a, x_2i sin a + x_2i+1 cos a) * amp,
+ *     a = m_eff * theta_i,
+ * [transformer架构] §1.1 (the 2x2 rotation R(m, theta_i)) with the scalings of §1.2.
+ * Apply it to Q and K only ([transformer架构] §1.1: V carries no position).
+ *
+ *   in, out      bf16; element (t, h, d) at t*stride_tok + h*stride_head + d
+ *                (strides in elements, multiples of 8; the same strides for in
+ *                and out).  out may equal in (in place); otherwise dims at or
+ *                after rotary_dim are copied.
+ *   positions    device int32 [n_tok], >= 0 (the m of each token)
+ *   n_tok >= 0 (0 is a no-op), n_heads >= 1, head_dim multiple of 8 in [8, 1024].
+ * Angles are formed in fp64 and reduced to [-pi, pi] before an fp32 sin/cos,
+ * so positions up to 2^31 keep full fp32 accuracy.
+ */
+gqa_status rope_apply(const void* in, void* out, const int32_t* positions,
+                      int64_t n_tok, int32_t n_heads, int32_t head_dim,
+                      int64_t stride_tok, int64_t stride_head,
+                      const gqa_rope_params* rope, void* stream);
+
+/*
+ * gqa_decode -- one new token per sequence attends to its whole KV cache
+ * (the decode step of [注意力变体与MoE] "生成时的瓶颈": the new q against every
+ * cached K/V; the new token's own k/v are already appended, as in
+ * [注意力机制进化史] "解码中的KV Cache").  For batch b and q head h:
+ *     q~   = RoPE(q[b][h], position seq_lens[b]-1)          (q_rope, may be NONE)
+ *     s_j  = scale * q~ . K[b][h/g][j],   j < seq_lens[b]
+ *     out  = sum_j softmax(s)_j V[b][h/g][j]
+ *
+ *   q          bf16 [B][Hq][D]
+ *   k_cache    bf16 [B][Hkv][S_max][D], keys already rotated (post-RoPE)
+ *   v_cache    bf16 [B][Hkv][S_max][D]
+ *   seq_lens   device int32 [B], each in [1, S_max]
+ *   q_rope     NULL or GQA_ROPE_NONE: q is used as given
+ *   out        bf16 [B][Hq][D]
+ *   workspace  >= gqa_decode_workspace_size(B, Hq, Hkv, D, S_max) bytes, device,
+ *              256-byte aligned; its contents on entry do not matter.
+ * Supported: D in {64, 128}; Hq % Hkv == 0; g = Hq/Hkv <= 64.
+ * Split-K over the context with a log-sum-exp combine; the result does not
+ * depend on the split.
+ */
+size_t gqa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S_max);
+
+gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                      int32_t D, int32_t S_max, float scale,
+                      const gqa_rope_params* q_rope, void* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* As gqa_decode, with the split length (rows per split, a multiple of 64 in
+ * [64, 4096]) chosen by the caller instead of by the library's heuristic.
+ * The workspace must then hold gqa_decode_workspace_size_split(...) bytes. */
+size_t gqa_decode_workspace_size_split(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                       int32_t S_max, int32_t split_rows);
+
+gqa_status gqa_decode_split(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                            int32_t D, int32_t S_max, float scale,
+                            const gqa_rope_params* q_rope, void* out,
+                            void* workspace, size_t workspace_bytes,
+                            int32_t split_rows, void* stream);
+
+/*
+ * gqa_prefill_causal -- causal GQA attention over a whole prompt
+ * ([注意力变体与MoE] "MQA 与 GQA", attention(): scores q k^T / sqrt(hd) with the
+ * strict upper triangle masked to -inf, softmax, weighted sum of V):
+ *     q~_i = RoPE(q_i, i), k~_j = RoPE(k_j, j),  positions 0..T-1
+ *     out_i = sum_{j<=i} softmax_j(scale * q~_i . k~_j) v_j
+ *
+ *   q    bf16 [B][Hq][T][D]        (pre-RoPE)
+ *   k    bf16 [B][Hkv][T][D]       (pre-RoPE)
+ *   v    bf16 [B][Hkv][T][D]
+ *   rope NULL or GQA_ROPE_NONE: no rotation
+ *   out  bf16 [B][Hq][T][D]
+ *   workspace >= gqa_prefill_workspace_size(B, Hkv, T, D, rope) bytes (it holds
+ *             the rotated keys); may be NULL when that size is 0.
+ * Supported: D in {8, 16, 32, 64, 128}; T >= 1; Hq % Hkv == 0.
+ */
+size_t gqa_prefill_workspace_size(int32_t B, int32_t Hkv, int32_t T, int32_t D,
+                                  const gqa_rope_params* rope);
+
+gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v,
+                              int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                              float scale, const gqa_rope_params* rope, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * topk_sparse_decode -- DSA-style sparse decode over an MLA latent cache,
+ * o = Attn(q, KV[TopK(ReLU(K_I . q_I))]) ([稀疏注意力] "改进一：DSA", the
+ * selection chain; [transformer架构] §2.2 (1)-(2)):
+ *   1. indexer: score_j = ReLU(q_index[b] . k_index[b][j]) for j < seq_lens[b];
+ *      the dot product is accumulated exactly (fp64) and rounded once to fp32.
+ *   2. top-k: the min(top_k, seq_lens[b]) largest scores; equal scores go to
+ *      the lower index; indices written ascending, the rest of the row -1.
+ *   3. attention of each of the H heads over the selected latent rows only
+ *      (the -inf token mask of [attention] DSA ③), every head reading the same
+ *      single latent row (the MQA form of absorbed MLA, [attention] DSA ② and
+ *      "乘法结合律" 的变换):
+ *        s_j = scale * q[b][h] . latent[b][j][0:Dqk],  out = sum_j p_j latent[b][j][0:Dv]
+ *
+ *   q           bf16 [B][H][Dqk]   (absorbed query; its RoPE part already rotated)
+ *   latent      bf16 [B][S_max][Dqk]; V is the first Dv columns of each row
+ *   q_index     bf16 [B][D_idx]
+ *   k_index     bf16 [B][S_max][D_idx]
+ *   seq_lens    device int32 [B], each in [1, S_max]
+ *   topk_idx    int32 [B][top_k]  (output)
+ *   out         bf16 [B][H][Dv]   (output)
+ *   workspace   >= topk_sparse_decode_workspace_size(B, H, S_max, top_k) bytes
+ * Supported: Dqk = 576, Dv = 512, D_idx = 128, H a multiple of 16 up to 128,
+ * 1 <= top_k <= min(S_max, 4096).
+ */
+size_t topk_sparse_decode_workspace_size(int32_t B, int32_t H, int32_t S_max, int32_t top_k);
+
+gqa_status topk_sparse_decode(const void* q, const void* latent, const void* q_index,
+                              const void* k_index, const int32_t* seq_lens,
+                              int32_t B, int32_t H, int32_t Dqk, int32_t Dv, int32_t D_idx,
+                              int32_t S_max, int32_t top_k, float scale,
+                              int32_t* topk_idx, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * KV-cache bytes per token, exact integers ([注意力变体与MoE] "生成时的瓶颈":
+ * 2 (K and V) x layers x n_kv_head x d_head x bytes; and "MLA": layers x
+ * (d_latent + d_rope) x bytes, no factor 2 because K and V share the latent).
+ * Return -1 for a negative argument or on int64 overflow.
+ */
+int64_t kv_bytes_per_token(int32_t layers, int32_t n_kv_heads, int32_t head_dim,
+                           int32_t bytes_per_elem);
+int64_t mla_kv_bytes_per_token(int32_t layers, int32_t d_latent, int32_t d_rope,
+                               int32_t bytes_per_elem);
+
+/* Static description of a status code (never NULL). */
+const char* gqa_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

@@ -1,0 +1,277 @@
+"""Thin Python binding of libgqa_attn.so (grouped-query attention over a bf16
+KV cache on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/gqa_attn.h``.  PyTorch is used
+for device memory and the current stream.  There is no fallback: importing
+this package fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgqa_attn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -m mqa_kv_cache_amd.build, or "
+        "__graft_entry__.build()); there is no non-HIP fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_DEVICE = 0, 1, 2, 3, 4
+ROPE_NONE, ROPE_PLAIN, ROPE_PI, ROPE_NTK, ROPE_YARN = 0, 1, 2, 3, 4
+
+EXPORTED = [
+    "rope_apply", "gqa_decode", "gqa_decode_split", "gqa_decode_workspace_size",
+    "gqa_decode_workspace_size_split", "gqa_prefill_causal", "gqa_prefill_workspace_size",
+    "topk_sparse_decode", "topk_sparse_decode_workspace_size", "kv_bytes_per_token",
+    "mla_kv_bytes_per_token", "gqa_status_string",
+]
+
+
+class RopeParams(ctypes.Structure):
+    _fields_ = [
+        ("scaling", ctypes.c_int32),
+        ("rotary_dim", ctypes.c_int32),
+        ("base", ctypes.c_double),
+        ("factor", ctypes.c_double),
+        ("original_max_position", ctypes.c_int32),
+        ("yarn_mscale", ctypes.c_int32),
+        ("yarn_alpha", ctypes.c_double),
+        ("yarn_beta", ctypes.c_double),
+    ]
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.gqa_status_string(status).decode()} (status {status})")
+
+
+_c_void_p, _c_int32, _c_int64, _c_size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_rope_p = ctypes.POINTER(RopeParams)
+
+_lib.gqa_status_string.restype = ctypes.c_char_p
+_lib.gqa_status_string.argtypes = [_c_int32]
+_lib.kv_bytes_per_token.restype = _c_int64
+_lib.kv_bytes_per_token.argtypes = [_c_int32] * 4
+_lib.mla_kv_bytes_per_token.restype = _c_int64
+_lib.mla_kv_bytes_per_token.argtypes = [_c_int32] * 4
+_lib.rope_apply.restype = _c_int32
+_lib.rope_apply.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_int64, _c_int32, _c_int32,
+                            _c_int64, _c_int64, _rope_p, _c_void_p]
+_lib.gqa_decode_workspace_size.restype = _c_size_t
+_lib.gqa_decode_workspace_size.argtypes = [_c_int32] * 5
+_lib.gqa_decode_workspace_size_split.restype = _c_size_t
+_lib.gqa_decode_workspace_size_split.argtypes = [_c_int32] * 6
+_lib.gqa_decode.restype = _c_int32
+_lib.gqa_decode.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int32, _c_int32,
+                            _c_int32, _c_int32, _c_int32, ctypes.c_float, _rope_p, _c_void_p,
+                            _c_void_p, _c_size_t, _c_void_p]
+_lib.gqa_decode_split.restype = _c_int32
+_lib.gqa_decode_split.argtypes = _lib.gqa_decode.argtypes[:-1] + [_c_int32, _c_void_p]
+_lib.gqa_prefill_workspace_size.restype = _c_size_t
+_lib.gqa_prefill_workspace_size.argtypes = [_c_int32] * 4 + [_rope_p]
+_lib.gqa_prefill_causal.restype = _c_int32
+_lib.gqa_prefill_causal.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_int32, _c_int32, _c_int32,
+                                    _c_int32, _c_int32, ctypes.c_float, _rope_p, _c_void_p,
+                                    _c_void_p, _c_size_t, _c_void_p]
+_lib.topk_sparse_decode_workspace_size.restype = _c_size_t
+_lib.topk_sparse_decode_workspace_size.argtypes = [_c_int32] * 4
+_lib.topk_sparse_decode.restype = _c_int32
+_lib.topk_sparse_decode.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                    _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                    _c_int32, ctypes.c_float, _c_void_p, _c_void_p, _c_void_p,
+                                    _c_size_t, _c_void_p]
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def rope_params(settings) -> "ctypes.pointer | None":
+    """dict(scaling, rotary_dim, base, factor, original_max_position, yarn_alpha,
+    yarn_beta, yarn_mscale) -> pointer to the C struct (None stays None)."""
+    if settings is None:
+        return None
+    if isinstance(settings, RopeParams):
+        return ctypes.pointer(settings)
+    p = RopeParams(int(settings.get("scaling", ROPE_NONE)), int(settings.get("rotary_dim", 0)),
+                   float(settings.get("base", 10000.0)), float(settings.get("factor", 1.0)),
+                   int(settings.get("original_max_position", 0)),
+                   int(settings.get("yarn_mscale", 1)), float(settings.get("yarn_alpha", 1.0)),
+                   float(settings.get("yarn_beta", 32.0)))
+    return ctypes.pointer(p)
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise GqaError(status, where)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=torch.bfloat16, contiguous=True):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _shape(t, want, name):
+    if tuple(t.shape) != tuple(want):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(want)}")
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def kv_bytes_per_token(layers: int, n_kv_heads: int, head_dim: int, bytes_per_elem: int = 2) -> int:
+    return int(_lib.kv_bytes_per_token(layers, n_kv_heads, head_dim, bytes_per_elem))
+
+
+def mla_kv_bytes_per_token(layers: int, d_latent: int, d_rope: int, bytes_per_elem: int = 2) -> int:
+    return int(_lib.mla_kv_bytes_per_token(layers, d_latent, d_rope, bytes_per_elem))
+
+
+def rope_apply(x: torch.Tensor, positions: torch.Tensor, rope, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """x: bf16 [n_tok, n_heads, head_dim] (last dim contiguous, any token/head
+    strides); positions: int32 [n_tok].  Returns out (same strides as x);
+    out=x rotates in place."""
+    if x.dim() != 3:
+        raise ValueError("x must be [n_tok, n_heads, head_dim]")
+    n_tok, n_heads, head_dim = x.shape
+    _dev(x, "x", contiguous=False)
+    if x.stride(2) != 1:
+        raise ValueError("x must be contiguous in its last dim")
+    if out is None:
+        out = torch.empty_strided(x.size(), x.stride(), dtype=x.dtype, device=x.device)
+    _dev(out, "out", contiguous=False)
+    if out.stride() != x.stride() or out.shape != x.shape:
+        raise ValueError("out must have the shape and strides of x")
+    _dev(positions, "positions", dtype=torch.int32)
+    _shape(positions, (n_tok,), "positions")
+    st = _lib.rope_apply(x.data_ptr(), out.data_ptr(), positions.data_ptr(), n_tok, n_heads,
+                         head_dim, x.stride(0), x.stride(1), rope_params(rope), _stream(stream))
+    _check(st, "rope_apply")
+    return out
+
+
+def gqa_decode_workspace_size(B, Hq, Hkv, D, S_max, split_rows=None) -> int:
+    if split_rows is None:
+        return int(_lib.gqa_decode_workspace_size(B, Hq, Hkv, D, S_max))
+    return int(_lib.gqa_decode_workspace_size_split(B, Hq, Hkv, D, S_max, split_rows))
+
+
+def gqa_decode(q, k_cache, v_cache, seq_lens, scale: float, q_rope=None, out=None,
+               workspace=None, split_rows: int | None = None, stream=None) -> torch.Tensor:
+    """q [B,Hq,D], k_cache/v_cache [B,Hkv,S_max,D] (bf16, keys post-RoPE),
+    seq_lens int32 [B] on the device.  Returns out [B,Hq,D] bf16."""
+    B, Hq, D = q.shape
+    Bk, Hkv, S_max, Dk = k_cache.shape
+    _shape(k_cache, (B, Hkv, S_max, D), "k_cache")
+    _shape(v_cache, (B, Hkv, S_max, D), "v_cache")
+    _shape(seq_lens, (B,), "seq_lens")
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, nm)
+    _dev(seq_lens, "seq_lens", dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _shape(out, (B, Hq, D), "out")
+    _dev(out, "out")
+    need = gqa_decode_workspace_size(B, Hq, Hkv, D, S_max, split_rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv,
+            D, S_max, float(scale), rope_params(q_rope), out.data_ptr(), workspace.data_ptr(),
+            workspace.numel())
+    if split_rows is None:
+        st = _lib.gqa_decode(*args, _stream(stream))
+    else:
+        st = _lib.gqa_decode_split(*args, int(split_rows), _stream(stream))
+    _check(st, "gqa_decode")
+    return out
+
+
+def gqa_prefill_workspace_size(B, Hkv, T, D, rope=None) -> int:
+    return int(_lib.gqa_prefill_workspace_size(B, Hkv, T, D, rope_params(rope)))
+
+
+def gqa_prefill_causal(q, k, v, scale: float, rope=None, out=None, workspace=None,
+                       stream=None) -> torch.Tensor:
+    """q [B,Hq,T,D], k/v [B,Hkv,T,D] bf16 (pre-RoPE).  Returns out [B,Hq,T,D]."""
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    _shape(k, (B, Hkv, T, D), "k")
+    _shape(v, (B, Hkv, T, D), "v")
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, nm)
+    if out is None:
+        out = torch.empty_like(q)
+    _shape(out, q.shape, "out")
+    _dev(out, "out")
+    need = gqa_prefill_workspace_size(B, Hkv, T, D, rope)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wp, wn = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
+    if workspace is not None:
+        _dev(workspace, "workspace", dtype=torch.uint8)
+    st = _lib.gqa_prefill_causal(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, Hq, Hkv, D,
+                                 float(scale), rope_params(rope), out.data_ptr(), wp or None, wn,
+                                 _stream(stream))
+    _check(st, "gqa_prefill_causal")
+    return out
+
+
+def topk_sparse_decode_workspace_size(B, H, S_max, top_k) -> int:
+    return int(_lib.topk_sparse_decode_workspace_size(B, H, S_max, top_k))
+
+
+def topk_sparse_decode(q, latent, q_index, k_index, seq_lens, top_k: int, scale: float, Dv: int = 512,
+                       topk_idx=None, out=None, workspace=None, stream=None):
+    """q [B,H,Dqk], latent [B,S_max,Dqk], q_index [B,D_idx], k_index [B,S_max,D_idx] (bf16),
+    seq_lens int32 [B].  Returns (topk_idx int32 [B,top_k], out bf16 [B,H,Dv])."""
+    B, H, Dqk = q.shape
+    S_max = latent.shape[1]
+    D_idx = q_index.shape[1]
+    _shape(latent, (B, S_max, Dqk), "latent")
+    _shape(q_index, (B, D_idx), "q_index")
+    _shape(k_index, (B, S_max, D_idx), "k_index")
+    _shape(seq_lens, (B,), "seq_lens")
+    for t, nm in ((q, "q"), (latent, "latent"), (q_index, "q_index"), (k_index, "k_index")):
+        _dev(t, nm)
+    _dev(seq_lens, "seq_lens", dtype=torch.int32)
+    if topk_idx is None:
+        topk_idx = torch.empty((B, top_k), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=torch.bfloat16, device=q.device)
+    _shape(topk_idx, (B, top_k), "topk_idx")
+    _shape(out, (B, H, Dv), "out")
+    _dev(topk_idx, "topk_idx", dtype=torch.int32)
+    _dev(out, "out")
+    need = topk_sparse_decode_workspace_size(B, H, S_max, top_k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    st = _lib.topk_sparse_decode(q.data_ptr(), latent.data_ptr(), q_index.data_ptr(),
+                                 k_index.data_ptr(), seq_lens.data_ptr(), B, H, Dqk, Dv, D_idx,
+                                 S_max, int(top_k), float(scale), topk_idx.data_ptr(),
+                                 out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                 _stream(stream))
+    _check(st, "topk_sparse_decode")
+    return topk_idx, out

@@ -1,0 +1,240 @@
+// C ABI of libgqa_attn: argument validation on the host, then launches on
+// the caller's stream.  Nothing here touches the device before validation
+// has passed, so every error path is testable without a GPU.
+#include <cmath>
+#include <cstring>
+
+#include "host_common.h"
+
+namespace gqa {
+
+static bool finite(double x) { return std::isfinite(x); }
+
+gqa_status rope_prepare(const gqa_rope_params* p, int32_t head_dim, RopeDev* out) {
+    std::memset(out, 0, sizeof(*out));
+    out->pos_scale = 1.0;
+    out->amp = 1.0f;
+    if (p == nullptr || p->scaling == GQA_ROPE_NONE) return GQA_OK;
+    if (p->scaling < GQA_ROPE_PLAIN || p->scaling > GQA_ROPE_YARN) return GQA_ERR_INVALID_ARGUMENT;
+    const int32_t rd = p->rotary_dim == 0 ? head_dim : p->rotary_dim;
+    if (rd < 2 || (rd & 1) || rd > head_dim) return GQA_ERR_INVALID_ARGUMENT;
+    if ((rd % 8) != 0 || rd / 2 > kMaxRotaryHalf) return GQA_ERR_UNSUPPORTED;
+    if (!finite(p->base) || !(p->base > 1.0)) return GQA_ERR_INVALID_ARGUMENT;
+    if (!finite(p->factor)) return GQA_ERR_INVALID_ARGUMENT;
+    if (p->scaling == GQA_ROPE_PLAIN) {
+        if (p->factor != 1.0) return GQA_ERR_INVALID_ARGUMENT;
+    } else if (!(p->factor >= 1.0)) {
+        return GQA_ERR_INVALID_ARGUMENT;
+    }
+    const int half = rd / 2;
+    const double s = p->factor;
+    double base = p->base;
+    if (p->scaling == GQA_ROPE_NTK) {
+        if (rd <= 2) return GQA_ERR_INVALID_ARGUMENT;
+        base = p->base * std::pow(s, (double)rd / (double)(rd - 2));  // b' = b s^(d/(d-2))
+    }
+    if (p->scaling == GQA_ROPE_YARN) {
+        if (p->original_max_position <= 0 || !finite(p->yarn_alpha) || !finite(p->yarn_beta) ||
+            !(p->yarn_beta > p->yarn_alpha))
+            return GQA_ERR_INVALID_ARGUMENT;
+    }
+    for (int i = 0; i < half; ++i) {
+        const double th = std::pow(base, -2.0 * i / (double)rd);
+        double eff = th;
+        if (p->scaling == GQA_ROPE_YARN) {
+            // r = turns of this pair within L_train; ramp 0 below alpha, 1 above beta
+            const double r = (double)p->original_max_position * th / (2.0 * M_PI);
+            double gamma;
+            if (r > p->yarn_beta) gamma = 1.0;
+            else if (r <= p->yarn_alpha) gamma = 0.0;
+            else gamma = (r - p->yarn_alpha) / (p->yarn_beta - p->yarn_alpha);
+            eff = (1.0 - gamma) * th / s + gamma * th;
+        }
+        out->theta[i] = eff;
+    }
+    if (p->scaling == GQA_ROPE_PI) out->pos_scale = 1.0 / s;
+    if (p->scaling == GQA_ROPE_YARN && p->yarn_mscale) out->amp = (float)(0.1 * std::log(s) + 1.0);
+    out->half = half;
+    return GQA_OK;
+}
+
+static gqa_status from_hip(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_DEVICE; }
+
+}  // namespace gqa
+
+using namespace gqa;
+
+extern "C" {
+
+const char* gqa_status_string(int32_t status) {
+    switch (status) {
+        case GQA_OK: return "ok";
+        case GQA_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case GQA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case GQA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case GQA_ERR_DEVICE: return "device error";
+        default: return "unknown status";
+    }
+}
+
+int64_t kv_bytes_per_token(int32_t layers, int32_t n_kv_heads, int32_t head_dim, int32_t bytes_per_elem) {
+    if (layers < 0 || n_kv_heads < 0 || head_dim < 0 || bytes_per_elem < 0) return -1;
+    __int128 v = (__int128)2 * layers * n_kv_heads * head_dim * bytes_per_elem;
+    if (v > (__int128)INT64_MAX) return -1;
+    return (int64_t)v;
+}
+
+int64_t mla_kv_bytes_per_token(int32_t layers, int32_t d_latent, int32_t d_rope, int32_t bytes_per_elem) {
+    if (layers < 0 || d_latent < 0 || d_rope < 0 || bytes_per_elem < 0) return -1;
+    __int128 v = (__int128)layers * ((__int128)d_latent + d_rope) * bytes_per_elem;
+    if (v > (__int128)INT64_MAX) return -1;
+    return (int64_t)v;
+}
+
+gqa_status rope_apply(const void* in, void* out, const int32_t* positions, int64_t n_tok,
+                      int32_t n_heads, int32_t head_dim, int64_t stride_tok, int64_t stride_head,
+                      const gqa_rope_params* rope, void* stream) {
+    if (n_tok < 0 || n_heads < 1 || head_dim < 1 || stride_tok < 0 || stride_head < 0)
+        return GQA_ERR_INVALID_ARGUMENT;
+    if ((head_dim % 8) != 0 || head_dim > 1024) return GQA_ERR_UNSUPPORTED;
+    if ((stride_tok % 8) != 0 || (stride_head % 8) != 0) return GQA_ERR_INVALID_ARGUMENT;
+    RopeDev rd;
+    gqa_status st = rope_prepare(rope, head_dim, &rd);
+    if (st != GQA_OK) return st;
+    if (n_tok == 0) return GQA_OK;
+    if (!in || !out || !aligned16(in) || !aligned16(out)) return GQA_ERR_INVALID_ARGUMENT;
+    if (rd.half > 0 && !positions) return GQA_ERR_INVALID_ARGUMENT;
+    return from_hip(launch_rope_apply(in, out, positions, n_tok, n_heads, head_dim, stride_tok,
+                                      stride_head, rd, (hipStream_t)stream));
+}
+
+static gqa_status check_decode_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S_max) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || S_max < 1) return GQA_ERR_INVALID_ARGUMENT;
+    if (Hq % Hkv) return GQA_ERR_INVALID_ARGUMENT;
+    if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
+    if (Hq / Hkv > 64) return GQA_ERR_UNSUPPORTED;
+    if ((int64_t)S_max * D * 2 >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hkv > 65535 * 65535LL) return GQA_ERR_UNSUPPORTED;
+    return GQA_OK;
+}
+
+size_t gqa_decode_workspace_size_split(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S_max,
+                                       int32_t split_rows) {
+    if (check_decode_shape(B, Hq, Hkv, D, S_max) != GQA_OK) return 0;
+    if (split_rows < 64 || split_rows > 4096 || (split_rows % 64)) return 0;
+    return decode_layout(B, Hq, D, S_max, split_rows).total;
+}
+
+size_t gqa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S_max) {
+    if (check_decode_shape(B, Hq, Hkv, D, S_max) != GQA_OK) return 0;
+    return decode_layout(B, Hq, D, S_max, decode_default_split(B, Hkv, S_max)).total;
+}
+
+gqa_status gqa_decode_split(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                            int32_t S_max, float scale, const gqa_rope_params* q_rope, void* out,
+                            void* workspace, size_t workspace_bytes, int32_t split_rows,
+                            void* stream) {
+    gqa_status st = check_decode_shape(B, Hq, Hkv, D, S_max);
+    if (st != GQA_OK) return st;
+    if (split_rows < 64 || split_rows > 4096 || (split_rows % 64)) return GQA_ERR_INVALID_ARGUMENT;
+    if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+    if (!q || !k_cache || !v_cache || !seq_lens || !out || !workspace) return GQA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return GQA_ERR_INVALID_ARGUMENT;
+    RopeDev rd;
+    st = rope_prepare(q_rope, D, &rd);
+    if (st != GQA_OK) return st;
+    const DecodeLayout lay = decode_layout(B, Hq, D, S_max, split_rows);
+    if (workspace_bytes < lay.total) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    return from_hip(launch_gqa_decode(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale,
+                                      rd, out, workspace, lay, (hipStream_t)stream));
+}
+
+gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                      int32_t S_max, float scale, const gqa_rope_params* q_rope, void* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    gqa_status st = check_decode_shape(B, Hq, Hkv, D, S_max);
+    if (st != GQA_OK) return st;
+    return gqa_decode_split(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale, q_rope, out,
+                            workspace, workspace_bytes, decode_default_split(B, Hkv, S_max), stream);
+}
+
+static gqa_status check_prefill_shape(int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t D) {
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1) return GQA_ERR_INVALID_ARGUMENT;
+    if (Hq % Hkv) return GQA_ERR_INVALID_ARGUMENT;
+    if (D != 8 && D != 16 && D != 32 && D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
+    if ((int64_t)T * D * 2 >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hq > 65535) return GQA_ERR_UNSUPPORTED;
+    return GQA_OK;
+}
+
+size_t gqa_prefill_workspace_size(int32_t B, int32_t Hkv, int32_t T, int32_t D,
+                                  const gqa_rope_params* rope) {
+    if (B < 1 || Hkv < 1 || T < 1 || D < 1) return 0;
+    RopeDev rd;
+    if (rope_prepare(rope, D, &rd) != GQA_OK || rd.half == 0) return 0;
+    return (((size_t)B * Hkv * T * D * 2) + 255) & ~(size_t)255;
+}
+
+gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, int32_t B, int32_t T,
+                              int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                              const gqa_rope_params* rope, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    gqa_status st = check_prefill_shape(B, T, Hq, Hkv, D);
+    if (st != GQA_OK) return st;
+    if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+    if (!q || !k || !v || !out) return GQA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return GQA_ERR_INVALID_ARGUMENT;
+    RopeDev rd;
+    st = rope_prepare(rope, D, &rd);
+    if (st != GQA_OK) return st;
+    const size_t need = gqa_prefill_workspace_size(B, Hkv, T, D, rope);
+    if (need > 0) {
+        if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GQA_ERR_INVALID_ARGUMENT;
+        if (workspace_bytes < need) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    }
+    return from_hip(launch_gqa_prefill(q, k, v, B, T, Hq, Hkv, D, scale, rd, out,
+                                       need > 0 ? workspace : nullptr, (hipStream_t)stream));
+}
+
+static gqa_status check_sparse_shape(int32_t B, int32_t H, int32_t Dqk, int32_t Dv, int32_t D_idx,
+                                     int32_t S_max, int32_t top_k) {
+    if (B < 1 || H < 1 || Dqk < 1 || Dv < 1 || D_idx < 1 || S_max < 1) return GQA_ERR_INVALID_ARGUMENT;
+    if (top_k < 1 || top_k > S_max || Dv > Dqk) return GQA_ERR_INVALID_ARGUMENT;
+    if (Dqk != 576 || Dv != 512 || D_idx != 128) return GQA_ERR_UNSUPPORTED;
+    if ((H % 16) || H > 128) return GQA_ERR_UNSUPPORTED;
+    if (top_k > 4096) return GQA_ERR_UNSUPPORTED;
+    if ((int64_t)S_max * Dqk * 2 >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
+    return GQA_OK;
+}
+
+size_t topk_sparse_decode_workspace_size(int32_t B, int32_t H, int32_t S_max, int32_t top_k) {
+    if (check_sparse_shape(B, H, 576, 512, 128, S_max, top_k) != GQA_OK) return 0;
+    return sparse_layout(B, H, S_max, top_k).total;
+}
+
+gqa_status topk_sparse_decode(const void* q, const void* latent, const void* q_index,
+                              const void* k_index, const int32_t* seq_lens, int32_t B, int32_t H,
+                              int32_t Dqk, int32_t Dv, int32_t D_idx, int32_t S_max, int32_t top_k,
+                              float scale, int32_t* topk_idx, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    gqa_status st = check_sparse_shape(B, H, Dqk, Dv, D_idx, S_max, top_k);
+    if (st != GQA_OK) return st;
+    if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+    if (!q || !latent || !q_index || !k_index || !seq_lens || !topk_idx || !out || !workspace)
+        return GQA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(latent) || !aligned16(q_index) || !aligned16(k_index) ||
+        !aligned16(topk_idx) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return GQA_ERR_INVALID_ARGUMENT;
+    const SparseLayout lay = sparse_layout(B, H, S_max, top_k);
+    if (workspace_bytes < lay.total) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    return from_hip(launch_topk_sparse_decode(q, latent, q_index, k_index, seq_lens, B, H, S_max,
+                                              top_k, scale, topk_idx, out, workspace, lay,
+                                              (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Device-side helpers shared by the gfx950 kernels of libgqa_attn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "host_common.h"
+
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Buffer resources: loads outside [0, num_bytes) return zero, so tails and
+// ragged lengths need no branches and can never fault.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+    // dword 3 = 0x00020000: raw (untyped) 32-bit data format on gfx9-family parts.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA 16x16x32 bf16 -> fp32 (gfx950).  Lane l = 16*G + n:
+//   A operand: A[m = n][k = 8G .. 8G+7]
+//   B operand: B[k = 8G .. 8G+7][n]
+//   C/D:       C[m = 4G + i][n], i = 0..3
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// RoPE cos/sin of pair i at position pos: angle formed in fp64, reduced to
+// [-pi, pi] in fp64, then an fp32 sincos; both scaled by the amplitude.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rope_cos_sin(const RopeDev& r, double pos, int i, float& c, float& s) {
+    const double two_pi_hi = 6.283185307179586232;
+    const double two_pi_lo = 2.4492935982947064e-16;
+    double a = pos * r.pos_scale * r.theta[i];
+    double k = rint(a * 0.15915494309189535);
+    double red = fma(-k, two_pi_hi, a);
+    red = fma(-k, two_pi_lo, red);
+    float x = (float)red;
+    float sv, cv;
+    sincosf(x, &sv, &cv);
+    c = cv * r.amp;
+    s = sv * r.amp;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace gqa

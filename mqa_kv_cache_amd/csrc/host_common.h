@@ -1,0 +1,68 @@
+// Internal declarations shared by the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/gqa_attn.h"
+
+namespace gqa {
+
+constexpr int kMaxRotaryHalf = 128;   // rotary_dim <= 256
+
+// RoPE frequencies prepared on the host (fp64) and passed by value to kernels.
+struct RopeDev {
+    double theta[kMaxRotaryHalf];  // effective theta_i after the scaling
+    double pos_scale;              // multiplies the position (PI: 1/s)
+    float amp;                     // multiplies cos and sin (YaRN temperature)
+    int32_t half;                  // rotary_dim / 2; 0 = no rotation
+};
+
+// Validates `p` against head_dim and fills `out`.  p == NULL or NONE gives half = 0.
+gqa_status rope_prepare(const gqa_rope_params* p, int32_t head_dim, RopeDev* out);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ----- launchers (defined next to their kernels) ---------------------------
+hipError_t launch_rope_apply(const void* in, void* out, const int32_t* positions, int64_t n_tok,
+                             int32_t n_heads, int32_t head_dim, int64_t stride_tok,
+                             int64_t stride_head, const RopeDev& rope, hipStream_t s);
+
+struct DecodeLayout {
+    int32_t split_rows;    // rows per split (multiple of 64)
+    int32_t n_split_max;   // ceil(S_max / split_rows)
+    size_t o_bytes;        // partial outputs  fp32 [B][Hq][n_split_max][D]
+    size_t ml_bytes;       // partial (m, l)   fp32 [B][Hq][n_split_max][2]
+    size_t total;
+};
+DecodeLayout decode_layout(int32_t B, int32_t Hq, int32_t D, int32_t S_max, int32_t split_rows);
+int32_t decode_default_split(int32_t B, int32_t Hkv, int32_t S_max);
+
+hipError_t launch_gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                             int32_t D, int32_t S_max, float scale, const RopeDev& rope,
+                             void* out, void* workspace, const DecodeLayout& lay, hipStream_t s);
+
+hipError_t launch_gqa_prefill(const void* q, const void* k, const void* v, int32_t B, int32_t T,
+                              int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                              const RopeDev& rope, void* out, void* k_rot, hipStream_t s);
+
+struct SparseLayout {
+    size_t scores_bytes;   // fp32 [B][S_max]
+    size_t hist_bytes;     // u32 [B][hist bins]
+    size_t o_bytes;        // fp32 partials
+    size_t ml_bytes;
+    size_t total;
+    int32_t n_chunks;      // attention splits over the selected rows
+};
+SparseLayout sparse_layout(int32_t B, int32_t H, int32_t S_max, int32_t top_k);
+
+hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const void* q_index,
+                                     const void* k_index, const int32_t* seq_lens, int32_t B,
+                                     int32_t H, int32_t S_max, int32_t top_k, float scale,
+                                     int32_t* topk_idx, void* out, void* workspace,
+                                     const SparseLayout& lay, hipStream_t s);
+
+}  // namespace gqa

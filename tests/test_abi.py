@@ -1,0 +1,151 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT, golden_rows
+
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import mqa_kv_cache_amd
+    return mqa_kv_cache_amd
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("rope_apply", "gqa_decode", "gqa_prefill_causal", "topk_sparse_decode",
+                 "kv_bytes_per_token", "mla_kv_bytes_per_token", "gqa_status_string"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(m):
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(m.EXPORTED) == declared_functions()
+
+
+def test_status_strings(m):
+    lib = m.lib()
+    for code in range(5):
+        assert lib.gqa_status_string(code)
+    assert lib.gqa_status_string(99) == b"unknown status"
+
+
+def test_kv_bytes_closed_forms(m):
+    for _, layers, kv, hd, bpe, kib, gib in golden_rows("kv_bytes_llama2_70b.txt"):
+        assert m.kv_bytes_per_token(int(layers), int(kv), int(hd), int(bpe)) == int(kib) * 1024
+    for L, h, hd, dc, dr, bpe, mha_kib, mla_kib, ratio, mla_b in golden_rows("kv_bytes_mla_v3.txt"):
+        assert m.mla_kv_bytes_per_token(int(L), int(dc), int(dr), int(bpe)) == int(mla_b)
+        assert m.kv_bytes_per_token(int(L), int(h), int(hd), int(bpe)) == int(mha_kib) * 1024
+    for layers, kv, hd, bpe, tokens, total in golden_rows("kv_bytes_llama2_7b.txt"):
+        assert m.kv_bytes_per_token(int(layers), int(kv), int(hd), int(bpe)) * int(tokens) == int(total)
+    assert m.kv_bytes_per_token(-1, 8, 128, 2) == -1
+    assert m.kv_bytes_per_token(2**31 - 1, 2**31 - 1, 2**31 - 1, 2) == -1
+    assert m.mla_kv_bytes_per_token(61, -1, 64, 2) == -1
+
+
+P = 0x10000       # aligned fake device pointer: never dereferenced (validation fails first)
+MIS = 0x10002     # misaligned
+
+
+def _rope(m, **kw):
+    return m.rope_params(dict(kw))
+
+
+def _decode(m, q=P, k=P, v=P, sl=P, B=2, Hq=16, Hkv=2, D=128, S=64, scale=0.1, rope=None,
+            out=P, ws=P, wsn=1 << 30):
+    return m.lib().gqa_decode(q, k, v, sl, B, Hq, Hkv, D, S, scale, rope, out, ws, wsn, None)
+
+
+def test_decode_validation(m):
+    assert _decode(m, Hq=15, Hkv=2) == m.ERR_INVALID_ARGUMENT
+    assert _decode(m, B=0) == m.ERR_INVALID_ARGUMENT
+    assert _decode(m, D=96) == m.ERR_UNSUPPORTED
+    assert _decode(m, Hq=128, Hkv=1) == m.ERR_UNSUPPORTED       # g > 64
+    assert _decode(m, q=0) == m.ERR_INVALID_ARGUMENT
+    assert _decode(m, k=MIS) == m.ERR_INVALID_ARGUMENT
+    assert _decode(m, ws=P + 16) == m.ERR_INVALID_ARGUMENT      # workspace not 256-aligned
+    assert _decode(m, scale=float("nan")) == m.ERR_INVALID_ARGUMENT
+    need = m.gqa_decode_workspace_size(2, 16, 2, 128, 64)
+    assert need > 0
+    assert _decode(m, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+    assert _decode(m, wsn=need - 1, rope=_rope(m, scaling=m.ROPE_PLAIN, base=1e4, factor=2.0)) \
+        == m.ERR_INVALID_ARGUMENT
+    assert _decode(m, wsn=0, rope=_rope(m, scaling=m.ROPE_YARN, base=1e4, factor=4.0,
+                                        original_max_position=8192, yarn_alpha=32.0,
+                                        yarn_beta=1.0)) == m.ERR_INVALID_ARGUMENT
+    assert _decode(m, wsn=0, rope=_rope(m, scaling=m.ROPE_PI, base=1e4, factor=0.5)) \
+        == m.ERR_INVALID_ARGUMENT
+    assert _decode(m, wsn=0, rope=_rope(m, scaling=m.ROPE_PLAIN, base=1e4, rotary_dim=7)) \
+        == m.ERR_INVALID_ARGUMENT
+    assert _decode(m, wsn=0, rope=_rope(m, scaling=m.ROPE_PLAIN, base=1e4, rotary_dim=12)) \
+        == m.ERR_UNSUPPORTED
+    assert _decode(m, wsn=0, rope=_rope(m, scaling=9, base=1e4)) == m.ERR_INVALID_ARGUMENT
+    assert m.gqa_decode_workspace_size(2, 15, 2, 128, 64) == 0
+    lib = m.lib()
+    assert lib.gqa_decode_split(P, P, P, P, 2, 16, 2, 128, 64, 0.1, None, P, P, 1 << 30, 100,
+                                None) == m.ERR_INVALID_ARGUMENT   # split not a multiple of 64
+
+
+def test_prefill_validation(m):
+    lib = m.lib()
+
+    def call(B=1, T=16, Hq=8, Hkv=2, D=128, rope=None, ws=P, wsn=0, q=P):
+        return lib.gqa_prefill_causal(q, P, P, B, T, Hq, Hkv, D, 0.1, rope, P, ws, wsn, None)
+
+    assert call(Hq=7) == m.ERR_INVALID_ARGUMENT
+    assert call(T=0) == m.ERR_INVALID_ARGUMENT
+    assert call(D=96) == m.ERR_UNSUPPORTED
+    assert call(q=MIS) == m.ERR_INVALID_ARGUMENT
+    r = _rope(m, scaling=m.ROPE_NTK, base=1e6, factor=4.0)
+    need = m.gqa_prefill_workspace_size(1, 2, 16, 128, r.contents)
+    assert need == 2 * 16 * 128 * 2
+    assert call(rope=r, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+    assert call(rope=r, ws=None, wsn=need) == m.ERR_INVALID_ARGUMENT
+    assert m.gqa_prefill_workspace_size(1, 2, 16, 128, None) == 0
+
+
+def test_sparse_validation(m):
+    lib = m.lib()
+
+    def call(B=2, H=128, Dqk=576, Dv=512, Di=128, S=4096, k=2048, wsn=0, idx=P):
+        return lib.topk_sparse_decode(P, P, P, P, P, B, H, Dqk, Dv, Di, S, k, 0.07, idx, P, P,
+                                      wsn, None)
+
+    assert call(k=0) == m.ERR_INVALID_ARGUMENT
+    assert call(k=5000, S=4096) == m.ERR_INVALID_ARGUMENT
+    assert call(k=8192, S=100000) == m.ERR_UNSUPPORTED
+    assert call(Dqk=512) == m.ERR_UNSUPPORTED
+    assert call(H=100) == m.ERR_UNSUPPORTED
+    assert call(idx=MIS) == m.ERR_INVALID_ARGUMENT
+    need = m.topk_sparse_decode_workspace_size(2, 128, 4096, 2048)
+    assert need > 0
+    assert call(wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_rope_validation(m):
+    lib = m.lib()
+    r = _rope(m, scaling=m.ROPE_PLAIN, base=1e4)
+    assert lib.rope_apply(P, P, P, -1, 2, 128, 256, 128, r, None) == m.ERR_INVALID_ARGUMENT
+    assert lib.rope_apply(P, P, P, 4, 2, 12, 24, 12, r, None) == m.ERR_UNSUPPORTED
+    assert lib.rope_apply(P, P, P, 4, 2, 128, 250, 128, r, None) == m.ERR_INVALID_ARGUMENT
+    assert lib.rope_apply(MIS, P, P, 4, 2, 128, 256, 128, r, None) == m.ERR_INVALID_ARGUMENT
+    assert lib.rope_apply(P, P, None, 4, 2, 128, 256, 128, r, None) == m.ERR_INVALID_ARGUMENT
+    assert lib.rope_apply(P, P, P, 0, 2, 128, 256, 128, r, None) == m.OK   # empty: no-op
+    bad = _rope(m, scaling=m.ROPE_PLAIN, base=0.5)
+    assert lib.rope_apply(P, P, P, 4, 2, 128, 256, 128, bad, None) == m.ERR_INVALID_ARGUMENT

@@ -1,0 +1,148 @@
+"""GPU parity of gqa_decode (through the C ABI) against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+
+from helpers import assert_close, from_dev, to_dev
+from oracle import attention as oatt
+from workloads import (DECODE_4K, DECODE_32K_YARN, ROPE_PLAIN, ROPE_YARN, bf16_bits_to_f64,
+                       bf16_tensor_to_f64, decode_inputs_host, device_randn_bf16, rope_settings)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import mqa_kv_cache_amd
+    return mqa_kv_cache_amd
+
+
+def _run_case(m, B, Hq, Hkv, D, S_max, seq_lens, rope, seed, split_rows=None, scale=None):
+    import torch
+    d = decode_inputs_host(B, Hq, Hkv, D, S_max, seed, seq_lens)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    print(f"[case] B={B} Hq={Hq} Hkv={Hkv} D={D} S_max={S_max} lens={list(seq_lens)} "
+          f"rope={rope and rope['scaling']} split={split_rows} seed={seed}", flush=True)
+    out = m.gqa_decode(to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"]),
+                       torch.from_numpy(d["seq_lens"]).cuda(), scale, q_rope=rope,
+                       split_rows=split_rows)
+    torch.cuda.synchronize()
+    ref = oatt.decode(bf16_bits_to_f64(d["q"]), bf16_bits_to_f64(d["k"]), bf16_bits_to_f64(d["v"]),
+                      d["seq_lens"], scale, rope)
+    return from_dev(out), ref
+
+
+CASES = [
+    # (B, Hq, Hkv, D, S_max, seq_lens)
+    (3, 16, 2, 128, 700, [700, 333, 1]),      # GQA g=8, ragged, a one-row context
+    (2, 8, 8, 128, 257, [257, 31]),           # MHA
+    (2, 16, 1, 128, 300, [300, 64]),          # MQA g=16
+    (1, 32, 1, 128, 200, [130]),              # g=32 (two head blocks)
+    (1, 64, 1, 128, 96, [96]),                # g=64 (four head blocks)
+    (2, 8, 2, 64, 333, [333, 65]),            # head dim 64
+    (2, 12, 4, 128, 129, [129, 33]),          # g=3: partial head block
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}D{c[3]}" for c in CASES])
+def test_decode_parity_small(m, case):
+    B, Hq, Hkv, D, S, lens = case
+    rope = rope_settings(ROPE_PLAIN, base=500000.0)
+    got, ref = _run_case(m, B, Hq, Hkv, D, S, np.array(lens, dtype=np.int32), rope, seed=11)
+    assert_close(got, ref, f"decode {case}")
+
+
+def test_decode_yarn_and_split_independence(m):
+    rope = rope_settings(ROPE_YARN, base=500000.0, factor=4.0, original_max_position=64)
+    lens = np.array([1000, 777, 64, 65], dtype=np.int32)
+    outs = []
+    for split in (None, 64, 128, 448, 1024, 4096):
+        got, ref = _run_case(m, 4, 16, 2, 128, 1000, lens, rope, seed=12, split_rows=split)
+        assert_close(got, ref, f"yarn split={split}")
+        outs.append(got)
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 4e-3
+
+
+def test_decode_no_rope_and_gqa_equals_repeated_mha(m):
+    """GQA on the GPU equals an MHA run over K/V materialised with each head
+    repeated g times (repeat_interleave)."""
+    import torch
+    B, Hq, Hkv, D, S = 2, 16, 4, 128, 300
+    d = decode_inputs_host(B, Hq, Hkv, D, S, 13, [300, 123])
+    sl = torch.from_numpy(d["seq_lens"]).cuda()
+    q, k, v = to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"])
+    o1 = m.gqa_decode(q, k, v, sl, 0.1)
+    g = Hq // Hkv
+    o2 = m.gqa_decode(q, k.repeat_interleave(g, dim=1).contiguous(),
+                      v.repeat_interleave(g, dim=1).contiguous(), sl, 0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    ref = oatt.decode(bf16_bits_to_f64(d["q"]), bf16_bits_to_f64(d["k"]), bf16_bits_to_f64(d["v"]),
+                      d["seq_lens"], 0.1, None)
+    assert_close(from_dev(o1), ref, "no-rope")
+
+
+def test_decode_structured_cases(m):
+    """V == 1 gives 1; q == 0 gives the mean of the visible V rows; a planted
+    needle key dominates (outputs of magnitude ~1, where the tolerance bites)."""
+    import torch
+    B, Hq, Hkv, D, S = 2, 8, 1, 128, 2000
+    lens = np.array([2000, 1500], dtype=np.int32)
+    d = decode_inputs_host(B, Hq, Hkv, D, S, 14, lens)
+    sl = torch.from_numpy(lens).cuda()
+    k, v = to_dev(d["k"]), to_dev(d["v"])
+    ones = torch.ones_like(v)
+    o = m.gqa_decode(to_dev(d["q"]), k, ones, sl, 0.09)
+    torch.cuda.synchronize()
+    assert_close(from_dev(o), np.ones((B, Hq, D)), "V=1")
+    qz = torch.zeros((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    o = m.gqa_decode(qz, k, v, sl, 0.09)
+    vf = bf16_bits_to_f64(d["v"])
+    ref = np.stack([np.repeat(vf[b, 0, :lens[b]].mean(0)[None], Hq, 0) for b in range(B)])
+    assert_close(from_dev(o), ref, "q=0 mean")
+    # needle: row 777 of batch 0 equals q (scaled up), every other key ~N(0,1)
+    q = d["q"].copy()
+    kk = d["k"].copy()
+    kk[0, 0, 777] = q[0, 0]
+    qf = bf16_bits_to_f64(q)
+    o = m.gqa_decode(to_dev(q), to_dev(kk), v, sl, 0.5)
+    ref = oatt.decode(qf, bf16_bits_to_f64(kk), vf, lens, 0.5, None)
+    assert_close(from_dev(o), ref, "needle")
+    assert np.abs(ref[0, 0] - vf[0, 0, 777]).max() < 1e-3
+
+
+def _full_size(m, cfg, n_pairs=24):
+    import torch
+    B, Hq, Hkv, D, S = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.S_max
+    lens = cfg.seq_lens()
+    print(f"[case] full size B={B} Hq={Hq} Hkv={Hkv} S_max={S} lens={list(lens)}", flush=True)
+    q = device_randn_bf16((B, Hq, D), cfg.seed * 10 + 1)
+    k = device_randn_bf16((B, Hkv, S, D), cfg.seed * 10 + 2)
+    v = device_randn_bf16((B, Hkv, S, D), cfg.seed * 10 + 3)
+    sl = torch.from_numpy(lens).cuda()
+    out = m.gqa_decode(q, k, v, sl, cfg.scale, q_rope=cfg.rope())
+    torch.cuda.synchronize()
+    got = from_dev(out)
+    rng = np.random.default_rng(cfg.seed)
+    pairs = [(int(rng.integers(B)), int(rng.integers(Hq))) for _ in range(n_pairs)]
+    qf = bf16_tensor_to_f64(q)
+    for b, h in pairs:
+        kv = h // (Hq // Hkv)
+        L = int(lens[b])
+        kb = bf16_tensor_to_f64(k[b, kv, :L])
+        vb = bf16_tensor_to_f64(v[b, kv, :L])
+        ref = oatt.decode_one(qf[b, h], kb, vb, L, cfg.scale, cfg.rope())
+        assert_close(got[b, h], ref, f"full-size (b={b}, h={h}, L={L})")
+    assert np.all(np.isfinite(got))
+
+
+def test_decode_full_size_4k(m):
+    _full_size(m, DECODE_4K)
+
+
+def test_decode_full_size_32k_yarn_ragged(m):
+    _full_size(m, DECODE_32K_YARN)
