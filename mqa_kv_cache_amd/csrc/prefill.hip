@@ -1,7 +1,286 @@
+// Causal GQA prefill on gfx950 bf16 MFMA (32x32x16).
+//
+// Prefill is a dense contraction: K/V are reused by every later query
+// ([注意力变体与MoE] "生成时的瓶颈", last paragraph), so it runs on the matrix
+// cores.  The operation is the pages' causal attention ([注意力变体与MoE]
+// "MQA 与 GQA", attention(): q k^T / sqrt(hd), strict upper triangle masked,
+// softmax, weighted sum of V) with RoPE on Q and K ([transformer架构] §1.1).
+//
+// Work split: one workgroup (4 waves) per (batch, q head, 128-query tile);
+// wave w owns 32 queries.  Query tiles are issued heaviest (latest) first so
+// the causal triangle balances across the machine.  Per 64-key tile:
+//   * the workgroup stages K (row-major, rows padded by 16 B) and V^T
+//     (transposed through registers, key columns permuted to match the P^T
+//     operand) in LDS;
+//   * S^T[64 keys][32 queries] = K . Q^T   (K from LDS as A, Q^T in registers as B)
+//   * online softmax per query in base 2 (scale*log2(e) is folded into Q)
+//   * O^T[D][32 queries] += V^T . P^T       (P^T straight from the S^T accumulators)
+// The S^T accumulator layout is the P^T operand layout, so probabilities
+// never cross lanes; the only cross-lane step is one xor-32 shuffle for each
+// max and sum.  Q is rotated while loaded (fp64 angle, fp32 sincos); K is
+// rotated once by a pre-pass into the workspace, because every K row is
+// re-read by all later query tiles.
 #include "device_common.h"
+
 namespace gqa {
-hipError_t launch_gqa_prefill(const void*, const void*, const void*, int32_t, int32_t, int32_t,
-                              int32_t, int32_t, float, const RopeDev&, void*, void*, hipStream_t) {
-    return hipErrorNotSupported;
+
+hipError_t launch_rope_rows(const void* in, void* out, int64_t n_tok, int32_t n_heads,
+                            int32_t head_dim, int64_t stride_tok, int64_t stride_head,
+                            const RopeDev& rope, hipStream_t s);
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int BM = 128;   // queries per workgroup (4 waves x 32)
+constexpr int BN = 64;    // keys per tile
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+
+// Column of 4-key chunk a (0..3) inside its 16-key group in the V^T tile:
+// chunks are stored in the order 0, 2, 1, 3 so lane group h reads its
+// keys {4h..4h+3, 8+4h..8+4h+3} as one 16-byte run.
+__device__ __forceinline__ int chunk_col(int a) { return (a == 0) ? 0 : (a == 1) ? 8 : (a == 2) ? 4 : 12; }
+
+template <int D>
+struct Geo {
+    static constexpr int DP = D < 16 ? 16 : D;        // head dim padded to one MFMA k-step
+    static constexpr int KSTEPS = DP / 16;            // MFMA k-steps for S^T
+    static constexpr int DM = D < 32 ? 32 : D;        // d rows of O^T padded to one 32-row tile
+    static constexpr int MT = DM / 32;                // O^T m-tiles
+    static constexpr int KSTR = DP + 8;               // K tile row stride (elements)
+    static constexpr int VSTR = BN + 8;               // V^T tile row stride (elements)
+    static constexpr int K_ELEMS = BN * KSTR;
+    static constexpr int V_ELEMS = DM * VSTR;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ out, int T, int Hq, int Hkv, float qscale, RopeDev rope) {
+    using Gm = Geo<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t k_s[Gm::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t vt_s[Gm::V_ELEMS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, h = lane >> 5;
+    const int n_qt = (T + BM - 1) / BM;
+    const int qt = n_qt - 1 - (int)blockIdx.x;
+    const int hq = blockIdx.y, b = blockIdx.z;
+    const int g = Hq / Hkv;
+    const int kvh = hq / g;
+    const int q0 = qt * BM + 32 * wave;      // first query of this wave
+    const int qi = q0 + n;                    // this lane's query
+
+    const size_t qbase = ((size_t)b * Hq + hq) * (size_t)T * D;
+    const size_t kvbase = ((size_t)b * Hkv + kvh) * (size_t)T * D;
+    const uint32_t nbytes = (uint32_t)T * D * 2u;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + qbase, nbytes);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kvbase, nbytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kvbase, nbytes);
+
+    // ---- Q^T operands: lane holds query qi, dims 16u + 8h .. +7 (rotated, scaled)
+    u32x4 qf[Gm::KSTEPS];
+#pragma unroll
+    for (int u = 0; u < Gm::KSTEPS; ++u) {
+        const int d0 = 16 * u + 8 * h;
+        u32x4 raw = (d0 < D && qi < T) ? buf_load16(qr, (uint32_t)((qi * D + d0) * 2)) : u32x4{0, 0, 0, 0};
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = bf16_lo(raw[j]);
+            x[2 * j + 1] = bf16_hi(raw[j]);
+        }
+        if (rope.half && d0 < D) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int i = d0 / 2 + p;
+                if (i < rope.half) {
+                    float c, s;
+                    rope_cos_sin(rope, (double)qi, i, c, s);
+                    const float xe = x[2 * p], xo = x[2 * p + 1];
+                    x[2 * p] = xe * c - xo * s;
+                    x[2 * p + 1] = xe * s + xo * c;
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qf[u][j] = pack_bf16x2(x[2 * j] * qscale, x[2 * j + 1] * qscale);
+    }
+
+    f32x16 o[Gm::MT];
+#pragma unroll
+    for (int mt = 0; mt < Gm::MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[mt][e] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int q_last_wg = min(qt * BM + BM - 1, T - 1);
+    const int n_kt = q_last_wg / BN + 1;
+    constexpr int CPR = (D < 8 ? 1 : D / 8);            // 16-byte chunks per row
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int ks = kt * BN;
+        __syncthreads();
+        // ---- stage K tile (row-major)
+        for (int c = tid; c < BN * CPR; c += 256) {
+            const int key = c / CPR, dc = c - key * CPR;
+            u32x4 val = buf_load16(kr, (uint32_t)(((ks + key) * D + 8 * dc) * 2));
+            *reinterpret_cast<u32x4*>(&k_s[key * Gm::KSTR + 8 * dc]) = val;
+        }
+        if constexpr (D < 16) {
+            for (int c = tid; c < BN; c += 256)
+                *reinterpret_cast<u32x4*>(&k_s[c * Gm::KSTR + 8]) = u32x4{0, 0, 0, 0};
+        }
+        // ---- stage V^T tile: 4 keys x 8 dims per item, transposed in registers
+        for (int c = tid; c < (BN / 4) * CPR; c += 256) {
+            const int kg = c / CPR, dc = c - kg * CPR;
+            u32x4 r4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                r4[r] = buf_load16(vr, (uint32_t)(((ks + 4 * kg + r) * D + 8 * dc) * 2));
+            const int col = 16 * (kg >> 2) + chunk_col(kg & 3);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int w = t >> 1;
+                u32x2 pr;
+                if (t & 1) {
+                    pr[0] = (r4[0][w] >> 16) | (r4[1][w] & 0xFFFF0000u);
+                    pr[1] = (r4[2][w] >> 16) | (r4[3][w] & 0xFFFF0000u);
+                } else {
+                    pr[0] = (r4[0][w] & 0xFFFFu) | (r4[1][w] << 16);
+                    pr[1] = (r4[2][w] & 0xFFFFu) | (r4[3][w] << 16);
+                }
+                *reinterpret_cast<u32x2*>(&vt_s[(8 * dc + t) * Gm::VSTR + col]) = pr;
+            }
+        }
+        if constexpr (D < 32) {
+            for (int c = tid; c < (Gm::DM - D) * (BN / 4); c += 256) {
+                const int row = D + c / (BN / 4), cc = c % (BN / 4);
+                *reinterpret_cast<u32x2*>(&vt_s[row * Gm::VSTR + 4 * cc]) = u32x2{0, 0};
+            }
+        }
+        __syncthreads();
+        if (ks > q0 + 31) continue;   // the whole tile is in this wave's future
+
+        // ---- S^T = K . Q^T  (two 32-key halves)
+        f32x16 s[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[st][e] = 0.f;
+#pragma unroll
+            for (int u = 0; u < Gm::KSTEPS; ++u) {
+                const u32x4 kf = *reinterpret_cast<const u32x4*>(&k_s[(32 * st + n) * Gm::KSTR + 16 * u + 8 * h]);
+                s[st] = mfma32(kf, qf[u], s[st]);
+            }
+        }
+        // ---- causal mask (only tiles that reach past this wave's first query)
+        if (ks + BN - 1 > q0) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = ks + 32 * st + 8 * j + 4 * h + i;
+                        if (key > qi) s[st][4 * j + i] = -INFINITY;
+                    }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[st][e]);
+        mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);           // finite: key ks <= q0 <= qi is visible
+        const float alpha = fast_exp2(m_run - m_new);
+        float ls = 0.f;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                s[st][e] = fast_exp2(s[st][e] - m_new);
+                ls += s[st][e];
+            }
+        ls += wave_shfl_xor(ls, 32);
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+#pragma unroll
+        for (int mt = 0; mt < Gm::MT; ++mt) o[mt] *= alpha;
+
+        // ---- O^T += V^T . P^T, four 16-key steps
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                u32x4 pb;
+                pb[0] = pack_bf16x2(s[st][8 * c + 0], s[st][8 * c + 1]);
+                pb[1] = pack_bf16x2(s[st][8 * c + 2], s[st][8 * c + 3]);
+                pb[2] = pack_bf16x2(s[st][8 * c + 4], s[st][8 * c + 5]);
+                pb[3] = pack_bf16x2(s[st][8 * c + 6], s[st][8 * c + 7]);
+                const int col = 16 * (2 * st + c) + 8 * h;
+#pragma unroll
+                for (int mt = 0; mt < Gm::MT; ++mt) {
+                    const u32x4 vf = *reinterpret_cast<const u32x4*>(&vt_s[(32 * mt + n) * Gm::VSTR + col]);
+                    o[mt] = mfma32(vf, pb, o[mt]);
+                }
+            }
+    }
+
+    // ---- normalise and write: lane holds query qi, d = 32 mt + 8 j + 4 h + i
+    if (qi < T) {
+        const float inv = 1.0f / l_run;
+        uint16_t* orow = out + qbase + (size_t)qi * D;
+#pragma unroll
+        for (int mt = 0; mt < Gm::MT; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = 32 * mt + 8 * j + 4 * h;
+                if (d0 < D) {
+                    u32x2 w;
+                    w[0] = pack_bf16x2(o[mt][4 * j + 0] * inv, o[mt][4 * j + 1] * inv);
+                    w[1] = pack_bf16x2(o[mt][4 * j + 2] * inv, o[mt][4 * j + 3] * inv);
+                    *reinterpret_cast<u32x2*>(orow + d0) = w;
+                }
+            }
+    }
+}
+
+template <int D>
+void launch_d(const void* q, const void* k, const void* v, void* out, int B, int T, int Hq, int Hkv,
+              float qscale, const RopeDev& rope, hipStream_t s) {
+    dim3 grid((T + BM - 1) / BM, Hq, B);
+    hipLaunchKernelGGL((prefill_kernel<D>), grid, dim3(256), 0, s, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)out, T, Hq, Hkv, qscale,
+                       rope);
+}
+
+}  // namespace
+
+hipError_t launch_gqa_prefill(const void* q, const void* k, const void* v, int32_t B, int32_t T,
+                              int32_t Hq, int32_t Hkv, int32_t D, float scale, const RopeDev& rope,
+                              void* out, void* k_rot, hipStream_t s) {
+    const void* kk = k;
+    if (rope.half > 0) {
+        // rotate K once: rows are (token t, head bh) with bh over B*Hkv, position = t
+        hipError_t e = launch_rope_rows(k, k_rot, T, B * Hkv, D, D, (int64_t)T * D, rope, s);
+        if (e != hipSuccess) return e;
+        kk = k_rot;
+    }
+    const float qscale = scale * kLog2e;
+    switch (D) {
+        case 8: launch_d<8>(q, kk, v, out, B, T, Hq, Hkv, qscale, rope, s); break;
+        case 16: launch_d<16>(q, kk, v, out, B, T, Hq, Hkv, qscale, rope, s); break;
+        case 32: launch_d<32>(q, kk, v, out, B, T, Hq, Hkv, qscale, rope, s); break;
+        case 64: launch_d<64>(q, kk, v, out, B, T, Hq, Hkv, qscale, rope, s); break;
+        default: launch_d<128>(q, kk, v, out, B, T, Hq, Hkv, qscale, rope, s); break;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace gqa

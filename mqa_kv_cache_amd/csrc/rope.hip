@@ -27,7 +27,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_apply_kernel(
         const int64_t tok = tok0 + tl;
         if (tok < n_tok) {
             float c, s;
-            rope_cos_sin(rope, (double)positions[tok], i, c, s);
+            rope_cos_sin(rope, positions ? (double)positions[tok] : (double)tok, i, c, s);
             cs_c[e] = c;
             cs_s[e] = s;
         }
@@ -61,6 +61,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_apply_kernel(
 
 }  // namespace
 
+// positions == nullptr: the position of token t is t (used to rotate K for prefill).
 hipError_t launch_rope_apply(const void* in, void* out, const int32_t* positions, int64_t n_tok,
                              int32_t n_heads, int32_t head_dim, int64_t stride_tok,
                              int64_t stride_head, const RopeDev& rope, hipStream_t s) {
@@ -78,6 +79,13 @@ hipError_t launch_rope_apply(const void* in, void* out, const int32_t* positions
                        (const uint16_t*)in, (uint16_t*)out, positions, n_tok, n_heads, head_dim,
                        stride_tok, stride_head, rope, tb);
     return hipGetLastError();
+}
+
+hipError_t launch_rope_rows(const void* in, void* out, int64_t n_tok, int32_t n_heads,
+                            int32_t head_dim, int64_t stride_tok, int64_t stride_head,
+                            const RopeDev& rope, hipStream_t s) {
+    return launch_rope_apply(in, out, nullptr, n_tok, n_heads, head_dim, stride_tok, stride_head,
+                             rope, s);
 }
 
 }  // namespace gqa
