@@ -154,9 +154,14 @@ gqa_status gqa_decode_split(const void* q, const void* k_cache, const void* v_ca
  *   v    bf16 [B][Hkv][T][D]
  *   rope NULL or GQA_ROPE_NONE: no rotation
  *   out  bf16 [B][Hq][T][D]
- *   workspace >= gqa_prefill_workspace_size(B, Hkv, T, D, rope) bytes (it holds
- *             the rotated keys); may be NULL when that size is 0.
- * Supported: D in {8, 16, 32, 64, 128}; T >= 1; Hq % Hkv == 0.
+ *   workspace >= gqa_prefill_workspace_size(B, Hkv, T, D, rope) bytes, device,
+ *             256-byte aligned (it receives fp16 copies of the rotated K and of
+ *             V, tiled for the matrix cores); contents on entry do not matter.
+ * Supported: D in {8, 16, 32, 64, 128}; T >= 1; Hq % Hkv == 0; B*Hq <= 65535.
+ * Precision: rotated Q (times scale*log2 e) and K, the probabilities and V
+ * enter the matrix cores as fp16 with fp32 accumulation, so |v|, |k| and the
+ * rotated, scaled |q| must stay below 65504 (fp16 range); larger inputs
+ * overflow.
  */
 size_t gqa_prefill_workspace_size(int32_t B, int32_t Hkv, int32_t T, int32_t D,
                                   const gqa_rope_params* rope);

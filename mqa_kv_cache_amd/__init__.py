@@ -226,14 +226,12 @@ def gqa_prefill_causal(q, k, v, scale: float, rope=None, out=None, workspace=Non
     _shape(out, q.shape, "out")
     _dev(out, "out")
     need = gqa_prefill_workspace_size(B, Hkv, T, D, rope)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    wp, wn = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
-    if workspace is not None:
-        _dev(workspace, "workspace", dtype=torch.uint8)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", dtype=torch.uint8)
     st = _lib.gqa_prefill_causal(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, Hq, Hkv, D,
-                                 float(scale), rope_params(rope), out.data_ptr(), wp or None, wn,
-                                 _stream(stream))
+                                 float(scale), rope_params(rope), out.data_ptr(),
+                                 workspace.data_ptr(), workspace.numel(), _stream(stream))
     _check(st, "gqa_prefill_causal")
     return out
 

@@ -175,8 +175,8 @@ size_t gqa_prefill_workspace_size(int32_t B, int32_t Hkv, int32_t T, int32_t D,
                                   const gqa_rope_params* rope) {
     if (B < 1 || Hkv < 1 || T < 1 || D < 1) return 0;
     RopeDev rd;
-    if (rope_prepare(rope, D, &rd) != GQA_OK || rd.half == 0) return 0;
-    return (((size_t)B * Hkv * T * D * 2) + 255) & ~(size_t)255;
+    if (rope_prepare(rope, D, &rd) != GQA_OK) return 0;
+    return 2 * prefill_prep_bytes(B, Hkv, T, D);
 }
 
 gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, int32_t B, int32_t T,
@@ -192,13 +192,10 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, int32
     RopeDev rd;
     st = rope_prepare(rope, D, &rd);
     if (st != GQA_OK) return st;
-    const size_t need = gqa_prefill_workspace_size(B, Hkv, T, D, rope);
-    if (need > 0) {
-        if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GQA_ERR_INVALID_ARGUMENT;
-        if (workspace_bytes < need) return GQA_ERR_WORKSPACE_TOO_SMALL;
-    }
-    return from_hip(launch_gqa_prefill(q, k, v, B, T, Hq, Hkv, D, scale, rd, out,
-                                       need > 0 ? workspace : nullptr, (hipStream_t)stream));
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GQA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < 2 * prefill_prep_bytes(B, Hkv, T, D)) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    return from_hip(launch_gqa_prefill(q, k, v, B, T, Hq, Hkv, D, scale, rd, out, workspace,
+                                       (hipStream_t)stream));
 }
 
 static gqa_status check_sparse_shape(int32_t B, int32_t H, int32_t Dqk, int32_t Dv, int32_t D_idx,

@@ -45,9 +45,12 @@ hipError_t launch_gqa_decode(const void* q, const void* k_cache, const void* v_c
                              int32_t D, int32_t S_max, float scale, const RopeDev& rope,
                              void* out, void* workspace, const DecodeLayout& lay, hipStream_t s);
 
+// Bytes of one prepared tensor (fp16 K rows, or fp16 V^T tiles) for prefill.
+size_t prefill_prep_bytes(int32_t B, int32_t Hkv, int32_t T, int32_t D);
+
 hipError_t launch_gqa_prefill(const void* q, const void* k, const void* v, int32_t B, int32_t T,
                               int32_t Hq, int32_t Hkv, int32_t D, float scale,
-                              const RopeDev& rope, void* out, void* k_rot, hipStream_t s);
+                              const RopeDev& rope, void* out, void* workspace, hipStream_t s);
 
 struct SparseLayout {
     size_t scores_bytes;   // fp32 [B][S_max]

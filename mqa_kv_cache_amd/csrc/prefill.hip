@@ -1,4 +1,4 @@
-// Causal GQA prefill on gfx950 bf16 MFMA (32x32x16).
+// Causal GQA prefill on gfx950 MFMA (32x32x16, fp16 operands, fp32 accumulation).
 //
 // Prefill is a dense contraction: K/V are reused by every later query
 // ([注意力变体与MoE] "生成时的瓶颈", last paragraph), so it runs on the matrix
@@ -6,27 +6,30 @@
 // "MQA 与 GQA", attention(): q k^T / sqrt(hd), strict upper triangle masked,
 // softmax, weighted sum of V) with RoPE on Q and K ([transformer架构] §1.1).
 //
-// Work split: one workgroup (4 waves) per (batch, q head, 128-query tile);
+// Operand precision: the rotated Q and K and the probabilities P are rounded
+// to fp16 (11-bit significand) rather than bf16 (8-bit): with bf16 the
+// rounding of rotated Q/K alone moves short-context outputs by up to ~2e-3,
+// the size of the absolute tolerance.  V converts from bf16 to fp16 exactly
+// (inside the fp16 range), and fp16 MFMA runs at the bf16 rate.
+//
+// Pre-pass (one read of K and V): K is rotated at its position and stored as
+// fp16 rows; V is stored as fp16 and transposed per 64-key tile, key columns
+// permuted to match the P^T operand.  Every later query tile re-reads these
+// tiles, so neither the rotation nor the transpose is repeated.
+//
+// Main kernel: one workgroup (4 waves) per (batch, q head, 128-query tile);
 // wave w owns 32 queries.  Query tiles are issued heaviest (latest) first so
 // the causal triangle balances across the machine.  Per 64-key tile:
-//   * the workgroup stages K (row-major, rows padded by 16 B) and V^T
-//     (transposed through registers, key columns permuted to match the P^T
-//     operand) in LDS;
+//   * the workgroup stages K (rows padded by 16 B) and V^T in LDS;
 //   * S^T[64 keys][32 queries] = K . Q^T   (K from LDS as A, Q^T in registers as B)
 //   * online softmax per query in base 2 (scale*log2(e) is folded into Q)
 //   * O^T[D][32 queries] += V^T . P^T       (P^T straight from the S^T accumulators)
 // The S^T accumulator layout is the P^T operand layout, so probabilities
 // never cross lanes; the only cross-lane step is one xor-32 shuffle for each
-// max and sum.  Q is rotated while loaded (fp64 angle, fp32 sincos); K is
-// rotated once by a pre-pass into the workspace, because every K row is
-// re-read by all later query tiles.
+// max and sum.  Q is rotated while it is loaded (fp64 angle, fp32 sincos).
 #include "device_common.h"
 
 namespace gqa {
-
-hipError_t launch_rope_rows(const void* in, void* out, int64_t n_tok, int32_t n_heads,
-                            int32_t head_dim, int64_t stride_tok, int64_t stride_head,
-                            const RopeDev& rope, hipStream_t s);
 
 namespace {
 
@@ -36,9 +39,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int BM = 128;   // queries per workgroup (4 waves x 32)
 constexpr int BN = 64;    // keys per tile
 
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma32h(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// fp32 -> fp16 x2, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    f16x2 h = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, h);
 }
 
 // Column of 4-key chunk a (0..3) inside its 16-key group in the V^T tile:
@@ -60,8 +72,8 @@ struct Geo {
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ out, int T, int Hq, int Hkv, float qscale, RopeDev rope) {
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vt,
+    uint16_t* __restrict__ out, int T, int T_pad, int Hq, int Hkv, float qscale, RopeDev rope) {
     using Gm = Geo<D>;
     __shared__ __attribute__((aligned(16))) uint16_t k_s[Gm::K_ELEMS];
     __shared__ __attribute__((aligned(16))) uint16_t vt_s[Gm::V_ELEMS];
@@ -78,13 +90,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const int qi = q0 + n;                    // this lane's query
 
     const size_t qbase = ((size_t)b * Hq + hq) * (size_t)T * D;
-    const size_t kvbase = ((size_t)b * Hkv + kvh) * (size_t)T * D;
-    const uint32_t nbytes = (uint32_t)T * D * 2u;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + qbase, nbytes);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k + kvbase, nbytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(v + kvbase, nbytes);
+    const size_t kvbase = ((size_t)b * Hkv + kvh) * (size_t)T_pad * D;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + qbase, (uint32_t)T * D * 2u);
 
-    // ---- Q^T operands: lane holds query qi, dims 16u + 8h .. +7 (rotated, scaled)
+    // ---- Q^T operands: lane holds query qi, dims 16u + 8h .. +7 (rotated, scaled, fp16)
     u32x4 qf[Gm::KSTEPS];
 #pragma unroll
     for (int u = 0; u < Gm::KSTEPS; ++u) {
@@ -110,7 +119,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
             }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) qf[u][j] = pack_bf16x2(x[2 * j] * qscale, x[2 * j + 1] * qscale);
+        for (int j = 0; j < 4; ++j) qf[u][j] = pack_f16x2(x[2 * j] * qscale, x[2 * j + 1] * qscale);
     }
 
     f32x16 o[Gm::MT];
@@ -122,46 +131,32 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 
     const int q_last_wg = min(qt * BM + BM - 1, T - 1);
     const int n_kt = q_last_wg / BN + 1;
-    constexpr int CPR = (D < 8 ? 1 : D / 8);            // 16-byte chunks per row
+    constexpr int CPR = D / 8;                          // 16-byte chunks per K row
+    const uint16_t* kbase = kh + kvbase;
+    const uint16_t* vbase = vt + kvbase;                // V^T tiles: [T_pad/64][D][64]
     for (int kt = 0; kt < n_kt; ++kt) {
         const int ks = kt * BN;
         __syncthreads();
-        // ---- stage K tile (row-major)
+        // ---- stage K tile (row-major fp16, rows padded by 16 B)
         for (int c = tid; c < BN * CPR; c += 256) {
             const int key = c / CPR, dc = c - key * CPR;
-            u32x4 val = buf_load16(kr, (uint32_t)(((ks + key) * D + 8 * dc) * 2));
-            *reinterpret_cast<u32x4*>(&k_s[key * Gm::KSTR + 8 * dc]) = val;
+            *reinterpret_cast<u32x4*>(&k_s[key * Gm::KSTR + 8 * dc]) =
+                *reinterpret_cast<const u32x4*>(kbase + (size_t)(ks + key) * D + 8 * dc);
         }
         if constexpr (D < 16) {
             for (int c = tid; c < BN; c += 256)
                 *reinterpret_cast<u32x4*>(&k_s[c * Gm::KSTR + 8]) = u32x4{0, 0, 0, 0};
         }
-        // ---- stage V^T tile: 4 keys x 8 dims per item, transposed in registers
-        for (int c = tid; c < (BN / 4) * CPR; c += 256) {
-            const int kg = c / CPR, dc = c - kg * CPR;
-            u32x4 r4[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                r4[r] = buf_load16(vr, (uint32_t)(((ks + 4 * kg + r) * D + 8 * dc) * 2));
-            const int col = 16 * (kg >> 2) + chunk_col(kg & 3);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int w = t >> 1;
-                u32x2 pr;
-                if (t & 1) {
-                    pr[0] = (r4[0][w] >> 16) | (r4[1][w] & 0xFFFF0000u);
-                    pr[1] = (r4[2][w] >> 16) | (r4[3][w] & 0xFFFF0000u);
-                } else {
-                    pr[0] = (r4[0][w] & 0xFFFFu) | (r4[1][w] << 16);
-                    pr[1] = (r4[2][w] & 0xFFFFu) | (r4[3][w] << 16);
-                }
-                *reinterpret_cast<u32x2*>(&vt_s[(8 * dc + t) * Gm::VSTR + col]) = pr;
-            }
+        // ---- stage V^T tile (already transposed and permuted by the pre-pass)
+        for (int c = tid; c < D * (BN / 8); c += 256) {
+            const int d = c / (BN / 8), cc = c - d * (BN / 8);
+            *reinterpret_cast<u32x4*>(&vt_s[d * Gm::VSTR + 8 * cc]) =
+                *reinterpret_cast<const u32x4*>(vbase + ((size_t)kt * D + d) * BN + 8 * cc);
         }
         if constexpr (D < 32) {
-            for (int c = tid; c < (Gm::DM - D) * (BN / 4); c += 256) {
-                const int row = D + c / (BN / 4), cc = c % (BN / 4);
-                *reinterpret_cast<u32x2*>(&vt_s[row * Gm::VSTR + 4 * cc]) = u32x2{0, 0};
+            for (int c = tid; c < (Gm::DM - D) * (BN / 8); c += 256) {
+                const int row = D + c / (BN / 8), cc = c % (BN / 8);
+                *reinterpret_cast<u32x4*>(&vt_s[row * Gm::VSTR + 8 * cc]) = u32x4{0, 0, 0, 0};
             }
         }
         __syncthreads();
@@ -176,7 +171,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 #pragma unroll
             for (int u = 0; u < Gm::KSTEPS; ++u) {
                 const u32x4 kf = *reinterpret_cast<const u32x4*>(&k_s[(32 * st + n) * Gm::KSTR + 16 * u + 8 * h]);
-                s[st] = mfma32(kf, qf[u], s[st]);
+                s[st] = mfma32h(kf, qf[u], s[st]);
             }
         }
         // ---- causal mask (only tiles that reach past this wave's first query)
@@ -219,15 +214,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 u32x4 pb;
-                pb[0] = pack_bf16x2(s[st][8 * c + 0], s[st][8 * c + 1]);
-                pb[1] = pack_bf16x2(s[st][8 * c + 2], s[st][8 * c + 3]);
-                pb[2] = pack_bf16x2(s[st][8 * c + 4], s[st][8 * c + 5]);
-                pb[3] = pack_bf16x2(s[st][8 * c + 6], s[st][8 * c + 7]);
+                pb[0] = pack_f16x2(s[st][8 * c + 0], s[st][8 * c + 1]);
+                pb[1] = pack_f16x2(s[st][8 * c + 2], s[st][8 * c + 3]);
+                pb[2] = pack_f16x2(s[st][8 * c + 4], s[st][8 * c + 5]);
+                pb[3] = pack_f16x2(s[st][8 * c + 6], s[st][8 * c + 7]);
                 const int col = 16 * (2 * st + c) + 8 * h;
 #pragma unroll
                 for (int mt = 0; mt < Gm::MT; ++mt) {
                     const u32x4 vf = *reinterpret_cast<const u32x4*>(&vt_s[(32 * mt + n) * Gm::VSTR + col]);
-                    o[mt] = mfma32(vf, pb, o[mt]);
+                    o[mt] = mfma32h(vf, pb, o[mt]);
                 }
             }
     }
@@ -251,34 +246,114 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     }
 }
 
+// Pre-pass, one block per (64-key tile, kv head, batch):
+//   K  -> RoPE at its position (fp64 angle, fp32 sincos) -> fp16 rows   [B][Hkv][T_pad][D]
+//   V  -> fp16 (exact for bf16 values in fp16 range), transposed per tile into
+//         [B][Hkv][T_pad/64][D][64] with key columns permuted for the P^T operand.
+// Rows at or past T are written as zeros.
 template <int D>
-void launch_d(const void* q, const void* k, const void* v, void* out, int B, int T, int Hq, int Hkv,
-              float qscale, const RopeDev& rope, hipStream_t s) {
+__global__ __launch_bounds__(256) void prefill_prep_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ kh,
+    uint16_t* __restrict__ vt, int T, int T_pad, int Hkv, RopeDev rope) {
+    __shared__ float cs_c[BN * kMaxRotaryHalf / 2];
+    __shared__ float cs_s[BN * kMaxRotaryHalf / 2];
+    constexpr int CPR = D / 8;
+    const int tid = threadIdx.x;
+    const int kt = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int ks = kt * BN;
+    const int half = rope.half;   // <= D/2 <= 64
+    for (int e = tid; e < BN * half; e += 256) {
+        const int tl = e / half, i = e - tl * half;
+        float c, s;
+        rope_cos_sin(rope, (double)(ks + tl), i, c, s);
+        cs_c[e] = c;
+        cs_s[e] = s;
+    }
+    __syncthreads();
+    const size_t in_base = ((size_t)b * Hkv + kvh) * (size_t)T * D;
+    const size_t out_base = ((size_t)b * Hkv + kvh) * (size_t)T_pad * D;
+    for (int c = tid; c < BN * CPR; c += 256) {
+        const int key = c / CPR, dc = c - key * CPR;
+        const int t = ks + key;
+        u32x4 val = u32x4{0, 0, 0, 0};
+        if (t < T) {
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(k + in_base + (size_t)t * D + 8 * dc);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                float xe = bf16_lo(raw[p]), xo = bf16_hi(raw[p]);
+                const int i = 4 * dc + p;
+                if (i < half) {
+                    const float cc = cs_c[key * half + i], ss = cs_s[key * half + i];
+                    const float ye = xe * cc - xo * ss, yo = xe * ss + xo * cc;
+                    xe = ye;
+                    xo = yo;
+                }
+                val[p] = pack_f16x2(xe, xo);
+            }
+        }
+        *reinterpret_cast<u32x4*>(kh + out_base + (size_t)t * D + 8 * dc) = val;
+    }
+    for (int c = tid; c < (BN / 4) * CPR; c += 256) {
+        const int kg = c / CPR, dc = c - kg * CPR;
+        u32x4 r4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = ks + 4 * kg + r;
+            u32x4 raw = u32x4{0, 0, 0, 0};
+            if (t < T) raw = *reinterpret_cast<const u32x4*>(v + in_base + (size_t)t * D + 8 * dc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r4[r][j] = pack_f16x2(bf16_lo(raw[j]), bf16_hi(raw[j]));
+        }
+        const int col = 16 * (kg >> 2) + chunk_col(kg & 3);
+        uint16_t* tile = vt + out_base + (size_t)kt * D * BN;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int w = t >> 1;
+            u32x2 pr;
+            if (t & 1) {
+                pr[0] = (r4[0][w] >> 16) | (r4[1][w] & 0xFFFF0000u);
+                pr[1] = (r4[2][w] >> 16) | (r4[3][w] & 0xFFFF0000u);
+            } else {
+                pr[0] = (r4[0][w] & 0xFFFFu) | (r4[1][w] << 16);
+                pr[1] = (r4[2][w] & 0xFFFFu) | (r4[3][w] << 16);
+            }
+            *reinterpret_cast<u32x2*>(tile + (size_t)(8 * dc + t) * BN + col) = pr;
+        }
+    }
+}
+
+template <int D>
+void launch_d(const void* q, const void* k, const void* v, void* out, void* kh, void* vt, int B,
+              int T, int Hq, int Hkv, float qscale, const RopeDev& rope, hipStream_t s) {
+    const int T_pad = (T + BN - 1) / BN * BN;
+    hipLaunchKernelGGL((prefill_prep_kernel<D>), dim3(T_pad / BN, Hkv, B), dim3(256), 0, s,
+                       (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)kh, (uint16_t*)vt, T,
+                       T_pad, Hkv, rope);
     dim3 grid((T + BM - 1) / BM, Hq, B);
     hipLaunchKernelGGL((prefill_kernel<D>), grid, dim3(256), 0, s, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)out, T, Hq, Hkv, qscale,
-                       rope);
+                       (const uint16_t*)kh, (const uint16_t*)vt, (uint16_t*)out, T, T_pad, Hq, Hkv,
+                       qscale, rope);
 }
 
 }  // namespace
 
+size_t prefill_prep_bytes(int32_t B, int32_t Hkv, int32_t T, int32_t D) {
+    const size_t T_pad = ((size_t)T + BN - 1) / BN * BN;
+    return (((size_t)B * Hkv * T_pad * D * 2) + 255) & ~(size_t)255;
+}
+
 hipError_t launch_gqa_prefill(const void* q, const void* k, const void* v, int32_t B, int32_t T,
                               int32_t Hq, int32_t Hkv, int32_t D, float scale, const RopeDev& rope,
-                              void* out, void* k_rot, hipStream_t s) {
-    const void* kk = k;
-    if (rope.half > 0) {
-        // rotate K once: rows are (token t, head bh) with bh over B*Hkv, position = t
-        hipError_t e = launch_rope_rows(k, k_rot, T, B * Hkv, D, D, (int64_t)T * D, rope, s);
-        if (e != hipSuccess) return e;
-        kk = k_rot;
-    }
+                              void* out, void* workspace, hipStream_t s) {
     const float qscale = scale * kLog2e;
+    void* kh = workspace;
+    void* vt = reinterpret_cast<char*>(workspace) + prefill_prep_bytes(B, Hkv, T, D);
     switch (D) {
-        case 8: launch_d<8>(q, kk, v, out, B, T, Hq, Hkv, qscale, rope, s); break;
-        case 16: launch_d<16>(q, kk, v, out, B, T, Hq, Hkv, qscale, rope, s); break;
-        case 32: launch_d<32>(q, kk, v, out, B, T, Hq, Hkv, qscale, rope, s); break;
-        case 64: launch_d<64>(q, kk, v, out, B, T, Hq, Hkv, qscale, rope, s); break;
-        default: launch_d<128>(q, kk, v, out, B, T, Hq, Hkv, qscale, rope, s); break;
+        case 8: launch_d<8>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, s); break;
+        case 16: launch_d<16>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, s); break;
+        case 32: launch_d<32>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, s); break;
+        case 64: launch_d<64>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, s); break;
+        default: launch_d<128>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, s); break;
     }
     return hipGetLastError();
 }

@@ -114,10 +114,10 @@ def test_prefill_validation(m):
     assert call(q=MIS) == m.ERR_INVALID_ARGUMENT
     r = _rope(m, scaling=m.ROPE_NTK, base=1e6, factor=4.0)
     need = m.gqa_prefill_workspace_size(1, 2, 16, 128, r.contents)
-    assert need == 2 * 16 * 128 * 2
+    assert need == 2 * (2 * 64 * 128 * 2)      # fp16 K rows + fp16 V^T tiles, T padded to 64
     assert call(rope=r, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
     assert call(rope=r, ws=None, wsn=need) == m.ERR_INVALID_ARGUMENT
-    assert m.gqa_prefill_workspace_size(1, 2, 16, 128, None) == 0
+    assert m.gqa_prefill_workspace_size(1, 2, 16, 128, None) == need
 
 
 def test_sparse_validation(m):
