@@ -24,33 +24,12 @@
 // The combine kernel merges the per-split (m, l, o) with the usual
 // log-sum-exp rescaling; the result equals the softmax over the whole row.
 #include "device_common.h"
+#include "combine.h"
 
 namespace gqa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-
-// Row (within a 32-row tile) that k-slot r of lane group G stands for.  It is
-// the row the S^T accumulator of that lane group holds in register r:
-// rows 4G..4G+3 of the first 16-row half, 16+4G..16+4G+3 of the second.
-__device__ __forceinline__ int slot_row(int G, int r) {
-    return (r < 4) ? (4 * G + r) : (16 + 4 * G + (r - 4));
-}
-
-// Column t (0..7) of an 8x8 bf16 block held as 8 rows of 16 bytes, packed as
-// one MFMA operand whose k-slots are the rows.
-__device__ __forceinline__ u32x4 column_of(const u32x4 (&rows)[8], int t) {
-    u32x4 r;
-    const int w = t >> 1;
-    if (t & 1) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] = (rows[2 * j][w] >> 16) | (rows[2 * j + 1][w] & 0xFFFF0000u);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] = (rows[2 * j][w] & 0xFFFFu) | (rows[2 * j + 1][w] << 16);
-    }
-    return r;
-}
 
 template <int D, int NB>
 __global__ __launch_bounds__(256) void decode_split_kernel(
@@ -221,42 +200,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     }
 }
 
-// One wave per (batch, q head): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ seq_lens, int Hq, int S_max, int split_rows, int n_split_max,
-    int BH, uint16_t* __restrict__ out) {
-    constexpr int PER = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (idx >= BH) return;
-    const int b = idx / Hq;
-    const int L = min(max(seq_lens[b], 1), S_max);
-    const int ns = (L + split_rows - 1) / split_rows;
-    const float* ml = part_ml + (size_t)idx * n_split_max * 2;
-    const float* po = part_o + (size_t)idx * n_split_max * D;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
-    float acc[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-    float den = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float w = fast_exp2(ml[2 * s] - M);
-        den += w * ml[2 * s + 1];
-#pragma unroll
-        for (int j = 0; j < PER; ++j) acc[j] += w * po[(size_t)s * D + lane * PER + j];
-    }
-    const float inv = 1.0f / den;
-    uint16_t* o = out + (size_t)idx * D + lane * PER;
-    if constexpr (PER == 2) {
-        *reinterpret_cast<uint32_t*>(o) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    } else {
-        o[0] = (uint16_t)f32_to_bf16_bits(acc[0] * inv);
-    }
-}
-
 template <int D, int NB>
 void launch_split(dim3 grid, hipStream_t s, const void* q, const void* k, const void* v,
                   const int32_t* sl, int Hq, int Hkv, int S_max, float qscale, const RopeDev& rope,
@@ -312,11 +255,11 @@ hipError_t launch_gqa_decode(const void* q, const void* k_cache, const void* v_c
     const int BH = B * Hq;
     dim3 cgrid((BH + 3) / 4);
     if (D == 128)
-        hipLaunchKernelGGL((decode_combine_kernel<128>), cgrid, dim3(256), 0, s, po, pml, seq_lens,
-                           Hq, S_max, lay.split_rows, lay.n_split_max, BH, (uint16_t*)out);
+        hipLaunchKernelGGL((combine_partials_kernel<128>), cgrid, dim3(256), 0, s, po, pml, seq_lens,
+                           Hq, S_max, S_max, lay.split_rows, lay.n_split_max, BH, (uint16_t*)out);
     else
-        hipLaunchKernelGGL((decode_combine_kernel<64>), cgrid, dim3(256), 0, s, po, pml, seq_lens,
-                           Hq, S_max, lay.split_rows, lay.n_split_max, BH, (uint16_t*)out);
+        hipLaunchKernelGGL((combine_partials_kernel<64>), cgrid, dim3(256), 0, s, po, pml, seq_lens,
+                           Hq, S_max, S_max, lay.split_rows, lay.n_split_max, BH, (uint16_t*)out);
     return hipGetLastError();
 }
 

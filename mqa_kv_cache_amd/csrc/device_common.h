@@ -80,6 +80,28 @@ __device__ __forceinline__ void rope_cos_sin(const RopeDev& r, double pos, int i
     s = sv * r.amp;
 }
 
+// Row (within a 32-row tile) that k-slot r of lane group G stands for.  It is
+// the row the S^T accumulator of that lane group holds in register r:
+// rows 4G..4G+3 of the first 16-row half, 16+4G..16+4G+3 of the second.
+__device__ __forceinline__ int slot_row(int G, int r) {
+    return (r < 4) ? (4 * G + r) : (16 + 4 * G + (r - 4));
+}
+
+// Column t (0..7) of an 8x8 bf16 block held as 8 rows of 16 bytes, packed as
+// one MFMA operand whose k-slots are the rows.
+__device__ __forceinline__ u32x4 column_of(const u32x4 (&rows)[8], int t) {
+    u32x4 r;
+    const int w = t >> 1;
+    if (t & 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = (rows[2 * j][w] >> 16) | (rows[2 * j + 1][w] & 0xFFFF0000u);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = (rows[2 * j][w] & 0xFFFFu) | (rows[2 * j + 1][w] << 16);
+    }
+    return r;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
     return __shfl_xor(v, mask, 64);

@@ -1,14 +1,440 @@
+// DSA-style top-k sparse decode over an MLA latent cache on gfx950:
+//   o = Attn(q, KV[TopK(ReLU(K_I . q_I))])
+// ([稀疏注意力] "改进一：DSA", the selection chain; [transformer架构] §2.2 (1)-(2);
+// [attention] DSA ①-③).
+//
+// 1. indexer_kernel: one HBM pass over the indexer keys.  Sixteen lanes share a
+//    128-dim row (16 bytes each); products of bf16 values are exact in fp64 and
+//    are summed in fp64, then rounded once to fp32 and passed through ReLU.
+//    The pass also builds the first radix-select histogram (top 12 bits of
+//    the non-negative fp32 score) in LDS and flushes it with atomics.
+// 2. topk_select_kernel: one 1024-thread workgroup per batch row finds the
+//    exact k-th largest score (first digit from the histogram; the rest from
+//    the candidates of that bin, kept in LDS, or from further passes over the
+//    scores when the bin is too large), then writes the selected indices in
+//    ascending order: every score above the threshold, plus the first
+//    equal-to-threshold scores in index order until k are taken.
+// 3. sparse_attn_kernel: MQA attention of the H heads over the gathered
+//    latent rows (the indexed rows are read straight from the cache; no copy
+//    of the selection is made).  Same MFMA structure as the dense decode:
+//    S^T = C . Q^T over 576 dims, online softmax, O^T += C[:, :512]^T . P^T;
+//    each wave covers 16 heads and 128 selected rows and writes a partial
+//    (m, l, o) that combine_partials_kernel merges.
 #include "device_common.h"
+#include "combine.h"
+
 namespace gqa {
+namespace {
+
+constexpr int kDqk = 576, kDv = 512, kDidx = 128;
+constexpr int kHistBins = 4096;      // first digit: score bits 31..20
+constexpr int kRowsPerChunk = 128;   // selected rows per attention wave
+constexpr int kCandCap = 8192;       // LDS candidates of the threshold bin
+constexpr float kLog2e = 1.4426950408889634f;
+
+__global__ void zero_u32_kernel(uint32_t* __restrict__ p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// 1. indexer
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void indexer_kernel(
+    const uint16_t* __restrict__ q_index, const uint16_t* __restrict__ k_index,
+    const int32_t* __restrict__ seq_lens, int S_max, int rows_per_block,
+    float* __restrict__ scores, uint32_t* __restrict__ hist) {
+    __shared__ uint32_t lh[kHistBins];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = lane >> 4, n = lane & 15;
+    const int b = blockIdx.y;
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int r_begin = blockIdx.x * rows_per_block;
+    const int r_end = min(r_begin + rows_per_block, L);
+    for (int i = tid; i < kHistBins; i += 256) lh[i] = 0u;
+    __syncthreads();
+    if (r_begin < r_end) {
+        const u32x4 qraw = *reinterpret_cast<const u32x4*>(q_index + (size_t)b * kDidx + 8 * n);
+        double qv[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            qv[2 * j] = (double)bf16_lo(qraw[j]);
+            qv[2 * j + 1] = (double)bf16_hi(qraw[j]);
+        }
+        const __amdgpu_buffer_rsrc_t kr =
+            make_rsrc(k_index + (size_t)b * S_max * kDidx, (uint32_t)L * kDidx * 2u);
+        float* srow = scores + (size_t)b * S_max;
+        for (int r = r_begin + 16 * wave; r < r_end; r += 64) {
+            u32x4 raw[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                raw[a] = buf_load16(kr, (uint32_t)(((r + 4 * a + G) * kDidx + 8 * n) * 2));
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                double acc = 0.0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc = fma(qv[2 * j], (double)bf16_lo(raw[a][j]), acc);
+                    acc = fma(qv[2 * j + 1], (double)bf16_hi(raw[a][j]), acc);
+                }
+                acc += __shfl_xor(acc, 8, 64);
+                acc += __shfl_xor(acc, 4, 64);
+                acc += __shfl_xor(acc, 2, 64);
+                acc += __shfl_xor(acc, 1, 64);
+                const int row = r + 4 * a + G;
+                if (n == 0 && row < r_end) {
+                    const float s = acc > 0.0 ? (float)acc : 0.0f;   // ReLU, +0 for ties
+                    srow[row] = s;
+                    const uint32_t bin = __float_as_uint(s) >> 20;
+                    if (bin) atomicAdd(&lh[bin], 1u);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < kHistBins; i += 256)
+        if (lh[i]) atomicAdd(&hist[(size_t)b * kHistBins + i], lh[i]);
+}
+
+// ---------------------------------------------------------------------------
+// 2. top-k selection
+// ---------------------------------------------------------------------------
+constexpr int kSelThreads = 1024;
+
+// Inclusive prefix sum of one value per thread across the 1024-thread block.
+__device__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* wsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t w = lane < kSelThreads / 64 ? wsum[lane] : 0u;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const uint32_t t = __shfl_up(w, o, 64);
+            if (lane >= o) w += t;
+        }
+        if (lane < kSelThreads / 64) wsum[lane] = w;   // inclusive wave totals
+    }
+    __syncthreads();
+    const uint32_t add = wave ? wsum[wave - 1] : 0u;
+    __syncthreads();
+    return v + add;
+}
+
+// Over a histogram h[0..nbins) in LDS, find the largest bin B with
+// (count in bins >= B) >= need.  Writes B and the count in bins > B to
+// out[0], out[1].  Every thread must call it.
+__device__ void find_crossing(const uint32_t* h, int nbins, uint32_t need, uint32_t* wsum,
+                              uint32_t* out) {
+    const int per = (nbins + kSelThreads - 1) / kSelThreads;
+    // thread t owns bins [hi - per, hi) counting down from the top: reverse order
+    const int t = threadIdx.x;
+    const int hi = nbins - t * per;
+    const int lo = max(hi - per, 0);
+    uint32_t c = 0;
+    for (int i = lo; i < hi; ++i) c += h[i];
+    const uint32_t incl = block_inclusive_scan(c, wsum);   // count in bins >= lo
+    const uint32_t excl = incl - c;                         // count in bins >= hi
+    if (excl < need && incl >= need) {
+        uint32_t acc = excl;
+        for (int i = hi - 1; i >= lo; --i) {
+            if (acc + h[i] >= need) {
+                out[0] = (uint32_t)i;
+                out[1] = acc;
+                break;
+            }
+            acc += h[i];
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
+    const float* __restrict__ scores, const uint32_t* __restrict__ hist_g,
+    const int32_t* __restrict__ seq_lens, int S_max, int top_k, int32_t* __restrict__ topk_idx) {
+    __shared__ uint32_t h[kHistBins];
+    __shared__ uint32_t cand[kCandCap];
+    __shared__ uint32_t wsum[kSelThreads / 64];
+    __shared__ uint32_t res[2];
+    __shared__ uint32_t ccount;
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x;
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int k = min(top_k, L);
+    const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_max);
+    int32_t* outp = topk_idx + (size_t)b * top_k;
+    for (int i = k + tid; i < top_k; i += kSelThreads) outp[i] = -1;
+    if (k == L) {   // everything is selected
+        for (int i = tid; i < L; i += kSelThreads) outp[i] = i;
+        return;
+    }
+
+    // ---- digit 1 (bits 31..20) from the indexer's histogram; bin 0 is implied
+    uint32_t nz = 0;
+    for (int i = tid; i < kHistBins; i += kSelThreads) {
+        const uint32_t v = i ? hist_g[(size_t)b * kHistBins + i] : 0u;
+        h[i] = v;
+        nz += v;
+    }
+    if (tid == 0) ccount = 0;
+    const uint32_t tot = block_inclusive_scan(nz, wsum);
+    if (tid == kSelThreads - 1) h[0] = (uint32_t)L - tot;
+    __syncthreads();
+    find_crossing(h, kHistBins, (uint32_t)k, wsum, res);
+    const uint32_t B1 = res[0];
+    uint32_t above = res[1];
+    uint32_t need = (uint32_t)k - above;
+    const uint32_t bin_count = h[B1];
+    __syncthreads();
+
+    uint32_t T;   // the k-th largest key
+    if (bin_count <= (uint32_t)kCandCap) {
+        // ---- gather the keys of bin B1 into LDS, then refine there
+        for (int j = tid; j < L; j += kSelThreads) {
+            const uint32_t key = keys[j];
+            if ((key >> 20) == B1) cand[atomicAdd(&ccount, 1u)] = key;
+        }
+        __syncthreads();
+        const uint32_t nc = ccount;
+        for (int i = tid; i < kHistBins; i += kSelThreads) h[i] = 0u;
+        __syncthreads();
+        for (uint32_t i = tid; i < nc; i += kSelThreads) atomicAdd(&h[(cand[i] >> 8) & 0xFFFu], 1u);
+        __syncthreads();
+        find_crossing(h, kHistBins, need, wsum, res);
+        const uint32_t B2 = res[0];
+        above += res[1];
+        need -= res[1];
+        __syncthreads();
+        for (int i = tid; i < 256; i += kSelThreads) h[i] = 0u;
+        __syncthreads();
+        const uint32_t pre = (B1 << 12) | B2;
+        for (uint32_t i = tid; i < nc; i += kSelThreads)
+            if ((cand[i] >> 8) == pre) atomicAdd(&h[cand[i] & 0xFFu], 1u);
+        __syncthreads();
+        find_crossing(h, 256, need, wsum, res);
+        T = (pre << 8) | res[0];
+        above += res[1];
+        need -= res[1];
+    } else {
+        // ---- large bin: two more passes over the scores
+        for (int i = tid; i < kHistBins; i += kSelThreads) h[i] = 0u;
+        __syncthreads();
+        for (int j = tid; j < L; j += kSelThreads) {
+            const uint32_t key = keys[j];
+            if ((key >> 20) == B1) atomicAdd(&h[(key >> 8) & 0xFFFu], 1u);
+        }
+        __syncthreads();
+        find_crossing(h, kHistBins, need, wsum, res);
+        const uint32_t B2 = res[0];
+        above += res[1];
+        need -= res[1];
+        __syncthreads();
+        for (int i = tid; i < 256; i += kSelThreads) h[i] = 0u;
+        __syncthreads();
+        const uint32_t pre = (B1 << 12) | B2;
+        for (int j = tid; j < L; j += kSelThreads) {
+            const uint32_t key = keys[j];
+            if ((key >> 8) == pre) atomicAdd(&h[key & 0xFFu], 1u);
+        }
+        __syncthreads();
+        find_crossing(h, 256, need, wsum, res);
+        T = (pre << 8) | res[0];
+        above += res[1];
+        need -= res[1];
+    }
+    // `above` keys are > T; `need` of the keys == T are taken, lowest indices first.
+
+    // ---- ordered compaction: thread t owns indices [t*C, t*C + C)
+    const int C = (L + kSelThreads - 1) / kSelThreads;
+    const int j0 = min(tid * C, L), j1 = min(j0 + C, L);
+    uint32_t gt = 0, eq = 0;
+    for (int j = j0; j < j1; ++j) {
+        const uint32_t key = keys[j];
+        gt += key > T;
+        eq += key == T;
+    }
+    const uint32_t gt_in = block_inclusive_scan(gt, wsum);
+    const uint32_t eq_in = block_inclusive_scan(eq, wsum);
+    uint32_t eq_seen = eq_in - eq;
+    uint32_t pos = (gt_in - gt) + min(eq_seen, need);
+    for (int j = j0; j < j1; ++j) {
+        const uint32_t key = keys[j];
+        if (key > T) {
+            outp[pos++] = j;
+        } else if (key == T) {
+            if (eq_seen < need) outp[pos++] = j;
+            ++eq_seen;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. attention over the selected latent rows
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void sparse_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ seq_lens, int H, int S_max,
+    int top_k, float qscale, float* __restrict__ part_o, float* __restrict__ part_ml,
+    int n_chunks) {
+    constexpr int KU = kDqk / 32;   // 18 MFMA k-steps for the scores
+    const int lane = threadIdx.x;
+    const int G = lane >> 4, n = lane & 15;
+    const int chunk = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int k = min(top_k, L);
+    const int c0 = chunk * kRowsPerChunk;
+    if (c0 >= k) return;
+    const int c1 = min(c0 + kRowsPerChunk, k);
+    const int h = hb * 16 + n;
+
+    // q is bf16 already: used exactly as the B operand; the scale is applied to S.
+    u32x4 qf[KU];
+    const uint16_t* qrow = q + ((size_t)b * H + h) * kDqk;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u + 8 * G);
+
+    const __amdgpu_buffer_rsrc_t cr =
+        make_rsrc(latent + (size_t)b * S_max * kDqk, (uint32_t)S_max * kDqk * 2u);
+    const int32_t* sel = topk_idx + (size_t)b * top_k;
+
+    f32x4 o[4][8];
+#pragma unroll
+    for (int dq = 0; dq < 4; ++dq)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[dq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int t0 = c0; t0 < c1; t0 += 32) {
+        // row byte offsets of this lane's K rows (n, 16+n) and V rows (slot_row(G, r))
+        uint32_t koff[2], voff[8];
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+            const int p = t0 + 16 * th + n;
+            const int idx = p < c1 ? sel[p] : -1;
+            koff[th] = idx >= 0 ? (uint32_t)idx * (kDqk * 2) : 0x80000000u;
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int p = t0 + slot_row(G, r);
+            const int idx = p < c1 ? sel[p] : -1;
+            voff[r] = idx >= 0 ? (uint32_t)idx * (kDqk * 2) : 0x80000000u;
+        }
+        f32x4 sc[2];
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+            sc[th] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {
+                const u32x4 kf = buf_load16(cr, koff[th] + (32 * u + 8 * G) * 2);
+                sc[th] = mfma16(kf, qf[u], sc[th]);
+            }
+        }
+        const bool tail = (t0 + 32 > c1);
+#pragma unroll
+        for (int th = 0; th < 2; ++th)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sc[th][i] *= qscale;
+                if (tail && t0 + 16 * th + 4 * G + i >= c1) sc[th][i] = -INFINITY;
+            }
+        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+        mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        float p[2][4];
+        float ls = 0.f;
+#pragma unroll
+        for (int th = 0; th < 2; ++th)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[th][i] = fast_exp2(sc[th][i] - m_new);
+                ls += p[th][i];
+            }
+        ls += wave_shfl_xor(ls, 16);
+        ls += wave_shfl_xor(ls, 32);
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+        u32x4 pb;
+        pb[0] = pack_bf16x2(p[0][0], p[0][1]);
+        pb[1] = pack_bf16x2(p[0][2], p[0][3]);
+        pb[2] = pack_bf16x2(p[1][0], p[1][1]);
+        pb[3] = pack_bf16x2(p[1][2], p[1][3]);
+#pragma unroll
+        for (int dq = 0; dq < 4; ++dq) {
+            u32x4 vreg[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) vreg[r] = buf_load16(cr, voff[r] + (128 * dq + 8 * n) * 2);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                o[dq][t] *= alpha;
+                o[dq][t] = mfma16(column_of(vreg, t), pb, o[dq][t]);
+            }
+        }
+    }
+
+    const size_t idx = ((size_t)b * H + h) * n_chunks + chunk;
+    float* po = part_o + idx * kDv;
+#pragma unroll
+    for (int dq = 0; dq < 4; ++dq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 128 * dq + 8 * (4 * G + i);   // this lane holds d = d0 + t
+            *reinterpret_cast<f32x4*>(po + d0) = f32x4{o[dq][0][i], o[dq][1][i], o[dq][2][i], o[dq][3][i]};
+            *reinterpret_cast<f32x4*>(po + d0 + 4) = f32x4{o[dq][4][i], o[dq][5][i], o[dq][6][i], o[dq][7][i]};
+        }
+    if (G == 0) {
+        part_ml[idx * 2] = m_run;
+        part_ml[idx * 2 + 1] = l_run;
+    }
+}
+
+}  // namespace
+
 SparseLayout sparse_layout(int32_t B, int32_t H, int32_t S_max, int32_t top_k) {
     SparseLayout l{};
-    l.scores_bytes = ((size_t)B * S_max * 4 + 255) & ~(size_t)255;
-    l.total = l.scores_bytes;
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    l.n_chunks = (top_k + kRowsPerChunk - 1) / kRowsPerChunk;
+    l.scores_bytes = al((size_t)B * S_max * sizeof(float));
+    l.hist_bytes = al((size_t)B * kHistBins * sizeof(uint32_t));
+    l.o_bytes = al((size_t)B * H * l.n_chunks * kDv * sizeof(float));
+    l.ml_bytes = al((size_t)B * H * l.n_chunks * 2 * sizeof(float));
+    l.total = l.scores_bytes + l.hist_bytes + l.o_bytes + l.ml_bytes;
     return l;
 }
-hipError_t launch_topk_sparse_decode(const void*, const void*, const void*, const void*,
-                                     const int32_t*, int32_t, int32_t, int32_t, int32_t, float,
-                                     int32_t*, void*, void*, const SparseLayout&, hipStream_t) {
-    return hipErrorNotSupported;
+
+hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const void* q_index,
+                                     const void* k_index, const int32_t* seq_lens, int32_t B,
+                                     int32_t H, int32_t S_max, int32_t top_k, float scale,
+                                     int32_t* topk_idx, void* out, void* workspace,
+                                     const SparseLayout& lay, hipStream_t s) {
+    char* w = reinterpret_cast<char*>(workspace);
+    float* scores = reinterpret_cast<float*>(w);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(w + lay.scores_bytes);
+    float* po = reinterpret_cast<float*>(w + lay.scores_bytes + lay.hist_bytes);
+    float* pml = reinterpret_cast<float*>(w + lay.scores_bytes + lay.hist_bytes + lay.o_bytes);
+
+    const int nh = B * kHistBins;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((nh + 255) / 256), dim3(256), 0, s, hist, nh);
+    const int rows_per_block = 1024;
+    hipLaunchKernelGGL(indexer_kernel, dim3((S_max + rows_per_block - 1) / rows_per_block, B),
+                       dim3(256), 0, s, (const uint16_t*)q_index, (const uint16_t*)k_index,
+                       seq_lens, S_max, rows_per_block, scores, hist);
+    hipLaunchKernelGGL(topk_select_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, hist,
+                       seq_lens, S_max, top_k, topk_idx);
+    hipLaunchKernelGGL(sparse_attn_kernel, dim3(lay.n_chunks, H / 16, B), dim3(64), 0, s,
+                       (const uint16_t*)q, (const uint16_t*)latent, topk_idx, seq_lens, H, S_max,
+                       top_k, scale * kLog2e, po, pml, lay.n_chunks);
+    const int BH = B * H;
+    hipLaunchKernelGGL((combine_partials_kernel<kDv>), dim3((BH + 3) / 4), dim3(256), 0, s, po, pml,
+                       seq_lens, H, S_max, top_k, kRowsPerChunk, lay.n_chunks, BH, (uint16_t*)out);
+    return hipGetLastError();
 }
+
 }  // namespace gqa

@@ -1,0 +1,111 @@
+"""GPU parity of topk_sparse_decode (through the C ABI) against the fp64 oracle:
+index sets bit-exact, attention outputs within tolerance."""
+import math
+
+import numpy as np
+import pytest
+
+from helpers import assert_close, from_dev, to_dev
+from oracle import sparse as osp
+from workloads import (SPARSE_128K, bf16_bits_to_f64, bf16_tensor_to_f64, device_randn_bf16,
+                       f32_to_bf16_bits, sparse_inputs_host)
+
+pytestmark = pytest.mark.gpu
+SCALE = 1 / math.sqrt(192)
+
+
+@pytest.fixture(scope="module")
+def m():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import mqa_kv_cache_amd
+    return mqa_kv_cache_amd
+
+
+def _run(m, d, top_k, heads=None):
+    import torch
+    B, H, _ = d["q"].shape
+    print(f"[case] sparse B={B} H={H} S_max={d['latent'].shape[1]} lens={list(d['seq_lens'])} "
+          f"k={top_k}", flush=True)
+    idx, out = m.topk_sparse_decode(to_dev(d["q"]), to_dev(d["latent"]), to_dev(d["q_index"]),
+                                    to_dev(d["k_index"]), torch.from_numpy(d["seq_lens"]).cuda(),
+                                    top_k, SCALE)
+    torch.cuda.synchronize()
+    ridx, rout = osp.topk_sparse_decode(bf16_bits_to_f64(d["q"]), bf16_bits_to_f64(d["latent"]),
+                                        bf16_bits_to_f64(d["q_index"]),
+                                        bf16_bits_to_f64(d["k_index"]), d["seq_lens"], top_k,
+                                        SCALE, 512, heads=heads)
+    gidx = idx.cpu().numpy()
+    for b in range(B):
+        if not np.array_equal(gidx[b], ridx[b]):
+            diff = np.setxor1d(gidx[b][gidx[b] >= 0], ridx[b][ridx[b] >= 0])
+            raise AssertionError(f"batch {b}: index sets differ at {diff[:10]}")
+    got = from_dev(out)
+    if heads is not None:
+        got, rout = got[:, heads], rout[:, heads]
+    assert_close(got, rout, "sparse out")
+    return gidx
+
+
+def test_sparse_small(m):
+    d = sparse_inputs_host(2, 16, 3000, 576, 128, 41, [3000, 1500])
+    _run(m, d, 256)
+
+
+def test_sparse_short_context_and_full_selection(m):
+    d = sparse_inputs_host(2, 32, 600, 576, 128, 42, [100, 600])
+    idx = _run(m, d, 512)
+    assert list(idx[0][:100]) == list(range(100)) and np.all(idx[0][100:] == -1)
+
+
+def test_sparse_ties_and_relu_zeros(m):
+    """Few distinct scores (rows repeat), most of them ReLU zeros: the lower
+    index must win every tie."""
+    rng = np.random.default_rng(43)
+    d = sparse_inputs_host(2, 16, 4000, 576, 128, 43, [4000, 3999])
+    base = d["k_index"][:, :8].copy()
+    reps = rng.integers(0, 8, size=(2, 4000))
+    d["k_index"] = np.stack([base[b][reps[b]] for b in range(2)])
+    _run(m, d, 700)
+    # all-negative dot products except a few: zeros dominate the selection
+    d2 = sparse_inputs_host(1, 16, 5000, 576, 128, 44, [5000])
+    qi = np.zeros((1, 128), np.float32)
+    qi[0, 0] = 1.0
+    ki = -np.abs(bf16_bits_to_f64(d2["k_index"]).astype(np.float32))
+    ki[0, ::97, 0] = 1.5
+    d2["q_index"] = f32_to_bf16_bits(qi)
+    d2["k_index"] = f32_to_bf16_bits(ki)
+    _run(m, d2, 300)
+
+
+def test_sparse_large_threshold_bin(m):
+    """More than 8192 equal scores in the threshold bin: the multi-pass path."""
+    d = sparse_inputs_host(1, 16, 20000, 576, 128, 45, [20000])
+    d["k_index"][0, :] = d["k_index"][0, 0]
+    d["q_index"][0] = d["k_index"][0, 0]      # every score equals |k_0|^2 > 0
+    _run(m, d, 2048)
+
+
+def test_sparse_full_size_128k(m):
+    import torch
+    cfg = SPARSE_128K
+    B, H, S, k = cfg.B, cfg.H, cfg.S_max, cfg.top_k
+    print(f"[case] sparse full size B={B} H={H} S={S} k={k}", flush=True)
+    q = device_randn_bf16((B, H, cfg.Dqk), cfg.seed * 10 + 1)
+    lat = device_randn_bf16((B, S, cfg.Dqk), cfg.seed * 10 + 2)
+    qi = device_randn_bf16((B, cfg.D_idx), cfg.seed * 10 + 3)
+    ki = device_randn_bf16((B, S, cfg.D_idx), cfg.seed * 10 + 4)
+    lens = torch.from_numpy(cfg.seq_lens()).cuda()
+    idx, out = m.topk_sparse_decode(q, lat, qi, ki, lens, k, cfg.scale)
+    torch.cuda.synchronize()
+    gidx = idx.cpu().numpy()
+    got = from_dev(out)
+    qf, qif = bf16_tensor_to_f64(q), bf16_tensor_to_f64(qi)
+    for b in range(B):
+        kib = bf16_tensor_to_f64(ki[b])
+        ridx = osp.topk_select(osp.indexer_scores(qif[b], kib, S), k)
+        assert np.array_equal(gidx[b], ridx), f"batch {b}: index sets differ"
+        latb = bf16_tensor_to_f64(lat[b])
+        for h in (0, 77, 127):
+            ref = osp.sparse_attention_one(qf[b, h], latb, ridx, cfg.scale, cfg.Dv)
+            assert_close(got[b, h], ref, f"full-size (b={b}, h={h})")
