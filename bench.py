@@ -1,0 +1,371 @@
+"""Benchmark of the GQA/MQA attention hot path on one MI355X.
+
+Headline (the JSON line's `value`): single-token GQA decode over a bf16 KV
+cache at 32K context, in GB/s of algorithmic KV bytes (sum over the batch of
+seq_len x n_kv_head x head_dim x 2 bytes x 2 for K and V) per second.  A step
+is one whole decode (per-piece partial softmax states, then their merge) for
+the whole batch; inputs are resident in HBM before timing starts and two
+independent caches alternate so the 256 MB Infinity Cache cannot serve them.
+
+The same run also measures the other hot-path entry points (decode at 4K,
+causal prefill at 8K on the matrix cores, top-k sparse decode at 128K and
+rope_apply) and times the CPU fp64 oracle on a bounded sample of the
+headline workload.  All data is synthetic and seeded.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GQA decode KV GB/s (% of HBM peak) at 32K ctx; causal prefill TFLOP/s"
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix peak
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default="", help="comma list of sections (decode32k,decode4k,"
+                    "prefill,sparse,rope) for profiling runs")
+    return ap.parse_args()
+
+
+class EventTimer:
+    """Average duration of the work enqueued between start() and stop() on the
+    current stream, over many calls, from HIP events on that stream."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append([e, None])
+
+    def stop(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[-1][1] = e
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) for a, b in self.pairs]
+        return sum(ts) / len(ts)
+
+
+def timed_loop(fn, steps, warmup):
+    """Run warmup calls, then time exactly `steps` calls bracketed by device syncs."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mqa_kv_cache_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(profile_name, src_hash):
+    """HBM bytes per dispatch recorded from rocprofv3 PMC counters in
+    profiles/<profile_name>, or None when absent or taken on other sources."""
+    path = os.path.join(PROFILE_DIR, profile_name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != src_hash:
+        return None
+    try:
+        return float(vals["traffic_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# sections
+# ---------------------------------------------------------------------------
+
+def bench_decode(cfg, steps, warmup, nsets, label):
+    import torch
+
+    import mqa_kv_cache_amd as m
+    from workloads import device_randn_bf16
+    B, Hq, Hkv, D, S = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.S_max
+    lens = torch.from_numpy(cfg.seq_lens()).cuda()
+    sets = [(device_randn_bf16((B, Hq, D), cfg.seed * 100 + 10 * i + 1),
+             device_randn_bf16((B, Hkv, S, D), cfg.seed * 100 + 10 * i + 2),
+             device_randn_bf16((B, Hkv, S, D), cfg.seed * 100 + 10 * i + 3)) for i in range(nsets)]
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(m.gqa_decode_workspace_size(B, Hq, Hkv, D, S), dtype=torch.uint8, device="cuda")
+    kv_bytes = int(lens.sum().item()) * Hkv * D * 2 * 2
+    rope = cfg.rope()
+    timer = EventTimer()
+
+    def step(i, record=False):
+        q, k, v = sets[i % nsets]
+        if record:
+            timer.start()
+        m.gqa_decode_partial(q, k, v, lens, cfg.scale, ws, q_rope=rope)
+        if record:
+            timer.stop()
+        m.gqa_decode_combine(lens, B, Hq, Hkv, D, S, ws, out)
+
+    ms = timed_loop(lambda i: step(i, record=True), steps, warmup)
+    timer.pairs = timer.pairs[warmup:]
+    kern_ms = timer.mean_ms()
+    log(f"[bench] {label}: step {ms * 1e3:.1f} us, partial kernel {kern_ms * 1e3:.1f} us, "
+        f"{kv_bytes / ms / 1e6:.0f} GB/s")
+    return dict(ms=ms, kern_ms=kern_ms, kv_bytes=kv_bytes, lens=lens.cpu().numpy(), sets=sets)
+
+
+def bench_prefill(cfg, steps, warmup):
+    import torch
+
+    import mqa_kv_cache_amd as m
+    from workloads import device_randn_bf16
+    B, T, Hq, Hkv, D = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.D
+    q = device_randn_bf16((B, Hq, T, D), cfg.seed * 100 + 1)
+    k = device_randn_bf16((B, Hkv, T, D), cfg.seed * 100 + 2)
+    v = device_randn_bf16((B, Hkv, T, D), cfg.seed * 100 + 3)
+    out = torch.empty_like(q)
+    ws = torch.empty(m.gqa_prefill_workspace_size(B, Hkv, T, D, cfg.rope()), dtype=torch.uint8,
+                     device="cuda")
+    flops = 2 * D * Hq * T * (T + 1) * B       # QK^T and PV over the causal triangle incl. diagonal
+    timer = EventTimer()
+
+    def step(i):
+        timer.start()
+        m.gqa_prefill_causal(q, k, v, cfg.scale, rope=cfg.rope(), out=out, workspace=ws)
+        timer.stop()
+
+    ms = timed_loop(step, max(steps // 2, 5), max(warmup // 2, 2))
+    timer.pairs = timer.pairs[max(warmup // 2, 2):]
+    ev_ms = timer.mean_ms()
+    tf = flops / ev_ms / 1e9
+    log(f"[bench] prefill T={T}: {ev_ms * 1e3:.1f} us per call, {tf:.1f} TFLOP/s")
+    return dict(ms=ms, ev_ms=ev_ms, flops=flops, tflops=tf)
+
+
+def bench_sparse(cfg, steps, warmup):
+    import torch
+
+    import mqa_kv_cache_amd as m
+    from workloads import device_randn_bf16
+    B, H, S, k = cfg.B, cfg.H, cfg.S_max, cfg.top_k
+    nsets = 2
+    sets = [(device_randn_bf16((B, H, cfg.Dqk), cfg.seed * 100 + 10 * i + 1),
+             device_randn_bf16((B, S, cfg.Dqk), cfg.seed * 100 + 10 * i + 2),
+             device_randn_bf16((B, cfg.D_idx), cfg.seed * 100 + 10 * i + 3),
+             device_randn_bf16((B, S, cfg.D_idx), cfg.seed * 100 + 10 * i + 4)) for i in range(nsets)]
+    lens = torch.from_numpy(cfg.seq_lens()).cuda()
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, H, cfg.Dv), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(m.topk_sparse_decode_workspace_size(B, H, S, k), dtype=torch.uint8, device="cuda")
+    # algorithmic bytes: indexer keys + selected latent rows + q, q_index, outputs
+    alg = (B * S * cfg.D_idx * 2 + B * k * cfg.Dqk * 2 + B * H * cfg.Dqk * 2 + B * cfg.D_idx * 2
+           + B * k * 4 + B * H * cfg.Dv * 2)
+    timer = EventTimer()
+
+    def step(i):
+        q, lat, qi, ki = sets[i % nsets]
+        timer.start()
+        m.topk_sparse_decode(q, lat, qi, ki, lens, k, cfg.scale, topk_idx=idx, out=out, workspace=ws)
+        timer.stop()
+
+    ms = timed_loop(step, steps, warmup)
+    timer.pairs = timer.pairs[warmup:]
+    ev_ms = timer.mean_ms()
+    log(f"[bench] sparse: {ev_ms * 1e3:.1f} us per call, {alg / ev_ms / 1e6:.0f} GB/s algorithmic")
+    return dict(ms=ev_ms, alg_bytes=alg, gbs=alg / ev_ms / 1e6)
+
+
+def bench_rope(cfg, steps, warmup):
+    import torch
+
+    import mqa_kv_cache_amd as m
+    from workloads import device_randn_bf16
+    T, Hq, D = cfg.T, cfg.Hq, cfg.D
+    x = device_randn_bf16((T, Hq, D), 7)
+    y = torch.empty_like(x)
+    pos = torch.arange(T, dtype=torch.int32, device="cuda")
+    byts = 2 * T * Hq * D * 2
+    timer = EventTimer()
+
+    def step(i):
+        timer.start()
+        m.rope_apply(x, pos, cfg.rope(), out=y)
+        timer.stop()
+
+    timed_loop(step, steps, warmup)
+    timer.pairs = timer.pairs[warmup:]
+    ev_ms = timer.mean_ms()
+    log(f"[bench] rope_apply: {ev_ms * 1e3:.1f} us, {byts / ev_ms / 1e6:.0f} GB/s")
+    return dict(ms=ev_ms, gbs=byts / ev_ms / 1e6)
+
+
+def cpu_baseline(cfg, dec, budget_s=12.0):
+    """The fp64 oracle on the host cores, on a bounded sample of the headline
+    workload: whole sequences (every q head) of the headline batch, taken in
+    order until about `budget_s` seconds of oracle time.  Inputs are copied to
+    host float64 beforehand; only the oracle calls are timed."""
+    from oracle import attention as oatt
+    from workloads import bf16_tensor_to_f64
+    q, k, v = dec["sets"][0]
+    lens = dec["lens"]
+    Hq, Hkv, D = cfg.Hq, cfg.Hkv, cfg.D
+    g = Hq // Hkv
+    wall = cpu = 0.0
+    rows = nb = 0
+    for b in range(cfg.B):
+        L = int(lens[b])
+        qf = bf16_tensor_to_f64(q[b])
+        kvs = [(bf16_tensor_to_f64(k[b, kv, :L]), bf16_tensor_to_f64(v[b, kv, :L])) for kv in range(Hkv)]
+        c0, t0 = time.process_time(), time.perf_counter()
+        for kv, (kb, vb) in enumerate(kvs):
+            for hl in range(g):
+                oatt.decode_one(qf[kv * g + hl], kb, vb, L, cfg.scale, cfg.rope())
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        rows += L
+        nb += 1
+        del kvs
+        if wall >= budget_s:
+            break
+    sample_bytes = rows * Hkv * D * 2 * 2
+    return {"value": round(sample_bytes / wall / 1e9, 3), "unit": "GB/s",
+            "cores": max(1, round(cpu / wall)), "kind": "oracle",
+            "sample": f"all {Hq} q heads of the first {nb} of {cfg.B} sequences of the headline "
+                      f"batch ({rows} context rows, {sample_bytes} KV bytes), numpy float64 oracle; "
+                      f"{wall:.1f} s wall, {cpu:.1f} s CPU; os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mqa_kv_cache_amd as m  # noqa: F401  (fails loudly without the HIP library)
+    from workloads import DECODE_4K, DECODE_32K_YARN, PREFILL_8K, SPARSE_128K
+    torch.cuda.set_device(0)
+    only = set(s for s in args.only.split(",") if s)
+    want = (lambda s: not only or s in only)
+    K, W = args.steps, args.warmup
+
+    res = {}
+    if want("decode32k"):
+        res["d32"] = bench_decode(DECODE_32K_YARN, K, W, nsets=2, label="decode 32K")
+    if want("decode4k"):
+        res["d4"] = bench_decode(DECODE_4K, K, W, nsets=4, label="decode 4K")
+    if want("prefill"):
+        res["p"] = bench_prefill(PREFILL_8K, K, W)
+    if want("sparse"):
+        res["s"] = bench_sparse(SPARSE_128K, K, W)
+    if want("rope"):
+        res["r"] = bench_rope(PREFILL_8K, K, W)
+    if only and "d32" not in res:
+        return
+
+    d = res["d32"]
+    cfg = DECODE_32K_YARN
+    value = d["kv_bytes"] / d["ms"] / 1e6
+    achieved = d["kv_bytes"] / d["kern_ms"] / 1e6
+    src = source_hash("decode.hip", "device_common.h")
+    traffic = recorded_traffic("decode_split_kernel_decode32k_yarn.pmc.txt", src)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(d["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"gqa_decode: B={cfg.B} sequences x 1 new token, Hq={cfg.Hq}, "
+                         f"Hkv={cfg.Hkv}, D={cfg.D}, S_max={cfg.S_max}, seq_lens~U[{cfg.ragged_lo},"
+                         f"{cfg.S_max}] (seed {cfg.seed}), YaRN s=4 on q, bf16 KV cache"),
+            "global_batch": cfg.B,
+            "seq_len": cfg.S_max,
+            "parallelism": "single GPU",
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_split_kernel<128,1>",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": d["kv_bytes"],
+            "kernel_ms": round(d["kern_ms"], 5),
+            "source_sha256_16": src,
+        },
+    }
+    if "d4" in res:
+        d4 = res["d4"]
+        line["decode_4k"] = {"GB/s": round(d4["kv_bytes"] / d4["ms"] / 1e6, 1),
+                             "kernel_GB/s": round(d4["kv_bytes"] / d4["kern_ms"] / 1e6, 1),
+                             "pct_of_hbm_peak": round(100 * d4["kv_bytes"] / d4["ms"] / 1e6 / HBM_PEAK_GBS, 2),
+                             "ms_per_step": round(d4["ms"], 5)}
+    if "p" in res:
+        p = res["p"]
+        line["prefill_8k"] = {"TFLOP/s": round(p["tflops"], 1),
+                              "pct_of_mfma_peak": round(100 * p["tflops"] / BF16_PEAK_TFLOPS, 2),
+                              "ms_per_call": round(p["ev_ms"], 4), "flops": p["flops"],
+                              "bound": "mfma", "peak": BF16_PEAK_TFLOPS}
+    if "s" in res:
+        s = res["s"]
+        line["sparse_128k"] = {"GB/s": round(s["gbs"], 1), "ms_per_call": round(s["ms"], 5),
+                               "algorithmic_bytes": s["alg_bytes"],
+                               "pct_of_hbm_peak": round(100 * s["gbs"] / HBM_PEAK_GBS, 2)}
+    if "r" in res:
+        line["rope_apply"] = {"GB/s": round(res["r"]["gbs"], 1), "ms_per_call": round(res["r"]["ms"], 5)}
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(cfg, d)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

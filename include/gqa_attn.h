@@ -118,8 +118,8 @@ gqa_status rope_apply(const void* in, void* out, const int32_t* positions,
  *   workspace  >= gqa_decode_workspace_size(B, Hq, Hkv, D, S_max) bytes, device,
  *              256-byte aligned; its contents on entry do not matter.
  * Supported: D in {64, 128}; Hq % Hkv == 0; g = Hq/Hkv <= 64.
- * Split-K over the context with a log-sum-exp combine; the result does not
- * depend on the split.
+ * The work is split over the context (split-K) with a log-sum-exp merge;
+ * the result does not depend on the split.
  */
 size_t gqa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S_max);
 
@@ -129,18 +129,46 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                       const gqa_rope_params* q_rope, void* out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* As gqa_decode, with the split length (rows per split, a multiple of 64 in
- * [64, 4096]) chosen by the caller instead of by the library's heuristic.
- * The workspace must then hold gqa_decode_workspace_size_split(...) bytes. */
-size_t gqa_decode_workspace_size_split(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
-                                       int32_t S_max, int32_t split_rows);
+/* As gqa_decode with the number of work ranges chosen by the caller:
+ * the rows of all B*Hkv contexts, taken in (batch, kv head, row) order, are
+ * cut into n_parts equal ranges, each streamed by one wavefront (n_parts in
+ * [1, 2^20]; 0 = the library's default).  The workspace must then hold
+ * gqa_decode_workspace_size_parts(...) bytes (it grows with n_parts). */
+size_t gqa_decode_workspace_size_parts(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                       int32_t S_max, int32_t n_parts);
 
-gqa_status gqa_decode_split(const void* q, const void* k_cache, const void* v_cache,
+gqa_status gqa_decode_parts(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                             int32_t D, int32_t S_max, float scale,
                             const gqa_rope_params* q_rope, void* out,
                             void* workspace, size_t workspace_bytes,
-                            int32_t split_rows, void* stream);
+                            int32_t n_parts, void* stream);
+
+/*
+ * Two-phase decode: gqa_decode_parts == gqa_decode_partial then
+ * gqa_decode_combine with the same arguments.  The partial phase leaves in
+ * the workspace one softmax state per piece (a run of rows of one context
+ * inside one work range):
+ *     m = max_j t_j,  l = sum_j 2^(t_j - m),  o[d] = sum_j 2^(t_j - m) V[j][d],
+ *     t_j = scale * log2(e) * (q~ . K[j])        (base-2 logits)
+ * and the combine phase returns, per (batch, q head),
+ *     sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,   M = max_p m_p,
+ * which equals the one-pass softmax exactly in real arithmetic.  The state
+ * layout is internal to the pair; callers merging states of disjoint row
+ * ranges themselves (e.g. a context split across devices) apply the same
+ * formula to their own (m, l, o).
+ */
+gqa_status gqa_decode_partial(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t S_max, float scale,
+                              const gqa_rope_params* q_rope,
+                              void* workspace, size_t workspace_bytes,
+                              int32_t n_parts, void* stream);
+
+gqa_status gqa_decode_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t S_max,
+                              const void* workspace, size_t workspace_bytes,
+                              int32_t n_parts, void* out, void* stream);
 
 /*
  * gqa_prefill_causal -- causal GQA attention over a whole prompt

@@ -27,8 +27,9 @@ OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_DEVICE =
 ROPE_NONE, ROPE_PLAIN, ROPE_PI, ROPE_NTK, ROPE_YARN = 0, 1, 2, 3, 4
 
 EXPORTED = [
-    "rope_apply", "gqa_decode", "gqa_decode_split", "gqa_decode_workspace_size",
-    "gqa_decode_workspace_size_split", "gqa_prefill_causal", "gqa_prefill_workspace_size",
+    "rope_apply", "gqa_decode", "gqa_decode_parts", "gqa_decode_workspace_size",
+    "gqa_decode_workspace_size_parts", "gqa_decode_partial", "gqa_decode_combine",
+    "gqa_prefill_causal", "gqa_prefill_workspace_size",
     "topk_sparse_decode", "topk_sparse_decode_workspace_size", "kv_bytes_per_token",
     "mla_kv_bytes_per_token", "gqa_status_string",
 ]
@@ -67,14 +68,21 @@ _lib.rope_apply.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_int64, _c_int32,
                             _c_int64, _c_int64, _rope_p, _c_void_p]
 _lib.gqa_decode_workspace_size.restype = _c_size_t
 _lib.gqa_decode_workspace_size.argtypes = [_c_int32] * 5
-_lib.gqa_decode_workspace_size_split.restype = _c_size_t
-_lib.gqa_decode_workspace_size_split.argtypes = [_c_int32] * 6
+_lib.gqa_decode_workspace_size_parts.restype = _c_size_t
+_lib.gqa_decode_workspace_size_parts.argtypes = [_c_int32] * 6
 _lib.gqa_decode.restype = _c_int32
 _lib.gqa_decode.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int32, _c_int32,
                             _c_int32, _c_int32, _c_int32, ctypes.c_float, _rope_p, _c_void_p,
                             _c_void_p, _c_size_t, _c_void_p]
-_lib.gqa_decode_split.restype = _c_int32
-_lib.gqa_decode_split.argtypes = _lib.gqa_decode.argtypes[:-1] + [_c_int32, _c_void_p]
+_lib.gqa_decode_parts.restype = _c_int32
+_lib.gqa_decode_parts.argtypes = _lib.gqa_decode.argtypes[:-1] + [_c_int32, _c_void_p]
+_lib.gqa_decode_partial.restype = _c_int32
+_lib.gqa_decode_partial.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int32, _c_int32,
+                                    _c_int32, _c_int32, _c_int32, ctypes.c_float, _rope_p,
+                                    _c_void_p, _c_size_t, _c_int32, _c_void_p]
+_lib.gqa_decode_combine.restype = _c_int32
+_lib.gqa_decode_combine.argtypes = [_c_void_p, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                    _c_void_p, _c_size_t, _c_int32, _c_void_p, _c_void_p]
 _lib.gqa_prefill_workspace_size.restype = _c_size_t
 _lib.gqa_prefill_workspace_size.argtypes = [_c_int32] * 4 + [_rope_p]
 _lib.gqa_prefill_causal.restype = _c_int32
@@ -171,14 +179,14 @@ def rope_apply(x: torch.Tensor, positions: torch.Tensor, rope, out: torch.Tensor
     return out
 
 
-def gqa_decode_workspace_size(B, Hq, Hkv, D, S_max, split_rows=None) -> int:
-    if split_rows is None:
+def gqa_decode_workspace_size(B, Hq, Hkv, D, S_max, n_parts=None) -> int:
+    if n_parts is None:
         return int(_lib.gqa_decode_workspace_size(B, Hq, Hkv, D, S_max))
-    return int(_lib.gqa_decode_workspace_size_split(B, Hq, Hkv, D, S_max, split_rows))
+    return int(_lib.gqa_decode_workspace_size_parts(B, Hq, Hkv, D, S_max, n_parts))
 
 
 def gqa_decode(q, k_cache, v_cache, seq_lens, scale: float, q_rope=None, out=None,
-               workspace=None, split_rows: int | None = None, stream=None) -> torch.Tensor:
+               workspace=None, n_parts: int | None = None, stream=None) -> torch.Tensor:
     """q [B,Hq,D], k_cache/v_cache [B,Hkv,S_max,D] (bf16, keys post-RoPE),
     seq_lens int32 [B] on the device.  Returns out [B,Hq,D] bf16."""
     B, Hq, D = q.shape
@@ -193,18 +201,51 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, scale: float, q_rope=None, out=Non
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
     _shape(out, (B, Hq, D), "out")
     _dev(out, "out")
-    need = gqa_decode_workspace_size(B, Hq, Hkv, D, S_max, split_rows)
+    need = gqa_decode_workspace_size(B, Hq, Hkv, D, S_max, n_parts)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace", dtype=torch.uint8)
     args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv,
             D, S_max, float(scale), rope_params(q_rope), out.data_ptr(), workspace.data_ptr(),
             workspace.numel())
-    if split_rows is None:
+    if n_parts is None:
         st = _lib.gqa_decode(*args, _stream(stream))
     else:
-        st = _lib.gqa_decode_split(*args, int(split_rows), _stream(stream))
+        st = _lib.gqa_decode_parts(*args, int(n_parts), _stream(stream))
     _check(st, "gqa_decode")
+    return out
+
+
+def gqa_decode_partial(q, k_cache, v_cache, seq_lens, scale: float, workspace, q_rope=None,
+                       n_parts: int = 0, stream=None) -> None:
+    """Phase 1 of gqa_decode: per-split softmax states into `workspace`."""
+    B, Hq, D = q.shape
+    _, Hkv, S_max, _ = k_cache.shape
+    _shape(k_cache, (B, Hkv, S_max, D), "k_cache")
+    _shape(v_cache, (B, Hkv, S_max, D), "v_cache")
+    _shape(seq_lens, (B,), "seq_lens")
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, nm)
+    _dev(seq_lens, "seq_lens", dtype=torch.int32)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    st = _lib.gqa_decode_partial(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                 seq_lens.data_ptr(), B, Hq, Hkv, D, S_max, float(scale),
+                                 rope_params(q_rope), workspace.data_ptr(), workspace.numel(),
+                                 int(n_parts), _stream(stream))
+    _check(st, "gqa_decode_partial")
+
+
+def gqa_decode_combine(seq_lens, B, Hq, Hkv, D, S_max, workspace, out, n_parts: int = 0,
+                       stream=None) -> torch.Tensor:
+    """Phase 2 of gqa_decode: merge the per-split states into out [B,Hq,D] bf16."""
+    _shape(seq_lens, (B,), "seq_lens")
+    _dev(seq_lens, "seq_lens", dtype=torch.int32)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    _shape(out, (B, Hq, D), "out")
+    _dev(out, "out")
+    st = _lib.gqa_decode_combine(seq_lens.data_ptr(), B, Hq, Hkv, D, S_max, workspace.data_ptr(),
+                                 workspace.numel(), int(n_parts), out.data_ptr(), _stream(stream))
+    _check(st, "gqa_decode_combine")
     return out
 
 

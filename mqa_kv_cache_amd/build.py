@@ -15,16 +15,18 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into mqa_kv_cache_amd/libgqa_attn.so; return its path."""
+def build(verbose: bool = False, out_path: str = LIB, defines=()) -> str:
+    """Compile every HIP source into mqa_kv_cache_amd/libgqa_attn.so (or
+    out_path, with extra -D defines for tuning builds); return its path."""
     objs = []
-    build_dir = os.path.join(HERE, "_build")
+    build_dir = os.path.join(os.path.dirname(out_path), "_build")
     os.makedirs(build_dir, exist_ok=True)
     procs = []
     for src in SOURCES:
         obj = os.path.join(build_dir, src.replace(".", "_") + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [HIPCC] + [f for f in FLAGS if f != "-shared"] + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ([HIPCC] + [f for f in FLAGS if f != "-shared"] + [f"-D{d}" for d in defines] + lang
+               + ["-c", os.path.join(CSRC, src), "-o", obj])
         procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         objs.append(obj)
     failed = False
@@ -40,11 +42,11 @@ def build(verbose: bool = False) -> str:
             sys.stderr.write(f"[build] {src}:\n{text}\n")
     if failed:
         raise RuntimeError("hipcc failed")
-    tmp = LIB + ".tmp"
+    tmp = out_path + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out_path)
+    return out_path
 
 
 if __name__ == "__main__":

@@ -118,48 +118,81 @@ static gqa_status check_decode_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t
     return GQA_OK;
 }
 
-size_t gqa_decode_workspace_size_split(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S_max,
-                                       int32_t split_rows) {
+static int32_t pick_parts(int32_t n_parts) { return n_parts == 0 ? kDecodeDefaultParts : n_parts; }
+
+static bool parts_ok(int32_t n_parts) { return n_parts >= 1 && n_parts <= (1 << 20); }
+
+size_t gqa_decode_workspace_size_parts(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S_max,
+                                       int32_t n_parts) {
     if (check_decode_shape(B, Hq, Hkv, D, S_max) != GQA_OK) return 0;
-    if (split_rows < 64 || split_rows > 4096 || (split_rows % 64)) return 0;
-    return decode_layout(B, Hq, D, S_max, split_rows).total;
+    n_parts = pick_parts(n_parts);
+    if (!parts_ok(n_parts)) return 0;
+    return decode_layout(B, Hq, Hkv, D, n_parts).total;
 }
 
 size_t gqa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S_max) {
-    if (check_decode_shape(B, Hq, Hkv, D, S_max) != GQA_OK) return 0;
-    return decode_layout(B, Hq, D, S_max, decode_default_split(B, Hkv, S_max)).total;
+    return gqa_decode_workspace_size_parts(B, Hq, Hkv, D, S_max, 0);
 }
 
-gqa_status gqa_decode_split(const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
-                            int32_t S_max, float scale, const gqa_rope_params* q_rope, void* out,
-                            void* workspace, size_t workspace_bytes, int32_t split_rows,
-                            void* stream) {
+gqa_status gqa_decode_partial(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                              int32_t S_max, float scale, const gqa_rope_params* q_rope,
+                              void* workspace, size_t workspace_bytes, int32_t n_parts,
+                              void* stream) {
     gqa_status st = check_decode_shape(B, Hq, Hkv, D, S_max);
     if (st != GQA_OK) return st;
-    if (split_rows < 64 || split_rows > 4096 || (split_rows % 64)) return GQA_ERR_INVALID_ARGUMENT;
+    n_parts = pick_parts(n_parts);
+    if (!parts_ok(n_parts)) return GQA_ERR_INVALID_ARGUMENT;
     if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
-    if (!q || !k_cache || !v_cache || !seq_lens || !out || !workspace) return GQA_ERR_INVALID_ARGUMENT;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+    if (!q || !k_cache || !v_cache || !seq_lens || !workspace) return GQA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return GQA_ERR_INVALID_ARGUMENT;
     RopeDev rd;
     st = rope_prepare(q_rope, D, &rd);
     if (st != GQA_OK) return st;
-    const DecodeLayout lay = decode_layout(B, Hq, D, S_max, split_rows);
+    const DecodeLayout lay = decode_layout(B, Hq, Hkv, D, n_parts);
     if (workspace_bytes < lay.total) return GQA_ERR_WORKSPACE_TOO_SMALL;
-    return from_hip(launch_gqa_decode(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale,
-                                      rd, out, workspace, lay, (hipStream_t)stream));
+    return from_hip(launch_gqa_decode_partial(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max,
+                                              scale, rd, workspace, lay, (hipStream_t)stream));
+}
+
+gqa_status gqa_decode_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                              int32_t S_max, const void* workspace, size_t workspace_bytes,
+                              int32_t n_parts, void* out, void* stream) {
+    gqa_status st = check_decode_shape(B, Hq, Hkv, D, S_max);
+    if (st != GQA_OK) return st;
+    n_parts = pick_parts(n_parts);
+    if (!parts_ok(n_parts)) return GQA_ERR_INVALID_ARGUMENT;
+    if (!seq_lens || !workspace || !out) return GQA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return GQA_ERR_INVALID_ARGUMENT;
+    const DecodeLayout lay = decode_layout(B, Hq, Hkv, D, n_parts);
+    if (workspace_bytes < lay.total) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    return from_hip(launch_gqa_decode_combine(seq_lens, B, Hq, Hkv, D, S_max, workspace, lay, out,
+                                              (hipStream_t)stream));
+}
+
+gqa_status gqa_decode_parts(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                            int32_t S_max, float scale, const gqa_rope_params* q_rope, void* out,
+                            void* workspace, size_t workspace_bytes, int32_t n_parts,
+                            void* stream) {
+    if (!out) return GQA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(out)) return GQA_ERR_INVALID_ARGUMENT;
+    gqa_status st = gqa_decode_partial(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale,
+                                       q_rope, workspace, workspace_bytes, n_parts, stream);
+    if (st != GQA_OK) return st;
+    return gqa_decode_combine(seq_lens, B, Hq, Hkv, D, S_max, workspace, workspace_bytes, n_parts,
+                              out, stream);
 }
 
 gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                       int32_t S_max, float scale, const gqa_rope_params* q_rope, void* out,
                       void* workspace, size_t workspace_bytes, void* stream) {
-    gqa_status st = check_decode_shape(B, Hq, Hkv, D, S_max);
-    if (st != GQA_OK) return st;
-    return gqa_decode_split(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale, q_rope, out,
-                            workspace, workspace_bytes, decode_default_split(B, Hkv, S_max), stream);
+    return gqa_decode_parts(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, scale, q_rope, out,
+                            workspace, workspace_bytes, 0, stream);
 }
 
 static gqa_status check_prefill_shape(int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t D) {

@@ -9,50 +9,148 @@
 // the group's g <= 16 rotated queries as the B operand of a 16x16x32 bf16
 // MFMA, so every K/V byte loaded from HBM feeds all g heads at once.
 //
-// Per wave, one split of the context (split_rows rows of one (batch, kv
-// head)), in tiles of 32 rows:
-//   S^T[32 rows][16 heads] = K_tile . Q^T          (K as A operand, 8 MFMAs x2 for q hi/lo)
-//   online softmax per head in fp32 (base-2; scale*log2(e) is folded into q)
-//   O^T[128 d][16 heads] += V_tile^T . P^T          (8 MFMAs)
+// Work split: the rows of every (batch, kv head) context are concatenated
+// into one global row space (batch-major, kv head, row) of
+// total = Hkv * sum_b seq_lens[b] rows, cut into n_parts equal ranges of
+// R = ceil(total / n_parts) rows.  Wave w streams range w, which may span
+// several contexts; it emits one partial softmax state per (context, range)
+// piece.  Every wave therefore moves the same number of bytes whatever the
+// length mix, and a wave starts up (q load, RoPE) once per piece rather
+// than once per short split.  Piece p of context i (starting at global row
+// x) is stored at slot floor(x / R) + i, so slots are unique and the states
+// of one context are contiguous.  Per piece, in tiles of 32 rows:
+//   S^T[32 rows][16 heads] = K_tile . Q^T     (K as A operand; q as hi+lo bf16, 2x8 MFMAs)
+//   online softmax per head in fp32 (base 2; scale*log2(e) is folded into q)
+//   O^T[D][16 heads]      += V_tile^T . P^T   (8 MFMAs for D = 128)
 // The S^T accumulator layout is exactly the P^T operand layout the second
 // MFMA needs, so probabilities never leave their lane.  V^T operands come
-// from 16-byte row loads transposed 8x8 in registers.  Every K and V load is
-// a 16-byte buffer load; a group of 16 lanes covers 64 contiguous bytes of a
-// K row or a whole 256-byte V row.  Loads past seq_len return zero through
-// the buffer descriptor's bound, so ragged tails need no branches.
+// from 16-byte row loads transposed 8x8 in registers.  The next tile's loads
+// are issued before the current tile's math (two register sets), so each
+// wave keeps a whole tile (16 KB) in flight.  All K/V loads are 16-byte
+// buffer loads bounded at the split's end: rows past it read as zero with
+// no memory traffic, so ragged tails and the prefetch past the end cost
+// nothing.
 //
-// The combine kernel merges the per-split (m, l, o) with the usual
-// log-sum-exp rescaling; the result equals the softmax over the whole row.
+// combine_partials_kernel merges the per-split (m, l, o) with log-sum-exp
+// rescaling; the result equals the softmax over the whole row.
 #include "device_common.h"
-#include "combine.h"
 
 namespace gqa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaves = 4;   // waves per workgroup (each an independent work item)
+
+// Compile-time tuning: minimum resident waves per SIMD requested from the
+// register allocator, and whether the next tile is prefetched into a second
+// register set.
+#ifndef GQA_DECODE_MIN_WAVES
+#define GQA_DECODE_MIN_WAVES 1
+#endif
+#ifndef GQA_DECODE_PREFETCH
+#define GQA_DECODE_PREFETCH 1
+#endif
+
+template <int D>
+struct DecodeTile {
+    static constexpr int KU = D / 32;  // MFMA k-steps over the head dim
+    u32x4 k[2][KU];
+    u32x4 v[8];
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(DecodeTile<D>& t, __amdgpu_buffer_rsrc_t kr,
+                                          __amdgpu_buffer_rsrc_t vr, int t0, int G, int n) {
+    constexpr int VN = D / 8;   // lanes of a 16-lane group that carry V columns
+#pragma unroll
+    for (int th = 0; th < 2; ++th)
+#pragma unroll
+        for (int u = 0; u < DecodeTile<D>::KU; ++u)
+            t.k[th][u] = buf_load16(kr, (uint32_t)(((t0 + 16 * th + n) * D + 32 * u + 8 * G) * 2));
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const uint32_t off = (n < VN) ? (uint32_t)(((t0 + slot_row(G, r)) * D + 8 * n) * 2)
+                                      : 0x80000000u;  // out of range -> zeros
+        t.v[r] = buf_load16(vr, off);
+    }
+}
 
 template <int D, int NB>
-__global__ __launch_bounds__(256) void decode_split_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ seq_lens, int Hq, int Hkv,
-    int S_max, float qscale, RopeDev rope, float* __restrict__ part_o,
-    float* __restrict__ part_ml, int split_rows, int n_split_max) {
-    constexpr int KU = D / 32;  // MFMA k-steps over the head dim
-    constexpr int VN = D / 8;   // lanes of a 16-lane group that carry V columns
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int G = lane >> 4, n = lane & 15;
-    const int b = blockIdx.z, kv = blockIdx.y;
-    const int split = blockIdx.x * 4 + wave;
-    const int g = Hq / Hkv;
+__device__ __forceinline__ void tile_math(const DecodeTile<D>& t, int t0, int r1, int G,
+                                          const u32x4 (&qhi)[NB][D / 32],
+                                          const u32x4 (&qlo)[NB][D / 32], f32x4 (&o)[NB][8],
+                                          float (&m_run)[NB], float (&l_run)[NB]) {
+    constexpr int KU = D / 32;
+    const bool tail = (t0 + 32 > r1);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        f32x4 sc[2];
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+            sc[th] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {
+                sc[th] = mfma16(t.k[th][u], qhi[nb][u], sc[th]);
+                sc[th] = mfma16(t.k[th][u], qlo[nb][u], sc[th]);
+            }
+        }
+        if (tail) {
+#pragma unroll
+            for (int th = 0; th < 2; ++th)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (t0 + 16 * th + 4 * G + i >= r1) sc[th][i] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+        mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[nb], mx);   // finite: row t0 < r1 is visible
+        const float alpha = fast_exp2(m_run[nb] - m_new);
+        float p[2][4];
+        float ls = 0.f;
+#pragma unroll
+        for (int th = 0; th < 2; ++th)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[th][i] = fast_exp2(sc[th][i] - m_new);
+                ls += p[th][i];
+            }
+        ls += wave_shfl_xor(ls, 16);
+        ls += wave_shfl_xor(ls, 32);
+        l_run[nb] = l_run[nb] * alpha + ls;
+        m_run[nb] = m_new;
+        u32x4 pb;
+        pb[0] = pack_bf16x2(p[0][0], p[0][1]);
+        pb[1] = pack_bf16x2(p[0][2], p[0][3]);
+        pb[2] = pack_bf16x2(p[1][0], p[1][1]);
+        pb[3] = pack_bf16x2(p[1][2], p[1][3]);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            o[nb][c] *= alpha;
+            o[nb][c] = mfma16(column_of(t.v, c), pb, o[nb][c]);
+        }
+    }
+}
 
-    const int L = min(max(seq_lens[b], 1), S_max);
-    const int r0 = split * split_rows;
-    if (r0 >= L) return;
-    const int r1 = min(r0 + split_rows, L);
+// The row space shared by the decode kernel and the combine: per batch b the
+// contexts of its Hkv heads, each seq_lens[b] rows (clamped to [1, S_max]).
+struct RowSpace {
+    int64_t total;
+    int64_t R;
+};
+__device__ __forceinline__ RowSpace row_space(const int32_t* seq_lens, int B, int Hkv, int S_max,
+                                              int n_parts) {
+    int64_t total = 0;
+    for (int b = 0; b < B; ++b) total += (int64_t)Hkv * min(max(seq_lens[b], 1), S_max);
+    return RowSpace{total, (total + n_parts - 1) / n_parts};
+}
 
-    // ---- queries of the group: RoPE at position L-1, times scale*log2(e), as hi+lo bf16
-    u32x4 qhi[NB][KU], qlo[NB][KU];
+template <int D, int NB>
+__device__ __forceinline__ void load_q(const uint16_t* q, int b, int kv, int Hq, int g, int L,
+                                       float qscale, const RopeDev& rope, int G, int n,
+                                       u32x4 (&qhi)[NB][D / 32], u32x4 (&qlo)[NB][D / 32]) {
+    constexpr int KU = D / 32;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int hl = nb * 16 + n;
@@ -90,176 +188,262 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
             }
         }
     }
+}
 
-    const size_t slice = ((size_t)b * Hkv + kv) * (size_t)S_max * D;
-    const uint32_t nbytes = (uint32_t)L * D * 2u;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k_cache + slice, nbytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_cache + slice, nbytes);
+template <int D, int NB>
+__global__ __launch_bounds__(64 * kWaves, GQA_DECODE_MIN_WAVES) void decode_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ seq_lens, int B, int Hq,
+    int Hkv, int S_max, float qscale, RopeDev rope, float* __restrict__ part_o,
+    float* __restrict__ part_ml, int n_parts) {
+    constexpr int KU = D / 32;
+    const int lane = threadIdx.x & 63;
+    const int G = lane >> 4, n = lane & 15;
+    const int g = Hq / Hkv;
+    // wave-uniform by construction; readfirstlane lets the compiler keep every
+    // derived address and buffer descriptor in scalar registers
+    const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
+    if (w >= n_parts) return;
+    const RowSpace rs = row_space(seq_lens, B, Hkv, S_max, n_parts);
+    int64_t gs = (int64_t)w * rs.R;
+    const int64_t ge = min(gs + rs.R, rs.total);
+    if (gs >= ge) return;
 
-    f32x4 o[NB][8];
-    float m_run[NB], l_run[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) o[nb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_run[nb] = -INFINITY;
-        l_run[nb] = 0.f;
+    // locate the context holding global row gs
+    int b = 0, L = 0;
+    int64_t base = 0;   // global row of (b, kv 0, row 0)
+    for (; b < B; ++b) {
+        L = min(max(seq_lens[b], 1), S_max);
+        if (gs < base + (int64_t)Hkv * L) break;
+        base += (int64_t)Hkv * L;
     }
+    int kv = (int)((gs - base) / L);
 
-    for (int t0 = r0; t0 < r1; t0 += 32) {
-        u32x4 kreg[2][KU], vreg[8];
-#pragma unroll
-        for (int th = 0; th < 2; ++th)
-#pragma unroll
-            for (int u = 0; u < KU; ++u)
-                kreg[th][u] = buf_load16(kr, (uint32_t)(((t0 + 16 * th + n) * D + 32 * u + 8 * G) * 2));
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const uint32_t off = (n < VN) ? (uint32_t)(((t0 + slot_row(G, r)) * D + 8 * n) * 2)
-                                          : 0x80000000u;  // out of range -> zeros
-            vreg[r] = buf_load16(vr, off);
-        }
+    while (gs < ge) {
+        const int64_t ctx0 = base + (int64_t)kv * L;        // global row of this context's row 0
+        const int r0 = (int)(gs - ctx0);
+        const int r1 = (int)min((int64_t)L, ge - ctx0);
 
-        u32x4 vt[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) vt[t] = column_of(vreg, t);
+        // buffers end at this piece's last row: the prefetch past it reads zeros for free
+        const size_t slice = ((size_t)b * Hkv + kv) * (size_t)S_max * D;
+        const uint32_t nbytes = (uint32_t)r1 * D * 2u;
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(k_cache + slice, nbytes);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_cache + slice, nbytes);
 
-        const bool tail = (t0 + 32 > r1);
+        // the first tiles are requested before q is prepared, hiding its latency
+#if GQA_DECODE_PREFETCH >= 1
+        DecodeTile<D> ta, tb;
+        load_tile<D>(ta, kr, vr, r0, G, n);
+#endif
+#if GQA_DECODE_PREFETCH >= 2
+        DecodeTile<D> tc;
+        load_tile<D>(tb, kr, vr, r0 + 32, G, n);
+#endif
+
+        u32x4 qhi[NB][KU], qlo[NB][KU];
+        load_q<D, NB>(q, b, kv, Hq, g, L, qscale, rope, G, n, qhi, qlo);
+
+        f32x4 o[NB][8];
+        float m_run[NB], l_run[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            f32x4 sc[2];
 #pragma unroll
-            for (int th = 0; th < 2; ++th) {
-                sc[th] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < 8; ++c) o[nb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m_run[nb] = -INFINITY;
+            l_run[nb] = 0.f;
+        }
+
+#if GQA_DECODE_PREFETCH == 0
+        for (int t0 = r0; t0 < r1; t0 += 32) {
+            DecodeTile<D> ta;
+            load_tile<D>(ta, kr, vr, t0, G, n);
+            tile_math<D, NB>(ta, t0, r1, G, qhi, qlo, o, m_run, l_run);
+        }
+#elif GQA_DECODE_PREFETCH == 1
+        for (int t0 = r0;;) {
+            load_tile<D>(tb, kr, vr, t0 + 32, G, n);
+            tile_math<D, NB>(ta, t0, r1, G, qhi, qlo, o, m_run, l_run);
+            t0 += 32;
+            if (t0 >= r1) break;
+            load_tile<D>(ta, kr, vr, t0 + 32, G, n);
+            tile_math<D, NB>(tb, t0, r1, G, qhi, qlo, o, m_run, l_run);
+            t0 += 32;
+            if (t0 >= r1) break;
+        }
+#else
+        // ring of three tiles: two in flight while one is consumed
+        for (int t0 = r0;;) {
+            load_tile<D>(tc, kr, vr, t0 + 64, G, n);
+            tile_math<D, NB>(ta, t0, r1, G, qhi, qlo, o, m_run, l_run);
+            t0 += 32;
+            if (t0 >= r1) break;
+            load_tile<D>(ta, kr, vr, t0 + 64, G, n);
+            tile_math<D, NB>(tb, t0, r1, G, qhi, qlo, o, m_run, l_run);
+            t0 += 32;
+            if (t0 >= r1) break;
+            load_tile<D>(tb, kr, vr, t0 + 64, G, n);
+            tile_math<D, NB>(tc, t0, r1, G, qhi, qlo, o, m_run, l_run);
+            t0 += 32;
+            if (t0 >= r1) break;
+        }
+#endif
+
+        // ---- partial (m, l, o) of this piece
+        const int64_t slot = gs / rs.R + ((int64_t)b * Hkv + kv);
 #pragma unroll
-                for (int u = 0; u < KU; ++u) {
-                    sc[th] = mfma16(kreg[th][u], qhi[nb][u], sc[th]);
-                    sc[th] = mfma16(kreg[th][u], qlo[nb][u], sc[th]);
+        for (int nb = 0; nb < NB; ++nb) {
+            const int hl = nb * 16 + n;
+            if (hl >= g) continue;
+            const size_t idx = (size_t)slot * g + hl;
+            float* po = part_o + idx * D;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 8 * (4 * G + i);  // this lane holds d = d0 + c, c = 0..7
+                if (d0 < D) {
+                    *reinterpret_cast<f32x4*>(po + d0) =
+                        f32x4{o[nb][0][i], o[nb][1][i], o[nb][2][i], o[nb][3][i]};
+                    *reinterpret_cast<f32x4*>(po + d0 + 4) =
+                        f32x4{o[nb][4][i], o[nb][5][i], o[nb][6][i], o[nb][7][i]};
                 }
             }
-            if (tail) {
-#pragma unroll
-                for (int th = 0; th < 2; ++th)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (t0 + 16 * th + 4 * G + i >= r1) sc[th][i] = -INFINITY;
+            if (G == 0) {
+                part_ml[idx * 2] = m_run[nb];
+                part_ml[idx * 2 + 1] = l_run[nb];
             }
-            float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                             fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-            mx = fmaxf(mx, wave_shfl_xor(mx, 16));
-            mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run[nb], mx);
-            const float alpha = fast_exp2(m_run[nb] - m_new);
-            float p[2][4];
-            float ls = 0.f;
-#pragma unroll
-            for (int th = 0; th < 2; ++th)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[th][i] = fast_exp2(sc[th][i] - m_new);
-                    ls += p[th][i];
-                }
-            ls += wave_shfl_xor(ls, 16);
-            ls += wave_shfl_xor(ls, 32);
-            l_run[nb] = l_run[nb] * alpha + ls;
-            m_run[nb] = m_new;
-            u32x4 pb;
-            pb[0] = pack_bf16x2(p[0][0], p[0][1]);
-            pb[1] = pack_bf16x2(p[0][2], p[0][3]);
-            pb[2] = pack_bf16x2(p[1][0], p[1][1]);
-            pb[3] = pack_bf16x2(p[1][2], p[1][3]);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                o[nb][t] *= alpha;
-                o[nb][t] = mfma16(vt[t], pb, o[nb][t]);
-            }
+        }
+
+        // ---- next context
+        gs = ctx0 + r1;
+        if (++kv == Hkv) {
+            kv = 0;
+            base += (int64_t)Hkv * L;
+            if (++b >= B) break;
+            L = min(max(seq_lens[b], 1), S_max);
         }
     }
+}
 
-    // ---- partial (m, l, o) of this split
+// One wave per (batch, q head): merges the states of the pieces of its
+// context, slots floor(x/R) + i for the global rows x of context i.  Lane j
+// reads the (m, l) of piece j, so the maximum and the weights take one
+// round trip; the o rows are then read with independent loads.
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ seq_lens, int B, int Hq, int Hkv, int S_max, int n_parts,
+    uint16_t* __restrict__ out) {
+    constexpr int PER = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int idx = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    if (idx >= B * Hq) return;
+    const int b = idx / Hq, h = idx - b * Hq;
+    const int g = Hq / Hkv, kv = h / g, hl = h - kv * g;
+    const RowSpace rs = row_space(seq_lens, B, Hkv, S_max, n_parts);
+    int64_t base = 0;
+    for (int bb = 0; bb < b; ++bb) base += (int64_t)Hkv * min(max(seq_lens[bb], 1), S_max);
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int64_t x0 = base + (int64_t)kv * L;
+    const int64_t ctx = (int64_t)b * Hkv + kv;
+    const int64_t s0 = x0 / rs.R + ctx;
+    const int np = (int)((x0 + L - 1) / rs.R + ctx - s0 + 1);
+    float acc[PER];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int hl = nb * 16 + n;
-        if (hl >= g) continue;
-        const size_t idx = ((size_t)b * Hq + (size_t)kv * g + hl) * n_split_max + split;
-        float* po = part_o + idx * D;
+    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+    float den = 0.f, M_run = -INFINITY;
+    for (int c0 = 0; c0 < np; c0 += 64) {          // one chunk unless > 64 pieces
+        const int cn = min(64, np - c0);
+        float m = -INFINITY, l = 0.f;
+        if (lane < cn) {
+            const size_t i2 = (size_t)(s0 + c0 + lane) * g + hl;
+            m = part_ml[i2 * 2];
+            l = part_ml[i2 * 2 + 1];
+        }
+        float M = m;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d0 = 8 * (4 * G + i);  // this lane holds d = d0 + t, t = 0..7
-            if (d0 < D) {
-                *reinterpret_cast<f32x4*>(po + d0) =
-                    f32x4{o[nb][0][i], o[nb][1][i], o[nb][2][i], o[nb][3][i]};
-                *reinterpret_cast<f32x4*>(po + d0 + 4) =
-                    f32x4{o[nb][4][i], o[nb][5][i], o[nb][6][i], o[nb][7][i]};
-            }
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, wave_shfl_xor(M, o));
+        const float M_new = fmaxf(M_run, M);       // finite: every piece has a row
+        const float rescale = fast_exp2(M_run - M_new);
+        den *= rescale;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] *= rescale;
+        const float wl = lane < cn ? fast_exp2(m - M_new) : 0.f;
+        float dsum = wl * l;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) dsum += wave_shfl_xor(dsum, o);
+        den += dsum;
+        for (int j = 0; j < cn; ++j) {
+            const float wgt = __shfl(wl, j, 64);
+            const float* po = part_o + ((size_t)(s0 + c0 + j) * g + hl) * D + lane * PER;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] += wgt * po[e];
         }
-        if (G == 0) {
-            part_ml[idx * 2] = m_run[nb];
-            part_ml[idx * 2 + 1] = l_run[nb];
-        }
+        M_run = M_new;
+    }
+    const float inv = 1.0f / den;
+    uint16_t* o = out + (size_t)idx * D + lane * PER;
+    if constexpr (PER == 2) {
+        *reinterpret_cast<uint32_t*>(o) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+        o[0] = (uint16_t)f32_to_bf16_bits(acc[0] * inv);
     }
 }
 
 template <int D, int NB>
-void launch_split(dim3 grid, hipStream_t s, const void* q, const void* k, const void* v,
-                  const int32_t* sl, int Hq, int Hkv, int S_max, float qscale, const RopeDev& rope,
-                  float* po, float* pml, int split_rows, int nsm) {
-    hipLaunchKernelGGL((decode_split_kernel<D, NB>), grid, dim3(256), 0, s,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sl, Hq, Hkv,
-                       S_max, qscale, rope, po, pml, split_rows, nsm);
+void launch_split(hipStream_t s, const void* q, const void* k, const void* v, const int32_t* sl,
+                  int B, int Hq, int Hkv, int S_max, float qscale, const RopeDev& rope, float* po,
+                  float* pml, int n_parts) {
+    hipLaunchKernelGGL((decode_split_kernel<D, NB>), dim3((n_parts + kWaves - 1) / kWaves),
+                       dim3(64 * kWaves), 0, s, (const uint16_t*)q, (const uint16_t*)k,
+                       (const uint16_t*)v, sl, B, Hq, Hkv, S_max, qscale, rope, po, pml, n_parts);
 }
 
 }  // namespace
 
-DecodeLayout decode_layout(int32_t B, int32_t Hq, int32_t D, int32_t S_max, int32_t split_rows) {
+DecodeLayout decode_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t n_parts) {
     DecodeLayout l;
-    l.split_rows = split_rows;
-    l.n_split_max = (S_max + split_rows - 1) / split_rows;
-    const size_t units = (size_t)B * Hq * l.n_split_max;
+    l.n_parts = n_parts;
+    l.slots = (int64_t)n_parts + (int64_t)B * Hkv;
+    const size_t units = (size_t)l.slots * (Hq / Hkv);
     l.o_bytes = (units * D * sizeof(float) + 255) & ~(size_t)255;
     l.ml_bytes = (units * 2 * sizeof(float) + 255) & ~(size_t)255;
     l.total = l.o_bytes + l.ml_bytes;
     return l;
 }
 
-int32_t decode_default_split(int32_t B, int32_t Hkv, int32_t S_max) {
-    // Aim for about 4096 waves over the whole cache (16 per CU on 256 CUs).
-    const int64_t rows = (int64_t)B * Hkv * S_max;
-    int64_t p = rows / 4096;
-    int32_t split = 128;
-    while (split < p && split < 1024) split *= 2;
-    return split;
-}
-
-hipError_t launch_gqa_decode(const void* q, const void* k_cache, const void* v_cache,
-                             const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
-                             int32_t D, int32_t S_max, float scale, const RopeDev& rope, void* out,
-                             void* workspace, const DecodeLayout& lay, hipStream_t s) {
+hipError_t launch_gqa_decode_partial(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                     int32_t D, int32_t S_max, float scale, const RopeDev& rope,
+                                     void* workspace, const DecodeLayout& lay, hipStream_t s) {
     float* po = reinterpret_cast<float*>(workspace);
     float* pml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + lay.o_bytes);
     const int g = Hq / Hkv;
     const int NB = (g + 15) / 16;
     const float qscale = scale * kLog2e;
-    dim3 grid((lay.n_split_max + 3) / 4, Hkv, B);
+    const int np = lay.n_parts;
     if (D == 128) {
-        if (NB == 1) launch_split<128, 1>(grid, s, q, k_cache, v_cache, seq_lens, Hq, Hkv, S_max, qscale, rope, po, pml, lay.split_rows, lay.n_split_max);
-        else if (NB == 2) launch_split<128, 2>(grid, s, q, k_cache, v_cache, seq_lens, Hq, Hkv, S_max, qscale, rope, po, pml, lay.split_rows, lay.n_split_max);
-        else launch_split<128, 4>(grid, s, q, k_cache, v_cache, seq_lens, Hq, Hkv, S_max, qscale, rope, po, pml, lay.split_rows, lay.n_split_max);
+        if (NB == 1) launch_split<128, 1>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np);
+        else if (NB == 2) launch_split<128, 2>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np);
+        else launch_split<128, 4>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np);
     } else {
-        if (NB == 1) launch_split<64, 1>(grid, s, q, k_cache, v_cache, seq_lens, Hq, Hkv, S_max, qscale, rope, po, pml, lay.split_rows, lay.n_split_max);
-        else if (NB == 2) launch_split<64, 2>(grid, s, q, k_cache, v_cache, seq_lens, Hq, Hkv, S_max, qscale, rope, po, pml, lay.split_rows, lay.n_split_max);
-        else launch_split<64, 4>(grid, s, q, k_cache, v_cache, seq_lens, Hq, Hkv, S_max, qscale, rope, po, pml, lay.split_rows, lay.n_split_max);
+        if (NB == 1) launch_split<64, 1>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np);
+        else if (NB == 2) launch_split<64, 2>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np);
+        else launch_split<64, 4>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int BH = B * Hq;
-    dim3 cgrid((BH + 3) / 4);
+    return hipGetLastError();
+}
+
+hipError_t launch_gqa_decode_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                     int32_t D, int32_t S_max, const void* workspace,
+                                     const DecodeLayout& lay, void* out, hipStream_t s) {
+    const float* po = reinterpret_cast<const float*>(workspace);
+    const float* pml = reinterpret_cast<const float*>(reinterpret_cast<const char*>(workspace) + lay.o_bytes);
+    dim3 cgrid((B * Hq + 3) / 4);
     if (D == 128)
-        hipLaunchKernelGGL((combine_partials_kernel<128>), cgrid, dim3(256), 0, s, po, pml, seq_lens,
-                           Hq, S_max, S_max, lay.split_rows, lay.n_split_max, BH, (uint16_t*)out);
+        hipLaunchKernelGGL((decode_combine_kernel<128>), cgrid, dim3(256), 0, s, po, pml, seq_lens,
+                           B, Hq, Hkv, S_max, lay.n_parts, (uint16_t*)out);
     else
-        hipLaunchKernelGGL((combine_partials_kernel<64>), cgrid, dim3(256), 0, s, po, pml, seq_lens,
-                           Hq, S_max, S_max, lay.split_rows, lay.n_split_max, BH, (uint16_t*)out);
+        hipLaunchKernelGGL((decode_combine_kernel<64>), cgrid, dim3(256), 0, s, po, pml, seq_lens,
+                           B, Hq, Hkv, S_max, lay.n_parts, (uint16_t*)out);
     return hipGetLastError();
 }
 

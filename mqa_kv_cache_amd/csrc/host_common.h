@@ -31,19 +31,22 @@ hipError_t launch_rope_apply(const void* in, void* out, const int32_t* positions
                              int64_t stride_head, const RopeDev& rope, hipStream_t s);
 
 struct DecodeLayout {
-    int32_t split_rows;    // rows per split (multiple of 64)
-    int32_t n_split_max;   // ceil(S_max / split_rows)
-    size_t o_bytes;        // partial outputs  fp32 [B][Hq][n_split_max][D]
-    size_t ml_bytes;       // partial (m, l)   fp32 [B][Hq][n_split_max][2]
+    int32_t n_parts;       // equal row ranges of the global row space (one wave each)
+    int64_t slots;         // n_parts + B*Hkv partial-state slots
+    size_t o_bytes;        // partial outputs  fp32 [slots][g][D]
+    size_t ml_bytes;       // partial (m, l)   fp32 [slots][g][2]
     size_t total;
 };
-DecodeLayout decode_layout(int32_t B, int32_t Hq, int32_t D, int32_t S_max, int32_t split_rows);
-int32_t decode_default_split(int32_t B, int32_t Hkv, int32_t S_max);
+constexpr int32_t kDecodeDefaultParts = 1024;
+DecodeLayout decode_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t n_parts);
 
-hipError_t launch_gqa_decode(const void* q, const void* k_cache, const void* v_cache,
-                             const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
-                             int32_t D, int32_t S_max, float scale, const RopeDev& rope,
-                             void* out, void* workspace, const DecodeLayout& lay, hipStream_t s);
+hipError_t launch_gqa_decode_partial(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                     int32_t D, int32_t S_max, float scale, const RopeDev& rope,
+                                     void* workspace, const DecodeLayout& lay, hipStream_t s);
+hipError_t launch_gqa_decode_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                     int32_t D, int32_t S_max, const void* workspace,
+                                     const DecodeLayout& lay, void* out, hipStream_t s);
 
 // Bytes of one prepared tensor (fp16 K rows, or fp16 V^T tiles) for prefill.
 size_t prefill_prep_bytes(int32_t B, int32_t Hkv, int32_t T, int32_t D);

@@ -98,8 +98,12 @@ def test_decode_validation(m):
     assert _decode(m, wsn=0, rope=_rope(m, scaling=9, base=1e4)) == m.ERR_INVALID_ARGUMENT
     assert m.gqa_decode_workspace_size(2, 15, 2, 128, 64) == 0
     lib = m.lib()
-    assert lib.gqa_decode_split(P, P, P, P, 2, 16, 2, 128, 64, 0.1, None, P, P, 1 << 30, 100,
-                                None) == m.ERR_INVALID_ARGUMENT   # split not a multiple of 64
+    assert lib.gqa_decode_parts(P, P, P, P, 2, 16, 2, 128, 64, 0.1, None, P, P, 1 << 30, -3,
+                                None) == m.ERR_INVALID_ARGUMENT   # negative part count
+    assert lib.gqa_decode_parts(P, P, P, P, 2, 16, 2, 128, 64, 0.1, None, P, P, 1 << 30,
+                                (1 << 20) + 1, None) == m.ERR_INVALID_ARGUMENT
+    assert m.gqa_decode_workspace_size(2, 16, 2, 128, 64, 5000) > m.gqa_decode_workspace_size(2, 16, 2, 128, 64, 10)
+    assert lib.gqa_decode_combine(P, 2, 16, 2, 128, 64, P, 1, 0, P, None) == m.ERR_WORKSPACE_TOO_SMALL
 
 
 def test_prefill_validation(m):

@@ -20,15 +20,15 @@ def m():
     return mqa_kv_cache_amd
 
 
-def _run_case(m, B, Hq, Hkv, D, S_max, seq_lens, rope, seed, split_rows=None, scale=None):
+def _run_case(m, B, Hq, Hkv, D, S_max, seq_lens, rope, seed, n_parts=None, scale=None):
     import torch
     d = decode_inputs_host(B, Hq, Hkv, D, S_max, seed, seq_lens)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     print(f"[case] B={B} Hq={Hq} Hkv={Hkv} D={D} S_max={S_max} lens={list(seq_lens)} "
-          f"rope={rope and rope['scaling']} split={split_rows} seed={seed}", flush=True)
+          f"rope={rope and rope['scaling']} parts={n_parts} seed={seed}", flush=True)
     out = m.gqa_decode(to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"]),
                        torch.from_numpy(d["seq_lens"]).cuda(), scale, q_rope=rope,
-                       split_rows=split_rows)
+                       n_parts=n_parts)
     torch.cuda.synchronize()
     ref = oatt.decode(bf16_bits_to_f64(d["q"]), bf16_bits_to_f64(d["k"]), bf16_bits_to_f64(d["v"]),
                       d["seq_lens"], scale, rope)
@@ -56,12 +56,14 @@ def test_decode_parity_small(m, case):
 
 
 def test_decode_yarn_and_split_independence(m):
+    """The output does not depend on how the rows are cut into work ranges,
+    including ranges that span several contexts or hold a single row."""
     rope = rope_settings(ROPE_YARN, base=500000.0, factor=4.0, original_max_position=64)
     lens = np.array([1000, 777, 64, 65], dtype=np.int32)
     outs = []
-    for split in (None, 64, 128, 448, 1024, 4096):
-        got, ref = _run_case(m, 4, 16, 2, 128, 1000, lens, rope, seed=12, split_rows=split)
-        assert_close(got, ref, f"yarn split={split}")
+    for parts in (None, 1, 2, 7, 64, 1000, 5000, 20000):
+        got, ref = _run_case(m, 4, 16, 2, 128, 1000, lens, rope, seed=12, n_parts=parts)
+        assert_close(got, ref, f"yarn parts={parts}")
         outs.append(got)
     for o in outs[1:]:
         assert np.max(np.abs(o - outs[0])) <= 4e-3
@@ -69,18 +71,24 @@ def test_decode_yarn_and_split_independence(m):
 
 def test_decode_no_rope_and_gqa_equals_repeated_mha(m):
     """GQA on the GPU equals an MHA run over K/V materialised with each head
-    repeated g times (repeat_interleave)."""
+    repeated g times (repeat_interleave): bit for bit when every context is
+    one piece (n_parts=1), within rounding for the default work split (whose
+    piece boundaries depend on the total row count)."""
     import torch
     B, Hq, Hkv, D, S = 2, 16, 4, 128, 300
     d = decode_inputs_host(B, Hq, Hkv, D, S, 13, [300, 123])
     sl = torch.from_numpy(d["seq_lens"]).cuda()
     q, k, v = to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"])
-    o1 = m.gqa_decode(q, k, v, sl, 0.1)
     g = Hq // Hkv
-    o2 = m.gqa_decode(q, k.repeat_interleave(g, dim=1).contiguous(),
-                      v.repeat_interleave(g, dim=1).contiguous(), sl, 0.1)
+    kr = k.repeat_interleave(g, dim=1).contiguous()
+    vr = v.repeat_interleave(g, dim=1).contiguous()
+    o1 = m.gqa_decode(q, k, v, sl, 0.1, n_parts=1)
+    o2 = m.gqa_decode(q, kr, vr, sl, 0.1, n_parts=1)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+    o3 = m.gqa_decode(q, kr, vr, sl, 0.1)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(from_dev(o3) - from_dev(o1))) <= 4e-3
     ref = oatt.decode(bf16_bits_to_f64(d["q"]), bf16_bits_to_f64(d["k"]), bf16_bits_to_f64(d["v"]),
                       d["seq_lens"], 0.1, None)
     assert_close(from_dev(o1), ref, "no-rope")
