@@ -56,12 +56,16 @@ hipError_t launch_gqa_prefill(const void* q, const void* k, const void* v, int32
                               const RopeDev& rope, void* out, void* workspace, hipStream_t s);
 
 struct SparseLayout {
-    size_t scores_bytes;   // fp32 [B][S_max]
-    size_t hist_bytes;     // u32 [B][hist bins]
-    size_t o_bytes;        // fp32 partials
+    size_t scores_bytes;   // fp32 [B][S_max rounded up to 4]
+    size_t hist_bytes;     // u32 [B][4096] first-digit histogram + u32 [B] candidate counts
+    size_t cand_bytes;     // u32 [B][8192] keys of the threshold bin
+    size_t info_bytes;     // per-batch threshold, ties to take
+    size_t counts_bytes;   // u32 [B][key chunks][2] per-chunk counts above / equal to it
+    size_t o_bytes;        // fp32 attention partials
     size_t ml_bytes;
     size_t total;
     int32_t n_chunks;      // attention splits over the selected rows
+    int32_t n_key_chunks;  // 4096-key chunks of the scores
 };
 SparseLayout sparse_layout(int32_t B, int32_t H, int32_t S_max, int32_t top_k);
 

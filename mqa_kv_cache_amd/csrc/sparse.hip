@@ -8,12 +8,13 @@
 //    are summed in fp64, then rounded once to fp32 and passed through ReLU.
 //    The pass also builds the first radix-select histogram (top 12 bits of
 //    the non-negative fp32 score) in LDS and flushes it with atomics.
-// 2. topk_select_kernel: one 1024-thread workgroup per batch row finds the
-//    exact k-th largest score (first digit from the histogram; the rest from
-//    the candidates of that bin, kept in LDS, or from further passes over the
-//    scores when the bin is too large), then writes the selected indices in
-//    ascending order: every score above the threshold, plus the first
-//    equal-to-threshold scores in index order until k are taken.
+// 2. top-k selection by radix select over the fp32 score bits: the first
+//    12-bit digit comes from the indexer's histogram, the keys of the bin
+//    that holds the k-th score are gathered (4096-key chunk workgroups) and
+//    refined to the exact k-th key T by one workgroup per batch row (or by
+//    extra passes over the scores when that bin is huge); chunk workgroups
+//    then count and write, in ascending index order, every score above T
+//    plus the first equal-to-T scores until k are taken.
 // 3. sparse_attn_kernel: MQA attention of the H heads over the gathered
 //    latent rows (the indexed rows are read straight from the cache; no copy
 //    of the selection is made).  Same MFMA structure as the dense decode:
@@ -42,7 +43,7 @@ __global__ void zero_u32_kernel(uint32_t* __restrict__ p, int n) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void indexer_kernel(
     const uint16_t* __restrict__ q_index, const uint16_t* __restrict__ k_index,
-    const int32_t* __restrict__ seq_lens, int S_max, int rows_per_block,
+    const int32_t* __restrict__ seq_lens, int S_max, int S_stride, int rows_per_block,
     float* __restrict__ scores, uint32_t* __restrict__ hist) {
     __shared__ uint32_t lh[kHistBins];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -63,14 +64,15 @@ __global__ __launch_bounds__(256) void indexer_kernel(
         }
         const __amdgpu_buffer_rsrc_t kr =
             make_rsrc(k_index + (size_t)b * S_max * kDidx, (uint32_t)L * kDidx * 2u);
-        float* srow = scores + (size_t)b * S_max;
-        for (int r = r_begin + 16 * wave; r < r_end; r += 64) {
-            u32x4 raw[4];
+        float* srow = scores + (size_t)b * S_stride;
+        constexpr int RA = 16;   // row groups per wave step: 64 rows, 16 KB in flight per wave
+        for (int r = r_begin + 4 * RA * wave; r < r_end; r += 4 * RA * 4) {
+            u32x4 raw[RA];
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < RA; ++a)
                 raw[a] = buf_load16(kr, (uint32_t)(((r + 4 * a + G) * kDidx + 8 * n) * 2));
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
+            for (int a = 0; a < RA; ++a) {
                 double acc = 0.0;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -97,11 +99,30 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 2. top-k selection
+// 2. top-k selection, spread over (chunk, batch) workgroups:
+//    topk_candidates_kernel  first digit from the histogram; keys of the
+//                            threshold bin appended to a per-batch list
+//    topk_threshold_kernel   exact k-th key T from the candidates (or from
+//                            extra passes when the bin is too large), the
+//                            count above T and the number of ties to take
+//    topk_count_kernel       per-chunk counts of keys > T and == T
+//    topk_write_kernel       ordered output: chunk prefix + in-chunk ranks
+// Keys are the bit patterns of non-negative fp32 scores, so unsigned order
+// is score order.
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 1024;
+constexpr int kChunkThreads = 256;
+constexpr int kChunkKeys = 4096;          // keys per chunk workgroup
 
-// Inclusive prefix sum of one value per thread across the 1024-thread block.
+struct SelInfo {
+    uint32_t T;        // k-th largest key
+    uint32_t need;     // keys == T to take, lowest indices first
+    uint32_t B1;       // first-digit bin of T
+    uint32_t pad;
+};
+
+// Inclusive prefix sum of one value per thread across a block of NT threads.
+template <int NT>
 __device__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* wsum) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -112,13 +133,13 @@ __device__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* wsum) {
     if (lane == 63) wsum[wave] = v;
     __syncthreads();
     if (wave == 0) {
-        uint32_t w = lane < kSelThreads / 64 ? wsum[lane] : 0u;
+        uint32_t w = lane < NT / 64 ? wsum[lane] : 0u;
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
+        for (int o = 1; o < NT / 64; o <<= 1) {
             const uint32_t t = __shfl_up(w, o, 64);
             if (lane >= o) w += t;
         }
-        if (lane < kSelThreads / 64) wsum[lane] = w;   // inclusive wave totals
+        if (lane < NT / 64) wsum[lane] = w;   // inclusive wave totals
     }
     __syncthreads();
     const uint32_t add = wave ? wsum[wave - 1] : 0u;
@@ -128,18 +149,18 @@ __device__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* wsum) {
 
 // Over a histogram h[0..nbins) in LDS, find the largest bin B with
 // (count in bins >= B) >= need.  Writes B and the count in bins > B to
-// out[0], out[1].  Every thread must call it.
+// out[0], out[1].  Every thread of the NT-thread block must call it.
+template <int NT>
 __device__ void find_crossing(const uint32_t* h, int nbins, uint32_t need, uint32_t* wsum,
                               uint32_t* out) {
-    const int per = (nbins + kSelThreads - 1) / kSelThreads;
-    // thread t owns bins [hi - per, hi) counting down from the top: reverse order
-    const int t = threadIdx.x;
+    const int per = (nbins + NT - 1) / NT;
+    const int t = threadIdx.x;             // thread t owns bins [hi - per, hi), from the top
     const int hi = nbins - t * per;
     const int lo = max(hi - per, 0);
     uint32_t c = 0;
     for (int i = lo; i < hi; ++i) c += h[i];
-    const uint32_t incl = block_inclusive_scan(c, wsum);   // count in bins >= lo
-    const uint32_t excl = incl - c;                         // count in bins >= hi
+    const uint32_t incl = block_inclusive_scan<NT>(c, wsum);   // count in bins >= lo
+    const uint32_t excl = incl - c;                             // count in bins >= hi
     if (excl < need && incl >= need) {
         uint32_t acc = excl;
         for (int i = hi - 1; i >= lo; --i) {
@@ -154,60 +175,95 @@ __device__ void find_crossing(const uint32_t* h, int nbins, uint32_t need, uint3
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
-    const float* __restrict__ scores, const uint32_t* __restrict__ hist_g,
-    const int32_t* __restrict__ seq_lens, int S_max, int top_k, int32_t* __restrict__ topk_idx) {
-    __shared__ uint32_t h[kHistBins];
-    __shared__ uint32_t cand[kCandCap];
-    __shared__ uint32_t wsum[kSelThreads / 64];
-    __shared__ uint32_t res[2];
-    __shared__ uint32_t ccount;
-    const int tid = threadIdx.x;
-    const int b = blockIdx.x;
-    const int L = min(max(seq_lens[b], 1), S_max);
-    const int k = min(top_k, L);
-    const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_max);
-    int32_t* outp = topk_idx + (size_t)b * top_k;
-    for (int i = k + tid; i < top_k; i += kSelThreads) outp[i] = -1;
-    if (k == L) {   // everything is selected
-        for (int i = tid; i < L; i += kSelThreads) outp[i] = i;
-        return;
-    }
-
-    // ---- digit 1 (bits 31..20) from the indexer's histogram; bin 0 is implied
+// Loads the first-digit histogram of batch b (bin 0 implied by L) and finds
+// the bin holding the k-th largest key: out = {B1, count above B1}.
+template <int NT>
+__device__ void first_digit(const uint32_t* hist_g, int b, int L, int k, uint32_t* h,
+                            uint32_t* wsum, uint32_t* out) {
     uint32_t nz = 0;
-    for (int i = tid; i < kHistBins; i += kSelThreads) {
+    for (int i = threadIdx.x; i < kHistBins; i += NT) {
         const uint32_t v = i ? hist_g[(size_t)b * kHistBins + i] : 0u;
         h[i] = v;
         nz += v;
     }
-    if (tid == 0) ccount = 0;
-    const uint32_t tot = block_inclusive_scan(nz, wsum);
-    if (tid == kSelThreads - 1) h[0] = (uint32_t)L - tot;
+    const uint32_t tot = block_inclusive_scan<NT>(nz, wsum);
+    if (threadIdx.x == NT - 1) h[0] = (uint32_t)L - tot;
     __syncthreads();
-    find_crossing(h, kHistBins, (uint32_t)k, wsum, res);
-    const uint32_t B1 = res[0];
-    uint32_t above = res[1];
-    uint32_t need = (uint32_t)k - above;
-    const uint32_t bin_count = h[B1];
-    __syncthreads();
+    find_crossing<NT>(h, kHistBins, (uint32_t)k, wsum, out);
+}
 
-    uint32_t T;   // the k-th largest key
-    if (bin_count <= (uint32_t)kCandCap) {
-        // ---- gather the keys of bin B1 into LDS, then refine there
-        for (int j = tid; j < L; j += kSelThreads) {
-            const uint32_t key = keys[j];
-            if ((key >> 20) == B1) cand[atomicAdd(&ccount, 1u)] = key;
+// Keys of the threshold bin found in chunk c go to that chunk's own slice of
+// the candidate buffer (the chunk's index range), their number to
+// cand_cnt[b][c]: no cross-workgroup atomics.
+__global__ __launch_bounds__(kChunkThreads) void topk_candidates_kernel(
+    const float* __restrict__ scores, const uint32_t* __restrict__ hist_g,
+    const int32_t* __restrict__ seq_lens, int S_max, int S_stride, int top_k,
+    uint32_t* __restrict__ cand_g, uint32_t* __restrict__ cand_cnt, int n_chunks) {
+    __shared__ uint32_t h[kHistBins];
+    __shared__ uint32_t wsum[kChunkThreads / 64];
+    __shared__ uint32_t res[2];
+    __shared__ uint32_t lcount;
+    const int b = blockIdx.y, c = blockIdx.x;
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int k = min(top_k, L);
+    const int c0 = c * kChunkKeys;
+    if (k == L || c0 >= L) return;
+    if (threadIdx.x == 0) lcount = 0;
+    first_digit<kChunkThreads>(hist_g, b, L, k, h, wsum, res);
+    const uint32_t B1 = res[0];
+    const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride);
+    const int c1 = min(c0 + kChunkKeys, L);
+    uint32_t* cand = cand_g + (size_t)b * n_chunks * kChunkKeys + c0;
+    for (int j = c0 + threadIdx.x; j < c1; j += kChunkThreads) {
+        const uint32_t key = keys[j];
+        if ((key >> 20) == B1) cand[atomicAdd(&lcount, 1u)] = key;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) cand_cnt[(size_t)b * n_chunks + c] = lcount;
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
+    const float* __restrict__ scores, const uint32_t* __restrict__ hist_g,
+    const int32_t* __restrict__ seq_lens, int S_max, int S_stride, int top_k,
+    const uint32_t* __restrict__ cand_g, const uint32_t* __restrict__ cand_cnt, int n_chunks,
+    SelInfo* __restrict__ info) {
+    __shared__ uint32_t h[kHistBins];
+    __shared__ uint32_t cand[kCandCap];
+    __shared__ uint32_t wsum[kSelThreads / 64];
+    __shared__ uint32_t res[2];
+    __shared__ uint32_t cstart[1024];   // prefix of the per-chunk candidate counts
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x;
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int k = min(top_k, L);
+    if (k == L) return;
+    first_digit<kSelThreads>(hist_g, b, L, k, h, wsum, res);
+    const uint32_t B1 = res[0];
+    uint32_t need = (uint32_t)k - res[1];
+    const int nkc = min(n_chunks, (L + kChunkKeys - 1) / kChunkKeys);
+    const uint32_t cnt = tid < nkc ? cand_cnt[(size_t)b * n_chunks + tid] : 0u;
+    const uint32_t incl = block_inclusive_scan<kSelThreads>(cnt, wsum);
+    if (tid < nkc) cstart[tid] = incl - cnt;
+    if (tid == kSelThreads - 1) res[0] = incl;                 // total candidates
+    __syncthreads();
+    const uint32_t nc = res[0];
+    const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride);
+    __syncthreads();
+    uint32_t T;
+    if (nc <= (uint32_t)kCandCap) {
+        // gather every chunk's slice: wave w copies chunks w, w+16, ...
+        const int lane = tid & 63, wave = tid >> 6;
+        for (int c = wave; c < nkc; c += kSelThreads / 64) {
+            const uint32_t n_c = cand_cnt[(size_t)b * n_chunks + c];
+            const uint32_t* src = cand_g + ((size_t)b * n_chunks + c) * kChunkKeys;
+            for (uint32_t i = lane; i < n_c; i += 64) cand[cstart[c] + i] = src[i];
         }
-        __syncthreads();
-        const uint32_t nc = ccount;
         for (int i = tid; i < kHistBins; i += kSelThreads) h[i] = 0u;
         __syncthreads();
         for (uint32_t i = tid; i < nc; i += kSelThreads) atomicAdd(&h[(cand[i] >> 8) & 0xFFFu], 1u);
         __syncthreads();
-        find_crossing(h, kHistBins, need, wsum, res);
+        find_crossing<kSelThreads>(h, kHistBins, need, wsum, res);
         const uint32_t B2 = res[0];
-        above += res[1];
         need -= res[1];
         __syncthreads();
         for (int i = tid; i < 256; i += kSelThreads) h[i] = 0u;
@@ -216,12 +272,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
         for (uint32_t i = tid; i < nc; i += kSelThreads)
             if ((cand[i] >> 8) == pre) atomicAdd(&h[cand[i] & 0xFFu], 1u);
         __syncthreads();
-        find_crossing(h, 256, need, wsum, res);
+        find_crossing<kSelThreads>(h, 256, need, wsum, res);
         T = (pre << 8) | res[0];
-        above += res[1];
         need -= res[1];
     } else {
-        // ---- large bin: two more passes over the scores
+        // the threshold bin overflowed the candidate list: two passes over the keys
         for (int i = tid; i < kHistBins; i += kSelThreads) h[i] = 0u;
         __syncthreads();
         for (int j = tid; j < L; j += kSelThreads) {
@@ -229,9 +284,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
             if ((key >> 20) == B1) atomicAdd(&h[(key >> 8) & 0xFFFu], 1u);
         }
         __syncthreads();
-        find_crossing(h, kHistBins, need, wsum, res);
+        find_crossing<kSelThreads>(h, kHistBins, need, wsum, res);
         const uint32_t B2 = res[0];
-        above += res[1];
         need -= res[1];
         __syncthreads();
         for (int i = tid; i < 256; i += kSelThreads) h[i] = 0u;
@@ -242,34 +296,123 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
             if ((key >> 8) == pre) atomicAdd(&h[key & 0xFFu], 1u);
         }
         __syncthreads();
-        find_crossing(h, 256, need, wsum, res);
+        find_crossing<kSelThreads>(h, 256, need, wsum, res);
         T = (pre << 8) | res[0];
-        above += res[1];
         need -= res[1];
     }
-    // `above` keys are > T; `need` of the keys == T are taken, lowest indices first.
+    if (tid == 0) info[b] = SelInfo{T, need, B1, 0u};
+}
 
-    // ---- ordered compaction: thread t owns indices [t*C, t*C + C)
-    const int C = (L + kSelThreads - 1) / kSelThreads;
-    const int j0 = min(tid * C, L), j1 = min(j0 + C, L);
+__global__ __launch_bounds__(kChunkThreads) void topk_count_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int S_max,
+    int S_stride, int top_k, const SelInfo* __restrict__ info, uint32_t* __restrict__ counts,
+    int n_chunks) {
+    __shared__ uint32_t red[2][kChunkThreads / 64];
+    const int b = blockIdx.y, c = blockIdx.x;
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int k = min(top_k, L);
+    const int c0 = c * kChunkKeys;
+    if (k == L || c0 >= L) return;
+    const int c1 = min(c0 + kChunkKeys, L);
+    const uint32_t T = info[b].T;
+    const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride);
     uint32_t gt = 0, eq = 0;
-    for (int j = j0; j < j1; ++j) {
+    for (int j = c0 + threadIdx.x; j < c1; j += kChunkThreads) {
         const uint32_t key = keys[j];
         gt += key > T;
         eq += key == T;
     }
-    const uint32_t gt_in = block_inclusive_scan(gt, wsum);
-    const uint32_t eq_in = block_inclusive_scan(eq, wsum);
-    uint32_t eq_seen = eq_in - eq;
-    uint32_t pos = (gt_in - gt) + min(eq_seen, need);
-    for (int j = j0; j < j1; ++j) {
-        const uint32_t key = keys[j];
-        if (key > T) {
-            outp[pos++] = j;
-        } else if (key == T) {
-            if (eq_seen < need) outp[pos++] = j;
-            ++eq_seen;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        gt += __shfl_xor(gt, o, 64);
+        eq += __shfl_xor(eq, o, 64);
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        red[0][wave] = gt;
+        red[1][wave] = eq;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t g2 = 0, e2 = 0;
+        for (int w = 0; w < kChunkThreads / 64; ++w) {
+            g2 += red[0][w];
+            e2 += red[1][w];
         }
+        counts[((size_t)b * n_chunks + c) * 2] = g2;
+        counts[((size_t)b * n_chunks + c) * 2 + 1] = e2;
+    }
+}
+
+// Writes the selected indices of one chunk in ascending order.  Wave w of
+// the chunk owns a contiguous quarter of it; a selected index's slot is
+// (selected before the chunk) + (before the wave) + (earlier in the wave).
+__global__ __launch_bounds__(kChunkThreads) void topk_write_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int S_max,
+    int S_stride, int top_k, const SelInfo* __restrict__ info,
+    const uint32_t* __restrict__ counts, int n_chunks, int32_t* __restrict__ topk_idx) {
+    __shared__ uint32_t wgt[kChunkThreads / 64], weq[kChunkThreads / 64];
+    const int b = blockIdx.y, c = blockIdx.x;
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int k = min(top_k, L);
+    int32_t* outp = topk_idx + (size_t)b * top_k;
+    const int c0 = c * kChunkKeys;
+    if (c == 0)
+        for (int i = k + threadIdx.x; i < top_k; i += kChunkThreads) outp[i] = -1;
+    if (c0 >= L) return;
+    const int c1 = min(c0 + kChunkKeys, L);
+    if (k == L) {   // everything is selected
+        for (int j = c0 + threadIdx.x; j < c1; j += kChunkThreads) outp[j] = j;
+        return;
+    }
+    const uint32_t T = info[b].T, need = info[b].need;
+    uint32_t gt_before = 0, eq_before = 0;
+    for (int c2 = 0; c2 < c; ++c2) {
+        gt_before += counts[((size_t)b * n_chunks + c2) * 2];
+        eq_before += counts[((size_t)b * n_chunks + c2) * 2 + 1];
+    }
+    const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int NW = kChunkThreads / 64;
+    const int span = kChunkKeys / NW;
+    const int j0 = min(c0 + wave * span, c1), j1 = min(j0 + span, c1);
+    uint32_t gt = 0, eq = 0;
+    for (int j = j0 + lane; j < j1; j += 64) {
+        const uint32_t key = keys[j];
+        gt += key > T;
+        eq += key == T;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        gt += __shfl_xor(gt, o, 64);
+        eq += __shfl_xor(eq, o, 64);
+    }
+    if (lane == 0) {
+        wgt[wave] = gt;
+        weq[wave] = eq;
+    }
+    __syncthreads();
+    for (int w2 = 0; w2 < wave; ++w2) {
+        gt_before += wgt[w2];
+        eq_before += weq[w2];
+    }
+    uint32_t sel_seen = gt_before + min(eq_before, need);   // selected before this step
+    uint32_t eq_seen = eq_before;                            // ties before this step
+    for (int jb = j0; jb < j1; jb += 64) {
+        const int j = jb + lane;
+        const uint32_t key = j < j1 ? keys[j] : 0u;
+        const bool is_gt = j < j1 && key > T;
+        const bool is_eq = j < j1 && key == T;
+        const uint64_t eq_mask = __ballot(is_eq);
+        const uint32_t eq_rank = eq_seen + __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(eq_mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eq_mask, 0u));
+        const bool take = is_gt || (is_eq && eq_rank < need);
+        const uint64_t take_mask = __ballot(take);
+        const uint32_t pos = sel_seen + __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(take_mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)take_mask, 0u));
+        if (take) outp[pos] = j;
+        sel_seen += (uint32_t)__popcll(take_mask);
+        eq_seen += (uint32_t)__popcll(eq_mask);
     }
 }
 
@@ -401,11 +544,17 @@ SparseLayout sparse_layout(int32_t B, int32_t H, int32_t S_max, int32_t top_k) {
     SparseLayout l{};
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     l.n_chunks = (top_k + kRowsPerChunk - 1) / kRowsPerChunk;
-    l.scores_bytes = al((size_t)B * S_max * sizeof(float));
+    l.n_key_chunks = (S_max + kChunkKeys - 1) / kChunkKeys;
+    l.scores_bytes = al((size_t)B * ((S_max + 3) & ~3) * sizeof(float));
     l.hist_bytes = al((size_t)B * kHistBins * sizeof(uint32_t));
+    // candidate keys in per-chunk slices [B][key chunks][4096], then counts [B][key chunks]
+    l.cand_bytes = al((size_t)B * l.n_key_chunks * (kChunkKeys + 1) * sizeof(uint32_t));
+    l.info_bytes = al((size_t)B * sizeof(SelInfo));
+    l.counts_bytes = al((size_t)B * l.n_key_chunks * 2 * sizeof(uint32_t));
     l.o_bytes = al((size_t)B * H * l.n_chunks * kDv * sizeof(float));
     l.ml_bytes = al((size_t)B * H * l.n_chunks * 2 * sizeof(float));
-    l.total = l.scores_bytes + l.hist_bytes + l.o_bytes + l.ml_bytes;
+    l.total = l.scores_bytes + l.hist_bytes + l.cand_bytes + l.info_bytes + l.counts_bytes +
+              l.o_bytes + l.ml_bytes;
     return l;
 }
 
@@ -416,18 +565,36 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
                                      const SparseLayout& lay, hipStream_t s) {
     char* w = reinterpret_cast<char*>(workspace);
     float* scores = reinterpret_cast<float*>(w);
-    uint32_t* hist = reinterpret_cast<uint32_t*>(w + lay.scores_bytes);
-    float* po = reinterpret_cast<float*>(w + lay.scores_bytes + lay.hist_bytes);
-    float* pml = reinterpret_cast<float*>(w + lay.scores_bytes + lay.hist_bytes + lay.o_bytes);
+    w += lay.scores_bytes;
+    uint32_t* hist = reinterpret_cast<uint32_t*>(w);
+    w += lay.hist_bytes;
+    uint32_t* cand = reinterpret_cast<uint32_t*>(w);
+    uint32_t* cand_cnt = cand + (size_t)B * lay.n_key_chunks * kChunkKeys;
+    w += lay.cand_bytes;
+    SelInfo* info = reinterpret_cast<SelInfo*>(w);
+    w += lay.info_bytes;
+    uint32_t* counts = reinterpret_cast<uint32_t*>(w);
+    w += lay.counts_bytes;
+    float* po = reinterpret_cast<float*>(w);
+    w += lay.o_bytes;
+    float* pml = reinterpret_cast<float*>(w);
+    const int S_stride = (S_max + 3) & ~3;
+    const int nkc = lay.n_key_chunks;
 
-    const int nh = B * kHistBins;
-    hipLaunchKernelGGL(zero_u32_kernel, dim3((nh + 255) / 256), dim3(256), 0, s, hist, nh);
+    const int nz = B * kHistBins;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((nz + 255) / 256), dim3(256), 0, s, hist, nz);
     const int rows_per_block = 1024;
     hipLaunchKernelGGL(indexer_kernel, dim3((S_max + rows_per_block - 1) / rows_per_block, B),
                        dim3(256), 0, s, (const uint16_t*)q_index, (const uint16_t*)k_index,
-                       seq_lens, S_max, rows_per_block, scores, hist);
-    hipLaunchKernelGGL(topk_select_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, hist,
-                       seq_lens, S_max, top_k, topk_idx);
+                       seq_lens, S_max, S_stride, rows_per_block, scores, hist);
+    hipLaunchKernelGGL(topk_candidates_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores,
+                       hist, seq_lens, S_max, S_stride, top_k, cand, cand_cnt, nkc);
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, hist,
+                       seq_lens, S_max, S_stride, top_k, cand, cand_cnt, nkc, info);
+    hipLaunchKernelGGL(topk_count_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores,
+                       seq_lens, S_max, S_stride, top_k, info, counts, nkc);
+    hipLaunchKernelGGL(topk_write_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores,
+                       seq_lens, S_max, S_stride, top_k, info, counts, nkc, topk_idx);
     hipLaunchKernelGGL(sparse_attn_kernel, dim3(lay.n_chunks, H / 16, B), dim3(64), 0, s,
                        (const uint16_t*)q, (const uint16_t*)latent, topk_idx, seq_lens, H, S_max,
                        top_k, scale * kLog2e, po, pml, lay.n_chunks);

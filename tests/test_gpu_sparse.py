@@ -52,6 +52,12 @@ def test_sparse_small(m):
     _run(m, d, 256)
 
 
+def test_sparse_odd_capacity(m):
+    """S_max not a multiple of 4 (score rows are padded internally)."""
+    d = sparse_inputs_host(3, 16, 3001, 576, 128, 46, [3001, 2999, 1])
+    _run(m, d, 129)
+
+
 def test_sparse_short_context_and_full_selection(m):
     d = sparse_inputs_host(2, 32, 600, 576, 128, 42, [100, 600])
     idx = _run(m, d, 512)
