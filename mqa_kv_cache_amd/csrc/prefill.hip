@@ -37,6 +37,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int BM = 128;   // queries per workgroup (4 waves x 32)
+
+// Minimum resident waves per SIMD requested from the register allocator.
+#ifndef GQA_PREFILL_MIN_WAVES
+#define GQA_PREFILL_MIN_WAVES 2
+#endif
 constexpr int BN = 64;    // keys per tile
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -70,13 +75,151 @@ struct Geo {
     static constexpr int V_ELEMS = DM * VSTR;
 };
 
+// One 64-key tile of prepared fp16 K rows and V^T rows, 16-byte chunks spread
+// over the 256 threads of the workgroup.
 template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(
+struct TileRegs {
+    static constexpr int KCH = (BN * (D / 8) + 255) / 256;    // K chunks per thread
+    static constexpr int VCH = (D * (BN / 8) + 255) / 256;    // V^T chunks per thread
+    u32x4 k[KCH];
+    u32x4 v[VCH];
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile_regs(TileRegs<D>& r, const uint16_t* kbase,
+                                               const uint16_t* vbase, int kt, int tid) {
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+        const int c = tid + 256 * i;
+        if (c < BN * CPR) {
+            const int key = c / CPR, dc = c - key * CPR;
+            r.k[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(kt * BN + key) * D + 8 * dc);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TileRegs<D>::VCH; ++i) {
+        const int c = tid + 256 * i;
+        if (c < D * (BN / 8)) {
+            const int d = c / (BN / 8), cc = c - d * (BN / 8);
+            r.v[i] = *reinterpret_cast<const u32x4*>(vbase + ((size_t)kt * D + d) * BN + 8 * cc);
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile_lds(const TileRegs<D>& r, uint16_t* k_s, uint16_t* vt_s,
+                                               int tid) {
+    using Gm = Geo<D>;
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int i = 0; i < TileRegs<D>::KCH; ++i) {
+        const int c = tid + 256 * i;
+        if (c < BN * CPR) {
+            const int key = c / CPR, dc = c - key * CPR;
+            *reinterpret_cast<u32x4*>(&k_s[key * Gm::KSTR + 8 * dc]) = r.k[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TileRegs<D>::VCH; ++i) {
+        const int c = tid + 256 * i;
+        if (c < D * (BN / 8)) {
+            const int d = c / (BN / 8), cc = c - d * (BN / 8);
+            *reinterpret_cast<u32x4*>(&vt_s[d * Gm::VSTR + 8 * cc]) = r.v[i];
+        }
+    }
+}
+
+// Rescaling of the running output is lazy: the reference maximum m_run is
+// only raised when some query's tile maximum exceeds it by more than
+// kLazy (in base-2 units), so the probabilities stay below 2^kLazy (well
+// inside fp16) and most tiles skip the rescale.  O and l always share the
+// same reference, so O / l is unchanged.
+constexpr float kLazy = 8.0f;
+
+template <int D, bool MASK>
+__device__ __forceinline__ void tile_step(const uint16_t* k_s, const uint16_t* vt_s,
+                                          const u32x4 (&qf)[Geo<D>::KSTEPS],
+                                          f32x16 (&o)[Geo<D>::MT], float& m_run, float& l_run,
+                                          int ks, int qi, int n, int h) {
+    using Gm = Geo<D>;
+    // ---- S^T = K . Q^T  (two 32-key halves, accumulator chains interleaved)
+    f32x16 s[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[st][e] = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int u = 0; u < Gm::KSTEPS; ++u) {
+            const u32x4 kf = *reinterpret_cast<const u32x4*>(&k_s[(32 * st + n) * Gm::KSTR + 16 * u + 8 * h]);
+            s[st] = mfma32h(kf, qf[u], s[st]);
+        }
+    if constexpr (MASK) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = ks + 32 * st + 8 * j + 4 * h + i;
+                    if (key > qi) s[st][4 * j + i] = -INFINITY;
+                }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[st][e]);
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    // finite: key ks <= q0 <= qi is visible in every processed tile
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy)) {
+        asm volatile("" ::: "memory");   // keep the rescale behind the (rarely taken) branch
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < Gm::MT; ++mt) o[mt] *= alpha;
+        m_run = m_new;
+    }
+    float ls = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            s[st][e] = fast_exp2(s[st][e] - m_run);
+            ls += s[st][e];
+        }
+    ls += wave_shfl_xor(ls, 32);
+    l_run += ls;
+
+    // ---- O^T += V^T . P^T, four 16-key steps
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            u32x4 pb;
+            pb[0] = pack_f16x2(s[st][8 * c + 0], s[st][8 * c + 1]);
+            pb[1] = pack_f16x2(s[st][8 * c + 2], s[st][8 * c + 3]);
+            pb[2] = pack_f16x2(s[st][8 * c + 4], s[st][8 * c + 5]);
+            pb[3] = pack_f16x2(s[st][8 * c + 6], s[st][8 * c + 7]);
+            const int col = 16 * (2 * st + c) + 8 * h;
+#pragma unroll
+            for (int mt = 0; mt < Gm::MT; ++mt) {
+                const u32x4 vf = *reinterpret_cast<const u32x4*>(&vt_s[(32 * mt + n) * Gm::VSTR + col]);
+                o[mt] = mfma32h(vf, pb, o[mt]);
+            }
+        }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vt,
     uint16_t* __restrict__ out, int T, int T_pad, int Hq, int Hkv, float qscale, RopeDev rope) {
     using Gm = Geo<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t k_s[Gm::K_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_s[Gm::V_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t k_s[2][Gm::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t vt_s[2][Gm::V_ELEMS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -131,100 +274,45 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 
     const int q_last_wg = min(qt * BM + BM - 1, T - 1);
     const int n_kt = q_last_wg / BN + 1;
-    constexpr int CPR = D / 8;                          // 16-byte chunks per K row
     const uint16_t* kbase = kh + kvbase;
     const uint16_t* vbase = vt + kvbase;                // V^T tiles: [T_pad/64][D][64]
+
+    // Tiles are double-buffered in LDS and prefetched through registers: the
+    // global loads of tile kt+1 are issued before tile kt is consumed and
+    // stored to the other buffer afterwards, so one barrier per tile
+    // suffices and the load latency hides behind the matrix work.
+    // Padding lanes of both buffers (K columns past D when D < 16, V^T rows
+    // past D when D < 32) are never written by the staging and stay zero.
+    if constexpr (D < 16) {
+        for (int c = tid; c < 2 * BN; c += 256)
+            *reinterpret_cast<u32x4*>(&k_s[c / BN][(c % BN) * Gm::KSTR + 8]) = u32x4{0, 0, 0, 0};
+    }
+    if constexpr (D < 32) {
+        for (int c = tid; c < 2 * (Gm::DM - D) * (BN / 8); c += 256) {
+            const int buf = c / ((Gm::DM - D) * (BN / 8));
+            const int r = c - buf * ((Gm::DM - D) * (BN / 8));
+            const int row = D + r / (BN / 8), cc = r % (BN / 8);
+            *reinterpret_cast<u32x4*>(&vt_s[buf][row * Gm::VSTR + 8 * cc]) = u32x4{0, 0, 0, 0};
+        }
+    }
+    TileRegs<D> pre;
+    load_tile_regs<D>(pre, kbase, vbase, 0, tid);
+    store_tile_lds<D>(pre, k_s[0], vt_s[0], tid);
+    __syncthreads();
     for (int kt = 0; kt < n_kt; ++kt) {
         const int ks = kt * BN;
+        const int cur = kt & 1;
+        const bool more = kt + 1 < n_kt;
+        if (more) load_tile_regs<D>(pre, kbase, vbase, kt + 1, tid);
+        if (ks <= q0 + 31) {          // otherwise the whole tile is in this wave's future
+            const bool diag = ks + BN - 1 > q0;   // wave-uniform: reaches past the first query
+            if (diag)
+                tile_step<D, true>(k_s[cur], vt_s[cur], qf, o, m_run, l_run, ks, qi, n, h);
+            else
+                tile_step<D, false>(k_s[cur], vt_s[cur], qf, o, m_run, l_run, ks, qi, n, h);
+        }
+        if (more) store_tile_lds<D>(pre, k_s[cur ^ 1], vt_s[cur ^ 1], tid);
         __syncthreads();
-        // ---- stage K tile (row-major fp16, rows padded by 16 B)
-        for (int c = tid; c < BN * CPR; c += 256) {
-            const int key = c / CPR, dc = c - key * CPR;
-            *reinterpret_cast<u32x4*>(&k_s[key * Gm::KSTR + 8 * dc]) =
-                *reinterpret_cast<const u32x4*>(kbase + (size_t)(ks + key) * D + 8 * dc);
-        }
-        if constexpr (D < 16) {
-            for (int c = tid; c < BN; c += 256)
-                *reinterpret_cast<u32x4*>(&k_s[c * Gm::KSTR + 8]) = u32x4{0, 0, 0, 0};
-        }
-        // ---- stage V^T tile (already transposed and permuted by the pre-pass)
-        for (int c = tid; c < D * (BN / 8); c += 256) {
-            const int d = c / (BN / 8), cc = c - d * (BN / 8);
-            *reinterpret_cast<u32x4*>(&vt_s[d * Gm::VSTR + 8 * cc]) =
-                *reinterpret_cast<const u32x4*>(vbase + ((size_t)kt * D + d) * BN + 8 * cc);
-        }
-        if constexpr (D < 32) {
-            for (int c = tid; c < (Gm::DM - D) * (BN / 8); c += 256) {
-                const int row = D + c / (BN / 8), cc = c % (BN / 8);
-                *reinterpret_cast<u32x4*>(&vt_s[row * Gm::VSTR + 8 * cc]) = u32x4{0, 0, 0, 0};
-            }
-        }
-        __syncthreads();
-        if (ks > q0 + 31) continue;   // the whole tile is in this wave's future
-
-        // ---- S^T = K . Q^T  (two 32-key halves)
-        f32x16 s[2];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[st][e] = 0.f;
-#pragma unroll
-            for (int u = 0; u < Gm::KSTEPS; ++u) {
-                const u32x4 kf = *reinterpret_cast<const u32x4*>(&k_s[(32 * st + n) * Gm::KSTR + 16 * u + 8 * h]);
-                s[st] = mfma32h(kf, qf[u], s[st]);
-            }
-        }
-        // ---- causal mask (only tiles that reach past this wave's first query)
-        if (ks + BN - 1 > q0) {
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = ks + 32 * st + 8 * j + 4 * h + i;
-                        if (key > qi) s[st][4 * j + i] = -INFINITY;
-                    }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[st][e]);
-        mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);           // finite: key ks <= q0 <= qi is visible
-        const float alpha = fast_exp2(m_run - m_new);
-        float ls = 0.f;
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                s[st][e] = fast_exp2(s[st][e] - m_new);
-                ls += s[st][e];
-            }
-        ls += wave_shfl_xor(ls, 32);
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
-#pragma unroll
-        for (int mt = 0; mt < Gm::MT; ++mt) o[mt] *= alpha;
-
-        // ---- O^T += V^T . P^T, four 16-key steps
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                u32x4 pb;
-                pb[0] = pack_f16x2(s[st][8 * c + 0], s[st][8 * c + 1]);
-                pb[1] = pack_f16x2(s[st][8 * c + 2], s[st][8 * c + 3]);
-                pb[2] = pack_f16x2(s[st][8 * c + 4], s[st][8 * c + 5]);
-                pb[3] = pack_f16x2(s[st][8 * c + 6], s[st][8 * c + 7]);
-                const int col = 16 * (2 * st + c) + 8 * h;
-#pragma unroll
-                for (int mt = 0; mt < Gm::MT; ++mt) {
-                    const u32x4 vf = *reinterpret_cast<const u32x4*>(&vt_s[(32 * mt + n) * Gm::VSTR + col]);
-                    o[mt] = mfma32h(vf, pb, o[mt]);
-                }
-            }
     }
 
     // ---- normalise and write: lane holds query qi, d = 32 mt + 8 j + 4 h + i
