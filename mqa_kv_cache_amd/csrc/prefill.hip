@@ -43,6 +43,10 @@ constexpr int BM = 128;   // queries per workgroup (4 waves x 32)
 #define GQA_PREFILL_MIN_WAVES 2
 #endif
 constexpr int BN = 64;    // keys per tile
+#ifndef GQA_PREFILL_XCDS
+#define GQA_PREFILL_XCDS 8
+#endif
+constexpr int kXcds = GQA_PREFILL_XCDS;   // XCDs that share the dispatch round-robin
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -225,10 +229,34 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
     const int lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, h = lane >> 5;
     const int n_qt = (T + BM - 1) / BM;
-    const int qt = n_qt - 1 - (int)blockIdx.x;
-    const int hq = blockIdx.y, b = blockIdx.z;
     const int g = Hq / Hkv;
-    const int kvh = hq / g;
+    int qt, hq, b, kvh;
+    {
+        // Work order: heaviest (latest) query tiles first.  Workgroups are
+        // handed to the 8 XCDs round-robin by linear id; when the (batch, kv
+        // head) groups divide evenly over them, each XCD takes whole groups so
+        // the K/V tiles that its query tiles share stay in its own L2.
+        const int L = blockIdx.x;
+        const int G = (int)gridDim.x / (n_qt * g);   // B * Hkv
+        if (G % kXcds == 0) {
+            const int x = L % kXcds, k = L / kXcds;
+            const int per_qt = (G / kXcds) * g;
+            const int r = k / per_qt, rem = k - r * per_qt;
+            const int jg = rem / g, hl = rem - jg * g;
+            const int grp = x + kXcds * jg;
+            b = grp / Hkv;
+            kvh = grp - b * Hkv;
+            hq = kvh * g + hl;
+            qt = n_qt - 1 - r;
+        } else {
+            const int per_qt = G * g;       // B * Hq
+            const int r = L / per_qt, rem = L - r * per_qt;
+            b = rem / Hq;
+            hq = rem - b * Hq;
+            kvh = hq / g;
+            qt = n_qt - 1 - r;
+        }
+    }
     const int q0 = qt * BM + 32 * wave;      // first query of this wave
     const int qi = q0 + n;                    // this lane's query
 
@@ -417,7 +445,7 @@ void launch_d(const void* q, const void* k, const void* v, void* out, void* kh, 
     hipLaunchKernelGGL((prefill_prep_kernel<D>), dim3(T_pad / BN, Hkv, B), dim3(256), 0, s,
                        (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)kh, (uint16_t*)vt, T,
                        T_pad, Hkv, rope);
-    dim3 grid((T + BM - 1) / BM, Hq, B);
+    dim3 grid((T + BM - 1) / BM * Hq * B);   // one workgroup per (query tile, q head, batch)
     hipLaunchKernelGGL((prefill_kernel<D>), grid, dim3(256), 0, s, (const uint16_t*)q,
                        (const uint16_t*)kh, (const uint16_t*)vt, (uint16_t*)out, T, T_pad, Hq, Hkv,
                        qscale, rope);
