@@ -107,4 +107,27 @@ __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
 
+// Both halves of the wave's values of v, through the gfx950 lane-half swap
+// (a VALU op, no LDS round trip): every lane gets lane (l mod 32)'s value as
+// the first element and lane 32 + (l mod 32)'s as the second, so a max or sum
+// of the pair is bit-identical in both halves.  The instruction is written
+// out: this toolchain's optimizer replaces the second result of the builtin
+// with the first.  The nops cover the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ void halves(float v, float& lo, float& hi) {
+    float a = v, b = v;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    lo = a;
+    hi = b;
+}
+__device__ __forceinline__ float halves_max(float v) {
+    float lo, hi;
+    halves(v, lo, hi);
+    return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float halves_sum(float v) {
+    float lo, hi;
+    halves(v, lo, hi);
+    return lo + hi;
+}
+
 }  // namespace gqa

@@ -47,6 +47,12 @@ constexpr int BN = 64;    // keys per tile
 #define GQA_PREFILL_XCDS 8
 #endif
 constexpr int kXcds = GQA_PREFILL_XCDS;   // XCDs that share the dispatch round-robin
+#ifndef GQA_PREFILL_SWAP
+#define GQA_PREFILL_SWAP 1
+#endif
+#ifndef GQA_PREFILL_EARLY_V
+#define GQA_PREFILL_EARLY_V 1
+#endif
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -69,69 +75,61 @@ __device__ __forceinline__ int chunk_col(int a) { return (a == 0) ? 0 : (a == 1)
 
 template <int D>
 struct Geo {
-    static constexpr int DP = D < 16 ? 16 : D;        // head dim padded to one MFMA k-step
-    static constexpr int KSTEPS = DP / 16;            // MFMA k-steps for S^T
-    static constexpr int DM = D < 32 ? 32 : D;        // d rows of O^T padded to one 32-row tile
-    static constexpr int MT = DM / 32;                // O^T m-tiles
-    static constexpr int KSTR = DP + 8;               // K tile row stride (elements)
-    static constexpr int VSTR = BN + 8;               // V^T tile row stride (elements)
+    static constexpr int DP = D < 16 ? 16 : D;            // head dim padded to one MFMA k-step
+    static constexpr int KSTEPS = DP / 16;                // MFMA k-steps for S^T
+    static constexpr int MT = D < 32 ? 1 : D / 32;        // O^T m-tiles of 32 d rows (D < 32 is zero-padded)
+    // LDS rows are padded by 16 bytes so the 32 rows that one MFMA operand
+    // read touches (same column) fall on distinct banks.
+    static constexpr int KSTR = D + 8;                    // K tile row stride (fp16 elements)
+    static constexpr int VSTR = BN + 8;                   // V^T tile row stride (fp16 elements)
     static constexpr int K_ELEMS = BN * KSTR;
-    static constexpr int V_ELEMS = DM * VSTR;
+    static constexpr int V_ELEMS = (D < 32 ? 32 : D) * VSTR;
 };
 
-// One 64-key tile of prepared fp16 K rows and V^T rows, 16-byte chunks spread
-// over the 256 threads of the workgroup.
-template <int D>
-struct TileRegs {
-    static constexpr int KCH = (BN * (D / 8) + 255) / 256;    // K chunks per thread
-    static constexpr int VCH = (D * (BN / 8) + 255) / 256;    // V^T chunks per thread
-    u32x4 k[KCH];
-    u32x4 v[VCH];
+// Copies the rows of one tile (prepared fp16 K rows or V^T rows) from global
+// memory straight into padded LDS rows, with no register staging.  A
+// wave-wide 16-byte buffer load fills 1 KB of LDS starting where its M0 base
+// points, lane l writing bytes [16 l, 16 l + 16).  Each copy starts at a row
+// boundary and covers RPI whole padded rows; the lanes past them write the
+// start of the next row, the same bytes the next copy writes, so overlapping
+// copies agree.  Lanes on row padding read past the buffer end, which
+// fetches nothing and stores zeros.  With this shape one per-lane offset
+// serves every copy of every tile.
+template <int ROWS, int ROW_BYTES, int STRIDE>
+struct RowCopy {
+    static constexpr int RPI = 1024 / STRIDE;                 // whole rows per copy
+    static constexpr int N = (ROWS + RPI - 1) / RPI;          // copies per tile
+    uint32_t voff;                                            // this lane's source offset within a copy
+    int rr;                                                   // this lane's row within a copy
+    __device__ __forceinline__ explicit RowCopy(int lane) {
+        const int x = 16 * lane;
+        rr = x / STRIDE;
+        const int col = x - rr * STRIDE;
+        voff = col < ROW_BYTES ? (uint32_t)(rr * ROW_BYTES + col) : 0x80000000u;
+    }
+    __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t src, uint32_t tile_off, uint16_t* dst,
+                                        int wave) const {
+#pragma unroll
+        for (int i = 0; i < (N + 3) / 4; ++i) {
+            const int j = 4 * i + wave;                       // wave-uniform
+            if (j < N - 1 || (j == N - 1 && j * RPI + rr < ROWS))
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(src, dst + j * RPI * (STRIDE / 2), 16, voff,
+                                                         tile_off + (uint32_t)(j * RPI * ROW_BYTES), 0, 0);
+        }
+    }
 };
 
+// K operand (A of S^T = K . Q^T): key row r, dims 8c .. 8c+7 (zero past D).
 template <int D>
-__device__ __forceinline__ void load_tile_regs(TileRegs<D>& r, const uint16_t* kbase,
-                                               const uint16_t* vbase, int kt, int tid) {
-    constexpr int CPR = D / 8;
-#pragma unroll
-    for (int i = 0; i < TileRegs<D>::KCH; ++i) {
-        const int c = tid + 256 * i;
-        if (c < BN * CPR) {
-            const int key = c / CPR, dc = c - key * CPR;
-            r.k[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(kt * BN + key) * D + 8 * dc);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < TileRegs<D>::VCH; ++i) {
-        const int c = tid + 256 * i;
-        if (c < D * (BN / 8)) {
-            const int d = c / (BN / 8), cc = c - d * (BN / 8);
-            r.v[i] = *reinterpret_cast<const u32x4*>(vbase + ((size_t)kt * D + d) * BN + 8 * cc);
-        }
-    }
+__device__ __forceinline__ u32x4 k_frag(const uint16_t* k_s, int r, int c) {
+    if (D < 16 && 8 * c >= D) return u32x4{0, 0, 0, 0};
+    return *reinterpret_cast<const u32x4*>(&k_s[r * Geo<D>::KSTR + 8 * c]);
 }
-
+// V^T operand (A of O^T += V^T . P^T): d row, key columns 8c .. 8c+7 (zero past D).
 template <int D>
-__device__ __forceinline__ void store_tile_lds(const TileRegs<D>& r, uint16_t* k_s, uint16_t* vt_s,
-                                               int tid) {
-    using Gm = Geo<D>;
-    constexpr int CPR = D / 8;
-#pragma unroll
-    for (int i = 0; i < TileRegs<D>::KCH; ++i) {
-        const int c = tid + 256 * i;
-        if (c < BN * CPR) {
-            const int key = c / CPR, dc = c - key * CPR;
-            *reinterpret_cast<u32x4*>(&k_s[key * Gm::KSTR + 8 * dc]) = r.k[i];
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < TileRegs<D>::VCH; ++i) {
-        const int c = tid + 256 * i;
-        if (c < D * (BN / 8)) {
-            const int d = c / (BN / 8), cc = c - d * (BN / 8);
-            *reinterpret_cast<u32x4*>(&vt_s[d * Gm::VSTR + 8 * cc]) = r.v[i];
-        }
-    }
+__device__ __forceinline__ u32x4 v_frag(const uint16_t* vt_s, int d, int c) {
+    if (D < 32 && d >= D) return u32x4{0, 0, 0, 0};
+    return *reinterpret_cast<const u32x4*>(&vt_s[d * Geo<D>::VSTR + 8 * c]);
 }
 
 // Rescaling of the running output is lazy: the reference maximum m_run is
@@ -141,26 +139,31 @@ __device__ __forceinline__ void store_tile_lds(const TileRegs<D>& r, uint16_t* k
 // same reference, so O / l is unchanged.
 constexpr float kLazy = 8.0f;
 
-template <int D, bool MASK>
+template <int D>
 __device__ __forceinline__ void tile_step(const uint16_t* k_s, const uint16_t* vt_s,
                                           const u32x4 (&qf)[Geo<D>::KSTEPS],
                                           f32x16 (&o)[Geo<D>::MT], float& m_run, float& l_run,
-                                          int ks, int qi, int n, int h) {
+                                          bool diag, int ks, int qi, int n, int h) {
     using Gm = Geo<D>;
-    // ---- S^T = K . Q^T  (two 32-key halves, accumulator chains interleaved)
+    // ---- S^T = K . Q^T  (two 32-key halves)
     f32x16 s[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[st][e] = 0.f;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+        for (int u = 0; u < Gm::KSTEPS; ++u) s[st] = mfma32h(k_frag<D>(k_s, 32 * st + n, 2 * u + h), qf[u], s[st]);
+    }
+    // The first 32 keys' V^T fragments do not depend on the softmax: issue
+    // their reads now (the other half is read while the first is consumed).
+    u32x4 vf[2][2][Gm::MT];
+#if GQA_PREFILL_EARLY_V
 #pragma unroll
-        for (int u = 0; u < Gm::KSTEPS; ++u) {
-            const u32x4 kf = *reinterpret_cast<const u32x4*>(&k_s[(32 * st + n) * Gm::KSTR + 16 * u + 8 * h]);
-            s[st] = mfma32h(kf, qf[u], s[st]);
-        }
-    if constexpr (MASK) {
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int mt = 0; mt < Gm::MT; ++mt) vf[0][c][mt] = v_frag<D>(vt_s, 32 * mt + n, 2 * c + h);
+#endif
+    if (diag) {   // wave-uniform: the tile reaches past the wave's first query
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -176,7 +179,11 @@ __device__ __forceinline__ void tile_step(const uint16_t* k_s, const uint16_t* v
     for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[st][e]);
+#if GQA_PREFILL_SWAP
+    mx = halves_max(mx);
+#else
     mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+#endif
     // finite: key ks <= q0 <= qi is visible in every processed tile
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy)) {
         asm volatile("" ::: "memory");   // keep the rescale behind the (rarely taken) branch
@@ -195,10 +202,26 @@ __device__ __forceinline__ void tile_step(const uint16_t* k_s, const uint16_t* v
             s[st][e] = fast_exp2(s[st][e] - m_run);
             ls += s[st][e];
         }
-    ls += wave_shfl_xor(ls, 32);
-    l_run += ls;
+#if GQA_PREFILL_SWAP
+    l_run += halves_sum(ls);
+#else
+    l_run += ls + wave_shfl_xor(ls, 32);
+#endif
 
     // ---- O^T += V^T . P^T, four 16-key steps
+#if GQA_PREFILL_EARLY_V
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int mt = 0; mt < Gm::MT; ++mt) vf[1][c][mt] = v_frag<D>(vt_s, 32 * mt + n, 2 * (2 + c) + h);
+#else
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int mt = 0; mt < Gm::MT; ++mt) vf[st][c][mt] = v_frag<D>(vt_s, 32 * mt + n, 2 * (2 * st + c) + h);
+#endif
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -208,12 +231,8 @@ __device__ __forceinline__ void tile_step(const uint16_t* k_s, const uint16_t* v
             pb[1] = pack_f16x2(s[st][8 * c + 2], s[st][8 * c + 3]);
             pb[2] = pack_f16x2(s[st][8 * c + 4], s[st][8 * c + 5]);
             pb[3] = pack_f16x2(s[st][8 * c + 6], s[st][8 * c + 7]);
-            const int col = 16 * (2 * st + c) + 8 * h;
 #pragma unroll
-            for (int mt = 0; mt < Gm::MT; ++mt) {
-                const u32x4 vf = *reinterpret_cast<const u32x4*>(&vt_s[(32 * mt + n) * Gm::VSTR + col]);
-                o[mt] = mfma32h(vf, pb, o[mt]);
-            }
+            for (int mt = 0; mt < Gm::MT; ++mt) o[mt] = mfma32h(vf[st][c][mt], pb, o[mt]);
         }
 }
 
@@ -222,11 +241,17 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vt,
     uint16_t* __restrict__ out, int T, int T_pad, int Hq, int Hkv, float qscale, RopeDev rope) {
     using Gm = Geo<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t k_s[2][Gm::K_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_s[2][Gm::V_ELEMS];
+    // Two buffers per operand, as separate LDS objects: the compiler then
+    // tells the tile being read from the one being copied into, and does not
+    // make the reads wait for the copy in flight.
+    __shared__ __attribute__((aligned(16))) uint16_t k_s0[Gm::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t k_s1[Gm::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t vt_s0[Gm::V_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t vt_s1[Gm::V_ELEMS];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, h = lane >> 5;
     const int n_qt = (T + BM - 1) / BM;
     const int g = Hq / Hkv;
@@ -262,8 +287,23 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
 
     const size_t qbase = ((size_t)b * Hq + hq) * (size_t)T * D;
     const size_t kvbase = ((size_t)b * Hkv + kvh) * (size_t)T_pad * D;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + qbase, (uint32_t)T * D * 2u);
+    const uint16_t* kbase = kh + kvbase;
+    const uint16_t* vbase = vt + kvbase;                // V^T tiles: [T_pad/64][D][64]
+    const int q_last_wg = min(qt * BM + BM - 1, T - 1);
+    const int n_kt = q_last_wg / BN + 1;
 
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, (uint32_t)T_pad * D * 2u);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, (uint32_t)T_pad * D * 2u);
+    const RowCopy<BN, 2 * D, 2 * Gm::KSTR> kcopy(lane);
+    const RowCopy<D, 2 * BN, 2 * Gm::VSTR> vcopy(lane);
+    auto copy_tile = [&](int kt, uint16_t* ks_dst, uint16_t* vs_dst) {
+        kcopy.run(kr, (uint32_t)kt * BN * D * 2u, ks_dst, wave);
+        vcopy.run(vr, (uint32_t)kt * BN * D * 2u, vs_dst, wave);
+    };
+    // the first tile's copy overlaps the Q load and rotation
+    copy_tile(0, k_s0, vt_s0);
+
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + qbase, (uint32_t)T * D * 2u);
     // ---- Q^T operands: lane holds query qi, dims 16u + 8h .. +7 (rotated, scaled, fp16)
     u32x4 qf[Gm::KSTEPS];
 #pragma unroll
@@ -300,47 +340,37 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
         for (int e = 0; e < 16; ++e) o[mt][e] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int q_last_wg = min(qt * BM + BM - 1, T - 1);
-    const int n_kt = q_last_wg / BN + 1;
-    const uint16_t* kbase = kh + kvbase;
-    const uint16_t* vbase = vt + kvbase;                // V^T tiles: [T_pad/64][D][64]
-
-    // Tiles are double-buffered in LDS and prefetched through registers: the
-    // global loads of tile kt+1 are issued before tile kt is consumed and
-    // stored to the other buffer afterwards, so one barrier per tile
-    // suffices and the load latency hides behind the matrix work.
-    // Padding lanes of both buffers (K columns past D when D < 16, V^T rows
-    // past D when D < 32) are never written by the staging and stay zero.
-    if constexpr (D < 16) {
-        for (int c = tid; c < 2 * BN; c += 256)
-            *reinterpret_cast<u32x4*>(&k_s[c / BN][(c % BN) * Gm::KSTR + 8]) = u32x4{0, 0, 0, 0};
-    }
-    if constexpr (D < 32) {
-        for (int c = tid; c < 2 * (Gm::DM - D) * (BN / 8); c += 256) {
-            const int buf = c / ((Gm::DM - D) * (BN / 8));
-            const int r = c - buf * ((Gm::DM - D) * (BN / 8));
-            const int row = D + r / (BN / 8), cc = r % (BN / 8);
-            *reinterpret_cast<u32x4*>(&vt_s[buf][row * Gm::VSTR + 8 * cc]) = u32x4{0, 0, 0, 0};
-        }
-    }
-    TileRegs<D> pre;
-    load_tile_regs<D>(pre, kbase, vbase, 0, tid);
-    store_tile_lds<D>(pre, k_s[0], vt_s[0], tid);
-    __syncthreads();
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const int ks = kt * BN;
-        const int cur = kt & 1;
-        const bool more = kt + 1 < n_kt;
-        if (more) load_tile_regs<D>(pre, kbase, vbase, kt + 1, tid);
-        if (ks <= q0 + 31) {          // otherwise the whole tile is in this wave's future
-            const bool diag = ks + BN - 1 > q0;   // wave-uniform: reaches past the first query
-            if (diag)
-                tile_step<D, true>(k_s[cur], vt_s[cur], qf, o, m_run, l_run, ks, qi, n, h);
-            else
-                tile_step<D, false>(k_s[cur], vt_s[cur], qf, o, m_run, l_run, ks, qi, n, h);
-        }
-        if (more) store_tile_lds<D>(pre, k_s[cur ^ 1], vt_s[cur ^ 1], tid);
+    // Double-buffered tiles, one barrier per tile: at the top of step kt the
+    // wave waits for its own copies of tile kt, the barrier then makes every
+    // wave's copies visible and also guarantees that all waves are done with
+    // tile kt-1, whose buffer the copy of tile kt+1 (issued right after)
+    // overwrites while tile kt is computed.  Tile kt lives in buffer kt & 1;
+    // the loop is unrolled by two so each step names its buffers statically.
+    // This wave's queries see tiles 0 .. n_w-1; only the last of them holds
+    // keys past its first query (q0 is a multiple of 32, tiles are 64 wide).
+    // Once done it keeps copying its share of the later tiles and meeting
+    // the barriers of the other waves.
+    const int n_w = min((q0 + 31) / BN + 1, n_kt);
+    auto step = [&](int kt, const uint16_t* ks_cur, const uint16_t* vs_cur, uint16_t* ks_nxt,
+                    uint16_t* vs_nxt) {
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if (kt + 1 < n_kt) copy_tile(kt + 1, ks_nxt, vs_nxt);
+        tile_step<D>(ks_cur, vs_cur, qf, o, m_run, l_run, kt == n_w - 1, kt * BN, qi, n, h);
+    };
+    int kt = 0;
+    for (; kt + 1 < n_w; kt += 2) {
+        step(kt, k_s0, vt_s0, k_s1, vt_s1);
+        step(kt + 1, k_s1, vt_s1, k_s0, vt_s0);
+    }
+    if (kt < n_w) step(kt++, k_s0, vt_s0, k_s1, vt_s1);
+    for (; kt < n_kt; ++kt) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 < n_kt) {
+            if (kt & 1) copy_tile(kt + 1, k_s0, vt_s0);
+            else copy_tile(kt + 1, k_s1, vt_s1);
+        }
     }
 
     // ---- normalise and write: lane holds query qi, d = 32 mt + 8 j + 4 h + i
