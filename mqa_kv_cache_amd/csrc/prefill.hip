@@ -139,101 +139,157 @@ __device__ __forceinline__ u32x4 v_frag(const uint16_t* vt_s, int d, int c) {
 // same reference, so O / l is unchanged.
 constexpr float kLazy = 8.0f;
 
+// S^T[64 keys][32 queries] = K . Q^T for one tile (two 32-key halves).
 template <int D>
-__device__ __forceinline__ void tile_step(const uint16_t* k_s, const uint16_t* vt_s,
-                                          const u32x4 (&qf)[Geo<D>::KSTEPS],
-                                          f32x16 (&o)[Geo<D>::MT], float& m_run, float& l_run,
-                                          bool diag, int ks, int qi, int n, int h) {
-    using Gm = Geo<D>;
-    // ---- S^T = K . Q^T  (two 32-key halves)
-    f32x16 s[2];
+__device__ __forceinline__ void qk_tile(const uint16_t* k_s, const u32x4 (&qf)[Geo<D>::KSTEPS],
+                                        f32x16 (&s)[2], int n, int h) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[st][e] = 0.f;
 #pragma unroll
-        for (int u = 0; u < Gm::KSTEPS; ++u) s[st] = mfma32h(k_frag<D>(k_s, 32 * st + n, 2 * u + h), qf[u], s[st]);
+        for (int u = 0; u < Geo<D>::KSTEPS; ++u)
+            s[st] = mfma32h(k_frag<D>(k_s, 32 * st + n, 2 * u + h), qf[u], s[st]);
     }
-    // The first 32 keys' V^T fragments do not depend on the softmax: issue
-    // their reads now (the other half is read while the first is consumed).
-    u32x4 vf[2][2][Gm::MT];
-#if GQA_PREFILL_EARLY_V
+}
+
+// Causal mask: keys past the lane's query qi (only the diagonal tile has any).
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int ks, int qi, int h) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int mt = 0; mt < Gm::MT; ++mt) vf[0][c][mt] = v_frag<D>(vt_s, 32 * mt + n, 2 * c + h);
-#endif
-    if (diag) {   // wave-uniform: the tile reaches past the wave's first query
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = ks + 32 * st + 8 * j + 4 * h + i;
-                    if (key > qi) s[st][4 * j + i] = -INFINITY;
-                }
-    }
+            for (int i = 0; i < 4; ++i) {
+                const int key = ks + 32 * st + 8 * j + 4 * h + i;
+                if (key > qi) s[st][4 * j + i] = -INFINITY;
+            }
+}
+
+// Folds the tile's row maxima into m_run (lazily, see kLazy).  Finite: every
+// processed tile holds a visible key for each query.
+template <int D>
+__device__ __forceinline__ void tile_max(const f32x16 (&s)[2], f32x16 (&o)[Geo<D>::MT],
+                                         float& m_run, float& l_run) {
     float mx = -INFINITY;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[st][e]);
-#if GQA_PREFILL_SWAP
     mx = halves_max(mx);
-#else
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-#endif
-    // finite: key ks <= q0 <= qi is visible in every processed tile
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy)) {
         asm volatile("" ::: "memory");   // keep the rescale behind the (rarely taken) branch
         const float m_new = fmaxf(m_run, mx);
         const float alpha = fast_exp2(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
-        for (int mt = 0; mt < Gm::MT; ++mt) o[mt] *= alpha;
+        for (int mt = 0; mt < Geo<D>::MT; ++mt) o[mt] *= alpha;
         m_run = m_new;
     }
-    float ls = 0.f;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            s[st][e] = fast_exp2(s[st][e] - m_run);
-            ls += s[st][e];
-        }
-#if GQA_PREFILL_SWAP
-    l_run += halves_sum(ls);
-#else
-    l_run += ls + wave_shfl_xor(ls, 32);
-#endif
+}
 
-    // ---- O^T += V^T . P^T, four 16-key steps
-#if GQA_PREFILL_EARLY_V
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int mt = 0; mt < Gm::MT; ++mt) vf[1][c][mt] = v_frag<D>(vt_s, 32 * mt + n, 2 * (2 + c) + h);
-#else
+// P = exp2(S - m) as fp16 pairs in the P^T operand layout (step 2 st + c
+// holds keys 32 st + 16 c .. +15); returns the lane's part of the row sum.
+__device__ __forceinline__ float probs(const f32x16 (&s)[2], float m, u32x4 (&pb)[4]) {
+    float ls = 0.f;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int mt = 0; mt < Gm::MT; ++mt) vf[st][c][mt] = v_frag<D>(vt_s, 32 * mt + n, 2 * (2 * st + c) + h);
-#endif
+            for (int w = 0; w < 4; ++w) {
+                const float p0 = fast_exp2(s[st][8 * c + 2 * w] - m);
+                const float p1 = fast_exp2(s[st][8 * c + 2 * w + 1] - m);
+                ls += p0 + p1;
+                pb[2 * st + c][w] = pack_f16x2(p0, p1);
+            }
+    return ls;
+}
+
+// O^T[D][32 queries] += V^T . P^T over the tile's four 16-key steps.
+template <int D>
+__device__ __forceinline__ void pv_tile(const uint16_t* vt_s, const u32x4 (&pb)[4],
+                                        f32x16 (&o)[Geo<D>::MT], int n, int h) {
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+        for (int mt = 0; mt < Geo<D>::MT; ++mt)
+            o[mt] = mfma32h(v_frag<D>(vt_s, 32 * mt + n, 2 * k4 + h), pb[k4], o[mt]);
+}
+
+// One pipelined step, written as explicit groups that the scheduler may not
+// mix (sched_barrier): phase A issues the S^T MFMAs of the next tile, each
+// with one K fragment read two MFMAs ahead and a slice of the softmax of the
+// current tile; phase B issues the P.V MFMAs of the current tile, each with
+// one V fragment read two ahead and a slice of the next tile's maximum.  The
+// VALU work then runs under the matrix pipe instead of between its bursts.
+template <int D>
+__device__ __forceinline__ void pipelined_step(const uint16_t* k_nx, const uint16_t* v_cu,
+                                               const u32x4 (&qf)[Geo<D>::KSTEPS],
+                                               const f32x16 (&s_c)[2], f32x16 (&s_n)[2],
+                                               f32x16 (&o)[Geo<D>::MT], float& m_run, float& l_run,
+                                               bool diag_next, int ks_next, int qi, int n, int h) {
+    constexpr int KS = Geo<D>::KSTEPS, MT = Geo<D>::MT;
+    constexpr int NQK = 2 * KS;          // S^T MFMAs of a tile
+    constexpr int NPV = 4 * MT;          // P.V MFMAs of a tile
+    constexpr int PAIRS = 16 / NQK;      // probability pairs per phase-A group
+    constexpr int MAXV = 32 / NPV;       // scores per phase-B group
+    const float m = m_run;
+
+    // ---- phase A: S^T(next) || P(current)
+    u32x4 kf[NQK];
+    u32x4 pb[4];
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2 && i < NQK; ++i) kf[i] = k_frag<D>(k_nx, 32 * (i / KS) + n, 2 * (i % KS) + h);
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            u32x4 pb;
-            pb[0] = pack_f16x2(s[st][8 * c + 0], s[st][8 * c + 1]);
-            pb[1] = pack_f16x2(s[st][8 * c + 2], s[st][8 * c + 3]);
-            pb[2] = pack_f16x2(s[st][8 * c + 4], s[st][8 * c + 5]);
-            pb[3] = pack_f16x2(s[st][8 * c + 6], s[st][8 * c + 7]);
+        for (int e = 0; e < 16; ++e) s_n[st][e] = 0.f;
 #pragma unroll
-            for (int mt = 0; mt < Gm::MT; ++mt) o[mt] = mfma32h(vf[st][c][mt], pb, o[mt]);
+    for (int i = 0; i < NQK; ++i) {
+        if (i + 2 < NQK) kf[i + 2] = k_frag<D>(k_nx, 32 * ((i + 2) / KS) + n, 2 * ((i + 2) % KS) + h);
+        s_n[i / KS] = mfma32h(kf[i], qf[i % KS], s_n[i / KS]);
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+            const int p = i * PAIRS + q;             // pair: st = p / 8, c = (p / 4) % 2, w = p % 4
+            const int st = p >> 3, c = (p >> 2) & 1, w = p & 3;
+            const float p0 = fast_exp2(s_c[st][8 * c + 2 * w] - m);
+            const float p1 = fast_exp2(s_c[st][8 * c + 2 * w + 1] - m);
+            ls += p0 + p1;
+            pb[2 * st + c][w] = pack_f16x2(p0, p1);
         }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += halves_sum(ls);
+    if (diag_next) mask_tile(s_n, ks_next, qi, h);
+
+    // ---- phase B: O += V.P(current) || max S^T(next)
+    u32x4 vf[NPV];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < 2 && g < NPV; ++g) vf[g] = v_frag<D>(v_cu, 32 * (g % MT) + n, 2 * (g / MT) + h);
+#pragma unroll
+    for (int g = 0; g < NPV; ++g) {
+        if (g + 2 < NPV) vf[g + 2] = v_frag<D>(v_cu, 32 * ((g + 2) % MT) + n, 2 * ((g + 2) / MT) + h);
+        o[g % MT] = mfma32h(vf[g], pb[g / MT], o[g % MT]);
+#pragma unroll
+        for (int q = 0; q < MAXV; ++q) {
+            const int e = g * MAXV + q;
+            mx = fmaxf(mx, s_n[e >> 4][e & 15]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    mx = halves_max(mx);
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy)) {
+        asm volatile("" ::: "memory");   // keep the rescale behind the (rarely taken) branch
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+        m_run = m_new;
+    }
 }
 
 template <int D>
@@ -296,12 +352,9 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, (uint32_t)T_pad * D * 2u);
     const RowCopy<BN, 2 * D, 2 * Gm::KSTR> kcopy(lane);
     const RowCopy<D, 2 * BN, 2 * Gm::VSTR> vcopy(lane);
-    auto copy_tile = [&](int kt, uint16_t* ks_dst, uint16_t* vs_dst) {
-        kcopy.run(kr, (uint32_t)kt * BN * D * 2u, ks_dst, wave);
-        vcopy.run(vr, (uint32_t)kt * BN * D * 2u, vs_dst, wave);
-    };
     // the first tile's copy overlaps the Q load and rotation
-    copy_tile(0, k_s0, vt_s0);
+    kcopy.run(kr, 0u, k_s0, wave);
+    vcopy.run(vr, 0u, vt_s0, wave);
 
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + qbase, (uint32_t)T * D * 2u);
     // ---- Q^T operands: lane holds query qi, dims 16u + 8h .. +7 (rotated, scaled, fp16)
@@ -340,36 +393,71 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
         for (int e = 0; e < 16; ++e) o[mt][e] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    // Double-buffered tiles, one barrier per tile: at the top of step kt the
-    // wave waits for its own copies of tile kt, the barrier then makes every
-    // wave's copies visible and also guarantees that all waves are done with
-    // tile kt-1, whose buffer the copy of tile kt+1 (issued right after)
-    // overwrites while tile kt is computed.  Tile kt lives in buffer kt & 1;
-    // the loop is unrolled by two so each step names its buffers statically.
-    // This wave's queries see tiles 0 .. n_w-1; only the last of them holds
-    // keys past its first query (q0 is a multiple of 32, tiles are 64 wide).
-    // Once done it keeps copying its share of the later tiles and meeting
-    // the barriers of the other waves.
+    // Software pipeline over 64-key tiles.  K runs one tile ahead of V:
+    // step t computes S^T of tile t+1 (MFMA) while it turns the scores of
+    // tile t into probabilities (VALU), then accumulates P.V of tile t while
+    // it takes the maximum of tile t+1.  Tile t of K lives in k_s[t & 1] and
+    // of V in vt_s[t & 1] (separate LDS objects, named statically through an
+    // unroll by two, so reads never wait for an unrelated copy in flight).
+    // At the top of step t every wave waits for its own copies and meets the
+    // barrier; all waves are then done with K(t) and V(t-1), so the copies
+    // of K(t+2) and V(t+1) go into those buffers.  This wave's queries see
+    // tiles 0 .. n_w-1 and only the last of them holds keys past its first
+    // query (q0 is a multiple of 32, tiles are 64 wide); a wave done early
+    // keeps copying its share and meeting the barriers of the others.
     const int n_w = min((q0 + 31) / BN + 1, n_kt);
-    auto step = [&](int kt, const uint16_t* ks_cur, const uint16_t* vs_cur, uint16_t* ks_nxt,
-                    uint16_t* vs_nxt) {
+    if (n_kt > 1) kcopy.run(kr, (uint32_t)BN * D * 2u, k_s1, wave);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 s_cur[2];
+    qk_tile<D>(k_s0, qf, s_cur, n, h);
+    if (n_w == 1) mask_tile(s_cur, 0, qi, h);
+    tile_max<D>(s_cur, o, m_run, l_run);
+
+    auto top = [&](int t, uint16_t* k_dst, uint16_t* v_dst) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (kt + 1 < n_kt) copy_tile(kt + 1, ks_nxt, vs_nxt);
-        tile_step<D>(ks_cur, vs_cur, qf, o, m_run, l_run, kt == n_w - 1, kt * BN, qi, n, h);
+        if (t + 2 < n_kt) kcopy.run(kr, (uint32_t)(t + 2) * BN * D * 2u, k_dst, wave);
+        if (t + 1 < n_kt) vcopy.run(vr, (uint32_t)(t + 1) * BN * D * 2u, v_dst, wave);
     };
-    int kt = 0;
-    for (; kt + 1 < n_w; kt += 2) {
-        step(kt, k_s0, vt_s0, k_s1, vt_s1);
-        step(kt + 1, k_s1, vt_s1, k_s0, vt_s0);
+    // a step with a next tile: scores s_cur -> P.V, S^T of tile t+1 -> s_nxt
+    auto full = [&](int t, f32x16 (&s_c)[2], f32x16 (&s_n)[2], const uint16_t* k_next,
+                    const uint16_t* v_cur, uint16_t* k_dst, uint16_t* v_dst) {
+        top(t, k_dst, v_dst);
+        pipelined_step<D>(k_next, v_cur, qf, s_c, s_n, o, m_run, l_run, t + 1 == n_w - 1,
+                          (t + 1) * BN, qi, n, h);
+    };
+    // this wave's last step
+    auto last = [&](int t, const f32x16 (&s_c)[2], const uint16_t* v_cur, uint16_t* k_dst,
+                    uint16_t* v_dst) {
+        top(t, k_dst, v_dst);
+        u32x4 pb[4];
+        l_run += halves_sum(probs(s_c, m_run, pb));
+        pv_tile<D>(v_cur, pb, o, n, h);
+    };
+    f32x16 s_alt[2];
+    int t = 0;
+    for (; t + 2 < n_w; t += 2) {
+        full(t, s_cur, s_alt, k_s1, vt_s0, k_s0, vt_s1);
+        full(t + 1, s_alt, s_cur, k_s0, vt_s1, k_s1, vt_s0);
     }
-    if (kt < n_w) step(kt++, k_s0, vt_s0, k_s1, vt_s1);
-    for (; kt < n_kt; ++kt) {
+    if (t + 1 < n_w) {
+        full(t, s_cur, s_alt, k_s1, vt_s0, k_s0, vt_s1);
+        last(t + 1, s_alt, vt_s1, k_s1, vt_s0);
+        t += 2;
+    } else {
+        last(t, s_cur, vt_s0, k_s0, vt_s1);
+        t += 1;
+    }
+    for (; t < n_kt; ++t) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (kt + 1 < n_kt) {
-            if (kt & 1) copy_tile(kt + 1, k_s0, vt_s0);
-            else copy_tile(kt + 1, k_s1, vt_s1);
+        if (t & 1) {
+            if (t + 2 < n_kt) kcopy.run(kr, (uint32_t)(t + 2) * BN * D * 2u, k_s1, wave);
+            if (t + 1 < n_kt) vcopy.run(vr, (uint32_t)(t + 1) * BN * D * 2u, vt_s0, wave);
+        } else {
+            if (t + 2 < n_kt) kcopy.run(kr, (uint32_t)(t + 2) * BN * D * 2u, k_s0, wave);
+            if (t + 1 < n_kt) vcopy.run(vr, (uint32_t)(t + 1) * BN * D * 2u, vt_s1, wave);
         }
     }
 
