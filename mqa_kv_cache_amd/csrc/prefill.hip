@@ -155,15 +155,18 @@ __device__ __forceinline__ void qk_tile(const uint16_t* k_s, const u32x4 (&qf)[G
 
 // Causal mask: keys past the lane's query qi (only the diagonal tile has any).
 __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int ks, int qi, int h) {
+    // key = ks + 32 st + 8 j + 4 h + i is masked when 32 st + 8 j + i > lim;
+    // lim is opaque so the 32 compares happen here rather than being hoisted
+    // into (spilled) scalar masks
+    int lim = qi - ks - 4 * h;
+    asm volatile("" : "+v"(lim));
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = ks + 32 * st + 8 * j + 4 * h + i;
-                if (key > qi) s[st][4 * j + i] = -INFINITY;
-            }
+            for (int i = 0; i < 4; ++i)
+                if (32 * st + 8 * j + i > lim) s[st][4 * j + i] = -INFINITY;
 }
 
 // Folds the tile's row maxima into m_run (lazily, see kLazy).  Finite: every
@@ -188,6 +191,12 @@ __device__ __forceinline__ void tile_max(const f32x16 (&s)[2], f32x16 (&o)[Geo<D
     }
 }
 
+// acc + lo + hi of a packed fp16 pair (one dot2 instruction).
+__device__ __forceinline__ float sum_f16x2(uint32_t pk, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), one, acc, false);
+}
+
 // P = exp2(S - m) as fp16 pairs in the P^T operand layout (step 2 st + c
 // holds keys 32 st + 16 c .. +15); returns the lane's part of the row sum.
 __device__ __forceinline__ float probs(const f32x16 (&s)[2], float m, u32x4 (&pb)[4]) {
@@ -200,8 +209,9 @@ __device__ __forceinline__ float probs(const f32x16 (&s)[2], float m, u32x4 (&pb
             for (int w = 0; w < 4; ++w) {
                 const float p0 = fast_exp2(s[st][8 * c + 2 * w] - m);
                 const float p1 = fast_exp2(s[st][8 * c + 2 * w + 1] - m);
-                ls += p0 + p1;
-                pb[2 * st + c][w] = pack_f16x2(p0, p1);
+                const uint32_t pk = pack_f16x2(p0, p1);
+                pb[2 * st + c][w] = pk;
+                ls = sum_f16x2(pk, ls);
             }
     return ls;
 }
@@ -256,8 +266,9 @@ __device__ __forceinline__ void pipelined_step(const uint16_t* k_nx, const uint1
             const int st = p >> 3, c = (p >> 2) & 1, w = p & 3;
             const float p0 = fast_exp2(s_c[st][8 * c + 2 * w] - m);
             const float p1 = fast_exp2(s_c[st][8 * c + 2 * w + 1] - m);
-            ls += p0 + p1;
-            pb[2 * st + c][w] = pack_f16x2(p0, p1);
+            const uint32_t pk = pack_f16x2(p0, p1);
+            pb[2 * st + c][w] = pk;
+            ls = sum_f16x2(pk, ls);     // the row sum sees the same rounded P as the MFMA
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -417,8 +428,12 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
     auto top = [&](int t, uint16_t* k_dst, uint16_t* v_dst) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (t + 2 < n_kt) kcopy.run(kr, (uint32_t)(t + 2) * BN * D * 2u, k_dst, wave);
-        if (t + 1 < n_kt) vcopy.run(vr, (uint32_t)(t + 1) * BN * D * 2u, v_dst, wave);
+        // the wave index is made opaque here so the copy addresses are formed
+        // per step with a few scalar ops instead of being hoisted (and spilled)
+        int wv = wave;
+        asm volatile("" : "+s"(wv));
+        if (t + 2 < n_kt) kcopy.run(kr, (uint32_t)(t + 2) * BN * D * 2u, k_dst, wv);
+        if (t + 1 < n_kt) vcopy.run(vr, (uint32_t)(t + 1) * BN * D * 2u, v_dst, wv);
     };
     // a step with a next tile: scores s_cur -> P.V, S^T of tile t+1 -> s_nxt
     auto full = [&](int t, f32x16 (&s_c)[2], f32x16 (&s_n)[2], const uint16_t* k_next,
