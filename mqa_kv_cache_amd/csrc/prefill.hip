@@ -82,8 +82,13 @@ struct Geo {
     // read touches (same column) fall on distinct banks.
     static constexpr int KSTR = D + 8;                    // K tile row stride (fp16 elements)
     static constexpr int VSTR = BN + 8;                   // V^T tile row stride (fp16 elements)
-    static constexpr int K_ELEMS = BN * KSTR;
-    static constexpr int V_ELEMS = (D < 32 ? 32 : D) * VSTR;
+    // Copies of a tile (see RowCopy) cover RPI padded rows each and always
+    // write a whole 1 KB, so each buffer has room for the last copy's spill.
+    static constexpr int K_RPI = 1024 / (2 * KSTR), K_N = (BN + K_RPI - 1) / K_RPI;
+    static constexpr int V_RPI = 1024 / (2 * VSTR), V_N = (D + V_RPI - 1) / V_RPI;
+    static constexpr int cmax(int a, int b) { return a > b ? a : b; }
+    static constexpr int K_ELEMS = cmax(BN * KSTR, (K_N - 1) * K_RPI * KSTR + 512);
+    static constexpr int V_ELEMS = cmax((D < 32 ? 32 : D) * VSTR, (V_N - 1) * V_RPI * VSTR + 512);
 };
 
 // Copies the rows of one tile (prepared fp16 K rows or V^T rows) from global
@@ -92,18 +97,19 @@ struct Geo {
 // points, lane l writing bytes [16 l, 16 l + 16).  Each copy starts at a row
 // boundary and covers RPI whole padded rows; the lanes past them write the
 // start of the next row, the same bytes the next copy writes, so overlapping
-// copies agree.  Lanes on row padding read past the buffer end, which
-// fetches nothing and stores zeros.  With this shape one per-lane offset
-// serves every copy of every tile.
+// copies agree, and the last copy spills into slack after the tile that
+// nothing reads (its source rows are the next tile's, or past the buffer).
+// Lanes on row padding read past the buffer end, which fetches nothing and
+// stores zeros.  With this shape one per-lane offset serves every copy of
+// every tile, and no copy needs a lane mask.
 template <int ROWS, int ROW_BYTES, int STRIDE>
 struct RowCopy {
     static constexpr int RPI = 1024 / STRIDE;                 // whole rows per copy
     static constexpr int N = (ROWS + RPI - 1) / RPI;          // copies per tile
     uint32_t voff;                                            // this lane's source offset within a copy
-    int rr;                                                   // this lane's row within a copy
     __device__ __forceinline__ explicit RowCopy(int lane) {
         const int x = 16 * lane;
-        rr = x / STRIDE;
+        const int rr = x / STRIDE;
         const int col = x - rr * STRIDE;
         voff = col < ROW_BYTES ? (uint32_t)(rr * ROW_BYTES + col) : 0x80000000u;
     }
@@ -112,7 +118,7 @@ struct RowCopy {
 #pragma unroll
         for (int i = 0; i < (N + 3) / 4; ++i) {
             const int j = 4 * i + wave;                       // wave-uniform
-            if (j < N - 1 || (j == N - 1 && j * RPI + rr < ROWS))
+            if (j < N)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(src, dst + j * RPI * (STRIDE / 2), 16, voff,
                                                          tile_off + (uint32_t)(j * RPI * ROW_BYTES), 0, 0);
         }
