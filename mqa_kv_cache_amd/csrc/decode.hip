@@ -39,6 +39,7 @@ namespace gqa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;
 constexpr int kWaves = 4;   // waves per workgroup (each an independent work item)
 
 // Compile-time tuning: minimum resident waves per SIMD requested from the
@@ -103,33 +104,37 @@ __device__ __forceinline__ void tile_math(const DecodeTile<D>& t, int t0, int r1
         }
         float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                          fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-        mx = fmaxf(mx, wave_shfl_xor(mx, 16));
-        mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[nb], mx);   // finite: row t0 < r1 is visible
-        const float alpha = fast_exp2(m_run[nb] - m_new);
+        mx = rows4_max(mx);   // over the 4 lane groups: the head's max over the 32 rows
+        // Lazy rescale: the reference maximum only moves when some head's tile
+        // maximum exceeds it by more than kLazy (base 2), so probabilities stay
+        // below 2^kLazy and most tiles skip the O rescale.  O and l share the
+        // reference, so O / l is unchanged.  Finite: row t0 < r1 is visible.
+        if (__builtin_amdgcn_ballot_w64(mx > m_run[nb] + kLazy)) {
+            asm volatile("" ::: "memory");   // keep the rescale behind the (rarely taken) branch
+            const float m_new = fmaxf(m_run[nb], mx);
+            const float alpha = fast_exp2(m_run[nb] - m_new);
+            l_run[nb] *= alpha;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) o[nb][c] *= alpha;
+            m_run[nb] = m_new;
+        }
         float p[2][4];
         float ls = 0.f;
 #pragma unroll
         for (int th = 0; th < 2; ++th)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[th][i] = fast_exp2(sc[th][i] - m_new);
+                p[th][i] = fast_exp2(sc[th][i] - m_run[nb]);
                 ls += p[th][i];
             }
-        ls += wave_shfl_xor(ls, 16);
-        ls += wave_shfl_xor(ls, 32);
-        l_run[nb] = l_run[nb] * alpha + ls;
-        m_run[nb] = m_new;
+        l_run[nb] += rows4_sum(ls);
         u32x4 pb;
         pb[0] = pack_bf16x2(p[0][0], p[0][1]);
         pb[1] = pack_bf16x2(p[0][2], p[0][3]);
         pb[2] = pack_bf16x2(p[1][0], p[1][1]);
         pb[3] = pack_bf16x2(p[1][2], p[1][3]);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            o[nb][c] *= alpha;
-            o[nb][c] = mfma16(column_of(t.v, c), pb, o[nb][c]);
-        }
+        for (int c = 0; c < 8; ++c) o[nb][c] = mfma16(column_of(t.v, c), pb, o[nb][c]);
     }
 }
 

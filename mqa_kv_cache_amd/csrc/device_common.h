@@ -119,6 +119,28 @@ __device__ __forceinline__ void halves(float v, float& lo, float& hi) {
     lo = a;
     hi = b;
 }
+// Max / sum over the four 16-lane rows of the wave (lanes l, l^16, l^32,
+// l^48), through the gfx950 row swaps: the 16-lane swap pairs rows (0,1) and
+// (2,3), the half swap then pairs the two results.  Bit-identical in every
+// lane.
+__device__ __forceinline__ void rows16(float v, float& lo, float& hi) {
+    float a = v, b = v;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    lo = a;
+    hi = b;
+}
+__device__ __forceinline__ float rows4_max(float v) {
+    float lo, hi, a, b;
+    rows16(v, lo, hi);
+    halves(fmaxf(lo, hi), a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+    float lo, hi, a, b;
+    rows16(v, lo, hi);
+    halves(lo + hi, a, b);
+    return a + b;
+}
 __device__ __forceinline__ float halves_max(float v) {
     float lo, hi;
     halves(v, lo, hi);
