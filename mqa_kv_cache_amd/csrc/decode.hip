@@ -140,47 +140,142 @@ __device__ __forceinline__ void tile_math(const DecodeTile<D>& t, int t0, int r1
 
 // The row space shared by the decode kernel and the combine: per batch b the
 // contexts of its Hkv heads, each seq_lens[b] rows (clamped to [1, S_max]).
+// The lengths are read by the wave's lanes in chunks of 64 and prefix-summed
+// across the lanes, so the wave pays one load round trip per 64 batches
+// instead of one per batch.
 struct RowSpace {
     int64_t total;
     int64_t R;
 };
+__device__ __forceinline__ int ctx_len(const int32_t* seq_lens, int b, int S_max) {
+    return min(max(seq_lens[b], 1), S_max);
+}
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ int64_t wave_scan_incl(int64_t x, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
 __device__ __forceinline__ RowSpace row_space(const int32_t* seq_lens, int B, int Hkv, int S_max,
-                                              int n_parts) {
+                                              int n_parts, int lane) {
     int64_t total = 0;
-    for (int b = 0; b < B; ++b) total += (int64_t)Hkv * min(max(seq_lens[b], 1), S_max);
+    for (int c0 = 0; c0 < B; c0 += 64) {
+        const int bb = c0 + lane;
+        int64_t rows = bb < B ? (int64_t)Hkv * ctx_len(seq_lens, bb, S_max) : 0;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) rows += __shfl_xor(rows, o, 64);
+        total += rows;
+    }
     return RowSpace{total, (total + n_parts - 1) / n_parts};
 }
+// The context holding global row x < total: batch b, the global row `base` of
+// its (kv 0, row 0), and its length L.
+__device__ __forceinline__ void locate(const int32_t* seq_lens, int B, int Hkv, int S_max,
+                                       int64_t x, int lane, int& b, int64_t& base, int& L) {
+    int64_t run = 0;
+    for (int c0 = 0; c0 < B; c0 += 64) {
+        const int bb = c0 + lane;
+        const int Lb = bb < B ? ctx_len(seq_lens, bb, S_max) : 0;
+        const int64_t incl = wave_scan_incl((int64_t)Hkv * Lb, lane);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(bb < B && x < run + incl);
+        if (hit) {
+            const int f = __builtin_ctzll(hit);
+            b = c0 + f;
+            L = __shfl(Lb, f, 64);
+            base = run + __shfl(incl, f, 64) - (int64_t)Hkv * L;
+            return;
+        }
+        run += __shfl(incl, 63, 64);
+    }
+    b = B;   // not reached for x < total
+    base = run;
+    L = 1;
+}
 
+// Per-lane RoPE frequencies of the q dims this lane holds (dims 32u + 8G ..
+// +7, pairs i = 16u + 4G + p), read once per wave: the table sits in the
+// kernel arguments and a lane-dependent index would otherwise cost a memory
+// round trip per pair.
+template <int D>
+struct QFreq {
+    double th[D / 32][4];
+};
+template <int D>
+__device__ __forceinline__ void load_freq(const RopeDev& rope, int G, QFreq<D>& f) {
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int i = 16 * u + 4 * G + p;
+            f.th[u][p] = i < rope.half ? rope.theta[i] : 0.0;
+        }
+}
+// cos/sin of angle pos * pos_scale * theta, reduced to [-pi, pi] in fp64,
+// then fp32 sincos, both scaled by amp (the same steps as rope_cos_sin).
+__device__ __forceinline__ void cos_sin_theta(double theta, double pos, const RopeDev& r, float& c,
+                                              float& s) {
+    const double two_pi_hi = 6.283185307179586232;
+    const double two_pi_lo = 2.4492935982947064e-16;
+    const double a = pos * r.pos_scale * theta;
+    const double k = rint(a * 0.15915494309189535);
+    double red = fma(-k, two_pi_hi, a);
+    red = fma(-k, two_pi_lo, red);
+    float sv, cv;
+    sincosf((float)red, &sv, &cv);
+    c = cv * r.amp;
+    s = sv * r.amp;
+}
+
+// Raw q rows of the group's heads (issued before the first tile loads, so
+// waiting for them does not wait for the tiles).
 template <int D, int NB>
-__device__ __forceinline__ void load_q(const uint16_t* q, int b, int kv, int Hq, int g, int L,
-                                       float qscale, const RopeDev& rope, int G, int n,
-                                       u32x4 (&qhi)[NB][D / 32], u32x4 (&qlo)[NB][D / 32]) {
-    constexpr int KU = D / 32;
+__device__ __forceinline__ void load_q_raw(const uint16_t* q, int b, int kv, int Hq, int g, int G,
+                                           int n, u32x4 (&raw)[NB][D / 32]) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int hl = nb * 16 + n;
         const bool valid = hl < g;
         const uint16_t* qrow = q + ((size_t)b * Hq + (size_t)kv * g + (valid ? hl : 0)) * D;
 #pragma unroll
+        for (int u = 0; u < D / 32; ++u)
+            raw[nb][u] = valid ? *reinterpret_cast<const u32x4*>(qrow + 32 * u + 8 * G) : u32x4{0, 0, 0, 0};
+    }
+}
+// Rotates q at position L-1, folds in scale*log2(e) and splits it into the
+// hi + lo bf16 pair the two MFMA passes use.
+template <int D, int NB>
+__device__ __forceinline__ void prep_q(const u32x4 (&raw)[NB][D / 32], const QFreq<D>& fq, int L,
+                                       float qscale, const RopeDev& rope, int G,
+                                       u32x4 (&qhi)[NB][D / 32], u32x4 (&qlo)[NB][D / 32]) {
+    constexpr int KU = D / 32;
+    float cs[KU][4], sn[KU][4];
+    if (rope.half) {
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) cos_sin_theta(fq.th[u][p], (double)(L - 1), rope, cs[u][p], sn[u][p]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
         for (int u = 0; u < KU; ++u) {
             const int d0 = 32 * u + 8 * G;
-            u32x4 raw = valid ? *reinterpret_cast<const u32x4*>(qrow + d0) : u32x4{0, 0, 0, 0};
             float x[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                x[2 * j] = bf16_lo(raw[j]);
-                x[2 * j + 1] = bf16_hi(raw[j]);
+                x[2 * j] = bf16_lo(raw[nb][u][j]);
+                x[2 * j + 1] = bf16_hi(raw[nb][u][j]);
             }
             if (rope.half) {
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const int i = d0 / 2 + p;
-                    if (i < rope.half) {
-                        float c, s;
-                        rope_cos_sin(rope, (double)(L - 1), i, c, s);
+                    if (d0 / 2 + p < rope.half) {
                         const float xe = x[2 * p], xo = x[2 * p + 1];
-                        x[2 * p] = xe * c - xo * s;
-                        x[2 * p + 1] = xe * s + xo * c;
+                        x[2 * p] = xe * cs[u][p] - xo * sn[u][p];
+                        x[2 * p + 1] = xe * sn[u][p] + xo * cs[u][p];
                     }
                 }
             }
@@ -192,7 +287,6 @@ __device__ __forceinline__ void load_q(const uint16_t* q, int b, int kv, int Hq,
                 qlo[nb][u][j] = pack_bf16x2(a - __uint_as_float(ha << 16), c2 - __uint_as_float(hc << 16));
             }
         }
-    }
 }
 
 template <int D, int NB>
@@ -209,20 +303,20 @@ __global__ __launch_bounds__(64 * kWaves, GQA_DECODE_MIN_WAVES) void decode_spli
     // derived address and buffer descriptor in scalar registers
     const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
     if (w >= n_parts) return;
-    const RowSpace rs = row_space(seq_lens, B, Hkv, S_max, n_parts);
+    const RowSpace rs = row_space(seq_lens, B, Hkv, S_max, n_parts, lane);
     int64_t gs = (int64_t)w * rs.R;
     const int64_t ge = min(gs + rs.R, rs.total);
     if (gs >= ge) return;
 
     // locate the context holding global row gs
-    int b = 0, L = 0;
-    int64_t base = 0;   // global row of (b, kv 0, row 0)
-    for (; b < B; ++b) {
-        L = min(max(seq_lens[b], 1), S_max);
-        if (gs < base + (int64_t)Hkv * L) break;
-        base += (int64_t)Hkv * L;
-    }
+    int b, L;
+    int64_t base;   // global row of (b, kv 0, row 0)
+    locate(seq_lens, B, Hkv, S_max, gs, lane, b, base, L);
+    b = __builtin_amdgcn_readfirstlane(b);
+    L = __builtin_amdgcn_readfirstlane(L);
     int kv = (int)((gs - base) / L);
+    QFreq<D> fq;
+    load_freq<D>(rope, G, fq);
 
     while (gs < ge) {
         const int64_t ctx0 = base + (int64_t)kv * L;        // global row of this context's row 0
@@ -235,7 +329,10 @@ __global__ __launch_bounds__(64 * kWaves, GQA_DECODE_MIN_WAVES) void decode_spli
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(k_cache + slice, nbytes);
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_cache + slice, nbytes);
 
-        // the first tiles are requested before q is prepared, hiding its latency
+        // q is requested first, then the first tiles; q is prepared while the
+        // tiles are in flight
+        u32x4 qraw[NB][KU];
+        load_q_raw<D, NB>(q, b, kv, Hq, g, G, n, qraw);
 #if GQA_DECODE_PREFETCH >= 1
         DecodeTile<D> ta, tb;
         load_tile<D>(ta, kr, vr, r0, G, n);
@@ -246,7 +343,7 @@ __global__ __launch_bounds__(64 * kWaves, GQA_DECODE_MIN_WAVES) void decode_spli
 #endif
 
         u32x4 qhi[NB][KU], qlo[NB][KU];
-        load_q<D, NB>(q, b, kv, Hq, g, L, qscale, rope, G, n, qhi, qlo);
+        prep_q<D, NB>(qraw, fq, L, qscale, rope, G, qhi, qlo);
 
         f32x4 o[NB][8];
         float m_run[NB], l_run[NB];
@@ -331,7 +428,8 @@ __global__ __launch_bounds__(64 * kWaves, GQA_DECODE_MIN_WAVES) void decode_spli
 // One wave per (batch, q head): merges the states of the pieces of its
 // context, slots floor(x/R) + i for the global rows x of context i.  Lane j
 // reads the (m, l) of piece j, so the maximum and the weights take one
-// round trip; the o rows are then read with independent loads.
+// round trip; the o rows (lane: D/64 values) are then read eight pieces at
+// a time with independent loads.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -343,10 +441,17 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     if (idx >= B * Hq) return;
     const int b = idx / Hq, h = idx - b * Hq;
     const int g = Hq / Hkv, kv = h / g, hl = h - kv * g;
-    const RowSpace rs = row_space(seq_lens, B, Hkv, S_max, n_parts);
+    const RowSpace rs = row_space(seq_lens, B, Hkv, S_max, n_parts, lane);
+    // global row of (b, kv 0, row 0): prefix over the batches before b
     int64_t base = 0;
-    for (int bb = 0; bb < b; ++bb) base += (int64_t)Hkv * min(max(seq_lens[bb], 1), S_max);
-    const int L = min(max(seq_lens[b], 1), S_max);
+    for (int c0 = 0; c0 < b; c0 += 64) {
+        const int bb = c0 + lane;
+        int64_t rows = bb < b ? (int64_t)Hkv * ctx_len(seq_lens, bb, S_max) : 0;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) rows += __shfl_xor(rows, o, 64);
+        base += rows;
+    }
+    const int L = ctx_len(seq_lens, b, S_max);
     const int64_t x0 = base + (int64_t)kv * L;
     const int64_t ctx = (int64_t)b * Hkv + kv;
     const int64_t s0 = x0 / rs.R + ctx;
@@ -376,11 +481,21 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) dsum += wave_shfl_xor(dsum, o);
         den += dsum;
-        for (int j = 0; j < cn; ++j) {
-            const float wgt = __shfl(wl, j, 64);
-            const float* po = part_o + ((size_t)(s0 + c0 + j) * g + hl) * D + lane * PER;
+        const float* pbase = part_o + ((size_t)(s0 + c0) * g + hl) * D + lane * PER;
+        const size_t pstride = (size_t)g * D;
+        for (int j0 = 0; j0 < cn; j0 += 8) {
+            float v[8][PER];
 #pragma unroll
-            for (int e = 0; e < PER; ++e) acc[e] += wgt * po[e];
+            for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+                for (int e = 0; e < PER; ++e) v[jj][e] = j0 + jj < cn ? pbase[(j0 + jj) * pstride + e] : 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const float wgt = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), min(j0 + jj, 63)));
+#pragma unroll
+                for (int e = 0; e < PER; ++e) acc[e] += wgt * v[jj][e];
+            }
         }
         M_run = M_new;
     }
