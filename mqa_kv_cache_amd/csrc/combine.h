@@ -12,31 +12,64 @@ namespace {
 //   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,   M = max_s m_s,
 // an exact rewriting of the single-pass softmax.  The number of splits of
 // batch b is ceil(min(seq_lens[b], cap) / rows_per_split).
-template <int D>
+template <int D>   // D a multiple of 256 (each lane holds D/64 >= 4 contiguous values)
 __global__ __launch_bounds__(256) void combine_partials_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, int H, int S_max, int cap, int rows_per_split,
     int n_split_max, int BH, uint16_t* __restrict__ out) {
     constexpr int PER = D / 64;
     const int lane = threadIdx.x & 63;
-    const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int idx = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     if (idx >= BH) return;
     const int b = idx / H;
     const int L = min(min(max(seq_lens[b], 1), S_max), cap);
     const int ns = (L + rows_per_split - 1) / rows_per_split;
     const float* ml = part_ml + (size_t)idx * n_split_max * 2;
-    const float* po = part_o + (size_t)idx * n_split_max * D;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+    const float* po = part_o + (size_t)idx * n_split_max * D + lane * PER;
     float acc[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-    float den = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float w = fast_exp2(ml[2 * s] - M);
-        den += w * ml[2 * s + 1];
+    float den = 0.f, M_run = -INFINITY;
+    // lane s reads the (m, l) of split s (64 splits at a time); the o rows
+    // are then read four splits at a time with independent loads
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+        const int cn = min(64, ns - s0);
+        const float m = lane < cn ? ml[2 * (s0 + lane)] : -INFINITY;
+        const float l = lane < cn ? ml[2 * (s0 + lane) + 1] : 0.f;
+        float M = m;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) acc[j] += w * po[(size_t)s * D + lane * PER + j];
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, wave_shfl_xor(M, o));
+        const float M_new = fmaxf(M_run, M);   // finite: every split holds a row
+        const float rescale = fast_exp2(M_run - M_new);
+        den *= rescale;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] *= rescale;
+        const float wl = lane < cn ? fast_exp2(m - M_new) : 0.f;
+        float dsum = wl * l;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) dsum += wave_shfl_xor(dsum, o);
+        den += dsum;
+        for (int j0 = 0; j0 < cn; j0 += 4) {
+            f32x4 v[4][PER / 4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int sj = s0 + min(j0 + jj, cn - 1);   // past the end: a valid split, weight 0
+                const f32x4* src = reinterpret_cast<const f32x4*>(po + (size_t)sj * D);
+#pragma unroll
+                for (int e = 0; e < PER / 4; ++e) v[jj][e] = src[e];
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float wgt = j0 + jj < cn ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                     __builtin_bit_cast(int, wl), min(j0 + jj, 63)))
+                                               : 0.f;
+#pragma unroll
+                for (int e = 0; e < PER / 4; ++e)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[4 * e + c] += wgt * v[jj][e][c];
+            }
+        }
+        M_run = M_new;
     }
     const float inv = 1.0f / den;
     uint16_t* o = out + (size_t)idx * D + lane * PER;

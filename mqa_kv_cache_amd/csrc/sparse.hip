@@ -18,9 +18,9 @@
 // 3. sparse_attn_kernel: MQA attention of the H heads over the gathered
 //    latent rows (the indexed rows are read straight from the cache; no copy
 //    of the selection is made).  Same MFMA structure as the dense decode:
-//    S^T = C . Q^T over 576 dims, online softmax, O^T += C[:, :512]^T . P^T;
-//    each wave covers 16 heads and 128 selected rows and writes a partial
-//    (m, l, o) that combine_partials_kernel merges.
+//    S^T = C . Q^T over 576 dims, softmax, O^T = C[:, :512]^T . P^T; a
+//    workgroup covers 16 heads and 128 selected rows (32 per wave, merged in
+//    LDS) and writes a partial (m, l, o) that combine_partials_kernel merges.
 #include "device_common.h"
 #include "combine.h"
 
@@ -419,91 +419,99 @@ __global__ __launch_bounds__(kChunkThreads) void topk_write_kernel(
 // ---------------------------------------------------------------------------
 // 3. attention over the selected latent rows
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void sparse_attn_kernel(
+// One workgroup per (128 selected rows, 16 heads, batch row); wave w takes
+// rows 32 w .. 32 w + 31 of the chunk.  A wave first reads its row indices,
+// then issues every K and V fragment load of its rows at once (one round
+// trip to L2/HBM instead of one per k-step group), computes
+//   S^T[32 rows][16 heads] = C . Q^T   (18 k-steps of 16x16x32 bf16 MFMA)
+// and its own softmax state over the 32 rows, then
+//   O^T[512][16 heads] = C[:, :512]^T . P^T.
+// The four waves' states are merged in LDS (log-sum-exp) into one partial
+// per (chunk, head), which combine_partials_kernel merges over the chunks.
+constexpr int kAttnWaves = kRowsPerChunk / 32;
+constexpr int kOStride = kDv + 4;   // LDS floats per head row (padded against bank conflicts)
+
+__global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ seq_lens, int H, int S_max,
     int top_k, float qscale, float* __restrict__ part_o, float* __restrict__ part_ml,
     int n_chunks) {
     constexpr int KU = kDqk / 32;   // 18 MFMA k-steps for the scores
-    const int lane = threadIdx.x;
+    __shared__ __attribute__((aligned(16))) float o_s[kAttnWaves][16][kOStride];
+    __shared__ float ml_s[kAttnWaves][16][2];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = lane >> 4, n = lane & 15;
     const int chunk = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
     const int L = min(max(seq_lens[b], 1), S_max);
     const int k = min(top_k, L);
     const int c0 = chunk * kRowsPerChunk;
-    if (c0 >= k) return;
+    if (c0 >= k) return;                        // whole workgroup
     const int c1 = min(c0 + kRowsPerChunk, k);
+    const int w0 = c0 + 32 * wave;
     const int h = hb * 16 + n;
 
-    // q is bf16 already: used exactly as the B operand; the scale is applied to S.
-    u32x4 qf[KU];
-    const uint16_t* qrow = q + ((size_t)b * H + h) * kDqk;
-#pragma unroll
-    for (int u = 0; u < KU; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u + 8 * G);
-
-    const __amdgpu_buffer_rsrc_t cr =
-        make_rsrc(latent + (size_t)b * S_max * kDqk, (uint32_t)S_max * kDqk * 2u);
-    const int32_t* sel = topk_idx + (size_t)b * top_k;
-
-    f32x4 o[4][8];
-#pragma unroll
-    for (int dq = 0; dq < 4; ++dq)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) o[dq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
-
-    for (int t0 = c0; t0 < c1; t0 += 32) {
-        // row byte offsets of this lane's K rows (n, 16+n) and V rows (slot_row(G, r))
+    if (w0 < c1) {
+        const int32_t* sel = topk_idx + (size_t)b * top_k;
         uint32_t koff[2], voff[8];
 #pragma unroll
         for (int th = 0; th < 2; ++th) {
-            const int p = t0 + 16 * th + n;
+            const int p = w0 + 16 * th + n;
             const int idx = p < c1 ? sel[p] : -1;
             koff[th] = idx >= 0 ? (uint32_t)idx * (kDqk * 2) : 0x80000000u;
         }
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const int p = t0 + slot_row(G, r);
+            const int p = w0 + slot_row(G, r);
             const int idx = p < c1 ? sel[p] : -1;
             voff[r] = idx >= 0 ? (uint32_t)idx * (kDqk * 2) : 0x80000000u;
         }
+        // q is bf16 already: used exactly as the B operand; the scale is applied to S.
+        u32x4 qf[KU];
+        const uint16_t* qrow = q + ((size_t)b * H + h) * kDqk;
+#pragma unroll
+        for (int u = 0; u < KU; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u + 8 * G);
+
+        const __amdgpu_buffer_rsrc_t cr =
+            make_rsrc(latent + (size_t)b * S_max * kDqk, (uint32_t)S_max * kDqk * 2u);
+        u32x4 kf[2][KU], vr[4][8];
+#pragma unroll
+        for (int th = 0; th < 2; ++th)
+#pragma unroll
+            for (int u = 0; u < KU; ++u) kf[th][u] = buf_load16(cr, koff[th] + (32 * u + 8 * G) * 2);
+#pragma unroll
+        for (int dq = 0; dq < 4; ++dq)
+#pragma unroll
+            for (int r = 0; r < 8; ++r) vr[dq][r] = buf_load16(cr, voff[r] + (128 * dq + 8 * n) * 2);
+
         f32x4 sc[2];
 #pragma unroll
         for (int th = 0; th < 2; ++th) {
             sc[th] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < KU; ++u) {
-                const u32x4 kf = buf_load16(cr, koff[th] + (32 * u + 8 * G) * 2);
-                sc[th] = mfma16(kf, qf[u], sc[th]);
-            }
+            for (int u = 0; u < KU; ++u) sc[th] = mfma16(kf[th][u], qf[u], sc[th]);
         }
-        const bool tail = (t0 + 32 > c1);
 #pragma unroll
         for (int th = 0; th < 2; ++th)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 sc[th][i] *= qscale;
-                if (tail && t0 + 16 * th + 4 * G + i >= c1) sc[th][i] = -INFINITY;
+                if (w0 + 16 * th + 4 * G + i >= c1) sc[th][i] = -INFINITY;
             }
         float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                          fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-        mx = fmaxf(mx, wave_shfl_xor(mx, 16));
-        mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
+        mx = rows4_max(mx);                     // finite: row w0 < c1 is visible
         float p[2][4];
         float ls = 0.f;
 #pragma unroll
         for (int th = 0; th < 2; ++th)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[th][i] = fast_exp2(sc[th][i] - m_new);
+                p[th][i] = fast_exp2(sc[th][i] - mx);
                 ls += p[th][i];
             }
-        ls += wave_shfl_xor(ls, 16);
-        ls += wave_shfl_xor(ls, 32);
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
+        ls = rows4_sum(ls);
         u32x4 pb;
         pb[0] = pack_bf16x2(p[0][0], p[0][1]);
         pb[1] = pack_bf16x2(p[0][2], p[0][3]);
@@ -511,30 +519,47 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
         pb[3] = pack_bf16x2(p[1][2], p[1][3]);
 #pragma unroll
         for (int dq = 0; dq < 4; ++dq) {
-            u32x4 vreg[8];
+            f32x4 o[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) vreg[r] = buf_load16(cr, voff[r] + (128 * dq + 8 * n) * 2);
+            for (int t = 0; t < 8; ++t) o[t] = mfma16(column_of(vr[dq], t), pb, f32x4{0.f, 0.f, 0.f, 0.f});
+            // this lane holds head n, d = 128 dq + 8 (4 G + i) + t
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                o[dq][t] *= alpha;
-                o[dq][t] = mfma16(column_of(vreg, t), pb, o[dq][t]);
+            for (int i = 0; i < 4; ++i) {
+                float* dst = &o_s[wave][n][128 * dq + 8 * (4 * G + i)];
+                *reinterpret_cast<f32x4*>(dst) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
+                *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
             }
         }
-    }
-
-    const size_t idx = ((size_t)b * H + h) * n_chunks + chunk;
-    float* po = part_o + idx * kDv;
-#pragma unroll
-    for (int dq = 0; dq < 4; ++dq)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d0 = 128 * dq + 8 * (4 * G + i);   // this lane holds d = d0 + t
-            *reinterpret_cast<f32x4*>(po + d0) = f32x4{o[dq][0][i], o[dq][1][i], o[dq][2][i], o[dq][3][i]};
-            *reinterpret_cast<f32x4*>(po + d0 + 4) = f32x4{o[dq][4][i], o[dq][5][i], o[dq][6][i], o[dq][7][i]};
+        if (G == 0) {
+            ml_s[wave][n][0] = mx;
+            ml_s[wave][n][1] = ls;
         }
-    if (G == 0) {
-        part_ml[idx * 2] = m_run;
-        part_ml[idx * 2 + 1] = l_run;
+    }
+    __syncthreads();
+
+    // ---- merge the waves' states: thread -> (head hh, 32 dims)
+    const int nw = (c1 - c0 + 31) / 32;         // waves that held rows
+    const int hh = tid >> 4, dseg = (tid & 15) * 32;
+    float M = -INFINITY;
+    for (int w = 0; w < nw; ++w) M = fmaxf(M, ml_s[w][hh][0]);
+    float den = 0.f;
+    f32x4 acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < nw; ++w) {
+        const float wt = fast_exp2(ml_s[w][hh][0] - M);
+        den += wt * ml_s[w][hh][1];
+        const f32x4* src = reinterpret_cast<const f32x4*>(&o_s[w][hh][dseg]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += wt * src[e];
+    }
+    const size_t idx = ((size_t)b * H + hb * 16 + hh) * n_chunks + chunk;
+    f32x4* po = reinterpret_cast<f32x4*>(part_o + idx * kDv + dseg);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) po[e] = acc[e];
+    if ((tid & 15) == 0) {
+        part_ml[idx * 2] = M;
+        part_ml[idx * 2 + 1] = den;
     }
 }
 
@@ -595,7 +620,7 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
                        seq_lens, S_max, S_stride, top_k, info, counts, nkc);
     hipLaunchKernelGGL(topk_write_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores,
                        seq_lens, S_max, S_stride, top_k, info, counts, nkc, topk_idx);
-    hipLaunchKernelGGL(sparse_attn_kernel, dim3(lay.n_chunks, H / 16, B), dim3(64), 0, s,
+    hipLaunchKernelGGL(sparse_attn_kernel, dim3(lay.n_chunks, H / 16, B), dim3(64 * kAttnWaves), 0, s,
                        (const uint16_t*)q, (const uint16_t*)latent, topk_idx, seq_lens, H, S_max,
                        top_k, scale * kLog2e, po, pml, lay.n_chunks);
     const int BH = B * H;
