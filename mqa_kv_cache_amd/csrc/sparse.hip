@@ -18,9 +18,11 @@
 // 3. sparse_attn_kernel: MQA attention of the H heads over the gathered
 //    latent rows (the indexed rows are read straight from the cache; no copy
 //    of the selection is made).  Same MFMA structure as the dense decode:
-//    S^T = C . Q^T over 576 dims, softmax, O^T = C[:, :512]^T . P^T; a
-//    workgroup covers 16 heads and 128 selected rows (32 per wave, merged in
-//    LDS) and writes a partial (m, l, o) that combine_partials_kernel merges.
+//    S^T = C . Q^T over 576 dims, online softmax, O^T += C[:, :512]^T . P^T;
+//    a workgroup covers 32 heads and 128 selected rows staged through LDS and
+//    writes a partial (m, l, o) per head that combine_partials_kernel merges.
+#include <type_traits>
+
 #include "device_common.h"
 #include "combine.h"
 
@@ -419,147 +421,212 @@ __global__ __launch_bounds__(kChunkThreads) void topk_write_kernel(
 // ---------------------------------------------------------------------------
 // 3. attention over the selected latent rows
 // ---------------------------------------------------------------------------
-// One workgroup per (128 selected rows, 16 heads, batch row); wave w takes
-// rows 32 w .. 32 w + 31 of the chunk.  A wave first reads its row indices,
-// then issues every K and V fragment load of its rows at once (one round
-// trip to L2/HBM instead of one per k-step group), computes
+// One workgroup per (128 selected rows, 32 heads, batch row), two waves of 16
+// heads.  The gathered latent rows are staged in LDS in four 32-row
+// sub-chunks, all requested at once and copied straight from global memory
+// by buffer loads into LDS, so each row is fetched once per 32 heads instead
+// of once per 16 and per operand, and the gather latency is paid once.  Per sub-chunk each wave computes
 //   S^T[32 rows][16 heads] = C . Q^T   (18 k-steps of 16x16x32 bf16 MFMA)
-// and its own softmax state over the 32 rows, then
-//   O^T[512][16 heads] = C[:, :512]^T . P^T.
-// The four waves' states are merged in LDS (log-sum-exp) into one partial
-// per (chunk, head), which combine_partials_kernel merges over the chunks.
-constexpr int kAttnWaves = kRowsPerChunk / 32;
-constexpr int kOStride = kDv + 4;   // LDS floats per head row (padded against bank conflicts)
+// folds it into its running softmax state and accumulates
+//   O^T[512][16 heads] += C[:, :512]^T . P^T,
+// and at the end writes one partial per (chunk, head) for
+// combine_partials_kernel.
+constexpr int kAttnWaves = 2;                        // 16 heads each
+constexpr int kSubRows = 32;                         // rows per LDS sub-chunk
+constexpr int kRowBytes = kDqk * 2;                  // 1152
+constexpr int kRowStride = kRowBytes + 16;           // padded: 8 consecutive rows hit distinct banks
+constexpr int kSubCopies = (kSubRows * kRowStride + 1023) / 1024;   // 1 KB copies per sub-chunk
+constexpr int kSubBytes = kSubCopies * 1024;         // the last copy spills into slack nothing reads
+
+__device__ __forceinline__ void sparse_sub_step(const uint8_t* rows, const u32x4 (&qf)[kDqk / 32],
+                                                f32x4 (&o)[4][8], float& m_run, float& l_run,
+                                                int p0, int c1, float qscale, int G, int n) {
+    constexpr int KU = kDqk / 32;
+    const uint8_t* kb = rows + n * kRowStride + 16 * G;
+    f32x4 sc[2];
+#pragma unroll
+    for (int th = 0; th < 2; ++th) {
+        sc[th] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+            sc[th] = mfma16(*reinterpret_cast<const u32x4*>(kb + 16 * th * kRowStride + 64 * u), qf[u], sc[th]);
+    }
+#pragma unroll
+    for (int th = 0; th < 2; ++th)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sc[th][i] *= qscale;
+            if (p0 + 16 * th + 4 * G + i >= c1) sc[th][i] = -INFINITY;
+        }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = rows4_max(mx);                   // finite: row p0 < c1 is visible
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f)) {   // lazy rescale (probabilities < 2^8)
+        asm volatile("" ::: "memory");
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int dq = 0; dq < 4; ++dq)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) o[dq][t] *= alpha;
+        m_run = m_new;
+    }
+    float pr[2][4];
+    float ls = 0.f;
+#pragma unroll
+    for (int th = 0; th < 2; ++th)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pr[th][i] = fast_exp2(sc[th][i] - m_run);
+            ls += pr[th][i];
+        }
+    l_run += rows4_sum(ls);
+    u32x4 pb;
+    pb[0] = pack_bf16x2(pr[0][0], pr[0][1]);
+    pb[1] = pack_bf16x2(pr[0][2], pr[0][3]);
+    pb[2] = pack_bf16x2(pr[1][0], pr[1][1]);
+    pb[3] = pack_bf16x2(pr[1][2], pr[1][3]);
+#pragma unroll
+    for (int dq = 0; dq < 4; ++dq) {
+        u32x4 vr[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            vr[r] = *reinterpret_cast<const u32x4*>(rows + slot_row(G, r) * kRowStride + (128 * dq + 8 * n) * 2);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[dq][t] = mfma16(column_of(vr, t), pb, o[dq][t]);
+    }
+}
 
 __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ seq_lens, int H, int S_max,
     int top_k, float qscale, float* __restrict__ part_o, float* __restrict__ part_ml,
     int n_chunks) {
-    constexpr int KU = kDqk / 32;   // 18 MFMA k-steps for the scores
-    __shared__ __attribute__((aligned(16))) float o_s[kAttnWaves][16][kOStride];
-    __shared__ float ml_s[kAttnWaves][16][2];
+    constexpr int KU = kDqk / 32;
+    // one buffer per sub-chunk, as separate LDS objects (the compiler then
+    // knows a read does not alias the copies still in flight)
+    __shared__ __attribute__((aligned(16))) uint8_t rows0[kSubBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t rows1[kSubBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t rows2[kSubBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t rows3[kSubBytes];
+    __shared__ int32_t sel_s[kRowsPerChunk];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = lane >> 4, n = lane & 15;
-    const int chunk = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
+    const int chunk = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
     const int L = min(max(seq_lens[b], 1), S_max);
     const int k = min(top_k, L);
     const int c0 = chunk * kRowsPerChunk;
     if (c0 >= k) return;                        // whole workgroup
     const int c1 = min(c0 + kRowsPerChunk, k);
-    const int w0 = c0 + 32 * wave;
-    const int h = hb * 16 + n;
+    const int nsub = (c1 - c0 + kSubRows - 1) / kSubRows;
+    const int h = hg * (16 * kAttnWaves) + 16 * wave + n;
+    const bool heads = hg * (16 * kAttnWaves) + 16 * wave < H;   // wave-uniform (H % 16 == 0)
 
-    if (w0 < c1) {
-        const int32_t* sel = topk_idx + (size_t)b * top_k;
-        uint32_t koff[2], voff[8];
-#pragma unroll
-        for (int th = 0; th < 2; ++th) {
-            const int p = w0 + 16 * th + n;
-            const int idx = p < c1 ? sel[p] : -1;
-            koff[th] = idx >= 0 ? (uint32_t)idx * (kDqk * 2) : 0x80000000u;
-        }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int p = w0 + slot_row(G, r);
-            const int idx = p < c1 ? sel[p] : -1;
-            voff[r] = idx >= 0 ? (uint32_t)idx * (kDqk * 2) : 0x80000000u;
-        }
-        // q is bf16 already: used exactly as the B operand; the scale is applied to S.
-        u32x4 qf[KU];
-        const uint16_t* qrow = q + ((size_t)b * H + h) * kDqk;
-#pragma unroll
-        for (int u = 0; u < KU; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u + 8 * G);
-
-        const __amdgpu_buffer_rsrc_t cr =
-            make_rsrc(latent + (size_t)b * S_max * kDqk, (uint32_t)S_max * kDqk * 2u);
-        u32x4 kf[2][KU], vr[4][8];
-#pragma unroll
-        for (int th = 0; th < 2; ++th)
-#pragma unroll
-            for (int u = 0; u < KU; ++u) kf[th][u] = buf_load16(cr, koff[th] + (32 * u + 8 * G) * 2);
-#pragma unroll
-        for (int dq = 0; dq < 4; ++dq)
-#pragma unroll
-            for (int r = 0; r < 8; ++r) vr[dq][r] = buf_load16(cr, voff[r] + (128 * dq + 8 * n) * 2);
-
-        f32x4 sc[2];
-#pragma unroll
-        for (int th = 0; th < 2; ++th) {
-            sc[th] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int u = 0; u < KU; ++u) sc[th] = mfma16(kf[th][u], qf[u], sc[th]);
-        }
-#pragma unroll
-        for (int th = 0; th < 2; ++th)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sc[th][i] *= qscale;
-                if (w0 + 16 * th + 4 * G + i >= c1) sc[th][i] = -INFINITY;
-            }
-        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-        mx = rows4_max(mx);                     // finite: row w0 < c1 is visible
-        float p[2][4];
-        float ls = 0.f;
-#pragma unroll
-        for (int th = 0; th < 2; ++th)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[th][i] = fast_exp2(sc[th][i] - mx);
-                ls += p[th][i];
-            }
-        ls = rows4_sum(ls);
-        u32x4 pb;
-        pb[0] = pack_bf16x2(p[0][0], p[0][1]);
-        pb[1] = pack_bf16x2(p[0][2], p[0][3]);
-        pb[2] = pack_bf16x2(p[1][0], p[1][1]);
-        pb[3] = pack_bf16x2(p[1][2], p[1][3]);
-#pragma unroll
-        for (int dq = 0; dq < 4; ++dq) {
-            f32x4 o[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) o[t] = mfma16(column_of(vr[dq], t), pb, f32x4{0.f, 0.f, 0.f, 0.f});
-            // this lane holds head n, d = 128 dq + 8 (4 G + i) + t
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float* dst = &o_s[wave][n][128 * dq + 8 * (4 * G + i)];
-                *reinterpret_cast<f32x4*>(dst) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
-                *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
-            }
-        }
-        if (G == 0) {
-            ml_s[wave][n][0] = mx;
-            ml_s[wave][n][1] = ls;
-        }
-    }
+    for (int i = tid; i < kRowsPerChunk; i += 64 * kAttnWaves)
+        sel_s[i] = c0 + i < c1 ? topk_idx[(size_t)b * top_k + c0 + i] : -1;
     __syncthreads();
 
-    // ---- merge the waves' states: thread -> (head hh, 32 dims)
-    const int nw = (c1 - c0 + 31) / 32;         // waves that held rows
-    const int hh = tid >> 4, dseg = (tid & 15) * 32;
-    float M = -INFINITY;
-    for (int w = 0; w < nw; ++w) M = fmaxf(M, ml_s[w][hh][0]);
-    float den = 0.f;
-    f32x4 acc[8];
+    const __amdgpu_buffer_rsrc_t cr =
+        make_rsrc(latent + (size_t)b * S_max * kDqk, (uint32_t)S_max * kDqk * 2u);
+    // This wave's copies: copy j = kAttnWaves * i + wave fills LDS bytes
+    // [1024 j, +1024) of a sub-chunk buffer, lane l the 16 bytes at 1024 j + 16 l,
+    // i.e. row r = x / kRowStride, column x mod kRowStride.  The (row, column)
+    // of each of the lane's copies is the same for every sub-chunk; only the
+    // row index read from sel_s changes, and those reads are batched.
+    constexpr int kCopiesPerWave = (kSubCopies + kAttnWaves - 1) / kAttnWaves;
+    int rr[kCopiesPerWave], cc[kCopiesPerWave];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int w = 0; w < nw; ++w) {
-        const float wt = fast_exp2(ml_s[w][hh][0] - M);
-        den += wt * ml_s[w][hh][1];
-        const f32x4* src = reinterpret_cast<const f32x4*>(&o_s[w][hh][dseg]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += wt * src[e];
+    for (int i = 0; i < kCopiesPerWave; ++i) {
+        const int x = 1024 * (kAttnWaves * i + wave) + 16 * lane;
+        rr[i] = x / kRowStride;
+        cc[i] = x - rr[i] * kRowStride;
     }
-    const size_t idx = ((size_t)b * H + hb * 16 + hh) * n_chunks + chunk;
-    f32x4* po = reinterpret_cast<f32x4*>(part_o + idx * kDv + dseg);
+    auto copy_sub = [&](int s, uint8_t* dst) {
+        int idx[kCopiesPerWave];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) po[e] = acc[e];
-    if ((tid & 15) == 0) {
-        part_ml[idx * 2] = M;
-        part_ml[idx * 2 + 1] = den;
+        for (int i = 0; i < kCopiesPerWave; ++i) idx[i] = sel_s[kSubRows * s + min(rr[i], kSubRows - 1)];
+        int wv = wave;
+        asm volatile("" : "+s"(wv));
+#pragma unroll
+        for (int i = 0; i < kCopiesPerWave; ++i) {
+            const int j = kAttnWaves * i + wv;
+            if (j < kSubCopies) {
+                const bool ok = rr[i] < kSubRows && cc[i] < kRowBytes && idx[i] >= 0;
+                const uint32_t voff = ok ? (uint32_t)idx[i] * kRowBytes + (uint32_t)cc[i] : 0x80000000u;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, dst + 1024 * j, 16, voff, 0, 0, 0);
+            }
+        }
+    };
+
+    // (a wave past the last head still copies its share and meets the barriers)
+    u32x4 qf[KU];
+    const uint16_t* qrow = q + ((size_t)b * H + (heads ? h : 0)) * kDqk;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u + 8 * G);
+    // q is complete before the copies are issued: the compiler's wait counts
+    // do not include loads into LDS, so a wait for q placed after them would
+    // also wait for every copy
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);
+    // all four sub-chunks are requested at once: one gather latency per chunk
+    // (rows past the selection read as zeros without traffic)
+    copy_sub(0, rows0);
+    copy_sub(1, rows1);
+    copy_sub(2, rows2);
+    copy_sub(3, rows3);
+
+    f32x4 o[4][8];
+#pragma unroll
+    for (int dq = 0; dq < 4; ++dq)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[dq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // Sub-chunk s is complete once at most the copies of the later sub-chunks
+    // are outstanding (every wave issues at least kCopiesMin per sub-chunk;
+    // vmcnt counts in issue order); a plain s_barrier then makes every wave's
+    // copies visible.  (__syncthreads would add a vmcnt(0) for its fence and
+    // wait for all four sub-chunks.)  The asm memory clobber keeps the LDS
+    // reads below the barrier.
+    constexpr int kCopiesMin = kSubCopies / kAttnWaves;
+    static_assert(3 * kCopiesMin < 64, "vmcnt range");
+    auto wait_sub = [&](auto later) {   // later: copies of later sub-chunks allowed in flight
+        constexpr int v = decltype(later)::value;
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (v & 15) | ((v >> 4) << 14));
+        asm volatile("s_barrier" ::: "memory");
+    };
+    wait_sub(std::integral_constant<int, 3 * kCopiesMin>{});
+    if (heads) sparse_sub_step(rows0, qf, o, m_run, l_run, c0, c1, qscale, G, n);
+    if (nsub > 1) {
+        wait_sub(std::integral_constant<int, 2 * kCopiesMin>{});
+        if (heads) sparse_sub_step(rows1, qf, o, m_run, l_run, c0 + kSubRows, c1, qscale, G, n);
+    }
+    if (nsub > 2) {
+        wait_sub(std::integral_constant<int, kCopiesMin>{});
+        if (heads) sparse_sub_step(rows2, qf, o, m_run, l_run, c0 + 2 * kSubRows, c1, qscale, G, n);
+    }
+    if (nsub > 3) {
+        wait_sub(std::integral_constant<int, 0>{});
+        if (heads) sparse_sub_step(rows3, qf, o, m_run, l_run, c0 + 3 * kSubRows, c1, qscale, G, n);
+    }
+    if (!heads) return;
+
+    const size_t idx = ((size_t)b * H + h) * n_chunks + chunk;
+    float* po = part_o + idx * kDv;
+#pragma unroll
+    for (int dq = 0; dq < 4; ++dq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 128 * dq + 8 * (4 * G + i);   // this lane holds d = d0 + t
+            *reinterpret_cast<f32x4*>(po + d0) = f32x4{o[dq][0][i], o[dq][1][i], o[dq][2][i], o[dq][3][i]};
+            *reinterpret_cast<f32x4*>(po + d0 + 4) = f32x4{o[dq][4][i], o[dq][5][i], o[dq][6][i], o[dq][7][i]};
+        }
+    if (G == 0) {
+        part_ml[idx * 2] = m_run;
+        part_ml[idx * 2 + 1] = l_run;
     }
 }
 
@@ -620,7 +687,8 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
                        seq_lens, S_max, S_stride, top_k, info, counts, nkc);
     hipLaunchKernelGGL(topk_write_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores,
                        seq_lens, S_max, S_stride, top_k, info, counts, nkc, topk_idx);
-    hipLaunchKernelGGL(sparse_attn_kernel, dim3(lay.n_chunks, H / 16, B), dim3(64 * kAttnWaves), 0, s,
+    hipLaunchKernelGGL(sparse_attn_kernel, dim3(lay.n_chunks, (H + 16 * kAttnWaves - 1) / (16 * kAttnWaves), B),
+                       dim3(64 * kAttnWaves), 0, s,
                        (const uint16_t*)q, (const uint16_t*)latent, topk_idx, seq_lens, H, S_max,
                        top_k, scale * kLog2e, po, pml, lay.n_chunks);
     const int BH = B * H;
