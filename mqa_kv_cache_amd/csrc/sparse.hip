@@ -35,6 +35,21 @@ constexpr int kRowsPerChunk = 128;   // selected rows per attention wave
 constexpr int kCandCap = 8192;       // LDS candidates of the threshold bin
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Sum over each group of four lanes, every lane receiving it (DPP quad
+// permutations xor 1 and xor 2, no LDS round trip).  The terms here are sums
+// of exact bf16 x bf16 products, so the fp64 result does not depend on the
+// order.
+template <int CTRL>
+__device__ __forceinline__ double dpp_add(double v) {
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false);
+    return v + __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double quad_sum(double v) {
+    // quad_perm [1,0,3,2] = 0xB1 (lane ^ 1), [2,3,0,1] = 0x4E (lane ^ 2)
+    return dpp_add<0x4E>(dpp_add<0xB1>(v));
+}
+
 __global__ void zero_u32_kernel(uint32_t* __restrict__ p, int n) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = 0u;
@@ -49,7 +64,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     float* __restrict__ scores, uint32_t* __restrict__ hist) {
     __shared__ uint32_t lh[kHistBins];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int G = lane >> 4, n = lane & 15;
+    // four lanes per key row, 32 dims (64 bytes) each: lane -> row lr, quarter qq
+    const int lr = lane >> 2, qq = lane & 3;
     const int b = blockIdx.y;
     const int L = min(max(seq_lens[b], 1), S_max);
     const int r_begin = blockIdx.x * rows_per_block;
@@ -57,42 +73,64 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     for (int i = tid; i < kHistBins; i += 256) lh[i] = 0u;
     __syncthreads();
     if (r_begin < r_end) {
-        const u32x4 qraw = *reinterpret_cast<const u32x4*>(q_index + (size_t)b * kDidx + 8 * n);
-        double qv[8];
+        double qv[32];
+        const uint16_t* qrow = q_index + (size_t)b * kDidx + 32 * qq;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            qv[2 * j] = (double)bf16_lo(qraw[j]);
-            qv[2 * j + 1] = (double)bf16_hi(qraw[j]);
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 qraw = *reinterpret_cast<const u32x4*>(qrow + 8 * c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                qv[8 * c + 2 * j] = (double)bf16_lo(qraw[j]);
+                qv[8 * c + 2 * j + 1] = (double)bf16_hi(qraw[j]);
+            }
         }
         const __amdgpu_buffer_rsrc_t kr =
             make_rsrc(k_index + (size_t)b * S_max * kDidx, (uint32_t)L * kDidx * 2u);
         float* srow = scores + (size_t)b * S_stride;
-        constexpr int RA = 16;   // row groups per wave step: 64 rows, 16 KB in flight per wave
-        for (int r = r_begin + 4 * RA * wave; r < r_end; r += 4 * RA * 4) {
-            u32x4 raw[RA];
+        constexpr int RA = 4;   // 16-row groups per wave step: 64 rows, 16 KB per register set
+        // two register sets: the next step's rows are requested before this
+        // step's rows are reduced
+        auto load = [&](u32x4 (&raw)[RA][4], int r) {
 #pragma unroll
             for (int a = 0; a < RA; ++a)
-                raw[a] = buf_load16(kr, (uint32_t)(((r + 4 * a + G) * kDidx + 8 * n) * 2));
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    raw[a][c] = buf_load16(kr, (uint32_t)(((r + 16 * a + lr) * kDidx + 32 * qq + 8 * c) * 2));
+        };
+        auto reduce = [&](const u32x4 (&raw)[RA][4], int r) {
 #pragma unroll
             for (int a = 0; a < RA; ++a) {
                 double acc = 0.0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc = fma(qv[2 * j], (double)bf16_lo(raw[a][j]), acc);
-                    acc = fma(qv[2 * j + 1], (double)bf16_hi(raw[a][j]), acc);
-                }
-                acc += __shfl_xor(acc, 8, 64);
-                acc += __shfl_xor(acc, 4, 64);
-                acc += __shfl_xor(acc, 2, 64);
-                acc += __shfl_xor(acc, 1, 64);
-                const int row = r + 4 * a + G;
-                if (n == 0 && row < r_end) {
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc = fma(qv[8 * c + 2 * j], (double)bf16_lo(raw[a][c][j]), acc);
+                        acc = fma(qv[8 * c + 2 * j + 1], (double)bf16_hi(raw[a][c][j]), acc);
+                    }
+                acc = quad_sum(acc);
+                const int row = r + 16 * a + lr;
+                if (qq == 0 && row < r_end) {
                     const float s = acc > 0.0 ? (float)acc : 0.0f;   // ReLU, +0 for ties
                     srow[row] = s;
                     const uint32_t bin = __float_as_uint(s) >> 20;
                     if (bin) atomicAdd(&lh[bin], 1u);
                 }
             }
+        };
+        constexpr int kWaveRows = 16 * RA;
+        constexpr int kStep = kWaveRows * 4;   // rows per workgroup step (4 waves)
+        u32x4 ra[RA][4], rb[RA][4];
+        int r = r_begin + kWaveRows * wave;
+        if (r < r_end) load(ra, r);
+        while (r < r_end) {
+            if (r + kStep < r_end) load(rb, r + kStep);
+            reduce(ra, r);
+            r += kStep;
+            if (r >= r_end) break;
+            if (r + kStep < r_end) load(ra, r + kStep);
+            reduce(rb, r);
+            r += kStep;
         }
     }
     __syncthreads();
