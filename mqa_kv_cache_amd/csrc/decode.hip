@@ -67,12 +67,12 @@ __device__ __forceinline__ void load_tile(DecodeTile<D>& t, __amdgpu_buffer_rsrc
     for (int th = 0; th < 2; ++th)
 #pragma unroll
         for (int u = 0; u < DecodeTile<D>::KU; ++u)
-            t.k[th][u] = buf_load16(kr, (uint32_t)(((t0 + 16 * th + n) * D + 32 * u + 8 * G) * 2));
+            t.k[th][u] = buf_load16_nt(kr, (uint32_t)(((t0 + 16 * th + n) * D + 32 * u + 8 * G) * 2));
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const uint32_t off = (n < VN) ? (uint32_t)(((t0 + slot_row(G, r)) * D + 8 * n) * 2)
                                       : 0x80000000u;  // out of range -> zeros
-        t.v[r] = buf_load16(vr, off);
+        t.v[r] = buf_load16_nt(vr, off);
     }
 }
 

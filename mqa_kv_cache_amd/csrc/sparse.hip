@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
             for (int a = 0; a < RA; ++a)
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    raw[a][c] = buf_load16(kr, (uint32_t)(((r + 16 * a + lr) * kDidx + 32 * qq + 8 * c) * 2));
+                    raw[a][c] = buf_load16_nt(kr, (uint32_t)(((r + 16 * a + lr) * kDidx + 32 * qq + 8 * c) * 2));
         };
         auto reduce = [&](const u32x4 (&raw)[RA][4], int r) {
 #pragma unroll
