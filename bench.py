@@ -186,7 +186,9 @@ def bench_sparse(cfg, steps, warmup):
     import mqa_kv_cache_amd as m
     from workloads import device_randn_bf16
     B, H, S, k = cfg.B, cfg.H, cfg.S_max, cfg.top_k
-    nsets = 2
+    # three input sets rotate: a call reads ~137 MB, so the 256 MB Infinity
+    # Cache cannot hold the set that comes round again
+    nsets = 3
     sets = [(device_randn_bf16((B, H, cfg.Dqk), cfg.seed * 100 + 10 * i + 1),
              device_randn_bf16((B, S, cfg.Dqk), cfg.seed * 100 + 10 * i + 2),
              device_randn_bf16((B, cfg.D_idx), cfg.seed * 100 + 10 * i + 3),
@@ -219,15 +221,18 @@ def bench_rope(cfg, steps, warmup):
     import mqa_kv_cache_amd as m
     from workloads import device_randn_bf16
     T, Hq, D = cfg.T, cfg.Hq, cfg.D
-    x = device_randn_bf16((T, Hq, D), 7)
-    y = torch.empty_like(x)
+    # four (input, output) pairs rotate (512 MiB) so the 256 MB Infinity Cache
+    # cannot serve a pair that comes round again
+    nsets = 4
+    xs = [device_randn_bf16((T, Hq, D), 7 + i) for i in range(nsets)]
+    ys = [torch.empty_like(xs[0]) for _ in range(nsets)]
     pos = torch.arange(T, dtype=torch.int32, device="cuda")
     byts = 2 * T * Hq * D * 2
     timer = EventTimer()
 
     def step(i):
         timer.start()
-        m.rope_apply(x, pos, cfg.rope(), out=y)
+        m.rope_apply(xs[i % nsets], pos, cfg.rope(), out=ys[i % nsets])
         timer.stop()
 
     timed_loop(step, steps, warmup)

@@ -532,7 +532,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
         const int t = ks + key;
         u32x4 val = u32x4{0, 0, 0, 0};
         if (t < T) {
-            const u32x4 raw = *reinterpret_cast<const u32x4*>(k + in_base + (size_t)t * D + 8 * dc);
+            const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + in_base + (size_t)t * D + 8 * dc));
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 float xe = bf16_lo(raw[p]), xo = bf16_hi(raw[p]);
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
         for (int r = 0; r < 4; ++r) {
             const int t = ks + 4 * kg + r;
             u32x4 raw = u32x4{0, 0, 0, 0};
-            if (t < T) raw = *reinterpret_cast<const u32x4*>(v + in_base + (size_t)t * D + 8 * dc);
+            if (t < T) raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + in_base + (size_t)t * D + 8 * dc));
 #pragma unroll
             for (int j = 0; j < 4; ++j) r4[r][j] = pack_f16x2(bf16_lo(raw[j]), bf16_hi(raw[j]));
         }

@@ -1,17 +1,19 @@
 // Standalone RoPE ([transformer架构] §1.1 rotation, §1.2 PI / NTK / YaRN).
 //
-// One block covers a group of tokens.  The block first forms cos/sin of each
-// (token, frequency) once in LDS (fp64 angle, reduced, fp32 sincos, times the
-// YaRN amplitude), then every thread rotates 16-byte chunks (4 adjacent
-// pairs) of the (token, head) rows, so the transcendental work is shared by
-// all heads of a token.  The kernel is HBM-bound: each element is read once
-// and written once.
+// One block covers a group of tokens.  Each thread first requests up to
+// eight 16-byte chunks (4 adjacent pairs each) of the block's (token, head)
+// rows, then, while they are in flight, the block forms cos/sin of each
+// (token, frequency) once in LDS (fp64 angle, reduced, fp32 sincos, times
+// the YaRN amplitude), so the transcendental work is shared by all heads of
+// a token and hidden behind the loads.  The kernel is HBM-bound: each
+// element is read once and written once.
 #include "device_common.h"
 
 namespace gqa {
 namespace {
 
 constexpr int kRopeThreads = 256;
+constexpr int kRopeChunks = 8;        // 16-byte chunks per thread per pass
 constexpr int kRopeLdsFloats = 4096;  // per table (cos and sin): TB * half <= 4096
 
 __global__ __launch_bounds__(kRopeThreads) void rope_apply_kernel(
@@ -22,39 +24,54 @@ __global__ __launch_bounds__(kRopeThreads) void rope_apply_kernel(
     __shared__ float cs_s[kRopeLdsFloats];
     const int half = rope.half;
     const int64_t tok0 = (int64_t)blockIdx.x * tok_per_block;
-    for (int e = threadIdx.x; e < tok_per_block * half; e += kRopeThreads) {
-        const int tl = e / half, i = e - tl * half;
-        const int64_t tok = tok0 + tl;
-        if (tok < n_tok) {
-            float c, s;
-            rope_cos_sin(rope, positions ? (double)positions[tok] : (double)tok, i, c, s);
-            cs_c[e] = c;
-            cs_s[e] = s;
-        }
-    }
-    __syncthreads();
     const int chunks = head_dim / 8;
     const int items = n_heads * chunks;
     const int rot_chunks = (2 * half) / 8;
-    for (int it = threadIdx.x; it < tok_per_block * items; it += kRopeThreads) {
-        const int tl = it / items;
-        const int rem = it - tl * items;
-        const int h = rem / chunks, c = rem - h * chunks;
-        const int64_t tok = tok0 + tl;
-        if (tok >= n_tok) continue;
-        const int64_t off = tok * stride_tok + (int64_t)h * stride_head + 8 * c;
-        u32x4 v = *reinterpret_cast<const u32x4*>(in + off);
-        if (c < rot_chunks) {
-            const float* cc = cs_c + tl * half + 4 * c;
-            const float* ss = cs_s + tl * half + 4 * c;
+    const int total = tok_per_block * items;
+    const int tid = threadIdx.x;
+    for (int base = 0; base < total; base += kRopeThreads * kRopeChunks) {
+        u32x4 v[kRopeChunks];
+        int64_t off[kRopeChunks];
+        int tl[kRopeChunks], cc[kRopeChunks];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const float xe = bf16_lo(v[p]), xo = bf16_hi(v[p]);
-                v[p] = pack_bf16x2(xe * cc[p] - xo * ss[p], xe * ss[p] + xo * cc[p]);
+        for (int k = 0; k < kRopeChunks; ++k) {
+            const int it = base + tid + kRopeThreads * k;
+            tl[k] = it / items;
+            const int rem = it - tl[k] * items;
+            const int h = rem / chunks;
+            cc[k] = rem - h * chunks;
+            const bool ok = it < total && tok0 + tl[k] < n_tok;
+            off[k] = ok ? (tok0 + tl[k]) * stride_tok + (int64_t)h * stride_head + 8 * cc[k] : -1;
+            if (ok) v[k] = *reinterpret_cast<const u32x4*>(in + off[k]);
+        }
+        if (base == 0) {
+            for (int e = tid; e < tok_per_block * half; e += kRopeThreads) {
+                const int t = e / half, i = e - t * half;
+                const int64_t tok = tok0 + t;
+                if (tok < n_tok) {
+                    float c, sn;
+                    rope_cos_sin(rope, positions ? (double)positions[tok] : (double)tok, i, c, sn);
+                    cs_c[e] = c;
+                    cs_s[e] = sn;
+                }
             }
-            *reinterpret_cast<u32x4*>(out + off) = v;
-        } else if (out != in) {
-            *reinterpret_cast<u32x4*>(out + off) = v;
+            __syncthreads();
+        }
+#pragma unroll
+        for (int k = 0; k < kRopeChunks; ++k) {
+            if (off[k] < 0) continue;
+            if (cc[k] < rot_chunks) {
+                const float* cp = cs_c + tl[k] * half + 4 * cc[k];
+                const float* sp = cs_s + tl[k] * half + 4 * cc[k];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float xe = bf16_lo(v[k][p]), xo = bf16_hi(v[k][p]);
+                    v[k][p] = pack_bf16x2(xe * cp[p] - xo * sp[p], xe * sp[p] + xo * cp[p]);
+                }
+                *reinterpret_cast<u32x4*>(out + off[k]) = v[k];
+            } else if (out != in) {
+                *reinterpret_cast<u32x4*>(out + off[k]) = v[k];
+            }
         }
     }
 }
@@ -67,7 +84,7 @@ hipError_t launch_rope_apply(const void* in, void* out, const int32_t* positions
                              int64_t stride_head, const RopeDev& rope, hipStream_t s) {
     if (n_tok == 0) return hipSuccess;
     const int items = n_heads * (head_dim / 8);
-    int tb = kRopeThreads / items;
+    int tb = kRopeThreads * kRopeChunks / items;
     if (tb < 1) tb = 1;
     if (tb > 64) tb = 64;
     if (rope.half > 0) {

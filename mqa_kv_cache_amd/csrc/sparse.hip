@@ -63,8 +63,9 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     const int32_t* __restrict__ seq_lens, int S_max, int S_stride, int rows_per_block,
     float* __restrict__ scores, uint32_t* __restrict__ hist) {
     __shared__ uint32_t lh[kHistBins];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // four lanes per key row, 32 dims (64 bytes) each: lane -> row lr, quarter qq
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // four lanes per key row, 32 dims each: lane -> row lr, quarter qq
     const int lr = lane >> 2, qq = lane & 3;
     const int b = blockIdx.y;
     const int L = min(max(seq_lens[b], 1), S_max);
@@ -73,21 +74,28 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     for (int i = tid; i < kHistBins; i += 256) lh[i] = 0u;
     __syncthreads();
     if (r_begin < r_end) {
+        // lane quarter qq holds dims 32 c + 8 qq + (0..7), c = 0..3, so each
+        // load instruction covers 64 contiguous bytes of each of 16 rows
         double qv[32];
-        const uint16_t* qrow = q_index + (size_t)b * kDidx + 32 * qq;
+        const uint16_t* qrow = q_index + (size_t)b * kDidx + 8 * qq;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const u32x4 qraw = *reinterpret_cast<const u32x4*>(qrow + 8 * c);
+            const u32x4 qraw = *reinterpret_cast<const u32x4*>(qrow + 32 * c);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 qv[8 * c + 2 * j] = (double)bf16_lo(qraw[j]);
                 qv[8 * c + 2 * j + 1] = (double)bf16_hi(qraw[j]);
             }
         }
-        const __amdgpu_buffer_rsrc_t kr =
-            make_rsrc(k_index + (size_t)b * S_max * kDidx, (uint32_t)L * kDidx * 2u);
-        float* srow = scores + (size_t)b * S_stride;
-        constexpr int RA = 4;   // 16-row groups per wave step: 64 rows, 16 KB per register set
+        // the descriptor covers exactly this block's rows: loads past them
+        // return zeros without memory traffic, so every load is unconditional
+        // and the compiler's wait counts stay exact across the loop
+        const int nrows = r_end - r_begin;
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(
+            k_index + ((size_t)b * S_max + r_begin) * kDidx, (uint32_t)nrows * kDidx * 2u);
+        const __amdgpu_buffer_rsrc_t sr =
+            make_rsrc(scores + (size_t)b * S_stride + r_begin, (uint32_t)nrows * 4u);
+        constexpr int RA = 2;   // 16-row groups per wave step: 32 rows, 8 KB per register set
         // two register sets: the next step's rows are requested before this
         // step's rows are reduced
         auto load = [&](u32x4 (&raw)[RA][4], int r) {
@@ -95,7 +103,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
             for (int a = 0; a < RA; ++a)
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    raw[a][c] = buf_load16_nt(kr, (uint32_t)(((r + 16 * a + lr) * kDidx + 32 * qq + 8 * c) * 2));
+                    raw[a][c] = buf_load16_nt(kr, (uint32_t)(((r + 16 * a + lr) * kDidx + 32 * c + 8 * qq) * 2));
         };
         auto reduce = [&](const u32x4 (&raw)[RA][4], int r) {
 #pragma unroll
@@ -109,29 +117,31 @@ __global__ __launch_bounds__(256) void indexer_kernel(
                         acc = fma(qv[8 * c + 2 * j + 1], (double)bf16_hi(raw[a][c][j]), acc);
                     }
                 acc = quad_sum(acc);
-                const int row = r + 16 * a + lr;
-                if (qq == 0 && row < r_end) {
-                    const float s = acc > 0.0 ? (float)acc : 0.0f;   // ReLU, +0 for ties
-                    srow[row] = s;
-                    const uint32_t bin = __float_as_uint(s) >> 20;
-                    if (bin) atomicAdd(&lh[bin], 1u);
-                }
+                const int row = r + 16 * a + lr;   // local to the block
+                const float sc = acc > 0.0 ? (float)acc : 0.0f;   // ReLU, +0 for ties
+                // every lane stores (lanes of a row's other quarters and rows
+                // past the block fall outside the descriptor and are dropped),
+                // so no branch around a memory access blurs the wait counts
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), sr,
+                                                      qq == 0 ? (uint32_t)row * 4u : 0x80000000u, 0, 0);
+                const uint32_t bin = __float_as_uint(sc) >> 20;
+                if (qq == 0 && row < nrows && bin) atomicAdd(&lh[bin], 1u);
             }
         };
         constexpr int kWaveRows = 16 * RA;
         constexpr int kStep = kWaveRows * 4;   // rows per workgroup step (4 waves)
         u32x4 ra[RA][4], rb[RA][4];
-        int r = r_begin + kWaveRows * wave;
-        if (r < r_end) load(ra, r);
-        while (r < r_end) {
-            if (r + kStep < r_end) load(rb, r + kStep);
+        const int n_steps = (nrows + kStep - 1) / kStep;   // uniform over the workgroup
+        int r = kWaveRows * wave;
+        load(ra, r);
+        for (int st = 0; st + 1 < n_steps; st += 2) {   // no early exit: one loop state
+            load(rb, r + kStep);
             reduce(ra, r);
-            r += kStep;
-            if (r >= r_end) break;
-            if (r + kStep < r_end) load(ra, r + kStep);
-            reduce(rb, r);
-            r += kStep;
+            load(ra, r + 2 * kStep);
+            reduce(rb, r + kStep);
+            r += 2 * kStep;
         }
+        if (n_steps & 1) reduce(ra, r);
     }
     __syncthreads();
     for (int i = tid; i < kHistBins; i += 256)
