@@ -49,31 +49,6 @@ def parse():
     return ap.parse_args()
 
 
-class EventTimer:
-    """Average duration of the work enqueued between start() and stop() on the
-    current stream, over many calls, from HIP events on that stream."""
-
-    def __init__(self):
-        import torch
-        self.torch = torch
-        self.pairs = []
-
-    def start(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.pairs.append([e, None])
-
-    def stop(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.pairs[-1][1] = e
-
-    def mean_ms(self):
-        self.torch.cuda.synchronize()
-        ts = [a.elapsed_time(b) for a, b in self.pairs]
-        return sum(ts) / len(ts)
-
-
 def timed_loop(fn, steps, warmup):
     """Run warmup calls, then time exactly `steps` calls bracketed by device syncs."""
     import torch
@@ -85,6 +60,24 @@ def timed_loop(fn, steps, warmup):
         fn(i)
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def region_ms(fn, steps, warmup):
+    """Mean GPU time per call of `steps` back-to-back calls of fn on the
+    current stream, from one HIP event pair around the whole region (events
+    between the calls would add their own packets to what is measured)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def source_hash(*names):
@@ -133,20 +126,19 @@ def bench_decode(cfg, steps, warmup, nsets, label):
     ws = torch.empty(m.gqa_decode_workspace_size(B, Hq, Hkv, D, S), dtype=torch.uint8, device="cuda")
     kv_bytes = int(lens.sum().item()) * Hkv * D * 2 * 2
     rope = cfg.rope()
-    timer = EventTimer()
 
-    def step(i, record=False):
+    def partial(i):
         q, k, v = sets[i % nsets]
-        if record:
-            timer.start()
         m.gqa_decode_partial(q, k, v, lens, cfg.scale, ws, q_rope=rope)
-        if record:
-            timer.stop()
+
+    def step(i):
+        partial(i)
         m.gqa_decode_combine(lens, B, Hq, Hkv, D, S, ws, out)
 
-    ms = timed_loop(lambda i: step(i, record=True), steps, warmup)
-    timer.pairs = timer.pairs[warmup:]
-    kern_ms = timer.mean_ms()
+    # whole steps (partial + combine), nothing else on the stream
+    ms = timed_loop(step, steps, warmup)
+    # the partial kernel alone, the same launches back to back
+    kern_ms = region_ms(partial, steps, warmup)
     log(f"[bench] {label}: step {ms * 1e3:.1f} us, partial kernel {kern_ms * 1e3:.1f} us, "
         f"{kv_bytes / ms / 1e6:.0f} GB/s")
     return dict(ms=ms, kern_ms=kern_ms, kv_bytes=kv_bytes, lens=lens.cpu().numpy(), sets=sets)
@@ -165,19 +157,14 @@ def bench_prefill(cfg, steps, warmup):
     ws = torch.empty(m.gqa_prefill_workspace_size(B, Hkv, T, D, cfg.rope()), dtype=torch.uint8,
                      device="cuda")
     flops = 2 * D * Hq * T * (T + 1) * B       # QK^T and PV over the causal triangle incl. diagonal
-    timer = EventTimer()
 
     def step(i):
-        timer.start()
         m.gqa_prefill_causal(q, k, v, cfg.scale, rope=cfg.rope(), out=out, workspace=ws)
-        timer.stop()
 
-    ms = timed_loop(step, max(steps // 2, 5), max(warmup // 2, 2))
-    timer.pairs = timer.pairs[max(warmup // 2, 2):]
-    ev_ms = timer.mean_ms()
+    ev_ms = region_ms(step, max(steps // 2, 5), max(warmup // 2, 2))
     tf = flops / ev_ms / 1e9
     log(f"[bench] prefill T={T}: {ev_ms * 1e3:.1f} us per call, {tf:.1f} TFLOP/s")
-    return dict(ms=ms, ev_ms=ev_ms, flops=flops, tflops=tf)
+    return dict(ev_ms=ev_ms, flops=flops, tflops=tf)
 
 
 def bench_sparse(cfg, steps, warmup):
@@ -200,17 +187,12 @@ def bench_sparse(cfg, steps, warmup):
     # algorithmic bytes: indexer keys + selected latent rows + q, q_index, outputs
     alg = (B * S * cfg.D_idx * 2 + B * k * cfg.Dqk * 2 + B * H * cfg.Dqk * 2 + B * cfg.D_idx * 2
            + B * k * 4 + B * H * cfg.Dv * 2)
-    timer = EventTimer()
 
     def step(i):
         q, lat, qi, ki = sets[i % nsets]
-        timer.start()
         m.topk_sparse_decode(q, lat, qi, ki, lens, k, cfg.scale, topk_idx=idx, out=out, workspace=ws)
-        timer.stop()
 
-    ms = timed_loop(step, steps, warmup)
-    timer.pairs = timer.pairs[warmup:]
-    ev_ms = timer.mean_ms()
+    ev_ms = region_ms(step, steps, warmup)
     log(f"[bench] sparse: {ev_ms * 1e3:.1f} us per call, {alg / ev_ms / 1e6:.0f} GB/s algorithmic")
     return dict(ms=ev_ms, alg_bytes=alg, gbs=alg / ev_ms / 1e6)
 
@@ -228,16 +210,11 @@ def bench_rope(cfg, steps, warmup):
     ys = [torch.empty_like(xs[0]) for _ in range(nsets)]
     pos = torch.arange(T, dtype=torch.int32, device="cuda")
     byts = 2 * T * Hq * D * 2
-    timer = EventTimer()
 
     def step(i):
-        timer.start()
         m.rope_apply(xs[i % nsets], pos, cfg.rope(), out=ys[i % nsets])
-        timer.stop()
 
-    timed_loop(step, steps, warmup)
-    timer.pairs = timer.pairs[warmup:]
-    ev_ms = timer.mean_ms()
+    ev_ms = region_ms(step, steps, warmup)
     log(f"[bench] rope_apply: {ev_ms * 1e3:.1f} us, {byts / ev_ms / 1e6:.0f} GB/s")
     return dict(ms=ev_ms, gbs=byts / ev_ms / 1e6)
 
