@@ -151,11 +151,12 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 // ---------------------------------------------------------------------------
 // 2. top-k selection, spread over (chunk, batch) workgroups:
 //    topk_candidates_kernel  first digit from the histogram; keys of the
-//                            threshold bin appended to a per-batch list
+//                            threshold bin copied to the chunk's own slice,
+//                            keys of higher bins counted per chunk
 //    topk_threshold_kernel   exact k-th key T from the candidates (or from
 //                            extra passes when the bin is too large), the
-//                            count above T and the number of ties to take
-//    topk_count_kernel       per-chunk counts of keys > T and == T
+//                            number of ties to take, and per chunk the
+//                            counts of keys > T and == T (from the slices)
 //    topk_write_kernel       ordered output: chunk prefix + in-chunk ranks
 // Keys are the bit patterns of non-negative fp32 scores, so unsigned order
 // is score order.
@@ -244,39 +245,67 @@ __device__ void first_digit(const uint32_t* hist_g, int b, int L, int k, uint32_
 
 // Keys of the threshold bin found in chunk c go to that chunk's own slice of
 // the candidate buffer (the chunk's index range), their number to
-// cand_cnt[b][c]: no cross-workgroup atomics.
+// cand_cnt[b][c], and the number of keys in higher bins to cand_above[b][c]:
+// no cross-workgroup atomics.  The chunk's keys are requested before the
+// histogram work so the two latencies overlap.
+constexpr int kKeysPerThread = kChunkKeys / kChunkThreads;   // 16
+
 __global__ __launch_bounds__(kChunkThreads) void topk_candidates_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist_g,
     const int32_t* __restrict__ seq_lens, int S_max, int S_stride, int top_k,
-    uint32_t* __restrict__ cand_g, uint32_t* __restrict__ cand_cnt, int n_chunks) {
+    uint32_t* __restrict__ cand_g, uint32_t* __restrict__ cand_cnt,
+    uint32_t* __restrict__ cand_above, int n_chunks) {
     __shared__ uint32_t h[kHistBins];
     __shared__ uint32_t wsum[kChunkThreads / 64];
     __shared__ uint32_t res[2];
     __shared__ uint32_t lcount;
+    __shared__ uint32_t labove;
     const int b = blockIdx.y, c = blockIdx.x;
     const int L = min(max(seq_lens[b], 1), S_max);
     const int k = min(top_k, L);
     const int c0 = c * kChunkKeys;
     if (k == L || c0 >= L) return;
-    if (threadIdx.x == 0) lcount = 0;
+    const int c1 = min(c0 + kChunkKeys, L);
+    const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride);
+    uint32_t kv[kKeysPerThread];
+#pragma unroll
+    for (int it = 0; it < kKeysPerThread; ++it) {
+        const int j = c0 + it * kChunkThreads + threadIdx.x;
+        kv[it] = j < c1 ? keys[j] : 0u;
+    }
+    if (threadIdx.x == 0) {
+        lcount = 0;
+        labove = 0;
+    }
     first_digit<kChunkThreads>(hist_g, b, L, k, h, wsum, res);
     const uint32_t B1 = res[0];
-    const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride);
-    const int c1 = min(c0 + kChunkKeys, L);
     uint32_t* cand = cand_g + (size_t)b * n_chunks * kChunkKeys + c0;
-    for (int j = c0 + threadIdx.x; j < c1; j += kChunkThreads) {
-        const uint32_t key = keys[j];
-        if ((key >> 20) == B1) cand[atomicAdd(&lcount, 1u)] = key;
+    uint32_t above = 0;
+#pragma unroll
+    for (int it = 0; it < kKeysPerThread; ++it) {
+        const int j = c0 + it * kChunkThreads + threadIdx.x;
+        const uint32_t bin = kv[it] >> 20;
+        if (j < c1) {
+            above += bin > B1;
+            if (bin == B1) cand[atomicAdd(&lcount, 1u)] = kv[it];
+        }
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) above += __shfl_xor(above, o, 64);
+    if ((threadIdx.x & 63) == 0) atomicAdd(&labove, above);
     __syncthreads();
-    if (threadIdx.x == 0) cand_cnt[(size_t)b * n_chunks + c] = lcount;
+    if (threadIdx.x == 0) {
+        cand_cnt[(size_t)b * n_chunks + c] = lcount;
+        cand_above[(size_t)b * n_chunks + c] = labove;
+    }
 }
 
 __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist_g,
     const int32_t* __restrict__ seq_lens, int S_max, int S_stride, int top_k,
-    const uint32_t* __restrict__ cand_g, const uint32_t* __restrict__ cand_cnt, int n_chunks,
-    SelInfo* __restrict__ info) {
+    const uint32_t* __restrict__ cand_g, const uint32_t* __restrict__ cand_cnt,
+    const uint32_t* __restrict__ cand_above, int n_chunks, SelInfo* __restrict__ info,
+    uint32_t* __restrict__ counts) {
     __shared__ uint32_t h[kHistBins];
     __shared__ uint32_t cand[kCandCap];
     __shared__ uint32_t wsum[kSelThreads / 64];
@@ -351,46 +380,31 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
         need -= res[1];
     }
     if (tid == 0) info[b] = SelInfo{T, need, B1, 0u};
-}
-
-__global__ __launch_bounds__(kChunkThreads) void topk_count_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int S_max,
-    int S_stride, int top_k, const SelInfo* __restrict__ info, uint32_t* __restrict__ counts,
-    int n_chunks) {
-    __shared__ uint32_t red[2][kChunkThreads / 64];
-    const int b = blockIdx.y, c = blockIdx.x;
-    const int L = min(max(seq_lens[b], 1), S_max);
-    const int k = min(top_k, L);
-    const int c0 = c * kChunkKeys;
-    if (k == L || c0 >= L) return;
-    const int c1 = min(c0 + kChunkKeys, L);
-    const uint32_t T = info[b].T;
-    const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride);
-    uint32_t gt = 0, eq = 0;
-    for (int j = c0 + threadIdx.x; j < c1; j += kChunkThreads) {
-        const uint32_t key = keys[j];
-        gt += key > T;
-        eq += key == T;
-    }
+    // per chunk: keys > T are the higher bins plus the slice's candidates
+    // above T; ties are the slice's keys equal to T (wave w takes chunks
+    // w, w + 16, ...)
+    {
+        const int lane = tid & 63, wave = tid >> 6;
+        for (int c = wave; c < nkc; c += kSelThreads / 64) {
+            const size_t ci = (size_t)b * n_chunks + c;
+            const uint32_t n_c = cand_cnt[ci];
+            const uint32_t* src = cand_g + ci * kChunkKeys;
+            uint32_t gt = 0, eq = 0;
+            for (uint32_t i = lane; i < n_c; i += 64) {
+                const uint32_t key = src[i];
+                gt += key > T;
+                eq += key == T;
+            }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        gt += __shfl_xor(gt, o, 64);
-        eq += __shfl_xor(eq, o, 64);
-    }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) {
-        red[0][wave] = gt;
-        red[1][wave] = eq;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t g2 = 0, e2 = 0;
-        for (int w = 0; w < kChunkThreads / 64; ++w) {
-            g2 += red[0][w];
-            e2 += red[1][w];
+            for (int o = 32; o >= 1; o >>= 1) {
+                gt += __shfl_xor(gt, o, 64);
+                eq += __shfl_xor(eq, o, 64);
+            }
+            if (lane == 0) {
+                counts[ci * 2] = cand_above[ci] + gt;
+                counts[ci * 2 + 1] = eq;
+            }
         }
-        counts[((size_t)b * n_chunks + c) * 2] = g2;
-        counts[((size_t)b * n_chunks + c) * 2 + 1] = e2;
     }
 }
 
@@ -416,21 +430,35 @@ __global__ __launch_bounds__(kChunkThreads) void topk_write_kernel(
         return;
     }
     const uint32_t T = info[b].T, need = info[b].need;
-    uint32_t gt_before = 0, eq_before = 0;
-    for (int c2 = 0; c2 < c; ++c2) {
-        gt_before += counts[((size_t)b * n_chunks + c2) * 2];
-        eq_before += counts[((size_t)b * n_chunks + c2) * 2 + 1];
-    }
     const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     constexpr int NW = kChunkThreads / 64;
-    const int span = kChunkKeys / NW;
+    constexpr int span = kChunkKeys / NW;
+    constexpr int KPL = span / 64;
     const int j0 = min(c0 + wave * span, c1), j1 = min(j0 + span, c1);
+    uint32_t kv[KPL];   // the wave's keys, all requested at once
+#pragma unroll
+    for (int it = 0; it < KPL; ++it) {
+        const int j = j0 + 64 * it + lane;
+        kv[it] = j < j1 ? keys[j] : 0u;
+    }
+    // selected and tied keys of the earlier chunks (lane-parallel)
+    uint32_t gt_before = 0, eq_before = 0;
+    for (int c2 = lane; c2 < c; c2 += 64) {
+        gt_before += counts[((size_t)b * n_chunks + c2) * 2];
+        eq_before += counts[((size_t)b * n_chunks + c2) * 2 + 1];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        gt_before += __shfl_xor(gt_before, o, 64);
+        eq_before += __shfl_xor(eq_before, o, 64);
+    }
     uint32_t gt = 0, eq = 0;
-    for (int j = j0 + lane; j < j1; j += 64) {
-        const uint32_t key = keys[j];
-        gt += key > T;
-        eq += key == T;
+#pragma unroll
+    for (int it = 0; it < KPL; ++it) {
+        const bool ok = j0 + 64 * it + lane < j1;
+        gt += ok && kv[it] > T;
+        eq += ok && kv[it] == T;
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -448,9 +476,10 @@ __global__ __launch_bounds__(kChunkThreads) void topk_write_kernel(
     }
     uint32_t sel_seen = gt_before + min(eq_before, need);   // selected before this step
     uint32_t eq_seen = eq_before;                            // ties before this step
-    for (int jb = j0; jb < j1; jb += 64) {
-        const int j = jb + lane;
-        const uint32_t key = j < j1 ? keys[j] : 0u;
+#pragma unroll
+    for (int it = 0; it < KPL; ++it) {
+        const int j = j0 + 64 * it + lane;
+        const uint32_t key = kv[it];
         const bool is_gt = j < j1 && key > T;
         const bool is_eq = j < j1 && key == T;
         const uint64_t eq_mask = __ballot(is_eq);
@@ -687,8 +716,9 @@ SparseLayout sparse_layout(int32_t B, int32_t H, int32_t S_max, int32_t top_k) {
     l.n_key_chunks = (S_max + kChunkKeys - 1) / kChunkKeys;
     l.scores_bytes = al((size_t)B * ((S_max + 3) & ~3) * sizeof(float));
     l.hist_bytes = al((size_t)B * kHistBins * sizeof(uint32_t));
-    // candidate keys in per-chunk slices [B][key chunks][4096], then counts [B][key chunks]
-    l.cand_bytes = al((size_t)B * l.n_key_chunks * (kChunkKeys + 1) * sizeof(uint32_t));
+    // candidate keys in per-chunk slices [B][key chunks][4096], then their counts
+    // [B][key chunks] and the higher-bin counts [B][key chunks]
+    l.cand_bytes = al((size_t)B * l.n_key_chunks * (kChunkKeys + 2) * sizeof(uint32_t));
     l.info_bytes = al((size_t)B * sizeof(SelInfo));
     l.counts_bytes = al((size_t)B * l.n_key_chunks * 2 * sizeof(uint32_t));
     l.o_bytes = al((size_t)B * H * l.n_chunks * kDv * sizeof(float));
@@ -710,6 +740,7 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
     w += lay.hist_bytes;
     uint32_t* cand = reinterpret_cast<uint32_t*>(w);
     uint32_t* cand_cnt = cand + (size_t)B * lay.n_key_chunks * kChunkKeys;
+    uint32_t* cand_above = cand_cnt + (size_t)B * lay.n_key_chunks;
     w += lay.cand_bytes;
     SelInfo* info = reinterpret_cast<SelInfo*>(w);
     w += lay.info_bytes;
@@ -728,11 +759,10 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
                        dim3(256), 0, s, (const uint16_t*)q_index, (const uint16_t*)k_index,
                        seq_lens, S_max, S_stride, rows_per_block, scores, hist);
     hipLaunchKernelGGL(topk_candidates_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores,
-                       hist, seq_lens, S_max, S_stride, top_k, cand, cand_cnt, nkc);
+                       hist, seq_lens, S_max, S_stride, top_k, cand, cand_cnt, cand_above, nkc);
     hipLaunchKernelGGL(topk_threshold_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, hist,
-                       seq_lens, S_max, S_stride, top_k, cand, cand_cnt, nkc, info);
-    hipLaunchKernelGGL(topk_count_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores,
-                       seq_lens, S_max, S_stride, top_k, info, counts, nkc);
+                       seq_lens, S_max, S_stride, top_k, cand, cand_cnt, cand_above, nkc, info,
+                       counts);
     hipLaunchKernelGGL(topk_write_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores,
                        seq_lens, S_max, S_stride, top_k, info, counts, nkc, topk_idx);
     hipLaunchKernelGGL(sparse_attn_kernel, dim3(lay.n_chunks, (H + 16 * kAttnWaves - 1) / (16 * kAttnWaves), B),
