@@ -163,8 +163,17 @@ def bench_prefill(cfg, steps, warmup):
 
     ev_ms = region_ms(step, max(steps // 2, 5), max(warmup // 2, 2))
     tf = flops / ev_ms / 1e9
-    log(f"[bench] prefill T={T}: {ev_ms * 1e3:.1f} us per call, {tf:.1f} TFLOP/s")
-    return dict(ev_ms=ev_ms, flops=flops, tflops=tf)
+    # context: what the vendor GEMM (torch.matmul -> hipBLASLt) reaches on the
+    # same GPU in the same run, a practical ceiling for dense bf16 MFMA work
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    bm = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    gemm_ms = region_ms(lambda i: a @ bm, 10, 3)
+    gemm_tf = 2 * n ** 3 / gemm_ms / 1e9
+    del a, bm
+    log(f"[bench] prefill T={T}: {ev_ms * 1e3:.1f} us per call, {tf:.1f} TFLOP/s "
+        f"(library bf16 GEMM {n}^3 on this GPU: {gemm_tf:.0f} TFLOP/s)")
+    return dict(ev_ms=ev_ms, flops=flops, tflops=tf, gemm_tflops=gemm_tf)
 
 
 def bench_sparse(cfg, steps, warmup):
@@ -336,7 +345,8 @@ def main():
         line["prefill_8k"] = {"TFLOP/s": round(p["tflops"], 1),
                               "pct_of_mfma_peak": round(100 * p["tflops"] / BF16_PEAK_TFLOPS, 2),
                               "ms_per_call": round(p["ev_ms"], 4), "flops": p["flops"],
-                              "bound": "mfma", "peak": BF16_PEAK_TFLOPS}
+                              "bound": "mfma", "peak": BF16_PEAK_TFLOPS,
+                              "library_gemm_8192_TFLOP/s": round(p["gemm_tflops"], 1)}
     if "s" in res:
         s = res["s"]
         line["sparse_128k"] = {"GB/s": round(s["gbs"], 1), "ms_per_call": round(s["ms"], 5),

@@ -238,7 +238,8 @@ __device__ __forceinline__ void pv_tile(const uint16_t* vt_s, const u32x4 (&pb)[
 // with one K fragment read two MFMAs ahead and a slice of the softmax of the
 // current tile; phase B issues the P.V MFMAs of the current tile, each with
 // one V fragment read two ahead and a slice of the next tile's maximum.  The
-// VALU work then runs under the matrix pipe instead of between its bursts.
+// VALU work then runs under the matrix pipe instead of between its bursts,
+// and phase A's last two groups already read phase B's first V fragments.
 template <int D>
 __device__ __forceinline__ void pipelined_step(const uint16_t* k_nx, const uint16_t* v_cu,
                                                const u32x4 (&qf)[Geo<D>::KSTEPS],
@@ -254,6 +255,7 @@ __device__ __forceinline__ void pipelined_step(const uint16_t* k_nx, const uint1
 
     // ---- phase A: S^T(next) || P(current)
     u32x4 kf[NQK];
+    u32x4 vf[NPV];
     u32x4 pb[4];
     float ls = 0.f;
 #pragma unroll
@@ -264,7 +266,10 @@ __device__ __forceinline__ void pipelined_step(const uint16_t* k_nx, const uint1
         for (int e = 0; e < 16; ++e) s_n[st][e] = 0.f;
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
-        if (i + 2 < NQK) kf[i + 2] = k_frag<D>(k_nx, 32 * ((i + 2) / KS) + n, 2 * ((i + 2) % KS) + h);
+        if (i + 2 < NQK)
+            kf[i + 2] = k_frag<D>(k_nx, 32 * ((i + 2) / KS) + n, 2 * ((i + 2) % KS) + h);
+        else if (i + 2 - NQK < NPV)   // the first V fragments of phase B, read under phase A
+            vf[i + 2 - NQK] = v_frag<D>(v_cu, 32 * ((i + 2 - NQK) % MT) + n, 2 * ((i + 2 - NQK) / MT) + h);
         s_n[i / KS] = mfma32h(kf[i], qf[i % KS], s_n[i / KS]);
 #pragma unroll
         for (int q = 0; q < PAIRS; ++q) {
@@ -282,10 +287,7 @@ __device__ __forceinline__ void pipelined_step(const uint16_t* k_nx, const uint1
     if (diag_next) mask_tile(s_n, ks_next, qi, h);
 
     // ---- phase B: O += V.P(current) || max S^T(next)
-    u32x4 vf[NPV];
     float mx = -INFINITY;
-#pragma unroll
-    for (int g = 0; g < 2 && g < NPV; ++g) vf[g] = v_frag<D>(v_cu, 32 * (g % MT) + n, 2 * (g / MT) + h);
 #pragma unroll
     for (int g = 0; g < NPV; ++g) {
         if (g + 2 < NPV) vf[g + 2] = v_frag<D>(v_cu, 32 * ((g + 2) % MT) + n, 2 * ((g + 2) / MT) + h);
