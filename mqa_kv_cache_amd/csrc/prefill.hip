@@ -519,48 +519,73 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     const int kt = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int ks = kt * BN;
     const int half = rope.half;   // <= D/2 <= 64
-    for (int e = tid; e < BN * half; e += 256) {
-        const int tl = e / half, i = e - tl * half;
-        float c, s;
-        rope_cos_sin(rope, (double)(ks + tl), i, c, s);
-        cs_c[e] = c;
-        cs_s[e] = s;
-    }
-    __syncthreads();
     const size_t in_base = ((size_t)b * Hkv + kvh) * (size_t)T * D;
     const size_t out_base = ((size_t)b * Hkv + kvh) * (size_t)T_pad * D;
-    for (int c = tid; c < BN * CPR; c += 256) {
+    // the tile's K and V chunks are requested first; the cos/sin table is
+    // formed while they are in flight
+    constexpr int NK = (BN * CPR + 255) / 256;          // K chunks per thread
+    constexpr int NV = ((BN / 4) * CPR + 255) / 256;    // V 4-row groups per thread
+    u32x4 kraw[NK], vraw[NV][4];
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+        const int c = tid + 256 * j;
         const int key = c / CPR, dc = c - key * CPR;
         const int t = ks + key;
-        u32x4 val = u32x4{0, 0, 0, 0};
-        if (t < T) {
-            const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + in_base + (size_t)t * D + 8 * dc));
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                float xe = bf16_lo(raw[p]), xo = bf16_hi(raw[p]);
-                const int i = 4 * dc + p;
-                if (i < half) {
-                    const float cc = cs_c[key * half + i], ss = cs_s[key * half + i];
-                    const float ye = xe * cc - xo * ss, yo = xe * ss + xo * cc;
-                    xe = ye;
-                    xo = yo;
-                }
-                val[p] = pack_f16x2(xe, xo);
-            }
-        }
-        *reinterpret_cast<u32x4*>(kh + out_base + (size_t)t * D + 8 * dc) = val;
+        kraw[j] = (c < BN * CPR && t < T)
+                      ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + in_base + (size_t)t * D + 8 * dc))
+                      : u32x4{0, 0, 0, 0};
     }
-    for (int c = tid; c < (BN / 4) * CPR; c += 256) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = tid + 256 * j;
         const int kg = c / CPR, dc = c - kg * CPR;
-        u32x4 r4[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = ks + 4 * kg + r;
-            u32x4 raw = u32x4{0, 0, 0, 0};
-            if (t < T) raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + in_base + (size_t)t * D + 8 * dc));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) r4[r][j] = pack_f16x2(bf16_lo(raw[j]), bf16_hi(raw[j]));
+            vraw[j][r] = (c < (BN / 4) * CPR && t < T)
+                             ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + in_base + (size_t)t * D + 8 * dc))
+                             : u32x4{0, 0, 0, 0};
         }
+    }
+    for (int e = tid; e < BN * half; e += 256) {
+        const int tl = e / half, i = e - tl * half;
+        float c, sn;
+        rope_cos_sin(rope, (double)(ks + tl), i, c, sn);
+        cs_c[e] = c;
+        cs_s[e] = sn;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+        const int c = tid + 256 * j;
+        if (c >= BN * CPR) break;
+        const int key = c / CPR, dc = c - key * CPR;
+        const int t = ks + key;
+        u32x4 val;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            float xe = bf16_lo(kraw[j][p]), xo = bf16_hi(kraw[j][p]);
+            const int i = 4 * dc + p;
+            if (i < half) {
+                const float cc = cs_c[key * half + i], ss = cs_s[key * half + i];
+                const float ye = xe * cc - xo * ss, yo = xe * ss + xo * cc;
+                xe = ye;
+                xo = yo;
+            }
+            val[p] = pack_f16x2(xe, xo);
+        }
+        *reinterpret_cast<u32x4*>(kh + out_base + (size_t)t * D + 8 * dc) = val;   // zeros past T
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = tid + 256 * j;
+        if (c >= (BN / 4) * CPR) break;
+        const int kg = c / CPR, dc = c - kg * CPR;
+        u32x4 r4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) r4[r][w] = pack_f16x2(bf16_lo(vraw[j][r][w]), bf16_hi(vraw[j][r][w]));
         const int col = 16 * (kg >> 2) + chunk_col(kg & 3);
         uint16_t* tile = vt + out_base + (size_t)kt * D * BN;
 #pragma unroll

@@ -85,3 +85,23 @@ def test_rope_none_copies(m):
     out = m.rope_apply(to_dev(x), pos, rope_settings(ROPE_NONE))
     torch.cuda.synchronize()
     assert np.array_equal(from_dev(out), bf16_bits_to_f64(x))
+
+
+@pytest.mark.parametrize("H,n_tok", [(160, 33), (24, 41)])
+def test_rope_many_heads_and_ragged_token_groups(m, H, n_tok):
+    """Rows wider than one pass of the block (160 heads x 16 chunks > 2048
+    chunks: several passes after the cos/sin table), and token groups that do
+    not divide the token count (24 heads: 5 tokens per block)."""
+    import torch
+    rng = np.random.default_rng(H + n_tok)
+    D = 128
+    x = randn_bf16(rng, (n_tok, H, D))
+    pos = rng.integers(0, 70000, size=n_tok).astype(np.int32)
+    p = rope_settings(ROPE_YARN, base=5e5, factor=4.0, original_max_position=8192, rotary_dim=96)
+    print(f"[case] rope H={H} n_tok={n_tok}", flush=True)
+    out = m.rope_apply(to_dev(x), torch.from_numpy(pos).cuda(), p)
+    torch.cuda.synchronize()
+    ref = orope.rotate_rows(bf16_bits_to_f64(x), pos, p)
+    got = from_dev(out)
+    assert_close(got, ref, f"rope H={H}")
+    assert np.array_equal(got[..., 96:], bf16_bits_to_f64(x)[..., 96:])
