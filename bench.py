@@ -182,9 +182,10 @@ def bench_sparse(cfg, steps, warmup):
     import mqa_kv_cache_amd as m
     from workloads import device_randn_bf16
     B, H, S, k = cfg.B, cfg.H, cfg.S_max, cfg.top_k
-    # three input sets rotate: a call reads ~137 MB, so the 256 MB Infinity
-    # Cache cannot hold the set that comes round again
-    nsets = 3
+    # eight input sets rotate (~1.1 GB of indexer keys and gathered rows
+    # between two uses of a set), so the 256 MB Infinity Cache cannot serve
+    # the set that comes round again
+    nsets = 8
     sets = [(device_randn_bf16((B, H, cfg.Dqk), cfg.seed * 100 + 10 * i + 1),
              device_randn_bf16((B, S, cfg.Dqk), cfg.seed * 100 + 10 * i + 2),
              device_randn_bf16((B, cfg.D_idx), cfg.seed * 100 + 10 * i + 3),

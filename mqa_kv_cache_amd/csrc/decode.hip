@@ -428,8 +428,8 @@ __global__ __launch_bounds__(64 * kWaves, GQA_DECODE_MIN_WAVES) void decode_spli
 // One wave per (batch, q head): merges the states of the pieces of its
 // context, slots floor(x/R) + i for the global rows x of context i.  Lane j
 // reads the (m, l) of piece j, so the maximum and the weights take one
-// round trip; the o rows (lane: D/64 values) are then read eight pieces at
-// a time with independent loads.
+// round trip, and the o rows of the first 16 pieces (lane: D/64 values) are
+// requested in the same round trip; further pieces are read eight at a time.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -441,27 +441,43 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     if (idx >= B * Hq) return;
     const int b = idx / Hq, h = idx - b * Hq;
     const int g = Hq / Hkv, kv = h / g, hl = h - kv * g;
-    const RowSpace rs = row_space(seq_lens, B, Hkv, S_max, n_parts, lane);
-    // global row of (b, kv 0, row 0): prefix over the batches before b
-    int64_t base = 0;
-    for (int c0 = 0; c0 < b; c0 += 64) {
+    // one pass over seq_lens gives both the row space total and the global
+    // row of (b, kv 0, row 0) (the prefix over the batches before b)
+    int64_t total = 0, base = 0;
+    for (int c0 = 0; c0 < B; c0 += 64) {
         const int bb = c0 + lane;
-        int64_t rows = bb < b ? (int64_t)Hkv * ctx_len(seq_lens, bb, S_max) : 0;
+        int64_t rows = bb < B ? (int64_t)Hkv * ctx_len(seq_lens, bb, S_max) : 0;
+        int64_t before = bb < b ? rows : 0;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) rows += __shfl_xor(rows, o, 64);
-        base += rows;
+        for (int o = 32; o >= 1; o >>= 1) {
+            rows += __shfl_xor(rows, o, 64);
+            before += __shfl_xor(before, o, 64);
+        }
+        total += rows;
+        base += before;
     }
+    const int64_t R = (total + n_parts - 1) / n_parts;
     const int L = ctx_len(seq_lens, b, S_max);
     const int64_t x0 = base + (int64_t)kv * L;
     const int64_t ctx = (int64_t)b * Hkv + kv;
-    const int64_t s0 = x0 / rs.R + ctx;
-    const int np = (int)((x0 + L - 1) / rs.R + ctx - s0 + 1);
+    const int64_t s0 = x0 / R + ctx;
+    const int np = (int)((x0 + L - 1) / R + ctx - s0 + 1);
+    const size_t pstride = (size_t)g * D;
     float acc[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] = 0.f;
     float den = 0.f, M_run = -INFINITY;
     for (int c0 = 0; c0 < np; c0 += 64) {          // one chunk unless > 64 pieces
         const int cn = min(64, np - c0);
+        const float* pbase = part_o + ((size_t)(s0 + c0) * g + hl) * D + lane * PER;
+        // the o rows of the first 16 pieces are requested with the (m, l)
+        // pair: they do not depend on the weights
+        constexpr int kFirst = 16;
+        float v0[kFirst][PER];
+#pragma unroll
+        for (int jj = 0; jj < kFirst; ++jj)
+#pragma unroll
+            for (int e = 0; e < PER; ++e) v0[jj][e] = jj < cn ? pbase[jj * pstride + e] : 0.f;
         float m = -INFINITY, l = 0.f;
         if (lane < cn) {
             const size_t i2 = (size_t)(s0 + c0 + lane) * g + hl;
@@ -481,9 +497,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) dsum += wave_shfl_xor(dsum, o);
         den += dsum;
-        const float* pbase = part_o + ((size_t)(s0 + c0) * g + hl) * D + lane * PER;
-        const size_t pstride = (size_t)g * D;
-        for (int j0 = 0; j0 < cn; j0 += 8) {
+#pragma unroll
+        for (int jj = 0; jj < kFirst; ++jj) {
+            const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), jj));
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] += wgt * v0[jj][e];
+        }
+        for (int j0 = kFirst; j0 < cn; j0 += 8) {
             float v[8][PER];
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj)
