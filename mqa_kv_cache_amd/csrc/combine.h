@@ -30,10 +30,20 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] = 0.f;
     float den = 0.f, M_run = -INFINITY;
-    // lane s reads the (m, l) of split s (64 splits at a time); the o rows
-    // are then read four splits at a time with independent loads
+    // lane s reads the (m, l) of split s (64 splits at a time); the o rows of
+    // the first 16 splits are requested in the same round trip (they do not
+    // depend on the weights), further splits four at a time
+    constexpr int kFirst = 16;
     for (int s0 = 0; s0 < ns; s0 += 64) {
         const int cn = min(64, ns - s0);
+        f32x4 v0[kFirst][PER / 4];
+#pragma unroll
+        for (int jj = 0; jj < kFirst; ++jj) {
+            const int sj = s0 + min(jj, cn - 1);   // past the end: a valid split, weight 0
+            const f32x4* src = reinterpret_cast<const f32x4*>(po + (size_t)sj * D);
+#pragma unroll
+            for (int e = 0; e < PER / 4; ++e) v0[jj][e] = src[e];
+        }
         const float m = lane < cn ? ml[2 * (s0 + lane)] : -INFINITY;
         const float l = lane < cn ? ml[2 * (s0 + lane) + 1] : 0.f;
         float M = m;
@@ -49,7 +59,17 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) dsum += wave_shfl_xor(dsum, o);
         den += dsum;
-        for (int j0 = 0; j0 < cn; j0 += 4) {
+#pragma unroll
+        for (int jj = 0; jj < kFirst; ++jj) {
+            const float wgt = jj < cn ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                            __builtin_bit_cast(int, wl), jj))
+                                      : 0.f;
+#pragma unroll
+            for (int e = 0; e < PER / 4; ++e)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[4 * e + c] += wgt * v0[jj][e][c];
+        }
+        for (int j0 = kFirst; j0 < cn; j0 += 4) {
             f32x4 v[4][PER / 4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {

@@ -602,6 +602,13 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
     const int h = hg * (16 * kAttnWaves) + 16 * wave + n;
     const bool heads = hg * (16 * kAttnWaves) + 16 * wave < H;   // wave-uniform (H % 16 == 0)
 
+    // q and the selected indices are requested together; the barrier's
+    // wait covers both, so the copies below start after one load latency
+    // (a wave past the last head still copies its share and meets the barriers)
+    u32x4 qf[KU];
+    const uint16_t* qrow = q + ((size_t)b * H + (heads ? h : 0)) * kDqk;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u + 8 * G);
     for (int i = tid; i < kRowsPerChunk; i += 64 * kAttnWaves)
         sel_s[i] = c0 + i < c1 ? topk_idx[(size_t)b * top_k + c0 + i] : -1;
     __syncthreads();
@@ -638,14 +645,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
         }
     };
 
-    // (a wave past the last head still copies its share and meets the barriers)
-    u32x4 qf[KU];
-    const uint16_t* qrow = q + ((size_t)b * H + (heads ? h : 0)) * kDqk;
-#pragma unroll
-    for (int u = 0; u < KU; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u + 8 * G);
-    // q is complete before the copies are issued: the compiler's wait counts
-    // do not include loads into LDS, so a wait for q placed after them would
-    // also wait for every copy
+    // q is complete before the copies are issued (the barrier waited for
+    // it): the compiler's wait counts do not include loads into LDS, so a
+    // wait for q placed after them would also wait for every copy
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_sched_barrier(0);
     // all four sub-chunks are requested at once: one gather latency per chunk
