@@ -42,15 +42,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;
 constexpr int kWaves = 4;   // waves per workgroup (each an independent work item)
 
-// Compile-time tuning: minimum resident waves per SIMD requested from the
-// register allocator, and whether the next tile is prefetched into a second
-// register set.
-#ifndef GQA_DECODE_MIN_WAVES
-#define GQA_DECODE_MIN_WAVES 1
-#endif
-#ifndef GQA_DECODE_PREFETCH
-#define GQA_DECODE_PREFETCH 1
-#endif
 
 template <int D>
 struct DecodeTile {
@@ -290,7 +281,7 @@ __device__ __forceinline__ void prep_q(const u32x4 (&raw)[NB][D / 32], const QFr
 }
 
 template <int D, int NB>
-__global__ __launch_bounds__(64 * kWaves, GQA_DECODE_MIN_WAVES) void decode_split_kernel(
+__global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ seq_lens, int B, int Hq,
     int Hkv, int S_max, float qscale, RopeDev rope, float* __restrict__ part_o,
@@ -333,14 +324,8 @@ __global__ __launch_bounds__(64 * kWaves, GQA_DECODE_MIN_WAVES) void decode_spli
         // tiles are in flight
         u32x4 qraw[NB][KU];
         load_q_raw<D, NB>(q, b, kv, Hq, g, G, n, qraw);
-#if GQA_DECODE_PREFETCH >= 1
         DecodeTile<D> ta, tb;
         load_tile<D>(ta, kr, vr, r0, G, n);
-#endif
-#if GQA_DECODE_PREFETCH >= 2
-        DecodeTile<D> tc;
-        load_tile<D>(tb, kr, vr, r0 + 32, G, n);
-#endif
 
         u32x4 qhi[NB][KU], qlo[NB][KU];
         prep_q<D, NB>(qraw, fq, L, qscale, rope, G, qhi, qlo);
@@ -355,13 +340,6 @@ __global__ __launch_bounds__(64 * kWaves, GQA_DECODE_MIN_WAVES) void decode_spli
             l_run[nb] = 0.f;
         }
 
-#if GQA_DECODE_PREFETCH == 0
-        for (int t0 = r0; t0 < r1; t0 += 32) {
-            DecodeTile<D> ta;
-            load_tile<D>(ta, kr, vr, t0, G, n);
-            tile_math<D, NB>(ta, t0, r1, G, qhi, qlo, o, m_run, l_run);
-        }
-#elif GQA_DECODE_PREFETCH == 1
         for (int t0 = r0;;) {
             load_tile<D>(tb, kr, vr, t0 + 32, G, n);
             tile_math<D, NB>(ta, t0, r1, G, qhi, qlo, o, m_run, l_run);
@@ -372,23 +350,6 @@ __global__ __launch_bounds__(64 * kWaves, GQA_DECODE_MIN_WAVES) void decode_spli
             t0 += 32;
             if (t0 >= r1) break;
         }
-#else
-        // ring of three tiles: two in flight while one is consumed
-        for (int t0 = r0;;) {
-            load_tile<D>(tc, kr, vr, t0 + 64, G, n);
-            tile_math<D, NB>(ta, t0, r1, G, qhi, qlo, o, m_run, l_run);
-            t0 += 32;
-            if (t0 >= r1) break;
-            load_tile<D>(ta, kr, vr, t0 + 64, G, n);
-            tile_math<D, NB>(tb, t0, r1, G, qhi, qlo, o, m_run, l_run);
-            t0 += 32;
-            if (t0 >= r1) break;
-            load_tile<D>(tb, kr, vr, t0 + 64, G, n);
-            tile_math<D, NB>(tc, t0, r1, G, qhi, qlo, o, m_run, l_run);
-            t0 += 32;
-            if (t0 >= r1) break;
-        }
-#endif
 
         // ---- partial (m, l, o) of this piece
         const int64_t slot = gs / rs.R + ((int64_t)b * Hkv + kv);

@@ -47,12 +47,6 @@ constexpr int BN = 64;    // keys per tile
 #define GQA_PREFILL_XCDS 8
 #endif
 constexpr int kXcds = GQA_PREFILL_XCDS;   // XCDs that share the dispatch round-robin
-#ifndef GQA_PREFILL_SWAP
-#define GQA_PREFILL_SWAP 1
-#endif
-#ifndef GQA_PREFILL_EARLY_V
-#define GQA_PREFILL_EARLY_V 1
-#endif
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
