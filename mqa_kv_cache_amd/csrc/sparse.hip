@@ -153,7 +153,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 //    topk_candidates_kernel  first digit from the histogram; keys of the
 //                            threshold bin copied to the chunk's own slice,
 //                            keys of higher bins counted per chunk
-//    topk_threshold_kernel   exact k-th key T from the candidates (or from
+//    topk_threshold_kernel   (first digit as the chunk-0 candidate workgroup
+//                            found it) exact k-th key T from the candidates (or from
 //                            extra passes when the bin is too large), the
 //                            number of ties to take, and per chunk the
 //                            counts of keys > T and == T (from the slices)
@@ -169,7 +170,7 @@ struct SelInfo {
     uint32_t T;        // k-th largest key
     uint32_t need;     // keys == T to take, lowest indices first
     uint32_t B1;       // first-digit bin of T
-    uint32_t pad;
+    uint32_t above;    // keys in first-digit bins above B1
 };
 
 // Inclusive prefix sum of one value per thread across a block of NT threads.
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_candidates_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist_g,
     const int32_t* __restrict__ seq_lens, int S_max, int S_stride, int top_k,
     uint32_t* __restrict__ cand_g, uint32_t* __restrict__ cand_cnt,
-    uint32_t* __restrict__ cand_above, int n_chunks) {
+    uint32_t* __restrict__ cand_above, int n_chunks, SelInfo* __restrict__ info) {
     __shared__ uint32_t h[kHistBins];
     __shared__ uint32_t wsum[kChunkThreads / 64];
     __shared__ uint32_t res[2];
@@ -279,6 +280,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_candidates_kernel(
     }
     first_digit<kChunkThreads>(hist_g, b, L, k, h, wsum, res);
     const uint32_t B1 = res[0];
+    if (c == 0 && threadIdx.x == 0) info[b] = SelInfo{0u, 0u, B1, res[1]};   // for the threshold kernel
     uint32_t* cand = cand_g + (size_t)b * n_chunks * kChunkKeys + c0;
     uint32_t above = 0;
 #pragma unroll
@@ -301,8 +303,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_candidates_kernel(
 }
 
 __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
-    const float* __restrict__ scores, const uint32_t* __restrict__ hist_g,
-    const int32_t* __restrict__ seq_lens, int S_max, int S_stride, int top_k,
+    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int S_max, int S_stride, int top_k,
     const uint32_t* __restrict__ cand_g, const uint32_t* __restrict__ cand_cnt,
     const uint32_t* __restrict__ cand_above, int n_chunks, SelInfo* __restrict__ info,
     uint32_t* __restrict__ counts) {
@@ -316,9 +317,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
     const int L = min(max(seq_lens[b], 1), S_max);
     const int k = min(top_k, L);
     if (k == L) return;
-    first_digit<kSelThreads>(hist_g, b, L, k, h, wsum, res);
-    const uint32_t B1 = res[0];
-    uint32_t need = (uint32_t)k - res[1];
+    // first digit as the candidate kernel found it (its chunk-0 workgroup)
+    const SelInfo fd = info[b];
+    const uint32_t B1 = fd.B1;
+    uint32_t need = (uint32_t)k - fd.above;
     const int nkc = min(n_chunks, (L + kChunkKeys - 1) / kChunkKeys);
     const uint32_t cnt = tid < nkc ? cand_cnt[(size_t)b * n_chunks + tid] : 0u;
     const uint32_t incl = block_inclusive_scan<kSelThreads>(cnt, wsum);
@@ -379,7 +381,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
         T = (pre << 8) | res[0];
         need -= res[1];
     }
-    if (tid == 0) info[b] = SelInfo{T, need, B1, 0u};
+    if (tid == 0) info[b] = SelInfo{T, need, B1, fd.above};
     // per chunk: keys > T are the higher bins plus the slice's candidates
     // above T; ties are the slice's keys equal to T (wave w takes chunks
     // w, w + 16, ...)
@@ -761,8 +763,9 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
                        dim3(256), 0, s, (const uint16_t*)q_index, (const uint16_t*)k_index,
                        seq_lens, S_max, S_stride, rows_per_block, scores, hist);
     hipLaunchKernelGGL(topk_candidates_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores,
-                       hist, seq_lens, S_max, S_stride, top_k, cand, cand_cnt, cand_above, nkc);
-    hipLaunchKernelGGL(topk_threshold_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, hist,
+                       hist, seq_lens, S_max, S_stride, top_k, cand, cand_cnt, cand_above, nkc,
+                       info);
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3(B), dim3(kSelThreads), 0, s, scores,
                        seq_lens, S_max, S_stride, top_k, cand, cand_cnt, cand_above, nkc, info,
                        counts);
     hipLaunchKernelGGL(topk_write_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores,
