@@ -124,6 +124,38 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, rope_p, pairs=None) -> n
     return out
 
 
+def append_rows(k_cache, v_cache, k_new, v_new, seq_lens, rope_p):
+    """The decode step's cache write: the new token's key, rotated at its
+    position seq_lens[b]-1, and its value go into row seq_lens[b]-1 of every
+    kv head; returns new (float64) copies of the caches.
+
+    [注意力机制进化史] "解码中的KV Cache" (the new key and value are
+    concatenated to the past ones); [transformer架构] §1.1 (the key is
+    rotated at its own position, the value is not).  Keys are cached after
+    RoPE, as in :func:`decode`.
+    """
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    k_new = np.asarray(k_new, dtype=np.float64)
+    v_new = np.asarray(v_new, dtype=np.float64)
+    for b in range(kc.shape[0]):
+        pos = int(seq_lens[b]) - 1
+        kr = k_new[b]
+        if rope_p is not None:
+            kr = _rope.rotate_rows(k_new[b][None], np.array([pos]), rope_p)[0]
+        kc[b, :, pos] = kr
+        vc[b, :, pos] = v_new[b]
+    return kc, vc
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale: float, rope_p,
+                  pairs=None):
+    """One decode step with its cache write: :func:`append_rows`, then
+    :func:`decode` over the updated caches.  Returns (out, k_cache', v_cache')."""
+    kc, vc = append_rows(k_cache, v_cache, k_new, v_new, seq_lens, rope_p)
+    return decode(q, kc, vc, seq_lens, scale, rope_p, pairs=pairs), kc, vc
+
+
 def page_attention(x, Wq, Wk, Wv, n_head: int, n_kv_head: int) -> np.ndarray:
     """The pages' whole GQA attention function (projection, head split, K/V
     repeated g times along the head axis, causal softmax, heads merged), with

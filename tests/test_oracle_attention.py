@@ -112,6 +112,34 @@ def test_decode_of_last_token_equals_prefill_last_row():
     assert np.allclose(dec6, pre6[:, :, 6], rtol=1e-12, atol=1e-13)
 
 
+def test_decode_append_builds_the_prefill_cache():
+    """Appending tokens one at a time (rotated key and value written at the
+    token's position, then decode) reproduces every prefill row, and the
+    cache it leaves equals rope(K) and V; rows past the new token stay as
+    they were.  A wrong write position, a missing rotation or a rotation at
+    the wrong position fails the row comparison."""
+    B, Hq, Hkv, T, D = 2, 8, 2, 12, 32
+    q, k, v = _rand((B, Hq, T, D), 24), _rand((B, Hkv, T, D), 25), _rand((B, Hkv, T, D), 26)
+    p = rope_settings(ROPE_YARN, base=1e4, factor=4.0, original_max_position=8)
+    pre = att.prefill_causal(q, k, v, 0.3, p)
+    S_max = T + 5
+    junk_k, junk_v = _rand((B, Hkv, S_max, D), 27), _rand((B, Hkv, S_max, D), 28)
+    kc, vc = junk_k.copy(), junk_v.copy()
+    for t in range(T):
+        lens = np.array([t + 1] * B)
+        out, kc, vc = att.decode_append(q[:, :, t], k[:, :, t], v[:, :, t], kc, vc, lens, 0.3, p)
+        assert np.allclose(out, pre[:, :, t], rtol=1e-12, atol=1e-13), t
+    krot = rope.rotate_rows(k.transpose(2, 0, 1, 3), np.arange(T), p).transpose(1, 2, 0, 3)
+    assert np.allclose(kc[:, :, :T], krot, rtol=1e-14, atol=1e-14)
+    assert np.array_equal(vc[:, :, :T], v)
+    assert np.array_equal(kc[:, :, T:], junk_k[:, :, T:])
+    assert np.array_equal(vc[:, :, T:], junk_v[:, :, T:])
+    # without RoPE the key is stored as given
+    kc2, vc2 = att.append_rows(junk_k, junk_v, k[:, :, 3], v[:, :, 3], np.array([5, 9]), None)
+    assert np.array_equal(kc2[0, :, 4], k[0, :, 3]) and np.array_equal(kc2[1, :, 8], k[1, :, 3])
+    assert np.array_equal(vc2[0, :, 4], v[0, :, 3]) and np.array_equal(vc2[1, :, 8], v[1, :, 3])
+
+
 def test_tiny_demo_shapes_and_param_counts():
     """[注意力变体与MoE] "MQA 与 GQA": the demo's printed output shape and K/V
     parameter counts for n_kv_head = 8, 2, 1."""
