@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of sections (decode32k,decode4k,"
+    ap.add_argument("--only", default="", help="comma list of sections (decode32k,decode4k,append32k,"
                     "prefill,sparse,rope) for profiling runs")
     return ap.parse_args()
 
@@ -142,6 +142,36 @@ def bench_decode(cfg, steps, warmup, nsets, label):
     log(f"[bench] {label}: step {ms * 1e3:.1f} us, partial kernel {kern_ms * 1e3:.1f} us, "
         f"{kv_bytes / ms / 1e6:.0f} GB/s")
     return dict(ms=ms, kern_ms=kern_ms, kv_bytes=kv_bytes, lens=lens.cpu().numpy(), sets=sets)
+
+
+def bench_decode_append(cfg, steps, warmup, nsets=2):
+    """The decode step with its cache write (gqa_decode_append): the new
+    token's rotated key and value go into row seq_lens[b]-1, then it attends."""
+    import torch
+
+    import mqa_kv_cache_amd as m
+    from workloads import device_randn_bf16
+    B, Hq, Hkv, D, S = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.S_max
+    lens = torch.from_numpy(cfg.seq_lens()).cuda()
+    sets = [(device_randn_bf16((B, Hq, D), cfg.seed * 100 + 10 * i + 1),
+             device_randn_bf16((B, Hkv, S, D), cfg.seed * 100 + 10 * i + 2),
+             device_randn_bf16((B, Hkv, S, D), cfg.seed * 100 + 10 * i + 3),
+             device_randn_bf16((B, Hkv, D), cfg.seed * 100 + 10 * i + 4),
+             device_randn_bf16((B, Hkv, D), cfg.seed * 100 + 10 * i + 5)) for i in range(nsets)]
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(m.gqa_decode_workspace_size(B, Hq, Hkv, D, S), dtype=torch.uint8, device="cuda")
+    kv_bytes = int(lens.sum().item()) * Hkv * D * 2 * 2
+    rope = cfg.rope()
+
+    def step(i):
+        q, k, v, kn, vn = sets[i % nsets]
+        m.gqa_decode_append(q, kn, vn, k, v, lens, cfg.scale, q_rope=rope, out=out, workspace=ws)
+
+    ms = timed_loop(step, steps, warmup)
+    log(f"[bench] decode+append 32K: step {ms * 1e3:.1f} us, {kv_bytes / ms / 1e6:.0f} GB/s")
+    del sets
+    torch.cuda.empty_cache()
+    return dict(ms=ms, kv_bytes=kv_bytes)
 
 
 def bench_prefill(cfg, steps, warmup):
@@ -285,6 +315,8 @@ def main():
         res["d32"] = bench_decode(DECODE_32K_YARN, K, W, nsets=2, label="decode 32K")
     if want("decode4k"):
         res["d4"] = bench_decode(DECODE_4K, K, W, nsets=4, label="decode 4K")
+    if want("append32k"):
+        res["da"] = bench_decode_append(DECODE_32K_YARN, K, W)
     if want("prefill"):
         res["p"] = bench_prefill(PREFILL_8K, K, W)
     if want("sparse"):
@@ -341,6 +373,11 @@ def main():
                              "kernel_GB/s": round(d4["kv_bytes"] / d4["kern_ms"] / 1e6, 1),
                              "pct_of_hbm_peak": round(100 * d4["kv_bytes"] / d4["ms"] / 1e6 / HBM_PEAK_GBS, 2),
                              "ms_per_step": round(d4["ms"], 5)}
+    if "da" in res:
+        da = res["da"]
+        line["decode_append_32k"] = {"GB/s": round(da["kv_bytes"] / da["ms"] / 1e6, 1),
+                                     "pct_of_hbm_peak": round(100 * da["kv_bytes"] / da["ms"] / 1e6 / HBM_PEAK_GBS, 2),
+                                     "ms_per_step": round(da["ms"], 5)}
     if "p" in res:
         p = res["p"]
         line["prefill_8k"] = {"TFLOP/s": round(p["tflops"], 1),

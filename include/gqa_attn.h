@@ -171,6 +171,33 @@ gqa_status gqa_decode_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, in
                               int32_t n_parts, void* out, void* stream);
 
 /*
+ * gqa_decode_append -- a whole decode step: the new token's key and value
+ * are written into the caches, then the token attends as in gqa_decode
+ * ([注意力机制进化史] "解码中的KV Cache": the new k/v are concatenated to the
+ * past ones before attending; [transformer架构] §1.1: the key is rotated at
+ * its own position, the value is not).  For batch b and kv head j, with
+ * L = seq_lens[b] (which counts the new token):
+ *     k_cache[b][j][L-1] = bf16(RoPE(k_new[b][j], position L-1))  (q_rope's
+ *                          settings, YaRN amplitude included; as given when
+ *                          q_rope is NULL or NONE)
+ *     v_cache[b][j][L-1] = v_new[b][j]
+ * and out = gqa_decode(q, k_cache, v_cache, seq_lens, ...) over the updated
+ * caches.  The write is fused into the decode kernel: the wave that streams
+ * row L-1 takes it from k_new/v_new and stores it, so the step reads the
+ * caches once and launches the same two kernels as gqa_decode.
+ *
+ *   k_new, v_new  bf16 [B][Hkv][D], device, 16-byte aligned; k_new not rotated
+ *   k_cache, v_cache  as in gqa_decode, written at row seq_lens[b]-1 only
+ * Other arguments, limits and errors as gqa_decode.  Nothing is written when
+ * an error status is returned.
+ */
+gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, const int32_t* seq_lens,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S_max,
+                             float scale, const gqa_rope_params* q_rope, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gqa_prefill_causal -- causal GQA attention over a whole prompt
  * ([注意力变体与MoE] "MQA 与 GQA", attention(): scores q k^T / sqrt(hd) with the
  * strict upper triangle masked to -inf, softmax, weighted sum of V):

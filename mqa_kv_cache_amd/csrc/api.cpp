@@ -195,6 +195,32 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                             workspace, workspace_bytes, 0, stream);
 }
 
+gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                             void* v_cache, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t D, int32_t S_max, float scale,
+                             const gqa_rope_params* q_rope, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    gqa_status st = check_decode_shape(B, Hq, Hkv, D, S_max);
+    if (st != GQA_OK) return st;
+    if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !seq_lens || !workspace || !out)
+        return GQA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return GQA_ERR_INVALID_ARGUMENT;
+    RopeDev rd;
+    st = rope_prepare(q_rope, D, &rd);
+    if (st != GQA_OK) return st;
+    const DecodeLayout lay = decode_layout(B, Hq, Hkv, D, kDecodeDefaultParts);
+    if (workspace_bytes < lay.total) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    st = from_hip(launch_gqa_decode_partial(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max,
+                                            scale, rd, workspace, lay, (hipStream_t)stream, k_new,
+                                            v_new));
+    if (st != GQA_OK) return st;
+    return from_hip(launch_gqa_decode_combine(seq_lens, B, Hq, Hkv, D, S_max, workspace, lay, out,
+                                              (hipStream_t)stream));
+}
+
 static gqa_status check_prefill_shape(int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t D) {
     if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1) return GQA_ERR_INVALID_ARGUMENT;
     if (Hq % Hkv) return GQA_ERR_INVALID_ARGUMENT;

@@ -280,12 +280,93 @@ __device__ __forceinline__ void prep_q(const u32x4 (&raw)[NB][D / 32], const QFr
         }
 }
 
-template <int D, int NB>
+// The decode step's cache write, fused: the new token's row (position L-1,
+// the last row of its context) is taken from k_new / v_new instead of the
+// cache.  The key is rotated at L-1 with the frequencies this lane already
+// holds for q (the K pairs a lane holds are its q pairs), amplitude included,
+// and rounded to bf16; the value is used as given.  Both are also written to
+// row L-1 of the caches.  The new rows are read with q (so no wait of their
+// own) and kept in registers; the tile loop only swaps registers (no memory
+// access inside it, so its load pipelining and wait counts are those of the
+// plain kernel), and the stores follow the loop.
+struct AppendArgs {
+    const uint16_t* k_new;   // [B][Hkv][D] bf16, not rotated
+    const uint16_t* v_new;   // [B][Hkv][D] bf16
+    uint16_t* k_cache;       // the caches the kernel reads, written at row L-1
+    uint16_t* v_cache;
+};
+
+template <int D>
+struct NewRow {
+    u32x4 k[D / 32];   // lane (G, n): dims 32 u + 8 G .. +7 (rotated in place by rotate_new_key)
+    u32x4 v;           // lane (G, n), n < D/8: dims 8 n .. +7
+};
+
+template <int D>
+__device__ __forceinline__ void load_new_row(NewRow<D>& nr, const AppendArgs& app, size_t nrow,
+                                             int G, int n) {
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) nr.k[u] = *reinterpret_cast<const u32x4*>(app.k_new + nrow + 32 * u + 8 * G);
+    nr.v = n < D / 8 ? *reinterpret_cast<const u32x4*>(app.v_new + nrow + 8 * n) : u32x4{0, 0, 0, 0};
+}
+
+template <int D>
+__device__ __forceinline__ void rotate_new_key(NewRow<D>& nr, int L, const QFreq<D>& fq,
+                                               const RopeDev& rope, int G) {
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) {
+        u32x4 w;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            float xe = bf16_lo(nr.k[u][p]), xo = bf16_hi(nr.k[u][p]);
+            if (16 * u + 4 * G + p < rope.half) {
+                float c, sn;
+                cos_sin_theta(fq.th[u][p], (double)(L - 1), rope, c, sn);
+                const float ye = xe * c - xo * sn, yo = xe * sn + xo * c;
+                xe = ye;
+                xo = yo;
+            }
+            w[p] = f32_to_bf16_bits(xe) | (f32_to_bf16_bits(xo) << 16);
+        }
+        nr.k[u] = w;
+    }
+}
+
+// Swap the new row into the tile that holds it (rr = its row in the tile,
+// wave-uniform): K row rr is lane n = rr & 15 of half rr >> 4; V row rr is
+// register rs of lane group Gs (see slot_row).
+template <int D>
+__device__ __forceinline__ void swap_new_row(DecodeTile<D>& t, const NewRow<D>& nr, int rr, int G,
+                                             int n) {
+    const int th = rr >> 4, nn = rr & 15;
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+            if (h2 == th && n == nn) t.k[h2][u] = nr.k[u];
+    const int Gs = rr < 16 ? rr >> 2 : (rr - 16) >> 2;
+    const int rs = rr < 16 ? (rr & 3) : 4 + ((rr - 16) & 3);
+#pragma unroll
+    for (int r2 = 0; r2 < 8; ++r2)
+        if (r2 == rs && G == Gs && n < D / 8) t.v[r2] = nr.v;
+}
+
+template <int D>
+__device__ __forceinline__ void store_new_row(const NewRow<D>& nr, uint16_t* krow, uint16_t* vrow,
+                                              int rr, int G, int n) {
+    if (n == (rr & 15))
+#pragma unroll
+        for (int u = 0; u < D / 32; ++u) *reinterpret_cast<u32x4*>(krow + 32 * u + 8 * G) = nr.k[u];
+    const int Gs = rr < 16 ? rr >> 2 : (rr - 16) >> 2;
+    if (G == Gs && n < D / 8) *reinterpret_cast<u32x4*>(vrow + 8 * n) = nr.v;
+}
+
+template <int D, int NB, bool APPEND>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ seq_lens, int B, int Hq,
     int Hkv, int S_max, float qscale, RopeDev rope, float* __restrict__ part_o,
-    float* __restrict__ part_ml, int n_parts) {
+    float* __restrict__ part_ml, int n_parts, AppendArgs app) {
     constexpr int KU = D / 32;
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4, n = lane & 15;
@@ -324,11 +405,18 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
         // tiles are in flight
         u32x4 qraw[NB][KU];
         load_q_raw<D, NB>(q, b, kv, Hq, g, G, n, qraw);
+        [[maybe_unused]] NewRow<D> nr;
+        if constexpr (APPEND) load_new_row<D>(nr, app, ((size_t)b * Hkv + kv) * D, G, n);
         DecodeTile<D> ta, tb;
         load_tile<D>(ta, kr, vr, r0, G, n);
 
         u32x4 qhi[NB][KU], qlo[NB][KU];
         prep_q<D, NB>(qraw, fq, L, qscale, rope, G, qhi, qlo);
+        // this piece holds the new token's row when it ends the context
+        const bool ends = APPEND && r1 == L;
+        const int rr_new = (L - 1 - r0) & 31;     // its row in the tile that holds it
+        if constexpr (APPEND)
+            if (ends) rotate_new_key<D>(nr, L, fq, rope, G);
 
         f32x4 o[NB][8];
         float m_run[NB], l_run[NB];
@@ -340,16 +428,28 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
             l_run[nb] = 0.f;
         }
 
+        auto fix = [&](DecodeTile<D>& t, int t0) {
+            if constexpr (APPEND)
+                if (ends && t0 + 32 >= L) swap_new_row<D>(t, nr, rr_new, G, n);
+        };
         for (int t0 = r0;;) {
             load_tile<D>(tb, kr, vr, t0 + 32, G, n);
+            fix(ta, t0);
             tile_math<D, NB>(ta, t0, r1, G, qhi, qlo, o, m_run, l_run);
             t0 += 32;
             if (t0 >= r1) break;
             load_tile<D>(ta, kr, vr, t0 + 32, G, n);
+            fix(tb, t0);
             tile_math<D, NB>(tb, t0, r1, G, qhi, qlo, o, m_run, l_run);
             t0 += 32;
             if (t0 >= r1) break;
         }
+
+        if constexpr (APPEND)
+            if (ends) {
+                const size_t row = slice + (size_t)(L - 1) * D;
+                store_new_row<D>(nr, app.k_cache + row, app.v_cache + row, rr_new, G, n);
+            }
 
         // ---- partial (m, l, o) of this piece
         const int64_t slot = gs / rs.R + ((int64_t)b * Hkv + kv);
@@ -492,10 +592,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 template <int D, int NB>
 void launch_split(hipStream_t s, const void* q, const void* k, const void* v, const int32_t* sl,
                   int B, int Hq, int Hkv, int S_max, float qscale, const RopeDev& rope, float* po,
-                  float* pml, int n_parts) {
-    hipLaunchKernelGGL((decode_split_kernel<D, NB>), dim3((n_parts + kWaves - 1) / kWaves),
-                       dim3(64 * kWaves), 0, s, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, sl, B, Hq, Hkv, S_max, qscale, rope, po, pml, n_parts);
+                  float* pml, int n_parts, const AppendArgs& app) {
+    const dim3 grid((n_parts + kWaves - 1) / kWaves);
+    if (app.k_new)
+        hipLaunchKernelGGL((decode_split_kernel<D, NB, true>), grid, dim3(64 * kWaves), 0, s,
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sl, B, Hq,
+                           Hkv, S_max, qscale, rope, po, pml, n_parts, app);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<D, NB, false>), grid, dim3(64 * kWaves), 0, s,
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sl, B, Hq,
+                           Hkv, S_max, qscale, rope, po, pml, n_parts, app);
 }
 
 }  // namespace
@@ -514,7 +620,11 @@ DecodeLayout decode_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_
 hipError_t launch_gqa_decode_partial(const void* q, const void* k_cache, const void* v_cache,
                                      const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                                      int32_t D, int32_t S_max, float scale, const RopeDev& rope,
-                                     void* workspace, const DecodeLayout& lay, hipStream_t s) {
+                                     void* workspace, const DecodeLayout& lay, hipStream_t s,
+                                     const void* k_new, const void* v_new) {
+    const AppendArgs app{(const uint16_t*)k_new, (const uint16_t*)v_new,
+                         k_new ? (uint16_t*)const_cast<void*>(k_cache) : nullptr,
+                         k_new ? (uint16_t*)const_cast<void*>(v_cache) : nullptr};
     float* po = reinterpret_cast<float*>(workspace);
     float* pml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + lay.o_bytes);
     const int g = Hq / Hkv;
@@ -522,13 +632,13 @@ hipError_t launch_gqa_decode_partial(const void* q, const void* k_cache, const v
     const float qscale = scale * kLog2e;
     const int np = lay.n_parts;
     if (D == 128) {
-        if (NB == 1) launch_split<128, 1>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np);
-        else if (NB == 2) launch_split<128, 2>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np);
-        else launch_split<128, 4>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np);
+        if (NB == 1) launch_split<128, 1>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app);
+        else if (NB == 2) launch_split<128, 2>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app);
+        else launch_split<128, 4>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app);
     } else {
-        if (NB == 1) launch_split<64, 1>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np);
-        else if (NB == 2) launch_split<64, 2>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np);
-        else launch_split<64, 4>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np);
+        if (NB == 1) launch_split<64, 1>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app);
+        else if (NB == 2) launch_split<64, 2>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app);
+        else launch_split<64, 4>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app);
     }
     return hipGetLastError();
 }

@@ -43,7 +43,8 @@ DecodeLayout decode_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_
 hipError_t launch_gqa_decode_partial(const void* q, const void* k_cache, const void* v_cache,
                                      const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                                      int32_t D, int32_t S_max, float scale, const RopeDev& rope,
-                                     void* workspace, const DecodeLayout& lay, hipStream_t s);
+                                     void* workspace, const DecodeLayout& lay, hipStream_t s,
+                                     const void* k_new = nullptr, const void* v_new = nullptr);
 hipError_t launch_gqa_decode_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                                      int32_t D, int32_t S_max, const void* workspace,
                                      const DecodeLayout& lay, void* out, hipStream_t s);

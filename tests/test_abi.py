@@ -106,6 +106,29 @@ def test_decode_validation(m):
     assert lib.gqa_decode_combine(P, 2, 16, 2, 128, 64, P, 1, 0, P, None) == m.ERR_WORKSPACE_TOO_SMALL
 
 
+def test_decode_append_validation(m):
+    lib = m.lib()
+
+    def app(q=P, kn=P, vn=P, k=P, v=P, sl=P, B=2, Hq=16, Hkv=2, D=128, S=64, scale=0.1, rope=None,
+            out=P, ws=P, wsn=1 << 30):
+        return lib.gqa_decode_append(q, kn, vn, k, v, sl, B, Hq, Hkv, D, S, scale, rope, out, ws,
+                                     wsn, None)
+    assert app(kn=0) == m.ERR_INVALID_ARGUMENT
+    assert app(vn=0) == m.ERR_INVALID_ARGUMENT
+    assert app(kn=MIS) == m.ERR_INVALID_ARGUMENT
+    assert app(vn=MIS) == m.ERR_INVALID_ARGUMENT
+    assert app(out=0) == m.ERR_INVALID_ARGUMENT
+    assert app(out=MIS) == m.ERR_INVALID_ARGUMENT
+    assert app(Hq=15) == m.ERR_INVALID_ARGUMENT
+    assert app(D=96) == m.ERR_UNSUPPORTED
+    assert app(ws=P + 16) == m.ERR_INVALID_ARGUMENT
+    assert app(scale=float("inf")) == m.ERR_INVALID_ARGUMENT
+    need = m.gqa_decode_workspace_size(2, 16, 2, 128, 64)
+    assert app(wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+    assert app(wsn=0, rope=_rope(m, scaling=m.ROPE_PLAIN, base=1e4, rotary_dim=7)) \
+        == m.ERR_INVALID_ARGUMENT
+
+
 def test_prefill_validation(m):
     lib = m.lib()
 

@@ -154,3 +154,123 @@ def test_decode_full_size_4k(m):
 
 def test_decode_full_size_32k_yarn_ragged(m):
     _full_size(m, DECODE_32K_YARN)
+
+
+# ---------------------------------------------------------------------------
+# gqa_decode_append: the decode step with its cache write fused
+# ---------------------------------------------------------------------------
+
+def _bf16_ulp(x):
+    """One bf16 unit in the last place at the magnitude of x (x != 0)."""
+    return np.exp2(np.floor(np.log2(np.maximum(np.abs(x), 1e-30))) - 7)
+
+
+def _check_written_rows(m, kc_dev, vc_dev, k0, v0, kref, kn, vn, lens):
+    """Row L-1 of every kv head holds the rotated new key (within one bf16
+    unit of the fp64 rotation: the kernel rotates in fp32) and exactly the
+    new value; every other row is untouched."""
+    kg, vg = from_dev(kc_dev), from_dev(vc_dev)
+    for b, L in enumerate(lens):
+        r = int(L) - 1
+        err = np.abs(kg[b, :, r] - kref[b, :, r])
+        assert np.all(err <= _bf16_ulp(kref[b, :, r]) + 1e-30), f"written key row b={b}"
+        assert np.array_equal(vg[b, :, r], bf16_bits_to_f64(vn)[b]), f"written value row b={b}"
+        kg[b, :, r] = k0[b, :, r]
+        vg[b, :, r] = v0[b, :, r]
+    assert np.array_equal(kg, k0) and np.array_equal(vg, v0), "rows other than L-1 changed"
+
+
+APPEND_CASES = [
+    # (B, Hq, Hkv, D, S_max, seq_lens, rope)
+    (3, 16, 2, 128, 700, [700, 333, 1], "yarn"),    # new row: last of the cache, mid tile, alone
+    (4, 8, 8, 128, 130, [32, 33, 64, 65], "plain"),  # new row at both ends of a 32-row tile
+    (2, 16, 1, 128, 300, [300, 97], "none"),        # MQA, key stored as given
+    (2, 8, 2, 64, 200, [200, 17], "yarn"),          # head dim 64
+    (2, 12, 4, 128, 129, [129, 2], "plain"),        # g=3
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}D{c[3]}{c[6]}"
+                                                    for c in APPEND_CASES])
+def test_decode_append_parity(m, case):
+    import torch
+    from workloads import ROPE_NONE, randn_bf16
+    B, Hq, Hkv, D, S, lens, kind = case
+    rope = {"yarn": rope_settings(ROPE_YARN, base=5e5, factor=4.0, original_max_position=64),
+            "plain": rope_settings(ROPE_PLAIN, base=1e4),
+            "none": rope_settings(ROPE_NONE)}[kind]
+    lens = np.array(lens, dtype=np.int32)
+    d = decode_inputs_host(B, Hq, Hkv, D, S, 31, lens)
+    rng = np.random.default_rng(32)
+    kn, vn = randn_bf16(rng, (B, Hkv, D)), randn_bf16(rng, (B, Hkv, D))
+    scale = 1.0 / math.sqrt(D)
+    print(f"[case] append B={B} Hq={Hq} Hkv={Hkv} D={D} lens={list(lens)} rope={kind}", flush=True)
+    kc, vc = to_dev(d["k"]), to_dev(d["v"])
+    out = m.gqa_decode_append(to_dev(d["q"]), to_dev(kn), to_dev(vn), kc, vc,
+                              torch.from_numpy(lens).cuda(), scale, q_rope=rope)
+    torch.cuda.synchronize()
+    k0, v0 = bf16_bits_to_f64(d["k"]), bf16_bits_to_f64(d["v"])
+    ref, kref, _ = oatt.decode_append(bf16_bits_to_f64(d["q"]), bf16_bits_to_f64(kn),
+                                      bf16_bits_to_f64(vn), k0, v0, lens, scale,
+                                      None if kind == "none" else rope)
+    assert_close(from_dev(out), ref, f"append {case}")
+    _check_written_rows(m, kc, vc, k0, v0, kref, kn, vn, lens)
+
+
+def test_decode_append_then_decode_matches(m):
+    """After an append the caches hold the new row: a plain decode over them
+    gives the append step's output."""
+    import torch
+    from workloads import randn_bf16
+    B, Hq, Hkv, D, S = 2, 16, 2, 128, 400
+    lens = np.array([400, 123], dtype=np.int32)
+    d = decode_inputs_host(B, Hq, Hkv, D, S, 41, lens)
+    rng = np.random.default_rng(42)
+    kn, vn = randn_bf16(rng, (B, Hkv, D)), randn_bf16(rng, (B, Hkv, D))
+    rope = rope_settings(ROPE_YARN, base=5e5, factor=4.0, original_max_position=64)
+    sl = torch.from_numpy(lens).cuda()
+    kc, vc, q = to_dev(d["k"]), to_dev(d["v"]), to_dev(d["q"])
+    print("[case] append then decode", flush=True)
+    o1 = m.gqa_decode_append(q, to_dev(kn), to_dev(vn), kc, vc, sl, 0.1, q_rope=rope)
+    o2 = m.gqa_decode(q, kc, vc, sl, 0.1, q_rope=rope)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_decode_append_full_size_32k_yarn_ragged(m, n_pairs=16):
+    import torch
+    cfg = DECODE_32K_YARN
+    B, Hq, Hkv, D, S = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.S_max
+    lens = cfg.seq_lens()
+    print(f"[case] append full size B={B} S_max={S}", flush=True)
+    q = device_randn_bf16((B, Hq, D), cfg.seed * 10 + 1)
+    k = device_randn_bf16((B, Hkv, S, D), cfg.seed * 10 + 2)
+    v = device_randn_bf16((B, Hkv, S, D), cfg.seed * 10 + 3)
+    kn = device_randn_bf16((B, Hkv, D), cfg.seed * 10 + 4)
+    vn = device_randn_bf16((B, Hkv, D), cfg.seed * 10 + 5)
+    k0, v0 = k.clone(), v.clone()
+    sl = torch.from_numpy(lens).cuda()
+    out = m.gqa_decode_append(q, kn, vn, k, v, sl, cfg.scale, q_rope=cfg.rope())
+    torch.cuda.synchronize()
+    # every row but L-1 untouched (compared on the device)
+    rows = torch.from_numpy(lens.astype(np.int64) - 1).cuda()
+    bi = torch.arange(B, device="cuda")
+    k0[bi, :, rows] = k[bi, :, rows]
+    v0[bi, :, rows] = v[bi, :, rows]
+    assert torch.equal(k0, k) and torch.equal(v0, v)
+    assert torch.equal(v[bi, :, rows], vn)
+    got = from_dev(out)
+    rng = np.random.default_rng(cfg.seed + 7)
+    pairs = [(int(rng.integers(B)), int(rng.integers(Hq))) for _ in range(n_pairs)]
+    qf, knf, vnf = bf16_tensor_to_f64(q), bf16_tensor_to_f64(kn), bf16_tensor_to_f64(vn)
+    for b, h in pairs:
+        kv = h // (Hq // Hkv)
+        L = int(lens[b])
+        kb = bf16_tensor_to_f64(k0[b, kv, :L])      # rows < L-1 as they were
+        vb = bf16_tensor_to_f64(v0[b, kv, :L])
+        kc, vc = oatt.append_rows(kb[None, None], vb[None, None], knf[b, kv][None, None],
+                                  vnf[b, kv][None, None], np.array([L]), cfg.rope())
+        ref = oatt.decode_one(qf[b, h], kc[0, 0], vc[0, 0], L, cfg.scale, cfg.rope())
+        assert_close(got[b, h], ref, f"append full size (b={b}, h={h}, L={L})")
+        kw = bf16_tensor_to_f64(k[b, kv, L - 1])
+        assert np.all(np.abs(kw - kc[0, 0, L - 1]) <= _bf16_ulp(kc[0, 0, L - 1]))
