@@ -156,6 +156,66 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale: float, rop
     return decode(q, kc, vc, seq_lens, scale, rope_p, pairs=pairs), kc, vc
 
 
+def window_rows(seq_len: int, S_max: int, window: int = 0, rolling: bool = False):
+    """Cache rows the new token (position seq_len-1) attends to.
+
+    Sliding window ([transformer架构] §2.5.1): query i sees keys j with
+    i - w + 1 <= j <= i.  Linear cache: position p is row p (window 0 = no
+    window).  Rolling buffer ([transformer架构] §2.5.2): position t lives in
+    slot t mod S_max, so the buffer holds the last S_max positions and the
+    window is the buffer (window must be 0).
+    """
+    L = int(seq_len)
+    if rolling:
+        if window:
+            raise ValueError("a rolling buffer's window is its size")
+        positions = np.arange(max(0, L - S_max), L)
+        return positions % S_max
+    w = int(window) if window else L
+    return np.arange(max(0, L - w), L)
+
+
+def decode_window(q, k_cache, v_cache, seq_lens, scale: float, rope_p, window: int = 0,
+                  rolling: bool = False, pairs=None) -> np.ndarray:
+    """Single-token decode over the rows of :func:`window_rows`; q rotated at
+    its absolute position seq_lens[b]-1 (keys are cached after RoPE, so a
+    rolling buffer needs no re-rotation)."""
+    B, Hq, _ = q.shape
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    out = np.full((B, Hq, v_cache.shape[-1]), np.nan)
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(Hq)]
+    for b, h in pairs:
+        kv = kv_head_of(h, Hq, Hkv)
+        L = int(seq_lens[b])
+        rows = window_rows(L, S_max, window, rolling)
+        qv = np.asarray(q[b, h], dtype=np.float64)[None, :]
+        if rope_p is not None:
+            qv = _rope.rotate_rows(qv, np.array([L - 1]), rope_p)
+        out[b, h] = attend(qv[0], np.asarray(k_cache[b, kv], np.float64)[rows],
+                           np.asarray(v_cache[b, kv], np.float64)[rows], scale)
+    return out
+
+
+def append_rows_window(k_cache, v_cache, k_new, v_new, seq_lens, rope_p, rolling: bool = False):
+    """:func:`append_rows` for either cache: the new token (position
+    seq_lens[b]-1) goes to row seq_lens[b]-1 of a linear cache, or to slot
+    (seq_lens[b]-1) mod S_max of a rolling buffer ([transformer架构] §2.5.2:
+    the oldest entry is overwritten)."""
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    S_max = kc.shape[2]
+    for b in range(kc.shape[0]):
+        pos = int(seq_lens[b]) - 1
+        row = pos % S_max if rolling else pos
+        kr = np.asarray(k_new[b], dtype=np.float64)
+        if rope_p is not None:
+            kr = _rope.rotate_rows(kr[None], np.array([pos]), rope_p)[0]
+        kc[b, :, row] = kr
+        vc[b, :, row] = np.asarray(v_new[b], dtype=np.float64)
+    return kc, vc
+
+
 def page_attention(x, Wq, Wk, Wv, n_head: int, n_kv_head: int) -> np.ndarray:
     """The pages' whole GQA attention function (projection, head split, K/V
     repeated g times along the head axis, causal softmax, heads merged), with

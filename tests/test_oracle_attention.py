@@ -140,6 +140,71 @@ def test_decode_append_builds_the_prefill_cache():
     assert np.array_equal(vc2[0, :, 4], v[0, :, 3]) and np.array_equal(vc2[1, :, 8], v[1, :, 3])
 
 
+def test_sliding_window_decode_pins():
+    """Window 1 attends only to the new token itself (output = its value);
+    window 2 is the two-key logistic; a window at least as long as the
+    context is plain decode; and the last row of the pages' band-masked
+    attention (softmax(QK^T scale + M) V with M = 0 for i-w+1 <= j <= i,
+    -inf elsewhere) equals the windowed decode."""
+    B, Hq, Hkv, S, D = 2, 4, 2, 40, 16
+    q, k, v = _rand((B, Hq, D), 51), _rand((B, Hkv, S, D), 52), _rand((B, Hkv, S, D), 53)
+    lens = np.array([40, 23])
+    p = rope_settings(ROPE_PLAIN, base=1e4)
+    o1 = att.decode_window(q, k, v, lens, 0.3, p, window=1)
+    for b in range(B):
+        for h in range(Hq):
+            assert np.allclose(o1[b, h], v[b, h // 2, lens[b] - 1], rtol=0, atol=1e-15)
+    o2 = att.decode_window(q, k, v, lens, 0.3, None, window=2)
+    for b in range(B):
+        for h in range(Hq):
+            L, kv = lens[b], h // 2
+            d = 0.3 * (q[b, h] @ k[b, kv, L - 1] - q[b, h] @ k[b, kv, L - 2])
+            w_new = 1.0 / (1.0 + math.exp(-d))
+            ref = w_new * v[b, kv, L - 1] + (1 - w_new) * v[b, kv, L - 2]
+            assert np.allclose(o2[b, h], ref, rtol=1e-13, atol=1e-14)
+    assert np.allclose(att.decode_window(q, k, v, lens, 0.3, p, window=64),
+                       att.decode(q, k, v, lens, 0.3, p), rtol=0, atol=0)
+    w = 7
+    ow = att.decode_window(q, k, v, lens, 0.3, p, window=w)
+    for b in range(B):
+        L = lens[b]
+        i = L - 1
+        qr = rope.rotate_rows(q[b], np.full(Hq, i), p)
+        for h in range(Hq):
+            s_ = 0.3 * k[b, h // 2, :L] @ qr[h]
+            M = np.where((np.arange(L) >= i - w + 1) & (np.arange(L) <= i), 0.0, -np.inf)
+            a = np.exp(s_ + M - np.max(s_ + M))
+            assert np.allclose(ow[b, h], (a / a.sum()) @ v[b, h // 2, :L], rtol=1e-12, atol=1e-13)
+
+
+def test_rolling_buffer_equals_linear_cache_with_its_window():
+    """Writing position t to slot t mod S of a rolling buffer and attending
+    to every filled slot is the linear cache with window S, for contexts
+    shorter and longer than the buffer (older positions overwritten)."""
+    B, Hq, Hkv, D, S = 3, 4, 1, 16, 16
+    lens = np.array([5, 16, 53])
+    Lmax = int(lens.max())
+    kpos, vpos = _rand((B, Hkv, Lmax, D), 61), _rand((B, Hkv, Lmax, D), 62)
+    q = _rand((B, Hq, D), 63)
+    p = rope_settings(ROPE_YARN, base=1e4, factor=4.0, original_max_position=8)
+    roll_k, roll_v = _rand((B, Hkv, S, D), 64), _rand((B, Hkv, S, D), 65)   # junk in unwritten slots
+    for b in range(B):
+        for t in range(lens[b]):
+            roll_k[b, :, t % S], roll_v[b, :, t % S] = kpos[b, :, t], vpos[b, :, t]
+    a = att.decode_window(q, roll_k, roll_v, lens, 0.25, p, rolling=True)
+    lin = att.decode_window(q, kpos, vpos, lens, 0.25, p, window=S)
+    assert np.allclose(a, lin, rtol=1e-13, atol=1e-14)
+    # the append step writes slot (L-1) mod S (rolling) or row L-1 (linear)
+    kn, vn = _rand((B, Hkv, D), 66), _rand((B, Hkv, D), 67)
+    kr, vr = att.append_rows_window(roll_k, roll_v, kn, vn, lens, p, rolling=True)
+    for b in range(B):
+        slot = (lens[b] - 1) % S
+        assert np.array_equal(vr[b, :, slot], vn[b])
+        assert np.allclose(kr[b, :, slot], rope.rotate_rows(kn[b], np.full(Hkv, lens[b] - 1), p))
+        others = [r for r in range(S) if r != slot]
+        assert np.array_equal(kr[b, :, others], roll_k[b, :, others])
+
+
 def test_tiny_demo_shapes_and_param_counts():
     """[注意力变体与MoE] "MQA 与 GQA": the demo's printed output shape and K/V
     parameter counts for n_kv_head = 8, 2, 1."""
