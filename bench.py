@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of sections (decode32k,decode4k,append32k,"
+    ap.add_argument("--only", default="", help="comma list of sections (decode32k,decode4k,append32k,window,"
                     "prefill,sparse,rope) for profiling runs")
     return ap.parse_args()
 
@@ -172,6 +172,40 @@ def bench_decode_append(cfg, steps, warmup, nsets=2):
     del sets
     torch.cuda.empty_cache()
     return dict(ms=ms, kv_bytes=kv_bytes)
+
+
+def bench_decode_window(cfg, steps, warmup, window, rolling, nsets=4):
+    """gqa_decode_window on the 32K workload's batch, q heads and lengths: a
+    `window`-token sliding window over the linear cache, or a rolling buffer
+    of `window` slots (contexts longer than the buffer)."""
+    import torch
+
+    import mqa_kv_cache_amd as m
+    from workloads import device_randn_bf16
+    B, Hq, Hkv, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.D
+    S = window if rolling else cfg.S_max
+    lens_np = cfg.seq_lens()
+    lens = torch.from_numpy(lens_np).cuda()
+    sets = [(device_randn_bf16((B, Hq, D), cfg.seed * 100 + 10 * i + 1),
+             device_randn_bf16((B, Hkv, S, D), cfg.seed * 100 + 10 * i + 2),
+             device_randn_bf16((B, Hkv, S, D), cfg.seed * 100 + 10 * i + 3)) for i in range(nsets)]
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(m.gqa_decode_workspace_size(B, Hq, Hkv, D, S), dtype=torch.uint8, device="cuda")
+    rows = int(sum(min(int(L), window) for L in lens_np))
+    kv_bytes = rows * Hkv * D * 2 * 2
+    rope = cfg.rope()
+
+    def step(i):
+        q, k, v = sets[i % nsets]
+        m.gqa_decode_window(q, k, v, lens, cfg.scale, window=0 if rolling else window,
+                            rolling=rolling, q_rope=rope, out=out, workspace=ws)
+
+    ms = timed_loop(step, steps, warmup)
+    label = f"rolling{window}" if rolling else f"window{window}"
+    log(f"[bench] decode {label} (32K contexts): step {ms * 1e3:.1f} us, {kv_bytes / ms / 1e6:.0f} GB/s")
+    del sets
+    torch.cuda.empty_cache()
+    return dict(ms=ms, kv_bytes=kv_bytes, label=label)
 
 
 def bench_prefill(cfg, steps, warmup):
@@ -317,6 +351,9 @@ def main():
         res["d4"] = bench_decode(DECODE_4K, K, W, nsets=4, label="decode 4K")
     if want("append32k"):
         res["da"] = bench_decode_append(DECODE_32K_YARN, K, W)
+    if want("window"):
+        res["dw"] = bench_decode_window(DECODE_32K_YARN, K, W, 4096, False)
+        res["dr"] = bench_decode_window(DECODE_32K_YARN, K, W, 4096, True)
     if want("prefill"):
         res["p"] = bench_prefill(PREFILL_8K, K, W)
     if want("sparse"):
@@ -378,6 +415,13 @@ def main():
         line["decode_append_32k"] = {"GB/s": round(da["kv_bytes"] / da["ms"] / 1e6, 1),
                                      "pct_of_hbm_peak": round(100 * da["kv_bytes"] / da["ms"] / 1e6 / HBM_PEAK_GBS, 2),
                                      "ms_per_step": round(da["ms"], 5)}
+    for key in ("dw", "dr"):
+        if key in res:
+            r = res[key]
+            line[f"decode_{r['label']}_32k"] = {
+                "GB/s": round(r["kv_bytes"] / r["ms"] / 1e6, 1),
+                "pct_of_hbm_peak": round(100 * r["kv_bytes"] / r["ms"] / 1e6 / HBM_PEAK_GBS, 2),
+                "ms_per_step": round(r["ms"], 5)}
     if "p" in res:
         p = res["p"]
         line["prefill_8k"] = {"TFLOP/s": round(p["tflops"], 1),

@@ -198,6 +198,33 @@ gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gqa_decode_window -- gqa_decode (optionally with gqa_decode_append's cache
+ * write) over a sliding window or a rolling-buffer cache.
+ * Sliding window ([transformer架构] §2.5.1): the query at position i sees
+ * keys i-w+1 .. i.  With a linear cache (rolling = 0, row = position,
+ * seq_lens[b] in [1, S_max]) the new token (position L-1, L = seq_lens[b])
+ * attends to rows max(0, L-window) .. L-1; window 0 means no window.
+ * Rolling buffer ([transformer架构] §2.5.2, rolling = 1, window 0): position t
+ * lives in slot t mod S_max, so the cache holds the last S_max positions and
+ * the new token attends to every filled slot, min(L, S_max) of them; L may
+ * exceed S_max.  q is rotated at its absolute position L-1 in both; keys are
+ * cached after RoPE, so nothing is re-rotated.
+ *
+ *   k_new, v_new  NULL (no cache write) or, both, as in gqa_decode_append: the
+ *                 new row goes to row L-1 (linear) or slot (L-1) mod S_max
+ *                 (rolling) before the attention reads it
+ *   window        >= 0; must be 0 when rolling = 1 (the buffer is the window)
+ *   rolling       0 or 1
+ * Other arguments, limits and errors as gqa_decode / gqa_decode_append.
+ */
+gqa_status gqa_decode_window(const void* q, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, const int32_t* seq_lens,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S_max,
+                             int32_t window, int32_t rolling, float scale,
+                             const gqa_rope_params* q_rope, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gqa_prefill_causal -- causal GQA attention over a whole prompt
  * ([注意力变体与MoE] "MQA 与 GQA", attention(): scores q k^T / sqrt(hd) with the
  * strict upper triangle masked to -inf, softmax, weighted sum of V):

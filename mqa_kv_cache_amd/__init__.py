@@ -27,7 +27,8 @@ OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_DEVICE =
 ROPE_NONE, ROPE_PLAIN, ROPE_PI, ROPE_NTK, ROPE_YARN = 0, 1, 2, 3, 4
 
 EXPORTED = [
-    "rope_apply", "gqa_decode", "gqa_decode_parts", "gqa_decode_append", "gqa_decode_workspace_size",
+    "rope_apply", "gqa_decode", "gqa_decode_parts", "gqa_decode_append", "gqa_decode_window",
+    "gqa_decode_workspace_size",
     "gqa_decode_workspace_size_parts", "gqa_decode_partial", "gqa_decode_combine",
     "gqa_prefill_causal", "gqa_prefill_workspace_size",
     "topk_sparse_decode", "topk_sparse_decode_workspace_size", "kv_bytes_per_token",
@@ -78,6 +79,11 @@ _lib.gqa_decode_append.restype = _c_int32
 _lib.gqa_decode_append.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                    _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, ctypes.c_float,
                                    _rope_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]
+_lib.gqa_decode_window.restype = _c_int32
+_lib.gqa_decode_window.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                   _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                   _c_int32, ctypes.c_float, _rope_p, _c_void_p, _c_void_p,
+                                   _c_size_t, _c_void_p]
 _lib.gqa_decode_parts.restype = _c_int32
 _lib.gqa_decode_parts.argtypes = _lib.gqa_decode.argtypes[:-1] + [_c_int32, _c_void_p]
 _lib.gqa_decode_partial.restype = _c_int32
@@ -250,6 +256,46 @@ def gqa_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale: float,
                                 float(scale), rope_params(q_rope), out.data_ptr(),
                                 workspace.data_ptr(), workspace.numel(), _stream(stream))
     _check(st, "gqa_decode_append")
+    return out
+
+
+def gqa_decode_window(q, k_cache, v_cache, seq_lens, scale: float, window: int = 0,
+                      rolling: bool = False, k_new=None, v_new=None, q_rope=None, out=None,
+                      workspace=None, stream=None) -> torch.Tensor:
+    """gqa_decode over the last `window` positions of a linear cache, or over a
+    rolling buffer (rolling=True, window 0: position t in slot t mod S_max),
+    optionally writing the new token's k_new/v_new [B,Hkv,D] first.  Returns
+    out [B,Hq,D] bf16."""
+    B, Hq, D = q.shape
+    _, Hkv, S_max, _ = k_cache.shape
+    _shape(k_cache, (B, Hkv, S_max, D), "k_cache")
+    _shape(v_cache, (B, Hkv, S_max, D), "v_cache")
+    _shape(seq_lens, (B,), "seq_lens")
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, nm)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None:
+        _shape(k_new, (B, Hkv, D), "k_new")
+        _shape(v_new, (B, Hkv, D), "v_new")
+        _dev(k_new, "k_new")
+        _dev(v_new, "v_new")
+    _dev(seq_lens, "seq_lens", dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _shape(out, (B, Hq, D), "out")
+    _dev(out, "out")
+    need = gqa_decode_workspace_size(B, Hq, Hkv, D, S_max)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    st = _lib.gqa_decode_window(q.data_ptr(), k_new.data_ptr() if k_new is not None else None,
+                                v_new.data_ptr() if v_new is not None else None, k_cache.data_ptr(),
+                                v_cache.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, S_max,
+                                int(window), int(bool(rolling)), float(scale), rope_params(q_rope),
+                                out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                _stream(stream))
+    _check(st, "gqa_decode_window")
     return out
 
 

@@ -195,18 +195,22 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                             workspace, workspace_bytes, 0, stream);
 }
 
-gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+gqa_status gqa_decode_window(const void* q, const void* k_new, const void* v_new, void* k_cache,
                              void* v_cache, const int32_t* seq_lens, int32_t B, int32_t Hq,
-                             int32_t Hkv, int32_t D, int32_t S_max, float scale,
-                             const gqa_rope_params* q_rope, void* out, void* workspace,
+                             int32_t Hkv, int32_t D, int32_t S_max, int32_t window, int32_t rolling,
+                             float scale, const gqa_rope_params* q_rope, void* out, void* workspace,
                              size_t workspace_bytes, void* stream) {
     gqa_status st = check_decode_shape(B, Hq, Hkv, D, S_max);
     if (st != GQA_OK) return st;
-    if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
-    if (!q || !k_new || !v_new || !k_cache || !v_cache || !seq_lens || !workspace || !out)
+    if (!std::isfinite(scale) || window < 0 || (rolling != 0 && rolling != 1))
         return GQA_ERR_INVALID_ARGUMENT;
-    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
-        !aligned16(v_cache) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    if (rolling && window != 0) return GQA_ERR_INVALID_ARGUMENT;
+    if ((k_new == nullptr) != (v_new == nullptr)) return GQA_ERR_INVALID_ARGUMENT;
+    if (!q || !k_cache || !v_cache || !seq_lens || !workspace || !out)
+        return GQA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || (k_new && (!aligned16(k_new) || !aligned16(v_new))) ||
+        !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return GQA_ERR_INVALID_ARGUMENT;
     RopeDev rd;
     st = rope_prepare(q_rope, D, &rd);
@@ -215,10 +219,20 @@ gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new
     if (workspace_bytes < lay.total) return GQA_ERR_WORKSPACE_TOO_SMALL;
     st = from_hip(launch_gqa_decode_partial(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max,
                                             scale, rd, workspace, lay, (hipStream_t)stream, k_new,
-                                            v_new));
+                                            v_new, window, rolling));
     if (st != GQA_OK) return st;
     return from_hip(launch_gqa_decode_combine(seq_lens, B, Hq, Hkv, D, S_max, workspace, lay, out,
-                                              (hipStream_t)stream));
+                                              (hipStream_t)stream, window, rolling));
+}
+
+gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                             void* v_cache, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t D, int32_t S_max, float scale,
+                             const gqa_rope_params* q_rope, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    if (!k_new || !v_new) return GQA_ERR_INVALID_ARGUMENT;
+    return gqa_decode_window(q, k_new, v_new, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max, 0,
+                             0, scale, q_rope, out, workspace, workspace_bytes, stream);
 }
 
 static gqa_status check_prefill_shape(int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t D) {

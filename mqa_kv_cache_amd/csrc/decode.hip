@@ -138,8 +138,36 @@ struct RowSpace {
     int64_t total;
     int64_t R;
 };
-__device__ __forceinline__ int ctx_len(const int32_t* seq_lens, int b, int S_max) {
-    return min(max(seq_lens[b], 1), S_max);
+// Which cache rows a context's new token attends to ([transformer架构]
+// §2.5.1 sliding window: query i sees keys i-w+1 .. i; §2.5.2 rolling
+// buffer: position t lives in slot t mod S_max).  Linear cache: positions
+// max(0, L-window) .. L-1 are rows of the same index (window 0: all L);
+// rolling buffer: every filled slot, min(L, S_max) of them from row 0.  The
+// query's position is L-1 in both (keys are cached after RoPE).
+struct CacheView {
+    int window;    // 0 = no window
+    int rolling;   // 1 = rolling buffer of S_max slots (window 0)
+};
+struct CtxGeom {
+    int lo;        // first cache row
+    int n;         // rows attended
+    int qpos;      // the new token's position
+    int newrow;    // the cache row of that position
+};
+__device__ __forceinline__ CtxGeom ctx_geom(const int32_t* seq_lens, int b, int S_max,
+                                           const CacheView& cv) {
+    const int raw = max(seq_lens[b], 1);
+    if (cv.rolling) {
+        const int n = min(raw, S_max);
+        return CtxGeom{0, n, raw - 1, (int)((unsigned)(raw - 1) % (unsigned)S_max)};
+    }
+    const int L = min(raw, S_max);
+    const int lo = cv.window > 0 ? max(0, L - cv.window) : 0;
+    return CtxGeom{lo, L - lo, L - 1, L - 1};
+}
+__device__ __forceinline__ int ctx_len(const int32_t* seq_lens, int b, int S_max,
+                                       const CacheView& cv) {
+    return ctx_geom(seq_lens, b, S_max, cv).n;
 }
 // inclusive prefix sum over the 64 lanes
 __device__ __forceinline__ int64_t wave_scan_incl(int64_t x, int lane) {
@@ -151,11 +179,11 @@ __device__ __forceinline__ int64_t wave_scan_incl(int64_t x, int lane) {
     return x;
 }
 __device__ __forceinline__ RowSpace row_space(const int32_t* seq_lens, int B, int Hkv, int S_max,
-                                              int n_parts, int lane) {
+                                              int n_parts, int lane, const CacheView& cv) {
     int64_t total = 0;
     for (int c0 = 0; c0 < B; c0 += 64) {
         const int bb = c0 + lane;
-        int64_t rows = bb < B ? (int64_t)Hkv * ctx_len(seq_lens, bb, S_max) : 0;
+        int64_t rows = bb < B ? (int64_t)Hkv * ctx_len(seq_lens, bb, S_max, cv) : 0;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) rows += __shfl_xor(rows, o, 64);
         total += rows;
@@ -163,13 +191,14 @@ __device__ __forceinline__ RowSpace row_space(const int32_t* seq_lens, int B, in
     return RowSpace{total, (total + n_parts - 1) / n_parts};
 }
 // The context holding global row x < total: batch b, the global row `base` of
-// its (kv 0, row 0), and its length L.
+// its (kv 0, row 0), and its number of attended rows L.
 __device__ __forceinline__ void locate(const int32_t* seq_lens, int B, int Hkv, int S_max,
-                                       int64_t x, int lane, int& b, int64_t& base, int& L) {
+                                       int64_t x, int lane, const CacheView& cv, int& b,
+                                       int64_t& base, int& L) {
     int64_t run = 0;
     for (int c0 = 0; c0 < B; c0 += 64) {
         const int bb = c0 + lane;
-        const int Lb = bb < B ? ctx_len(seq_lens, bb, S_max) : 0;
+        const int Lb = bb < B ? ctx_len(seq_lens, bb, S_max, cv) : 0;
         const int64_t incl = wave_scan_incl((int64_t)Hkv * Lb, lane);
         const uint64_t hit = __builtin_amdgcn_ballot_w64(bb < B && x < run + incl);
         if (hit) {
@@ -366,7 +395,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ seq_lens, int B, int Hq,
     int Hkv, int S_max, float qscale, RopeDev rope, float* __restrict__ part_o,
-    float* __restrict__ part_ml, int n_parts, AppendArgs app) {
+    float* __restrict__ part_ml, int n_parts, AppendArgs app, CacheView cv) {
     constexpr int KU = D / 32;
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4, n = lane & 15;
@@ -375,7 +404,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
     // derived address and buffer descriptor in scalar registers
     const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
     if (w >= n_parts) return;
-    const RowSpace rs = row_space(seq_lens, B, Hkv, S_max, n_parts, lane);
+    const RowSpace rs = row_space(seq_lens, B, Hkv, S_max, n_parts, lane, cv);
     int64_t gs = (int64_t)w * rs.R;
     const int64_t ge = min(gs + rs.R, rs.total);
     if (gs >= ge) return;
@@ -383,9 +412,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
     // locate the context holding global row gs
     int b, L;
     int64_t base;   // global row of (b, kv 0, row 0)
-    locate(seq_lens, B, Hkv, S_max, gs, lane, b, base, L);
+    locate(seq_lens, B, Hkv, S_max, gs, lane, cv, b, base, L);
     b = __builtin_amdgcn_readfirstlane(b);
     L = __builtin_amdgcn_readfirstlane(L);
+    CtxGeom geo = ctx_geom(seq_lens, b, S_max, cv);   // geo.n == L
     int kv = (int)((gs - base) / L);
     QFreq<D> fq;
     load_freq<D>(rope, G, fq);
@@ -395,11 +425,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
         const int r0 = (int)(gs - ctx0);
         const int r1 = (int)min((int64_t)L, ge - ctx0);
 
-        // buffers end at this piece's last row: the prefetch past it reads zeros for free
+        // rows r of the piece are cache rows geo.lo + r; buffers end at this
+        // piece's last row: the prefetch past it reads zeros for free
         const size_t slice = ((size_t)b * Hkv + kv) * (size_t)S_max * D;
+        const size_t first = slice + (size_t)geo.lo * D;
         const uint32_t nbytes = (uint32_t)r1 * D * 2u;
-        const __amdgpu_buffer_rsrc_t kr = make_rsrc(k_cache + slice, nbytes);
-        const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_cache + slice, nbytes);
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(k_cache + first, nbytes);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_cache + first, nbytes);
 
         // q is requested first, then the first tiles; q is prepared while the
         // tiles are in flight
@@ -411,12 +443,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
         load_tile<D>(ta, kr, vr, r0, G, n);
 
         u32x4 qhi[NB][KU], qlo[NB][KU];
-        prep_q<D, NB>(qraw, fq, L, qscale, rope, G, qhi, qlo);
-        // this piece holds the new token's row when it ends the context
-        const bool ends = APPEND && r1 == L;
-        const int rr_new = (L - 1 - r0) & 31;     // its row in the tile that holds it
+        prep_q<D, NB>(qraw, fq, geo.qpos + 1, qscale, rope, G, qhi, qlo);
+        // the new token's row, as a row of this context's attended range
+        const int r_new = geo.newrow - geo.lo;
+        const bool ends = APPEND && r0 <= r_new && r_new < r1;   // this piece holds it
+        const int rr_new = (r_new - r0) & 31;                     // its row in its tile
         if constexpr (APPEND)
-            if (ends) rotate_new_key<D>(nr, L, fq, rope, G);
+            if (ends) rotate_new_key<D>(nr, geo.qpos + 1, fq, rope, G);
 
         f32x4 o[NB][8];
         float m_run[NB], l_run[NB];
@@ -430,7 +463,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
 
         auto fix = [&](DecodeTile<D>& t, int t0) {
             if constexpr (APPEND)
-                if (ends && t0 + 32 >= L) swap_new_row<D>(t, nr, rr_new, G, n);
+                if (ends && t0 <= r_new && r_new < t0 + 32) swap_new_row<D>(t, nr, rr_new, G, n);
         };
         for (int t0 = r0;;) {
             load_tile<D>(tb, kr, vr, t0 + 32, G, n);
@@ -447,7 +480,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
 
         if constexpr (APPEND)
             if (ends) {
-                const size_t row = slice + (size_t)(L - 1) * D;
+                const size_t row = slice + (size_t)geo.newrow * D;
                 store_new_row<D>(nr, app.k_cache + row, app.v_cache + row, rr_new, G, n);
             }
 
@@ -481,7 +514,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
             kv = 0;
             base += (int64_t)Hkv * L;
             if (++b >= B) break;
-            L = min(max(seq_lens[b], 1), S_max);
+            geo = ctx_geom(seq_lens, b, S_max, cv);
+            L = geo.n;
         }
     }
 }
@@ -495,7 +529,7 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, int B, int Hq, int Hkv, int S_max, int n_parts,
-    uint16_t* __restrict__ out) {
+    uint16_t* __restrict__ out, CacheView cv) {
     constexpr int PER = D / 64;
     const int lane = threadIdx.x & 63;
     const int idx = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
@@ -507,7 +541,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     int64_t total = 0, base = 0;
     for (int c0 = 0; c0 < B; c0 += 64) {
         const int bb = c0 + lane;
-        int64_t rows = bb < B ? (int64_t)Hkv * ctx_len(seq_lens, bb, S_max) : 0;
+        int64_t rows = bb < B ? (int64_t)Hkv * ctx_len(seq_lens, bb, S_max, cv) : 0;
         int64_t before = bb < b ? rows : 0;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) {
@@ -518,7 +552,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
         base += before;
     }
     const int64_t R = (total + n_parts - 1) / n_parts;
-    const int L = ctx_len(seq_lens, b, S_max);
+    const int L = ctx_len(seq_lens, b, S_max, cv);
     const int64_t x0 = base + (int64_t)kv * L;
     const int64_t ctx = (int64_t)b * Hkv + kv;
     const int64_t s0 = x0 / R + ctx;
@@ -592,16 +626,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 template <int D, int NB>
 void launch_split(hipStream_t s, const void* q, const void* k, const void* v, const int32_t* sl,
                   int B, int Hq, int Hkv, int S_max, float qscale, const RopeDev& rope, float* po,
-                  float* pml, int n_parts, const AppendArgs& app) {
+                  float* pml, int n_parts, const AppendArgs& app, const CacheView& cv) {
     const dim3 grid((n_parts + kWaves - 1) / kWaves);
     if (app.k_new)
         hipLaunchKernelGGL((decode_split_kernel<D, NB, true>), grid, dim3(64 * kWaves), 0, s,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sl, B, Hq,
-                           Hkv, S_max, qscale, rope, po, pml, n_parts, app);
+                           Hkv, S_max, qscale, rope, po, pml, n_parts, app, cv);
     else
         hipLaunchKernelGGL((decode_split_kernel<D, NB, false>), grid, dim3(64 * kWaves), 0, s,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sl, B, Hq,
-                           Hkv, S_max, qscale, rope, po, pml, n_parts, app);
+                           Hkv, S_max, qscale, rope, po, pml, n_parts, app, cv);
 }
 
 }  // namespace
@@ -621,7 +655,9 @@ hipError_t launch_gqa_decode_partial(const void* q, const void* k_cache, const v
                                      const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                                      int32_t D, int32_t S_max, float scale, const RopeDev& rope,
                                      void* workspace, const DecodeLayout& lay, hipStream_t s,
-                                     const void* k_new, const void* v_new) {
+                                     const void* k_new, const void* v_new, int32_t window,
+                                     int32_t rolling) {
+    const CacheView cv{window, rolling};
     const AppendArgs app{(const uint16_t*)k_new, (const uint16_t*)v_new,
                          k_new ? (uint16_t*)const_cast<void*>(k_cache) : nullptr,
                          k_new ? (uint16_t*)const_cast<void*>(v_cache) : nullptr};
@@ -632,29 +668,31 @@ hipError_t launch_gqa_decode_partial(const void* q, const void* k_cache, const v
     const float qscale = scale * kLog2e;
     const int np = lay.n_parts;
     if (D == 128) {
-        if (NB == 1) launch_split<128, 1>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app);
-        else if (NB == 2) launch_split<128, 2>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app);
-        else launch_split<128, 4>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app);
+        if (NB == 1) launch_split<128, 1>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app, cv);
+        else if (NB == 2) launch_split<128, 2>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app, cv);
+        else launch_split<128, 4>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app, cv);
     } else {
-        if (NB == 1) launch_split<64, 1>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app);
-        else if (NB == 2) launch_split<64, 2>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app);
-        else launch_split<64, 4>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app);
+        if (NB == 1) launch_split<64, 1>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app, cv);
+        else if (NB == 2) launch_split<64, 2>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app, cv);
+        else launch_split<64, 4>(s, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, S_max, qscale, rope, po, pml, np, app, cv);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_gqa_decode_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                                      int32_t D, int32_t S_max, const void* workspace,
-                                     const DecodeLayout& lay, void* out, hipStream_t s) {
+                                     const DecodeLayout& lay, void* out, hipStream_t s,
+                                     int32_t window, int32_t rolling) {
+    const CacheView cv{window, rolling};
     const float* po = reinterpret_cast<const float*>(workspace);
     const float* pml = reinterpret_cast<const float*>(reinterpret_cast<const char*>(workspace) + lay.o_bytes);
     dim3 cgrid((B * Hq + 3) / 4);
     if (D == 128)
         hipLaunchKernelGGL((decode_combine_kernel<128>), cgrid, dim3(256), 0, s, po, pml, seq_lens,
-                           B, Hq, Hkv, S_max, lay.n_parts, (uint16_t*)out);
+                           B, Hq, Hkv, S_max, lay.n_parts, (uint16_t*)out, cv);
     else
         hipLaunchKernelGGL((decode_combine_kernel<64>), cgrid, dim3(256), 0, s, po, pml, seq_lens,
-                           B, Hq, Hkv, S_max, lay.n_parts, (uint16_t*)out);
+                           B, Hq, Hkv, S_max, lay.n_parts, (uint16_t*)out, cv);
     return hipGetLastError();
 }
 

@@ -44,10 +44,12 @@ hipError_t launch_gqa_decode_partial(const void* q, const void* k_cache, const v
                                      const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                                      int32_t D, int32_t S_max, float scale, const RopeDev& rope,
                                      void* workspace, const DecodeLayout& lay, hipStream_t s,
-                                     const void* k_new = nullptr, const void* v_new = nullptr);
+                                     const void* k_new = nullptr, const void* v_new = nullptr,
+                                     int32_t window = 0, int32_t rolling = 0);
 hipError_t launch_gqa_decode_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                                      int32_t D, int32_t S_max, const void* workspace,
-                                     const DecodeLayout& lay, void* out, hipStream_t s);
+                                     const DecodeLayout& lay, void* out, hipStream_t s,
+                                     int32_t window = 0, int32_t rolling = 0);
 
 // Bytes of one prepared tensor (fp16 K rows, or fp16 V^T tiles) for prefill.
 size_t prefill_prep_bytes(int32_t B, int32_t Hkv, int32_t T, int32_t D);

@@ -129,6 +129,22 @@ def test_decode_append_validation(m):
         == m.ERR_INVALID_ARGUMENT
 
 
+def test_decode_window_validation(m):
+    lib = m.lib()
+
+    def win(kn=0, vn=0, window=0, rolling=0, wsn=1 << 30):
+        return lib.gqa_decode_window(P, kn, vn, P, P, P, 2, 16, 2, 128, 64, window, rolling, 0.1,
+                                     None, P, P, wsn, None)
+    assert win(window=-1) == m.ERR_INVALID_ARGUMENT
+    assert win(rolling=2) == m.ERR_INVALID_ARGUMENT
+    assert win(rolling=1, window=8) == m.ERR_INVALID_ARGUMENT    # the buffer is the window
+    assert win(kn=P) == m.ERR_INVALID_ARGUMENT                   # k_new without v_new
+    assert win(kn=P, vn=MIS) == m.ERR_INVALID_ARGUMENT
+    need = m.gqa_decode_workspace_size(2, 16, 2, 128, 64)
+    assert win(window=5, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+    assert win(rolling=1, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+
+
 def test_prefill_validation(m):
     lib = m.lib()
 

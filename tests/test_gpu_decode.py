@@ -274,3 +274,93 @@ def test_decode_append_full_size_32k_yarn_ragged(m, n_pairs=16):
         assert_close(got[b, h], ref, f"append full size (b={b}, h={h}, L={L})")
         kw = bf16_tensor_to_f64(k[b, kv, L - 1])
         assert np.all(np.abs(kw - kc[0, 0, L - 1]) <= _bf16_ulp(kc[0, 0, L - 1]))
+
+
+# ---------------------------------------------------------------------------
+# gqa_decode_window: sliding window over a linear cache, rolling buffer
+# ---------------------------------------------------------------------------
+
+WINDOW_CASES = [
+    # (B, Hq, Hkv, D, S_max, seq_lens, window, rolling, append)
+    (3, 16, 2, 128, 700, [700, 333, 9], 64, 0, False),     # window < L and a context shorter than it
+    (2, 8, 8, 128, 300, [300, 200], 1, 0, False),          # window 1: the token itself
+    (2, 16, 1, 128, 300, [300, 97], 33, 0, True),          # MQA, append, window crossing a tile
+    (2, 8, 2, 64, 200, [200, 17], 100, 0, True),           # head dim 64
+    (4, 16, 2, 128, 64, [5, 64, 65, 300], 0, 1, False),    # rolling: short, exactly full, wrapped
+    (3, 16, 2, 128, 96, [96, 150, 1000], 0, 1, True),      # rolling with the write (slot (L-1) mod S)
+    (2, 12, 4, 64, 50, [31, 77], 0, 1, True),              # rolling, g=3, head dim 64
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=[f"B{c[0]}Hq{c[1]}D{c[3]}w{c[6]}r{c[7]}a{int(c[8])}"
+                                                    for c in WINDOW_CASES])
+def test_decode_window_parity(m, case):
+    import torch
+    from workloads import randn_bf16
+    B, Hq, Hkv, D, S, lens, window, rolling, append = case
+    lens = np.array(lens, dtype=np.int32)
+    d = decode_inputs_host(B, Hq, Hkv, D, S, 71, np.minimum(lens, S))
+    rng = np.random.default_rng(72)
+    kn, vn = randn_bf16(rng, (B, Hkv, D)), randn_bf16(rng, (B, Hkv, D))
+    rope = rope_settings(ROPE_YARN, base=5e5, factor=4.0, original_max_position=64)
+    scale = 1.0 / math.sqrt(D)
+    print(f"[case] window B={B} Hq={Hq} Hkv={Hkv} D={D} S={S} lens={list(lens)} w={window} "
+          f"rolling={rolling} append={append}", flush=True)
+    kc, vc = to_dev(d["k"]), to_dev(d["v"])
+    out = m.gqa_decode_window(to_dev(d["q"]), kc, vc, torch.from_numpy(lens).cuda(), scale,
+                              window=window, rolling=bool(rolling),
+                              k_new=to_dev(kn) if append else None,
+                              v_new=to_dev(vn) if append else None, q_rope=rope)
+    torch.cuda.synchronize()
+    k0, v0 = bf16_bits_to_f64(d["k"]), bf16_bits_to_f64(d["v"])
+    kref, vref = k0, v0
+    if append:
+        kref, vref = oatt.append_rows_window(k0, v0, bf16_bits_to_f64(kn), bf16_bits_to_f64(vn),
+                                             lens, rope, rolling=bool(rolling))
+    ref = oatt.decode_window(bf16_bits_to_f64(d["q"]), kref, vref, lens, scale, rope,
+                             window=window, rolling=bool(rolling))
+    assert_close(from_dev(out), ref, f"window {case}")
+    kg, vg = from_dev(kc), from_dev(vc)
+    if append:
+        for b, L in enumerate(lens):
+            r = (int(L) - 1) % S if rolling else int(L) - 1
+            assert np.all(np.abs(kg[b, :, r] - kref[b, :, r]) <= _bf16_ulp(kref[b, :, r])), b
+            assert np.array_equal(vg[b, :, r], vref[b, :, r]), b
+            kg[b, :, r], vg[b, :, r] = k0[b, :, r], v0[b, :, r]
+    assert np.array_equal(kg, k0) and np.array_equal(vg, v0), "rows other than the new one changed"
+
+
+@pytest.mark.parametrize("mode", ["window4096", "rolling4096"])
+def test_decode_window_full_size_32k(m, mode, n_pairs=12):
+    """The 32K workload (ragged 16K-32K contexts, YaRN) with a 4096-token
+    sliding window over its linear cache, and as a 4096-slot rolling buffer
+    (contexts far longer than the buffer), sampled heads against the oracle."""
+    import torch
+    cfg = DECODE_32K_YARN
+    B, Hq, Hkv, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.D
+    lens = cfg.seq_lens()
+    S = cfg.S_max if mode == "window4096" else 4096
+    window, rolling = (4096, False) if mode == "window4096" else (0, True)
+    print(f"[case] window full size {mode}", flush=True)
+    q = device_randn_bf16((B, Hq, D), cfg.seed * 10 + 1)
+    k = device_randn_bf16((B, Hkv, S, D), cfg.seed * 10 + 2)
+    v = device_randn_bf16((B, Hkv, S, D), cfg.seed * 10 + 3)
+    sl = torch.from_numpy(lens).cuda()
+    out = m.gqa_decode_window(q, k, v, sl, cfg.scale, window=window, rolling=rolling,
+                              q_rope=cfg.rope())
+    torch.cuda.synchronize()
+    got = from_dev(out)
+    rng = np.random.default_rng(cfg.seed + 11)
+    pairs = [(int(rng.integers(B)), int(rng.integers(Hq))) for _ in range(n_pairs)]
+    qf = bf16_tensor_to_f64(q)
+    for b, h in pairs:
+        kv = h // (Hq // Hkv)
+        L = int(lens[b])
+        rows = oatt.window_rows(L, S, window, rolling)
+        kb = bf16_tensor_to_f64(k[b, kv][torch.from_numpy(rows).cuda()])
+        vb = bf16_tensor_to_f64(v[b, kv][torch.from_numpy(rows).cuda()])
+        qv = qf[b, h][None]
+        from oracle import rope as orope
+        qv = orope.rotate_rows(qv, np.array([L - 1]), cfg.rope())
+        ref = oatt.attend(qv[0], kb, vb, cfg.scale)
+        assert_close(got[b, h], ref, f"{mode} (b={b}, h={h}, L={L})")
