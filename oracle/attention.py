@@ -51,14 +51,16 @@ def kv_head_of(h: int, n_head: int, n_kv_head: int) -> int:
     return h // (n_head // n_kv_head)
 
 
-def causal_attention(q, k, v, scale: float, rows=None, heads=None) -> np.ndarray:
+def causal_attention(q, k, v, scale: float, rows=None, heads=None, window: int = 0) -> np.ndarray:
     """Causal GQA attention on already-rotated inputs.
 
     q: [B, Hq, T, D]; k: [B, Hkv, T, D]; v: [B, Hkv, T, Dv].  Row i attends to
-    keys 0..i.  ``rows``/``heads`` restrict the computation to a sample; the
-    result then holds NaN elsewhere.
+    keys 0..i, or with a sliding window w > 0 to keys i-w+1..i.
+    ``rows``/``heads`` restrict the computation to a sample; the result then
+    holds NaN elsewhere.
 
-    [注意力变体与MoE] "MQA 与 GQA", attention(): masked_fill(triu(1), -inf).
+    [注意力变体与MoE] "MQA 与 GQA", attention(): masked_fill(triu(1), -inf);
+    [transformer架构] §2.5.1: the band mask (0 for i-w+1 <= j <= i).
     """
     B, Hq, T, _ = q.shape
     Hkv = k.shape[1]
@@ -71,12 +73,15 @@ def causal_attention(q, k, v, scale: float, rows=None, heads=None) -> np.ndarray
         for h in heads:
             kv = kv_head_of(h, Hq, Hkv)
             for i in rows:
-                out[b, h, i] = attend(q[b, h, i], k[b, kv, :i + 1], v[b, kv, :i + 1], scale)
+                j0 = max(0, i - window + 1) if window else 0
+                out[b, h, i] = attend(q[b, h, i], k[b, kv, j0:i + 1], v[b, kv, j0:i + 1], scale)
     return out
 
 
-def prefill_causal(q, k, v, scale: float, rope_p: dict, rows=None, heads=None) -> np.ndarray:
-    """RoPE on Q and K at positions 0..T-1, then causal GQA attention.
+def prefill_causal(q, k, v, scale: float, rope_p: dict, rows=None, heads=None,
+                   window: int = 0) -> np.ndarray:
+    """RoPE on Q and K at positions 0..T-1, then causal GQA attention (with a
+    sliding window when window > 0).
 
     [transformer架构] §1.1 (rotate Q and K, not V) and §1.2 (scalings);
     attention as in :func:`causal_attention`.
@@ -88,7 +93,7 @@ def prefill_causal(q, k, v, scale: float, rope_p: dict, rows=None, heads=None) -
     # rotate along the position axis: move T first
     qr = _rope.rotate_rows(q.transpose(2, 0, 1, 3), pos, rope_p).transpose(1, 2, 0, 3)
     kr = _rope.rotate_rows(k.transpose(2, 0, 1, 3), pos, rope_p).transpose(1, 2, 0, 3)
-    return causal_attention(qr, kr, v, scale, rows=rows, heads=heads)
+    return causal_attention(qr, kr, v, scale, rows=rows, heads=heads, window=window)
 
 
 def decode_one(q_vec, K, V, seq_len: int, scale: float, rope_p) -> np.ndarray:

@@ -177,6 +177,33 @@ def test_sliding_window_decode_pins():
             assert np.allclose(ow[b, h], (a / a.sum()) @ v[b, h // 2, :L], rtol=1e-12, atol=1e-13)
 
 
+def test_sliding_window_prefill_pins():
+    """Every row of the windowed prefill equals the pages' band-masked
+    softmax(QK^T scale + M)V written out as a full matrix; window 1 gives
+    out_i = v_i; a window of T or more is plain causal prefill; the last row
+    equals the windowed decode of the last token over a cache of rope(K)."""
+    B, Hq, Hkv, T, D = 1, 4, 2, 19, 16
+    q, k, v = _rand((B, Hq, T, D), 81), _rand((B, Hkv, T, D), 82), _rand((B, Hkv, T, D), 83)
+    p = rope_settings(ROPE_YARN, base=1e4, factor=4.0, original_max_position=8)
+    w = 5
+    got = att.prefill_causal(q, k, v, 0.3, p, window=w)
+    qr = rope.rotate_rows(q.transpose(2, 0, 1, 3), np.arange(T), p).transpose(1, 2, 0, 3)
+    kr = rope.rotate_rows(k.transpose(2, 0, 1, 3), np.arange(T), p).transpose(1, 2, 0, 3)
+    i, j = np.arange(T)[:, None], np.arange(T)[None, :]
+    M = np.where((j >= i - w + 1) & (j <= i), 0.0, -np.inf)
+    for h in range(Hq):
+        S_ = 0.3 * qr[0, h] @ kr[0, h // 2].T + M
+        A = np.exp(S_ - S_.max(1, keepdims=True))
+        A /= A.sum(1, keepdims=True)
+        assert np.allclose(got[0, h], A @ v[0, h // 2], rtol=1e-12, atol=1e-13)
+    one = att.prefill_causal(q, k, v, 0.3, p, window=1)
+    assert np.allclose(one, np.repeat(v, Hq // Hkv, axis=1), rtol=0, atol=1e-15)
+    assert np.array_equal(att.prefill_causal(q, k, v, 0.3, p, window=T),
+                          att.prefill_causal(q, k, v, 0.3, p))
+    dec = att.decode_window(q[:, :, T - 1], kr, v, np.array([T]), 0.3, p, window=w)
+    assert np.allclose(dec, got[:, :, T - 1], rtol=1e-12, atol=1e-13)
+
+
 def test_rolling_buffer_equals_linear_cache_with_its_window():
     """Writing position t to slot t mod S of a rolling buffer and attending
     to every filled slot is the linear cache with window S, for contexts
