@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default="", help="comma list of sections (decode32k,decode4k,append32k,window,"
-                    "prefill,sparse,rope) for profiling runs")
+                    "prefill,prefill_window,sparse,rope) for profiling runs")
     return ap.parse_args()
 
 
@@ -240,6 +240,32 @@ def bench_prefill(cfg, steps, warmup):
     return dict(ev_ms=ev_ms, flops=flops, tflops=tf, gemm_tflops=gemm_tf)
 
 
+def bench_prefill_window(cfg, steps, warmup, window=4096):
+    """gqa_prefill_window on the 8K prefill with a `window`-token band."""
+    import torch
+
+    import mqa_kv_cache_amd as m
+    from workloads import device_randn_bf16
+    B, T, Hq, Hkv, D = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.D
+    q = device_randn_bf16((B, Hq, T, D), cfg.seed * 100 + 1)
+    k = device_randn_bf16((B, Hkv, T, D), cfg.seed * 100 + 2)
+    v = device_randn_bf16((B, Hkv, T, D), cfg.seed * 100 + 3)
+    out = torch.empty_like(q)
+    ws = torch.empty(m.gqa_prefill_workspace_size(B, Hkv, T, D, cfg.rope()), dtype=torch.uint8,
+                     device="cuda")
+    pairs = sum(min(i + 1, window) for i in range(T))      # visible (query, key) pairs per head
+    flops = 4 * D * Hq * pairs * B                          # QK^T and PV, 2 flops per product
+
+    def step(i):
+        m.gqa_prefill_causal(q, k, v, cfg.scale, rope=cfg.rope(), out=out, workspace=ws,
+                             window=window)
+
+    ev_ms = region_ms(step, max(steps // 2, 5), max(warmup // 2, 2))
+    tf = flops / ev_ms / 1e9
+    log(f"[bench] prefill T={T} window {window}: {ev_ms * 1e3:.1f} us per call, {tf:.1f} TFLOP/s")
+    return dict(ev_ms=ev_ms, flops=flops, tflops=tf, window=window)
+
+
 def bench_sparse(cfg, steps, warmup):
     import torch
 
@@ -356,6 +382,8 @@ def main():
         res["dr"] = bench_decode_window(DECODE_32K_YARN, K, W, 4096, True)
     if want("prefill"):
         res["p"] = bench_prefill(PREFILL_8K, K, W)
+    if want("prefill_window"):
+        res["pw"] = bench_prefill_window(PREFILL_8K, K, W)
     if want("sparse"):
         res["s"] = bench_sparse(SPARSE_128K, K, W)
     if want("rope"):
@@ -429,6 +457,11 @@ def main():
                               "ms_per_call": round(p["ev_ms"], 4), "flops": p["flops"],
                               "bound": "mfma", "peak": BF16_PEAK_TFLOPS,
                               "library_gemm_8192_TFLOP/s": round(p["gemm_tflops"], 1)}
+    if "pw" in res:
+        pw = res["pw"]
+        line[f"prefill_8k_window{pw['window']}"] = {
+            "TFLOP/s": round(pw["tflops"], 1), "pct_of_mfma_peak": round(100 * pw["tflops"] / BF16_PEAK_TFLOPS, 2),
+            "ms_per_call": round(pw["ev_ms"], 4), "flops": pw["flops"]}
     if "s" in res:
         s = res["s"]
         line["sparse_128k"] = {"GB/s": round(s["gbs"], 1), "ms_per_call": round(s["ms"], 5),

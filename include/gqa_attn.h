@@ -254,6 +254,20 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gqa_prefill_window -- gqa_prefill_causal with a sliding window
+ * ([transformer架构] §2.5.1, the band mask): row i attends to keys
+ * max(0, i-window+1) .. i, so
+ *     out_i = sum_{i-window < j <= i} softmax_j(scale * q~_i . k~_j) v_j
+ * window >= 0; 0 (or any window >= T) is gqa_prefill_causal.  Key tiles wholly
+ * below a query tile's window are not read.  Arguments, workspace, limits
+ * and errors as gqa_prefill_causal.
+ */
+gqa_status gqa_prefill_window(const void* q, const void* k, const void* v,
+                              int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                              int32_t window, float scale, const gqa_rope_params* rope,
+                              void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * topk_sparse_decode -- DSA-style sparse decode over an MLA latent cache,
  * o = Attn(q, KV[TopK(ReLU(K_I . q_I))]) ([稀疏注意力] "改进一：DSA", the
  * selection chain; [transformer架构] §2.2 (1)-(2)):

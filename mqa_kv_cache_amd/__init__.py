@@ -30,7 +30,7 @@ EXPORTED = [
     "rope_apply", "gqa_decode", "gqa_decode_parts", "gqa_decode_append", "gqa_decode_window",
     "gqa_decode_workspace_size",
     "gqa_decode_workspace_size_parts", "gqa_decode_partial", "gqa_decode_combine",
-    "gqa_prefill_causal", "gqa_prefill_workspace_size",
+    "gqa_prefill_causal", "gqa_prefill_window", "gqa_prefill_workspace_size",
     "topk_sparse_decode", "topk_sparse_decode_workspace_size", "kv_bytes_per_token",
     "mla_kv_bytes_per_token", "gqa_status_string",
 ]
@@ -99,6 +99,9 @@ _lib.gqa_prefill_causal.restype = _c_int32
 _lib.gqa_prefill_causal.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_int32, _c_int32, _c_int32,
                                     _c_int32, _c_int32, ctypes.c_float, _rope_p, _c_void_p,
                                     _c_void_p, _c_size_t, _c_void_p]
+_lib.gqa_prefill_window.restype = _c_int32
+_lib.gqa_prefill_window.argtypes = (_lib.gqa_prefill_causal.argtypes[:8] + [_c_int32]
+                                    + _lib.gqa_prefill_causal.argtypes[8:])
 _lib.topk_sparse_decode_workspace_size.restype = _c_size_t
 _lib.topk_sparse_decode_workspace_size.argtypes = [_c_int32] * 4
 _lib.topk_sparse_decode.restype = _c_int32
@@ -337,8 +340,9 @@ def gqa_prefill_workspace_size(B, Hkv, T, D, rope=None) -> int:
 
 
 def gqa_prefill_causal(q, k, v, scale: float, rope=None, out=None, workspace=None,
-                       stream=None) -> torch.Tensor:
-    """q [B,Hq,T,D], k/v [B,Hkv,T,D] bf16 (pre-RoPE).  Returns out [B,Hq,T,D]."""
+                       stream=None, window: int = 0) -> torch.Tensor:
+    """q [B,Hq,T,D], k/v [B,Hkv,T,D] bf16 (pre-RoPE).  Returns out [B,Hq,T,D].
+    window > 0: sliding window (row i sees keys i-window+1 .. i)."""
     B, Hq, T, D = q.shape
     Hkv = k.shape[1]
     _shape(k, (B, Hkv, T, D), "k")
@@ -353,6 +357,12 @@ def gqa_prefill_causal(q, k, v, scale: float, rope=None, out=None, workspace=Non
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace", dtype=torch.uint8)
+    if window:
+        st = _lib.gqa_prefill_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, Hq, Hkv, D,
+                                     int(window), float(scale), rope_params(rope), out.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel(), _stream(stream))
+        _check(st, "gqa_prefill_window")
+        return out
     st = _lib.gqa_prefill_causal(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, Hq, Hkv, D,
                                  float(scale), rope_params(rope), out.data_ptr(),
                                  workspace.data_ptr(), workspace.numel(), _stream(stream))

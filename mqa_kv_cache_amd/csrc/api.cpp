@@ -252,13 +252,13 @@ size_t gqa_prefill_workspace_size(int32_t B, int32_t Hkv, int32_t T, int32_t D,
     return 2 * prefill_prep_bytes(B, Hkv, T, D);
 }
 
-gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, int32_t B, int32_t T,
-                              int32_t Hq, int32_t Hkv, int32_t D, float scale,
+gqa_status gqa_prefill_window(const void* q, const void* k, const void* v, int32_t B, int32_t T,
+                              int32_t Hq, int32_t Hkv, int32_t D, int32_t window, float scale,
                               const gqa_rope_params* rope, void* out, void* workspace,
                               size_t workspace_bytes, void* stream) {
     gqa_status st = check_prefill_shape(B, T, Hq, Hkv, D);
     if (st != GQA_OK) return st;
-    if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+    if (!std::isfinite(scale) || window < 0) return GQA_ERR_INVALID_ARGUMENT;
     if (!q || !k || !v || !out) return GQA_ERR_INVALID_ARGUMENT;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return GQA_ERR_INVALID_ARGUMENT;
@@ -268,7 +268,15 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, int32
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GQA_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < 2 * prefill_prep_bytes(B, Hkv, T, D)) return GQA_ERR_WORKSPACE_TOO_SMALL;
     return from_hip(launch_gqa_prefill(q, k, v, B, T, Hq, Hkv, D, scale, rd, out, workspace,
-                                       (hipStream_t)stream));
+                                       (hipStream_t)stream, window >= T ? 0 : window));
+}
+
+gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, int32_t B, int32_t T,
+                              int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                              const gqa_rope_params* rope, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    return gqa_prefill_window(q, k, v, B, T, Hq, Hkv, D, 0, scale, rope, out, workspace,
+                              workspace_bytes, stream);
 }
 
 static gqa_status check_sparse_shape(int32_t B, int32_t H, int32_t Dqk, int32_t Dv, int32_t D_idx,

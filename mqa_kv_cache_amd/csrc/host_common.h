@@ -56,7 +56,8 @@ size_t prefill_prep_bytes(int32_t B, int32_t Hkv, int32_t T, int32_t D);
 
 hipError_t launch_gqa_prefill(const void* q, const void* k, const void* v, int32_t B, int32_t T,
                               int32_t Hq, int32_t Hkv, int32_t D, float scale,
-                              const RopeDev& rope, void* out, void* workspace, hipStream_t s);
+                              const RopeDev& rope, void* out, void* workspace, hipStream_t s,
+                              int32_t window = 0);
 
 struct SparseLayout {
     size_t scores_bytes;   // fp32 [B][S_max rounded up to 4]

@@ -169,8 +169,29 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int ks, int qi, int h)
                 if (32 * st + 8 * j + i > lim) s[st][4 * j + i] = -INFINITY;
 }
 
-// Folds the tile's row maxima into m_run (lazily, see kLazy).  Finite: every
-// processed tile holds a visible key for each query.
+// Sliding window (band mask): keys below the lane's query qi minus
+// (window - 1) are masked; only the first tiles of a wave hold any.
+__device__ __forceinline__ void mask_low(f32x16 (&s)[2], int ks, int qi, int h, int window) {
+    // key = ks + 32 st + 8 j + 4 h + i is masked when 32 st + 8 j + i < lim
+    int lim = qi - window + 1 - ks - 4 * h;
+    asm volatile("" : "+v"(lim));
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (32 * st + 8 * j + i < lim) s[st][4 * j + i] = -INFINITY;
+}
+
+// The reference maximum while a query has seen no visible key yet (only with
+// a window, on a wave's first tiles): exp2(-inf - 0) = 0 instead of NaN.
+__device__ __forceinline__ float ref_max(float m_run) { return m_run == -INFINITY ? 0.f : m_run; }
+
+// Folds the tile's row maxima into m_run (lazily, see kLazy).  Without a
+// window every tile a wave processes holds a visible key for each query; with
+// one, a query's first tiles may hold none (m_run then stays -inf, and the
+// rescale and ref_max keep that from producing NaN).
 template <int D>
 __device__ __forceinline__ void tile_max(const f32x16 (&s)[2], f32x16 (&o)[Geo<D>::MT],
                                          float& m_run, float& l_run) {
@@ -183,7 +204,7 @@ __device__ __forceinline__ void tile_max(const f32x16 (&s)[2], f32x16 (&o)[Geo<D
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy)) {
         asm volatile("" ::: "memory");   // keep the rescale behind the (rarely taken) branch
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);   // no key seen yet: nothing to scale
         l_run *= alpha;
 #pragma unroll
         for (int mt = 0; mt < Geo<D>::MT; ++mt) o[mt] *= alpha;
@@ -239,13 +260,14 @@ __device__ __forceinline__ void pipelined_step(const uint16_t* k_nx, const uint1
                                                const u32x4 (&qf)[Geo<D>::KSTEPS],
                                                const f32x16 (&s_c)[2], f32x16 (&s_n)[2],
                                                f32x16 (&o)[Geo<D>::MT], float& m_run, float& l_run,
-                                               bool diag_next, int ks_next, int qi, int n, int h) {
+                                               bool diag_next, bool low_next, int window,
+                                               int ks_next, int qi, int n, int h) {
     constexpr int KS = Geo<D>::KSTEPS, MT = Geo<D>::MT;
     constexpr int NQK = 2 * KS;          // S^T MFMAs of a tile
     constexpr int NPV = 4 * MT;          // P.V MFMAs of a tile
     constexpr int PAIRS = 16 / NQK;      // probability pairs per phase-A group
     constexpr int MAXV = 32 / NPV;       // scores per phase-B group
-    const float m = m_run;
+    const float m = ref_max(m_run);
 
     // ---- phase A: S^T(next) || P(current)
     u32x4 kf[NQK];
@@ -279,6 +301,7 @@ __device__ __forceinline__ void pipelined_step(const uint16_t* k_nx, const uint1
     }
     l_run += halves_sum(ls);
     if (diag_next) mask_tile(s_n, ks_next, qi, h);
+    if (low_next) mask_low(s_n, ks_next, qi, h, window);
 
     // ---- phase B: O += V.P(current) || max S^T(next)
     float mx = -INFINITY;
@@ -297,7 +320,7 @@ __device__ __forceinline__ void pipelined_step(const uint16_t* k_nx, const uint1
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy)) {
         asm volatile("" ::: "memory");   // keep the rescale behind the (rarely taken) branch
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);   // no key seen yet: nothing to scale
         l_run *= alpha;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
@@ -308,7 +331,8 @@ __device__ __forceinline__ void pipelined_step(const uint16_t* k_nx, const uint1
 template <int D>
 __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vt,
-    uint16_t* __restrict__ out, int T, int T_pad, int Hq, int Hkv, float qscale, RopeDev rope) {
+    uint16_t* __restrict__ out, int T, int T_pad, int Hq, int Hkv, float qscale, RopeDev rope,
+    int window) {
     using Gm = Geo<D>;
     // Two buffers per operand, as separate LDS objects: the compiler then
     // tells the tile being read from the one being copied into, and does not
@@ -359,10 +383,16 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
     const uint16_t* kbase = kh + kvbase;
     const uint16_t* vbase = vt + kvbase;                // V^T tiles: [T_pad/64][D][64]
     const int q_last_wg = min(qt * BM + BM - 1, T - 1);
-    const int n_kt = q_last_wg / BN + 1;
+    // With a sliding window (band mask, window > 0) the workgroup starts at the
+    // tile holding the first key its first query sees; tile t below is key
+    // tile kt0 + t, and the buffer descriptors start there.
+    const int kt0 = window > 0 ? max(0, qt * BM - window + 1) / BN : 0;
+    const int n_kt = q_last_wg / BN + 1 - kt0;
 
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, (uint32_t)T_pad * D * 2u);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, (uint32_t)T_pad * D * 2u);
+    const __amdgpu_buffer_rsrc_t kr =
+        make_rsrc(kbase + (size_t)kt0 * BN * D, (uint32_t)(T_pad - kt0 * BN) * D * 2u);
+    const __amdgpu_buffer_rsrc_t vr =
+        make_rsrc(vbase + (size_t)kt0 * BN * D, (uint32_t)(T_pad - kt0 * BN) * D * 2u);
     const RowCopy<BN, 2 * D, 2 * Gm::KSTR> kcopy(lane);
     const RowCopy<D, 2 * BN, 2 * Gm::VSTR> vcopy(lane);
     // the first tile's copy overlaps the Q load and rotation
@@ -418,13 +448,17 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
     // tiles 0 .. n_w-1 and only the last of them holds keys past its first
     // query (q0 is a multiple of 32, tiles are 64 wide); a wave done early
     // keeps copying its share and meeting the barriers of the others.
-    const int n_w = min((q0 + 31) / BN + 1, n_kt);
+    const int n_w = min((q0 + 31) / BN + 1 - kt0, n_kt);
+    // tile t holds keys below some query's window when its first key is
+    // below the last query's lower bound
+    auto low = [&](int t) { return window > 0 && (kt0 + t) * BN < q0 + 32 - window; };
     if (n_kt > 1) kcopy.run(kr, (uint32_t)BN * D * 2u, k_s1, wave);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 s_cur[2];
     qk_tile<D>(k_s0, qf, s_cur, n, h);
-    if (n_w == 1) mask_tile(s_cur, 0, qi, h);
+    if (n_w == 1) mask_tile(s_cur, kt0 * BN, qi, h);
+    if (low(0)) mask_low(s_cur, kt0 * BN, qi, h, window);
     tile_max<D>(s_cur, o, m_run, l_run);
 
     auto top = [&](int t, uint16_t* k_dst, uint16_t* v_dst) {
@@ -442,14 +476,14 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
                     const uint16_t* v_cur, uint16_t* k_dst, uint16_t* v_dst) {
         top(t, k_dst, v_dst);
         pipelined_step<D>(k_next, v_cur, qf, s_c, s_n, o, m_run, l_run, t + 1 == n_w - 1,
-                          (t + 1) * BN, qi, n, h);
+                          low(t + 1), window, (kt0 + t + 1) * BN, qi, n, h);
     };
     // this wave's last step
     auto last = [&](int t, const f32x16 (&s_c)[2], const uint16_t* v_cur, uint16_t* k_dst,
                     uint16_t* v_dst) {
         top(t, k_dst, v_dst);
         u32x4 pb[4];
-        l_run += halves_sum(probs(s_c, m_run, pb));
+        l_run += halves_sum(probs(s_c, ref_max(m_run), pb));
         pv_tile<D>(v_cur, pb, o, n, h);
     };
     f32x16 s_alt[2];
@@ -600,7 +634,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
 
 template <int D>
 void launch_d(const void* q, const void* k, const void* v, void* out, void* kh, void* vt, int B,
-              int T, int Hq, int Hkv, float qscale, const RopeDev& rope, hipStream_t s) {
+              int T, int Hq, int Hkv, float qscale, const RopeDev& rope, int window, hipStream_t s) {
     const int T_pad = (T + BN - 1) / BN * BN;
     hipLaunchKernelGGL((prefill_prep_kernel<D>), dim3(T_pad / BN, Hkv, B), dim3(256), 0, s,
                        (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)kh, (uint16_t*)vt, T,
@@ -608,7 +642,7 @@ void launch_d(const void* q, const void* k, const void* v, void* out, void* kh, 
     dim3 grid((T + BM - 1) / BM * Hq * B);   // one workgroup per (query tile, q head, batch)
     hipLaunchKernelGGL((prefill_kernel<D>), grid, dim3(256), 0, s, (const uint16_t*)q,
                        (const uint16_t*)kh, (const uint16_t*)vt, (uint16_t*)out, T, T_pad, Hq, Hkv,
-                       qscale, rope);
+                       qscale, rope, window);
 }
 
 }  // namespace
@@ -620,16 +654,16 @@ size_t prefill_prep_bytes(int32_t B, int32_t Hkv, int32_t T, int32_t D) {
 
 hipError_t launch_gqa_prefill(const void* q, const void* k, const void* v, int32_t B, int32_t T,
                               int32_t Hq, int32_t Hkv, int32_t D, float scale, const RopeDev& rope,
-                              void* out, void* workspace, hipStream_t s) {
+                              void* out, void* workspace, hipStream_t s, int32_t window) {
     const float qscale = scale * kLog2e;
     void* kh = workspace;
     void* vt = reinterpret_cast<char*>(workspace) + prefill_prep_bytes(B, Hkv, T, D);
     switch (D) {
-        case 8: launch_d<8>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, s); break;
-        case 16: launch_d<16>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, s); break;
-        case 32: launch_d<32>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, s); break;
-        case 64: launch_d<64>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, s); break;
-        default: launch_d<128>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, s); break;
+        case 8: launch_d<8>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, window, s); break;
+        case 16: launch_d<16>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, window, s); break;
+        case 32: launch_d<32>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, window, s); break;
+        case 64: launch_d<64>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, window, s); break;
+        default: launch_d<128>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, window, s); break;
     }
     return hipGetLastError();
 }

@@ -163,6 +163,16 @@ def test_prefill_validation(m):
     assert m.gqa_prefill_workspace_size(1, 2, 16, 128, None) == need
 
 
+def test_prefill_window_validation(m):
+    lib = m.lib()
+    assert lib.gqa_prefill_window(P, P, P, 1, 64, 8, 2, 128, -1, 0.1, None, P, P, 1 << 30,
+                                  None) == m.ERR_INVALID_ARGUMENT
+    assert lib.gqa_prefill_window(P, P, P, 1, 64, 8, 2, 96, 16, 0.1, None, P, P, 1 << 30,
+                                  None) == m.ERR_UNSUPPORTED
+    assert lib.gqa_prefill_window(P, P, P, 1, 64, 8, 2, 128, 16, 0.1, None, P, P, 1,
+                                  None) == m.ERR_WORKSPACE_TOO_SMALL
+
+
 def test_sparse_validation(m):
     lib = m.lib()
 

@@ -117,3 +117,66 @@ def test_prefill_full_size_8k_sampled_rows(m):
         ref = oatt.prefill_causal(qf[:, h:h + 1, :i + 1], kf[:, kv:kv + 1, :i + 1],
                                   vf[:, kv:kv + 1, :i + 1], cfg.scale, cfg.rope(), rows=[i])
         assert_close(got[:, h, i], ref[:, 0, i], f"full-size row (h={h}, i={i})")
+
+
+# ---------------------------------------------------------------------------
+# gqa_prefill_window: the band mask (row i sees keys i-w+1 .. i)
+# ---------------------------------------------------------------------------
+
+WINDOW_CASES = [
+    # (B, T, Hq, Hkv, D, window)
+    (1, 300, 8, 2, 128, 1),      # each row sees only itself
+    (2, 517, 8, 2, 128, 5),      # narrow band: most rows' windows inside one tile
+    (1, 400, 4, 4, 128, 64),     # one tile wide
+    (1, 400, 4, 1, 128, 65),
+    (1, 700, 8, 2, 128, 200),    # band spans several tiles, ragged tail
+    (2, 333, 6, 2, 64, 100),     # head dim 64
+    (1, 100, 4, 2, 32, 7),
+    (1, 150, 4, 2, 128, 150),    # window = T: plain causal
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=[f"B{c[0]}T{c[1]}Hq{c[2]}D{c[4]}w{c[5]}"
+                                                    for c in WINDOW_CASES])
+def test_prefill_window_parity(m, case):
+    import torch
+    B, T, Hq, Hkv, D, w = case
+    p = prefill_inputs_host(B, T, Hq, Hkv, D, seed=37)
+    rope = rope_settings(ROPE_NTK, base=1e6, factor=4.0)
+    scale = 1 / math.sqrt(D)
+    print(f"[case] prefill window B={B} T={T} Hq={Hq} Hkv={Hkv} D={D} w={w}", flush=True)
+    out = m.gqa_prefill_causal(to_dev(p["q"]), to_dev(p["k"]), to_dev(p["v"]), scale, rope=rope,
+                               window=w)
+    torch.cuda.synchronize()
+    ref = oatt.prefill_causal(bf16_bits_to_f64(p["q"]), bf16_bits_to_f64(p["k"]),
+                              bf16_bits_to_f64(p["v"]), scale, rope, window=w)
+    got = from_dev(out)
+    assert np.all(np.isfinite(got))
+    assert_close(got, ref, f"prefill window {case}")
+
+
+def test_prefill_window_full_size_8k_sampled_rows(m):
+    """The 8K prefill with a 4096-token window: sampled rows, including rows
+    whose window starts mid-tile and the first rows that lose early keys."""
+    import torch
+    cfg = PREFILL_8K
+    B, T, Hq, Hkv, D = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.D
+    w = 4096
+    print(f"[case] prefill window full size T={T} w={w}", flush=True)
+    q = device_randn_bf16((B, Hq, T, D), cfg.seed * 10 + 1)
+    k = device_randn_bf16((B, Hkv, T, D), cfg.seed * 10 + 2)
+    v = device_randn_bf16((B, Hkv, T, D), cfg.seed * 10 + 3)
+    out = m.gqa_prefill_causal(q, k, v, cfg.scale, rope=cfg.rope(), window=w)
+    torch.cuda.synchronize()
+    got = from_dev(out)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(5)
+    samples = [(0, 0), (3, 4095), (4, 4096), (31, T - 1), (7, 5000), (12, 4097 + 63)]
+    samples += [(int(rng.integers(Hq)), int(rng.integers(T))) for _ in range(8)]
+    kf, vf, qf = bf16_tensor_to_f64(k), bf16_tensor_to_f64(v), bf16_tensor_to_f64(q)
+    for h, i in samples:
+        kv = h // (Hq // Hkv)
+        ref = oatt.prefill_causal(qf[:, h:h + 1, :i + 1], kf[:, kv:kv + 1, :i + 1],
+                                  vf[:, kv:kv + 1, :i + 1], cfg.scale, cfg.rope(), rows=[i],
+                                  window=w)
+        assert_close(got[:, h, i], ref[:, 0, i], f"window full-size row (h={h}, i={i})")
