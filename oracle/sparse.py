@@ -88,3 +88,22 @@ def topk_sparse_decode(q, latent, q_index, k_index, seq_lens, top_k: int, scale:
         for h in heads:
             out[b, h] = sparse_attention_one(q[b, h], latent[b], idx[b], scale, Dv)
     return idx, out
+
+
+def mla_dense_decode(q, latent, seq_lens, scale: float, Dv: int, heads=None) -> np.ndarray:
+    """Dense absorbed-MLA decode: every head attends to all seq_lens[b] latent
+    rows (no selection), scores over the full row, values its first Dv dims.
+
+    [attention] DSA ② (the MQA form of absorbed MLA: every head reads the one
+    shared latent row) without the indexer and top-k steps; equivalently
+    :func:`sparse_attention_one` with every row selected.
+    """
+    B, H, _ = q.shape
+    heads = range(H) if heads is None else heads
+    out = np.full((B, H, Dv), np.nan)
+    for b in range(B):
+        L = int(seq_lens[b])
+        for h in heads:
+            out[b, h] = sparse_attention_one(q[b, h], latent[b], np.arange(L), scale, Dv)
+    return out
+

@@ -105,3 +105,37 @@ def test_relu_zeroes_negative_scores():
     q = np.ones(4)
     k = np.array([[1, 1, 1, 1], [-1, -1, -1, -1], [0.5, -0.5, 0, 0]], dtype=np.float64)
     assert list(sparse.indexer_scores(q, k, 3)) == [4.0, 0.0, 0.0]
+
+
+def test_dense_mla_decode_equals_unabsorbed_multihead_attention():
+    """The absorbed (MQA) form equals multi-head attention with per-head keys
+    W_UK[h] c_j plus the shared rope key, and values W_UV[h] c_j: scores
+    q_h . k_hj = (W_UK[h]^T q_h) . c_j + q_h^R . k_j^R (matrix associativity),
+    and sum_j p_j W_UV[h] c_j = W_UV[h] (sum_j p_j c_j)."""
+    rng = np.random.default_rng(21)
+    B, H, L, dc, dR, dh = 2, 3, 17, 8, 4, 6
+    c = rng.standard_normal((B, L, dc))
+    kR = rng.standard_normal((B, L, dR))
+    W_UK = rng.standard_normal((H, dh, dc))
+    W_UV = rng.standard_normal((H, dh, dc))
+    qn = rng.standard_normal((B, H, dh))
+    qR = rng.standard_normal((B, H, dR))
+    seq = np.array([17, 9])
+    scale = 0.37
+    # unabsorbed: per-head keys [W_UK c ; k^R] and values W_UV c (MHA, Hkv = H)
+    K = np.concatenate([np.einsum("hdc,blc->bhld", W_UK, c), np.broadcast_to(kR[:, None], (B, H, L, dR))], -1)
+    V = np.einsum("hdc,blc->bhld", W_UV, c)
+    qfull = np.concatenate([qn, qR], -1)
+    mha = att.decode(qfull, K, V, seq, scale, None)
+    # absorbed: q~ = [W_UK^T q ; q^R] against latent rows [c ; k^R], then W_UV
+    qa = np.concatenate([np.einsum("hdc,bhd->bhc", W_UK, qn), qR], -1)
+    lat = np.concatenate([c, kR], -1)
+    o_lat = sparse.mla_dense_decode(qa, lat, seq, scale, Dv=dc)
+    absorbed = np.einsum("hdc,bhc->bhd", W_UV, o_lat)
+    assert np.allclose(absorbed, mha, rtol=1e-11, atol=1e-12)
+    # and it is the sparse path with every row selected
+    for b in range(B):
+        for h in range(H):
+            one = sparse.sparse_attention_one(qa[b, h], lat[b], np.arange(seq[b]), scale, dc)
+            assert np.array_equal(one, o_lat[b, h])
+
