@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of sections (decode32k,decode4k,append32k,window,"
+    ap.add_argument("--only", default="", help="comma list of sections (decode32k,decode4k,append32k,window,mla,"
                     "prefill,prefill_window,sparse,rope) for profiling runs")
     return ap.parse_args()
 
@@ -297,6 +297,35 @@ def bench_sparse(cfg, steps, warmup):
     return dict(ms=ev_ms, alg_bytes=alg, gbs=alg / ev_ms / 1e6)
 
 
+def bench_mla(cfg, steps, warmup):
+    """Dense absorbed-MLA decode over the full latent cache (no selection)."""
+    import torch
+
+    import mqa_kv_cache_amd as m
+    from workloads import device_randn_bf16
+    B, H, S = cfg.B, cfg.H, cfg.S_max
+    # two sets (604 MB of latent rows each) rotate past the 256 MB Infinity Cache
+    nsets = 2
+    sets = [(device_randn_bf16((B, H, cfg.Dqk), cfg.seed * 100 + 10 * i + 5),
+             device_randn_bf16((B, S, cfg.Dqk), cfg.seed * 100 + 10 * i + 6)) for i in range(nsets)]
+    lens = torch.from_numpy(cfg.seq_lens()).cuda()
+    out = torch.empty((B, H, cfg.Dv), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(m.mla_decode_workspace_size(B, H, S), dtype=torch.uint8, device="cuda")
+    rows = int(cfg.seq_lens().sum())
+    alg = rows * cfg.Dqk * 2 + B * H * cfg.Dqk * 2 + B * H * cfg.Dv * 2
+    flops = 2 * rows * H * (cfg.Dqk + cfg.Dv)
+
+    def step(i):
+        q, lat = sets[i % nsets]
+        m.mla_decode(q, lat, lens, cfg.scale, out=out, workspace=ws)
+
+    ev_ms = region_ms(step, steps, warmup)
+    log(f"[bench] mla dense: {ev_ms * 1e3:.1f} us per call, {alg / ev_ms / 1e6:.0f} GB/s, "
+        f"{flops / ev_ms / 1e9:.0f} TFLOP/s")
+    return dict(ms=ev_ms, alg_bytes=alg, flops=flops, gbs=alg / ev_ms / 1e6,
+                tflops=flops / ev_ms / 1e9)
+
+
 def bench_rope(cfg, steps, warmup):
     import torch
 
@@ -386,6 +415,8 @@ def main():
         res["pw"] = bench_prefill_window(PREFILL_8K, K, W)
     if want("sparse"):
         res["s"] = bench_sparse(SPARSE_128K, K, W)
+    if want("mla"):
+        res["mla"] = bench_mla(SPARSE_128K, K, W)
     if want("rope"):
         res["r"] = bench_rope(PREFILL_8K, K, W)
     if only and "d32" not in res:
@@ -467,6 +498,13 @@ def main():
         line["sparse_128k"] = {"GB/s": round(s["gbs"], 1), "ms_per_call": round(s["ms"], 5),
                                "algorithmic_bytes": s["alg_bytes"],
                                "pct_of_hbm_peak": round(100 * s["gbs"] / HBM_PEAK_GBS, 2)}
+    if "mla" in res:
+        ml = res["mla"]
+        line["mla_dense_128k"] = {"GB/s": round(ml["gbs"], 1), "TFLOP/s": round(ml["tflops"], 1),
+                                  "pct_of_hbm_peak": round(100 * ml["gbs"] / HBM_PEAK_GBS, 2),
+                                  "pct_of_mfma_peak": round(100 * ml["tflops"] / BF16_PEAK_TFLOPS, 2),
+                                  "ms_per_call": round(ml["ms"], 5), "flops": ml["flops"],
+                                  "algorithmic_bytes": ml["alg_bytes"]}
     if "r" in res:
         line["rope_apply"] = {"GB/s": round(res["r"]["gbs"], 1), "ms_per_call": round(res["r"]["ms"], 5)}
     if not args.no_cpu:

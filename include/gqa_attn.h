@@ -302,6 +302,34 @@ gqa_status topk_sparse_decode(const void* q, const void* latent, const void* q_i
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode -- dense decode over an MLA latent cache in the absorbed form
+ * ([attention] DSA ② and "乘法结合律" 的变换; [注意力变体与MoE] "MLA"): with
+ * W_UK folded into the query and W_UV applied after the sum, every head
+ * attends to the same single latent row, i.e. MQA with Dqk-dim keys and the
+ * first Dv columns as values, over all rows j < seq_lens[b]:
+ *     s_j = scale * q[b][h] . latent[b][j][0:Dqk],
+ *     out[b][h] = sum_j softmax_j(s) latent[b][j][0:Dv]
+ * This is topk_sparse_decode with every row selected.
+ *
+ *   q           bf16 [B][H][Dqk]   (absorbed query; its RoPE part already rotated)
+ *   latent      bf16 [B][S_max][Dqk]; V is the first Dv columns of each row
+ *   seq_lens    device int32 [B], each in [1, S_max] (clamped into that range)
+ *   out         bf16 [B][H][Dv]   (output)
+ *   workspace   >= mla_decode_workspace_size(B, H, S_max) bytes, 256-byte aligned;
+ *               fp32 partial softmax states of the row ranges, owned by the caller
+ * Supported: Dqk = 576, Dv = 512, H a multiple of 16 up to 128,
+ * S_max * Dqk * 2 < 2^31.  Other Dqk/Dv or H: GQA_ERR_UNSUPPORTED; null or
+ * misaligned pointers, non-finite scale: GQA_ERR_INVALID_ARGUMENT; short
+ * workspace: GQA_ERR_WORKSPACE_TOO_SMALL.  Asynchronous on `stream`.
+ */
+size_t mla_decode_workspace_size(int32_t B, int32_t H, int32_t S_max);
+
+gqa_status mla_decode(const void* q, const void* latent, const int32_t* seq_lens,
+                      int32_t B, int32_t H, int32_t Dqk, int32_t Dv, int32_t S_max,
+                      float scale, void* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
  * KV-cache bytes per token, exact integers ([注意力变体与MoE] "生成时的瓶颈":
  * 2 (K and V) x layers x n_kv_head x d_head x bytes; and "MLA": layers x
  * (d_latent + d_rope) x bytes, no factor 2 because K and V share the latent).

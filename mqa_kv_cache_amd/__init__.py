@@ -31,7 +31,8 @@ EXPORTED = [
     "gqa_decode_workspace_size",
     "gqa_decode_workspace_size_parts", "gqa_decode_partial", "gqa_decode_combine",
     "gqa_prefill_causal", "gqa_prefill_window", "gqa_prefill_workspace_size",
-    "topk_sparse_decode", "topk_sparse_decode_workspace_size", "kv_bytes_per_token",
+    "topk_sparse_decode", "topk_sparse_decode_workspace_size", "mla_decode",
+    "mla_decode_workspace_size", "kv_bytes_per_token",
     "mla_kv_bytes_per_token", "gqa_status_string",
 ]
 
@@ -109,6 +110,11 @@ _lib.topk_sparse_decode.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, 
                                     _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                     _c_int32, ctypes.c_float, _c_void_p, _c_void_p, _c_void_p,
                                     _c_size_t, _c_void_p]
+_lib.mla_decode_workspace_size.restype = _c_size_t
+_lib.mla_decode_workspace_size.argtypes = [_c_int32] * 3
+_lib.mla_decode.restype = _c_int32
+_lib.mla_decode.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_int32, _c_int32, _c_int32, _c_int32,
+                            _c_int32, ctypes.c_float, _c_void_p, _c_void_p, _c_size_t, _c_void_p]
 
 
 def lib() -> ctypes.CDLL:
@@ -407,3 +413,33 @@ def topk_sparse_decode(q, latent, q_index, k_index, seq_lens, top_k: int, scale:
                                  _stream(stream))
     _check(st, "topk_sparse_decode")
     return topk_idx, out
+
+
+def mla_decode_workspace_size(B, H, S_max) -> int:
+    return int(_lib.mla_decode_workspace_size(B, H, S_max))
+
+
+def mla_decode(q, latent, seq_lens, scale: float, Dv: int = 512, out=None, workspace=None,
+               stream=None):
+    """q [B,H,Dqk], latent [B,S_max,Dqk] (bf16), seq_lens int32 [B].
+    Returns out bf16 [B,H,Dv]: every head attends to all latent rows < seq_lens[b]."""
+    B, H, Dqk = q.shape
+    S_max = latent.shape[1]
+    _shape(latent, (B, S_max, Dqk), "latent")
+    _shape(seq_lens, (B,), "seq_lens")
+    _dev(q, "q")
+    _dev(latent, "latent")
+    _dev(seq_lens, "seq_lens", dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=torch.bfloat16, device=q.device)
+    _shape(out, (B, H, Dv), "out")
+    _dev(out, "out")
+    need = mla_decode_workspace_size(B, H, S_max)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    st = _lib.mla_decode(q.data_ptr(), latent.data_ptr(), seq_lens.data_ptr(), B, H, Dqk, Dv, S_max,
+                         float(scale), out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                         _stream(stream))
+    _check(st, "mla_decode")
+    return out

@@ -315,4 +315,33 @@ gqa_status topk_sparse_decode(const void* q, const void* latent, const void* q_i
                                               (hipStream_t)stream));
 }
 
+static gqa_status check_mla_shape(int32_t B, int32_t H, int32_t Dqk, int32_t Dv, int32_t S_max) {
+    if (B < 1 || H < 1 || Dqk < 1 || Dv < 1 || S_max < 1 || Dv > Dqk) return GQA_ERR_INVALID_ARGUMENT;
+    if (Dqk != 576 || Dv != 512) return GQA_ERR_UNSUPPORTED;
+    if ((H % 16) || H > 128) return GQA_ERR_UNSUPPORTED;
+    if ((int64_t)S_max * Dqk * 2 >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
+    return GQA_OK;
+}
+
+size_t mla_decode_workspace_size(int32_t B, int32_t H, int32_t S_max) {
+    if (check_mla_shape(B, H, 576, 512, S_max) != GQA_OK) return 0;
+    return mla_layout(B, H, S_max).total;
+}
+
+gqa_status mla_decode(const void* q, const void* latent, const int32_t* seq_lens, int32_t B,
+                      int32_t H, int32_t Dqk, int32_t Dv, int32_t S_max, float scale, void* out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    gqa_status st = check_mla_shape(B, H, Dqk, Dv, S_max);
+    if (st != GQA_OK) return st;
+    if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+    if (!q || !latent || !seq_lens || !out || !workspace) return GQA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(latent) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return GQA_ERR_INVALID_ARGUMENT;
+    const MlaLayout lay = mla_layout(B, H, S_max);
+    if (workspace_bytes < lay.total) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    return from_hip(launch_mla_decode(q, latent, seq_lens, B, H, S_max, scale, out, workspace, lay,
+                                      (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -74,6 +74,18 @@ struct SparseLayout {
 };
 SparseLayout sparse_layout(int32_t B, int32_t H, int32_t S_max, int32_t top_k);
 
+struct MlaLayout {
+    int32_t rows_per_split;   // latent rows per workgroup (a multiple of 32)
+    int32_t n_split;          // row ranges per batch row
+    size_t o_bytes;           // fp32 partial outputs [B][H][n_split][512]
+    size_t ml_bytes;          // fp32 (m, l) [B][H][n_split][2]
+    size_t total;
+};
+MlaLayout mla_layout(int32_t B, int32_t H, int32_t S_max);
+hipError_t launch_mla_decode(const void* q, const void* latent, const int32_t* seq_lens, int32_t B,
+                             int32_t H, int32_t S_max, float scale, void* out, void* workspace,
+                             const MlaLayout& lay, hipStream_t s);
+
 hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const void* q_index,
                                      const void* k_index, const int32_t* seq_lens, int32_t B,
                                      int32_t H, int32_t S_max, int32_t top_k, float scale,

@@ -21,6 +21,7 @@
 //    S^T = C . Q^T over 576 dims, online softmax, O^T += C[:, :512]^T . P^T;
 //    a workgroup covers 32 heads and 128 selected rows staged through LDS and
 //    writes a partial (m, l, o) per head that combine_partials_kernel merges.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -711,6 +712,335 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
     }
 }
 
+// The sub-step of the dense kernel: sparse_sub_step with the key reads of the
+// score product issued in batches of six per row half ahead of their MFMAs
+// (one read in flight at a time otherwise: the register budget is tight).
+// ---------------------------------------------------------------------------
+// 4. dense absorbed-MLA decode (no selection: every row of the context).
+// The same MQA attention as sparse_attn_kernel over contiguous rows.  One
+// workgroup per (row range, 16*NW heads, batch row), one wave per SIMD (the
+// 16-head output tile and the 576-dim query need more than half the register
+// file).  The head groups of one row range are consecutive on one XCD, so the
+// second group reads the range from that XCD's L2.  The range is streamed
+// through a ring of four LDS sub-chunk buffers: once every wave is past
+// sub-chunk s-1, sub-chunk s+3 is requested into its buffer, so three
+// sub-chunks are always in flight.  Requests past the range read zeros
+// without traffic, so every step issues the same copies and the explicit
+// wait counts hold to the end.
+//
+// Softmax reference.  The running maximum of the online softmax is fixed at
+// the first sub-chunk's maximum m0 (per head); later rows take
+// p = 2^(s - m0) directly: floating point keeps its relative precision at
+// any scale, and s - m0 below kMlaHeadroom keeps p <= 2^32 (sums far inside
+// fp32 range for any latent value below 2^70 in magnitude).  The main loop then has no
+// branch, which keeps the 128-register output tile in place in the
+// accumulation registers (a rescale branch makes the compiler copy the tile
+// through ordinary registers every step and starves the score product of
+// registers for its LDS reads).  A workgroup in which some score rises
+// further above m0 recomputes its range with the rescaling online softmax.
+constexpr float kMlaHeadroom = 32.f;
+
+// QK^T of one 32-row sub-chunk for the wave's 16 heads: sc[th][i] is the
+// scaled base-2 score of row p0 + 16 th + 4 G + i (-inf past c1).  Key
+// reads are issued in batches of six per row half ahead of their MFMAs.
+__device__ __forceinline__ void dense_scores(const uint8_t* rows, const u32x4 (&qf)[kDqk / 32],
+                                             f32x4 (&sc)[2], int p0, int c1, float qscale, int G,
+                                             int n) {
+    constexpr int KU = kDqk / 32;
+    // batches of two k-slices for both row halves (four reads, four MFMAs),
+    // two batches in flight ahead of the MFMAs that use them
+    constexpr int NBT = KU / 2;
+    const uint8_t* kb = rows + n * kRowStride + 16 * G;
+    u32x4 kr[NBT][4];
+    auto load = [&](int g) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            kr[g][2 * j] = *reinterpret_cast<const u32x4*>(kb + 64 * (2 * g + j));
+            kr[g][2 * j + 1] = *reinterpret_cast<const u32x4*>(kb + 16 * kRowStride + 64 * (2 * g + j));
+        }
+    };
+    sc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_sched_barrier(0);
+    load(0);
+    load(1);
+#pragma unroll
+    for (int g = 0; g < NBT; ++g) {
+        if (g + 2 < NBT) load(g + 2);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            sc[0] = mfma16(kr[g][2 * j], qf[2 * g + j], sc[0]);
+            sc[1] = mfma16(kr[g][2 * j + 1], qf[2 * g + j], sc[1]);
+        }
+    }
+    // the order above, held against the scheduler's short LDS latency model
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int g = 0; g < NBT; ++g) {
+        if (g + 2 < NBT) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int th = 0; th < 2; ++th)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sc[th][i] *= qscale;
+            if (p0 + 16 * th + 4 * G + i >= c1) sc[th][i] = -INFINITY;
+        }
+}
+
+__device__ __forceinline__ float dense_rowmax(const f32x4 (&sc)[2]) {
+    const float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                           fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    return rows4_max(mx);   // the head's max over the 32 rows
+}
+
+// p = 2^(s - m), l += sum p, o += V^T p for the sub-chunk.  p enters the
+// MFMA as two bf16 terms, hi = bf16(p) and lo = bf16(p - hi), sharing each V
+// operand: p is then carried to 2^-17 relative instead of bf16's 2^-9, so no
+// row's weight, the largest included, is rounded to bf16 precision.
+//
+// V^T operands come from gfx950's transposing LDS read: within each 16-lane
+// group, lane 4a + c of a ds_read_b64_tr_b16 receives element c of the
+// 8-byte chunks addressed by lanes a, a+4, a+8 and a+12.  Lane r of group G
+// addresses row (4G + r/4) [second read: 16 + 4G + r/4] at dims
+// tb + dv(r mod 4)..+3, dv(a) = 4 (a mod 2) + 64 (a / 2), so lane n receives
+// dim tb + dv(n/4) + n mod 4 of the four rows: the tile's A operand, with
+// k = the rows slot_row(G, 0..7) that the P operand uses.  The output tile
+// o[dq][t] (tb = 128 dq + 8 t) then holds dims tb + dv(G) + i.  The split
+// dims keep a 32-lane read on 64 distinct banks: with the 292-dword row
+// stride the eight rows start on distinct 4-bank groups mod 32, and each
+// row's four chunks take its group and the group 32 banks on.
+__device__ __forceinline__ void dense_pv(const uint8_t* rows, const f32x4 (&sc)[2], float m,
+                                         f32x4 (&o)[4][8], float& l_run, int G, int n) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    float pr[2][4];
+    float ls = 0.f;
+#pragma unroll
+    for (int th = 0; th < 2; ++th)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pr[th][i] = fast_exp2(sc[th][i] - m);
+            ls += pr[th][i];
+        }
+    l_run += rows4_sum(ls);
+    u32x4 ph, pl;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float a = pr[k >> 1][2 * (k & 1)], c = pr[k >> 1][2 * (k & 1) + 1];
+        const uint32_t ha = f32_to_bf16_bits(a), hc = f32_to_bf16_bits(c);
+        ph[k] = ha | (hc << 16);
+        pl[k] = pack_bf16x2(a - __uint_as_float(ha << 16), c - __uint_as_float(hc << 16));
+    }
+    const uint8_t* v0 = rows + (4 * G + (n >> 2)) * kRowStride + 8 * (n & 1) + 128 * ((n >> 1) & 1);
+    const uint8_t* v1 = v0 + 16 * kRowStride;
+    // per 128-dim quarter: 16 reads, then the hi products of its eight tiles,
+    // then the lo products (no MFMA waits on the one just before it)
+#pragma unroll
+    for (int dq = 0; dq < 4; ++dq) {
+        u32x4 col[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int off = (128 * dq + 8 * t) * 2;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v0 + off));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v1 + off));
+            col[t] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[dq][t] = mfma16(col[t], ph, o[dq][t]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[dq][t] = mfma16(col[t], pl, o[dq][t]);
+    }
+}
+
+// The rescaling online softmax for one sub-chunk (the recompute path): the
+// running max follows the scores, o and l are rescaled when it moves.
+__device__ __forceinline__ void dense_pv_rescale(const uint8_t* rows, const f32x4 (&sc)[2],
+                                                 float& m_run, f32x4 (&o)[4][8], float& l_run,
+                                                 int G, int n) {
+    const float m_new = fmaxf(m_run, dense_rowmax(sc));
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
+        const float alpha = fast_exp2(m_run - m_new);   // 0 on the first sub-chunk
+        l_run *= alpha;
+#pragma unroll
+        for (int dq = 0; dq < 4; ++dq)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) o[dq][t] *= alpha;
+        m_run = m_new;
+    }
+    dense_pv(rows, sc, m_run, o, l_run, G, n);
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void mla_dense_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
+    const int32_t* __restrict__ seq_lens, int H, int S_max, int rows_per_split, float qscale,
+    float* __restrict__ part_o, float* __restrict__ part_ml, int n_split, int n_hg, int n_units) {
+    constexpr int KU = kDqk / 32;
+    __shared__ __attribute__((aligned(16))) uint8_t rows0[kSubBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t rows1[kSubBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t rows2[kSubBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t rows3[kSubBytes];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = lane >> 4, n = lane & 15;
+    // workgroups go round-robin over the 8 XCDs: id and id + 8 share an XCD,
+    // so the n_hg head groups of a unit (batch row, row range) are 8 apart
+    const int id = blockIdx.x;
+    const int hg = (id >> 3) % n_hg;
+    const int unit = (id & 7) + 8 * ((id >> 3) / n_hg);
+    if (unit >= n_units) return;                // whole workgroup
+    const int b = unit / n_split, split = unit - b * n_split;
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int c0 = split * rows_per_split;
+    if (c0 >= L) return;                        // whole workgroup
+    const int c1 = min(c0 + rows_per_split, L);
+    const int nsub = (c1 - c0 + kSubRows - 1) / kSubRows;
+    const int h = hg * (16 * NW) + 16 * wave + n;
+    const bool heads = hg * (16 * NW) + 16 * wave < H;   // wave-uniform (H % 16 == 0)
+
+    u32x4 qf[KU];
+    const uint16_t* qrow = q + ((size_t)b * H + (heads ? h : 0)) * kDqk;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u + 8 * G);
+
+    const __amdgpu_buffer_rsrc_t cr =
+        make_rsrc(latent + (size_t)b * S_max * kDqk, (uint32_t)S_max * kDqk * 2u);
+    // copy j = NW * i + wave of a sub-chunk fills LDS bytes [1024 j, +1024),
+    // lane l the 16 bytes at x = 1024 j + 16 l: row x / kRowStride, column
+    // x mod kRowStride (the padding after a row's kRowBytes is not read)
+    // rel: the copy's byte offset within the sub-chunk's rows, or ~0u for the
+    // padding bytes; it lies in the sub-chunk's first lim rows exactly when
+    // rel < lim * kRowBytes
+    constexpr int kCopiesPerWave = (kSubCopies + NW - 1) / NW;
+    uint32_t rel[kCopiesPerWave];
+#pragma unroll
+    for (int i = 0; i < kCopiesPerWave; ++i) {
+        const int x = 1024 * (NW * i + wave) + 16 * lane;
+        const int rr = x / kRowStride, cc = x - rr * kRowStride;
+        rel[i] = rr < kSubRows && cc < kRowBytes ? (uint32_t)(rr * kRowBytes + cc) : ~0u;
+    }
+    auto copy_sub = [&](int sub, uint8_t* dst) {
+        const int r0 = c0 + kSubRows * sub;
+        const int lim = max(min(c1 - r0, kSubRows), 0);   // rows of this sub-chunk
+        const uint32_t lim_bytes = (uint32_t)lim * kRowBytes;
+        const uint32_t base = (uint32_t)r0 * kRowBytes;
+        int wv = wave;
+        asm volatile("" : "+s"(wv));
+#pragma unroll
+        for (int i = 0; i < kCopiesPerWave; ++i) {
+            // only the last copy index can pass kSubCopies for some waves
+            if (i + 1 < kCopiesPerWave || NW * i + wv < kSubCopies) {
+                const uint32_t voff = rel[i] < lim_bytes ? base + rel[i] : 0x80000000u;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, dst + 1024 * (NW * i + wv), 16, voff, 0, 0, 0);
+            }
+        }
+    };
+    // q is complete before the copies are issued (the compiler's wait counts
+    // do not include loads into LDS)
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_sub(0, rows0);
+    copy_sub(1, rows1);
+    copy_sub(2, rows2);
+
+    f32x4 o[4][8];
+#pragma unroll
+    for (int dq = 0; dq < 4; ++dq)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[dq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float l_run = 0.f;
+
+    // step s: this wave's copies of s are done once at most those of s+1 and
+    // s+2 are outstanding (every wave issues at least kCopiesMin per
+    // sub-chunk); after the barrier every wave is past s-1, whose buffer
+    // takes s+3.  (lgkmcnt(0) too: this wave's LDS reads of s-1 are complete
+    // before the barrier that lets the copy of s+3 overwrite them.)
+    constexpr int kCopiesMin = kSubCopies / NW;
+    constexpr int kAhead = 2 * kCopiesMin;
+    static_assert(kAhead < 64, "vmcnt range");
+    auto enter = [&](int sub, uint8_t* next3) {
+        __builtin_amdgcn_s_waitcnt(0x0070 | (kAhead & 15) | ((kAhead >> 4) << 14));
+        asm volatile("s_barrier" ::: "memory");
+        copy_sub(sub + 3, next3);
+    };
+    f32x4 sc[2];
+    enter(0, rows3);
+    dense_scores(rows0, qf, sc, c0, c1, qscale, G, n);
+    const float m0 = dense_rowmax(sc);          // finite: row c0 < c1 is visible
+    if (heads) dense_pv(rows0, sc, m0, o, l_run, G, n);
+    bool high = false;                          // a score above m0 + kMlaHeadroom
+    auto step = [&](int sub, const uint8_t* cur, uint8_t* next3) {
+        enter(sub, next3);
+        if (heads) {
+            dense_scores(cur, qf, sc, c0 + kSubRows * sub, c1, qscale, G, n);
+            high |= dense_rowmax(sc) > m0 + kMlaHeadroom;
+            dense_pv(cur, sc, m0, o, l_run, G, n);
+        }
+    };
+    // unrolled by eight: the compiler's own wait for copies into LDS cannot
+    // tell the ring's buffers apart across the loop's back edge and waits for
+    // every earlier copy in the first two steps after it
+    for (int sub = 1; sub < nsub; sub += 8) {
+        step(sub, rows1, rows0);
+        if (sub + 1 >= nsub) break;
+        step(sub + 1, rows2, rows1);
+        if (sub + 2 >= nsub) break;
+        step(sub + 2, rows3, rows2);
+        if (sub + 3 >= nsub) break;
+        step(sub + 3, rows0, rows3);
+        if (sub + 4 >= nsub) break;
+        step(sub + 4, rows1, rows0);
+        if (sub + 5 >= nsub) break;
+        step(sub + 5, rows2, rows1);
+        if (sub + 6 >= nsub) break;
+        step(sub + 6, rows3, rows2);
+        if (sub + 7 >= nsub) break;
+        step(sub + 7, rows0, rows3);
+    }
+    __builtin_amdgcn_s_waitcnt(0);              // the copies past the range
+    float m_run = m0;
+    if (__syncthreads_or(high)) {
+        // recompute the range with the rescaling online softmax, one
+        // sub-chunk at a time through rows0
+#pragma unroll
+        for (int dq = 0; dq < 4; ++dq)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) o[dq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_run = 0.f;
+        for (int sub = 0; sub < nsub; ++sub) {
+            copy_sub(sub, rows0);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (heads) {
+                dense_scores(rows0, qf, sc, c0 + kSubRows * sub, c1, qscale, G, n);
+                dense_pv_rescale(rows0, sc, m_run, o, l_run, G, n);
+            }
+            __syncthreads();
+        }
+    }
+    if (!heads) return;
+
+    const size_t idx = ((size_t)b * H + h) * n_split + split;
+    float* po = part_o + idx * kDv + 4 * (G & 1) + 64 * (G >> 1);
+#pragma unroll
+    for (int dq = 0; dq < 4; ++dq)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(po + 128 * dq + 8 * t) = o[dq][t];
+    if (G == 0) {
+        part_ml[idx * 2] = m_run;
+        part_ml[idx * 2 + 1] = l_run;
+    }
+}
+
+constexpr int kMlaWaves = 4;   // 64 heads per workgroup, one wave per SIMD
+constexpr int kMlaTargetWgs = 256;
+constexpr int kMlaMinRows = 256;
+
 }  // namespace
 
 SparseLayout sparse_layout(int32_t B, int32_t H, int32_t S_max, int32_t top_k) {
@@ -730,6 +1060,40 @@ SparseLayout sparse_layout(int32_t B, int32_t H, int32_t S_max, int32_t top_k) {
     l.total = l.scores_bytes + l.hist_bytes + l.cand_bytes + l.info_bytes + l.counts_bytes +
               l.o_bytes + l.ml_bytes;
     return l;
+}
+
+MlaLayout mla_layout(int32_t B, int32_t H, int32_t S_max) {
+    MlaLayout l{};
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    // One workgroup per CU (256): every range writes H partial rows of 2 KiB
+    // that the merge reads back, so ranges are made as long as filling the
+    // machine allows (whole sub-chunks, at least kMlaMinRows rows).
+    const int n_hg = (H + 16 * kMlaWaves - 1) / (16 * kMlaWaves);
+    const int want = std::max(1, (kMlaTargetWgs + B * n_hg - 1) / (B * n_hg));
+    const int per = (S_max + want - 1) / want;
+    l.rows_per_split = std::max(kMlaMinRows, (per + kSubRows - 1) / kSubRows * kSubRows);
+    l.n_split = (S_max + l.rows_per_split - 1) / l.rows_per_split;
+    l.o_bytes = al((size_t)B * H * l.n_split * kDv * sizeof(float));
+    l.ml_bytes = al((size_t)B * H * l.n_split * 2 * sizeof(float));
+    l.total = l.o_bytes + l.ml_bytes;
+    return l;
+}
+
+hipError_t launch_mla_decode(const void* q, const void* latent, const int32_t* seq_lens, int32_t B,
+                             int32_t H, int32_t S_max, float scale, void* out, void* workspace,
+                             const MlaLayout& lay, hipStream_t s) {
+    float* po = reinterpret_cast<float*>(workspace);
+    float* pml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + lay.o_bytes);
+    const int n_hg = (H + 16 * kMlaWaves - 1) / (16 * kMlaWaves);
+    const int n_units = B * lay.n_split;
+    const int grid = 8 * n_hg * ((n_units + 7) / 8);
+    hipLaunchKernelGGL((mla_dense_kernel<kMlaWaves>), dim3(grid), dim3(64 * kMlaWaves), 0, s,
+                       (const uint16_t*)q, (const uint16_t*)latent, seq_lens, H, S_max,
+                       lay.rows_per_split, scale * kLog2e, po, pml, lay.n_split, n_hg, n_units);
+    const int BH = B * H;
+    hipLaunchKernelGGL((combine_partials_kernel<kDv>), dim3((BH + 3) / 4), dim3(256), 0, s, po, pml,
+                       seq_lens, H, S_max, S_max, lay.rows_per_split, lay.n_split, BH, (uint16_t*)out);
+    return hipGetLastError();
 }
 
 hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const void* q_index,

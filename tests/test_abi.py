@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("rope_apply", "gqa_decode", "gqa_prefill_causal", "topk_sparse_decode",
+    for want in ("rope_apply", "gqa_decode", "gqa_prefill_causal", "topk_sparse_decode", "mla_decode",
                  "kv_bytes_per_token", "mla_kv_bytes_per_token", "gqa_status_string"):
         assert want in names
 
@@ -189,6 +189,35 @@ def test_sparse_validation(m):
     need = m.topk_sparse_decode_workspace_size(2, 128, 4096, 2048)
     assert need > 0
     assert call(wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_mla_validation(m):
+    lib = m.lib()
+
+    def call(B=2, H=128, Dqk=576, Dv=512, S=4096, scale=0.07, wsn=0, q=P, out=P, ws=P):
+        return lib.mla_decode(q, P, P, B, H, Dqk, Dv, S, scale, out, ws, wsn, None)
+
+    need = m.mla_decode_workspace_size(2, 128, 4096)
+    assert need > 0
+    assert call(B=0, wsn=need) == m.ERR_INVALID_ARGUMENT
+    assert call(Dv=600, wsn=need) == m.ERR_INVALID_ARGUMENT
+    assert call(Dqk=512, wsn=need) == m.ERR_UNSUPPORTED
+    assert call(H=100, wsn=need) == m.ERR_UNSUPPORTED
+    assert call(H=256, wsn=need) == m.ERR_UNSUPPORTED
+    assert call(S=1 << 22, wsn=need) == m.ERR_UNSUPPORTED
+    assert call(q=MIS, wsn=need) == m.ERR_INVALID_ARGUMENT
+    assert call(out=None, wsn=need) == m.ERR_INVALID_ARGUMENT
+    assert call(scale=float("inf"), wsn=need) == m.ERR_INVALID_ARGUMENT
+    assert call(wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+    assert m.mla_decode_workspace_size(2, 100, 4096) == 0
+
+
+def test_mla_workspace_covers_the_partials(m):
+    # at least one fp32 partial row (Dv values + m, l) per head per 4096 rows
+    for B, H, S in ((1, 16, 1), (4, 128, 131072), (3, 64, 1000), (16, 128, 4096)):
+        need = m.mla_decode_workspace_size(B, H, S)
+        assert need >= B * H * 514 * 4
+        assert need % 256 == 0
 
 
 def test_rope_validation(m):
