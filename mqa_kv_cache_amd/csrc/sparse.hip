@@ -3,9 +3,10 @@
 // ([稀疏注意力] "改进一：DSA", the selection chain; [transformer架构] §2.2 (1)-(2);
 // [attention] DSA ①-③).
 //
-// 1. indexer_kernel: one HBM pass over the indexer keys.  Sixteen lanes share a
-//    128-dim row (16 bytes each); products of bf16 values are exact in fp64 and
-//    are summed in fp64, then rounded once to fp32 and passed through ReLU.
+// 1. indexer_kernel: one HBM pass over the indexer keys.  Four lanes share a
+//    128-dim row (64 contiguous bytes per lane per load); products of bf16
+//    values are exact in fp64 and are summed in fp64, then rounded once to
+//    fp32 and passed through ReLU.
 //    The pass also builds the first radix-select histogram (top 12 bits of
 //    the non-negative fp32 score) in LDS and flushes it with atomics.
 // 2. top-k selection by radix select over the fp32 score bits: the first
@@ -21,6 +22,9 @@
 //    S^T = C . Q^T over 576 dims, online softmax, O^T += C[:, :512]^T . P^T;
 //    a workgroup covers 32 heads and 128 selected rows staged through LDS and
 //    writes a partial (m, l, o) per head that combine_partials_kernel merges.
+// 4. mla_dense_kernel: the same attention over every row of the context
+//    (dense absorbed-MLA decode), 64 heads per workgroup, the rows streamed
+//    through a ring of LDS buffers.
 #include <algorithm>
 #include <type_traits>
 
