@@ -90,6 +90,7 @@ def prefill_causal(q, k, v, scale: float, rope_p: dict, rows=None, heads=None,
     k = np.asarray(k, dtype=np.float64)
     T = q.shape[2]
     pos = np.arange(T)
+    rope_p = _rope.with_length(rope_p, T)
     # rotate along the position axis: move T first
     qr = _rope.rotate_rows(q.transpose(2, 0, 1, 3), pos, rope_p).transpose(1, 2, 0, 3)
     kr = _rope.rotate_rows(k.transpose(2, 0, 1, 3), pos, rope_p).transpose(1, 2, 0, 3)
@@ -101,7 +102,7 @@ def decode_one(q_vec, K, V, seq_len: int, scale: float, rope_p) -> np.ndarray:
     attends to the first seq_len rows of its kv head's cache."""
     qv = np.asarray(q_vec, dtype=np.float64)[None, :]
     if rope_p is not None:
-        qv = _rope.rotate_rows(qv, np.array([seq_len - 1]), rope_p)
+        qv = _rope.rotate_rows(qv, np.array([seq_len - 1]), _rope.with_length(rope_p, seq_len))
     return attend(qv[0], K[:seq_len], V[:seq_len], scale)
 
 
@@ -147,7 +148,8 @@ def append_rows(k_cache, v_cache, k_new, v_new, seq_lens, rope_p):
         pos = int(seq_lens[b]) - 1
         kr = k_new[b]
         if rope_p is not None:
-            kr = _rope.rotate_rows(k_new[b][None], np.array([pos]), rope_p)[0]
+            kr = _rope.rotate_rows(k_new[b][None], np.array([pos]),
+                                   _rope.with_length(rope_p, pos + 1))[0]
         kc[b, :, pos] = kr
         vc[b, :, pos] = v_new[b]
     return kc, vc
@@ -196,7 +198,7 @@ def decode_window(q, k_cache, v_cache, seq_lens, scale: float, rope_p, window: i
         rows = window_rows(L, S_max, window, rolling)
         qv = np.asarray(q[b, h], dtype=np.float64)[None, :]
         if rope_p is not None:
-            qv = _rope.rotate_rows(qv, np.array([L - 1]), rope_p)
+            qv = _rope.rotate_rows(qv, np.array([L - 1]), _rope.with_length(rope_p, L))
         out[b, h] = attend(qv[0], np.asarray(k_cache[b, kv], np.float64)[rows],
                            np.asarray(v_cache[b, kv], np.float64)[rows], scale)
     return out
@@ -215,7 +217,7 @@ def append_rows_window(k_cache, v_cache, k_new, v_new, seq_lens, rope_p, rolling
         row = pos % S_max if rolling else pos
         kr = np.asarray(k_new[b], dtype=np.float64)
         if rope_p is not None:
-            kr = _rope.rotate_rows(kr[None], np.array([pos]), rope_p)[0]
+            kr = _rope.rotate_rows(kr[None], np.array([pos]), _rope.with_length(rope_p, pos + 1))[0]
         kc[b, :, row] = kr
         vc[b, :, row] = np.asarray(v_new[b], dtype=np.float64)
     return kc, vc

@@ -11,6 +11,12 @@ Readings where the pages leave a step open:
   continuous with 0 at r = alpha and 1 at r = beta.  (parity unpinned: the page
   only says "linear transition".)
 * The YaRN temperature multiplies both cos and sin by 0.1 ln s + 1.
+* Dynamic NTK's current length L_cur is the length of the sequence at the
+  call, the token being processed included: T for a prefill of T tokens,
+  seq_lens[b] for a decode step (whose new token sits at seq_lens[b]-1), and
+  an explicit ``current_len`` for a plain rotation of given positions.  Every
+  rotation a call performs uses that call's s (keys cached by earlier calls
+  keep the s they were rotated with).
 """
 from __future__ import annotations
 
@@ -18,7 +24,7 @@ import math
 
 import numpy as np
 
-NONE, PLAIN, PI, NTK, YARN = 0, 1, 2, 3, 4
+NONE, PLAIN, PI, NTK, YARN, DYNAMIC_NTK = 0, 1, 2, 3, 4, 5
 
 
 def base_frequencies(rotary_dim: int, base: float) -> np.ndarray:
@@ -33,6 +39,27 @@ def base_frequencies(rotary_dim: int, base: float) -> np.ndarray:
 def ntk_base(base: float, s: float, rotary_dim: int) -> float:
     """b' = b * s^(d/(d-2)).  [transformer架构] §1.2 ② NTK-aware scaling."""
     return float(base) * float(s) ** (rotary_dim / (rotary_dim - 2.0))
+
+
+def dynamic_ntk_factor(L_cur: int, L_train: int) -> float:
+    """s = max(1, L_cur / L_train), recomputed for every call.
+
+    [transformer架构] §1.2 ④ Dynamic NTK: the factor follows the current
+    sequence length and is then put into the NTK formula (§1.2 ②); a
+    sequence no longer than L_train keeps the original frequencies (s = 1).
+    """
+    return max(1.0, float(L_cur) / float(L_train))
+
+
+def with_length(p, L_cur: int):
+    """The setting a call with current sequence length L_cur uses: Dynamic
+    NTK settings get ``current_len = L_cur``; every other setting (and None)
+    is returned as it is."""
+    if p is None or int(p["scaling"]) != DYNAMIC_NTK:
+        return p
+    q = dict(p)
+    q["current_len"] = int(L_cur)
+    return q
 
 
 def yarn_ramp(r, alpha: float, beta: float) -> np.ndarray:
@@ -84,6 +111,13 @@ def frequencies_and_scales(p: dict, rotary_dim: int):
     if kind == NTK:
         # [transformer架构] §1.2 ②: theta'_i = (b')^(-2i/d).
         return base_frequencies(rotary_dim, ntk_base(base, s, rotary_dim)), 1.0, 1.0
+    if kind == DYNAMIC_NTK:
+        # [transformer架构] §1.2 ④: s from the call's length, then §1.2 ②.
+        L_cur = int(p["current_len"])
+        if L_cur < 1:
+            raise ValueError("Dynamic NTK needs the call's current length (current_len >= 1)")
+        s_dyn = dynamic_ntk_factor(L_cur, int(p["original_max_position"]))
+        return base_frequencies(rotary_dim, ntk_base(base, s_dyn, rotary_dim)), 1.0, 1.0
     if kind == YARN:
         theta = yarn_frequencies(rotary_dim, base, s, int(p["original_max_position"]),
                                  float(p["yarn_alpha"]), float(p["yarn_beta"]))

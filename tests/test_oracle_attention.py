@@ -8,7 +8,8 @@ import torch
 from conftest import golden_rows
 from oracle import attention as att
 from oracle import rope
-from workloads import TINY, ROPE_NONE, ROPE_PLAIN, ROPE_YARN, rope_settings, tiny_inputs
+from workloads import (ROPE_DYNAMIC_NTK, ROPE_NONE, ROPE_NTK, ROPE_PLAIN, ROPE_YARN, TINY, rope_settings,
+                       tiny_inputs)
 
 NO_ROPE = rope_settings(ROPE_NONE)
 
@@ -263,3 +264,39 @@ def test_prefill_rope_is_relative():
     qr = rope.rotate_rows(q.transpose(2, 0, 1, 3), np.arange(T) + sh, p).transpose(1, 2, 0, 3)
     kr = rope.rotate_rows(k.transpose(2, 0, 1, 3), np.arange(T) + sh, p).transpose(1, 2, 0, 3)
     assert np.allclose(att.causal_attention(qr, kr, v, 0.25), out, rtol=1e-10, atol=1e-12)
+
+
+def test_dynamic_ntk_uses_each_calls_length():
+    """Dynamic NTK ([transformer架构] §1.2 ④) in the attention steps: a decode
+    step rotates q (and an appended key) with s from its own sequence's
+    length, a prefill with s from T.  Sequences no longer than L_train match
+    plain RoPE, longer ones match NTK at s = L / L_train."""
+    B, Hq, Hkv, S_max, D, L_train = 3, 4, 2, 24, 16, 8
+    q, kc, vc = _rand((B, Hq, D), 61), _rand((B, Hkv, S_max, D), 62), _rand((B, Hkv, S_max, D), 63)
+    dyn = rope_settings(ROPE_DYNAMIC_NTK, base=1e4, original_max_position=L_train)
+    lens = np.array([5, 8, 20])
+    got = att.decode(q, kc, vc, lens, 0.3, dyn)
+    plain = att.decode(q, kc, vc, lens, 0.3, rope_settings(ROPE_PLAIN, base=1e4))
+    ntk = att.decode(q, kc, vc, lens, 0.3, rope_settings(ROPE_NTK, base=1e4, factor=2.5))
+    assert np.array_equal(got[:2], plain[:2]) and np.array_equal(got[2], ntk[2])
+    assert not np.allclose(got[2], plain[2])
+    # windowed decode and the appended key follow the same rule
+    gw = att.decode_window(q, kc, vc, lens, 0.3, dyn, window=4)
+    nw = att.decode_window(q, kc, vc, lens, 0.3, rope_settings(ROPE_NTK, base=1e4, factor=2.5),
+                           window=4)
+    assert np.array_equal(gw[2], nw[2])
+    kn, vn = _rand((B, Hkv, D), 64), _rand((B, Hkv, D), 65)
+    k1, _ = att.append_rows(kc, vc, kn, vn, lens, dyn)
+    k2, _ = att.append_rows(kc, vc, kn, vn, lens, rope_settings(ROPE_NTK, base=1e4, factor=2.5))
+    k3, _ = att.append_rows(kc, vc, kn, vn, lens, rope_settings(ROPE_PLAIN, base=1e4))
+    assert np.array_equal(k1[2], k2[2]) and np.array_equal(k1[:2], k3[:2])
+    # prefill: s from T
+    T = 20
+    qp, kp, vp = _rand((1, Hq, T, D), 66), _rand((1, Hkv, T, D), 67), _rand((1, Hkv, T, D), 68)
+    pd = att.prefill_causal(qp, kp, vp, 0.3, dyn)
+    pn = att.prefill_causal(qp, kp, vp, 0.3, rope_settings(ROPE_NTK, base=1e4, factor=2.5))
+    assert np.array_equal(pd, pn)
+    ps = att.prefill_causal(qp[:, :, :6], kp[:, :, :6], vp[:, :, :6], 0.3, dyn)
+    pp = att.prefill_causal(qp[:, :, :6], kp[:, :, :6], vp[:, :, :6], 0.3,
+                            rope_settings(ROPE_PLAIN, base=1e4))
+    assert np.array_equal(ps, pp)

@@ -6,8 +6,8 @@ import numpy as np
 import pytest
 
 from oracle import rope
-from workloads import (ROPE_NTK, ROPE_PI, ROPE_PLAIN, ROPE_YARN, DECODE_32K_YARN,
-                       PREFILL_8K, rope_settings)
+from workloads import (ROPE_DYNAMIC_NTK, ROPE_NTK, ROPE_PI, ROPE_PLAIN, ROPE_YARN,
+                       DECODE_32K_YARN, PREFILL_8K, rope_settings)
 
 SETTINGS = {
     "plain_1e4": rope_settings(ROPE_PLAIN, base=1e4),
@@ -163,3 +163,33 @@ def test_yarn_ramp_reading_values():
     th = rope.base_frequencies(128, 5e5)
     r19 = 8192 * th[19] / (2 * math.pi)
     assert abs(rope.yarn_ramp(r19, 1.0, 32.0) - (r19 - 1.0) / 31.0) < 1e-15
+
+
+def test_dynamic_ntk_factor_and_reductions():
+    """[transformer架构] §1.2 ④: s = max(1, L_cur / L_train), then the NTK
+    formula.  A sequence no longer than L_train keeps the original
+    frequencies (s = 1); at 3 L_train the frequencies are NTK's with s = 3; at
+    1.5 L_train the lowest frequency is exactly PI-compressed by 1.5 and the
+    highest is unchanged."""
+    assert rope.dynamic_ntk_factor(100, 4096) == 1.0
+    assert rope.dynamic_ntk_factor(4096, 4096) == 1.0
+    assert rope.dynamic_ntk_factor(8192, 4096) == 2.0
+    assert rope.dynamic_ntk_factor(6144, 4096) == 1.5
+    d, base, L_train = 128, 5e5, 4096
+    dyn = rope_settings(ROPE_DYNAMIC_NTK, base=base, original_max_position=L_train)
+    plain = rope.frequencies_and_scales(rope_settings(ROPE_PLAIN, base=base), d)
+    for L in (1, 2000, 4096):
+        got = rope.frequencies_and_scales(rope.with_length(dyn, L), d)
+        assert np.array_equal(got[0], plain[0]) and got[1:] == (1.0, 1.0)
+    ntk3 = rope.frequencies_and_scales(rope_settings(ROPE_NTK, base=base, factor=3.0), d)
+    got = rope.frequencies_and_scales(rope.with_length(dyn, 3 * L_train), d)
+    assert np.array_equal(got[0], ntk3[0])
+    th = rope.frequencies_and_scales(rope.with_length(dyn, 6144), d)[0]
+    assert th[0] == 1.0
+    assert abs(th[-1] / (base ** (-(d - 2) / d) / 1.5) - 1.0) < 1e-12
+    # the length is part of the call: without it the setting is refused
+    with pytest.raises(ValueError):
+        rope.frequencies_and_scales(dyn, d)
+    # other settings pass through with_length unchanged
+    p = rope_settings(ROPE_NTK, base=base, factor=2.0)
+    assert rope.with_length(p, 99) is p and rope.with_length(None, 5) is None

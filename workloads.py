@@ -55,16 +55,16 @@ def randn_bf16(rng: np.random.Generator, shape) -> np.ndarray:
 # RoPE settings as plain data (each side builds its own struct from this)
 # ---------------------------------------------------------------------------
 
-ROPE_NONE, ROPE_PLAIN, ROPE_PI, ROPE_NTK, ROPE_YARN = 0, 1, 2, 3, 4
+ROPE_NONE, ROPE_PLAIN, ROPE_PI, ROPE_NTK, ROPE_YARN, ROPE_DYNAMIC_NTK = 0, 1, 2, 3, 4, 5
 
 
 def rope_settings(scaling: int, base: float = 10000.0, factor: float = 1.0,
                   rotary_dim: int = 0, original_max_position: int = 0,
                   yarn_alpha: float = 1.0, yarn_beta: float = 32.0,
-                  yarn_mscale: int = 1) -> dict:
+                  yarn_mscale: int = 1, current_len: int = 0) -> dict:
     return dict(scaling=scaling, rotary_dim=rotary_dim, base=base, factor=factor,
                 original_max_position=original_max_position, yarn_alpha=yarn_alpha,
-                yarn_beta=yarn_beta, yarn_mscale=yarn_mscale)
+                yarn_beta=yarn_beta, yarn_mscale=yarn_mscale, current_len=current_len)
 
 
 # ---------------------------------------------------------------------------
