@@ -17,6 +17,7 @@ headline workload.  All data is synthetic and seeded.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -44,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of sections (decode32k,decode4k,append32k,window,mla,"
+    ap.add_argument("--only", default="", help="comma list of sections (decode32k,decode4k,dynamic,append32k,window,mla,"
                     "prefill,prefill_window,sparse,rope) for profiling runs")
     return ap.parse_args()
 
@@ -404,6 +405,9 @@ def main():
         res["d32"] = bench_decode(DECODE_32K_YARN, K, W, nsets=2, label="decode 32K")
     if want("decode4k"):
         res["d4"] = bench_decode(DECODE_4K, K, W, nsets=4, label="decode 4K")
+    if want("dynamic"):
+        res["dd"] = bench_decode(dataclasses.replace(DECODE_32K_YARN, rope_kind="dynamic_ntk"), K, W,
+                                 nsets=2, label="decode 32K dynamic NTK")
     if want("append32k"):
         res["da"] = bench_decode_append(DECODE_32K_YARN, K, W)
     if want("window"):
@@ -469,6 +473,11 @@ def main():
                              "kernel_GB/s": round(d4["kv_bytes"] / d4["kern_ms"] / 1e6, 1),
                              "pct_of_hbm_peak": round(100 * d4["kv_bytes"] / d4["ms"] / 1e6 / HBM_PEAK_GBS, 2),
                              "ms_per_step": round(d4["ms"], 5)}
+    if "dd" in res:
+        dd = res["dd"]
+        line["decode_dynamic_ntk_32k"] = {"GB/s": round(dd["kv_bytes"] / dd["ms"] / 1e6, 1),
+                                          "pct_of_hbm_peak": round(100 * dd["kv_bytes"] / dd["ms"] / 1e6 / HBM_PEAK_GBS, 2),
+                                          "ms_per_step": round(dd["ms"], 5)}
     if "da" in res:
         da = res["da"]
         line["decode_append_32k"] = {"GB/s": round(da["kv_bytes"] / da["ms"] / 1e6, 1),

@@ -59,9 +59,14 @@ typedef enum {
     GQA_ROPE_PLAIN = 1,  /* theta_i = base^(-2i/d), angle m*theta_i                     (§1.1) */
     GQA_ROPE_PI = 2,     /* position interpolation: angle (m/s)*theta_i                    (§1.2 ①) */
     GQA_ROPE_NTK = 3,    /* NTK-aware: base' = base * s^(d/(d-2))                          (§1.2 ②) */
-    GQA_ROPE_YARN = 4    /* NTK-by-parts ramp gamma(r_i), r_i = L_train*theta_i/(2 pi),
+    GQA_ROPE_YARN = 4,   /* NTK-by-parts ramp gamma(r_i), r_i = L_train*theta_i/(2 pi),
                             theta_i' = (1-gamma) theta_i/s + gamma theta_i, and cos/sin
                             multiplied by 0.1 ln s + 1 when yarn_mscale != 0            (§1.2 ③) */
+    GQA_ROPE_DYNAMIC_NTK = 5  /* NTK with s = max(1, L_cur / L_train) chosen per call from the
+                            current sequence length L_cur (the token being processed
+                            included): T in a prefill, seq_lens[b] in a decode step (q and
+                            the appended key), current_len in rope_apply.  factor must be 1;
+                            L_train = original_max_position.                       (§1.2 ④) */
 } gqa_rope_scaling;
 
 /* All fields explicit; the library applies no hidden defaults. */
@@ -71,11 +76,13 @@ typedef struct {
                                       Pairs are adjacent dims (2i, 2i+1) of the first rotary_dim dims;
                                       later dims pass through unchanged. */
     double  base;                  /* > 1, e.g. 1e4, 5e5, 1e6 */
-    double  factor;                /* s >= 1 for PI / NTK / YaRN; must be 1 for PLAIN */
-    int32_t original_max_position; /* L_train (YaRN only), > 0 */
+    double  factor;                /* s >= 1 for PI / NTK / YaRN; must be 1 for PLAIN and DYNAMIC_NTK */
+    int32_t original_max_position; /* L_train (YaRN and DYNAMIC_NTK), > 0 */
     int32_t yarn_mscale;           /* YaRN only: nonzero folds the temperature into cos/sin */
     double  yarn_alpha;            /* YaRN ramp lower edge (page default 1) */
     double  yarn_beta;             /* YaRN ramp upper edge (page default 32), > alpha */
+    int32_t current_len;           /* DYNAMIC_NTK in rope_apply only: L_cur >= 1 (the other
+                                      entry points take L_cur from their own lengths) */
 } gqa_rope_params;
 
 /*

@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_DEVICE = 0, 1, 2, 3, 4
-ROPE_NONE, ROPE_PLAIN, ROPE_PI, ROPE_NTK, ROPE_YARN = 0, 1, 2, 3, 4
+ROPE_NONE, ROPE_PLAIN, ROPE_PI, ROPE_NTK, ROPE_YARN, ROPE_DYNAMIC_NTK = 0, 1, 2, 3, 4, 5
 
 EXPORTED = [
     "rope_apply", "gqa_decode", "gqa_decode_parts", "gqa_decode_append", "gqa_decode_window",
@@ -47,6 +47,7 @@ class RopeParams(ctypes.Structure):
         ("yarn_mscale", ctypes.c_int32),
         ("yarn_alpha", ctypes.c_double),
         ("yarn_beta", ctypes.c_double),
+        ("current_len", ctypes.c_int32),
     ]
 
 
@@ -123,7 +124,7 @@ def lib() -> ctypes.CDLL:
 
 def rope_params(settings) -> "ctypes.pointer | None":
     """dict(scaling, rotary_dim, base, factor, original_max_position, yarn_alpha,
-    yarn_beta, yarn_mscale) -> pointer to the C struct (None stays None)."""
+    yarn_beta, yarn_mscale, current_len) -> pointer to the C struct (None stays None)."""
     if settings is None:
         return None
     if isinstance(settings, RopeParams):
@@ -132,7 +133,7 @@ def rope_params(settings) -> "ctypes.pointer | None":
                    float(settings.get("base", 10000.0)), float(settings.get("factor", 1.0)),
                    int(settings.get("original_max_position", 0)),
                    int(settings.get("yarn_mscale", 1)), float(settings.get("yarn_alpha", 1.0)),
-                   float(settings.get("yarn_beta", 32.0)))
+                   float(settings.get("yarn_beta", 32.0)), int(settings.get("current_len", 0)))
     return ctypes.pointer(p)
 
 

@@ -1,6 +1,7 @@
 // C ABI of libgqa_attn: argument validation on the host, then launches on
 // the caller's stream.  Nothing here touches the device before validation
 // has passed, so every error path is testable without a GPU.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -10,26 +11,36 @@ namespace gqa {
 
 static bool finite(double x) { return std::isfinite(x); }
 
-gqa_status rope_prepare(const gqa_rope_params* p, int32_t head_dim, RopeDev* out) {
+gqa_status rope_prepare(const gqa_rope_params* p, int32_t head_dim, RopeDev* out, int64_t cur_len) {
     std::memset(out, 0, sizeof(*out));
     out->pos_scale = 1.0;
     out->amp = 1.0f;
     if (p == nullptr || p->scaling == GQA_ROPE_NONE) return GQA_OK;
-    if (p->scaling < GQA_ROPE_PLAIN || p->scaling > GQA_ROPE_YARN) return GQA_ERR_INVALID_ARGUMENT;
+    if (p->scaling < GQA_ROPE_PLAIN || p->scaling > GQA_ROPE_DYNAMIC_NTK) return GQA_ERR_INVALID_ARGUMENT;
     const int32_t rd = p->rotary_dim == 0 ? head_dim : p->rotary_dim;
     if (rd < 2 || (rd & 1) || rd > head_dim) return GQA_ERR_INVALID_ARGUMENT;
     if ((rd % 8) != 0 || rd / 2 > kMaxRotaryHalf) return GQA_ERR_UNSUPPORTED;
     if (!finite(p->base) || !(p->base > 1.0)) return GQA_ERR_INVALID_ARGUMENT;
     if (!finite(p->factor)) return GQA_ERR_INVALID_ARGUMENT;
-    if (p->scaling == GQA_ROPE_PLAIN) {
+    if (p->scaling == GQA_ROPE_PLAIN || p->scaling == GQA_ROPE_DYNAMIC_NTK) {
         if (p->factor != 1.0) return GQA_ERR_INVALID_ARGUMENT;
     } else if (!(p->factor >= 1.0)) {
         return GQA_ERR_INVALID_ARGUMENT;
     }
     const int half = rd / 2;
-    const double s = p->factor;
+    double s = p->factor;
+    if (p->scaling == GQA_ROPE_DYNAMIC_NTK) {
+        // s = max(1, L_cur / L_train) ([transformer架构] §1.2 ④), then NTK
+        if (p->original_max_position <= 0 || rd <= 2 || cur_len < 0) return GQA_ERR_INVALID_ARGUMENT;
+        if (cur_len == 0) {
+            out->dyn_train = p->original_max_position;
+            out->dyn_exp = -2.0 / (double)(rd - 2);
+        } else {
+            s = std::max(1.0, (double)cur_len / (double)p->original_max_position);
+        }
+    }
     double base = p->base;
-    if (p->scaling == GQA_ROPE_NTK) {
+    if (p->scaling == GQA_ROPE_NTK || (p->scaling == GQA_ROPE_DYNAMIC_NTK && cur_len > 0)) {
         if (rd <= 2) return GQA_ERR_INVALID_ARGUMENT;
         base = p->base * std::pow(s, (double)rd / (double)(rd - 2));  // b' = b s^(d/(d-2))
     }
@@ -99,7 +110,9 @@ gqa_status rope_apply(const void* in, void* out, const int32_t* positions, int64
     if ((head_dim % 8) != 0 || head_dim > 1024) return GQA_ERR_UNSUPPORTED;
     if ((stride_tok % 8) != 0 || (stride_head % 8) != 0) return GQA_ERR_INVALID_ARGUMENT;
     RopeDev rd;
-    gqa_status st = rope_prepare(rope, head_dim, &rd);
+    if (rope && rope->scaling == GQA_ROPE_DYNAMIC_NTK && rope->current_len < 1)
+        return GQA_ERR_INVALID_ARGUMENT;
+    gqa_status st = rope_prepare(rope, head_dim, &rd, rope ? rope->current_len : 0);
     if (st != GQA_OK) return st;
     if (n_tok == 0) return GQA_OK;
     if (!in || !out || !aligned16(in) || !aligned16(out)) return GQA_ERR_INVALID_ARGUMENT;
@@ -149,7 +162,7 @@ gqa_status gqa_decode_partial(const void* q, const void* k_cache, const void* v_
         (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return GQA_ERR_INVALID_ARGUMENT;
     RopeDev rd;
-    st = rope_prepare(q_rope, D, &rd);
+    st = rope_prepare(q_rope, D, &rd, 0);
     if (st != GQA_OK) return st;
     const DecodeLayout lay = decode_layout(B, Hq, Hkv, D, n_parts);
     if (workspace_bytes < lay.total) return GQA_ERR_WORKSPACE_TOO_SMALL;
@@ -213,7 +226,7 @@ gqa_status gqa_decode_window(const void* q, const void* k_new, const void* v_new
         (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return GQA_ERR_INVALID_ARGUMENT;
     RopeDev rd;
-    st = rope_prepare(q_rope, D, &rd);
+    st = rope_prepare(q_rope, D, &rd, 0);
     if (st != GQA_OK) return st;
     const DecodeLayout lay = decode_layout(B, Hq, Hkv, D, kDecodeDefaultParts);
     if (workspace_bytes < lay.total) return GQA_ERR_WORKSPACE_TOO_SMALL;
@@ -248,7 +261,7 @@ size_t gqa_prefill_workspace_size(int32_t B, int32_t Hkv, int32_t T, int32_t D,
                                   const gqa_rope_params* rope) {
     if (B < 1 || Hkv < 1 || T < 1 || D < 1) return 0;
     RopeDev rd;
-    if (rope_prepare(rope, D, &rd) != GQA_OK) return 0;
+    if (rope_prepare(rope, D, &rd, T) != GQA_OK) return 0;
     return 2 * prefill_prep_bytes(B, Hkv, T, D);
 }
 
@@ -263,7 +276,7 @@ gqa_status gqa_prefill_window(const void* q, const void* k, const void* v, int32
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return GQA_ERR_INVALID_ARGUMENT;
     RopeDev rd;
-    st = rope_prepare(rope, D, &rd);
+    st = rope_prepare(rope, D, &rd, T);
     if (st != GQA_OK) return st;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GQA_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < 2 * prefill_prep_bytes(B, Hkv, T, D)) return GQA_ERR_WORKSPACE_TOO_SMALL;

@@ -249,6 +249,17 @@ __device__ __forceinline__ void cos_sin_theta(double theta, double pos, const Ro
     s = sv * r.amp;
 }
 
+// Dynamic NTK ([transformer架构] §1.2 ④) for a sequence of current length L:
+// theta_i * s^(-2i/(d-2)), s = max(1, L / L_train), i.e. the frequency of the
+// NTK base b s^(d/(d-2)); log2 s is 0 (no change) when the setting is not
+// dynamic or L <= L_train.
+__device__ __forceinline__ double dyn_log2s(const RopeDev& r, int L) {
+    return (r.dyn_train > 0 && L > r.dyn_train) ? log2((double)L / (double)r.dyn_train) : 0.0;
+}
+__device__ __forceinline__ double dyn_theta(double th, int i, double l2s, const RopeDev& r) {
+    return l2s > 0.0 ? th * exp2(r.dyn_exp * (double)i * l2s) : th;
+}
+
 // Raw q rows of the group's heads (issued before the first tile loads, so
 // waiting for them does not wait for the tiles).
 template <int D, int NB>
@@ -273,10 +284,13 @@ __device__ __forceinline__ void prep_q(const u32x4 (&raw)[NB][D / 32], const QFr
     constexpr int KU = D / 32;
     float cs[KU][4], sn[KU][4];
     if (rope.half) {
+        const double l2s = dyn_log2s(rope, L);
 #pragma unroll
         for (int u = 0; u < KU; ++u)
 #pragma unroll
-            for (int p = 0; p < 4; ++p) cos_sin_theta(fq.th[u][p], (double)(L - 1), rope, cs[u][p], sn[u][p]);
+            for (int p = 0; p < 4; ++p)
+                cos_sin_theta(dyn_theta(fq.th[u][p], 16 * u + 4 * G + p, l2s, rope), (double)(L - 1),
+                              rope, cs[u][p], sn[u][p]);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -342,6 +356,7 @@ __device__ __forceinline__ void load_new_row(NewRow<D>& nr, const AppendArgs& ap
 template <int D>
 __device__ __forceinline__ void rotate_new_key(NewRow<D>& nr, int L, const QFreq<D>& fq,
                                                const RopeDev& rope, int G) {
+    const double l2s = dyn_log2s(rope, L);
 #pragma unroll
     for (int u = 0; u < D / 32; ++u) {
         u32x4 w;
@@ -350,7 +365,8 @@ __device__ __forceinline__ void rotate_new_key(NewRow<D>& nr, int L, const QFreq
             float xe = bf16_lo(nr.k[u][p]), xo = bf16_hi(nr.k[u][p]);
             if (16 * u + 4 * G + p < rope.half) {
                 float c, sn;
-                cos_sin_theta(fq.th[u][p], (double)(L - 1), rope, c, sn);
+                cos_sin_theta(dyn_theta(fq.th[u][p], 16 * u + 4 * G + p, l2s, rope), (double)(L - 1),
+                              rope, c, sn);
                 const float ye = xe * c - xo * sn, yo = xe * sn + xo * c;
                 xe = ye;
                 xo = yo;

@@ -18,10 +18,16 @@ struct RopeDev {
     double pos_scale;              // multiplies the position (PI: 1/s)
     float amp;                     // multiplies cos and sin (YaRN temperature)
     int32_t half;                  // rotary_dim / 2; 0 = no rotation
+    int32_t dyn_train;             // > 0: Dynamic NTK per sequence with this L_train; theta
+                                   // holds the unscaled base^(-2i/d) and the kernel multiplies
+                                   // theta_i by s^(dyn_exp * i), s = max(1, L / L_train)
+    double dyn_exp;                // -2 / (d - 2)
 };
 
-// Validates `p` against head_dim and fills `out`.  p == NULL or NONE gives half = 0.
-gqa_status rope_prepare(const gqa_rope_params* p, int32_t head_dim, RopeDev* out);
+// Validates `p` against head_dim and fills `out`.  p == NULL or NONE gives
+// half = 0.  cur_len is the call's sequence length for Dynamic NTK: > 0 folds
+// s into the table; 0 leaves s to the kernel, per sequence (decode).
+gqa_status rope_prepare(const gqa_rope_params* p, int32_t head_dim, RopeDev* out, int64_t cur_len);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

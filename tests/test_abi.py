@@ -231,3 +231,23 @@ def test_rope_validation(m):
     assert lib.rope_apply(P, P, P, 0, 2, 128, 256, 128, r, None) == m.OK   # empty: no-op
     bad = _rope(m, scaling=m.ROPE_PLAIN, base=0.5)
     assert lib.rope_apply(P, P, P, 4, 2, 128, 256, 128, bad, None) == m.ERR_INVALID_ARGUMENT
+
+
+def test_dynamic_ntk_validation(m):
+    """Dynamic NTK needs L_train > 0 and factor 1; rope_apply needs the call's
+    current length, the other entry points take it from their own sizes."""
+    lib = m.lib()
+    dyn = dict(scaling=m.ROPE_DYNAMIC_NTK, base=1e4, original_max_position=4096)
+    ok = _rope(m, current_len=8192, **dyn)
+    assert lib.rope_apply(P, P, P, 0, 2, 128, 256, 128, ok, None) == m.OK
+    assert lib.rope_apply(P, P, P, 4, 2, 128, 256, 128, _rope(m, **dyn), None) == m.ERR_INVALID_ARGUMENT
+    assert lib.rope_apply(P, P, P, 4, 2, 128, 256, 128,
+                          _rope(m, current_len=-3, **dyn), None) == m.ERR_INVALID_ARGUMENT
+    no_train = dict(dyn, original_max_position=0)
+    assert lib.rope_apply(P, P, P, 4, 2, 128, 256, 128,
+                          _rope(m, current_len=10, **no_train), None) == m.ERR_INVALID_ARGUMENT
+    assert _decode(m, rope=_rope(m, **no_train)) == m.ERR_INVALID_ARGUMENT
+    assert _decode(m, rope=_rope(m, factor=2.0, **dyn)) == m.ERR_INVALID_ARGUMENT
+    # decode and prefill accept it without current_len
+    assert m.gqa_prefill_workspace_size(1, 8, 64, 128, dyn) > 0
+    assert m.gqa_prefill_workspace_size(1, 8, 64, 128, no_train) == 0

@@ -102,7 +102,7 @@ class DecodeConfig:
     D: int
     S_max: int
     seed: int
-    rope_kind: str            # "plain" or "yarn"
+    rope_kind: str            # "plain", "yarn" or "dynamic_ntk" (L_train = yarn_L_train)
     base: float
     ragged_lo: Optional[int] = None   # seq_lens ~ U{lo..S_max} when set
     yarn_factor: float = 4.0
@@ -121,6 +121,9 @@ class DecodeConfig:
             return rope_settings(ROPE_YARN, base=self.base, factor=self.yarn_factor,
                                  original_max_position=self.yarn_L_train,
                                  yarn_alpha=1.0, yarn_beta=32.0, yarn_mscale=1)
+        if self.rope_kind == "dynamic_ntk":
+            return rope_settings(ROPE_DYNAMIC_NTK, base=self.base,
+                                 original_max_position=self.yarn_L_train)
         return rope_settings(ROPE_PLAIN, base=self.base)
 
     def seq_lens(self) -> np.ndarray:
