@@ -21,6 +21,11 @@ Readings where the pages leave a step open:
 * The query is given already absorbed into the latent space (weight
   absorption, [attention] "乘法结合律" 的变换) with its RoPE part already
   rotated; V is the first Dv dims of each latent row.
+* The multi-head weighted indexer (the page's formula with H_I heads and
+  per-head weights) is kept exact here (float64 dots, ReLU, weighted sum);
+  the selection is made on those values, ties to the lower index.  A device
+  that sums in float32 can only be checked for a selection that is valid
+  within its own rounding bound (see the GPU tests).
 """
 from __future__ import annotations
 
@@ -54,6 +59,32 @@ def topk_select(scores, k: int) -> np.ndarray:
     sel = np.sort(order[:keff]).astype(np.int32)
     out = np.full(k, -1, dtype=np.int32)
     out[:keff] = sel
+    return out
+
+
+def weighted_indexer_scores(q_index, w_index, k_index, seq_len: int) -> np.ndarray:
+    """I_s = sum_j w_j * ReLU(q_j . k_s) over the H_I indexer heads j, for
+    s < seq_len, in float64.
+
+    [稀疏注意力] DSA ① Lightning Indexer: H_I query heads q_j (64 on the
+    page), one key k_s shared by all heads, a learned weight w_j per head, ReLU
+    in place of softmax, summed over the heads.
+
+    q_index: [H_I, D_idx]; w_index: [H_I]; k_index: [L, D_idx].
+    """
+    k = np.asarray(k_index, dtype=np.float64)[:seq_len]
+    dots = k @ np.asarray(q_index, dtype=np.float64).T          # [L, H_I]
+    return np.maximum(dots, 0.0) @ np.asarray(w_index, dtype=np.float64)
+
+
+def topk_select_exact(scores, k: int) -> np.ndarray:
+    """:func:`topk_select` on float64 scores (no rounding to float32)."""
+    scores = np.asarray(scores, dtype=np.float64)
+    n = scores.shape[0]
+    order = np.lexsort((np.arange(n), -scores))
+    keff = min(k, n)
+    out = np.full(k, -1, dtype=np.int32)
+    out[:keff] = np.sort(order[:keff]).astype(np.int32)
     return out
 
 

@@ -139,3 +139,47 @@ def test_dense_mla_decode_equals_unabsorbed_multihead_attention():
             one = sparse.sparse_attention_one(qa[b, h], lat[b], np.arange(seq[b]), scale, dc)
             assert np.array_equal(one, o_lat[b, h])
 
+
+
+def test_weighted_indexer_pins():
+    """[稀疏注意力] DSA ①: I_s = sum_j w_j ReLU(q_j . k_s).
+    * one head with weight 1 is the single-head indexer (exactly, before its
+      float32 rounding);
+    * two heads q_0 = e_1, q_1 = -e_1 with weights (1, 2) give the closed form
+      k_1 for k_1 >= 0 and -2 k_1 for k_1 < 0 (ReLU per head, then weights;
+      summing before the ReLU would give max(0, -k_1) instead);
+    * linear in the weights, and a head whose dots are all negative adds
+      nothing whatever its weight."""
+    rng = np.random.default_rng(5)
+    L, D = 200, 16
+    k = rng.standard_normal((L, D))
+    q = rng.standard_normal((1, D))
+    one = sparse.weighted_indexer_scores(q, np.array([1.0]), k, L)
+    assert np.array_equal(one.astype(np.float32), sparse.indexer_scores(q[0], k, L))
+    q2 = np.zeros((2, D))
+    q2[0, 1], q2[1, 1] = 1.0, -1.0
+    got = sparse.weighted_indexer_scores(q2, np.array([1.0, 2.0]), k, L)
+    want = np.where(k[:, 1] >= 0, k[:, 1], -2.0 * k[:, 1])
+    assert np.array_equal(got, want)
+    qh = rng.standard_normal((3, D))
+    w1, w2 = rng.standard_normal(3), rng.standard_normal(3)
+    s12 = sparse.weighted_indexer_scores(qh, w1 + w2, k, L)
+    assert np.allclose(s12, sparse.weighted_indexer_scores(qh, w1, k, L)
+                       + sparse.weighted_indexer_scores(qh, w2, k, L), rtol=1e-12, atol=1e-12)
+    kpos = np.abs(k)
+    qneg = np.vstack([qh[:1], -np.abs(rng.standard_normal((1, D)))])   # head 1: all dots < 0
+    a = sparse.weighted_indexer_scores(qneg, np.array([0.7, 123.0]), kpos, L)
+    b = sparse.weighted_indexer_scores(qneg[:1], np.array([0.7]), kpos, L)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-15)   # (the product's summation order may differ)
+
+
+def test_topk_select_exact_matches_sorting():
+    """Exact-score top-k: the k largest by value, ties to the lower index."""
+    s = np.array([3.0, -1.0, 3.0, 7.5, 0.0, 3.0, -2.0])
+    assert list(sparse.topk_select_exact(s, 3)) == [0, 2, 3]
+    assert list(sparse.topk_select_exact(s, 4)) == [0, 2, 3, 5]
+    assert list(sparse.topk_select_exact(s[:2], 4)) == [0, 1, -1, -1]
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal(1000)
+    sel = sparse.topk_select_exact(v, 100)
+    assert set(sel) == set(np.argsort(-v)[:100])
