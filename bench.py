@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default="", help="comma list of sections (decode32k,decode4k,dynamic,append32k,window,mla,"
-                    "prefill,prefill_window,sparse,rope) for profiling runs")
+                    "prefill,prefill_window,sparse,sparse_weighted,rope) for profiling runs")
     return ap.parse_args()
 
 
@@ -298,6 +298,39 @@ def bench_sparse(cfg, steps, warmup):
     return dict(ms=ev_ms, alg_bytes=alg, gbs=alg / ev_ms / 1e6)
 
 
+def bench_sparse_weighted(cfg, steps, warmup, H_I=64):
+    """topk_sparse_decode_weighted: the 64-head weighted indexer on the matrix
+    cores, then the same top-k and attention."""
+    import numpy as np
+    import torch
+
+    import mqa_kv_cache_amd as m
+    from workloads import device_randn_bf16
+    B, H, S, k = cfg.B, cfg.H, cfg.S_max, cfg.top_k
+    nsets = 8
+    sets = [(device_randn_bf16((B, H, cfg.Dqk), cfg.seed * 100 + 10 * i + 1),
+             device_randn_bf16((B, S, cfg.Dqk), cfg.seed * 100 + 10 * i + 2),
+             device_randn_bf16((B, H_I, cfg.D_idx), cfg.seed * 100 + 10 * i + 3),
+             device_randn_bf16((B, S, cfg.D_idx), cfg.seed * 100 + 10 * i + 4)) for i in range(nsets)]
+    w = torch.from_numpy((np.random.default_rng(cfg.seed).standard_normal((B, H_I)) / 8)
+                         .astype(np.float32)).cuda()
+    lens = torch.from_numpy(cfg.seq_lens()).cuda()
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, H, cfg.Dv), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(m.topk_sparse_decode_workspace_size(B, H, S, k), dtype=torch.uint8, device="cuda")
+    alg = (B * S * cfg.D_idx * 2 + B * k * cfg.Dqk * 2 + B * H * cfg.Dqk * 2 + B * H_I * cfg.D_idx * 2
+           + B * k * 4 + B * H * cfg.Dv * 2)
+
+    def step(i):
+        q, lat, qi, ki = sets[i % nsets]
+        m.topk_sparse_decode_weighted(q, lat, qi, w, ki, lens, k, cfg.scale, topk_idx=idx, out=out,
+                                      workspace=ws)
+
+    ev_ms = region_ms(step, steps, warmup)
+    log(f"[bench] sparse weighted (H_I={H_I}): {ev_ms * 1e3:.1f} us per call, {alg / ev_ms / 1e6:.0f} GB/s algorithmic")
+    return dict(ms=ev_ms, alg_bytes=alg, gbs=alg / ev_ms / 1e6)
+
+
 def bench_mla(cfg, steps, warmup):
     """Dense absorbed-MLA decode over the full latent cache (no selection)."""
     import torch
@@ -419,6 +452,8 @@ def main():
         res["pw"] = bench_prefill_window(PREFILL_8K, K, W)
     if want("sparse"):
         res["s"] = bench_sparse(SPARSE_128K, K, W)
+    if want("sparse_weighted"):
+        res["sw"] = bench_sparse_weighted(SPARSE_128K, K, W)
     if want("mla"):
         res["mla"] = bench_mla(SPARSE_128K, K, W)
     if want("rope"):
@@ -507,6 +542,11 @@ def main():
         line["sparse_128k"] = {"GB/s": round(s["gbs"], 1), "ms_per_call": round(s["ms"], 5),
                                "algorithmic_bytes": s["alg_bytes"],
                                "pct_of_hbm_peak": round(100 * s["gbs"] / HBM_PEAK_GBS, 2)}
+    if "sw" in res:
+        sw = res["sw"]
+        line["sparse_weighted64_128k"] = {"GB/s": round(sw["gbs"], 1), "ms_per_call": round(sw["ms"], 5),
+                                          "algorithmic_bytes": sw["alg_bytes"],
+                                          "pct_of_hbm_peak": round(100 * sw["gbs"] / HBM_PEAK_GBS, 2)}
     if "mla" in res:
         ml = res["mla"]
         line["mla_dense_128k"] = {"GB/s": round(ml["gbs"], 1), "TFLOP/s": round(ml["tflops"], 1),

@@ -309,6 +309,29 @@ gqa_status topk_sparse_decode(const void* q, const void* latent, const void* q_i
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * topk_sparse_decode_weighted -- topk_sparse_decode with the multi-head
+ * weighted indexer ([稀疏注意力] DSA ①, the Lightning Indexer formula):
+ *     I_s = sum_{j < H_I} w_j * ReLU(q_index[j] . k_index[s])
+ * H_I query heads share the single key row; w_j is a per-head weight of
+ * either sign.  The indexer runs on the matrix cores: each head's dot
+ * product and the weighted sum are accumulated in fp32 (not the exact dots
+ * of topk_sparse_decode), and the top_k largest I_s (ties to the lower index)
+ * are selected as in topk_sparse_decode; steps 3 and the outputs are the same.
+ *
+ *   q_index     bf16 [B][H_I][D_idx]
+ *   w_index     fp32 [B][H_I] (device, 4-byte aligned)
+ *   H_I         16, 32, 48 or 64 (others: GQA_ERR_UNSUPPORTED; < 1: invalid)
+ *   other arguments, workspace (topk_sparse_decode_workspace_size), limits
+ *   and errors as topk_sparse_decode.
+ */
+gqa_status topk_sparse_decode_weighted(const void* q, const void* latent, const void* q_index,
+                                       const float* w_index, const void* k_index,
+                                       const int32_t* seq_lens, int32_t B, int32_t H, int32_t H_I,
+                                       int32_t Dqk, int32_t Dv, int32_t D_idx, int32_t S_max,
+                                       int32_t top_k, float scale, int32_t* topk_idx, void* out,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mla_decode -- dense decode over an MLA latent cache in the absorbed form
  * ([attention] DSA ② and "乘法结合律" 的变换; [注意力变体与MoE] "MLA"): with
  * W_UK folded into the query and W_UV applied after the sum, every head

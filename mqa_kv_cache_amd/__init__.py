@@ -31,7 +31,8 @@ EXPORTED = [
     "gqa_decode_workspace_size",
     "gqa_decode_workspace_size_parts", "gqa_decode_partial", "gqa_decode_combine",
     "gqa_prefill_causal", "gqa_prefill_window", "gqa_prefill_workspace_size",
-    "topk_sparse_decode", "topk_sparse_decode_workspace_size", "mla_decode",
+    "topk_sparse_decode", "topk_sparse_decode_workspace_size", "topk_sparse_decode_weighted",
+    "mla_decode",
     "mla_decode_workspace_size", "kv_bytes_per_token",
     "mla_kv_bytes_per_token", "gqa_status_string",
 ]
@@ -111,6 +112,11 @@ _lib.topk_sparse_decode.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, 
                                     _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                     _c_int32, ctypes.c_float, _c_void_p, _c_void_p, _c_void_p,
                                     _c_size_t, _c_void_p]
+_lib.topk_sparse_decode_weighted.restype = _c_int32
+_lib.topk_sparse_decode_weighted.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                             _c_void_p, _c_int32, _c_int32, _c_int32, _c_int32,
+                                             _c_int32, _c_int32, _c_int32, _c_int32, ctypes.c_float,
+                                             _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]
 _lib.mla_decode_workspace_size.restype = _c_size_t
 _lib.mla_decode_workspace_size.argtypes = [_c_int32] * 3
 _lib.mla_decode.restype = _c_int32
@@ -413,6 +419,45 @@ def topk_sparse_decode(q, latent, q_index, k_index, seq_lens, top_k: int, scale:
                                  out.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                  _stream(stream))
     _check(st, "topk_sparse_decode")
+    return topk_idx, out
+
+
+def topk_sparse_decode_weighted(q, latent, q_index, w_index, k_index, seq_lens, top_k: int,
+                                scale: float, Dv: int = 512, topk_idx=None, out=None,
+                                workspace=None, stream=None):
+    """topk_sparse_decode with the multi-head weighted indexer: q_index
+    [B,H_I,D_idx] bf16, w_index [B,H_I] float32.  Returns (topk_idx, out)."""
+    B, H, Dqk = q.shape
+    S_max = latent.shape[1]
+    H_I, D_idx = q_index.shape[1], q_index.shape[2]
+    _shape(latent, (B, S_max, Dqk), "latent")
+    _shape(q_index, (B, H_I, D_idx), "q_index")
+    _shape(w_index, (B, H_I), "w_index")
+    _shape(k_index, (B, S_max, D_idx), "k_index")
+    _shape(seq_lens, (B,), "seq_lens")
+    for t, nm in ((q, "q"), (latent, "latent"), (q_index, "q_index"), (k_index, "k_index")):
+        _dev(t, nm)
+    _dev(w_index, "w_index", dtype=torch.float32)
+    _dev(seq_lens, "seq_lens", dtype=torch.int32)
+    if topk_idx is None:
+        topk_idx = torch.empty((B, top_k), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=torch.bfloat16, device=q.device)
+    _shape(topk_idx, (B, top_k), "topk_idx")
+    _shape(out, (B, H, Dv), "out")
+    _dev(topk_idx, "topk_idx", dtype=torch.int32)
+    _dev(out, "out")
+    need = topk_sparse_decode_workspace_size(B, H, S_max, top_k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    st = _lib.topk_sparse_decode_weighted(q.data_ptr(), latent.data_ptr(), q_index.data_ptr(),
+                                          w_index.data_ptr(), k_index.data_ptr(),
+                                          seq_lens.data_ptr(), B, H, H_I, Dqk, Dv, D_idx, S_max,
+                                          int(top_k), float(scale), topk_idx.data_ptr(),
+                                          out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                          _stream(stream))
+    _check(st, "topk_sparse_decode_weighted")
     return topk_idx, out
 
 

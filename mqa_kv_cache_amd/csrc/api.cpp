@@ -328,6 +328,31 @@ gqa_status topk_sparse_decode(const void* q, const void* latent, const void* q_i
                                               (hipStream_t)stream));
 }
 
+gqa_status topk_sparse_decode_weighted(const void* q, const void* latent, const void* q_index,
+                                       const float* w_index, const void* k_index,
+                                       const int32_t* seq_lens, int32_t B, int32_t H, int32_t H_I,
+                                       int32_t Dqk, int32_t Dv, int32_t D_idx, int32_t S_max,
+                                       int32_t top_k, float scale, int32_t* topk_idx, void* out,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+    gqa_status st = check_sparse_shape(B, H, Dqk, Dv, D_idx, S_max, top_k);
+    if (st != GQA_OK) return st;
+    if (H_I < 1) return GQA_ERR_INVALID_ARGUMENT;
+    if (H_I != 16 && H_I != 32 && H_I != 48 && H_I != 64) return GQA_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+    if (!q || !latent || !q_index || !w_index || !k_index || !seq_lens || !topk_idx || !out ||
+        !workspace)
+        return GQA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(latent) || !aligned16(q_index) || !aligned16(k_index) ||
+        !aligned16(topk_idx) || !aligned16(out) || (reinterpret_cast<uintptr_t>(w_index) & 3u) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return GQA_ERR_INVALID_ARGUMENT;
+    const SparseLayout lay = sparse_layout(B, H, S_max, top_k);
+    if (workspace_bytes < lay.total) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    return from_hip(launch_topk_sparse_decode(q, latent, q_index, k_index, seq_lens, B, H, S_max,
+                                              top_k, scale, topk_idx, out, workspace, lay,
+                                              (hipStream_t)stream, w_index, H_I));
+}
+
 static gqa_status check_mla_shape(int32_t B, int32_t H, int32_t Dqk, int32_t Dv, int32_t S_max) {
     if (B < 1 || H < 1 || Dqk < 1 || Dv < 1 || S_max < 1 || Dv > Dqk) return GQA_ERR_INVALID_ARGUMENT;
     if (Dqk != 576 || Dv != 512) return GQA_ERR_UNSUPPORTED;

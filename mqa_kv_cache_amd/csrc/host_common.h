@@ -96,6 +96,7 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
                                      const void* k_index, const int32_t* seq_lens, int32_t B,
                                      int32_t H, int32_t S_max, int32_t top_k, float scale,
                                      int32_t* topk_idx, void* out, void* workspace,
-                                     const SparseLayout& lay, hipStream_t s);
+                                     const SparseLayout& lay, hipStream_t s, const float* w_index = nullptr,
+                                     int32_t H_I = 0);
 
 }  // namespace gqa

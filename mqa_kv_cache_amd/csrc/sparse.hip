@@ -154,6 +154,125 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// 1b. multi-head weighted indexer ([稀疏注意力] DSA ①):
+//     I_s = sum_j w_j ReLU(q_j . k_s) over H_I = 16 NHB heads.
+// S^T = K . Q^T on MFMA (16 keys x 16 heads per product, four 32-dim
+// k-steps), so the key rows stream from HBM once for all heads.  ReLU and
+// the weights are applied in fp32 per (key, head); the heads are summed in
+// the lane (over the NHB head blocks) and across the 16 lanes of the head
+// index (DPP).  The sums are fp32 (MFMA accumulation), not the exact dots of
+// the single-head indexer.  Scores are stored as order-preserving keys (sign
+// bit flipped for non-negative values, all bits for negative ones) because
+// the weights may be negative; the radix select below works on those keys
+// unchanged, and zero is always +0 so that equal scores stay equal keys.
+__device__ __forceinline__ float dpp_fadd(float v, int ctrl_id) {
+    int x;
+    switch (ctrl_id) {   // (a switch keeps the DPP control a constant)
+        case 0: x = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false); break;   // lane ^ 1
+        case 1: x = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false); break;   // lane ^ 2
+        case 2: x = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false); break;  // 7 - lane in 8
+        default: x = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false); break; // 15 - lane in 16
+    }
+    return v + __int_as_float(x);
+}
+// Sum over the 16 lanes of a row; every lane receives the same value.
+__device__ __forceinline__ float row16_sum(float v) {
+    v = dpp_fadd(v, 0);
+    v = dpp_fadd(v, 1);
+    v = dpp_fadd(v, 2);
+    return dpp_fadd(v, 3);
+}
+__device__ __forceinline__ uint32_t order_key(float v) {
+    v = (v == 0.0f) ? 0.0f : v;   // -0 -> +0
+    const uint32_t u = __float_as_uint(v);
+    return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+
+template <int NHB>
+__global__ __launch_bounds__(256) void indexer_weighted_kernel(
+    const uint16_t* __restrict__ q_index, const float* __restrict__ w_index,
+    const uint16_t* __restrict__ k_index, const int32_t* __restrict__ seq_lens, int S_max,
+    int S_stride, int rows_per_block, uint32_t* __restrict__ keys, uint32_t* __restrict__ hist) {
+    constexpr int HI = 16 * NHB;
+    __shared__ uint32_t lh[kHistBins];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = lane >> 4, n = lane & 15;
+    const int b = blockIdx.y;
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int r_begin = blockIdx.x * rows_per_block;
+    const int r_end = min(r_begin + rows_per_block, L);
+    for (int i = tid; i < kHistBins; i += 256) lh[i] = 0u;
+    __syncthreads();
+    if (r_begin < r_end) {
+        // B operand: lane (G, n) holds head 16 hb + n, dims 32 u + 8 G .. +7
+        u32x4 qf[NHB][4];
+        float w[NHB];
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+            const uint16_t* qrow = q_index + ((size_t)b * HI + 16 * hb + n) * kDidx + 8 * G;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) qf[hb][u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u);
+            w[hb] = w_index[(size_t)b * HI + 16 * hb + n];
+        }
+        // descriptors cover exactly this block's rows: loads past them read
+        // zeros and stores past them are dropped, so the loop has no branch
+        // around a memory access
+        const int nrows = r_end - r_begin;
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(
+            k_index + ((size_t)b * S_max + r_begin) * kDidx, (uint32_t)nrows * kDidx * 2u);
+        const __amdgpu_buffer_rsrc_t sr =
+            make_rsrc(keys + (size_t)b * S_stride + r_begin, (uint32_t)nrows * 4u);
+        // A operand of 16-key group g: lane (G, n) holds key 16 g + n, dims
+        // 32 u + 8 G .. +7 (each load covers 64 contiguous bytes of 16 rows)
+        auto load = [&](u32x4 (&kk)[4], int g) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                kk[u] = buf_load16_nt(kr, (uint32_t)(((16 * g + n) * kDidx + 32 * u + 8 * G) * 2));
+        };
+        auto score = [&](const u32x4 (&kk)[4], int g) {
+            float t[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int hb = 0; hb < NHB; ++hb) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc = mfma16(kk[u], qf[hb][u], acc);
+                // lane (G, n): keys 16 g + 4 G + i of head 16 hb + n
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t[i] = fmaf(w[hb], fmaxf(acc[i], 0.0f), t[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t[i] = row16_sum(t[i]);
+            // lane n < 4 of each row stores key 16 g + 4 G + n
+            const float v = n == 0 ? t[0] : n == 1 ? t[1] : n == 2 ? t[2] : t[3];
+            const uint32_t key = order_key(v);
+            const int row = 16 * g + 4 * G + n;
+            __builtin_amdgcn_raw_buffer_store_b32(key, sr, n < 4 ? (uint32_t)row * 4u : 0x80000000u, 0, 0);
+            const uint32_t bin = key >> 20;
+            if (n < 4 && row < nrows && bin) atomicAdd(&lh[bin], 1u);
+        };
+        // groups g = wave, wave + 4, ...: the four waves read adjacent 4 KB
+        // blocks; two register sets, the next group requested first
+        const int n_groups = (nrows + 15) / 16;
+        const int n_steps = (n_groups + 3) / 4;   // uniform over the workgroup
+        u32x4 ka[4], kb[4];
+        int g = wave;
+        load(ka, g);
+        for (int st = 0; st + 1 < n_steps; st += 2) {   // no early exit: one loop state
+            load(kb, g + 4);
+            score(ka, g);
+            load(ka, g + 8);
+            score(kb, g + 4);
+            g += 8;
+        }
+        if (n_steps & 1) score(ka, g);
+    }
+    __syncthreads();
+    for (int i = tid; i < kHistBins; i += 256)
+        if (lh[i]) atomicAdd(&hist[(size_t)b * kHistBins + i], lh[i]);
+}
+
+// ---------------------------------------------------------------------------
 // 2. top-k selection, spread over (chunk, batch) workgroups:
 //    topk_candidates_kernel  first digit from the histogram; keys of the
 //                            threshold bin copied to the chunk's own slice,
@@ -1104,7 +1223,8 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
                                      const void* k_index, const int32_t* seq_lens, int32_t B,
                                      int32_t H, int32_t S_max, int32_t top_k, float scale,
                                      int32_t* topk_idx, void* out, void* workspace,
-                                     const SparseLayout& lay, hipStream_t s) {
+                                     const SparseLayout& lay, hipStream_t s, const float* w_index,
+                                     int32_t H_I) {
     char* w = reinterpret_cast<char*>(workspace);
     float* scores = reinterpret_cast<float*>(w);
     w += lay.scores_bytes;
@@ -1127,9 +1247,34 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
     const int nz = B * kHistBins;
     hipLaunchKernelGGL(zero_u32_kernel, dim3((nz + 255) / 256), dim3(256), 0, s, hist, nz);
     const int rows_per_block = 1024;
-    hipLaunchKernelGGL(indexer_kernel, dim3((S_max + rows_per_block - 1) / rows_per_block, B),
-                       dim3(256), 0, s, (const uint16_t*)q_index, (const uint16_t*)k_index,
-                       seq_lens, S_max, S_stride, rows_per_block, scores, hist);
+    const dim3 igrid((S_max + rows_per_block - 1) / rows_per_block, B);
+    uint32_t* keys = reinterpret_cast<uint32_t*>(scores);
+    const uint16_t* qi = (const uint16_t*)q_index;
+    const uint16_t* ki = (const uint16_t*)k_index;
+    switch (H_I) {
+        case 0:
+            hipLaunchKernelGGL(indexer_kernel, igrid, dim3(256), 0, s, qi, ki, seq_lens, S_max,
+                               S_stride, rows_per_block, scores, hist);
+            break;
+        case 16:
+            hipLaunchKernelGGL((indexer_weighted_kernel<1>), igrid, dim3(256), 0, s, qi, w_index, ki,
+                               seq_lens, S_max, S_stride, rows_per_block, keys, hist);
+            break;
+        case 32:
+            hipLaunchKernelGGL((indexer_weighted_kernel<2>), igrid, dim3(256), 0, s, qi, w_index, ki,
+                               seq_lens, S_max, S_stride, rows_per_block, keys, hist);
+            break;
+        case 48:
+            hipLaunchKernelGGL((indexer_weighted_kernel<3>), igrid, dim3(256), 0, s, qi, w_index, ki,
+                               seq_lens, S_max, S_stride, rows_per_block, keys, hist);
+            break;
+        case 64:
+            hipLaunchKernelGGL((indexer_weighted_kernel<4>), igrid, dim3(256), 0, s, qi, w_index, ki,
+                               seq_lens, S_max, S_stride, rows_per_block, keys, hist);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
     hipLaunchKernelGGL(topk_candidates_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores,
                        hist, seq_lens, S_max, S_stride, top_k, cand, cand_cnt, cand_above, nkc,
                        info);

@@ -191,6 +191,24 @@ def test_sparse_validation(m):
     assert call(wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
 
 
+def test_sparse_weighted_validation(m):
+    lib = m.lib()
+    need = m.topk_sparse_decode_workspace_size(2, 128, 4096, 2048)
+
+    def call(HI=64, w=P, wsn=need, H=128, k=2048):
+        return lib.topk_sparse_decode_weighted(P, P, P, w, P, P, 2, H, HI, 576, 512, 128, 4096, k,
+                                               0.07, P, P, P, wsn, None)
+
+    assert call(HI=0) == m.ERR_INVALID_ARGUMENT
+    assert call(HI=24) == m.ERR_UNSUPPORTED
+    assert call(HI=128) == m.ERR_UNSUPPORTED
+    assert call(w=None) == m.ERR_INVALID_ARGUMENT
+    assert call(w=P + 2) == m.ERR_INVALID_ARGUMENT
+    assert call(k=0) == m.ERR_INVALID_ARGUMENT
+    assert call(H=100) == m.ERR_UNSUPPORTED
+    assert call(wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+
+
 def test_mla_validation(m):
     lib = m.lib()
 
