@@ -23,4 +23,4 @@ middle band (the pages say "linear transition" without a formula) and the
 particular numerical values of the synthetic outputs, which only this oracle
 defines.
 """
-from . import rope, attention, sparse, kv_bytes  # noqa: F401
+from . import rope, attention, sparse, qsa, kv_bytes  # noqa: F401
