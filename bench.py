@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default="", help="comma list of sections (decode32k,decode4k,dynamic,append32k,window,mla,"
-                    "prefill,prefill_window,sparse,sparse_weighted,rope) for profiling runs")
+                    "prefill,prefill_window,sparse,sparse_weighted,qsa,rope) for profiling runs")
     return ap.parse_args()
 
 
@@ -331,6 +331,39 @@ def bench_sparse_weighted(cfg, steps, warmup, H_I=64):
     return dict(ms=ev_ms, alg_bytes=alg, gbs=alg / ev_ms / 1e6)
 
 
+def bench_qsa(cfg, steps, warmup):
+    """qsa_sparse_decode: micro-block indexer over the 128K context, top 512
+    blocks plus the tail, sparse GQA over the <= 2051 tokens."""
+    import torch
+
+    import mqa_kv_cache_amd as m
+    from workloads import device_randn_bf16
+    B, Hq, Hkv, D, S = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.S_max
+    nsets = 2   # 1.2 GB of caches and indexer keys per set
+    sets = [(device_randn_bf16((B, Hq, D), cfg.seed * 100 + 10 * i + 1),
+             device_randn_bf16((B, Hkv, S, D), cfg.seed * 100 + 10 * i + 2),
+             device_randn_bf16((B, Hkv, S, D), cfg.seed * 100 + 10 * i + 3),
+             device_randn_bf16((B, cfg.H_I, cfg.D_idx), cfg.seed * 100 + 10 * i + 4),
+             device_randn_bf16((B, S, cfg.D_idx), cfg.seed * 100 + 10 * i + 5)) for i in range(nsets)]
+    lens = torch.from_numpy(cfg.seq_lens()).cuda()
+    tok = torch.empty((B, m.QSA_TOKENS), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(m.qsa_sparse_decode_workspace_size(B, Hq, S), dtype=torch.uint8, device="cuda")
+    rope = cfg.block_rope()
+    n_tok = min(512, S // 4) * 4 + S % 4
+    alg = (B * S * cfg.D_idx * 2 + B * Hkv * n_tok * D * 2 * 2 + B * Hq * D * 2 * 2
+           + B * cfg.H_I * cfg.D_idx * 2 + B * m.QSA_TOKENS * 4)
+
+    def step(i):
+        q, kc, vc, qi, ki = sets[i % nsets]
+        m.qsa_sparse_decode(q, kc, vc, qi, ki, lens, cfg.scale, block_rope=rope, token_idx=tok,
+                            out=out, workspace=ws)
+
+    ev_ms = region_ms(step, steps, warmup)
+    log(f"[bench] qsa: {ev_ms * 1e3:.1f} us per call, {alg / ev_ms / 1e6:.0f} GB/s algorithmic")
+    return dict(ms=ev_ms, alg_bytes=alg, gbs=alg / ev_ms / 1e6)
+
+
 def bench_mla(cfg, steps, warmup):
     """Dense absorbed-MLA decode over the full latent cache (no selection)."""
     import torch
@@ -427,7 +460,7 @@ def main():
     import torch
 
     import mqa_kv_cache_amd as m  # noqa: F401  (fails loudly without the HIP library)
-    from workloads import DECODE_4K, DECODE_32K_YARN, PREFILL_8K, SPARSE_128K
+    from workloads import DECODE_4K, DECODE_32K_YARN, PREFILL_8K, QSA_128K, SPARSE_128K
     torch.cuda.set_device(0)
     only = set(s for s in args.only.split(",") if s)
     want = (lambda s: not only or s in only)
@@ -454,6 +487,8 @@ def main():
         res["s"] = bench_sparse(SPARSE_128K, K, W)
     if want("sparse_weighted"):
         res["sw"] = bench_sparse_weighted(SPARSE_128K, K, W)
+    if want("qsa"):
+        res["qsa"] = bench_qsa(QSA_128K, K, W)
     if want("mla"):
         res["mla"] = bench_mla(SPARSE_128K, K, W)
     if want("rope"):
@@ -547,6 +582,11 @@ def main():
         line["sparse_weighted64_128k"] = {"GB/s": round(sw["gbs"], 1), "ms_per_call": round(sw["ms"], 5),
                                           "algorithmic_bytes": sw["alg_bytes"],
                                           "pct_of_hbm_peak": round(100 * sw["gbs"] / HBM_PEAK_GBS, 2)}
+    if "qsa" in res:
+        r = res["qsa"]
+        line["qsa_128k"] = {"GB/s": round(r["gbs"], 1), "ms_per_call": round(r["ms"], 5),
+                            "algorithmic_bytes": r["alg_bytes"],
+                            "pct_of_hbm_peak": round(100 * r["gbs"] / HBM_PEAK_GBS, 2)}
     if "mla" in res:
         ml = res["mla"]
         line["mla_dense_128k"] = {"GB/s": round(ml["gbs"], 1), "TFLOP/s": round(ml["tflops"], 1),

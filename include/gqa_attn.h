@@ -332,6 +332,41 @@ gqa_status topk_sparse_decode_weighted(const void* q, const void* latent, const 
                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qsa_sparse_decode -- QSA decode ([attention] Qwen Sparse Attention ①-④):
+ *   1. the first 4 * floor(L/4) indexer keys form 4-token micro-blocks; a
+ *      block's key is the mean of its keys, normalised to unit length,
+ *      rotated by block_rope at the block's first position 4 j;
+ *   2. block score = sum over the H_I indexer heads of ReLU(q_index[h] . key);
+ *   3. the 512 best blocks (ties to the lower block; all if there are fewer)
+ *      are expanded to their 4 tokens and the L mod 4 tail tokens are added:
+ *      token_idx[b] holds at most 2051 ascending positions, -1 after;
+ *   4. standard GQA attention of every query head over those tokens of its
+ *      kv head's cache:  out = softmax(scale * q . K[t]) V[t].
+ * The block keys are computed in fp32 and enter the score product as hi + lo
+ * bf16 terms; scores are summed in fp32.
+ *
+ *   q          bf16 [B][Hq][D], already rotated at its position (post-RoPE cache)
+ *   k_cache    bf16 [B][Hkv][S_max][D], v_cache the same
+ *   q_index    bf16 [B][H_I][D_idx], already rotated at the query position
+ *   k_index    bf16 [B][S_max][D_idx], indexer keys before RoPE
+ *   seq_lens   device int32 [B], each in [1, S_max]
+ *   block_rope NULL / NONE: no rotation; otherwise applied to the first
+ *              rotary_dim dims of the block keys (Dynamic NTK: unsupported)
+ *   token_idx  int32 [B][2051] (output), out bf16 [B][Hq][D] (output)
+ *   workspace  >= qsa_sparse_decode_workspace_size(B, Hq, S_max) bytes, 256-byte aligned
+ * Supported: D = 128, D_idx = 128, Hq/Hkv <= 16, H_I in {16, 32, 48, 64},
+ * S_max * D * 2 < 2^31.  Errors as topk_sparse_decode.
+ */
+size_t qsa_sparse_decode_workspace_size(int32_t B, int32_t Hq, int32_t S_max);
+
+gqa_status qsa_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
+                             const void* q_index, const void* k_index, const int32_t* seq_lens,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t H_I,
+                             int32_t D_idx, int32_t S_max, float scale,
+                             const gqa_rope_params* block_rope, int32_t* token_idx, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mla_decode -- dense decode over an MLA latent cache in the absorbed form
  * ([attention] DSA ② and "乘法结合律" 的变换; [注意力变体与MoE] "MLA"): with
  * W_UK folded into the query and W_UV applied after the sum, every head

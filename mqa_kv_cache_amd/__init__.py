@@ -32,6 +32,7 @@ EXPORTED = [
     "gqa_decode_workspace_size_parts", "gqa_decode_partial", "gqa_decode_combine",
     "gqa_prefill_causal", "gqa_prefill_window", "gqa_prefill_workspace_size",
     "topk_sparse_decode", "topk_sparse_decode_workspace_size", "topk_sparse_decode_weighted",
+    "qsa_sparse_decode", "qsa_sparse_decode_workspace_size",
     "mla_decode",
     "mla_decode_workspace_size", "kv_bytes_per_token",
     "mla_kv_bytes_per_token", "gqa_status_string",
@@ -117,6 +118,12 @@ _lib.topk_sparse_decode_weighted.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c
                                              _c_void_p, _c_int32, _c_int32, _c_int32, _c_int32,
                                              _c_int32, _c_int32, _c_int32, _c_int32, ctypes.c_float,
                                              _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]
+_lib.qsa_sparse_decode_workspace_size.restype = _c_size_t
+_lib.qsa_sparse_decode_workspace_size.argtypes = [_c_int32] * 3
+_lib.qsa_sparse_decode.restype = _c_int32
+_lib.qsa_sparse_decode.argtypes = ([_c_void_p] * 6 + [_c_int32] * 7
+                                   + [ctypes.c_float, _rope_p, _c_void_p, _c_void_p, _c_void_p,
+                                      _c_size_t, _c_void_p])
 _lib.mla_decode_workspace_size.restype = _c_size_t
 _lib.mla_decode_workspace_size.argtypes = [_c_int32] * 3
 _lib.mla_decode.restype = _c_int32
@@ -459,6 +466,51 @@ def topk_sparse_decode_weighted(q, latent, q_index, w_index, k_index, seq_lens, 
                                           _stream(stream))
     _check(st, "topk_sparse_decode_weighted")
     return topk_idx, out
+
+
+QSA_TOKENS = 4 * 512 + 3
+
+
+def qsa_sparse_decode_workspace_size(B, Hq, S_max) -> int:
+    return int(_lib.qsa_sparse_decode_workspace_size(B, Hq, S_max))
+
+
+def qsa_sparse_decode(q, k_cache, v_cache, q_index, k_index, seq_lens, scale: float,
+                      block_rope=None, token_idx=None, out=None, workspace=None, stream=None):
+    """q [B,Hq,D] (rotated), k/v caches [B,Hkv,S_max,D], q_index [B,H_I,D_idx]
+    (rotated), k_index [B,S_max,D_idx] (pre-RoPE), all bf16; seq_lens int32
+    [B].  Returns (token_idx int32 [B,2051], out bf16 [B,Hq,D])."""
+    B, Hq, D = q.shape
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    H_I, D_idx = q_index.shape[1], q_index.shape[2]
+    _shape(k_cache, (B, Hkv, S_max, D), "k_cache")
+    _shape(v_cache, (B, Hkv, S_max, D), "v_cache")
+    _shape(q_index, (B, H_I, D_idx), "q_index")
+    _shape(k_index, (B, S_max, D_idx), "k_index")
+    _shape(seq_lens, (B,), "seq_lens")
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (q_index, "q_index"),
+                  (k_index, "k_index")):
+        _dev(t, nm)
+    _dev(seq_lens, "seq_lens", dtype=torch.int32)
+    if token_idx is None:
+        token_idx = torch.empty((B, QSA_TOKENS), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _shape(token_idx, (B, QSA_TOKENS), "token_idx")
+    _shape(out, (B, Hq, D), "out")
+    _dev(token_idx, "token_idx", dtype=torch.int32)
+    _dev(out, "out")
+    need = qsa_sparse_decode_workspace_size(B, Hq, S_max)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", dtype=torch.uint8)
+    st = _lib.qsa_sparse_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                q_index.data_ptr(), k_index.data_ptr(), seq_lens.data_ptr(), B, Hq,
+                                Hkv, D, H_I, D_idx, S_max, float(scale), rope_params(block_rope),
+                                token_idx.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                                workspace.numel(), _stream(stream))
+    _check(st, "qsa_sparse_decode")
+    return token_idx, out
 
 
 def mla_decode_workspace_size(B, H, S_max) -> int:

@@ -353,6 +353,42 @@ gqa_status topk_sparse_decode_weighted(const void* q, const void* latent, const 
                                               (hipStream_t)stream, w_index, H_I));
 }
 
+size_t qsa_sparse_decode_workspace_size(int32_t B, int32_t Hq, int32_t S_max) {
+    if (B < 1 || Hq < 1 || S_max < 1) return 0;
+    return qsa_layout(B, Hq, S_max).total;
+}
+
+gqa_status qsa_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
+                             const void* q_index, const void* k_index, const int32_t* seq_lens,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t H_I,
+                             int32_t D_idx, int32_t S_max, float scale,
+                             const gqa_rope_params* block_rope, int32_t* token_idx, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || H_I < 1 || D_idx < 1 || S_max < 1)
+        return GQA_ERR_INVALID_ARGUMENT;
+    if (Hq % Hkv) return GQA_ERR_INVALID_ARGUMENT;
+    if (D != 128 || D_idx != 128 || Hq / Hkv > 16) return GQA_ERR_UNSUPPORTED;
+    if (H_I != 16 && H_I != 32 && H_I != 48 && H_I != 64) return GQA_ERR_UNSUPPORTED;
+    if ((int64_t)S_max * D * 2 >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+    if (block_rope && block_rope->scaling == GQA_ROPE_DYNAMIC_NTK) return GQA_ERR_UNSUPPORTED;
+    RopeDev rd;
+    gqa_status st = rope_prepare(block_rope, D_idx, &rd, 1);
+    if (st != GQA_OK) return st;
+    if (!q || !k_cache || !v_cache || !q_index || !k_index || !seq_lens || !token_idx || !out ||
+        !workspace)
+        return GQA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q_index) ||
+        !aligned16(k_index) || !aligned16(token_idx) || !aligned16(out) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return GQA_ERR_INVALID_ARGUMENT;
+    const QsaLayout lay = qsa_layout(B, Hq, S_max);
+    if (workspace_bytes < lay.total) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    return from_hip(launch_qsa_sparse_decode(q, k_cache, v_cache, q_index, k_index, seq_lens, B, Hq,
+                                             Hkv, H_I, S_max, scale, rd, token_idx, out, workspace,
+                                             lay, (hipStream_t)stream));
+}
+
 static gqa_status check_mla_shape(int32_t B, int32_t H, int32_t Dqk, int32_t Dv, int32_t S_max) {
     if (B < 1 || H < 1 || Dqk < 1 || Dv < 1 || S_max < 1 || Dv > Dqk) return GQA_ERR_INVALID_ARGUMENT;
     if (Dqk != 576 || Dv != 512) return GQA_ERR_UNSUPPORTED;

@@ -80,6 +80,24 @@ struct SparseLayout {
 };
 SparseLayout sparse_layout(int32_t B, int32_t H, int32_t S_max, int32_t top_k);
 
+struct QsaLayout {
+    SparseLayout sel;         // radix select over the block scores (no attention part)
+    int32_t n_blk_max;        // S_max / 4 (at least 1)
+    int32_t n_chunks;         // 128-token attention chunks of the 2051-token budget
+    size_t cnt_bytes;         // int32 [B] complete blocks per row
+    size_t blk_bytes;         // int32 [B][512] selected blocks
+    size_t o_bytes;           // fp32 [B][Hq][n_chunks][128] partial outputs
+    size_t ml_bytes;          // fp32 [B][Hq][n_chunks][2]
+    size_t total;
+};
+QsaLayout qsa_layout(int32_t B, int32_t Hq, int32_t S_max);
+hipError_t launch_qsa_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
+                                    const void* q_index, const void* k_index,
+                                    const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                    int32_t H_I, int32_t S_max, float scale, const RopeDev& rope,
+                                    int32_t* tok, void* out, void* workspace, const QsaLayout& lay,
+                                    hipStream_t s);
+
 struct MlaLayout {
     int32_t rows_per_split;   // latent rows per workgroup (a multiple of 32)
     int32_t n_split;          // row ranges per batch row

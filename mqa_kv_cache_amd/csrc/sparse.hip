@@ -1164,6 +1164,355 @@ constexpr int kMlaWaves = 4;   // 64 heads per workgroup, one wave per SIMD
 constexpr int kMlaTargetWgs = 256;
 constexpr int kMlaMinRows = 256;
 
+// ---------------------------------------------------------------------------
+// 5. QSA ([attention] Qwen Sparse Attention ①-④): micro-block selection, then
+//    standard sparse GQA over the selected tokens.
+//    qsa_block_kernel   one HBM pass over the indexer keys: per complete
+//                       4-token block the mean key, L2-normalised, rotated at
+//                       the block's first position (fp32, fp64 angles), fed
+//                       to the MFMA as hi + lo bf16 terms against the H_I
+//                       query heads; ReLU per head, summed; order keys and
+//                       the first-digit histogram as for the token indexer
+//    (the radix select of section 2 then takes the top 512 blocks)
+//    qsa_expand_kernel  blocks -> their 4 tokens, then the 0-3 tail tokens
+//    gqa_gather_attn_kernel  per (128 selected tokens, kv head, batch row):
+//                       the tokens' K and V rows gathered into LDS, the
+//                       decode MFMA scheme over D = 128 for the group's
+//                       g <= 16 query heads, a partial (m, l, o) per head
+//    qsa_combine_kernel the partials merged per (batch, head)
+// ---------------------------------------------------------------------------
+constexpr int kQsaBlock = 4;
+constexpr int kQsaTopBlocks = 512;
+constexpr int kQsaTokens = kQsaBlock * kQsaTopBlocks + kQsaBlock - 1;   // 2051
+constexpr int kGD = 128;                      // head dim of the GQA attention
+constexpr int kGRowStride = kGD * 2 + 16;     // 272 B: 8 consecutive rows on distinct banks
+constexpr int kGChunk = 128;                  // selected tokens per attention workgroup
+constexpr int kGSub = 32;                     // rows per sub-chunk
+constexpr int kGSubBytes = kGSub * kGRowStride;                  // 8704
+constexpr int kGSubCopies = (kGSubBytes + 1023) / 1024;          // 9 copies of 1 KB
+constexpr int kGBufBytes = kGSubCopies * 1024;
+
+template <int NHB>
+__global__ __launch_bounds__(256) void qsa_block_kernel(
+    const uint16_t* __restrict__ q_index, const uint16_t* __restrict__ k_index,
+    const int32_t* __restrict__ seq_lens, int S_max, int KS, int blocks_per_wg, RopeDev rope,
+    uint32_t* __restrict__ keys, uint32_t* __restrict__ hist) {
+    constexpr int HI = 16 * NHB;
+    __shared__ uint32_t lh[kHistBins];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = lane >> 4, n = lane & 15;
+    const int b = blockIdx.y;
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int nb = L / kQsaBlock;                            // complete blocks
+    const int k_begin = blockIdx.x * blocks_per_wg;
+    const int k_end = min(k_begin + blocks_per_wg, nb);
+    for (int i = tid; i < kHistBins; i += 256) lh[i] = 0u;
+    __syncthreads();
+    if (k_begin < k_end) {
+        u32x4 qf[NHB][4];
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+            const uint16_t* qrow = q_index + ((size_t)b * HI + 16 * hb + n) * kDidx + 8 * G;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) qf[hb][u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u);
+        }
+        const int nbl = k_end - k_begin;
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(
+            k_index + ((size_t)b * S_max + (size_t)kQsaBlock * k_begin) * kDidx,
+            (uint32_t)nbl * kQsaBlock * kDidx * 2u);
+        const __amdgpu_buffer_rsrc_t sr = make_rsrc(keys + (size_t)b * KS + k_begin, (uint32_t)nbl * 4u);
+        const int n_groups = (nbl + 15) / 16;
+        const int n_steps = (n_groups + 3) / 4;              // uniform over the workgroup
+        for (int st = 0; st < n_steps; ++st) {
+            const int g = 4 * st + wave;                     // 16-block group of this wave
+            // lane (G, n): block 16 g + n, dims 32 u + 8 G .. +7 of its 4 keys
+            u32x4 raw[kQsaBlock][4];
+#pragma unroll
+            for (int r = 0; r < kQsaBlock; ++r)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    raw[r][u] = buf_load16_nt(
+                        kr, (uint32_t)((((16 * g + n) * kQsaBlock + r) * kDidx + 32 * u + 8 * G) * 2));
+            float mk[4][8];
+            float ss = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float e0 = 0.f, e1 = 0.f;
+#pragma unroll
+                    for (int r = 0; r < kQsaBlock; ++r) {
+                        e0 += bf16_lo(raw[r][u][j]);
+                        e1 += bf16_hi(raw[r][u][j]);
+                    }
+                    mk[u][2 * j] = 0.25f * e0;
+                    mk[u][2 * j + 1] = 0.25f * e1;
+                    ss = fmaf(mk[u][2 * j], mk[u][2 * j], ss);
+                    ss = fmaf(mk[u][2 * j + 1], mk[u][2 * j + 1], ss);
+                }
+            ss = rows4_sum(ss);                              // the block's 128 dims
+            const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+            const double pos = (double)kQsaBlock * (k_begin + 16 * g + n);
+            u32x4 ahi[4], alo[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    float xe = mk[u][2 * p] * inv, xo = mk[u][2 * p + 1] * inv;
+                    const int i = 16 * u + 4 * G + p;        // pair (2i, 2i+1)
+                    if (i < rope.half) {
+                        float c, sn;
+                        rope_cos_sin(rope, pos, i, c, sn);
+                        const float ye = xe * c - xo * sn, yo = xe * sn + xo * c;
+                        xe = ye;
+                        xo = yo;
+                    }
+                    const uint32_t he = f32_to_bf16_bits(xe), ho = f32_to_bf16_bits(xo);
+                    ahi[u][p] = he | (ho << 16);
+                    alo[u][p] = pack_bf16x2(xe - __uint_as_float(he << 16), xo - __uint_as_float(ho << 16));
+                }
+            float t[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int hb = 0; hb < NHB; ++hb) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    acc = mfma16(ahi[u], qf[hb][u], acc);
+                    acc = mfma16(alo[u], qf[hb][u], acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t[i] += fmaxf(acc[i], 0.0f);   // blocks 4 G + i, head 16 hb + n
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t[i] = row16_sum(t[i]);
+            const float v = n == 0 ? t[0] : n == 1 ? t[1] : n == 2 ? t[2] : t[3];
+            const uint32_t key = order_key(v);
+            const int row = 16 * g + 4 * G + n;
+            __builtin_amdgcn_raw_buffer_store_b32(key, sr, n < 4 ? (uint32_t)row * 4u : 0x80000000u, 0, 0);
+            const uint32_t bin = key >> 20;
+            if (n < 4 && row < nbl && bin) atomicAdd(&lh[bin], 1u);
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < kHistBins; i += 256)
+        if (lh[i]) atomicAdd(&hist[(size_t)b * kHistBins + i], lh[i]);
+}
+
+// complete blocks per batch row (the radix select's "lengths")
+__global__ void qsa_block_counts_kernel(const int32_t* __restrict__ seq_lens, int S_max, int B,
+                                        int32_t* __restrict__ cnt) {
+    const int b = blockIdx.x * 64 + threadIdx.x;
+    if (b < B) cnt[b] = min(max(seq_lens[b], 1), S_max) / kQsaBlock;
+}
+
+// tokens of the selected blocks (ascending, as the blocks are), then the
+// tail; -1 after.  With no complete block only the tail is taken.
+__global__ __launch_bounds__(256) void qsa_expand_kernel(const int32_t* __restrict__ blk,
+                                                         const int32_t* __restrict__ seq_lens,
+                                                         int S_max, int32_t* __restrict__ tok) {
+    const int b = blockIdx.x;
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int nb = L / kQsaBlock;
+    const int c = min(kQsaTopBlocks, nb);
+    const int tail = L - kQsaBlock * nb;
+    for (int i = threadIdx.x; i < kQsaTokens; i += 256) {
+        int v = -1;
+        if (i < kQsaBlock * c) v = kQsaBlock * blk[(size_t)b * kQsaTopBlocks + i / kQsaBlock] + (i & 3);
+        else if (i < kQsaBlock * c + tail) v = kQsaBlock * nb + (i - kQsaBlock * c);
+        tok[(size_t)b * kQsaTokens + i] = v;
+    }
+}
+
+__device__ __forceinline__ int qsa_n_tokens(int L) {
+    const int nb = L / kQsaBlock;
+    return kQsaBlock * min(kQsaTopBlocks, nb) + (L - kQsaBlock * nb);
+}
+
+// One sub-chunk of 32 gathered rows (K in kb, V in vb, rows at kGRowStride):
+// S^T = K.Q^T over 128 dims, lazy online softmax (probabilities < 2^8),
+// O^T += V^T.P^T.  Rows p0 + 16 th + 4 G + i >= c1 are masked.
+__device__ __forceinline__ void gqa_gather_step(const uint8_t* kb, const uint8_t* vb,
+                                                const u32x4 (&qf)[4], f32x4 (&o)[8], float& m_run,
+                                                float& l_run, int p0, int c1, float qscale, int G,
+                                                int n) {
+    f32x4 sc[2];
+#pragma unroll
+    for (int th = 0; th < 2; ++th) {
+        sc[th] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint8_t* kr = kb + (16 * th + n) * kGRowStride + 16 * G;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sc[th] = mfma16(*reinterpret_cast<const u32x4*>(kr + 64 * u), qf[u], sc[th]);
+    }
+#pragma unroll
+    for (int th = 0; th < 2; ++th)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sc[th][i] *= qscale;
+            if (p0 + 16 * th + 4 * G + i >= c1) sc[th][i] = -INFINITY;
+        }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = rows4_max(mx);                    // finite: row p0 < c1 is visible
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[t] *= alpha;
+        m_run = m_new;
+    }
+    float pr[2][4];
+    float ls = 0.f;
+#pragma unroll
+    for (int th = 0; th < 2; ++th)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pr[th][i] = fast_exp2(sc[th][i] - m_run);
+            ls += pr[th][i];
+        }
+    l_run += rows4_sum(ls);
+    u32x4 pb;
+    pb[0] = pack_bf16x2(pr[0][0], pr[0][1]);
+    pb[1] = pack_bf16x2(pr[0][2], pr[0][3]);
+    pb[2] = pack_bf16x2(pr[1][0], pr[1][1]);
+    pb[3] = pack_bf16x2(pr[1][2], pr[1][3]);
+    u32x4 vr[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        vr[r] = *reinterpret_cast<const u32x4*>(vb + slot_row(G, r) * kGRowStride + 16 * n);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[t] = mfma16(column_of(vr, t), pb, o[t]);
+}
+
+// grid (chunks of 128 selected tokens, Hkv, B), one wave: the kv head's g
+// query heads (g <= 16).  All four sub-chunks' K and V rows are requested at
+// once (one gather latency per workgroup).
+__global__ __launch_bounds__(64) void gqa_gather_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ tok,
+    const int32_t* __restrict__ seq_lens, int Hq, int Hkv, int S_max, float qscale,
+    float* __restrict__ part_o, float* __restrict__ part_ml, int n_chunks) {
+    __shared__ __attribute__((aligned(16))) uint8_t k0[kGBufBytes], k1[kGBufBytes], k2[kGBufBytes], k3[kGBufBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t v0[kGBufBytes], v1[kGBufBytes], v2[kGBufBytes], v3[kGBufBytes];
+    __shared__ int32_t sel_s[kGChunk];
+    const int lane = threadIdx.x;
+    const int G = lane >> 4, n = lane & 15;
+    const int chunk = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+    const int g = Hq / Hkv;
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int n_tok = qsa_n_tokens(L);
+    const int c0 = chunk * kGChunk;
+    if (c0 >= n_tok) return;                       // whole workgroup
+    const int c1 = min(c0 + kGChunk, n_tok);
+    const int nsub = (c1 - c0 + kGSub - 1) / kGSub;
+
+    u32x4 qf[4];
+    const bool head = n < g;
+    const uint16_t* qrow = q + ((size_t)b * Hq + (size_t)kv * g + (head ? n : 0)) * kGD + 8 * G;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u);
+    for (int i = lane; i < kGChunk; i += 64)
+        sel_s[i] = c0 + i < c1 ? tok[(size_t)b * kQsaTokens + c0 + i] : -1;
+    __syncthreads();
+
+    const size_t slice = ((size_t)b * Hkv + kv) * S_max * kGD;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(k_cache + slice, (uint32_t)S_max * kGD * 2u);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_cache + slice, (uint32_t)S_max * kGD * 2u);
+    // copy j of a sub-chunk fills LDS bytes [1024 j, +1024): lane l the 16
+    // bytes at x = 1024 j + 16 l, row x / kGRowStride, column x mod it
+    auto copy_sub = [&](int s, uint8_t* kd, uint8_t* vd) {
+#pragma unroll
+        for (int j = 0; j < kGSubCopies; ++j) {
+            const int x = 1024 * j + 16 * lane;
+            const int rr = x / kGRowStride, cc = x - rr * kGRowStride;
+            const int row = sel_s[kGSub * s + min(rr, kGSub - 1)];
+            const bool ok = rr < kGSub && cc < kGD * 2 && row >= 0;
+            const uint32_t voff = ok ? (uint32_t)row * (kGD * 2) + (uint32_t)cc : 0x80000000u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kd + 1024 * j, 16, voff, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vd + 1024 * j, 16, voff, 0, 0, 0);
+        }
+    };
+    // q is complete before the copies are issued (the compiler's wait counts
+    // do not include loads into LDS)
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_sub(0, k0, v0);
+    copy_sub(1, k1, v1);
+    copy_sub(2, k2, v2);
+    copy_sub(3, k3, v3);
+
+    f32x4 o[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    // sub-chunk s is complete once at most the copies of the later ones are
+    // outstanding (2 kGSubCopies per sub-chunk, in issue order)
+    constexpr int kPer = 2 * kGSubCopies;
+    static_assert(3 * kPer < 64, "vmcnt range");
+    auto wait_sub = [&](auto later) {
+        constexpr int v = decltype(later)::value;
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (v & 15) | ((v >> 4) << 14));
+        asm volatile("s_barrier" ::: "memory");
+    };
+    wait_sub(std::integral_constant<int, 3 * kPer>{});
+    gqa_gather_step(k0, v0, qf, o, m_run, l_run, c0, c1, qscale, G, n);
+    if (nsub > 1) {
+        wait_sub(std::integral_constant<int, 2 * kPer>{});
+        gqa_gather_step(k1, v1, qf, o, m_run, l_run, c0 + kGSub, c1, qscale, G, n);
+    }
+    if (nsub > 2) {
+        wait_sub(std::integral_constant<int, kPer>{});
+        gqa_gather_step(k2, v2, qf, o, m_run, l_run, c0 + 2 * kGSub, c1, qscale, G, n);
+    }
+    if (nsub > 3) {
+        wait_sub(std::integral_constant<int, 0>{});
+        gqa_gather_step(k3, v3, qf, o, m_run, l_run, c0 + 3 * kGSub, c1, qscale, G, n);
+    }
+    __builtin_amdgcn_s_waitcnt(0);                 // copies of unused sub-chunks
+    if (!head) return;
+    const size_t idx = ((size_t)b * Hq + (size_t)kv * g + n) * n_chunks + chunk;
+    float* po = part_o + idx * kGD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int d0 = 8 * (4 * G + i);            // this lane holds d = d0 + t for head n
+        *reinterpret_cast<f32x4*>(po + d0) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
+        *reinterpret_cast<f32x4*>(po + d0 + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
+    }
+    if (G == 0) {
+        part_ml[idx * 2] = m_run;
+        part_ml[idx * 2 + 1] = l_run;
+    }
+}
+
+// one wave per (batch, head): the chunks' partials merged (log-sum-exp),
+// lane l holds dims 2 l and 2 l + 1
+__global__ __launch_bounds__(256) void qsa_combine_kernel(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_ml,
+                                                          const int32_t* __restrict__ seq_lens, int Hq,
+                                                          int S_max, int n_chunks, int BH,
+                                                          uint16_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int idx = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    if (idx >= BH) return;
+    const int b = idx / Hq;
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int nc = (qsa_n_tokens(L) + kGChunk - 1) / kGChunk;
+    const float* ml = part_ml + (size_t)idx * n_chunks * 2;
+    float M = -INFINITY;
+    for (int c = 0; c < nc; ++c) M = fmaxf(M, ml[2 * c]);
+    float den = 0.f, a0 = 0.f, a1 = 0.f;
+    for (int c = 0; c < nc; ++c) {
+        const float w = fast_exp2(ml[2 * c] - M);
+        den += w * ml[2 * c + 1];
+        const float* po = part_o + ((size_t)idx * n_chunks + c) * kGD + 2 * lane;
+        a0 += w * po[0];
+        a1 += w * po[1];
+    }
+    const float inv = 1.0f / den;
+    *reinterpret_cast<uint32_t*>(out + (size_t)idx * kGD + 2 * lane) = pack_bf16x2(a0 * inv, a1 * inv);
+}
+
 }  // namespace
 
 SparseLayout sparse_layout(int32_t B, int32_t H, int32_t S_max, int32_t top_k) {
@@ -1183,6 +1532,97 @@ SparseLayout sparse_layout(int32_t B, int32_t H, int32_t S_max, int32_t top_k) {
     l.total = l.scores_bytes + l.hist_bytes + l.cand_bytes + l.info_bytes + l.counts_bytes +
               l.o_bytes + l.ml_bytes;
     return l;
+}
+
+QsaLayout qsa_layout(int32_t B, int32_t Hq, int32_t S_max) {
+    QsaLayout l{};
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    l.n_blk_max = std::max(S_max / kQsaBlock, 1);
+    l.sel = sparse_layout(B, 0, l.n_blk_max, kQsaTopBlocks);
+    l.cnt_bytes = al((size_t)B * sizeof(int32_t));
+    l.blk_bytes = al((size_t)B * kQsaTopBlocks * sizeof(int32_t));
+    l.n_chunks = (kQsaTokens + kGChunk - 1) / kGChunk;
+    l.o_bytes = al((size_t)B * Hq * l.n_chunks * kGD * sizeof(float));
+    l.ml_bytes = al((size_t)B * Hq * l.n_chunks * 2 * sizeof(float));
+    l.total = l.sel.total + l.cnt_bytes + l.blk_bytes + l.o_bytes + l.ml_bytes;
+    return l;
+}
+
+hipError_t launch_qsa_sparse_decode(const void* q, const void* k_cache, const void* v_cache,
+                                    const void* q_index, const void* k_index,
+                                    const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                    int32_t H_I, int32_t S_max, float scale, const RopeDev& rope,
+                                    int32_t* tok, void* out, void* workspace, const QsaLayout& lay,
+                                    hipStream_t s) {
+    char* w = reinterpret_cast<char*>(workspace);
+    const SparseLayout& sl = lay.sel;
+    uint32_t* keys = reinterpret_cast<uint32_t*>(w);
+    float* scores = reinterpret_cast<float*>(w);
+    w += sl.scores_bytes;
+    uint32_t* hist = reinterpret_cast<uint32_t*>(w);
+    w += sl.hist_bytes;
+    uint32_t* cand = reinterpret_cast<uint32_t*>(w);
+    uint32_t* cand_cnt = cand + (size_t)B * sl.n_key_chunks * kChunkKeys;
+    uint32_t* cand_above = cand_cnt + (size_t)B * sl.n_key_chunks;
+    w += sl.cand_bytes;
+    SelInfo* info = reinterpret_cast<SelInfo*>(w);
+    w += sl.info_bytes;
+    uint32_t* counts = reinterpret_cast<uint32_t*>(w);
+    w += sl.counts_bytes;
+    w += sl.o_bytes + sl.ml_bytes;   // (empty)
+    int32_t* cnt = reinterpret_cast<int32_t*>(w);
+    w += lay.cnt_bytes;
+    int32_t* blk = reinterpret_cast<int32_t*>(w);
+    w += lay.blk_bytes;
+    float* po = reinterpret_cast<float*>(w);
+    w += lay.o_bytes;
+    float* pml = reinterpret_cast<float*>(w);
+    const int NB = lay.n_blk_max;
+    const int KS = (NB + 3) & ~3;
+    const int nkc = sl.n_key_chunks;
+
+    const int nz = B * kHistBins;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((nz + 255) / 256), dim3(256), 0, s, hist, nz);
+    hipLaunchKernelGGL(qsa_block_counts_kernel, dim3((B + 63) / 64), dim3(64), 0, s, seq_lens, S_max,
+                       B, cnt);
+    const int bpw = 256;   // blocks (1024 keys) per workgroup
+    const dim3 igrid((NB + bpw - 1) / bpw, B);
+    const uint16_t* qi = (const uint16_t*)q_index;
+    const uint16_t* ki = (const uint16_t*)k_index;
+    switch (H_I) {
+        case 16:
+            hipLaunchKernelGGL((qsa_block_kernel<1>), igrid, dim3(256), 0, s, qi, ki, seq_lens, S_max, KS,
+                               bpw, rope, keys, hist);
+            break;
+        case 32:
+            hipLaunchKernelGGL((qsa_block_kernel<2>), igrid, dim3(256), 0, s, qi, ki, seq_lens, S_max, KS,
+                               bpw, rope, keys, hist);
+            break;
+        case 48:
+            hipLaunchKernelGGL((qsa_block_kernel<3>), igrid, dim3(256), 0, s, qi, ki, seq_lens, S_max, KS,
+                               bpw, rope, keys, hist);
+            break;
+        case 64:
+            hipLaunchKernelGGL((qsa_block_kernel<4>), igrid, dim3(256), 0, s, qi, ki, seq_lens, S_max, KS,
+                               bpw, rope, keys, hist);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL(topk_candidates_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, hist,
+                       cnt, NB, KS, kQsaTopBlocks, cand, cand_cnt, cand_above, nkc, info);
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, cnt, NB, KS,
+                       kQsaTopBlocks, cand, cand_cnt, cand_above, nkc, info, counts);
+    hipLaunchKernelGGL(topk_write_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, cnt, NB, KS,
+                       kQsaTopBlocks, info, counts, nkc, blk);
+    hipLaunchKernelGGL(qsa_expand_kernel, dim3(B), dim3(256), 0, s, blk, seq_lens, S_max, tok);
+    hipLaunchKernelGGL(gqa_gather_attn_kernel, dim3(lay.n_chunks, Hkv, B), dim3(64), 0, s,
+                       (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, tok,
+                       seq_lens, Hq, Hkv, S_max, scale * kLog2e, po, pml, lay.n_chunks);
+    const int BH = B * Hq;
+    hipLaunchKernelGGL(qsa_combine_kernel, dim3((BH + 3) / 4), dim3(256), 0, s, po, pml, seq_lens, Hq,
+                       S_max, lay.n_chunks, BH, (uint16_t*)out);
+    return hipGetLastError();
 }
 
 MlaLayout mla_layout(int32_t B, int32_t H, int32_t S_max) {

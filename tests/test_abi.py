@@ -209,6 +209,30 @@ def test_sparse_weighted_validation(m):
     assert call(wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
 
 
+def test_qsa_validation(m):
+    lib = m.lib()
+    need = m.qsa_sparse_decode_workspace_size(2, 32, 4096)
+    assert need > 0
+
+    def call(Hq=32, Hkv=4, D=128, HI=64, Di=128, S=4096, scale=0.08, rope=None, wsn=need, tok=P):
+        return lib.qsa_sparse_decode(P, P, P, P, P, P, 2, Hq, Hkv, D, HI, Di, S, scale, rope, tok, P,
+                                     P, wsn, None)
+
+    assert call(Hq=30) == m.ERR_INVALID_ARGUMENT
+    assert call(D=64) == m.ERR_UNSUPPORTED
+    assert call(Di=64) == m.ERR_UNSUPPORTED
+    assert call(Hq=64, Hkv=2) == m.ERR_UNSUPPORTED     # g = 32 > 16
+    assert call(HI=24) == m.ERR_UNSUPPORTED
+    assert call(HI=0) == m.ERR_INVALID_ARGUMENT
+    assert call(scale=float("nan")) == m.ERR_INVALID_ARGUMENT
+    assert call(tok=MIS) == m.ERR_INVALID_ARGUMENT
+    assert call(wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+    dyn = _rope(m, scaling=m.ROPE_DYNAMIC_NTK, base=1e4, original_max_position=100)
+    assert call(rope=dyn) == m.ERR_UNSUPPORTED
+    bad = _rope(m, scaling=m.ROPE_PLAIN, base=0.5)
+    assert call(rope=bad) == m.ERR_INVALID_ARGUMENT
+
+
 def test_mla_validation(m):
     lib = m.lib()
 

@@ -174,6 +174,31 @@ class SparseConfig:
         return np.full(self.B, self.S_max, dtype=np.int32)
 
 
+@dataclasses.dataclass(frozen=True)
+class QsaConfig:
+    """QSA decode: GQA attention over the tokens of the top 512 micro-blocks."""
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    S_max: int
+    H_I: int
+    D_idx: int
+    seed: int
+    base: float = 1.0e4
+    rotary_dim: int = 64      # block-key RoPE on the first 64 indexer dims
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def block_rope(self) -> dict:
+        return rope_settings(ROPE_PLAIN, base=self.base, rotary_dim=self.rotary_dim)
+
+    def seq_lens(self) -> np.ndarray:
+        return np.full(self.B, self.S_max, dtype=np.int32)
+
+
 TINY = TinyConfig()
 DECODE_4K = DecodeConfig(B=16, Hq=64, Hkv=8, D=128, S_max=4096, seed=1,
                          rope_kind="plain", base=500000.0)
@@ -183,6 +208,7 @@ PREFILL_8K = PrefillConfig(B=1, T=8192, Hq=32, Hkv=8, D=128, seed=3, base=1.0e6,
                            ntk_factor=4.0)
 SPARSE_128K = SparseConfig(B=4, H=128, S_max=131072, Dqk=576, Dv=512, D_idx=128,
                            top_k=2048, seed=4)
+QSA_128K = QsaConfig(B=4, Hq=32, Hkv=4, D=128, S_max=131072, H_I=64, D_idx=128, seed=5)
 
 
 # ---------------------------------------------------------------------------
