@@ -19,8 +19,9 @@ cites the passage it follows.  The pages are cited by title:
 Pinned by ``tests/test_oracle_*.py`` against closed forms, printed values
 (``tests/golden/``), invariants and an independent library routine.  The only
 parts without an external pin ("parity unpinned") are the shape of the YaRN
-middle band (the pages say "linear transition" without a formula) and the
-particular numerical values of the synthetic outputs, which only this oracle
-defines.
+middle band (the pages say "linear transition" without a formula), QSA's
+block-key normalisation (read as L2 to unit length; the page only says
+"normalise") and the particular numerical values of the synthetic outputs,
+which only this oracle defines.
 """
 from . import rope, attention, sparse, qsa, kv_bytes  # noqa: F401
