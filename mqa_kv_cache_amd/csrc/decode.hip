@@ -316,9 +316,9 @@ __device__ __forceinline__ void prep_q(const u32x4 (&raw)[NB][D / 32], const QFr
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float a = x[2 * j] * qscale, c2 = x[2 * j + 1] * qscale;
-                const uint32_t ha = f32_to_bf16_bits(a), hc = f32_to_bf16_bits(c2);
-                qhi[nb][u][j] = ha | (hc << 16);
-                qlo[nb][u][j] = pack_bf16x2(a - __uint_as_float(ha << 16), c2 - __uint_as_float(hc << 16));
+                const u32x2 hl = split_bf16x2(a, c2);
+                qhi[nb][u][j] = hl[0];
+                qlo[nb][u][j] = hl[1];
             }
         }
 }
@@ -371,7 +371,7 @@ __device__ __forceinline__ void rotate_new_key(NewRow<D>& nr, int L, const QFreq
                 xe = ye;
                 xo = yo;
             }
-            w[p] = f32_to_bf16_bits(xe) | (f32_to_bf16_bits(xo) << 16);
+            w[p] = pack_bf16x2(xe, xo);
         }
         nr.k[u] = w;
     }

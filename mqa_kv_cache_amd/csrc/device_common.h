@@ -12,6 +12,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32
@@ -19,15 +21,19 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN): the conversion
+// is gfx950's v_cvt_pk_bf16_f32, one instruction per pair of values.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// a and b each as hi + lo bf16 terms: hi = bf16(x), lo = bf16(x - hi)
+// (x to about 2^-17 relative), packed in pairs: {hi pair, lo pair}.
+__device__ __forceinline__ u32x2 split_bf16x2(float a, float b) {
+    const uint32_t hi = pack_bf16x2(a, b);
+    return u32x2{hi, pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u))};
 }
 
 // ---------------------------------------------------------------------------
@@ -72,18 +78,24 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // RoPE cos/sin of pair i at position pos: angle formed in fp64, reduced to
 // [-pi, pi] in fp64, then an fp32 sincos; both scaled by the amplitude.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void rope_cos_sin(const RopeDev& r, double pos, int i, float& c, float& s) {
+__device__ __forceinline__ void cos_sin_fp64_angle(double a, float& c, float& s) {
     const double two_pi_hi = 6.283185307179586232;
     const double two_pi_lo = 2.4492935982947064e-16;
-    double a = pos * r.pos_scale * r.theta[i];
     double k = rint(a * 0.15915494309189535);
     double red = fma(-k, two_pi_hi, a);
     red = fma(-k, two_pi_lo, red);
-    float x = (float)red;
+    sincosf((float)red, &s, &c);
+}
+__device__ __forceinline__ void rope_cos_sin_theta(const RopeDev& r, double pos, double theta, float& c,
+                                                   float& s) {
     float sv, cv;
-    sincosf(x, &sv, &cv);
+    cos_sin_fp64_angle(pos * r.pos_scale * theta, cv, sv);
     c = cv * r.amp;
     s = sv * r.amp;
+}
+
+__device__ __forceinline__ void rope_cos_sin(const RopeDev& r, double pos, int i, float& c, float& s) {
+    rope_cos_sin_theta(r, pos, r.theta[i], c, s);
 }
 
 // Row (within a 32-row tile) that k-slot r of lane group G stands for.  It is

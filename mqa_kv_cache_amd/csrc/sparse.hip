@@ -953,9 +953,9 @@ __device__ __forceinline__ void dense_pv(const uint8_t* rows, const f32x4 (&sc)[
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const float a = pr[k >> 1][2 * (k & 1)], c = pr[k >> 1][2 * (k & 1) + 1];
-        const uint32_t ha = f32_to_bf16_bits(a), hc = f32_to_bf16_bits(c);
-        ph[k] = ha | (hc << 16);
-        pl[k] = pack_bf16x2(a - __uint_as_float(ha << 16), c - __uint_as_float(hc << 16));
+        const u32x2 hl = split_bf16x2(a, c);
+        ph[k] = hl[0];
+        pl[k] = hl[1];
     }
     const uint8_t* v0 = rows + (4 * G + (n >> 2)) * kRowStride + 8 * (n & 1) + 128 * ((n >> 1) & 1);
     const uint8_t* v1 = v0 + 16 * kRowStride;
@@ -1174,9 +1174,11 @@ constexpr int kMlaMinRows = 256;
 //                       query heads; ReLU per head, summed; order keys and
 //                       the first-digit histogram as for the token indexer
 //    (the radix select of section 2 then takes the top 512 blocks)
-//    qsa_expand_kernel  blocks -> their 4 tokens, then the 0-3 tail tokens
 //    gqa_gather_attn_kernel  per (128 selected tokens, kv head, batch row):
-//                       the tokens' K and V rows gathered into LDS, the
+//                       the tokens expanded from the selected blocks (their
+//                       4 tokens each, then the 0-3 tail tokens; the kv head
+//                       0 workgroups write the list out), the tokens' K and
+//                       V rows gathered into LDS, the
 //                       decode MFMA scheme over D = 128 for the group's
 //                       g <= 16 query heads, a partial (m, l, o) per head
 //    qsa_combine_kernel the partials merged per (batch, head)
@@ -1192,136 +1194,167 @@ constexpr int kGSubBytes = kGSub * kGRowStride;                  // 8704
 constexpr int kGSubCopies = (kGSubBytes + 1023) / 1024;          // 9 copies of 1 KB
 constexpr int kGBufBytes = kGSubCopies * 1024;
 
+constexpr int kQsaBlocksPerWg = 256;          // 16 groups of 16 blocks (1024 keys)
+
 template <int NHB>
 __global__ __launch_bounds__(256) void qsa_block_kernel(
     const uint16_t* __restrict__ q_index, const uint16_t* __restrict__ k_index,
-    const int32_t* __restrict__ seq_lens, int S_max, int KS, int blocks_per_wg, RopeDev rope,
+    const int32_t* __restrict__ seq_lens, int S_max, int KS, RopeDev rope,
     uint32_t* __restrict__ keys, uint32_t* __restrict__ hist) {
     constexpr int HI = 16 * NHB;
     __shared__ uint32_t lh[kHistBins];
+    // The rotation of block 16 g + n of the workgroup (position
+    // 4 k_begin + 64 g + 4 n) is the product of two table entries:
+    // ta[g][i] at 4 k_begin + 64 g (amplitude included) and tb[n][i] at 4 n,
+    // each from an fp64-reduced angle (the product adds ~2 fp32 roundings).
+    __shared__ f32x2 ta[16][kDidx / 2], tb[16][kDidx / 2];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = lane >> 4, n = lane & 15;
     const int b = blockIdx.y;
     const int L = min(max(seq_lens[b], 1), S_max);
     const int nb = L / kQsaBlock;                            // complete blocks
-    const int k_begin = blockIdx.x * blocks_per_wg;
-    const int k_end = min(k_begin + blocks_per_wg, nb);
+    const int k_begin = blockIdx.x * kQsaBlocksPerWg;
+    const int k_end = min(k_begin + kQsaBlocksPerWg, nb);
+    if (k_begin >= k_end) return;                            // whole workgroup
+    // requests first (theta, the query heads, this wave's first group of
+    // keys), then the tables while they are in flight
+    static_assert(kDidx / 2 == 64, "one rotary pair per lane");
+    const double th_lane = rope.theta[lane];                 // rope.half <= kDidx / 2
+    u32x4 qf[NHB][4];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+        const uint16_t* qrow = q_index + ((size_t)b * HI + 16 * hb + n) * kDidx + 8 * G;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) qf[hb][u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u);
+    }
+    const int nbl = k_end - k_begin;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(
+        k_index + ((size_t)b * S_max + (size_t)kQsaBlock * k_begin) * kDidx,
+        (uint32_t)nbl * kQsaBlock * kDidx * 2u);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(keys + (size_t)b * KS + k_begin, (uint32_t)nbl * 4u);
+    const int n_groups = (nbl + 15) / 16;
+    const int n_steps = (n_groups + 3) / 4;                  // uniform over the workgroup
+    // lane (G, n): block 16 g + n, dims 32 u + 8 G .. +7 of its 4 keys.
+    // The next group's keys are requested before this group's arithmetic
+    // (groups past the range read zeros through the resource bound).
+    u32x4 raw[kQsaBlock][4];
+    auto load_group = [&](int g, u32x4 (&dst)[kQsaBlock][4]) {
+#pragma unroll
+        for (int r = 0; r < kQsaBlock; ++r)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                dst[r][u] = buf_load16_nt(
+                    kr, (uint32_t)((((16 * g + n) * kQsaBlock + r) * kDidx + 32 * u + 8 * G) * 2));
+    };
+    load_group(wave, raw);
     for (int i = tid; i < kHistBins; i += 256) lh[i] = 0u;
+    if (lane < rope.half) {
+        // thread (wave, lane): pair i = lane, table rows wave + 4 t
+        const double th = th_lane * rope.pos_scale;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int r = wave + 4 * t;
+            float c, sn;
+            if (r < 16) {
+                cos_sin_fp64_angle(th * (4.0 * k_begin + 64.0 * r), c, sn);
+                ta[r][lane] = f32x2{c * rope.amp, sn * rope.amp};
+            } else {
+                cos_sin_fp64_angle(th * (4.0 * (r - 16)), c, sn);
+                tb[r - 16][lane] = f32x2{c, sn};
+            }
+        }
+    }
     __syncthreads();
-    if (k_begin < k_end) {
-        u32x4 qf[NHB][4];
+    for (int st = 0; st < n_steps; ++st) {
+        const int g = 4 * st + wave;                     // 16-block group of this wave
+        u32x4 nxt[kQsaBlock][4];
+        load_group(g + 4, nxt);
+        float mk[4][8];
+        float ss = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float e0 = 0.f, e1 = 0.f;
+#pragma unroll
+                for (int r = 0; r < kQsaBlock; ++r) {
+                    e0 += bf16_lo(raw[r][u][j]);
+                    e1 += bf16_hi(raw[r][u][j]);
+                }
+                mk[u][2 * j] = 0.25f * e0;
+                mk[u][2 * j + 1] = 0.25f * e1;
+                ss = fmaf(mk[u][2 * j], mk[u][2 * j], ss);
+                ss = fmaf(mk[u][2 * j + 1], mk[u][2 * j + 1], ss);
+            }
+        ss = rows4_sum(ss);                              // the block's 128 dims
+        const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+        u32x4 ahi[4], alo[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                float xe = mk[u][2 * p] * inv, xo = mk[u][2 * p + 1] * inv;
+                const int i = 16 * u + 4 * G + p;        // pair (2i, 2i+1)
+                if (i < rope.half) {
+                    const f32x2 a = ta[g][i], bt = tb[n][i];
+                    const float c = a.x * bt.x - a.y * bt.y, sn = a.x * bt.y + a.y * bt.x;
+                    const float ye = xe * c - xo * sn, yo = xe * sn + xo * c;
+                    xe = ye;
+                    xo = yo;
+                }
+                const u32x2 hl = split_bf16x2(xe, xo);
+                ahi[u][p] = hl[0];
+                alo[u][p] = hl[1];
+            }
+        float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
-            const uint16_t* qrow = q_index + ((size_t)b * HI + 16 * hb + n) * kDidx + 8 * G;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < 4; ++u) qf[hb][u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u);
-        }
-        const int nbl = k_end - k_begin;
-        const __amdgpu_buffer_rsrc_t kr = make_rsrc(
-            k_index + ((size_t)b * S_max + (size_t)kQsaBlock * k_begin) * kDidx,
-            (uint32_t)nbl * kQsaBlock * kDidx * 2u);
-        const __amdgpu_buffer_rsrc_t sr = make_rsrc(keys + (size_t)b * KS + k_begin, (uint32_t)nbl * 4u);
-        const int n_groups = (nbl + 15) / 16;
-        const int n_steps = (n_groups + 3) / 4;              // uniform over the workgroup
-        for (int st = 0; st < n_steps; ++st) {
-            const int g = 4 * st + wave;                     // 16-block group of this wave
-            // lane (G, n): block 16 g + n, dims 32 u + 8 G .. +7 of its 4 keys
-            u32x4 raw[kQsaBlock][4];
-#pragma unroll
-            for (int r = 0; r < kQsaBlock; ++r)
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    raw[r][u] = buf_load16_nt(
-                        kr, (uint32_t)((((16 * g + n) * kQsaBlock + r) * kDidx + 32 * u + 8 * G) * 2));
-            float mk[4][8];
-            float ss = 0.f;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float e0 = 0.f, e1 = 0.f;
-#pragma unroll
-                    for (int r = 0; r < kQsaBlock; ++r) {
-                        e0 += bf16_lo(raw[r][u][j]);
-                        e1 += bf16_hi(raw[r][u][j]);
-                    }
-                    mk[u][2 * j] = 0.25f * e0;
-                    mk[u][2 * j + 1] = 0.25f * e1;
-                    ss = fmaf(mk[u][2 * j], mk[u][2 * j], ss);
-                    ss = fmaf(mk[u][2 * j + 1], mk[u][2 * j + 1], ss);
-                }
-            ss = rows4_sum(ss);                              // the block's 128 dims
-            const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
-            const double pos = (double)kQsaBlock * (k_begin + 16 * g + n);
-            u32x4 ahi[4], alo[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    float xe = mk[u][2 * p] * inv, xo = mk[u][2 * p + 1] * inv;
-                    const int i = 16 * u + 4 * G + p;        // pair (2i, 2i+1)
-                    if (i < rope.half) {
-                        float c, sn;
-                        rope_cos_sin(rope, pos, i, c, sn);
-                        const float ye = xe * c - xo * sn, yo = xe * sn + xo * c;
-                        xe = ye;
-                        xo = yo;
-                    }
-                    const uint32_t he = f32_to_bf16_bits(xe), ho = f32_to_bf16_bits(xo);
-                    ahi[u][p] = he | (ho << 16);
-                    alo[u][p] = pack_bf16x2(xe - __uint_as_float(he << 16), xo - __uint_as_float(ho << 16));
-                }
-            float t[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int hb = 0; hb < NHB; ++hb) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    acc = mfma16(ahi[u], qf[hb][u], acc);
-                    acc = mfma16(alo[u], qf[hb][u], acc);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) t[i] += fmaxf(acc[i], 0.0f);   // blocks 4 G + i, head 16 hb + n
+            for (int u = 0; u < 4; ++u) {
+                acc = mfma16(ahi[u], qf[hb][u], acc);
+                acc = mfma16(alo[u], qf[hb][u], acc);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) t[i] = row16_sum(t[i]);
-            const float v = n == 0 ? t[0] : n == 1 ? t[1] : n == 2 ? t[2] : t[3];
-            const uint32_t key = order_key(v);
-            const int row = 16 * g + 4 * G + n;
-            __builtin_amdgcn_raw_buffer_store_b32(key, sr, n < 4 ? (uint32_t)row * 4u : 0x80000000u, 0, 0);
-            const uint32_t bin = key >> 20;
-            if (n < 4 && row < nbl && bin) atomicAdd(&lh[bin], 1u);
+            for (int i = 0; i < 4; ++i) t[i] += fmaxf(acc[i], 0.0f);   // blocks 4 G + i, head 16 hb + n
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = row16_sum(t[i]);
+        const float v = n == 0 ? t[0] : n == 1 ? t[1] : n == 2 ? t[2] : t[3];
+        const uint32_t key = order_key(v);
+        const int row = 16 * g + 4 * G + n;
+        __builtin_amdgcn_raw_buffer_store_b32(key, sr, n < 4 ? (uint32_t)row * 4u : 0x80000000u, 0, 0);
+        const uint32_t bin = key >> 20;
+        if (n < 4 && row < nbl && bin) atomicAdd(&lh[bin], 1u);
+#pragma unroll
+        for (int r = 0; r < kQsaBlock; ++r)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) raw[r][u] = nxt[r][u];
     }
     __syncthreads();
     for (int i = tid; i < kHistBins; i += 256)
         if (lh[i]) atomicAdd(&hist[(size_t)b * kHistBins + i], lh[i]);
 }
 
-// complete blocks per batch row (the radix select's "lengths")
-__global__ void qsa_block_counts_kernel(const int32_t* __restrict__ seq_lens, int S_max, int B,
-                                        int32_t* __restrict__ cnt) {
-    const int b = blockIdx.x * 64 + threadIdx.x;
-    if (b < B) cnt[b] = min(max(seq_lens[b], 1), S_max) / kQsaBlock;
+// the block histogram cleared (nz words) and the complete blocks per batch
+// row written (the radix select's "lengths"), in one launch
+__global__ void qsa_prep_kernel(uint32_t* __restrict__ hist, int nz, const int32_t* __restrict__ seq_lens,
+                                int S_max, int B, int32_t* __restrict__ cnt) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < nz) hist[i] = 0u;
+    if (i < B) cnt[i] = min(max(seq_lens[i], 1), S_max) / kQsaBlock;
 }
 
-// tokens of the selected blocks (ascending, as the blocks are), then the
-// tail; -1 after.  With no complete block only the tail is taken.
-__global__ __launch_bounds__(256) void qsa_expand_kernel(const int32_t* __restrict__ blk,
-                                                         const int32_t* __restrict__ seq_lens,
-                                                         int S_max, int32_t* __restrict__ tok) {
-    const int b = blockIdx.x;
-    const int L = min(max(seq_lens[b], 1), S_max);
+// Token i of a batch row's list: the tokens of the selected blocks
+// (ascending, as the blocks are), then the tail; -1 after.  With no complete
+// block only the tail is taken.
+__device__ __forceinline__ int32_t qsa_token(const int32_t* __restrict__ blk_row, int L, int i) {
     const int nb = L / kQsaBlock;
     const int c = min(kQsaTopBlocks, nb);
-    const int tail = L - kQsaBlock * nb;
-    for (int i = threadIdx.x; i < kQsaTokens; i += 256) {
-        int v = -1;
-        if (i < kQsaBlock * c) v = kQsaBlock * blk[(size_t)b * kQsaTopBlocks + i / kQsaBlock] + (i & 3);
-        else if (i < kQsaBlock * c + tail) v = kQsaBlock * nb + (i - kQsaBlock * c);
-        tok[(size_t)b * kQsaTokens + i] = v;
-    }
+    if (i < kQsaBlock * c) return kQsaBlock * blk_row[i / kQsaBlock] + (i & 3);
+    if (i < L - kQsaBlock * nb + kQsaBlock * c) return kQsaBlock * nb + (i - kQsaBlock * c);
+    return -1;
 }
 
 __device__ __forceinline__ int qsa_n_tokens(int L) {
@@ -1386,13 +1419,15 @@ __device__ __forceinline__ void gqa_gather_step(const uint8_t* kb, const uint8_t
 }
 
 // grid (chunks of 128 selected tokens, Hkv, B), one wave: the kv head's g
-// query heads (g <= 16).  All four sub-chunks' K and V rows are requested at
-// once (one gather latency per workgroup).
+// query heads (g <= 16).  The chunk's tokens are expanded from the selected
+// blocks (and written to tok by the kv head 0 workgroups, -1 padding
+// included); all four sub-chunks' K and V rows are requested at once (one
+// gather latency per workgroup).
 __global__ __launch_bounds__(64) void gqa_gather_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ tok,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ blk,
     const int32_t* __restrict__ seq_lens, int Hq, int Hkv, int S_max, float qscale,
-    float* __restrict__ part_o, float* __restrict__ part_ml, int n_chunks) {
+    int32_t* __restrict__ tok, float* __restrict__ part_o, float* __restrict__ part_ml, int n_chunks) {
     __shared__ __attribute__((aligned(16))) uint8_t k0[kGBufBytes], k1[kGBufBytes], k2[kGBufBytes], k3[kGBufBytes];
     __shared__ __attribute__((aligned(16))) uint8_t v0[kGBufBytes], v1[kGBufBytes], v2[kGBufBytes], v3[kGBufBytes];
     __shared__ int32_t sel_s[kGChunk];
@@ -1403,6 +1438,10 @@ __global__ __launch_bounds__(64) void gqa_gather_attn_kernel(
     const int L = min(max(seq_lens[b], 1), S_max);
     const int n_tok = qsa_n_tokens(L);
     const int c0 = chunk * kGChunk;
+    const int32_t* blk_row = blk + (size_t)b * kQsaTopBlocks;
+    if (kv == 0)
+        for (int i = c0 + lane; i < min(c0 + kGChunk, kQsaTokens); i += 64)
+            tok[(size_t)b * kQsaTokens + i] = qsa_token(blk_row, L, i);
     if (c0 >= n_tok) return;                       // whole workgroup
     const int c1 = min(c0 + kGChunk, n_tok);
     const int nsub = (c1 - c0 + kGSub - 1) / kGSub;
@@ -1412,8 +1451,7 @@ __global__ __launch_bounds__(64) void gqa_gather_attn_kernel(
     const uint16_t* qrow = q + ((size_t)b * Hq + (size_t)kv * g + (head ? n : 0)) * kGD + 8 * G;
 #pragma unroll
     for (int u = 0; u < 4; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u);
-    for (int i = lane; i < kGChunk; i += 64)
-        sel_s[i] = c0 + i < c1 ? tok[(size_t)b * kQsaTokens + c0 + i] : -1;
+    for (int i = lane; i < kGChunk; i += 64) sel_s[i] = c0 + i < c1 ? qsa_token(blk_row, L, c0 + i) : -1;
     __syncthreads();
 
     const size_t slice = ((size_t)b * Hkv + kv) * S_max * kGD;
@@ -1485,29 +1523,43 @@ __global__ __launch_bounds__(64) void gqa_gather_attn_kernel(
     }
 }
 
-// one wave per (batch, head): the chunks' partials merged (log-sum-exp),
-// lane l holds dims 2 l and 2 l + 1
+constexpr int kGChunks = (kQsaTokens + kGChunk - 1) / kGChunk;   // 17
+
+// one wave per (batch, head): the chunks' partials merged (log-sum-exp).
+// Lane c < nc holds chunk c's (m, l); for the output lane l holds dims 2 l
+// and 2 l + 1, and every chunk's pair is requested at once (a chunk past nc
+// re-reads the last one, with weight 0).
 __global__ __launch_bounds__(256) void qsa_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           const int32_t* __restrict__ seq_lens, int Hq,
-                                                          int S_max, int n_chunks, int BH,
-                                                          uint16_t* __restrict__ out) {
+                                                          int S_max, int BH, uint16_t* __restrict__ out) {
     const int lane = threadIdx.x & 63;
     const int idx = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     if (idx >= BH) return;
     const int b = idx / Hq;
     const int L = min(max(seq_lens[b], 1), S_max);
-    const int nc = (qsa_n_tokens(L) + kGChunk - 1) / kGChunk;
-    const float* ml = part_ml + (size_t)idx * n_chunks * 2;
-    float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, ml[2 * c]);
-    float den = 0.f, a0 = 0.f, a1 = 0.f;
-    for (int c = 0; c < nc; ++c) {
-        const float w = fast_exp2(ml[2 * c] - M);
-        den += w * ml[2 * c + 1];
-        const float* po = part_o + ((size_t)idx * n_chunks + c) * kGD + 2 * lane;
-        a0 += w * po[0];
-        a1 += w * po[1];
+    const int nc = (qsa_n_tokens(L) + kGChunk - 1) / kGChunk;   // 1 .. kGChunks
+    const float* ml = part_ml + (size_t)idx * kGChunks * 2;
+    const float* po = part_o + (size_t)idx * kGChunks * kGD + 2 * lane;
+    float2 p[kGChunks];
+#pragma unroll
+    for (int c = 0; c < kGChunks; ++c)
+        p[c] = *reinterpret_cast<const float2*>(po + (size_t)min(c, nc - 1) * kGD);
+    const float mc = lane < nc ? ml[2 * lane] : -INFINITY;
+    const float lc = lane < nc ? ml[2 * lane + 1] : 0.f;
+    float M = mc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
+    const float w = lane < nc ? fast_exp2(mc - M) : 0.f;
+    float den = w * lc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) den += __shfl_xor(den, d, 64);
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int c = 0; c < kGChunks; ++c) {
+        const float wc = __shfl(w, c, 64);
+        a0 += wc * p[c].x;
+        a1 += wc * p[c].y;
     }
     const float inv = 1.0f / den;
     *reinterpret_cast<uint32_t*>(out + (size_t)idx * kGD + 2 * lane) = pack_bf16x2(a0 * inv, a1 * inv);
@@ -1541,7 +1593,7 @@ QsaLayout qsa_layout(int32_t B, int32_t Hq, int32_t S_max) {
     l.sel = sparse_layout(B, 0, l.n_blk_max, kQsaTopBlocks);
     l.cnt_bytes = al((size_t)B * sizeof(int32_t));
     l.blk_bytes = al((size_t)B * kQsaTopBlocks * sizeof(int32_t));
-    l.n_chunks = (kQsaTokens + kGChunk - 1) / kGChunk;
+    l.n_chunks = kGChunks;
     l.o_bytes = al((size_t)B * Hq * l.n_chunks * kGD * sizeof(float));
     l.ml_bytes = al((size_t)B * Hq * l.n_chunks * 2 * sizeof(float));
     l.total = l.sel.total + l.cnt_bytes + l.blk_bytes + l.o_bytes + l.ml_bytes;
@@ -1582,29 +1634,27 @@ hipError_t launch_qsa_sparse_decode(const void* q, const void* k_cache, const vo
     const int nkc = sl.n_key_chunks;
 
     const int nz = B * kHistBins;
-    hipLaunchKernelGGL(zero_u32_kernel, dim3((nz + 255) / 256), dim3(256), 0, s, hist, nz);
-    hipLaunchKernelGGL(qsa_block_counts_kernel, dim3((B + 63) / 64), dim3(64), 0, s, seq_lens, S_max,
-                       B, cnt);
-    const int bpw = 256;   // blocks (1024 keys) per workgroup
-    const dim3 igrid((NB + bpw - 1) / bpw, B);
+    hipLaunchKernelGGL(qsa_prep_kernel, dim3((std::max(nz, (int)B) + 255) / 256), dim3(256), 0, s, hist, nz,
+                       seq_lens, S_max, B, cnt);
+    const dim3 igrid((NB + kQsaBlocksPerWg - 1) / kQsaBlocksPerWg, B);
     const uint16_t* qi = (const uint16_t*)q_index;
     const uint16_t* ki = (const uint16_t*)k_index;
     switch (H_I) {
         case 16:
             hipLaunchKernelGGL((qsa_block_kernel<1>), igrid, dim3(256), 0, s, qi, ki, seq_lens, S_max, KS,
-                               bpw, rope, keys, hist);
+                               rope, keys, hist);
             break;
         case 32:
             hipLaunchKernelGGL((qsa_block_kernel<2>), igrid, dim3(256), 0, s, qi, ki, seq_lens, S_max, KS,
-                               bpw, rope, keys, hist);
+                               rope, keys, hist);
             break;
         case 48:
             hipLaunchKernelGGL((qsa_block_kernel<3>), igrid, dim3(256), 0, s, qi, ki, seq_lens, S_max, KS,
-                               bpw, rope, keys, hist);
+                               rope, keys, hist);
             break;
         case 64:
             hipLaunchKernelGGL((qsa_block_kernel<4>), igrid, dim3(256), 0, s, qi, ki, seq_lens, S_max, KS,
-                               bpw, rope, keys, hist);
+                               rope, keys, hist);
             break;
         default:
             return hipErrorInvalidValue;
@@ -1615,13 +1665,12 @@ hipError_t launch_qsa_sparse_decode(const void* q, const void* k_cache, const vo
                        kQsaTopBlocks, cand, cand_cnt, cand_above, nkc, info, counts);
     hipLaunchKernelGGL(topk_write_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, cnt, NB, KS,
                        kQsaTopBlocks, info, counts, nkc, blk);
-    hipLaunchKernelGGL(qsa_expand_kernel, dim3(B), dim3(256), 0, s, blk, seq_lens, S_max, tok);
-    hipLaunchKernelGGL(gqa_gather_attn_kernel, dim3(lay.n_chunks, Hkv, B), dim3(64), 0, s,
-                       (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, tok,
-                       seq_lens, Hq, Hkv, S_max, scale * kLog2e, po, pml, lay.n_chunks);
+    hipLaunchKernelGGL(gqa_gather_attn_kernel, dim3(kGChunks, Hkv, B), dim3(64), 0, s,
+                       (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, blk,
+                       seq_lens, Hq, Hkv, S_max, scale * kLog2e, tok, po, pml, kGChunks);
     const int BH = B * Hq;
     hipLaunchKernelGGL(qsa_combine_kernel, dim3((BH + 3) / 4), dim3(256), 0, s, po, pml, seq_lens, Hq,
-                       S_max, lay.n_chunks, BH, (uint16_t*)out);
+                       S_max, BH, (uint16_t*)out);
     return hipGetLastError();
 }
 
