@@ -68,10 +68,10 @@ hipError_t launch_gqa_prefill(const void* q, const void* k, const void* v, int32
 struct SparseLayout {
     size_t scores_bytes;   // fp32 [B][S_max rounded up to 4]
     size_t hist_bytes;     // u32 [B][4096] first-digit histogram
-    size_t cand_bytes;     // u32 [B][key chunks][4096] threshold-bin keys per chunk, then
-                           // u32 [B][key chunks] their counts and [B][key chunks] higher-bin counts
-    size_t info_bytes;     // per-batch threshold, ties to take
-    size_t counts_bytes;   // u32 [B][key chunks][2] per-chunk counts above / equal to it
+    size_t cand_bytes;     // u32 [B][key chunks][4096] keys in bins >= the threshold bin per
+                           // chunk, u32 [B][key chunks][4096] their indices, u32 [B][key chunks]
+                           // their counts
+    size_t info_bytes;     // per-batch threshold bin and the count above it
     size_t o_bytes;        // fp32 attention partials
     size_t ml_bytes;
     size_t total;

@@ -37,7 +37,7 @@ namespace {
 constexpr int kDqk = 576, kDv = 512, kDidx = 128;
 constexpr int kHistBins = 4096;      // first digit: score bits 31..20
 constexpr int kRowsPerChunk = 128;   // selected rows per attention wave
-constexpr int kCandCap = 8192;       // LDS candidates of the threshold bin
+constexpr int kEntCap = 12288;       // LDS entries (keys in bins >= the threshold bin) per row
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Sum over each group of four lanes, every lane receiving it (DPP quad
@@ -273,27 +273,22 @@ __global__ __launch_bounds__(256) void indexer_weighted_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 2. top-k selection, spread over (chunk, batch) workgroups:
-//    topk_candidates_kernel  first digit from the histogram; keys of the
-//                            threshold bin copied to the chunk's own slice,
-//                            keys of higher bins counted per chunk
-//    topk_threshold_kernel   (first digit as the chunk-0 candidate workgroup
-//                            found it) exact k-th key T from the candidates (or from
-//                            extra passes when the bin is too large), the
-//                            number of ties to take, and per chunk the
-//                            counts of keys > T and == T (from the slices)
-//    topk_write_kernel       ordered output: chunk prefix + in-chunk ranks
-// Keys are the bit patterns of non-negative fp32 scores, so unsigned order
-// is score order.
+// 2. top-k selection (an exact radix select on 12 + 12 + 8 key bits):
+//    topk_compact_kernel  per (4096-key chunk, batch row): first digit B1
+//                         from the histogram; the keys in bins >= B1 as
+//                         ordered (key, index) entries to the chunk's slice
+//    topk_finish_kernel   per batch row: exact k-th key T from the entries
+//                         (two more digits), ties to take, and the selected
+//                         indices in ascending order
+// Keys are order-preserving bit patterns of the fp32 scores, so unsigned
+// order is score order.
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 1024;
 constexpr int kChunkThreads = 256;
 constexpr int kChunkKeys = 4096;          // keys per chunk workgroup
 
 struct SelInfo {
-    uint32_t T;        // k-th largest key
-    uint32_t need;     // keys == T to take, lowest indices first
-    uint32_t B1;       // first-digit bin of T
+    uint32_t B1;       // first-digit bin of the k-th largest key
     uint32_t above;    // keys in first-digit bins above B1
 };
 
@@ -368,256 +363,235 @@ __device__ void first_digit(const uint32_t* hist_g, int b, int L, int k, uint32_
     find_crossing<NT>(h, kHistBins, (uint32_t)k, wsum, out);
 }
 
-// Keys of the threshold bin found in chunk c go to that chunk's own slice of
-// the candidate buffer (the chunk's index range), their number to
-// cand_cnt[b][c], and the number of keys in higher bins to cand_above[b][c]:
-// no cross-workgroup atomics.  The chunk's keys are requested before the
-// histogram work so the two latencies overlap.
-constexpr int kKeysPerThread = kChunkKeys / kChunkThreads;   // 16
+// Per 4096-key chunk: the keys of the threshold bin and of the bins above it
+// (every selected key is one of them), as (key, index) entries in index
+// order, to the chunk's own slice (its index range of the entry arrays);
+// their number to ent_cnt[b][c]: no cross-workgroup atomics.  Wave w owns a
+// contiguous quarter of the chunk, its keys requested before the histogram
+// work so both latencies overlap; the order within a wave comes from
+// ballot/mbcnt.  With k = L every index is selected: the chunk writes its
+// indices straight to the output, and chunk 0 writes the -1 padding.
+constexpr int kKeysPerLane = kChunkKeys / kChunkThreads;     // 16
 
-__global__ __launch_bounds__(kChunkThreads) void topk_candidates_kernel(
+__global__ __launch_bounds__(kChunkThreads) void topk_compact_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist_g,
     const int32_t* __restrict__ seq_lens, int S_max, int S_stride, int top_k,
-    uint32_t* __restrict__ cand_g, uint32_t* __restrict__ cand_cnt,
-    uint32_t* __restrict__ cand_above, int n_chunks, SelInfo* __restrict__ info) {
+    uint32_t* __restrict__ ent_key, uint32_t* __restrict__ ent_idx, uint32_t* __restrict__ ent_cnt,
+    int n_chunks, SelInfo* __restrict__ info, int32_t* __restrict__ topk_idx) {
+    constexpr int NW = kChunkThreads / 64;
+    constexpr int span = kChunkKeys / NW;
     __shared__ uint32_t h[kHistBins];
-    __shared__ uint32_t wsum[kChunkThreads / 64];
+    __shared__ uint32_t wsum[NW];
     __shared__ uint32_t res[2];
-    __shared__ uint32_t lcount;
-    __shared__ uint32_t labove;
-    const int b = blockIdx.y, c = blockIdx.x;
-    const int L = min(max(seq_lens[b], 1), S_max);
-    const int k = min(top_k, L);
-    const int c0 = c * kChunkKeys;
-    if (k == L || c0 >= L) return;
-    const int c1 = min(c0 + kChunkKeys, L);
-    const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride);
-    uint32_t kv[kKeysPerThread];
-#pragma unroll
-    for (int it = 0; it < kKeysPerThread; ++it) {
-        const int j = c0 + it * kChunkThreads + threadIdx.x;
-        kv[it] = j < c1 ? keys[j] : 0u;
-    }
-    if (threadIdx.x == 0) {
-        lcount = 0;
-        labove = 0;
-    }
-    first_digit<kChunkThreads>(hist_g, b, L, k, h, wsum, res);
-    const uint32_t B1 = res[0];
-    if (c == 0 && threadIdx.x == 0) info[b] = SelInfo{0u, 0u, B1, res[1]};   // for the threshold kernel
-    uint32_t* cand = cand_g + (size_t)b * n_chunks * kChunkKeys + c0;
-    uint32_t above = 0;
-#pragma unroll
-    for (int it = 0; it < kKeysPerThread; ++it) {
-        const int j = c0 + it * kChunkThreads + threadIdx.x;
-        const uint32_t bin = kv[it] >> 20;
-        if (j < c1) {
-            above += bin > B1;
-            if (bin == B1) cand[atomicAdd(&lcount, 1u)] = kv[it];
-        }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) above += __shfl_xor(above, o, 64);
-    if ((threadIdx.x & 63) == 0) atomicAdd(&labove, above);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        cand_cnt[(size_t)b * n_chunks + c] = lcount;
-        cand_above[(size_t)b * n_chunks + c] = labove;
-    }
-}
-
-__global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int S_max, int S_stride, int top_k,
-    const uint32_t* __restrict__ cand_g, const uint32_t* __restrict__ cand_cnt,
-    const uint32_t* __restrict__ cand_above, int n_chunks, SelInfo* __restrict__ info,
-    uint32_t* __restrict__ counts) {
-    __shared__ uint32_t h[kHistBins];
-    __shared__ uint32_t cand[kCandCap];
-    __shared__ uint32_t wsum[kSelThreads / 64];
-    __shared__ uint32_t res[2];
-    __shared__ uint32_t cstart[1024];   // prefix of the per-chunk candidate counts
-    const int tid = threadIdx.x;
-    const int b = blockIdx.x;
-    const int L = min(max(seq_lens[b], 1), S_max);
-    const int k = min(top_k, L);
-    if (k == L) return;
-    // first digit as the candidate kernel found it (its chunk-0 workgroup)
-    const SelInfo fd = info[b];
-    const uint32_t B1 = fd.B1;
-    uint32_t need = (uint32_t)k - fd.above;
-    const int nkc = min(n_chunks, (L + kChunkKeys - 1) / kChunkKeys);
-    const uint32_t cnt = tid < nkc ? cand_cnt[(size_t)b * n_chunks + tid] : 0u;
-    const uint32_t incl = block_inclusive_scan<kSelThreads>(cnt, wsum);
-    if (tid < nkc) cstart[tid] = incl - cnt;
-    if (tid == kSelThreads - 1) res[0] = incl;                 // total candidates
-    __syncthreads();
-    const uint32_t nc = res[0];
-    const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride);
-    __syncthreads();
-    uint32_t T;
-    if (nc <= (uint32_t)kCandCap) {
-        // gather every chunk's slice: wave w copies chunks w, w+16, ...
-        const int lane = tid & 63, wave = tid >> 6;
-        for (int c = wave; c < nkc; c += kSelThreads / 64) {
-            const uint32_t n_c = cand_cnt[(size_t)b * n_chunks + c];
-            const uint32_t* src = cand_g + ((size_t)b * n_chunks + c) * kChunkKeys;
-            for (uint32_t i = lane; i < n_c; i += 64) cand[cstart[c] + i] = src[i];
-        }
-        for (int i = tid; i < kHistBins; i += kSelThreads) h[i] = 0u;
-        __syncthreads();
-        for (uint32_t i = tid; i < nc; i += kSelThreads) atomicAdd(&h[(cand[i] >> 8) & 0xFFFu], 1u);
-        __syncthreads();
-        find_crossing<kSelThreads>(h, kHistBins, need, wsum, res);
-        const uint32_t B2 = res[0];
-        need -= res[1];
-        __syncthreads();
-        for (int i = tid; i < 256; i += kSelThreads) h[i] = 0u;
-        __syncthreads();
-        const uint32_t pre = (B1 << 12) | B2;
-        for (uint32_t i = tid; i < nc; i += kSelThreads)
-            if ((cand[i] >> 8) == pre) atomicAdd(&h[cand[i] & 0xFFu], 1u);
-        __syncthreads();
-        find_crossing<kSelThreads>(h, 256, need, wsum, res);
-        T = (pre << 8) | res[0];
-        need -= res[1];
-    } else {
-        // the threshold bin overflowed the candidate list: two passes over the keys
-        for (int i = tid; i < kHistBins; i += kSelThreads) h[i] = 0u;
-        __syncthreads();
-        for (int j = tid; j < L; j += kSelThreads) {
-            const uint32_t key = keys[j];
-            if ((key >> 20) == B1) atomicAdd(&h[(key >> 8) & 0xFFFu], 1u);
-        }
-        __syncthreads();
-        find_crossing<kSelThreads>(h, kHistBins, need, wsum, res);
-        const uint32_t B2 = res[0];
-        need -= res[1];
-        __syncthreads();
-        for (int i = tid; i < 256; i += kSelThreads) h[i] = 0u;
-        __syncthreads();
-        const uint32_t pre = (B1 << 12) | B2;
-        for (int j = tid; j < L; j += kSelThreads) {
-            const uint32_t key = keys[j];
-            if ((key >> 8) == pre) atomicAdd(&h[key & 0xFFu], 1u);
-        }
-        __syncthreads();
-        find_crossing<kSelThreads>(h, 256, need, wsum, res);
-        T = (pre << 8) | res[0];
-        need -= res[1];
-    }
-    if (tid == 0) info[b] = SelInfo{T, need, B1, fd.above};
-    // per chunk: keys > T are the higher bins plus the slice's candidates
-    // above T; ties are the slice's keys equal to T (wave w takes chunks
-    // w, w + 16, ...)
-    {
-        const int lane = tid & 63, wave = tid >> 6;
-        for (int c = wave; c < nkc; c += kSelThreads / 64) {
-            const size_t ci = (size_t)b * n_chunks + c;
-            const uint32_t n_c = cand_cnt[ci];
-            const uint32_t* src = cand_g + ci * kChunkKeys;
-            uint32_t gt = 0, eq = 0;
-            for (uint32_t i = lane; i < n_c; i += 64) {
-                const uint32_t key = src[i];
-                gt += key > T;
-                eq += key == T;
-            }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                gt += __shfl_xor(gt, o, 64);
-                eq += __shfl_xor(eq, o, 64);
-            }
-            if (lane == 0) {
-                counts[ci * 2] = cand_above[ci] + gt;
-                counts[ci * 2 + 1] = eq;
-            }
-        }
-    }
-}
-
-// Writes the selected indices of one chunk in ascending order.  Wave w of
-// the chunk owns a contiguous quarter of it; a selected index's slot is
-// (selected before the chunk) + (before the wave) + (earlier in the wave).
-__global__ __launch_bounds__(kChunkThreads) void topk_write_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int S_max,
-    int S_stride, int top_k, const SelInfo* __restrict__ info,
-    const uint32_t* __restrict__ counts, int n_chunks, int32_t* __restrict__ topk_idx) {
-    __shared__ uint32_t wgt[kChunkThreads / 64], weq[kChunkThreads / 64];
+    __shared__ uint32_t wcnt[NW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.y, c = blockIdx.x;
     const int L = min(max(seq_lens[b], 1), S_max);
     const int k = min(top_k, L);
     int32_t* outp = topk_idx + (size_t)b * top_k;
-    const int c0 = c * kChunkKeys;
     if (c == 0)
-        for (int i = k + threadIdx.x; i < top_k; i += kChunkThreads) outp[i] = -1;
+        for (int i = k + tid; i < top_k; i += kChunkThreads) outp[i] = -1;
+    const int c0 = c * kChunkKeys;
     if (c0 >= L) return;
     const int c1 = min(c0 + kChunkKeys, L);
     if (k == L) {   // everything is selected
-        for (int j = c0 + threadIdx.x; j < c1; j += kChunkThreads) outp[j] = j;
+        for (int j = c0 + tid; j < c1; j += kChunkThreads) outp[j] = j;
         return;
     }
-    const uint32_t T = info[b].T, need = info[b].need;
     const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    constexpr int NW = kChunkThreads / 64;
-    constexpr int span = kChunkKeys / NW;
-    constexpr int KPL = span / 64;
     const int j0 = min(c0 + wave * span, c1), j1 = min(j0 + span, c1);
-    uint32_t kv[KPL];   // the wave's keys, all requested at once
+    uint32_t kv[kKeysPerLane];
 #pragma unroll
-    for (int it = 0; it < KPL; ++it) {
+    for (int it = 0; it < kKeysPerLane; ++it) {
         const int j = j0 + 64 * it + lane;
         kv[it] = j < j1 ? keys[j] : 0u;
     }
-    // selected and tied keys of the earlier chunks (lane-parallel)
-    uint32_t gt_before = 0, eq_before = 0;
-    for (int c2 = lane; c2 < c; c2 += 64) {
-        gt_before += counts[((size_t)b * n_chunks + c2) * 2];
-        eq_before += counts[((size_t)b * n_chunks + c2) * 2 + 1];
-    }
+    first_digit<kChunkThreads>(hist_g, b, L, k, h, wsum, res);
+    const uint32_t B1 = res[0];
+    if (c == 0 && tid == 0) info[b] = SelInfo{B1, res[1]};
+    uint32_t n_w = 0;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        gt_before += __shfl_xor(gt_before, o, 64);
-        eq_before += __shfl_xor(eq_before, o, 64);
-    }
-    uint32_t gt = 0, eq = 0;
+    for (int it = 0; it < kKeysPerLane; ++it)
+        n_w += (uint32_t)__popcll(__ballot(j0 + 64 * it + lane < j1 && (kv[it] >> 20) >= B1));
+    if (lane == 0) wcnt[wave] = n_w;
+    __syncthreads();
+    uint32_t pos = 0;
+    for (int w2 = 0; w2 < wave; ++w2) pos += wcnt[w2];
+    const size_t slice = ((size_t)b * n_chunks + c) * kChunkKeys;
 #pragma unroll
-    for (int it = 0; it < KPL; ++it) {
-        const bool ok = j0 + 64 * it + lane < j1;
-        gt += ok && kv[it] > T;
-        eq += ok && kv[it] == T;
+    for (int it = 0; it < kKeysPerLane; ++it) {
+        const int j = j0 + 64 * it + lane;
+        const bool keep = j < j1 && (kv[it] >> 20) >= B1;
+        const uint64_t mask = __ballot(keep);
+        const uint32_t p = pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        if (keep) {
+            ent_key[slice + p] = kv[it];
+            ent_idx[slice + p] = (uint32_t)j;
+        }
+        pos += (uint32_t)__popcll(mask);
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        gt += __shfl_xor(gt, o, 64);
-        eq += __shfl_xor(eq, o, 64);
+    if (tid == 0) {
+        uint32_t n = 0;
+        for (int w2 = 0; w2 < NW; ++w2) n += wcnt[w2];
+        ent_cnt[(size_t)b * n_chunks + c] = n;
     }
-    if (lane == 0) {
-        wgt[wave] = gt;
-        weq[wave] = eq;
+}
+
+// Radix passes 2 and 3 (12 and 8 bits) over the keys of the threshold bin B1
+// that `next(i)` yields for i in [0, n): the k-th largest key T and the
+// number of keys equal to T to take (need on entry: what is still to be
+// taken at bin B1).  Every thread of the block calls it.
+template <typename KeyAt>
+__device__ void lower_digits(uint32_t B1, uint32_t need, uint32_t n, KeyAt key_at, uint32_t* h,
+                             uint32_t* wsum, uint32_t* res, uint32_t& T, uint32_t& ties) {
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kHistBins; i += kSelThreads) h[i] = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < n; i += kSelThreads) {
+        const uint32_t key = key_at(i);
+        if ((key >> 20) == B1) atomicAdd(&h[(key >> 8) & 0xFFFu], 1u);
     }
     __syncthreads();
-    for (int w2 = 0; w2 < wave; ++w2) {
-        gt_before += wgt[w2];
-        eq_before += weq[w2];
+    find_crossing<kSelThreads>(h, kHistBins, need, wsum, res);
+    const uint32_t pre = (B1 << 12) | res[0];
+    need -= res[1];
+    __syncthreads();
+    for (int i = tid; i < 256; i += kSelThreads) h[i] = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < n; i += kSelThreads) {
+        const uint32_t key = key_at(i);
+        if ((key >> 8) == pre) atomicAdd(&h[key & 0xFFu], 1u);
     }
-    uint32_t sel_seen = gt_before + min(eq_before, need);   // selected before this step
-    uint32_t eq_seen = eq_before;                            // ties before this step
+    __syncthreads();
+    find_crossing<kSelThreads>(h, 256, need, wsum, res);
+    T = (pre << 8) | res[0];
+    ties = need - res[1];
+    __syncthreads();
+}
+
+// One workgroup per batch row: the exact k-th key T from the entries, then
+// the selected indices in ascending order (keys > T, and the first `ties`
+// keys == T by index).  The entries (at most k - 1 above the threshold bin
+// plus the bin itself) normally fit in LDS: there the two digit passes and
+// an ordered pass with two block scans finish the row.  A threshold bin too
+// large for LDS takes the digit passes over the row's keys and the ordered
+// pass in 1024-entry tiles over the entries in global memory (slow, and only
+// for rows with huge runs of near-equal scores).
+__global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int S_max, int S_stride,
+    int top_k, const uint32_t* __restrict__ ent_key, const uint32_t* __restrict__ ent_idx,
+    const uint32_t* __restrict__ ent_cnt, int n_chunks, const SelInfo* __restrict__ info,
+    int32_t* __restrict__ topk_idx) {
+    __shared__ uint32_t h[kHistBins];
+    __shared__ uint32_t lk[kEntCap], li[kEntCap];
+    __shared__ uint16_t emap[kEntCap];
+    __shared__ uint32_t wsum[kSelThreads / 64];
+    __shared__ uint32_t res[2];
+    __shared__ uint32_t cstart[kSelThreads];   // entry offset of each chunk
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.x;
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int k = min(top_k, L);
+    if (k == L) return;                        // written by the compact kernel
+    const SelInfo fd = info[b];
+    const uint32_t B1 = fd.B1;
+    const uint32_t need = (uint32_t)k - fd.above;
+    const int nkc = min(n_chunks, (L + kChunkKeys - 1) / kChunkKeys);
+    const uint32_t cnt = tid < nkc ? ent_cnt[(size_t)b * n_chunks + tid] : 0u;
+    const uint32_t incl = block_inclusive_scan<kSelThreads>(cnt, wsum);
+    if (tid < nkc) cstart[tid] = incl - cnt;
+    if (tid == kSelThreads - 1) res[0] = incl;
+    __syncthreads();
+    const uint32_t E = res[0];
+    __syncthreads();
+    const size_t row = (size_t)b * n_chunks * kChunkKeys;
+    int32_t* outp = topk_idx + (size_t)b * top_k;
+    uint32_t T, ties;
+    if (E <= (uint32_t)kEntCap) {
+        // the chunk of every entry (an LDS map: wave w fills chunks w, w + 16,
+        // ...), then every thread requests all its entries at once
+        for (int c = wave; c < nkc; c += kSelThreads / 64) {
+            const uint32_t n_c = (c + 1 < nkc ? cstart[c + 1] : E) - cstart[c];
+            for (uint32_t i = lane; i < n_c; i += 64) emap[cstart[c] + i] = (uint16_t)c;
+        }
+        __syncthreads();
+        static_assert(kEntCap % kSelThreads == 0, "whole entries per thread");
+        constexpr int kPerThread = kEntCap / kSelThreads;   // 12
+        uint32_t ek[kPerThread], ei[kPerThread];
 #pragma unroll
-    for (int it = 0; it < KPL; ++it) {
-        const int j = j0 + 64 * it + lane;
-        const uint32_t key = kv[it];
-        const bool is_gt = j < j1 && key > T;
-        const bool is_eq = j < j1 && key == T;
-        const uint64_t eq_mask = __ballot(is_eq);
-        const uint32_t eq_rank = eq_seen + __builtin_amdgcn_mbcnt_hi(
-            (uint32_t)(eq_mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eq_mask, 0u));
-        const bool take = is_gt || (is_eq && eq_rank < need);
-        const uint64_t take_mask = __ballot(take);
-        const uint32_t pos = sel_seen + __builtin_amdgcn_mbcnt_hi(
-            (uint32_t)(take_mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)take_mask, 0u));
-        if (take) outp[pos] = j;
-        sel_seen += (uint32_t)__popcll(take_mask);
-        eq_seen += (uint32_t)__popcll(eq_mask);
+        for (int u = 0; u < kPerThread; ++u) {
+            const uint32_t e = u * kSelThreads + tid;
+            ek[u] = ei[u] = 0u;
+            if (e < E) {
+                const int c = emap[e];
+                const size_t at = row + (size_t)c * kChunkKeys + (e - cstart[c]);
+                ek[u] = ent_key[at];
+                ei[u] = ent_idx[at];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kPerThread; ++u) {
+            const uint32_t e = u * kSelThreads + tid;
+            if (e < E) {
+                lk[e] = ek[u];
+                li[e] = ei[u];
+            }
+        }
+        __syncthreads();
+        lower_digits(B1, need, E, [&](uint32_t i) { return lk[i]; }, h, wsum, res, T, ties);
+        // thread t takes entries [t per, (t + 1) per): ranks of ties and
+        // output slots from two block scans
+        const uint32_t per = (E + kSelThreads - 1) / kSelThreads;
+        const uint32_t e0 = min((uint32_t)tid * per, E), e1 = min(e0 + per, E);
+        uint32_t eq = 0;
+        for (uint32_t e = e0; e < e1; ++e) eq += lk[e] == T;
+        uint32_t eq_seen = block_inclusive_scan<kSelThreads>(eq, wsum) - eq;
+        uint32_t take = 0;
+        for (uint32_t e = e0, r = eq_seen; e < e1; ++e) {
+            const uint32_t key = lk[e];
+            take += key > T || (key == T && r++ < ties);
+        }
+        uint32_t p = block_inclusive_scan<kSelThreads>(take, wsum) - take;
+        for (uint32_t e = e0; e < e1; ++e) {
+            const uint32_t key = lk[e];
+            bool tk = key > T;
+            if (key == T) tk = eq_seen++ < ties;
+            if (tk && p < (uint32_t)k) outp[p++] = (int32_t)li[e];   // p < k always holds
+        }
+        return;
+    }
+    // the threshold bin overflowed LDS: digit passes over the row's keys
+    const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride);
+    lower_digits(B1, need, (uint32_t)L, [&](uint32_t i) { return keys[i]; }, h, wsum, res, T, ties);
+    uint32_t eq_base = 0, sel_base = 0;
+    for (uint32_t t0 = 0; t0 < E; t0 += kSelThreads) {
+        const uint32_t e = t0 + tid;
+        uint32_t key = 0u, idx = 0u;
+        if (e < E) {
+            int lo = 0, hi = nkc;                // the chunk holding entry e
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (cstart[mid] <= e) lo = mid;
+                else hi = mid;
+            }
+            const size_t at = row + (size_t)lo * kChunkKeys + (e - cstart[lo]);
+            key = ent_key[at];
+            idx = ent_idx[at];
+        }
+        const uint32_t eqf = e < E && key == T;
+        const uint32_t eq_incl = block_inclusive_scan<kSelThreads>(eqf, wsum);
+        const uint32_t tk = e < E && (key > T || (eqf && eq_base + eq_incl - eqf < ties));
+        const uint32_t t_incl = block_inclusive_scan<kSelThreads>(tk, wsum);
+        if (tk && sel_base + t_incl - tk < (uint32_t)k) outp[sel_base + t_incl - tk] = (int32_t)idx;
+        if (tid == kSelThreads - 1) {
+            res[0] = eq_incl;
+            res[1] = t_incl;
+        }
+        __syncthreads();
+        eq_base += res[0];
+        sel_base += res[1];
+        __syncthreads();
     }
 }
 
@@ -1574,14 +1548,13 @@ SparseLayout sparse_layout(int32_t B, int32_t H, int32_t S_max, int32_t top_k) {
     l.n_key_chunks = (S_max + kChunkKeys - 1) / kChunkKeys;
     l.scores_bytes = al((size_t)B * ((S_max + 3) & ~3) * sizeof(float));
     l.hist_bytes = al((size_t)B * kHistBins * sizeof(uint32_t));
-    // candidate keys in per-chunk slices [B][key chunks][4096], then their counts
-    // [B][key chunks] and the higher-bin counts [B][key chunks]
-    l.cand_bytes = al((size_t)B * l.n_key_chunks * (kChunkKeys + 2) * sizeof(uint32_t));
+    // entries in per-chunk slices: keys [B][key chunks][4096], indices
+    // [B][key chunks][4096], then their counts [B][key chunks]
+    l.cand_bytes = al((size_t)B * l.n_key_chunks * (2 * kChunkKeys + 1) * sizeof(uint32_t));
     l.info_bytes = al((size_t)B * sizeof(SelInfo));
-    l.counts_bytes = al((size_t)B * l.n_key_chunks * 2 * sizeof(uint32_t));
     l.o_bytes = al((size_t)B * H * l.n_chunks * kDv * sizeof(float));
     l.ml_bytes = al((size_t)B * H * l.n_chunks * 2 * sizeof(float));
-    l.total = l.scores_bytes + l.hist_bytes + l.cand_bytes + l.info_bytes + l.counts_bytes +
+    l.total = l.scores_bytes + l.hist_bytes + l.cand_bytes + l.info_bytes +
               l.o_bytes + l.ml_bytes;
     return l;
 }
@@ -1614,13 +1587,11 @@ hipError_t launch_qsa_sparse_decode(const void* q, const void* k_cache, const vo
     uint32_t* hist = reinterpret_cast<uint32_t*>(w);
     w += sl.hist_bytes;
     uint32_t* cand = reinterpret_cast<uint32_t*>(w);
-    uint32_t* cand_cnt = cand + (size_t)B * sl.n_key_chunks * kChunkKeys;
-    uint32_t* cand_above = cand_cnt + (size_t)B * sl.n_key_chunks;
+    uint32_t* cand_idx = cand + (size_t)B * sl.n_key_chunks * kChunkKeys;
+    uint32_t* cand_cnt = cand_idx + (size_t)B * sl.n_key_chunks * kChunkKeys;
     w += sl.cand_bytes;
     SelInfo* info = reinterpret_cast<SelInfo*>(w);
     w += sl.info_bytes;
-    uint32_t* counts = reinterpret_cast<uint32_t*>(w);
-    w += sl.counts_bytes;
     w += sl.o_bytes + sl.ml_bytes;   // (empty)
     int32_t* cnt = reinterpret_cast<int32_t*>(w);
     w += lay.cnt_bytes;
@@ -1659,12 +1630,10 @@ hipError_t launch_qsa_sparse_decode(const void* q, const void* k_cache, const vo
         default:
             return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(topk_candidates_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, hist,
-                       cnt, NB, KS, kQsaTopBlocks, cand, cand_cnt, cand_above, nkc, info);
-    hipLaunchKernelGGL(topk_threshold_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, cnt, NB, KS,
-                       kQsaTopBlocks, cand, cand_cnt, cand_above, nkc, info, counts);
-    hipLaunchKernelGGL(topk_write_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, cnt, NB, KS,
-                       kQsaTopBlocks, info, counts, nkc, blk);
+    hipLaunchKernelGGL(topk_compact_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, hist, cnt,
+                       NB, KS, kQsaTopBlocks, cand, cand_idx, cand_cnt, nkc, info, blk);
+    hipLaunchKernelGGL(topk_finish_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, cnt, NB, KS,
+                       kQsaTopBlocks, cand, cand_idx, cand_cnt, nkc, info, blk);
     hipLaunchKernelGGL(gqa_gather_attn_kernel, dim3(kGChunks, Hkv, B), dim3(64), 0, s,
                        (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, blk,
                        seq_lens, Hq, Hkv, S_max, scale * kLog2e, tok, po, pml, kGChunks);
@@ -1720,13 +1689,11 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
     uint32_t* hist = reinterpret_cast<uint32_t*>(w);
     w += lay.hist_bytes;
     uint32_t* cand = reinterpret_cast<uint32_t*>(w);
-    uint32_t* cand_cnt = cand + (size_t)B * lay.n_key_chunks * kChunkKeys;
-    uint32_t* cand_above = cand_cnt + (size_t)B * lay.n_key_chunks;
+    uint32_t* cand_idx = cand + (size_t)B * lay.n_key_chunks * kChunkKeys;
+    uint32_t* cand_cnt = cand_idx + (size_t)B * lay.n_key_chunks * kChunkKeys;
     w += lay.cand_bytes;
     SelInfo* info = reinterpret_cast<SelInfo*>(w);
     w += lay.info_bytes;
-    uint32_t* counts = reinterpret_cast<uint32_t*>(w);
-    w += lay.counts_bytes;
     float* po = reinterpret_cast<float*>(w);
     w += lay.o_bytes;
     float* pml = reinterpret_cast<float*>(w);
@@ -1764,14 +1731,11 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
         default:
             return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(topk_candidates_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores,
-                       hist, seq_lens, S_max, S_stride, top_k, cand, cand_cnt, cand_above, nkc,
-                       info);
-    hipLaunchKernelGGL(topk_threshold_kernel, dim3(B), dim3(kSelThreads), 0, s, scores,
-                       seq_lens, S_max, S_stride, top_k, cand, cand_cnt, cand_above, nkc, info,
-                       counts);
-    hipLaunchKernelGGL(topk_write_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores,
-                       seq_lens, S_max, S_stride, top_k, info, counts, nkc, topk_idx);
+    hipLaunchKernelGGL(topk_compact_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, hist,
+                       seq_lens, S_max, S_stride, top_k, cand, cand_idx, cand_cnt, nkc, info,
+                       topk_idx);
+    hipLaunchKernelGGL(topk_finish_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, seq_lens, S_max,
+                       S_stride, top_k, cand, cand_idx, cand_cnt, nkc, info, topk_idx);
     hipLaunchKernelGGL(sparse_attn_kernel, dim3(lay.n_chunks, (H + 16 * kAttnWaves - 1) / (16 * kAttnWaves), B),
                        dim3(64 * kAttnWaves), 0, s,
                        (const uint16_t*)q, (const uint16_t*)latent, topk_idx, seq_lens, H, S_max,
