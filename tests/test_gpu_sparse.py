@@ -92,6 +92,18 @@ def test_sparse_large_threshold_bin(m):
     _run(m, d, 2048)
 
 
+@pytest.mark.parametrize("n_eq", [12000, 12400])
+def test_sparse_threshold_bin_at_lds_capacity(m, n_eq):
+    """n_eq equal top scores (|k_0|^2 ~ 128, the other scores ~ N(0, 128)):
+    the threshold bin just inside (12000) and just past (12400) the 12288
+    entries the row workgroup holds in LDS; the lowest 2048 indices win."""
+    d = sparse_inputs_host(1, 16, 16000, 576, 128, 47, [16000])
+    d["k_index"][0, :n_eq] = d["k_index"][0, 0]
+    d["q_index"][0] = d["k_index"][0, 0]
+    idx = _run(m, d, 2048)
+    assert list(idx[0]) == list(range(2048))
+
+
 def test_sparse_full_size_128k(m):
     import torch
     cfg = SPARSE_128K
