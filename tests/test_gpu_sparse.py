@@ -104,6 +104,18 @@ def test_sparse_threshold_bin_at_lds_capacity(m, n_eq):
     assert list(idx[0]) == list(range(2048))
 
 
+def test_sparse_overflow_and_lds_rows_in_one_call(m):
+    """Row 0: 20000 equal top scores (the finish kernel's overflow path);
+    row 1: ordinary scores (its LDS path); row 2 shorter than k (every index).
+    Each row takes its own path in the same launch."""
+    d = sparse_inputs_host(3, 16, 24000, 576, 128, 48, [24000, 23001, 1500])
+    d["k_index"][0, :20000] = d["k_index"][0, 0]
+    d["q_index"][0] = d["k_index"][0, 0]
+    idx = _run(m, d, 2048)
+    assert list(idx[0]) == list(range(2048))
+    assert list(idx[2][:1500]) == list(range(1500)) and np.all(idx[2][1500:] == -1)
+
+
 def test_sparse_full_size_128k(m):
     import torch
     cfg = SPARSE_128K
