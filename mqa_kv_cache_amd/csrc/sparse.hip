@@ -1182,6 +1182,7 @@ __global__ __launch_bounds__(256) void qsa_block_kernel(
     // ta[g][i] at 4 k_begin + 64 g (amplitude included) and tb[n][i] at 4 n,
     // each from an fp64-reduced angle (the product adds ~2 fp32 roundings).
     __shared__ f32x2 ta[16][kDidx / 2], tb[16][kDidx / 2];
+    __shared__ u32x4 qs[4 * NHB][64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = lane >> 4, n = lane & 15;
@@ -1195,24 +1196,26 @@ __global__ __launch_bounds__(256) void qsa_block_kernel(
     // keys), then the tables while they are in flight
     static_assert(kDidx / 2 == 64, "one rotary pair per lane");
     const double th_lane = rope.theta[lane];                 // rope.half <= kDidx / 2
-    u32x4 qf[NHB][4];
+    // the query heads' B-operand fragments, shared by the four waves through
+    // LDS: qs[4 hb + u][lane (G, n)] = head 16 hb + n, dims 32 u + 8 G .. +7
+    u32x4 qv[NHB];
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-        const uint16_t* qrow = q_index + ((size_t)b * HI + 16 * hb + n) * kDidx + 8 * G;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) qf[hb][u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u);
+    for (int i = 0; i < NHB; ++i) {
+        const int e = tid + 256 * i, f = e >> 6, l = e & 63;
+        qv[i] = *reinterpret_cast<const u32x4*>(
+            q_index + ((size_t)b * HI + 16 * (f >> 2) + (l & 15)) * kDidx + 32 * (f & 3) + 8 * (l >> 4));
     }
     const int nbl = k_end - k_begin;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(
         k_index + ((size_t)b * S_max + (size_t)kQsaBlock * k_begin) * kDidx,
         (uint32_t)nbl * kQsaBlock * kDidx * 2u);
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(keys + (size_t)b * KS + k_begin, (uint32_t)nbl * 4u);
-    const int n_groups = (nbl + 15) / 16;
-    const int n_steps = (n_groups + 3) / 4;                  // uniform over the workgroup
     // lane (G, n): block 16 g + n, dims 32 u + 8 G .. +7 of its 4 keys.
-    // The next group's keys are requested before this group's arithmetic
-    // (groups past the range read zeros through the resource bound).
-    u32x4 raw[kQsaBlock][4];
+    // Wave w takes groups w, w + 4, w + 8, w + 12 (all 16 of the workgroup),
+    // keys requested two groups ahead in three register sets; groups past
+    // the range read zeros through the resource bound, and their stores fall
+    // outside the score descriptor (their histogram updates are skipped).
+    u32x4 b0[kQsaBlock][4], b1[kQsaBlock][4], b2[kQsaBlock][4];
     auto load_group = [&](int g, u32x4 (&dst)[kQsaBlock][4]) {
 #pragma unroll
         for (int r = 0; r < kQsaBlock; ++r)
@@ -1221,7 +1224,10 @@ __global__ __launch_bounds__(256) void qsa_block_kernel(
                 dst[r][u] = buf_load16_nt(
                     kr, (uint32_t)((((16 * g + n) * kQsaBlock + r) * kDidx + 32 * u + 8 * G) * 2));
     };
-    load_group(wave, raw);
+    load_group(wave, b0);
+    load_group(wave + 4, b1);
+#pragma unroll
+    for (int i = 0; i < NHB; ++i) qs[(tid + 256 * i) >> 6][(tid + 256 * i) & 63] = qv[i];
     for (int i = tid; i < kHistBins; i += 256) lh[i] = 0u;
     if (lane < rope.half) {
         // thread (wave, lane): pair i = lane, table rows wave + 4 t
@@ -1240,10 +1246,8 @@ __global__ __launch_bounds__(256) void qsa_block_kernel(
         }
     }
     __syncthreads();
-    for (int st = 0; st < n_steps; ++st) {
+    auto step = [&](int st, const u32x4 (&raw)[kQsaBlock][4]) {
         const int g = 4 * st + wave;                     // 16-block group of this wave
-        u32x4 nxt[kQsaBlock][4];
-        load_group(g + 4, nxt);
         float mk[4][8];
         float ss = 0.f;
 #pragma unroll
@@ -1287,8 +1291,9 @@ __global__ __launch_bounds__(256) void qsa_block_kernel(
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                acc = mfma16(ahi[u], qf[hb][u], acc);
-                acc = mfma16(alo[u], qf[hb][u], acc);
+                const u32x4 qb = qs[4 * hb + u][lane];
+                acc = mfma16(ahi[u], qb, acc);
+                acc = mfma16(alo[u], qb, acc);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) t[i] += fmaxf(acc[i], 0.0f);   // blocks 4 G + i, head 16 hb + n
@@ -1301,11 +1306,14 @@ __global__ __launch_bounds__(256) void qsa_block_kernel(
         __builtin_amdgcn_raw_buffer_store_b32(key, sr, n < 4 ? (uint32_t)row * 4u : 0x80000000u, 0, 0);
         const uint32_t bin = key >> 20;
         if (n < 4 && row < nbl && bin) atomicAdd(&lh[bin], 1u);
-#pragma unroll
-        for (int r = 0; r < kQsaBlock; ++r)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) raw[r][u] = nxt[r][u];
-    }
+    };
+    static_assert(kQsaBlocksPerWg == 4 * 4 * 16, "four steps of four waves of 16 blocks");
+    load_group(wave + 8, b2);
+    step(0, b0);
+    load_group(wave + 12, b0);
+    step(1, b1);
+    step(2, b2);
+    step(3, b0);
     __syncthreads();
     for (int i = tid; i < kHistBins; i += 256)
         if (lh[i]) atomicAdd(&hist[(size_t)b * kHistBins + i], lh[i]);
