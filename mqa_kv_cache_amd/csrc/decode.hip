@@ -21,7 +21,7 @@
 // of one context are contiguous.  Per piece, in tiles of 32 rows:
 //   S^T[32 rows][16 heads] = K_tile . Q^T     (K as A operand; q as hi+lo bf16, 2x8 MFMAs)
 //   online softmax per head in fp32 (base 2; scale*log2(e) is folded into q)
-//   O^T[D][16 heads]      += V_tile^T . P^T   (8 MFMAs for D = 128)
+//   O^T[D][16 heads]      += V_tile^T . P^T   (P as hi+lo bf16, 2x8 MFMAs for D = 128)
 // The S^T accumulator layout is exactly the P^T operand layout the second
 // MFMA needs, so probabilities never leave their lane.  V^T operands come
 // from 16-byte row loads transposed 8x8 in registers.  The next tile's loads
@@ -119,13 +119,14 @@ __device__ __forceinline__ void tile_math(const DecodeTile<D>& t, int t0, int r1
                 ls += p[th][i];
             }
         l_run[nb] += rows4_sum(ls);
-        u32x4 pb;
-        pb[0] = pack_bf16x2(p[0][0], p[0][1]);
-        pb[1] = pack_bf16x2(p[0][2], p[0][3]);
-        pb[2] = pack_bf16x2(p[1][0], p[1][1]);
-        pb[3] = pack_bf16x2(p[1][2], p[1][3]);
+        u32x4 ph, pl;
+        pack_p_hilo(p, ph, pl);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o[nb][c] = mfma16(column_of(t.v, c), pb, o[nb][c]);
+        for (int c = 0; c < 8; ++c) {
+            const u32x4 vc = column_of(t.v, c);
+            o[nb][c] = mfma16(vc, ph, o[nb][c]);
+            o[nb][c] = mfma16(vc, pl, o[nb][c]);
+        }
     }
 }
 

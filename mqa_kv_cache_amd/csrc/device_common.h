@@ -36,6 +36,22 @@ __device__ __forceinline__ u32x2 split_bf16x2(float a, float b) {
     return u32x2{hi, pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u))};
 }
 
+// The probabilities of a 32-row tile as the P^T operand of the PV product,
+// in two bf16 terms (hi = bf16(p), lo = bf16(p - hi)): p reaches the matrix
+// core to about 2^-17 relative instead of bf16's 2^-9, which a sharp softmax
+// with cancelling values needs (a dominant row's single-term rounding error
+// alone can exceed the output tolerance).  p[th][i] is row 16 th + 4 G + i.
+__device__ __forceinline__ void pack_p_hilo(const float (&p)[2][4], u32x4& hi, u32x4& lo) {
+#pragma unroll
+    for (int th = 0; th < 2; ++th)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const u32x2 hl = split_bf16x2(p[th][2 * j], p[th][2 * j + 1]);
+            hi[2 * th + j] = hl[0];
+            lo[2 * th + j] = hl[1];
+        }
+}
+
 // ---------------------------------------------------------------------------
 // Buffer resources: loads outside [0, num_bytes) return zero, so tails and
 // ragged lengths need no branches and can never fault.

@@ -659,11 +659,8 @@ __device__ __forceinline__ void sparse_sub_step(const uint8_t* rows, const u32x4
             ls += pr[th][i];
         }
     l_run += rows4_sum(ls);
-    u32x4 pb;
-    pb[0] = pack_bf16x2(pr[0][0], pr[0][1]);
-    pb[1] = pack_bf16x2(pr[0][2], pr[0][3]);
-    pb[2] = pack_bf16x2(pr[1][0], pr[1][1]);
-    pb[3] = pack_bf16x2(pr[1][2], pr[1][3]);
+    u32x4 ph, pl;
+    pack_p_hilo(pr, ph, pl);
 #pragma unroll
     for (int dq = 0; dq < 4; ++dq) {
         u32x4 vr[8];
@@ -671,7 +668,11 @@ __device__ __forceinline__ void sparse_sub_step(const uint8_t* rows, const u32x4
         for (int r = 0; r < 8; ++r)
             vr[r] = *reinterpret_cast<const u32x4*>(rows + slot_row(G, r) * kRowStride + (128 * dq + 8 * n) * 2);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) o[dq][t] = mfma16(column_of(vr, t), pb, o[dq][t]);
+        for (int t = 0; t < 8; ++t) {
+            const u32x4 vc = column_of(vr, t);
+            o[dq][t] = mfma16(vc, ph, o[dq][t]);
+            o[dq][t] = mfma16(vc, pl, o[dq][t]);
+        }
     }
 }
 
@@ -1387,17 +1388,18 @@ __device__ __forceinline__ void gqa_gather_step(const uint8_t* kb, const uint8_t
             ls += pr[th][i];
         }
     l_run += rows4_sum(ls);
-    u32x4 pb;
-    pb[0] = pack_bf16x2(pr[0][0], pr[0][1]);
-    pb[1] = pack_bf16x2(pr[0][2], pr[0][3]);
-    pb[2] = pack_bf16x2(pr[1][0], pr[1][1]);
-    pb[3] = pack_bf16x2(pr[1][2], pr[1][3]);
+    u32x4 ph, pl;
+    pack_p_hilo(pr, ph, pl);
     u32x4 vr[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r)
         vr[r] = *reinterpret_cast<const u32x4*>(vb + slot_row(G, r) * kGRowStride + 16 * n);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) o[t] = mfma16(column_of(vr, t), pb, o[t]);
+    for (int t = 0; t < 8; ++t) {
+        const u32x4 vc = column_of(vr, t);
+        o[t] = mfma16(vc, ph, o[t]);
+        o[t] = mfma16(vc, pl, o[t]);
+    }
 }
 
 // grid (chunks of 128 selected tokens, Hkv, B), one wave: the kv head's g

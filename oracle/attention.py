@@ -5,8 +5,8 @@ Test infrastructure only (see the package docstring).
 Readings where the pages leave a step open:
 
 * q head h reads kv head floor(h / g), g = n_head / n_kv_head: the pages'
-  GQA code repeats each K/V head g times along the head axis
-  (repeat_interleave / expand+reshape), which gives exactly this map.
+  GQA code repeats each K/V head g times along the head axis, copies of one
+  head side by side, which gives exactly this map.
 * Prefill positions are 0 .. T-1 and row i sees keys j <= i (the pages mask
   the strict upper triangle with -inf).
 * A decode step's new token has already been appended to the cache:
@@ -25,7 +25,7 @@ from . import rope as _rope
 def softmax(s: np.ndarray) -> np.ndarray:
     """exp(s - max s) / sum, over the last axis.
 
-    [注意力变体与MoE] "MQA 与 GQA", attention(): s.softmax(-1).
+    [注意力变体与MoE] "MQA 与 GQA" (softmax over the key axis).
     """
     s = np.asarray(s, dtype=np.float64)
     e = np.exp(s - np.max(s, axis=-1, keepdims=True))
@@ -35,7 +35,7 @@ def softmax(s: np.ndarray) -> np.ndarray:
 def attend(q_vec, K, V, scale: float) -> np.ndarray:
     """One query row against the visible keys: softmax(scale * K q) @ V.
 
-    [注意力变体与MoE] "MQA 与 GQA", attention(): s = q k^T / sqrt(hd), softmax,
+    [注意力变体与MoE] "MQA 与 GQA": scores q.k divided by sqrt(hd), softmax,
     then the weighted sum of V.
     """
     s = (np.asarray(K, dtype=np.float64) @ np.asarray(q_vec, dtype=np.float64)) * scale
@@ -45,8 +45,10 @@ def attend(q_vec, K, V, scale: float) -> np.ndarray:
 def kv_head_of(h: int, n_head: int, n_kv_head: int) -> int:
     """The kv head that q head h reads.
 
-    [注意力变体与MoE] "MQA 与 GQA": k.repeat_interleave(g, dim=1), g = n_head //
-    n_kv_head; [attention] GQA code: unsqueeze(2).expand(...).reshape(...).
+    [注意力变体与MoE] "MQA 与 GQA" and [attention] GQA: each K/V head is
+    repeated g = n_head / n_kv_head times along the head axis, consecutive
+    copies next to each other, so q head h meets copy h of that expanded axis,
+    which is kv head floor(h / g).
     """
     return h // (n_head // n_kv_head)
 
@@ -59,8 +61,8 @@ def causal_attention(q, k, v, scale: float, rows=None, heads=None, window: int =
     ``rows``/``heads`` restrict the computation to a sample; the result then
     holds NaN elsewhere.
 
-    [注意力变体与MoE] "MQA 与 GQA", attention(): masked_fill(triu(1), -inf);
-    [transformer架构] §2.5.1: the band mask (0 for i-w+1 <= j <= i).
+    [注意力变体与MoE] "MQA 与 GQA" (the scores above the diagonal are masked
+    to -inf); [transformer架构] §2.5.1: the band mask (0 for i-w+1 <= j <= i).
     """
     B, Hq, T, _ = q.shape
     Hkv = k.shape[1]
@@ -104,6 +106,26 @@ def decode_one(q_vec, K, V, seq_len: int, scale: float, rope_p) -> np.ndarray:
     if rope_p is not None:
         qv = _rope.rotate_rows(qv, np.array([seq_len - 1]), _rope.with_length(rope_p, seq_len))
     return attend(qv[0], K[:seq_len], V[:seq_len], scale)
+
+
+def decode_group(q_rows, K, V, seq_len: int, scale: float, rope_p) -> np.ndarray:
+    """The decode outputs of several query heads that read one kv head: each
+    row of q_rows [n, D] is rotated at position seq_len-1 and attends to the
+    first seq_len rows of K and V, exactly as :func:`decode_one` does for one
+    head (the scores of all rows form one [n, seq_len] product).  Returns
+    [n, Dv].
+
+    [注意力变体与MoE] "MQA 与 GQA": the g heads of a group share their K/V
+    head, so they see the same keys; [注意力变体与MoE] "生成时的瓶颈" for the
+    decode step itself.
+    """
+    qv = np.asarray(q_rows, dtype=np.float64)
+    if rope_p is not None:
+        qv = _rope.rotate_rows(qv[None], np.array([seq_len - 1]),
+                               _rope.with_length(rope_p, seq_len))[0]
+    K = np.asarray(K, dtype=np.float64)[:seq_len]
+    V = np.asarray(V, dtype=np.float64)[:seq_len]
+    return softmax((qv @ K.T) * scale) @ V
 
 
 def decode(q, k_cache, v_cache, seq_lens, scale: float, rope_p, pairs=None) -> np.ndarray:
@@ -223,23 +245,38 @@ def append_rows_window(k_cache, v_cache, k_new, v_new, seq_lens, rope_p, rolling
     return kc, vc
 
 
-def page_attention(x, Wq, Wk, Wv, n_head: int, n_kv_head: int) -> np.ndarray:
-    """The pages' whole GQA attention function (projection, head split, K/V
-    repeated g times along the head axis, causal softmax, heads merged), with
-    no RoPE.  Output [B, T, C].
+def projected_attention(x, Wq, Wk, Wv, n_head: int, n_kv_head: int) -> np.ndarray:
+    """Causal GQA self-attention of a hidden-state sequence, no RoPE, written
+    from the definition one output element group at a time.  Output [B, T, C].
 
-    [注意力变体与MoE] "MQA 与 GQA", attention(x, Wq, Wk, Wv, n_head, n_kv_head).
+    x is [B, T, C] and the projections map C to n_head (Wq) or n_kv_head (Wk,
+    Wv) heads of width hd = C / n_head.  For batch b, query position i and
+    query head h (columns h*hd .. (h+1)*hd - 1 of the output): the query is
+    x[b, i] projected by head h's columns of Wq; it is compared with the keys
+    of positions j = 0 .. i, each x[b, j] projected by the columns of kv head
+    floor(h / g) of Wk (g = n_head / n_kv_head); the scores are divided by
+    sqrt(hd), normalised by softmax, and weight the same positions' values
+    (the same kv head's columns of Wv).
+
+    [注意力变体与MoE] "MQA 与 GQA" (the attention function there takes x, the
+    three projections and the two head counts; its output keeps x's shape).
     """
     x = np.asarray(x, dtype=np.float64)
+    Wq, Wk, Wv = (np.asarray(w, dtype=np.float64) for w in (Wq, Wk, Wv))
     B, T, C = x.shape
+    if C % n_head or n_head % n_kv_head:
+        raise ValueError("C must split into n_head heads and n_head into n_kv_head groups")
     hd = C // n_head
-    q = (x @ np.asarray(Wq, np.float64)).reshape(B, T, n_head, hd).transpose(0, 2, 1, 3)
-    k = (x @ np.asarray(Wk, np.float64)).reshape(B, T, n_kv_head, hd).transpose(0, 2, 1, 3)
-    v = (x @ np.asarray(Wv, np.float64)).reshape(B, T, n_kv_head, hd).transpose(0, 2, 1, 3)
     g = n_head // n_kv_head
-    k = np.repeat(k, g, axis=1)
-    v = np.repeat(v, g, axis=1)
-    s = (q @ k.transpose(0, 1, 3, 2)) / np.sqrt(hd)
-    s = np.where(np.triu(np.ones((T, T), dtype=bool), 1), -np.inf, s)
-    y = softmax(s) @ v
-    return y.transpose(0, 2, 1, 3).reshape(B, T, C)
+    y = np.zeros((B, T, n_head * hd))
+    for b in range(B):
+        for h in range(n_head):
+            kv = h // g
+            cq = slice(h * hd, (h + 1) * hd)
+            ckv = slice(kv * hd, (kv + 1) * hd)
+            for i in range(T):
+                qi = x[b, i] @ Wq[:, cq]
+                keys = np.array([x[b, j] @ Wk[:, ckv] for j in range(i + 1)])
+                vals = np.array([x[b, j] @ Wv[:, ckv] for j in range(i + 1)])
+                y[b, i, cq] = softmax(keys @ qi / np.sqrt(hd)) @ vals
+    return y

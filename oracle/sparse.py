@@ -101,6 +101,22 @@ def sparse_attention_one(q_vec, latent, idx, scale: float, Dv: int) -> np.ndarra
     return p @ rows[:, :Dv]
 
 
+def sparse_attention_heads(q_rows, latent, idx, scale: float, Dv: int) -> np.ndarray:
+    """:func:`sparse_attention_one` for several heads at once (q_rows [H, Dqk]):
+    every head reads the same selected latent rows, so the scores of all heads
+    form one [rows, H] product and each head's softmax runs over the rows.
+    Returns [H, Dv].
+
+    [attention] DSA ② (the heads share the one latent row) and ③.
+    """
+    idx = np.asarray(idx)
+    idx = idx[idx >= 0]
+    rows = np.asarray(latent, dtype=np.float64)[idx]
+    s = (rows @ np.asarray(q_rows, dtype=np.float64).T) * scale      # [rows, H]
+    p = softmax(s.T)                                                 # [H, rows]
+    return p @ rows[:, :Dv]
+
+
 def topk_sparse_decode(q, latent, q_index, k_index, seq_lens, top_k: int, scale: float,
                        Dv: int, batches=None, heads=None):
     """Whole chain per batch row.  Returns (topk_idx [B, k] int32, out [B, H, Dv]).

@@ -42,3 +42,62 @@ def gpu_available():
         return torch.cuda.is_available()
     except Exception:
         return False
+
+
+def pow2_bf16(bits, k):
+    """bf16 bit patterns times 2^k, exactly (the exponent field is raised by k;
+    zeros stay zero).  Used to sharpen the softmax: q times 4 or 8 spreads the
+    scores over many units, so a few rows dominate every head."""
+    b = np.asarray(bits, dtype=np.uint16)
+    nz = (b & 0x7FFF) != 0
+    exp = (b >> 7) & 0xFF
+    if np.any(nz & (exp + k >= 255)) or np.any(nz & (exp == 0)):
+        raise ValueError("pow2_bf16: exponent out of range")
+    return np.where(nz, (b.astype(np.uint32) + (k << 7)).astype(np.uint16), b)
+
+
+class Guarded:
+    """A device tensor of `shape` placed between two canary bands of `band`
+    bytes each (the band size keeps the view 256-byte aligned).  `view` is
+    handed to an entry point as an output or workspace; check() asserts that
+    no byte of either band changed."""
+
+    def __init__(self, shape, dtype, band=4096, seed=0):
+        import torch
+        esize = torch.empty((), dtype=dtype).element_size()
+        n = int(np.prod(shape)) if len(shape) else 1
+        nbytes = n * esize
+        self.band = band
+        rng = np.random.default_rng(seed)
+        total = band + ((nbytes + 255) // 256) * 256 + band
+        self.raw = torch.from_numpy(rng.integers(0, 256, size=total, dtype=np.uint8)).cuda()
+        self.expect = self.raw.clone()
+        self.view = self.raw[band:band + nbytes].view(dtype).view(shape)
+        self.nbytes = nbytes
+
+    def check(self, what=""):
+        import torch
+        torch.cuda.synchronize()
+        lo = self.band
+        hi = self.band + self.nbytes
+        assert torch.equal(self.raw[:lo], self.expect[:lo]), f"{what}: canary before the buffer changed"
+        assert torch.equal(self.raw[hi:], self.expect[hi:]), f"{what}: canary after the buffer changed"
+
+
+def check_every_head(got, q, k, v, lens, scale, rope, Hq, Hkv, what, qmul=1.0):
+    """Every (b, h) output of a full-size decode against the oracle: per
+    (batch, kv head) the group's g heads at once over that context's rows."""
+    g = Hq // Hkv
+    from oracle import attention as oatt
+    from workloads import bf16_tensor_to_f64
+    qf = bf16_tensor_to_f64(q) * qmul
+    worst = 0.0
+    for b in range(len(lens)):
+        L = int(lens[b])
+        for kv in range(Hkv):
+            kb = bf16_tensor_to_f64(k[b, kv, :L])
+            vb = bf16_tensor_to_f64(v[b, kv, :L])
+            ref = oatt.decode_group(qf[b, kv * g:(kv + 1) * g], kb, vb, L, scale, rope)
+            worst = max(worst, assert_close(got[b, kv * g:(kv + 1) * g], ref,
+                                            f"{what} (b={b}, kv={kv}, L={L})"))
+    print(f"[parity] {what}: every head, worst err/bound {worst:.3f}", flush=True)

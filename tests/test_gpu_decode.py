@@ -4,7 +4,7 @@ import math
 import numpy as np
 import pytest
 
-from helpers import assert_close, from_dev, to_dev
+from helpers import assert_close, check_every_head, from_dev, to_dev
 from oracle import attention as oatt
 from workloads import (DECODE_4K, DECODE_32K_YARN, ROPE_PLAIN, ROPE_YARN, bf16_bits_to_f64,
                        bf16_tensor_to_f64, decode_inputs_host, device_randn_bf16, rope_settings)
@@ -123,29 +123,31 @@ def test_decode_structured_cases(m):
     assert np.abs(ref[0, 0] - vf[0, 0, 777]).max() < 1e-3
 
 
-def _full_size(m, cfg, n_pairs=24):
+def _full_size(m, cfg, k2=0):
+    """The workload at full size with guarded output and workspace, run twice
+    (bitwise equal); every head against the oracle.  k2 > 0 multiplies q by
+    2^k2 on the device (exact in bf16): a sharp softmax."""
     import torch
+    from helpers import Guarded
     B, Hq, Hkv, D, S = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.S_max
     lens = cfg.seq_lens()
-    print(f"[case] full size B={B} Hq={Hq} Hkv={Hkv} S_max={S} lens={list(lens)}", flush=True)
-    q = device_randn_bf16((B, Hq, D), cfg.seed * 10 + 1)
+    print(f"[case] full size B={B} Hq={Hq} Hkv={Hkv} S_max={S} lens={list(lens)} q x{2 ** k2}",
+          flush=True)
+    q = device_randn_bf16((B, Hq, D), cfg.seed * 10 + 1) * float(2 ** k2)
     k = device_randn_bf16((B, Hkv, S, D), cfg.seed * 10 + 2)
     v = device_randn_bf16((B, Hkv, S, D), cfg.seed * 10 + 3)
     sl = torch.from_numpy(lens).cuda()
-    out = m.gqa_decode(q, k, v, sl, cfg.scale, q_rope=cfg.rope())
+    out = Guarded((B, Hq, D), torch.bfloat16, seed=1)
+    ws = Guarded((m.gqa_decode_workspace_size(B, Hq, Hkv, D, S),), torch.uint8, seed=2)
+    m.gqa_decode(q, k, v, sl, cfg.scale, q_rope=cfg.rope(), out=out.view, workspace=ws.view)
+    out.check("out")
+    ws.check("workspace")
+    first = out.view.clone()
+    m.gqa_decode(q, k, v, sl, cfg.scale, q_rope=cfg.rope(), out=out.view, workspace=ws.view)
     torch.cuda.synchronize()
-    got = from_dev(out)
-    rng = np.random.default_rng(cfg.seed)
-    pairs = [(int(rng.integers(B)), int(rng.integers(Hq))) for _ in range(n_pairs)]
-    qf = bf16_tensor_to_f64(q)
-    for b, h in pairs:
-        kv = h // (Hq // Hkv)
-        L = int(lens[b])
-        kb = bf16_tensor_to_f64(k[b, kv, :L])
-        vb = bf16_tensor_to_f64(v[b, kv, :L])
-        ref = oatt.decode_one(qf[b, h], kb, vb, L, cfg.scale, cfg.rope())
-        assert_close(got[b, h], ref, f"full-size (b={b}, h={h}, L={L})")
-    assert np.all(np.isfinite(got))
+    assert torch.equal(first, out.view), "two identical calls differ"
+    got = from_dev(out.view)
+    check_every_head(got, q, k, v, lens, cfg.scale, cfg.rope(), Hq, Hkv, "full size")
 
 
 def test_decode_full_size_4k(m):
@@ -154,6 +156,13 @@ def test_decode_full_size_4k(m):
 
 def test_decode_full_size_32k_yarn_ragged(m):
     _full_size(m, DECODE_32K_YARN)
+
+
+@pytest.mark.parametrize("k2", [2, 3])
+def test_decode_full_size_peaked(m, k2):
+    """Both decode workloads with q x 4 and x 8: outputs O(1), every head."""
+    _full_size(m, DECODE_4K, k2)
+    _full_size(m, DECODE_32K_YARN, k2)
 
 
 # ---------------------------------------------------------------------------
@@ -237,7 +246,7 @@ def test_decode_append_then_decode_matches(m):
     assert torch.equal(o1, o2)
 
 
-def test_decode_append_full_size_32k_yarn_ragged(m, n_pairs=16):
+def test_decode_append_full_size_32k_yarn_ragged(m):
     import torch
     cfg = DECODE_32K_YARN
     B, Hq, Hkv, D, S = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.S_max
@@ -260,20 +269,20 @@ def test_decode_append_full_size_32k_yarn_ragged(m, n_pairs=16):
     assert torch.equal(k0, k) and torch.equal(v0, v)
     assert torch.equal(v[bi, :, rows], vn)
     got = from_dev(out)
-    rng = np.random.default_rng(cfg.seed + 7)
-    pairs = [(int(rng.integers(B)), int(rng.integers(Hq))) for _ in range(n_pairs)]
     qf, knf, vnf = bf16_tensor_to_f64(q), bf16_tensor_to_f64(kn), bf16_tensor_to_f64(vn)
-    for b, h in pairs:
-        kv = h // (Hq // Hkv)
+    g = Hq // Hkv
+    for b in range(B):
         L = int(lens[b])
-        kb = bf16_tensor_to_f64(k0[b, kv, :L])      # rows < L-1 as they were
-        vb = bf16_tensor_to_f64(v0[b, kv, :L])
-        kc, vc = oatt.append_rows(kb[None, None], vb[None, None], knf[b, kv][None, None],
-                                  vnf[b, kv][None, None], np.array([L]), cfg.rope())
-        ref = oatt.decode_one(qf[b, h], kc[0, 0], vc[0, 0], L, cfg.scale, cfg.rope())
-        assert_close(got[b, h], ref, f"append full size (b={b}, h={h}, L={L})")
-        kw = bf16_tensor_to_f64(k[b, kv, L - 1])
-        assert np.all(np.abs(kw - kc[0, 0, L - 1]) <= _bf16_ulp(kc[0, 0, L - 1]))
+        for kv in range(Hkv):
+            kb = bf16_tensor_to_f64(k0[b, kv, :L])      # rows < L-1 as they were
+            vb = bf16_tensor_to_f64(v0[b, kv, :L])
+            kc, vc = oatt.append_rows(kb[None, None], vb[None, None], knf[b, kv][None, None],
+                                      vnf[b, kv][None, None], np.array([L]), cfg.rope())
+            ref = oatt.decode_group(qf[b, kv * g:(kv + 1) * g], kc[0, 0], vc[0, 0], L, cfg.scale,
+                                    cfg.rope())
+            assert_close(got[b, kv * g:(kv + 1) * g], ref, f"append full size (b={b}, kv={kv}, L={L})")
+            kw = bf16_tensor_to_f64(k[b, kv, L - 1])
+            assert np.all(np.abs(kw - kc[0, 0, L - 1]) <= _bf16_ulp(kc[0, 0, L - 1]))
 
 
 # ---------------------------------------------------------------------------
@@ -331,10 +340,10 @@ def test_decode_window_parity(m, case):
 
 
 @pytest.mark.parametrize("mode", ["window4096", "rolling4096"])
-def test_decode_window_full_size_32k(m, mode, n_pairs=12):
+def test_decode_window_full_size_32k(m, mode):
     """The 32K workload (ragged 16K-32K contexts, YaRN) with a 4096-token
     sliding window over its linear cache, and as a 4096-slot rolling buffer
-    (contexts far longer than the buffer), sampled heads against the oracle."""
+    (contexts far longer than the buffer), every head against the oracle."""
     import torch
     cfg = DECODE_32K_YARN
     B, Hq, Hkv, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.D
@@ -350,17 +359,15 @@ def test_decode_window_full_size_32k(m, mode, n_pairs=12):
                               q_rope=cfg.rope())
     torch.cuda.synchronize()
     got = from_dev(out)
-    rng = np.random.default_rng(cfg.seed + 11)
-    pairs = [(int(rng.integers(B)), int(rng.integers(Hq))) for _ in range(n_pairs)]
     qf = bf16_tensor_to_f64(q)
-    for b, h in pairs:
-        kv = h // (Hq // Hkv)
+    g = Hq // Hkv
+    from oracle import rope as orope
+    for b in range(B):
         L = int(lens[b])
-        rows = oatt.window_rows(L, S, window, rolling)
-        kb = bf16_tensor_to_f64(k[b, kv][torch.from_numpy(rows).cuda()])
-        vb = bf16_tensor_to_f64(v[b, kv][torch.from_numpy(rows).cuda()])
-        qv = qf[b, h][None]
-        from oracle import rope as orope
-        qv = orope.rotate_rows(qv, np.array([L - 1]), cfg.rope())
-        ref = oatt.attend(qv[0], kb, vb, cfg.scale)
-        assert_close(got[b, h], ref, f"{mode} (b={b}, h={h}, L={L})")
+        rows = torch.from_numpy(oatt.window_rows(L, S, window, rolling)).cuda()
+        qv = orope.rotate_rows(qf[b][None], np.array([L - 1]), cfg.rope())[0]
+        for kv in range(Hkv):
+            kb = bf16_tensor_to_f64(k[b, kv][rows])
+            vb = bf16_tensor_to_f64(v[b, kv][rows])
+            ref = oatt.decode_group(qv[kv * g:(kv + 1) * g], kb, vb, len(rows), cfg.scale, None)
+            assert_close(got[b, kv * g:(kv + 1) * g], ref, f"{mode} (b={b}, kv={kv}, L={L})")

@@ -93,30 +93,48 @@ def test_prefill_structured_and_gqa_equals_repeated_mha(m):
     assert torch.equal(o1, o2)
 
 
-def test_prefill_full_size_8k_sampled_rows(m):
-    """T=8192, 32 q heads, 8 kv heads, NTK s=4 base 1e6: sampled output rows."""
+# whole 128-row query tiles: the first, the two either side of row 4095/4096,
+# one in the middle and the last (every head, every row of each)
+FULL_TILES = [0, 31, 32, 45, 63]
+
+
+def _prefill_full(m, window, k2=0):
     import torch
+    from helpers import Guarded
     cfg = PREFILL_8K
     B, T, Hq, Hkv, D = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.D
-    print(f"[case] prefill full size T={T}", flush=True)
-    q = device_randn_bf16((B, Hq, T, D), cfg.seed * 10 + 1)
+    print(f"[case] prefill full size T={T} window={window} q x{2 ** k2}", flush=True)
+    q = device_randn_bf16((B, Hq, T, D), cfg.seed * 10 + 1) * float(2 ** k2)
     k = device_randn_bf16((B, Hkv, T, D), cfg.seed * 10 + 2)
     v = device_randn_bf16((B, Hkv, T, D), cfg.seed * 10 + 3)
-    out = m.gqa_prefill_causal(q, k, v, cfg.scale, rope=cfg.rope())
+    out = Guarded((B, Hq, T, D), torch.bfloat16, seed=3)
+    ws = Guarded((m.gqa_prefill_workspace_size(B, Hkv, T, D, cfg.rope()),), torch.uint8, seed=4)
+    m.gqa_prefill_causal(q, k, v, cfg.scale, rope=cfg.rope(), out=out.view, workspace=ws.view,
+                         window=window)
+    out.check("prefill out")
+    ws.check("prefill workspace")
+    first = out.view.clone()
+    m.gqa_prefill_causal(q, k, v, cfg.scale, rope=cfg.rope(), out=out.view, workspace=ws.view,
+                         window=window)
     torch.cuda.synchronize()
-    got = from_dev(out)
+    assert torch.equal(first, out.view), "two identical calls differ"
+    got = from_dev(out.view)
     assert np.all(np.isfinite(got))
-    rng = np.random.default_rng(3)
-    samples = [(0, 0), (5, 1), (31, T - 1), (17, 4095), (8, 127), (9, 128)]
-    samples += [(int(rng.integers(Hq)), int(rng.integers(T))) for _ in range(10)]
-    kf = bf16_tensor_to_f64(k)
-    vf = bf16_tensor_to_f64(v)
-    qf = bf16_tensor_to_f64(q)
-    for h, i in samples:
-        kv = h // (Hq // Hkv)
-        ref = oatt.prefill_causal(qf[:, h:h + 1, :i + 1], kf[:, kv:kv + 1, :i + 1],
-                                  vf[:, kv:kv + 1, :i + 1], cfg.scale, cfg.rope(), rows=[i])
-        assert_close(got[:, h, i], ref[:, 0, i], f"full-size row (h={h}, i={i})")
+    rows = [r for t in FULL_TILES for r in range(128 * t, 128 * (t + 1))]
+    ref = oatt.prefill_causal(bf16_tensor_to_f64(q), bf16_tensor_to_f64(k), bf16_tensor_to_f64(v),
+                              cfg.scale, cfg.rope(), rows=rows, window=window)
+    assert_close(got[:, :, rows], ref[:, :, rows], f"prefill full size w={window} x{2 ** k2}")
+
+
+def test_prefill_full_size_8k_whole_tiles(m):
+    """T=8192, 32 q heads, 8 kv heads, NTK s=4 base 1e6: every head over five
+    whole query tiles; guarded output and workspace; two calls bitwise equal."""
+    _prefill_full(m, 0)
+
+
+def test_prefill_full_size_8k_peaked(m):
+    """The same with q x 8 (a sharp softmax)."""
+    _prefill_full(m, 0, 3)
 
 
 # ---------------------------------------------------------------------------
@@ -155,28 +173,7 @@ def test_prefill_window_parity(m, case):
     assert_close(got, ref, f"prefill window {case}")
 
 
-def test_prefill_window_full_size_8k_sampled_rows(m):
-    """The 8K prefill with a 4096-token window: sampled rows, including rows
-    whose window starts mid-tile and the first rows that lose early keys."""
-    import torch
-    cfg = PREFILL_8K
-    B, T, Hq, Hkv, D = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.D
-    w = 4096
-    print(f"[case] prefill window full size T={T} w={w}", flush=True)
-    q = device_randn_bf16((B, Hq, T, D), cfg.seed * 10 + 1)
-    k = device_randn_bf16((B, Hkv, T, D), cfg.seed * 10 + 2)
-    v = device_randn_bf16((B, Hkv, T, D), cfg.seed * 10 + 3)
-    out = m.gqa_prefill_causal(q, k, v, cfg.scale, rope=cfg.rope(), window=w)
-    torch.cuda.synchronize()
-    got = from_dev(out)
-    assert np.all(np.isfinite(got))
-    rng = np.random.default_rng(5)
-    samples = [(0, 0), (3, 4095), (4, 4096), (31, T - 1), (7, 5000), (12, 4097 + 63)]
-    samples += [(int(rng.integers(Hq)), int(rng.integers(T))) for _ in range(8)]
-    kf, vf, qf = bf16_tensor_to_f64(k), bf16_tensor_to_f64(v), bf16_tensor_to_f64(q)
-    for h, i in samples:
-        kv = h // (Hq // Hkv)
-        ref = oatt.prefill_causal(qf[:, h:h + 1, :i + 1], kf[:, kv:kv + 1, :i + 1],
-                                  vf[:, kv:kv + 1, :i + 1], cfg.scale, cfg.rope(), rows=[i],
-                                  window=w)
-        assert_close(got[:, h, i], ref[:, 0, i], f"window full-size row (h={h}, i={i})")
+def test_prefill_window_full_size_8k_whole_tiles(m):
+    """The 8K prefill with a 4096-token window over the same whole tiles
+    (tile 32 holds the first rows that lose early keys)."""
+    _prefill_full(m, 4096)

@@ -5,7 +5,7 @@ import math
 import numpy as np
 import pytest
 
-from helpers import assert_close, from_dev, to_dev
+from helpers import Guarded, assert_close, from_dev, to_dev
 from oracle import sparse as osp
 from workloads import (SPARSE_128K, bf16_bits_to_f64, bf16_tensor_to_f64, device_randn_bf16,
                        f32_to_bf16_bits, sparse_inputs_host)
@@ -126,8 +126,17 @@ def test_sparse_full_size_128k(m):
     qi = device_randn_bf16((B, cfg.D_idx), cfg.seed * 10 + 3)
     ki = device_randn_bf16((B, S, cfg.D_idx), cfg.seed * 10 + 4)
     lens = torch.from_numpy(cfg.seq_lens()).cuda()
-    idx, out = m.topk_sparse_decode(q, lat, qi, ki, lens, k, cfg.scale)
+    out_g = Guarded((B, H, cfg.Dv), torch.bfloat16, seed=5)
+    idx_g = Guarded((B, k), torch.int32, seed=6)
+    ws = Guarded((m.topk_sparse_decode_workspace_size(B, H, S, k),), torch.uint8, seed=7)
+    idx, out = m.topk_sparse_decode(q, lat, qi, ki, lens, k, cfg.scale, topk_idx=idx_g.view,
+                                    out=out_g.view, workspace=ws.view)
     torch.cuda.synchronize()
+    first_idx, first_out = idx.clone(), out.clone()
+    m.topk_sparse_decode(q, lat, qi, ki, lens, k, cfg.scale, topk_idx=idx_g.view,
+                         out=out_g.view, workspace=ws.view)
+    torch.cuda.synchronize()
+    assert torch.equal(first_idx, idx) and torch.equal(first_out, out), "two identical calls differ"
     gidx = idx.cpu().numpy()
     got = from_dev(out)
     qf, qif = bf16_tensor_to_f64(q), bf16_tensor_to_f64(qi)
@@ -135,7 +144,9 @@ def test_sparse_full_size_128k(m):
         kib = bf16_tensor_to_f64(ki[b])
         ridx = osp.topk_select(osp.indexer_scores(qif[b], kib, S), k)
         assert np.array_equal(gidx[b], ridx), f"batch {b}: index sets differ"
-        latb = bf16_tensor_to_f64(lat[b])
-        for h in (0, 77, 127):
-            ref = osp.sparse_attention_one(qf[b, h], latb, ridx, cfg.scale, cfg.Dv)
-            assert_close(got[b, h], ref, f"full-size (b={b}, h={h})")
+        rows = bf16_tensor_to_f64(lat[b][torch.from_numpy(ridx.astype(np.int64)).cuda()])
+        ref = osp.sparse_attention_heads(qf[b], rows, np.arange(k), cfg.scale, cfg.Dv)
+        assert_close(got[b], ref, f"full-size every head (b={b})")
+    out_g.check("out")
+    idx_g.check("topk_idx")
+    ws.check("workspace")

@@ -238,10 +238,11 @@ def test_tiny_demo_shapes_and_param_counts():
     parameter counts for n_kv_head = 8, 2, 1."""
     for n_kv, ob, ot, oc, params in golden_rows("tiny_attention_demo.txt"):
         d = tiny_inputs(int(n_kv))
-        y = att.page_attention(d["x"], d["wq"], d["wk"], d["wv"], TINY.n_head, int(n_kv))
+        y = att.projected_attention(d["x"], d["wq"], d["wk"], d["wv"], TINY.n_head, int(n_kv))
         assert y.shape == (int(ob), int(ot), int(oc))
         assert d["wk"].size + d["wv"].size == int(params)
-        # the page function (K/V repeated) equals the oracle's head-mapped attention
+        # the element-by-element definition equals the oracle's vectorised,
+        # head-mapped causal attention on the projected and split heads
         x = d["x"].astype(np.float64)
         hd = TINY.head_dim
 
@@ -251,6 +252,23 @@ def test_tiny_demo_shapes_and_param_counts():
         o2 = att.causal_attention(split(d["wq"], 8), split(d["wk"], int(n_kv)),
                                   split(d["wv"], int(n_kv)), 1 / math.sqrt(hd))
         assert np.allclose(o2.transpose(0, 2, 1, 3).reshape(2, 10, 64), y, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_group_equals_per_head_decode_and_sdpa():
+    """decode_group (the g heads of one kv head at once) equals decode_one per
+    head, and torch's scaled_dot_product_attention (CPU float64) on the
+    rotated query rows -- an independent library routine."""
+    n, L, D = 8, 57, 32
+    qr, K, V = _rand((n, D), 81), _rand((70, D), 82), _rand((70, D), 83)
+    p = rope_settings(ROPE_YARN, base=5e5, factor=4.0, original_max_position=16)
+    got = att.decode_group(qr, K, V, L, 0.2, p)
+    for h in range(n):
+        assert np.allclose(got[h], att.decode_one(qr[h], K, V, L, 0.2, p), rtol=1e-13, atol=1e-15)
+    qrot = rope.rotate_rows(qr[None], np.array([L - 1]), p)[0]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qrot)[None, :, None], torch.from_numpy(K[:L])[None, None].expand(1, n, L, D),
+        torch.from_numpy(V[:L])[None, None].expand(1, n, L, D), scale=0.2).numpy()[0, :, 0]
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
 
 
 def test_prefill_rope_is_relative():

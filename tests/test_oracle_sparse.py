@@ -183,3 +183,24 @@ def test_topk_select_exact_matches_sorting():
     v = rng.standard_normal(1000)
     sel = sparse.topk_select_exact(v, 100)
     assert set(sel) == set(np.argsort(-v)[:100])
+
+
+def test_sparse_attention_heads_equals_one_head_at_a_time_and_sdpa():
+    """The grouped form equals sparse_attention_one per head and torch's
+    scaled_dot_product_attention (float64, CPU) on the selected rows, with
+    the first Dv columns as values."""
+    import torch
+    rng = np.random.default_rng(90)
+    H, L, Dqk, Dv = 6, 200, 40, 24
+    q = rng.standard_normal((H, Dqk))
+    lat = rng.standard_normal((L, Dqk))
+    idx = np.array(sorted(rng.choice(L, 50, replace=False)) + [-1, -1])
+    got = sparse.sparse_attention_heads(q, lat, idx, 0.3, Dv)
+    for h in range(H):
+        assert np.allclose(got[h], sparse.sparse_attention_one(q[h], lat, idx, 0.3, Dv),
+                           rtol=1e-13, atol=1e-15)
+    rows = torch.from_numpy(lat[idx[idx >= 0]])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, :, None], rows[None, None].expand(1, H, -1, -1),
+        rows[None, None, :, :Dv].expand(1, H, -1, -1), scale=0.3).numpy()[0, :, 0]
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
