@@ -53,11 +53,32 @@ def kv_head_of(h: int, n_head: int, n_kv_head: int) -> int:
     return h // (n_head // n_kv_head)
 
 
-def causal_attention(q, k, v, scale: float, rows=None, heads=None, window: int = 0) -> np.ndarray:
+def visible_keys(i: int, window: int = 0, sinks: int = 0) -> np.ndarray:
+    """Key positions query i attends to: 0..i (causal); with a sliding window
+    w > 0 only i-w+1..i; with s sink tokens beside a window also 0..s-1 (each
+    position once).
+
+    [transformer架构] §2.5.1 (the band mask); [attention] "Slide Window
+    Attention (SWA)", 修复方案 1. StreamingLLM: the effective context is the
+    first s tokens followed by the sliding window; [transformer架构] §2.5.4
+    (StreamingLLM's mask: the band plus the first k columns kept).  Reading:
+    the window is the band of §2.5.1 (w keys ending at i), so s = 0 is the
+    plain sliding window.
+    """
+    if not window:
+        return np.arange(i + 1)
+    lo = max(0, i - window + 1)
+    head = np.arange(min(sinks, lo))
+    return np.concatenate([head, np.arange(lo, i + 1)]).astype(np.int64)
+
+
+def causal_attention(q, k, v, scale: float, rows=None, heads=None, window: int = 0,
+                     sinks: int = 0) -> np.ndarray:
     """Causal GQA attention on already-rotated inputs.
 
     q: [B, Hq, T, D]; k: [B, Hkv, T, D]; v: [B, Hkv, T, Dv].  Row i attends to
-    keys 0..i, or with a sliding window w > 0 to keys i-w+1..i.
+    keys 0..i, or with a sliding window w > 0 to keys i-w+1..i, plus keys
+    0..s-1 with s sink tokens (:func:`visible_keys`).
     ``rows``/``heads`` restrict the computation to a sample; the result then
     holds NaN elsewhere.
 
@@ -75,15 +96,15 @@ def causal_attention(q, k, v, scale: float, rows=None, heads=None, window: int =
         for h in heads:
             kv = kv_head_of(h, Hq, Hkv)
             for i in rows:
-                j0 = max(0, i - window + 1) if window else 0
-                out[b, h, i] = attend(q[b, h, i], k[b, kv, j0:i + 1], v[b, kv, j0:i + 1], scale)
+                js = visible_keys(i, window, sinks)
+                out[b, h, i] = attend(q[b, h, i], k[b, kv, js], v[b, kv, js], scale)
     return out
 
 
 def prefill_causal(q, k, v, scale: float, rope_p: dict, rows=None, heads=None,
-                   window: int = 0) -> np.ndarray:
+                   window: int = 0, sinks: int = 0) -> np.ndarray:
     """RoPE on Q and K at positions 0..T-1, then causal GQA attention (with a
-    sliding window when window > 0).
+    sliding window when window > 0, and sink tokens beside it when sinks > 0).
 
     [transformer架构] §1.1 (rotate Q and K, not V) and §1.2 (scalings);
     attention as in :func:`causal_attention`.
@@ -96,7 +117,7 @@ def prefill_causal(q, k, v, scale: float, rope_p: dict, rows=None, heads=None,
     # rotate along the position axis: move T first
     qr = _rope.rotate_rows(q.transpose(2, 0, 1, 3), pos, rope_p).transpose(1, 2, 0, 3)
     kr = _rope.rotate_rows(k.transpose(2, 0, 1, 3), pos, rope_p).transpose(1, 2, 0, 3)
-    return causal_attention(qr, kr, v, scale, rows=rows, heads=heads, window=window)
+    return causal_attention(qr, kr, v, scale, rows=rows, heads=heads, window=window, sinks=sinks)
 
 
 def decode_one(q_vec, K, V, seq_len: int, scale: float, rope_p) -> np.ndarray:
@@ -185,27 +206,45 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale: float, rop
     return decode(q, kc, vc, seq_lens, scale, rope_p, pairs=pairs), kc, vc
 
 
-def window_rows(seq_len: int, S_max: int, window: int = 0, rolling: bool = False):
+def sink_slot(t: int, S_max: int, sinks: int = 0) -> int:
+    """Slot of position t in a rolling buffer of S_max slots whose first
+    `sinks` slots keep positions 0..sinks-1 for good: later positions cycle
+    through the other S_max - sinks slots, overwriting the oldest.
+
+    [transformer架构] §2.5.2 (the rolling buffer, position t in slot t mod w)
+    with [attention] "Slide Window Attention (SWA)", 修复方案 1 (StreamingLLM
+    keeps the sink tokens' KV cache); sinks = 0 is slot t mod S_max.
+    """
+    t = int(t)
+    return t if t < sinks else sinks + (t - sinks) % (S_max - sinks)
+
+
+def window_rows(seq_len: int, S_max: int, window: int = 0, rolling: bool = False,
+                sinks: int = 0):
     """Cache rows the new token (position seq_len-1) attends to.
 
     Sliding window ([transformer架构] §2.5.1): query i sees keys j with
-    i - w + 1 <= j <= i.  Linear cache: position p is row p (window 0 = no
-    window).  Rolling buffer ([transformer架构] §2.5.2): position t lives in
-    slot t mod S_max, so the buffer holds the last S_max positions and the
-    window is the buffer (window must be 0).
+    i - w + 1 <= j <= i; with s sink tokens also j < s (:func:`visible_keys`).
+    Linear cache: position p is row p (window 0 = no window).  Rolling
+    buffer ([transformer架构] §2.5.2): position t lives in slot
+    :func:`sink_slot`, so the buffer holds the sinks and the last
+    S_max - s positions, and the window is the buffer (window must be 0).
     """
     L = int(seq_len)
     if rolling:
         if window:
             raise ValueError("a rolling buffer's window is its size")
-        positions = np.arange(max(0, L - S_max), L)
-        return positions % S_max
-    w = int(window) if window else L
-    return np.arange(max(0, L - w), L)
+        if not 0 <= sinks < S_max:
+            raise ValueError("the sinks must leave a ring of at least one slot")
+        ring = S_max - sinks
+        positions = np.concatenate([np.arange(min(sinks, L)),
+                                    np.arange(max(sinks, L - ring), L)]).astype(np.int64)
+        return np.array([sink_slot(t, S_max, sinks) for t in positions], dtype=np.int64)
+    return visible_keys(L - 1, int(window), sinks)
 
 
 def decode_window(q, k_cache, v_cache, seq_lens, scale: float, rope_p, window: int = 0,
-                  rolling: bool = False, pairs=None) -> np.ndarray:
+                  rolling: bool = False, pairs=None, sinks: int = 0) -> np.ndarray:
     """Single-token decode over the rows of :func:`window_rows`; q rotated at
     its absolute position seq_lens[b]-1 (keys are cached after RoPE, so a
     rolling buffer needs no re-rotation)."""
@@ -217,7 +256,7 @@ def decode_window(q, k_cache, v_cache, seq_lens, scale: float, rope_p, window: i
     for b, h in pairs:
         kv = kv_head_of(h, Hq, Hkv)
         L = int(seq_lens[b])
-        rows = window_rows(L, S_max, window, rolling)
+        rows = window_rows(L, S_max, window, rolling, sinks)
         qv = np.asarray(q[b, h], dtype=np.float64)[None, :]
         if rope_p is not None:
             qv = _rope.rotate_rows(qv, np.array([L - 1]), _rope.with_length(rope_p, L))
@@ -226,17 +265,18 @@ def decode_window(q, k_cache, v_cache, seq_lens, scale: float, rope_p, window: i
     return out
 
 
-def append_rows_window(k_cache, v_cache, k_new, v_new, seq_lens, rope_p, rolling: bool = False):
+def append_rows_window(k_cache, v_cache, k_new, v_new, seq_lens, rope_p, rolling: bool = False,
+                       sinks: int = 0):
     """:func:`append_rows` for either cache: the new token (position
     seq_lens[b]-1) goes to row seq_lens[b]-1 of a linear cache, or to slot
-    (seq_lens[b]-1) mod S_max of a rolling buffer ([transformer架构] §2.5.2:
-    the oldest entry is overwritten)."""
+    :func:`sink_slot` of a rolling buffer ([transformer架构] §2.5.2: the
+    oldest entry is overwritten; sink slots never are)."""
     kc = np.array(k_cache, dtype=np.float64, copy=True)
     vc = np.array(v_cache, dtype=np.float64, copy=True)
     S_max = kc.shape[2]
     for b in range(kc.shape[0]):
         pos = int(seq_lens[b]) - 1
-        row = pos % S_max if rolling else pos
+        row = sink_slot(pos, S_max, sinks) if rolling else pos
         kr = np.asarray(k_new[b], dtype=np.float64)
         if rope_p is not None:
             kr = _rope.rotate_rows(kr[None], np.array([pos]), _rope.with_length(rope_p, pos + 1))[0]

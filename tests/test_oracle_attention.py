@@ -318,3 +318,81 @@ def test_dynamic_ntk_uses_each_calls_length():
     pp = att.prefill_causal(qp[:, :, :6], kp[:, :, :6], vp[:, :, :6], 0.3,
                             rope_settings(ROPE_PLAIN, base=1e4))
     assert np.array_equal(ps, pp)
+
+
+def _band_sink_mask(T, w, s):
+    """The StreamingLLM mask written from its description: row i keeps the
+    band i-w+1 <= j <= i ([transformer架构] §2.5.1) and the first s columns
+    (§2.5.4), never a column past the diagonal."""
+    m = np.zeros((T, T), dtype=bool)
+    for i in range(T):
+        for j in range(T):
+            m[i, j] = j <= i and (i - w + 1 <= j or j < s)
+    return m
+
+
+@pytest.mark.parametrize("w,s", [(5, 2), (1, 1), (8, 3), (3, 9)])
+def test_sink_window_equals_sdpa_with_the_page_mask(w, s):
+    """Prefill with s sink tokens and a window of w equals torch's
+    scaled_dot_product_attention (CPU, float64) given the band-plus-first-s-
+    columns boolean mask -- an independent routine fed the mask itself."""
+    B, Hq, Hkv, T, D = 1, 4, 2, 23, 16
+    q, k, v = _rand((B, Hq, T, D), 91), _rand((B, Hkv, T, D), 92), _rand((B, Hkv, T, D), 93)
+    ours = att.causal_attention(q, k, v, 0.3, window=w, sinks=s)
+    mask = torch.from_numpy(_band_sink_mask(T, w, s))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask, scale=0.3,
+        enable_gqa=True).numpy()
+    assert np.allclose(ours, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_sink_window_reductions_and_closed_form():
+    """s = 0 is the plain sliding window; s + w > i sees every earlier key
+    (plain causal); w = 1, s = 1 leaves two keys, 0 and i: the logistic of
+    their score gap."""
+    B, Hq, Hkv, T, D = 1, 2, 1, 30, 8
+    q, k, v = _rand((B, Hq, T, D), 94), _rand((B, Hkv, T, D), 95), _rand((B, Hkv, T, D), 96)
+    assert np.array_equal(att.causal_attention(q, k, v, 0.4, window=6, sinks=0),
+                          att.causal_attention(q, k, v, 0.4, window=6))
+    full = att.causal_attention(q, k, v, 0.4)
+    big = att.causal_attention(q, k, v, 0.4, window=20, sinks=10)
+    assert np.allclose(big, full, rtol=1e-14, atol=1e-15)
+    two = att.causal_attention(q, k, v, 0.4, window=1, sinks=1)
+    for i in range(1, T):
+        w0 = 1.0 / (1.0 + math.exp(0.4 * (q[0, 0, i] @ k[0, 0, i] - q[0, 0, i] @ k[0, 0, 0])))
+        assert np.allclose(two[0, 0, i], w0 * v[0, 0, 0] + (1 - w0) * v[0, 0, i], rtol=1e-12)
+    assert np.allclose(two[0, :, 0], v[0, 0, 0][None])
+    assert list(att.visible_keys(9, 3, 2)) == [0, 1, 7, 8, 9]
+    assert list(att.visible_keys(4, 3, 4)) == [0, 1, 2, 3, 4]
+
+
+def test_sink_decode_equals_prefill_rows_and_rolling_sinks():
+    """Decode with sinks over a cache of rope(K) reproduces prefill rows; a
+    rolling buffer whose first s slots keep the sinks equals the linear cache
+    with sinks and a window of S_max - s, and its written slot skips the
+    sink slots."""
+    B, Hq, Hkv, T, D = 1, 4, 2, 40, 16
+    q, k, v = _rand((B, Hq, T, D), 97), _rand((B, Hkv, T, D), 98), _rand((B, Hkv, T, D), 99)
+    p = rope_settings(ROPE_PLAIN, base=1e4)
+    w, s = 7, 3
+    kc = rope.rotate_rows(k.transpose(2, 0, 1, 3), np.arange(T), p).transpose(1, 2, 0, 3)
+    for L in (2, 5, 11, 40):
+        pre = att.prefill_causal(q, k, v, 0.3, p, rows=[L - 1], window=w, sinks=s)
+        dec = att.decode_window(q[:, :, L - 1], kc, v, np.array([L]), 0.3, p, window=w, sinks=s)
+        assert np.allclose(dec, pre[:, :, L - 1], rtol=1e-12, atol=1e-13)
+    # rolling buffer of S_max = 10 slots, 3 of them sinks: fill it token by token
+    S_max = 10
+    rk = np.zeros((B, Hkv, S_max, D))
+    rv = np.zeros((B, Hkv, S_max, D))
+    for t in range(T):
+        rk, rv = att.append_rows_window(rk, rv, k[:, :, t], v[:, :, t], np.array([t + 1]), p,
+                                        rolling=True, sinks=s)
+        slot = att.sink_slot(t, S_max, s)
+        assert slot == (t if t < s else s + (t - s) % (S_max - s))
+        dec_r = att.decode_window(q[:, :, t], rk, rv, np.array([t + 1]), 0.3, p, rolling=True,
+                                  sinks=s)
+        dec_l = att.decode_window(q[:, :, t], kc, v, np.array([t + 1]), 0.3, p, window=S_max - s,
+                                  sinks=s)
+        assert np.allclose(dec_r, dec_l, rtol=1e-12, atol=1e-13)
+    for j in range(s):   # the sink slots still hold positions 0..s-1
+        assert np.allclose(rk[:, :, j], kc[:, :, j]) and np.array_equal(rv[:, :, j], v[:, :, j])
