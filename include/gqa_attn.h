@@ -232,6 +232,29 @@ gqa_status gqa_decode_window(const void* q, const void* k_new, const void* v_new
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gqa_decode_sink_window -- gqa_decode_window with StreamingLLM sink tokens
+ * ([attention] "Slide Window Attention (SWA)", 修复方案 1. StreamingLLM: the
+ * effective context is the first s tokens followed by the sliding window;
+ * [transformer架构] §2.5.4: the band mask with the first k columns kept).
+ * Linear cache (rolling = 0): the new token at position L-1 attends to rows
+ * 0 .. min(sinks, lo)-1 and lo .. L-1, lo = max(0, L-window); window 0 means
+ * no window (every row; sinks are then moot).  Rolling buffer (rolling = 1,
+ * window 0, 0 <= sinks < S_max): slots 0 .. sinks-1 keep positions
+ * 0 .. sinks-1 for good and position t >= sinks lives in slot
+ * sinks + (t - sinks) mod (S_max - sinks); the new token attends to every
+ * filled slot (min(L, S_max) of them) and the fused write (k_new, v_new)
+ * goes to its position's slot.  sinks = 0 is exactly gqa_decode_window.
+ *   sinks  >= 0 (< S_max when rolling = 1)
+ * Other arguments, limits and errors as gqa_decode_window.
+ */
+gqa_status gqa_decode_sink_window(const void* q, const void* k_new, const void* v_new,
+                                  void* k_cache, void* v_cache, const int32_t* seq_lens,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S_max,
+                                  int32_t sinks, int32_t window, int32_t rolling, float scale,
+                                  const gqa_rope_params* q_rope, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gqa_prefill_causal -- causal GQA attention over a whole prompt
  * ([注意力变体与MoE] "MQA 与 GQA", attention(): scores q k^T / sqrt(hd) with the
  * strict upper triangle masked to -inf, softmax, weighted sum of V):
@@ -244,13 +267,19 @@ gqa_status gqa_decode_window(const void* q, const void* k_new, const void* v_new
  *   rope NULL or GQA_ROPE_NONE: no rotation
  *   out  bf16 [B][Hq][T][D]
  *   workspace >= gqa_prefill_workspace_size(B, Hkv, T, D, rope) bytes, device,
- *             256-byte aligned (it receives fp16 copies of the rotated K and of
- *             V, tiled for the matrix cores); contents on entry do not matter.
- * Supported: D in {8, 16, 32, 64, 128}; T >= 1; Hq % Hkv == 0; B*Hq <= 65535.
- * Precision: rotated Q (times scale*log2 e) and K, the probabilities and V
- * enter the matrix cores as fp16 with fp32 accumulation, so |v|, |k| and the
- * rotated, scaled |q| must stay below 65504 (fp16 range); larger inputs
- * overflow.
+ *             256-byte aligned (it receives the rotated K as hi and lo bf16
+ *             rows and an fp16 copy of V, tiled for the matrix cores);
+ *             contents on entry do not matter.
+ * Supported: D in {8, 16, 32, 64, 128}; T >= 1; Hq % Hkv == 0; B*Hq <= 65535;
+ * T * D * 2 < 2^31.
+ * Precision: the rotated Q (times scale*log2 e) and the rotated K enter the
+ * matrix cores as hi + lo bf16 terms and each score is the sum of the three
+ * products hi.hi + hi.lo + lo.hi (about 2^-17 relative, so a sharp softmax
+ * keeps the output within 2e-3 + 1e-2 |ref|); the probabilities and V enter
+ * the PV product as fp16 with fp32 accumulation, so |v| must stay below
+ * 65504 and V values below 2^-14 in magnitude lose bits as fp16 subnormals
+ * (an absolute error under 2^-25 each).  gqa_prefill_fp16 trades the score
+ * precision for speed.
  */
 size_t gqa_prefill_workspace_size(int32_t B, int32_t Hkv, int32_t T, int32_t D,
                                   const gqa_rope_params* rope);
@@ -273,6 +302,40 @@ gqa_status gqa_prefill_window(const void* q, const void* k, const void* v,
                               int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
                               int32_t window, float scale, const gqa_rope_params* rope,
                               void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gqa_prefill_sink_window -- gqa_prefill_window with StreamingLLM sink tokens
+ * ([attention] "Slide Window Attention (SWA)", 修复方案 1; [transformer架构]
+ * §2.5.4: the band plus the first k columns): row i attends to keys
+ * 0 .. min(sinks, lo)-1 and lo .. i, lo = max(0, i-window+1), so
+ *     out_i = sum_{j <= i, j < sinks or j > i-window} softmax_j(scale * q~_i . k~_j) v_j
+ * sinks >= 0, window >= 0; sinks = 0 is gqa_prefill_window, and window 0 (or
+ * >= T) is gqa_prefill_causal whatever sinks is.  Key tiles holding neither
+ * sinks nor band keys are not read.  Arguments, workspace, limits, precision
+ * and errors as gqa_prefill_causal.
+ */
+gqa_status gqa_prefill_sink_window(const void* q, const void* k, const void* v,
+                                   int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                                   int32_t sinks, int32_t window, float scale,
+                                   const gqa_rope_params* rope, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * gqa_prefill_fp16 -- gqa_prefill_sink_window with one-term fp16 scores: the
+ * rotated, scaled Q and the rotated K are rounded to fp16 (11-bit
+ * significand) and each score is one product, about half the matrix-core
+ * work of the default.  Each base-2 logit then carries an error of up to
+ * about 2^-10 * scale * log2(e) * |q~| |k~| (|.| the Euclidean norm of the
+ * rotated vectors): within 2e-3 + 1e-2 |ref| while the scores spread over
+ * about one unit (q, k ~ N(0,1) with scale 1/sqrt(d)), not for a sharp
+ * softmax.  |v|, |k| and the rotated, scaled |q| must stay below 65504.
+ * Arguments, workspace, masks and errors as gqa_prefill_sink_window.
+ */
+gqa_status gqa_prefill_fp16(const void* q, const void* k, const void* v,
+                            int32_t B, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                            int32_t sinks, int32_t window, float scale,
+                            const gqa_rope_params* rope, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * topk_sparse_decode -- DSA-style sparse decode over an MLA latent cache,

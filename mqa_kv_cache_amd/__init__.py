@@ -28,9 +28,10 @@ ROPE_NONE, ROPE_PLAIN, ROPE_PI, ROPE_NTK, ROPE_YARN, ROPE_DYNAMIC_NTK = 0, 1, 2,
 
 EXPORTED = [
     "rope_apply", "gqa_decode", "gqa_decode_parts", "gqa_decode_append", "gqa_decode_window",
-    "gqa_decode_workspace_size",
+    "gqa_decode_sink_window", "gqa_decode_workspace_size",
     "gqa_decode_workspace_size_parts", "gqa_decode_partial", "gqa_decode_combine",
-    "gqa_prefill_causal", "gqa_prefill_window", "gqa_prefill_workspace_size",
+    "gqa_prefill_causal", "gqa_prefill_window", "gqa_prefill_sink_window", "gqa_prefill_fp16",
+    "gqa_prefill_workspace_size",
     "topk_sparse_decode", "topk_sparse_decode_workspace_size", "topk_sparse_decode_weighted",
     "qsa_sparse_decode", "qsa_sparse_decode_workspace_size",
     "mla_decode",
@@ -88,6 +89,11 @@ _lib.gqa_decode_window.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _
                                    _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                    _c_int32, ctypes.c_float, _rope_p, _c_void_p, _c_void_p,
                                    _c_size_t, _c_void_p]
+_lib.gqa_decode_sink_window.restype = _c_int32
+_lib.gqa_decode_sink_window.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                        _c_void_p, _c_int32, _c_int32, _c_int32, _c_int32,
+                                        _c_int32, _c_int32, _c_int32, _c_int32, ctypes.c_float,
+                                        _rope_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]
 _lib.gqa_decode_parts.restype = _c_int32
 _lib.gqa_decode_parts.argtypes = _lib.gqa_decode.argtypes[:-1] + [_c_int32, _c_void_p]
 _lib.gqa_decode_partial.restype = _c_int32
@@ -106,6 +112,11 @@ _lib.gqa_prefill_causal.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_int32, _
 _lib.gqa_prefill_window.restype = _c_int32
 _lib.gqa_prefill_window.argtypes = (_lib.gqa_prefill_causal.argtypes[:8] + [_c_int32]
                                     + _lib.gqa_prefill_causal.argtypes[8:])
+_lib.gqa_prefill_sink_window.restype = _c_int32
+_lib.gqa_prefill_sink_window.argtypes = (_lib.gqa_prefill_causal.argtypes[:8] + [_c_int32, _c_int32]
+                                         + _lib.gqa_prefill_causal.argtypes[8:])
+_lib.gqa_prefill_fp16.restype = _c_int32
+_lib.gqa_prefill_fp16.argtypes = _lib.gqa_prefill_sink_window.argtypes
 _lib.topk_sparse_decode_workspace_size.restype = _c_size_t
 _lib.topk_sparse_decode_workspace_size.argtypes = [_c_int32] * 4
 _lib.topk_sparse_decode.restype = _c_int32
@@ -284,11 +295,13 @@ def gqa_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale: float,
 
 def gqa_decode_window(q, k_cache, v_cache, seq_lens, scale: float, window: int = 0,
                       rolling: bool = False, k_new=None, v_new=None, q_rope=None, out=None,
-                      workspace=None, stream=None) -> torch.Tensor:
+                      workspace=None, stream=None, sinks: int = 0) -> torch.Tensor:
     """gqa_decode over the last `window` positions of a linear cache, or over a
     rolling buffer (rolling=True, window 0: position t in slot t mod S_max),
-    optionally writing the new token's k_new/v_new [B,Hkv,D] first.  Returns
-    out [B,Hq,D] bf16."""
+    optionally writing the new token's k_new/v_new [B,Hkv,D] first.  sinks > 0
+    (gqa_decode_sink_window) also keeps the first `sinks` positions visible
+    (linear cache) or in the buffer's first slots (rolling).  Returns out
+    [B,Hq,D] bf16."""
     B, Hq, D = q.shape
     _, Hkv, S_max, _ = k_cache.shape
     _shape(k_cache, (B, Hkv, S_max, D), "k_cache")
@@ -312,8 +325,17 @@ def gqa_decode_window(q, k_cache, v_cache, seq_lens, scale: float, window: int =
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace", dtype=torch.uint8)
-    st = _lib.gqa_decode_window(q.data_ptr(), k_new.data_ptr() if k_new is not None else None,
-                                v_new.data_ptr() if v_new is not None else None, k_cache.data_ptr(),
+    kn = k_new.data_ptr() if k_new is not None else None
+    vn = v_new.data_ptr() if v_new is not None else None
+    if sinks:
+        st = _lib.gqa_decode_sink_window(q.data_ptr(), kn, vn, k_cache.data_ptr(),
+                                         v_cache.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D,
+                                         S_max, int(sinks), int(window), int(bool(rolling)),
+                                         float(scale), rope_params(q_rope), out.data_ptr(),
+                                         workspace.data_ptr(), workspace.numel(), _stream(stream))
+        _check(st, "gqa_decode_sink_window")
+        return out
+    st = _lib.gqa_decode_window(q.data_ptr(), kn, vn, k_cache.data_ptr(),
                                 v_cache.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, S_max,
                                 int(window), int(bool(rolling)), float(scale), rope_params(q_rope),
                                 out.data_ptr(), workspace.data_ptr(), workspace.numel(),
@@ -360,9 +382,12 @@ def gqa_prefill_workspace_size(B, Hkv, T, D, rope=None) -> int:
 
 
 def gqa_prefill_causal(q, k, v, scale: float, rope=None, out=None, workspace=None,
-                       stream=None, window: int = 0) -> torch.Tensor:
+                       stream=None, window: int = 0, sinks: int = 0,
+                       fp16_scores: bool = False) -> torch.Tensor:
     """q [B,Hq,T,D], k/v [B,Hkv,T,D] bf16 (pre-RoPE).  Returns out [B,Hq,T,D].
-    window > 0: sliding window (row i sees keys i-window+1 .. i)."""
+    window > 0: sliding window (row i sees keys i-window+1 .. i); sinks > 0
+    keeps keys 0 .. sinks-1 visible beside it (gqa_prefill_sink_window);
+    fp16_scores: one-product fp16 scores (gqa_prefill_fp16)."""
     B, Hq, T, D = q.shape
     Hkv = k.shape[1]
     _shape(k, (B, Hkv, T, D), "k")
@@ -377,6 +402,13 @@ def gqa_prefill_causal(q, k, v, scale: float, rope=None, out=None, workspace=Non
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace", dtype=torch.uint8)
+    if fp16_scores or sinks:
+        fn = _lib.gqa_prefill_fp16 if fp16_scores else _lib.gqa_prefill_sink_window
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, Hq, Hkv, D, int(sinks),
+                int(window), float(scale), rope_params(rope), out.data_ptr(),
+                workspace.data_ptr(), workspace.numel(), _stream(stream))
+        _check(st, "gqa_prefill_fp16" if fp16_scores else "gqa_prefill_sink_window")
+        return out
     if window:
         st = _lib.gqa_prefill_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, Hq, Hkv, D,
                                      int(window), float(scale), rope_params(rope), out.data_ptr(),

@@ -208,16 +208,17 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                             workspace, workspace_bytes, 0, stream);
 }
 
-gqa_status gqa_decode_window(const void* q, const void* k_new, const void* v_new, void* k_cache,
-                             void* v_cache, const int32_t* seq_lens, int32_t B, int32_t Hq,
-                             int32_t Hkv, int32_t D, int32_t S_max, int32_t window, int32_t rolling,
-                             float scale, const gqa_rope_params* q_rope, void* out, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+gqa_status gqa_decode_sink_window(const void* q, const void* k_new, const void* v_new,
+                                  void* k_cache, void* v_cache, const int32_t* seq_lens, int32_t B,
+                                  int32_t Hq, int32_t Hkv, int32_t D, int32_t S_max, int32_t sinks,
+                                  int32_t window, int32_t rolling, float scale,
+                                  const gqa_rope_params* q_rope, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
     gqa_status st = check_decode_shape(B, Hq, Hkv, D, S_max);
     if (st != GQA_OK) return st;
-    if (!std::isfinite(scale) || window < 0 || (rolling != 0 && rolling != 1))
+    if (!std::isfinite(scale) || window < 0 || sinks < 0 || (rolling != 0 && rolling != 1))
         return GQA_ERR_INVALID_ARGUMENT;
-    if (rolling && window != 0) return GQA_ERR_INVALID_ARGUMENT;
+    if (rolling && (window != 0 || sinks >= S_max)) return GQA_ERR_INVALID_ARGUMENT;
     if ((k_new == nullptr) != (v_new == nullptr)) return GQA_ERR_INVALID_ARGUMENT;
     if (!q || !k_cache || !v_cache || !seq_lens || !workspace || !out)
         return GQA_ERR_INVALID_ARGUMENT;
@@ -230,12 +231,23 @@ gqa_status gqa_decode_window(const void* q, const void* k_new, const void* v_new
     if (st != GQA_OK) return st;
     const DecodeLayout lay = decode_layout(B, Hq, Hkv, D, kDecodeDefaultParts);
     if (workspace_bytes < lay.total) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    if (!rolling && window == 0) sinks = 0;   // no band: every row is attended already
     st = from_hip(launch_gqa_decode_partial(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max,
                                             scale, rd, workspace, lay, (hipStream_t)stream, k_new,
-                                            v_new, window, rolling));
+                                            v_new, window, rolling, sinks));
     if (st != GQA_OK) return st;
     return from_hip(launch_gqa_decode_combine(seq_lens, B, Hq, Hkv, D, S_max, workspace, lay, out,
-                                              (hipStream_t)stream, window, rolling));
+                                              (hipStream_t)stream, window, rolling, sinks));
+}
+
+gqa_status gqa_decode_window(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                             void* v_cache, const int32_t* seq_lens, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t D, int32_t S_max, int32_t window, int32_t rolling,
+                             float scale, const gqa_rope_params* q_rope, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    return gqa_decode_sink_window(q, k_new, v_new, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max,
+                                  0, window, rolling, scale, q_rope, out, workspace,
+                                  workspace_bytes, stream);
 }
 
 gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
@@ -262,16 +274,18 @@ size_t gqa_prefill_workspace_size(int32_t B, int32_t Hkv, int32_t T, int32_t D,
     if (B < 1 || Hkv < 1 || T < 1 || D < 1) return 0;
     RopeDev rd;
     if (rope_prepare(rope, D, &rd, T) != GQA_OK) return 0;
-    return 2 * prefill_prep_bytes(B, Hkv, T, D);
+    return 3 * prefill_prep_bytes(B, Hkv, T, D);
 }
 
-gqa_status gqa_prefill_window(const void* q, const void* k, const void* v, int32_t B, int32_t T,
-                              int32_t Hq, int32_t Hkv, int32_t D, int32_t window, float scale,
-                              const gqa_rope_params* rope, void* out, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+// Every prefill entry point: validation, then the pre-pass and main kernel.
+static gqa_status prefill_common(const void* q, const void* k, const void* v, int32_t B, int32_t T,
+                                 int32_t Hq, int32_t Hkv, int32_t D, int32_t sinks, int32_t window,
+                                 float scale, const gqa_rope_params* rope, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 int32_t fp16_scores) {
     gqa_status st = check_prefill_shape(B, T, Hq, Hkv, D);
     if (st != GQA_OK) return st;
-    if (!std::isfinite(scale) || window < 0) return GQA_ERR_INVALID_ARGUMENT;
+    if (!std::isfinite(scale) || window < 0 || sinks < 0) return GQA_ERR_INVALID_ARGUMENT;
     if (!q || !k || !v || !out) return GQA_ERR_INVALID_ARGUMENT;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return GQA_ERR_INVALID_ARGUMENT;
@@ -279,17 +293,49 @@ gqa_status gqa_prefill_window(const void* q, const void* k, const void* v, int32
     st = rope_prepare(rope, D, &rd, T);
     if (st != GQA_OK) return st;
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GQA_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < 2 * prefill_prep_bytes(B, Hkv, T, D)) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    if (workspace_bytes < 3 * prefill_prep_bytes(B, Hkv, T, D)) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    // a window of T or more keys (or none) is the causal mask, and sinks only
+    // matter beside a band that leaves keys out
+    if (window >= T) window = 0;
+    if (window == 0 || sinks >= T) {
+        window = 0;
+        sinks = 0;
+    }
     return from_hip(launch_gqa_prefill(q, k, v, B, T, Hq, Hkv, D, scale, rd, out, workspace,
-                                       (hipStream_t)stream, window >= T ? 0 : window));
+                                       (hipStream_t)stream, window, sinks, fp16_scores));
+}
+
+gqa_status gqa_prefill_window(const void* q, const void* k, const void* v, int32_t B, int32_t T,
+                              int32_t Hq, int32_t Hkv, int32_t D, int32_t window, float scale,
+                              const gqa_rope_params* rope, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    return prefill_common(q, k, v, B, T, Hq, Hkv, D, 0, window, scale, rope, out, workspace,
+                          workspace_bytes, stream, 0);
 }
 
 gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, int32_t B, int32_t T,
                               int32_t Hq, int32_t Hkv, int32_t D, float scale,
                               const gqa_rope_params* rope, void* out, void* workspace,
                               size_t workspace_bytes, void* stream) {
-    return gqa_prefill_window(q, k, v, B, T, Hq, Hkv, D, 0, scale, rope, out, workspace,
-                              workspace_bytes, stream);
+    return prefill_common(q, k, v, B, T, Hq, Hkv, D, 0, 0, scale, rope, out, workspace,
+                          workspace_bytes, stream, 0);
+}
+
+gqa_status gqa_prefill_sink_window(const void* q, const void* k, const void* v, int32_t B,
+                                   int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t sinks,
+                                   int32_t window, float scale, const gqa_rope_params* rope,
+                                   void* out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    return prefill_common(q, k, v, B, T, Hq, Hkv, D, sinks, window, scale, rope, out, workspace,
+                          workspace_bytes, stream, 0);
+}
+
+gqa_status gqa_prefill_fp16(const void* q, const void* k, const void* v, int32_t B, int32_t T,
+                            int32_t Hq, int32_t Hkv, int32_t D, int32_t sinks, int32_t window,
+                            float scale, const gqa_rope_params* rope, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    return prefill_common(q, k, v, B, T, Hq, Hkv, D, sinks, window, scale, rope, out, workspace,
+                          workspace_bytes, stream, 1);
 }
 
 static gqa_status check_sparse_shape(int32_t B, int32_t H, int32_t Dqk, int32_t Dv, int32_t D_idx,

@@ -141,17 +141,24 @@ struct RowSpace {
 };
 // Which cache rows a context's new token attends to ([transformer架构]
 // §2.5.1 sliding window: query i sees keys i-w+1 .. i; §2.5.2 rolling
-// buffer: position t lives in slot t mod S_max).  Linear cache: positions
-// max(0, L-window) .. L-1 are rows of the same index (window 0: all L);
-// rolling buffer: every filled slot, min(L, S_max) of them from row 0.  The
-// query's position is L-1 in both (keys are cached after RoPE).
+// buffer: position t lives in slot t mod S_max; StreamingLLM, [attention]
+// "Slide Window Attention (SWA)" 修复方案 1: the first s tokens stay
+// visible beside the window).  Linear cache: positions max(0, L-window) ..
+// L-1 are rows of the same index (window 0: all L), preceded by the sink
+// rows 0 .. s-1 that lie below them; rolling buffer: every filled slot,
+// min(L, S_max) of them from row 0, where the first s slots keep positions
+// 0 .. s-1 and later positions cycle through the other S_max - s slots.  The
+// query's position is L-1 in all cases (keys are cached after RoPE).
+// Attended row r of a context is cache row r (r < ns) or lo + r - ns.
 struct CacheView {
     int window;    // 0 = no window
     int rolling;   // 1 = rolling buffer of S_max slots (window 0)
+    int sinks;     // sink tokens kept beside the window / in the buffer's first slots
 };
 struct CtxGeom {
-    int lo;        // first cache row
-    int n;         // rows attended
+    int lo;        // first cache row of the band
+    int n;         // rows attended (sink rows + band)
+    int ns;        // sink rows attended before the band (rows 0 .. ns-1)
     int qpos;      // the new token's position
     int newrow;    // the cache row of that position
 };
@@ -160,11 +167,16 @@ __device__ __forceinline__ CtxGeom ctx_geom(const int32_t* seq_lens, int b, int 
     const int raw = max(seq_lens[b], 1);
     if (cv.rolling) {
         const int n = min(raw, S_max);
-        return CtxGeom{0, n, raw - 1, (int)((unsigned)(raw - 1) % (unsigned)S_max)};
+        const int t = raw - 1;
+        const int slot = t < cv.sinks ? t
+                                      : cv.sinks + (int)((unsigned)(t - cv.sinks) %
+                                                         (unsigned)(S_max - cv.sinks));
+        return CtxGeom{0, n, 0, t, slot};
     }
     const int L = min(raw, S_max);
     const int lo = cv.window > 0 ? max(0, L - cv.window) : 0;
-    return CtxGeom{lo, L - lo, L - 1, L - 1};
+    const int ns = min(cv.sinks, lo);
+    return CtxGeom{lo, ns + L - lo, ns, L - 1, L - 1};
 }
 __device__ __forceinline__ int ctx_len(const int32_t* seq_lens, int b, int S_max,
                                        const CacheView& cv) {
@@ -442,13 +454,21 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
         const int r0 = (int)(gs - ctx0);
         const int r1 = (int)min((int64_t)L, ge - ctx0);
 
-        // rows r of the piece are cache rows geo.lo + r; buffers end at this
-        // piece's last row: the prefetch past it reads zeros for free
+        // The piece's rows [r0, r1) fall into the sink segment [r0, sa1) and
+        // the band segment [sb0, r1); the band's rows r are cache rows
+        // geo.lo - geo.ns + r.  Each segment's buffers end at its last row:
+        // the prefetch past it reads zeros for free.
         const size_t slice = ((size_t)b * Hkv + kv) * (size_t)S_max * D;
-        const size_t first = slice + (size_t)geo.lo * D;
+        const int sa1 = min(r1, geo.ns);
+        const int sb0 = max(r0, geo.ns);
+        const size_t first = slice + (size_t)(geo.lo - geo.ns) * D;
         const uint32_t nbytes = (uint32_t)r1 * D * 2u;
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(k_cache + first, nbytes);
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_cache + first, nbytes);
+        const uint32_t sbytes = (uint32_t)max(sa1, 0) * D * 2u;
+        const __amdgpu_buffer_rsrc_t ksr = make_rsrc(k_cache + slice, sbytes);
+        const __amdgpu_buffer_rsrc_t vsr = make_rsrc(v_cache + slice, sbytes);
+        const bool sink_seg = r0 < sa1;
 
         // q is requested first, then the first tiles; q is prepared while the
         // tiles are in flight
@@ -457,14 +477,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
         [[maybe_unused]] NewRow<D> nr;
         if constexpr (APPEND) load_new_row<D>(nr, app, ((size_t)b * Hkv + kv) * D, G, n);
         DecodeTile<D> ta, tb;
-        load_tile<D>(ta, kr, vr, r0, G, n);
+        if (sink_seg) load_tile<D>(ta, ksr, vsr, r0, G, n);
+        else load_tile<D>(ta, kr, vr, r0, G, n);
 
         u32x4 qhi[NB][KU], qlo[NB][KU];
         prep_q<D, NB>(qraw, fq, geo.qpos + 1, qscale, rope, G, qhi, qlo);
-        // the new token's row, as a row of this context's attended range
-        const int r_new = geo.newrow - geo.lo;
+        // the new token's row, as a row of this context's attended range (it
+        // is always in the band segment)
+        const int r_new = geo.newrow - geo.lo + geo.ns;
         const bool ends = APPEND && r0 <= r_new && r_new < r1;   // this piece holds it
-        const int rr_new = (r_new - r0) & 31;                     // its row in its tile
+        const int rr_new = (r_new - sb0) & 31;                    // its row in its tile
         if constexpr (APPEND)
             if (ends) rotate_new_key<D>(nr, geo.qpos + 1, fq, rope, G);
 
@@ -482,18 +504,26 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
             if constexpr (APPEND)
                 if (ends && t0 <= r_new && r_new < t0 + 32) swap_new_row<D>(t, nr, rr_new, G, n);
         };
-        for (int t0 = r0;;) {
-            load_tile<D>(tb, kr, vr, t0 + 32, G, n);
-            fix(ta, t0);
-            tile_math<D, NB>(ta, t0, r1, G, qhi, qlo, o, m_run, l_run);
-            t0 += 32;
-            if (t0 >= r1) break;
-            load_tile<D>(ta, kr, vr, t0 + 32, G, n);
-            fix(tb, t0);
-            tile_math<D, NB>(tb, t0, r1, G, qhi, qlo, o, m_run, l_run);
-            t0 += 32;
-            if (t0 >= r1) break;
+        // tiles t0 = s0, s0 + 32, .. of rows [s0, s1), the first already in ta
+        auto segment = [&](__amdgpu_buffer_rsrc_t sk, __amdgpu_buffer_rsrc_t sv, int s0, int s1) {
+            for (int t0 = s0;;) {
+                load_tile<D>(tb, sk, sv, t0 + 32, G, n);
+                fix(ta, t0);
+                tile_math<D, NB>(ta, t0, s1, G, qhi, qlo, o, m_run, l_run);
+                t0 += 32;
+                if (t0 >= s1) break;
+                load_tile<D>(ta, sk, sv, t0 + 32, G, n);
+                fix(tb, t0);
+                tile_math<D, NB>(tb, t0, s1, G, qhi, qlo, o, m_run, l_run);
+                t0 += 32;
+                if (t0 >= s1) break;
+            }
+        };
+        if (sink_seg) {
+            segment(ksr, vsr, r0, sa1);
+            if (sb0 < r1) load_tile<D>(ta, kr, vr, sb0, G, n);
         }
+        if (sb0 < r1) segment(kr, vr, sb0, r1);
 
         if constexpr (APPEND)
             if (ends) {
@@ -673,8 +703,8 @@ hipError_t launch_gqa_decode_partial(const void* q, const void* k_cache, const v
                                      int32_t D, int32_t S_max, float scale, const RopeDev& rope,
                                      void* workspace, const DecodeLayout& lay, hipStream_t s,
                                      const void* k_new, const void* v_new, int32_t window,
-                                     int32_t rolling) {
-    const CacheView cv{window, rolling};
+                                     int32_t rolling, int32_t sinks) {
+    const CacheView cv{window, rolling, sinks};
     const AppendArgs app{(const uint16_t*)k_new, (const uint16_t*)v_new,
                          k_new ? (uint16_t*)const_cast<void*>(k_cache) : nullptr,
                          k_new ? (uint16_t*)const_cast<void*>(v_cache) : nullptr};
@@ -699,8 +729,8 @@ hipError_t launch_gqa_decode_partial(const void* q, const void* k_cache, const v
 hipError_t launch_gqa_decode_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                                      int32_t D, int32_t S_max, const void* workspace,
                                      const DecodeLayout& lay, void* out, hipStream_t s,
-                                     int32_t window, int32_t rolling) {
-    const CacheView cv{window, rolling};
+                                     int32_t window, int32_t rolling, int32_t sinks) {
+    const CacheView cv{window, rolling, sinks};
     const float* po = reinterpret_cast<const float*>(workspace);
     const float* pml = reinterpret_cast<const float*>(reinterpret_cast<const char*>(workspace) + lay.o_bytes);
     dim3 cgrid((B * Hq + 3) / 4);

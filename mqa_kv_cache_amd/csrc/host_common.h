@@ -51,19 +51,22 @@ hipError_t launch_gqa_decode_partial(const void* q, const void* k_cache, const v
                                      int32_t D, int32_t S_max, float scale, const RopeDev& rope,
                                      void* workspace, const DecodeLayout& lay, hipStream_t s,
                                      const void* k_new = nullptr, const void* v_new = nullptr,
-                                     int32_t window = 0, int32_t rolling = 0);
+                                     int32_t window = 0, int32_t rolling = 0, int32_t sinks = 0);
 hipError_t launch_gqa_decode_combine(const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
                                      int32_t D, int32_t S_max, const void* workspace,
                                      const DecodeLayout& lay, void* out, hipStream_t s,
-                                     int32_t window = 0, int32_t rolling = 0);
+                                     int32_t window = 0, int32_t rolling = 0, int32_t sinks = 0);
 
-// Bytes of one prepared tensor (fp16 K rows, or fp16 V^T tiles) for prefill.
+// Bytes of one prepared tensor (K hi rows, K lo rows or fp16 V^T tiles) for
+// prefill; the workspace holds three of them.
 size_t prefill_prep_bytes(int32_t B, int32_t Hkv, int32_t T, int32_t D);
 
+// window 0 = causal; sinks > 0 keeps keys < sinks visible beside the band;
+// fp16_scores != 0 selects the one-product fp16 score path.
 hipError_t launch_gqa_prefill(const void* q, const void* k, const void* v, int32_t B, int32_t T,
                               int32_t Hq, int32_t Hkv, int32_t D, float scale,
                               const RopeDev& rope, void* out, void* workspace, hipStream_t s,
-                              int32_t window = 0);
+                              int32_t window, int32_t sinks, int32_t fp16_scores);
 
 struct SparseLayout {
     size_t scores_bytes;   // fp32 [B][S_max rounded up to 4]

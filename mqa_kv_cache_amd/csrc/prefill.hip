@@ -6,16 +6,32 @@
 // "MQA 与 GQA", attention(): q k^T / sqrt(hd), strict upper triangle masked,
 // softmax, weighted sum of V) with RoPE on Q and K ([transformer架构] §1.1).
 //
-// Operand precision: the rotated Q and K and the probabilities P are rounded
-// to fp16 (11-bit significand) rather than bf16 (8-bit): with bf16 the
-// rounding of rotated Q/K alone moves short-context outputs by up to ~2e-3,
-// the size of the absolute tolerance.  V converts from bf16 to fp16 exactly
-// (inside the fp16 range), and fp16 MFMA runs at the bf16 rate.
+// Score precision.  RoPE is fused into the load, so the rotated Q and K are
+// not bf16 inputs any more and must be rounded to reach the matrix cores.
+// Rounding both to one 16-bit term perturbs every logit by up to
+// 2^-11 |q~||k~| (fp16): with a sharp softmax (scores spread over several
+// units) that alone moves outputs past 2e-3 + 1e-2 |ref|.  The default
+// (SPLIT) path therefore carries rotated Q and K as hi + lo bf16 terms
+// (hi = bf16(x), lo = bf16(x - hi): ~2^-17 relative) and forms each score
+// from three products, Kh.Qh + Kh.Ql + Kl.Qh (the dropped Kl.Ql is ~2^-18
+// of the score); the fast path rounds both to fp16 and needs one product.
+// P is fp16 in both (2^-11 on weights that l sums exactly as rounded), V
+// converts from bf16 to fp16 exactly inside the fp16 range, and fp16 and
+// bf16 MFMA run at the same rate.
 //
 // Pre-pass (one read of K and V): K is rotated at its position and stored as
-// fp16 rows; V is stored as fp16 and transposed per 64-key tile, key columns
-// permuted to match the P^T operand.  Every later query tile re-reads these
-// tiles, so neither the rotation nor the transpose is repeated.
+// bf16 hi and lo rows (SPLIT) or fp16 rows; V is stored as fp16 and
+// transposed per 64-key tile, key columns permuted to match the P^T operand.
+// Every later query tile re-reads these tiles, so neither the rotation nor
+// the transpose is repeated.
+//
+// Masks: causal (key j <= query i); with a window w, the band
+// i - w + 1 <= j <= i ([transformer架构] §2.5.1); with s sink tokens
+// (StreamingLLM, [attention] "Slide Window Attention (SWA)", 修复方案 1) keys
+// j < s stay visible as well: the band plus the first s columns
+// ([transformer架构] §2.5.4).  A workgroup's key tiles are the sink tiles
+// (those holding keys < s) followed by the tiles of its band; the two runs
+// merge when the band reaches down to the sinks.
 //
 // Main kernel: one workgroup (4 waves) per (batch, q head, 128-query tile);
 // wave w owns 32 queries.  Query tiles are issued heaviest (latest) first so
@@ -54,6 +70,22 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f32x16 mfma32h(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32b(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// One score product step: fp16 operands (fast path) or the three products
+// of the hi + lo bf16 operands (SPLIT).
+template <bool SPLIT>
+__device__ __forceinline__ f32x16 score_mfma(u32x4 kh, u32x4 kl, u32x4 qh, u32x4 ql, f32x16 c) {
+    if constexpr (SPLIT) {
+        c = mfma32b(kh, qh, c);
+        c = mfma32b(kh, ql, c);
+        return mfma32b(kl, qh, c);
+    } else {
+        return mfma32h(kh, qh, c);
+    }
 }
 
 // fp32 -> fp16 x2, round to nearest even.
@@ -140,16 +172,20 @@ __device__ __forceinline__ u32x4 v_frag(const uint16_t* vt_s, int d, int c) {
 constexpr float kLazy = 8.0f;
 
 // S^T[64 keys][32 queries] = K . Q^T for one tile (two 32-key halves).
-template <int D>
-__device__ __forceinline__ void qk_tile(const uint16_t* k_s, const u32x4 (&qf)[Geo<D>::KSTEPS],
-                                        f32x16 (&s)[2], int n, int h) {
+template <int D, bool SPLIT>
+__device__ __forceinline__ void qk_tile(const uint16_t* k_s, const uint16_t* kl_s,
+                                        const u32x4 (&qf)[Geo<D>::KSTEPS],
+                                        const u32x4 (&qfl)[Geo<D>::KSTEPS], f32x16 (&s)[2], int n,
+                                        int h) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[st][e] = 0.f;
 #pragma unroll
         for (int u = 0; u < Geo<D>::KSTEPS; ++u)
-            s[st] = mfma32h(k_frag<D>(k_s, 32 * st + n, 2 * u + h), qf[u], s[st]);
+            s[st] = score_mfma<SPLIT>(k_frag<D>(k_s, 32 * st + n, 2 * u + h),
+                                      SPLIT ? k_frag<D>(kl_s, 32 * st + n, 2 * u + h) : u32x4{},
+                                      qf[u], qfl[u], s[st]);
     }
 }
 
@@ -170,18 +206,23 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int ks, int qi, int h)
 }
 
 // Sliding window (band mask): keys below the lane's query qi minus
-// (window - 1) are masked; only the first tiles of a wave hold any.
-__device__ __forceinline__ void mask_low(f32x16 (&s)[2], int ks, int qi, int h, int window) {
-    // key = ks + 32 st + 8 j + 4 h + i is masked when 32 st + 8 j + i < lim
+// (window - 1) are masked, except the sink keys (key < sinks); only the
+// sink tiles and the first band tiles of a wave hold any.
+__device__ __forceinline__ void mask_low(f32x16 (&s)[2], int ks, int qi, int h, int window,
+                                         int sinks) {
+    // key = ks + 32 st + 8 j + 4 h + i is masked when slim <= 32 st + 8 j + i < lim
     int lim = qi - window + 1 - ks - 4 * h;
-    asm volatile("" : "+v"(lim));
+    int slim = sinks - ks - 4 * h;
+    asm volatile("" : "+v"(lim), "+v"(slim));
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (32 * st + 8 * j + i < lim) s[st][4 * j + i] = -INFINITY;
+            for (int i = 0; i < 4; ++i) {
+                const int kk = 32 * st + 8 * j + i;
+                if (kk < lim && kk >= slim) s[st][4 * j + i] = -INFINITY;
+            }
 }
 
 // The reference maximum while a query has seen no visible key yet (only with
@@ -255,38 +296,45 @@ __device__ __forceinline__ void pv_tile(const uint16_t* vt_s, const u32x4 (&pb)[
 // one V fragment read two ahead and a slice of the next tile's maximum.  The
 // VALU work then runs under the matrix pipe instead of between its bursts,
 // and phase A's last two groups already read phase B's first V fragments.
-template <int D>
-__device__ __forceinline__ void pipelined_step(const uint16_t* k_nx, const uint16_t* v_cu,
+template <int D, bool SPLIT>
+__device__ __forceinline__ void pipelined_step(const uint16_t* k_nx, const uint16_t* kl_nx,
+                                               const uint16_t* v_cu,
                                                const u32x4 (&qf)[Geo<D>::KSTEPS],
+                                               const u32x4 (&qfl)[Geo<D>::KSTEPS],
                                                const f32x16 (&s_c)[2], f32x16 (&s_n)[2],
                                                f32x16 (&o)[Geo<D>::MT], float& m_run, float& l_run,
-                                               bool diag_next, bool low_next, int window,
+                                               bool diag_next, bool low_next, int window, int sinks,
                                                int ks_next, int qi, int n, int h) {
     constexpr int KS = Geo<D>::KSTEPS, MT = Geo<D>::MT;
-    constexpr int NQK = 2 * KS;          // S^T MFMAs of a tile
+    constexpr int NQK = 2 * KS;          // S^T MFMA steps of a tile (three MFMAs each when SPLIT)
     constexpr int NPV = 4 * MT;          // P.V MFMAs of a tile
     constexpr int PAIRS = 16 / NQK;      // probability pairs per phase-A group
     constexpr int MAXV = 32 / NPV;       // scores per phase-B group
     const float m = ref_max(m_run);
 
     // ---- phase A: S^T(next) || P(current)
-    u32x4 kf[NQK];
+    u32x4 kf[NQK], kfl[NQK];
     u32x4 vf[NPV];
     u32x4 pb[4];
     float ls = 0.f;
 #pragma unroll
-    for (int i = 0; i < 2 && i < NQK; ++i) kf[i] = k_frag<D>(k_nx, 32 * (i / KS) + n, 2 * (i % KS) + h);
+    for (int i = 0; i < 2 && i < NQK; ++i) {
+        kf[i] = k_frag<D>(k_nx, 32 * (i / KS) + n, 2 * (i % KS) + h);
+        if constexpr (SPLIT) kfl[i] = k_frag<D>(kl_nx, 32 * (i / KS) + n, 2 * (i % KS) + h);
+    }
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s_n[st][e] = 0.f;
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
-        if (i + 2 < NQK)
+        if (i + 2 < NQK) {
             kf[i + 2] = k_frag<D>(k_nx, 32 * ((i + 2) / KS) + n, 2 * ((i + 2) % KS) + h);
-        else if (i + 2 - NQK < NPV)   // the first V fragments of phase B, read under phase A
+            if constexpr (SPLIT) kfl[i + 2] = k_frag<D>(kl_nx, 32 * ((i + 2) / KS) + n, 2 * ((i + 2) % KS) + h);
+        } else if (i + 2 - NQK < NPV) {   // the first V fragments of phase B, read under phase A
             vf[i + 2 - NQK] = v_frag<D>(v_cu, 32 * ((i + 2 - NQK) % MT) + n, 2 * ((i + 2 - NQK) / MT) + h);
-        s_n[i / KS] = mfma32h(kf[i], qf[i % KS], s_n[i / KS]);
+        }
+        s_n[i / KS] = score_mfma<SPLIT>(kf[i], kfl[i], qf[i % KS], qfl[i % KS], s_n[i / KS]);
 #pragma unroll
         for (int q = 0; q < PAIRS; ++q) {
             const int p = i * PAIRS + q;             // pair: st = p / 8, c = (p / 4) % 2, w = p % 4
@@ -301,7 +349,7 @@ __device__ __forceinline__ void pipelined_step(const uint16_t* k_nx, const uint1
     }
     l_run += halves_sum(ls);
     if (diag_next) mask_tile(s_n, ks_next, qi, h);
-    if (low_next) mask_low(s_n, ks_next, qi, h, window);
+    if (low_next) mask_low(s_n, ks_next, qi, h, window, sinks);
 
     // ---- phase B: O += V.P(current) || max S^T(next)
     float mx = -INFINITY;
@@ -328,17 +376,21 @@ __device__ __forceinline__ void pipelined_step(const uint16_t* k_nx, const uint1
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vt,
-    uint16_t* __restrict__ out, int T, int T_pad, int Hq, int Hkv, float qscale, RopeDev rope,
-    int window) {
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(256, SPLIT ? 1 : GQA_PREFILL_MIN_WAVES) void prefill_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kh, const uint16_t* __restrict__ kl,
+    const uint16_t* __restrict__ vt, uint16_t* __restrict__ out, int T, int T_pad, int Hq, int Hkv,
+    float qscale, RopeDev rope, int window, int sinks) {
     using Gm = Geo<D>;
     // Two buffers per operand, as separate LDS objects: the compiler then
     // tells the tile being read from the one being copied into, and does not
-    // make the reads wait for the copy in flight.
+    // make the reads wait for the copy in flight.  (The lo K buffers hold
+    // nothing on the fast path.)
+    constexpr int KL_ELEMS = SPLIT ? Gm::K_ELEMS : 8;
     __shared__ __attribute__((aligned(16))) uint16_t k_s0[Gm::K_ELEMS];
     __shared__ __attribute__((aligned(16))) uint16_t k_s1[Gm::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t kl_s0[KL_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t kl_s1[KL_ELEMS];
     __shared__ __attribute__((aligned(16))) uint16_t vt_s0[Gm::V_ELEMS];
     __shared__ __attribute__((aligned(16))) uint16_t vt_s1[Gm::V_ELEMS];
 
@@ -380,28 +432,41 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
 
     const size_t qbase = ((size_t)b * Hq + hq) * (size_t)T * D;
     const size_t kvbase = ((size_t)b * Hkv + kvh) * (size_t)T_pad * D;
-    const uint16_t* kbase = kh + kvbase;
-    const uint16_t* vbase = vt + kvbase;                // V^T tiles: [T_pad/64][D][64]
     const int q_last_wg = min(qt * BM + BM - 1, T - 1);
-    // With a sliding window (band mask, window > 0) the workgroup starts at the
-    // tile holding the first key its first query sees; tile t below is key
-    // tile kt0 + t, and the buffer descriptors start there.
-    const int kt0 = window > 0 ? max(0, qt * BM - window + 1) / BN : 0;
-    const int n_kt = q_last_wg / BN + 1 - kt0;
+    // Key tiles of this workgroup.  With a window (band mask) the band starts
+    // at the tile holding the first key its first query sees (kt0); with s
+    // sink tokens the ns = ceil(s / 64) sink tiles come first when they lie
+    // below kt0 (ns_sep of them), otherwise the band already covers them.
+    // Logical tile t is physical tile t (t < ns_sep) or kt0 + t - ns_sep.
+    int kt0 = window > 0 ? max(0, qt * BM - window + 1) / BN : 0;
+    const int ns = (window > 0 && sinks > 0) ? (sinks + BN - 1) / BN : 0;
+    int ns_sep = ns;
+    if (kt0 <= ns) {
+        kt0 = 0;
+        ns_sep = 0;
+    }
+    const int n_kt = q_last_wg / BN + 1 - kt0 + ns_sep;
+    auto phys = [&](int t) { return t < ns_sep ? t : kt0 + t - ns_sep; };
 
-    const __amdgpu_buffer_rsrc_t kr =
-        make_rsrc(kbase + (size_t)kt0 * BN * D, (uint32_t)(T_pad - kt0 * BN) * D * 2u);
-    const __amdgpu_buffer_rsrc_t vr =
-        make_rsrc(vbase + (size_t)kt0 * BN * D, (uint32_t)(T_pad - kt0 * BN) * D * 2u);
+    const uint32_t kv_bytes = (uint32_t)T_pad * D * 2u;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh + kvbase, kv_bytes);
+    const __amdgpu_buffer_rsrc_t klr = make_rsrc(SPLIT ? kl + kvbase : kh + kvbase, kv_bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vt + kvbase, kv_bytes);   // V^T tiles: [T_pad/64][D][64]
+    auto tile_off = [&](int t) { return (uint32_t)phys(t) * BN * D * 2u; };
     const RowCopy<BN, 2 * D, 2 * Gm::KSTR> kcopy(lane);
     const RowCopy<D, 2 * BN, 2 * Gm::VSTR> vcopy(lane);
+    auto copy_k = [&](int t, uint16_t* dst, uint16_t* dst_lo, int wv) {
+        kcopy.run(kr, tile_off(t), dst, wv);
+        if constexpr (SPLIT) kcopy.run(klr, tile_off(t), dst_lo, wv);
+    };
     // the first tile's copy overlaps the Q load and rotation
-    kcopy.run(kr, 0u, k_s0, wave);
-    vcopy.run(vr, 0u, vt_s0, wave);
+    copy_k(0, k_s0, kl_s0, wave);
+    vcopy.run(vr, tile_off(0), vt_s0, wave);
 
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(q + qbase, (uint32_t)T * D * 2u);
-    // ---- Q^T operands: lane holds query qi, dims 16u + 8h .. +7 (rotated, scaled, fp16)
-    u32x4 qf[Gm::KSTEPS];
+    // ---- Q^T operands: lane holds query qi, dims 16u + 8h .. +7, rotated and
+    // scaled: hi + lo bf16 (SPLIT) or fp16
+    u32x4 qf[Gm::KSTEPS], qfl[Gm::KSTEPS];
 #pragma unroll
     for (int u = 0; u < Gm::KSTEPS; ++u) {
         const int d0 = 16 * u + 8 * h;
@@ -426,7 +491,16 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
             }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) qf[u][j] = pack_f16x2(x[2 * j] * qscale, x[2 * j + 1] * qscale);
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (SPLIT) {
+                const u32x2 hl = split_bf16x2(x[2 * j] * qscale, x[2 * j + 1] * qscale);
+                qf[u][j] = hl[0];
+                qfl[u][j] = hl[1];
+            } else {
+                qf[u][j] = pack_f16x2(x[2 * j] * qscale, x[2 * j + 1] * qscale);
+                qfl[u][j] = 0u;
+            }
+        }
     }
 
     f32x16 o[Gm::MT];
@@ -448,40 +522,42 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
     // tiles 0 .. n_w-1 and only the last of them holds keys past its first
     // query (q0 is a multiple of 32, tiles are 64 wide); a wave done early
     // keeps copying its share and meeting the barriers of the others.
-    const int n_w = min((q0 + 31) / BN + 1 - kt0, n_kt);
-    // tile t holds keys below some query's window when its first key is
-    // below the last query's lower bound
-    auto low = [&](int t) { return window > 0 && (kt0 + t) * BN < q0 + 32 - window; };
-    if (n_kt > 1) kcopy.run(kr, (uint32_t)BN * D * 2u, k_s1, wave);
+    const int n_w = min((q0 + 31) / BN + 1 - kt0 + ns_sep, n_kt);
+    // tile t holds keys below some query's band (other than sinks) when its
+    // first key is below the wave's last query's lower bound
+    auto low = [&](int t) { return window > 0 && phys(t) * BN < q0 + 32 - window; };
+    if (n_kt > 1) copy_k(1, k_s1, kl_s1, wave);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 s_cur[2];
-    qk_tile<D>(k_s0, qf, s_cur, n, h);
-    if (n_w == 1) mask_tile(s_cur, kt0 * BN, qi, h);
-    if (low(0)) mask_low(s_cur, kt0 * BN, qi, h, window);
+    qk_tile<D, SPLIT>(k_s0, kl_s0, qf, qfl, s_cur, n, h);
+    if (n_w == 1) mask_tile(s_cur, phys(0) * BN, qi, h);
+    if (low(0)) mask_low(s_cur, phys(0) * BN, qi, h, window, sinks);
     tile_max<D>(s_cur, o, m_run, l_run);
 
-    auto top = [&](int t, uint16_t* k_dst, uint16_t* v_dst) {
+    auto top = [&](int t, uint16_t* k_dst, uint16_t* kl_dst, uint16_t* v_dst) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         // the wave index is made opaque here so the copy addresses are formed
         // per step with a few scalar ops instead of being hoisted (and spilled)
         int wv = wave;
         asm volatile("" : "+s"(wv));
-        if (t + 2 < n_kt) kcopy.run(kr, (uint32_t)(t + 2) * BN * D * 2u, k_dst, wv);
-        if (t + 1 < n_kt) vcopy.run(vr, (uint32_t)(t + 1) * BN * D * 2u, v_dst, wv);
+        if (t + 2 < n_kt) copy_k(t + 2, k_dst, kl_dst, wv);
+        if (t + 1 < n_kt) vcopy.run(vr, tile_off(t + 1), v_dst, wv);
     };
     // a step with a next tile: scores s_cur -> P.V, S^T of tile t+1 -> s_nxt
     auto full = [&](int t, f32x16 (&s_c)[2], f32x16 (&s_n)[2], const uint16_t* k_next,
-                    const uint16_t* v_cur, uint16_t* k_dst, uint16_t* v_dst) {
-        top(t, k_dst, v_dst);
-        pipelined_step<D>(k_next, v_cur, qf, s_c, s_n, o, m_run, l_run, t + 1 == n_w - 1,
-                          low(t + 1), window, (kt0 + t + 1) * BN, qi, n, h);
+                    const uint16_t* kl_next, const uint16_t* v_cur, uint16_t* k_dst,
+                    uint16_t* kl_dst, uint16_t* v_dst) {
+        top(t, k_dst, kl_dst, v_dst);
+        pipelined_step<D, SPLIT>(k_next, kl_next, v_cur, qf, qfl, s_c, s_n, o, m_run, l_run,
+                                 t + 1 == n_w - 1, low(t + 1), window, sinks, phys(t + 1) * BN, qi,
+                                 n, h);
     };
     // this wave's last step
     auto last = [&](int t, const f32x16 (&s_c)[2], const uint16_t* v_cur, uint16_t* k_dst,
-                    uint16_t* v_dst) {
-        top(t, k_dst, v_dst);
+                    uint16_t* kl_dst, uint16_t* v_dst) {
+        top(t, k_dst, kl_dst, v_dst);
         u32x4 pb[4];
         l_run += halves_sum(probs(s_c, ref_max(m_run), pb));
         pv_tile<D>(v_cur, pb, o, n, h);
@@ -489,26 +565,26 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
     f32x16 s_alt[2];
     int t = 0;
     for (; t + 2 < n_w; t += 2) {
-        full(t, s_cur, s_alt, k_s1, vt_s0, k_s0, vt_s1);
-        full(t + 1, s_alt, s_cur, k_s0, vt_s1, k_s1, vt_s0);
+        full(t, s_cur, s_alt, k_s1, kl_s1, vt_s0, k_s0, kl_s0, vt_s1);
+        full(t + 1, s_alt, s_cur, k_s0, kl_s0, vt_s1, k_s1, kl_s1, vt_s0);
     }
     if (t + 1 < n_w) {
-        full(t, s_cur, s_alt, k_s1, vt_s0, k_s0, vt_s1);
-        last(t + 1, s_alt, vt_s1, k_s1, vt_s0);
+        full(t, s_cur, s_alt, k_s1, kl_s1, vt_s0, k_s0, kl_s0, vt_s1);
+        last(t + 1, s_alt, vt_s1, k_s1, kl_s1, vt_s0);
         t += 2;
     } else {
-        last(t, s_cur, vt_s0, k_s0, vt_s1);
+        last(t, s_cur, vt_s0, k_s0, kl_s0, vt_s1);
         t += 1;
     }
     for (; t < n_kt; ++t) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (t & 1) {
-            if (t + 2 < n_kt) kcopy.run(kr, (uint32_t)(t + 2) * BN * D * 2u, k_s1, wave);
-            if (t + 1 < n_kt) vcopy.run(vr, (uint32_t)(t + 1) * BN * D * 2u, vt_s0, wave);
+            if (t + 2 < n_kt) copy_k(t + 2, k_s1, kl_s1, wave);
+            if (t + 1 < n_kt) vcopy.run(vr, tile_off(t + 1), vt_s0, wave);
         } else {
-            if (t + 2 < n_kt) kcopy.run(kr, (uint32_t)(t + 2) * BN * D * 2u, k_s0, wave);
-            if (t + 1 < n_kt) vcopy.run(vr, (uint32_t)(t + 1) * BN * D * 2u, vt_s1, wave);
+            if (t + 2 < n_kt) copy_k(t + 2, k_s0, kl_s0, wave);
+            if (t + 1 < n_kt) vcopy.run(vr, tile_off(t + 1), vt_s1, wave);
         }
     }
 
@@ -532,14 +608,15 @@ __global__ __launch_bounds__(256, GQA_PREFILL_MIN_WAVES) void prefill_kernel(
 }
 
 // Pre-pass, one block per (64-key tile, kv head, batch):
-//   K  -> RoPE at its position (fp64 angle, fp32 sincos) -> fp16 rows   [B][Hkv][T_pad][D]
+//   K  -> RoPE at its position (fp64 angle, fp32 sincos) -> bf16 hi and lo
+//         rows (SPLIT) or fp16 rows                                     [B][Hkv][T_pad][D]
 //   V  -> fp16 (exact for bf16 values in fp16 range), transposed per tile into
 //         [B][Hkv][T_pad/64][D][64] with key columns permuted for the P^T operand.
 // Rows at or past T are written as zeros.
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(256) void prefill_prep_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ kh,
-    uint16_t* __restrict__ vt, int T, int T_pad, int Hkv, RopeDev rope) {
+    uint16_t* __restrict__ kl, uint16_t* __restrict__ vt, int T, int T_pad, int Hkv, RopeDev rope) {
     __shared__ float cs_c[BN * kMaxRotaryHalf / 2];
     __shared__ float cs_s[BN * kMaxRotaryHalf / 2];
     constexpr int CPR = D / 8;
@@ -589,7 +666,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
         if (c >= BN * CPR) break;
         const int key = c / CPR, dc = c - key * CPR;
         const int t = ks + key;
-        u32x4 val;
+        u32x4 val, lo;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             float xe = bf16_lo(kraw[j][p]), xo = bf16_hi(kraw[j][p]);
@@ -600,9 +677,16 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
                 xe = ye;
                 xo = yo;
             }
-            val[p] = pack_f16x2(xe, xo);
+            if constexpr (SPLIT) {
+                const u32x2 hl = split_bf16x2(xe, xo);
+                val[p] = hl[0];
+                lo[p] = hl[1];
+            } else {
+                val[p] = pack_f16x2(xe, xo);
+            }
         }
         *reinterpret_cast<u32x4*>(kh + out_base + (size_t)t * D + 8 * dc) = val;   // zeros past T
+        if constexpr (SPLIT) *reinterpret_cast<u32x4*>(kl + out_base + (size_t)t * D + 8 * dc) = lo;
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -632,17 +716,31 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     }
 }
 
-template <int D>
-void launch_d(const void* q, const void* k, const void* v, void* out, void* kh, void* vt, int B,
-              int T, int Hq, int Hkv, float qscale, const RopeDev& rope, int window, hipStream_t s) {
+template <int D, bool SPLIT>
+void launch_d(const void* q, const void* k, const void* v, void* out, void* kh, void* kl, void* vt,
+              int B, int T, int Hq, int Hkv, float qscale, const RopeDev& rope, int window,
+              int sinks, hipStream_t s) {
     const int T_pad = (T + BN - 1) / BN * BN;
-    hipLaunchKernelGGL((prefill_prep_kernel<D>), dim3(T_pad / BN, Hkv, B), dim3(256), 0, s,
-                       (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)kh, (uint16_t*)vt, T,
-                       T_pad, Hkv, rope);
+    hipLaunchKernelGGL((prefill_prep_kernel<D, SPLIT>), dim3(T_pad / BN, Hkv, B), dim3(256), 0, s,
+                       (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)kh, (uint16_t*)kl,
+                       (uint16_t*)vt, T, T_pad, Hkv, rope);
     dim3 grid((T + BM - 1) / BM * Hq * B);   // one workgroup per (query tile, q head, batch)
-    hipLaunchKernelGGL((prefill_kernel<D>), grid, dim3(256), 0, s, (const uint16_t*)q,
-                       (const uint16_t*)kh, (const uint16_t*)vt, (uint16_t*)out, T, T_pad, Hq, Hkv,
-                       qscale, rope, window);
+    hipLaunchKernelGGL((prefill_kernel<D, SPLIT>), grid, dim3(256), 0, s, (const uint16_t*)q,
+                       (const uint16_t*)kh, (const uint16_t*)kl, (const uint16_t*)vt,
+                       (uint16_t*)out, T, T_pad, Hq, Hkv, qscale, rope, window, sinks);
+}
+
+template <bool SPLIT>
+void launch_p(const void* q, const void* k, const void* v, void* out, void* kh, void* kl, void* vt,
+              int B, int T, int Hq, int Hkv, int D, float qscale, const RopeDev& rope, int window,
+              int sinks, hipStream_t s) {
+    switch (D) {
+        case 8: launch_d<8, SPLIT>(q, k, v, out, kh, kl, vt, B, T, Hq, Hkv, qscale, rope, window, sinks, s); break;
+        case 16: launch_d<16, SPLIT>(q, k, v, out, kh, kl, vt, B, T, Hq, Hkv, qscale, rope, window, sinks, s); break;
+        case 32: launch_d<32, SPLIT>(q, k, v, out, kh, kl, vt, B, T, Hq, Hkv, qscale, rope, window, sinks, s); break;
+        case 64: launch_d<64, SPLIT>(q, k, v, out, kh, kl, vt, B, T, Hq, Hkv, qscale, rope, window, sinks, s); break;
+        default: launch_d<128, SPLIT>(q, k, v, out, kh, kl, vt, B, T, Hq, Hkv, qscale, rope, window, sinks, s); break;
+    }
 }
 
 }  // namespace
@@ -654,17 +752,17 @@ size_t prefill_prep_bytes(int32_t B, int32_t Hkv, int32_t T, int32_t D) {
 
 hipError_t launch_gqa_prefill(const void* q, const void* k, const void* v, int32_t B, int32_t T,
                               int32_t Hq, int32_t Hkv, int32_t D, float scale, const RopeDev& rope,
-                              void* out, void* workspace, hipStream_t s, int32_t window) {
+                              void* out, void* workspace, hipStream_t s, int32_t window,
+                              int32_t sinks, int32_t fp16_scores) {
     const float qscale = scale * kLog2e;
+    const size_t pb = prefill_prep_bytes(B, Hkv, T, D);
     void* kh = workspace;
-    void* vt = reinterpret_cast<char*>(workspace) + prefill_prep_bytes(B, Hkv, T, D);
-    switch (D) {
-        case 8: launch_d<8>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, window, s); break;
-        case 16: launch_d<16>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, window, s); break;
-        case 32: launch_d<32>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, window, s); break;
-        case 64: launch_d<64>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, window, s); break;
-        default: launch_d<128>(q, k, v, out, kh, vt, B, T, Hq, Hkv, qscale, rope, window, s); break;
-    }
+    void* kl = reinterpret_cast<char*>(workspace) + pb;
+    void* vt = reinterpret_cast<char*>(workspace) + 2 * pb;
+    if (fp16_scores)
+        launch_p<false>(q, k, v, out, kh, kl, vt, B, T, Hq, Hkv, D, qscale, rope, window, sinks, s);
+    else
+        launch_p<true>(q, k, v, out, kh, kl, vt, B, T, Hq, Hkv, D, qscale, rope, window, sinks, s);
     return hipGetLastError();
 }
 

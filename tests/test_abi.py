@@ -157,7 +157,7 @@ def test_prefill_validation(m):
     assert call(q=MIS) == m.ERR_INVALID_ARGUMENT
     r = _rope(m, scaling=m.ROPE_NTK, base=1e6, factor=4.0)
     need = m.gqa_prefill_workspace_size(1, 2, 16, 128, r.contents)
-    assert need == 2 * (2 * 64 * 128 * 2)      # fp16 K rows + fp16 V^T tiles, T padded to 64
+    assert need == 3 * (2 * 64 * 128 * 2)      # K hi and lo rows + fp16 V^T tiles, T padded to 64
     assert call(rope=r, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
     assert call(rope=r, ws=None, wsn=need) == m.ERR_INVALID_ARGUMENT
     assert m.gqa_prefill_workspace_size(1, 2, 16, 128, None) == need
@@ -171,6 +171,34 @@ def test_prefill_window_validation(m):
                                   None) == m.ERR_UNSUPPORTED
     assert lib.gqa_prefill_window(P, P, P, 1, 64, 8, 2, 128, 16, 0.1, None, P, P, 1,
                                   None) == m.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_sink_window_validation(m):
+    """StreamingLLM entry points: negative sinks, a rolling buffer with no
+    ring slot left, and the usual shape/workspace checks."""
+    lib = m.lib()
+
+    def dec(sinks=4, window=64, rolling=0, wsn=1 << 30):
+        return lib.gqa_decode_sink_window(P, 0, 0, P, P, P, 2, 16, 2, 128, 64, sinks, window,
+                                          rolling, 0.1, None, P, P, wsn, None)
+    assert dec(sinks=-1) == m.ERR_INVALID_ARGUMENT
+    assert dec(window=-1) == m.ERR_INVALID_ARGUMENT
+    assert dec(rolling=1, window=0, sinks=64) == m.ERR_INVALID_ARGUMENT   # no ring slot left
+    assert dec(rolling=1, window=8) == m.ERR_INVALID_ARGUMENT
+    need = m.gqa_decode_workspace_size(2, 16, 2, 128, 64)
+    assert dec(wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+    assert dec(rolling=1, window=0, sinks=63, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+    for fn in (lib.gqa_prefill_sink_window, lib.gqa_prefill_fp16):
+        assert fn(P, P, P, 1, 64, 8, 2, 128, -1, 16, 0.1, None, P, P, 1 << 30,
+                  None) == m.ERR_INVALID_ARGUMENT
+        assert fn(P, P, P, 1, 64, 8, 2, 128, 4, -1, 0.1, None, P, P, 1 << 30,
+                  None) == m.ERR_INVALID_ARGUMENT
+        assert fn(P, P, P, 1, 64, 7, 2, 128, 4, 16, 0.1, None, P, P, 1 << 30,
+                  None) == m.ERR_INVALID_ARGUMENT
+        assert fn(P, P, P, 1, 64, 8, 2, 96, 4, 16, 0.1, None, P, P, 1 << 30,
+                  None) == m.ERR_UNSUPPORTED
+        assert fn(P, P, P, 1, 64, 8, 2, 128, 4, 16, 0.1, None, P, P, 1,
+                  None) == m.ERR_WORKSPACE_TOO_SMALL
 
 
 def test_sparse_validation(m):

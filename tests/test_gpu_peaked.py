@@ -154,23 +154,46 @@ def test_qsa_peaked(m):
 
 
 @pytest.mark.parametrize("k2", [2, 3])
-@pytest.mark.parametrize("window", [0, 300])
-def test_prefill_peaked(m, k2, window):
-    """Causal (and band-masked) prefill over several 64-key tiles with q x
-    2^k2: the fp16 probabilities (2^-11) of the matrix-core path."""
+@pytest.mark.parametrize("window,sinks", [(0, 0), (300, 0), (300, 4)])
+def test_prefill_peaked(m, k2, window, sinks):
+    """Causal (band-masked, with sinks) prefill over several 64-key tiles
+    with q x 2^k2: the rotated Q and K reach the matrix cores as hi + lo
+    terms (a single 16-bit rounding of each moves these outputs by more than
+    the tolerance), P as fp16."""
     import torch
     B, T, Hq, Hkv, D = 1, 700, 8, 2, 128
     p = prefill_inputs_host(B, T, Hq, Hkv, D, seed=250 + k2)
     q = pow2_bf16(p["q"], k2)
     rope = rope_settings(ROPE_NTK, base=1e6, factor=4.0)
     scale = 1 / math.sqrt(D)
-    print(f"[case] prefill peaked x{2 ** k2} window={window}", flush=True)
+    print(f"[case] prefill peaked x{2 ** k2} window={window} sinks={sinks}", flush=True)
     out = m.gqa_prefill_causal(to_dev(q), to_dev(p["k"]), to_dev(p["v"]), scale, rope=rope,
-                               window=window)
+                               window=window, sinks=sinks)
     torch.cuda.synchronize()
     ref = oatt.prefill_causal(bf16_bits_to_f64(q), bf16_bits_to_f64(p["k"]),
-                              bf16_bits_to_f64(p["v"]), scale, rope, window=window)
-    assert_close(from_dev(out), ref, f"prefill peaked x{2 ** k2} w={window}")
+                              bf16_bits_to_f64(p["v"]), scale, rope, window=window, sinks=sinks)
+    assert_close(from_dev(out), ref, f"prefill peaked x{2 ** k2} w={window} s={sinks}")
+
+
+def test_decode_sinks_peaked(m):
+    """The sink-window decode (linear cache and sink-keeping rolling buffer)
+    with q x 8."""
+    import torch
+    B, Hq, Hkv, D = 2, 16, 2, 128
+    for S, window, rolling in ((5000, 3000, False), (2048, 0, True)):
+        lens = np.array([5000, 2900], dtype=np.int32)
+        d = decode_inputs_host(B, Hq, Hkv, D, S, 270, np.minimum(lens, S))
+        q = pow2_bf16(d["q"], 3)
+        scale = 1 / math.sqrt(D)
+        print(f"[case] decode sinks peaked rolling={rolling}", flush=True)
+        out = m.gqa_decode_window(to_dev(q), to_dev(d["k"]), to_dev(d["v"]),
+                                  torch.from_numpy(lens).cuda(), scale, window=window,
+                                  rolling=rolling, sinks=4, q_rope=YARN)
+        torch.cuda.synchronize()
+        ref = oatt.decode_window(bf16_bits_to_f64(q), bf16_bits_to_f64(d["k"]),
+                                 bf16_bits_to_f64(d["v"]), lens, scale, YARN, window=window,
+                                 rolling=rolling, sinks=4)
+        assert_close(from_dev(out), ref, f"decode sinks peaked rolling={rolling}")
 
 
 def test_mla_and_weighted_peaked(m):
