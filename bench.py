@@ -8,9 +8,12 @@ the whole batch; inputs are resident in HBM before timing starts and two
 independent caches alternate so the 256 MB Infinity Cache cannot serve them.
 
 The same run also measures the other hot-path entry points (decode at 4K,
-causal prefill at 8K on the matrix cores, top-k sparse decode at 128K and
-rope_apply) and times the CPU fp64 oracle on a bounded sample of the
-headline workload.  All data is synthetic and seeded.
+with Dynamic NTK, with the cache write, over a window, a rolling buffer and
+StreamingLLM sinks; causal prefill at 8K on the matrix cores, also with its
+fp16-score option, a window and sinks; top-k sparse decode at 128K, the
+weighted indexer, QSA, dense MLA and rope_apply) and times the CPU fp64
+oracle on a bounded sample of the headline workload.  All data is synthetic
+and seeded.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu] [--gpus 1]
 """
@@ -45,8 +48,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of sections (decode32k,decode4k,dynamic,append32k,window,mla,"
-                    "prefill,prefill_window,sparse,sparse_weighted,qsa,rope) for profiling runs")
+    ap.add_argument("--only", default="", help="comma list of sections (decode32k,decode4k,dynamic,append32k,window,"
+                    "sinks,mla,prefill,prefill_fp16,prefill_window,sparse,sparse_weighted,qsa,rope) "
+                    "for profiling runs")
     return ap.parse_args()
 
 
@@ -175,10 +179,11 @@ def bench_decode_append(cfg, steps, warmup, nsets=2):
     return dict(ms=ms, kv_bytes=kv_bytes)
 
 
-def bench_decode_window(cfg, steps, warmup, window, rolling, nsets=4):
+def bench_decode_window(cfg, steps, warmup, window, rolling, nsets=4, sinks=0):
     """gqa_decode_window on the 32K workload's batch, q heads and lengths: a
     `window`-token sliding window over the linear cache, or a rolling buffer
-    of `window` slots (contexts longer than the buffer)."""
+    of `window` slots (contexts longer than the buffer); with `sinks` > 0
+    (gqa_decode_sink_window) the first positions stay visible as well."""
     import torch
 
     import mqa_kv_cache_amd as m
@@ -192,24 +197,30 @@ def bench_decode_window(cfg, steps, warmup, window, rolling, nsets=4):
              device_randn_bf16((B, Hkv, S, D), cfg.seed * 100 + 10 * i + 3)) for i in range(nsets)]
     out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(m.gqa_decode_workspace_size(B, Hq, Hkv, D, S), dtype=torch.uint8, device="cuda")
-    rows = int(sum(min(int(L), window) for L in lens_np))
+    if rolling:
+        rows = int(sum(min(int(L), window) for L in lens_np))
+    else:
+        rows = int(sum(min(int(L), window) + min(sinks, max(0, int(L) - window)) for L in lens_np))
     kv_bytes = rows * Hkv * D * 2 * 2
     rope = cfg.rope()
 
     def step(i):
         q, k, v = sets[i % nsets]
         m.gqa_decode_window(q, k, v, lens, cfg.scale, window=0 if rolling else window,
-                            rolling=rolling, q_rope=rope, out=out, workspace=ws)
+                            rolling=rolling, q_rope=rope, out=out, workspace=ws, sinks=sinks)
 
     ms = timed_loop(step, steps, warmup)
-    label = f"rolling{window}" if rolling else f"window{window}"
+    label = (f"sink{sinks}_" if sinks else "") + (f"rolling{window}" if rolling else f"window{window}")
     log(f"[bench] decode {label} (32K contexts): step {ms * 1e3:.1f} us, {kv_bytes / ms / 1e6:.0f} GB/s")
     del sets
     torch.cuda.empty_cache()
     return dict(ms=ms, kv_bytes=kv_bytes, label=label)
 
 
-def bench_prefill(cfg, steps, warmup):
+def bench_prefill(cfg, steps, warmup, fp16_scores=False):
+    """gqa_prefill_causal on the 8K workload (scores from hi + lo operands,
+    three products: the matrix cores do 2x the algorithmic flops), or with
+    fp16_scores the one-product gqa_prefill_fp16."""
     import torch
 
     import mqa_kv_cache_amd as m
@@ -224,25 +235,19 @@ def bench_prefill(cfg, steps, warmup):
     flops = 2 * D * Hq * T * (T + 1) * B       # QK^T and PV over the causal triangle incl. diagonal
 
     def step(i):
-        m.gqa_prefill_causal(q, k, v, cfg.scale, rope=cfg.rope(), out=out, workspace=ws)
+        m.gqa_prefill_causal(q, k, v, cfg.scale, rope=cfg.rope(), out=out, workspace=ws,
+                             fp16_scores=fp16_scores)
 
     ev_ms = region_ms(step, max(steps // 2, 5), max(warmup // 2, 2))
     tf = flops / ev_ms / 1e9
-    # context: what the vendor GEMM (torch.matmul -> hipBLASLt) reaches on the
-    # same GPU in the same run, a practical ceiling for dense bf16 MFMA work
-    n = 8192
-    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
-    bm = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
-    gemm_ms = region_ms(lambda i: a @ bm, 10, 3)
-    gemm_tf = 2 * n ** 3 / gemm_ms / 1e9
-    del a, bm
-    log(f"[bench] prefill T={T}: {ev_ms * 1e3:.1f} us per call, {tf:.1f} TFLOP/s "
-        f"(library bf16 GEMM {n}^3 on this GPU: {gemm_tf:.0f} TFLOP/s)")
-    return dict(ev_ms=ev_ms, flops=flops, tflops=tf, gemm_tflops=gemm_tf)
+    log(f"[bench] prefill T={T}{' fp16 scores' if fp16_scores else ''}: {ev_ms * 1e3:.1f} us per "
+        f"call, {tf:.1f} TFLOP/s")
+    return dict(ev_ms=ev_ms, flops=flops, tflops=tf, mfma_work=1.0 if fp16_scores else 2.0)
 
 
-def bench_prefill_window(cfg, steps, warmup, window=4096):
-    """gqa_prefill_window on the 8K prefill with a `window`-token band."""
+def bench_prefill_window(cfg, steps, warmup, window=4096, sinks=0):
+    """gqa_prefill_window on the 8K prefill with a `window`-token band (and
+    `sinks` sink tokens beside it: gqa_prefill_sink_window)."""
     import torch
 
     import mqa_kv_cache_amd as m
@@ -254,17 +259,19 @@ def bench_prefill_window(cfg, steps, warmup, window=4096):
     out = torch.empty_like(q)
     ws = torch.empty(m.gqa_prefill_workspace_size(B, Hkv, T, D, cfg.rope()), dtype=torch.uint8,
                      device="cuda")
-    pairs = sum(min(i + 1, window) for i in range(T))      # visible (query, key) pairs per head
+    # visible (query, key) pairs per head: the band plus the sinks below it
+    pairs = sum(min(i + 1, window) + min(sinks, max(0, i + 1 - window)) for i in range(T))
     flops = 4 * D * Hq * pairs * B                          # QK^T and PV, 2 flops per product
 
     def step(i):
         m.gqa_prefill_causal(q, k, v, cfg.scale, rope=cfg.rope(), out=out, workspace=ws,
-                             window=window)
+                             window=window, sinks=sinks)
 
     ev_ms = region_ms(step, max(steps // 2, 5), max(warmup // 2, 2))
     tf = flops / ev_ms / 1e9
-    log(f"[bench] prefill T={T} window {window}: {ev_ms * 1e3:.1f} us per call, {tf:.1f} TFLOP/s")
-    return dict(ev_ms=ev_ms, flops=flops, tflops=tf, window=window)
+    label = (f"sink{sinks}_" if sinks else "") + f"window{window}"
+    log(f"[bench] prefill T={T} {label}: {ev_ms * 1e3:.1f} us per call, {tf:.1f} TFLOP/s")
+    return dict(ev_ms=ev_ms, flops=flops, tflops=tf, label=label)
 
 
 def bench_sparse(cfg, steps, warmup):
@@ -479,10 +486,15 @@ def main():
     if want("window"):
         res["dw"] = bench_decode_window(DECODE_32K_YARN, K, W, 4096, False)
         res["dr"] = bench_decode_window(DECODE_32K_YARN, K, W, 4096, True)
+    if want("sinks"):
+        res["ds"] = bench_decode_window(DECODE_32K_YARN, K, W, 4096, False, sinks=4)
     if want("prefill"):
         res["p"] = bench_prefill(PREFILL_8K, K, W)
+    if want("prefill_fp16"):
+        res["pf"] = bench_prefill(PREFILL_8K, K, W, fp16_scores=True)
     if want("prefill_window"):
         res["pw"] = bench_prefill_window(PREFILL_8K, K, W)
+        res["pws"] = bench_prefill_window(PREFILL_8K, K, W, sinks=4)
     if want("sparse"):
         res["s"] = bench_sparse(SPARSE_128K, K, W)
     if want("sparse_weighted"):
@@ -553,25 +565,28 @@ def main():
         line["decode_append_32k"] = {"GB/s": round(da["kv_bytes"] / da["ms"] / 1e6, 1),
                                      "pct_of_hbm_peak": round(100 * da["kv_bytes"] / da["ms"] / 1e6 / HBM_PEAK_GBS, 2),
                                      "ms_per_step": round(da["ms"], 5)}
-    for key in ("dw", "dr"):
+    for key in ("dw", "dr", "ds"):
         if key in res:
             r = res[key]
             line[f"decode_{r['label']}_32k"] = {
                 "GB/s": round(r["kv_bytes"] / r["ms"] / 1e6, 1),
                 "pct_of_hbm_peak": round(100 * r["kv_bytes"] / r["ms"] / 1e6 / HBM_PEAK_GBS, 2),
                 "ms_per_step": round(r["ms"], 5)}
-    if "p" in res:
-        p = res["p"]
-        line["prefill_8k"] = {"TFLOP/s": round(p["tflops"], 1),
-                              "pct_of_mfma_peak": round(100 * p["tflops"] / BF16_PEAK_TFLOPS, 2),
-                              "ms_per_call": round(p["ev_ms"], 4), "flops": p["flops"],
-                              "bound": "mfma", "peak": BF16_PEAK_TFLOPS,
-                              "library_gemm_8192_TFLOP/s": round(p["gemm_tflops"], 1)}
-    if "pw" in res:
-        pw = res["pw"]
-        line[f"prefill_8k_window{pw['window']}"] = {
-            "TFLOP/s": round(pw["tflops"], 1), "pct_of_mfma_peak": round(100 * pw["tflops"] / BF16_PEAK_TFLOPS, 2),
-            "ms_per_call": round(pw["ev_ms"], 4), "flops": pw["flops"]}
+    for key, name in (("p", "prefill_8k"), ("pf", "prefill_8k_fp16_scores")):
+        if key in res:
+            p = res[key]
+            line[name] = {"TFLOP/s": round(p["tflops"], 1),
+                          "pct_of_mfma_peak": round(100 * p["tflops"] / BF16_PEAK_TFLOPS, 2),
+                          "ms_per_call": round(p["ev_ms"], 4), "flops": p["flops"],
+                          "matrix_core_flops_per_flop": p["mfma_work"],
+                          "bound": "mfma", "peak": BF16_PEAK_TFLOPS}
+    for key in ("pw", "pws"):
+        if key in res:
+            pw = res[key]
+            line[f"prefill_8k_{pw['label']}"] = {
+                "TFLOP/s": round(pw["tflops"], 1),
+                "pct_of_mfma_peak": round(100 * pw["tflops"] / BF16_PEAK_TFLOPS, 2),
+                "ms_per_call": round(pw["ev_ms"], 4), "flops": pw["flops"]}
     if "s" in res:
         s = res["s"]
         line["sparse_128k"] = {"GB/s": round(s["gbs"], 1), "ms_per_call": round(s["ms"], 5),
