@@ -152,6 +152,28 @@ gqa_status gqa_decode_parts(const void* q, const void* k_cache, const void* v_ca
                             int32_t n_parts, void* stream);
 
 /*
+ * gqa_decode_noalloc -- gqa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): no workspace argument, the per-piece softmax states go
+ * to a static scratch array of 16 MiB (16777216 bytes) that each device
+ * holds for the life of the process.  The call allocates nothing; its first
+ * call on a device looks up that device's copy of the array.
+ *   Limit: gqa_decode_workspace_size(B, Hq, Hkv, D, S_max) <= 16777216, else
+ *   GQA_ERR_WORKSPACE_TOO_SMALL and nothing is launched (the 32K and 4K
+ *   workloads of 16 sequences x 64 q heads need about 4.8 MB).
+ *   Sharing: every call on one device uses the same scratch, so calls that
+ *   overlap in time on one device (different streams, or host threads) race
+ *   and give wrong results; serialise them (one stream, or events).  Nothing
+ *   in the scratch needs to start at any value.
+ * Arguments, outputs, results (bit for bit those of gqa_decode) and other
+ * errors as gqa_decode.
+ */
+gqa_status gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t S_max, float scale,
+                              const gqa_rope_params* q_rope, void* out, void* stream);
+
+/*
  * Two-phase decode: gqa_decode_parts == gqa_decode_partial then
  * gqa_decode_combine with the same arguments.  The partial phase leaves in
  * the workspace one softmax state per piece (a run of rows of one context

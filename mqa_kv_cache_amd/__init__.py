@@ -28,7 +28,7 @@ ROPE_NONE, ROPE_PLAIN, ROPE_PI, ROPE_NTK, ROPE_YARN, ROPE_DYNAMIC_NTK = 0, 1, 2,
 
 EXPORTED = [
     "rope_apply", "gqa_decode", "gqa_decode_parts", "gqa_decode_append", "gqa_decode_window",
-    "gqa_decode_sink_window", "gqa_decode_workspace_size",
+    "gqa_decode_sink_window", "gqa_decode_noalloc", "gqa_decode_workspace_size",
     "gqa_decode_workspace_size_parts", "gqa_decode_partial", "gqa_decode_combine",
     "gqa_prefill_causal", "gqa_prefill_window", "gqa_prefill_sink_window", "gqa_prefill_fp16",
     "gqa_prefill_workspace_size",
@@ -94,6 +94,10 @@ _lib.gqa_decode_sink_window.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void
                                         _c_void_p, _c_int32, _c_int32, _c_int32, _c_int32,
                                         _c_int32, _c_int32, _c_int32, _c_int32, ctypes.c_float,
                                         _rope_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]
+_lib.gqa_decode_noalloc.restype = _c_int32
+_lib.gqa_decode_noalloc.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int32, _c_int32,
+                                    _c_int32, _c_int32, _c_int32, ctypes.c_float, _rope_p,
+                                    _c_void_p, _c_void_p]
 _lib.gqa_decode_parts.restype = _c_int32
 _lib.gqa_decode_parts.argtypes = _lib.gqa_decode.argtypes[:-1] + [_c_int32, _c_void_p]
 _lib.gqa_decode_partial.restype = _c_int32
@@ -257,6 +261,29 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, scale: float, q_rope=None, out=Non
     else:
         st = _lib.gqa_decode_parts(*args, int(n_parts), _stream(stream))
     _check(st, "gqa_decode")
+    return out
+
+
+def gqa_decode_noalloc(q, k_cache, v_cache, seq_lens, scale: float, q_rope=None, out=None,
+                       stream=None) -> torch.Tensor:
+    """gqa_decode without a workspace (the library's static per-device scratch;
+    calls overlapping on one device race).  Pass `out` to allocate nothing."""
+    B, Hq, D = q.shape
+    _, Hkv, S_max, _ = k_cache.shape
+    _shape(k_cache, (B, Hkv, S_max, D), "k_cache")
+    _shape(v_cache, (B, Hkv, S_max, D), "v_cache")
+    _shape(seq_lens, (B,), "seq_lens")
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, nm)
+    _dev(seq_lens, "seq_lens", dtype=torch.int32)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _shape(out, (B, Hq, D), "out")
+    _dev(out, "out")
+    st = _lib.gqa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                 seq_lens.data_ptr(), B, Hq, Hkv, D, S_max, float(scale),
+                                 rope_params(q_rope), out.data_ptr(), _stream(stream))
+    _check(st, "gqa_decode_noalloc")
     return out
 
 

@@ -208,6 +208,33 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                             workspace, workspace_bytes, 0, stream);
 }
 
+gqa_status gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t S_max, float scale, const gqa_rope_params* q_rope,
+                              void* out, void* stream) {
+    // the same validation as gqa_decode, then the size check against the
+    // static scratch; nothing is allocated
+    gqa_status st = check_decode_shape(B, Hq, Hkv, D, S_max);
+    if (st != GQA_OK) return st;
+    if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+    if (!q || !k_cache || !v_cache || !seq_lens || !out) return GQA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return GQA_ERR_INVALID_ARGUMENT;
+    RopeDev rd;
+    st = rope_prepare(q_rope, D, &rd, 0);
+    if (st != GQA_OK) return st;
+    const DecodeLayout lay = decode_layout(B, Hq, Hkv, D, kDecodeDefaultParts);
+    if (lay.total > kNoAllocScratchBytes) return GQA_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    st = from_hip(noalloc_scratch(&ws));
+    if (st != GQA_OK) return st;
+    st = from_hip(launch_gqa_decode_partial(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S_max,
+                                            scale, rd, ws, lay, (hipStream_t)stream));
+    if (st != GQA_OK) return st;
+    return from_hip(launch_gqa_decode_combine(seq_lens, B, Hq, Hkv, D, S_max, ws, lay, out,
+                                              (hipStream_t)stream));
+}
+
 gqa_status gqa_decode_sink_window(const void* q, const void* k_new, const void* v_new,
                                   void* k_cache, void* v_cache, const int32_t* seq_lens, int32_t B,
                                   int32_t Hq, int32_t Hkv, int32_t D, int32_t S_max, int32_t sinks,

@@ -33,9 +33,19 @@
 //
 // combine_partials_kernel merges the per-split (m, l, o) with log-sum-exp
 // rescaling; the result equals the softmax over the whole row.
+#include <mutex>
+
 #include "device_common.h"
 
 namespace gqa {
+
+// Scratch of the no-allocation decode entry point: the per-piece softmax
+// states live here instead of in a caller workspace.  Each device the
+// library runs on holds its own copy for the life of the process; its
+// device address is looked up once per device (noalloc_scratch) and only
+// that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -741,6 +751,30 @@ hipError_t launch_gqa_decode_combine(const int32_t* seq_lens, int32_t B, int32_t
         hipLaunchKernelGGL((decode_combine_kernel<64>), cgrid, dim3(256), 0, s, po, pml, seq_lens,
                            B, Hq, Hkv, S_max, lay.n_parts, (uint16_t*)out, cv);
     return hipGetLastError();
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    // once per device, with that device current: the array's device address
+    // (the host-side name of the array is not a device address)
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    *ptr = g_scratch_ptr[dev];
+    return *ptr ? hipSuccess : hipErrorInvalidSymbol;
 }
 
 }  // namespace gqa

@@ -44,6 +44,10 @@ struct DecodeLayout {
     size_t total;
 };
 constexpr int32_t kDecodeDefaultParts = 1024;
+// The no-allocation decode keeps its states in a static device array of this
+// size (one per device); noalloc_scratch returns the current device's copy.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(void** ptr);
 DecodeLayout decode_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t n_parts);
 
 hipError_t launch_gqa_decode_partial(const void* q, const void* k_cache, const void* v_cache,

@@ -173,6 +173,22 @@ def test_prefill_window_validation(m):
                                   None) == m.ERR_WORKSPACE_TOO_SMALL
 
 
+def test_decode_noalloc_validation(m):
+    """The no-allocation decode validates like gqa_decode and rejects shapes
+    whose states exceed its 16 MiB static scratch before touching a device."""
+    lib = m.lib()
+
+    def call(B=2, Hq=16, Hkv=2, D=128, S=64, q=P, out=P):
+        return lib.gqa_decode_noalloc(q, P, P, P, B, Hq, Hkv, D, S, 0.1, None, out, None)
+    assert call(Hq=15) == m.ERR_INVALID_ARGUMENT
+    assert call(D=96) == m.ERR_UNSUPPORTED
+    assert call(q=None) == m.ERR_INVALID_ARGUMENT
+    assert call(out=MIS) == m.ERR_INVALID_ARGUMENT
+    # 4096 sequences x 8 kv heads: (1024 + 32768) slots x 8 heads x 128 x 4 B > 16 MiB
+    assert m.gqa_decode_workspace_size(4096, 64, 8, 128, 64) > (16 << 20)
+    assert call(B=4096, Hq=64, Hkv=8) == m.ERR_WORKSPACE_TOO_SMALL
+
+
 def test_sink_window_validation(m):
     """StreamingLLM entry points: negative sinks, a rolling buffer with no
     ring slot left, and the usual shape/workspace checks."""
