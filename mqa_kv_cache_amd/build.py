@@ -15,9 +15,10 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, out_path: str = LIB, defines=()) -> str:
+def build(verbose: bool = False, out_path: str = LIB, defines=(), extra_flags=()) -> str:
     """Compile every HIP source into mqa_kv_cache_amd/libgqa_attn.so (or
-    out_path, with extra -D defines for tuning builds); return its path."""
+    out_path, with extra -D defines or compiler flags for tuning builds);
+    return its path."""
     objs = []
     build_dir = os.path.join(os.path.dirname(out_path), "_build")
     os.makedirs(build_dir, exist_ok=True)
@@ -25,7 +26,8 @@ def build(verbose: bool = False, out_path: str = LIB, defines=()) -> str:
     for src in SOURCES:
         obj = os.path.join(build_dir, src.replace(".", "_") + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = ([HIPCC] + [f for f in FLAGS if f != "-shared"] + [f"-D{d}" for d in defines] + lang
+        cmd = ([HIPCC] + [f for f in FLAGS if f != "-shared"] + [f"-D{d}" for d in defines]
+               + list(extra_flags) + lang
                + ["-c", os.path.join(CSRC, src), "-o", obj])
         procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         objs.append(obj)

@@ -98,11 +98,4 @@ hipError_t launch_rope_apply(const void* in, void* out, const int32_t* positions
     return hipGetLastError();
 }
 
-hipError_t launch_rope_rows(const void* in, void* out, int64_t n_tok, int32_t n_heads,
-                            int32_t head_dim, int64_t stride_tok, int64_t stride_head,
-                            const RopeDev& rope, hipStream_t s) {
-    return launch_rope_apply(in, out, nullptr, n_tok, n_heads, head_dim, stride_tok, stride_head,
-                             rope, s);
-}
-
 }  // namespace gqa
