@@ -14,7 +14,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgqa_attn.so")
+# MQA_KV_CACHE_AMD_LIB names another build of the same library (e.g. one
+# with a sanitized host layer); the default is the in-tree build.
+LIB_PATH = os.environ.get("MQA_KV_CACHE_AMD_LIB") or os.path.join(_HERE, "libgqa_attn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

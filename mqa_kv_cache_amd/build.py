@@ -15,7 +15,7 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, out_path: str = LIB, defines=(), extra_flags=()) -> str:
+def build(verbose: bool = False, out_path: str = LIB, defines=(), extra_flags=(), link_flags=()) -> str:
     """Compile every HIP source into mqa_kv_cache_amd/libgqa_attn.so (or
     out_path, with extra -D defines or compiler flags for tuning builds);
     return its path."""
@@ -45,7 +45,7 @@ def build(verbose: bool = False, out_path: str = LIB, defines=(), extra_flags=()
     if failed:
         raise RuntimeError("hipcc failed")
     tmp = out_path + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + list(link_flags) + ["-o", tmp] + objs
     subprocess.run(cmd, check=True)
     os.replace(tmp, out_path)
     return out_path
