@@ -238,6 +238,39 @@ __device__ __forceinline__ void locate(const int32_t* seq_lens, int B, int Hkv, 
     L = 1;
 }
 
+// The wave's first piece: the row space total, the range length R, the
+// wave's first global row gs = w R and the context holding it (batch b, the
+// global row `base` of its (kv 0, row 0), its attended rows L).  With at
+// most 64 sequences one vector load of seq_lens and one wave-wide prefix sum
+// give all of them; more sequences take the chunked passes.  Returns false
+// when the wave's range is empty.
+__device__ __forceinline__ bool first_piece(const int32_t* seq_lens, int B, int Hkv, int S_max,
+                                            int n_parts, int w, int lane, const CacheView& cv,
+                                            int64_t& total, int64_t& R, int64_t& gs, int& b,
+                                            int64_t& base, int& L) {
+    if (B <= 64) {
+        const int Lb = lane < B ? ctx_len(seq_lens, lane, S_max, cv) : 0;
+        const int64_t incl = wave_scan_incl((int64_t)Hkv * Lb, lane);
+        total = __shfl(incl, 63, 64);
+        R = (total + n_parts - 1) / n_parts;
+        gs = (int64_t)w * R;
+        if (gs >= total) return false;
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < B && gs < incl);
+        const int f = __builtin_ctzll(hit);
+        b = f;
+        L = __shfl(Lb, f, 64);
+        base = __shfl(incl, f, 64) - (int64_t)Hkv * L;
+        return true;
+    }
+    const RowSpace rs = row_space(seq_lens, B, Hkv, S_max, n_parts, lane, cv);
+    total = rs.total;
+    R = rs.R;
+    gs = (int64_t)w * R;
+    if (gs >= total) return false;
+    locate(seq_lens, B, Hkv, S_max, gs, lane, cv, b, base, L);
+    return true;
+}
+
 // Per-lane RoPE frequencies of the q dims this lane holds (dims 32u + 8G ..
 // +7, pairs i = 16u + 4G + p), read once per wave: the table sits in the
 // kernel arguments and a lane-dependent index would otherwise cost a memory
@@ -443,21 +476,22 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
     // derived address and buffer descriptor in scalar registers
     const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
     if (w >= n_parts) return;
-    const RowSpace rs = row_space(seq_lens, B, Hkv, S_max, n_parts, lane, cv);
-    int64_t gs = (int64_t)w * rs.R;
-    const int64_t ge = min(gs + rs.R, rs.total);
-    if (gs >= ge) return;
-
-    // locate the context holding global row gs
+    int64_t total, R, gs, base;   // base: global row of (b, kv 0, row 0)
     int b, L;
-    int64_t base;   // global row of (b, kv 0, row 0)
-    locate(seq_lens, B, Hkv, S_max, gs, lane, cv, b, base, L);
+    if (!first_piece(seq_lens, B, Hkv, S_max, n_parts, w, lane, cv, total, R, gs, b, base, L))
+        return;
+    const int64_t ge = min(gs + R, total);
     b = __builtin_amdgcn_readfirstlane(b);
     L = __builtin_amdgcn_readfirstlane(L);
     CtxGeom geo = ctx_geom(seq_lens, b, S_max, cv);   // geo.n == L
     int kv = (int)((gs - base) / L);
     QFreq<D> fq;
     load_freq<D>(rope, G, fq);
+    const RowSpace rs{total, R};
+    // the first tile of the next segment or piece, requested with the last
+    // tile of the current one (pre_b: it went into tb rather than ta)
+    bool have_pre = false, pre_b = false;
+    DecodeTile<D> ta, tb;
 
     while (gs < ge) {
         const int64_t ctx0 = base + (int64_t)kv * L;        // global row of this context's row 0
@@ -480,15 +514,42 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
         const __amdgpu_buffer_rsrc_t vsr = make_rsrc(v_cache + slice, sbytes);
         const bool sink_seg = r0 < sa1;
 
+        // The piece after this one starts at row 0 of the next context; its
+        // first segment's buffers (none when this is the wave's last piece:
+        // an empty buffer reads zeros without traffic).
+        const int64_t gs_n = ctx0 + r1;
+        const uint16_t* nkp = k_cache;
+        const uint16_t* nvp = v_cache;
+        uint32_t nbytes_n = 0u;
+        if (gs_n < ge) {
+            const int kv_n = kv + 1 == Hkv ? 0 : kv + 1;
+            const int b_n = kv + 1 == Hkv ? b + 1 : b;
+            const CtxGeom geo_n = kv + 1 == Hkv ? ctx_geom(seq_lens, b_n, S_max, cv) : geo;
+            const int r1_n = (int)min((int64_t)geo_n.n, ge - gs_n);
+            const size_t slice_n = ((size_t)b_n * Hkv + kv_n) * (size_t)S_max * D;
+            if (geo_n.ns > 0) {          // its sink segment comes first
+                nkp = k_cache + slice_n;
+                nvp = v_cache + slice_n;
+                nbytes_n = (uint32_t)min(r1_n, geo_n.ns) * D * 2u;
+            } else {
+                nkp = k_cache + slice_n + (size_t)geo_n.lo * D;
+                nvp = v_cache + slice_n + (size_t)geo_n.lo * D;
+                nbytes_n = (uint32_t)r1_n * D * 2u;
+            }
+        }
+
         // q is requested first, then the first tiles; q is prepared while the
         // tiles are in flight
         u32x4 qraw[NB][KU];
         load_q_raw<D, NB>(q, b, kv, Hq, g, G, n, qraw);
         [[maybe_unused]] NewRow<D> nr;
         if constexpr (APPEND) load_new_row<D>(nr, app, ((size_t)b * Hkv + kv) * D, G, n);
-        DecodeTile<D> ta, tb;
-        if (sink_seg) load_tile<D>(ta, ksr, vsr, r0, G, n);
-        else load_tile<D>(ta, kr, vr, r0, G, n);
+        if (!have_pre) {
+            if (sink_seg) load_tile<D>(ta, ksr, vsr, r0, G, n);
+            else load_tile<D>(ta, kr, vr, r0, G, n);
+        } else if (pre_b) {
+            ta = tb;
+        }
 
         u32x4 qhi[NB][KU], qlo[NB][KU];
         prep_q<D, NB>(qraw, fq, geo.qpos + 1, qscale, rope, G, qhi, qlo);
@@ -514,26 +575,51 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
             if constexpr (APPEND)
                 if (ends && t0 <= r_new && r_new < t0 + 32) swap_new_row<D>(t, nr, rr_new, G, n);
         };
-        // tiles t0 = s0, s0 + 32, .. of rows [s0, s1), the first already in ta
-        auto segment = [&](__amdgpu_buffer_rsrc_t sk, __amdgpu_buffer_rsrc_t sv, int s0, int s1) {
+        // Tiles t0 = s0, s0 + 32, .. of rows [s0, s1), the first already in
+        // ta.  Each step requests the step after next's tile; the last step
+        // requests instead the first tile of what follows (row x0 of the
+        // buffers xk, xv), so the wave never waits a whole load latency
+        // between segments or pieces.  Returns true when that tile went into
+        // tb.
+        // (buffers are passed as base pointers and byte sizes, so the choice
+        // is a scalar select and every step issues the same loads)
+        struct Buf {
+            const uint16_t* k;
+            const uint16_t* v;
+            uint32_t bytes;
+        };
+        auto segment = [&](Buf sb, int s0, int s1, Buf xb, int x0) {
             for (int t0 = s0;;) {
-                load_tile<D>(tb, sk, sv, t0 + 32, G, n);
+                bool last = t0 + 32 >= s1;
+                load_tile<D>(tb, make_rsrc(last ? xb.k : sb.k, last ? xb.bytes : sb.bytes),
+                             make_rsrc(last ? xb.v : sb.v, last ? xb.bytes : sb.bytes),
+                             last ? x0 : t0 + 32, G, n);
                 fix(ta, t0);
                 tile_math<D, NB>(ta, t0, s1, G, qhi, qlo, o, m_run, l_run);
                 t0 += 32;
-                if (t0 >= s1) break;
-                load_tile<D>(ta, sk, sv, t0 + 32, G, n);
+                if (t0 >= s1) return true;
+                last = t0 + 32 >= s1;
+                load_tile<D>(ta, make_rsrc(last ? xb.k : sb.k, last ? xb.bytes : sb.bytes),
+                             make_rsrc(last ? xb.v : sb.v, last ? xb.bytes : sb.bytes),
+                             last ? x0 : t0 + 32, G, n);
                 fix(tb, t0);
                 tile_math<D, NB>(tb, t0, s1, G, qhi, qlo, o, m_run, l_run);
                 t0 += 32;
-                if (t0 >= s1) break;
+                if (t0 >= s1) return false;
             }
         };
+        const Buf band{k_cache + first, v_cache + first, nbytes};
+        const Buf next{nkp, nvp, nbytes_n};
         if (sink_seg) {
-            segment(ksr, vsr, r0, sa1);
-            if (sb0 < r1) load_tile<D>(ta, kr, vr, sb0, G, n);
+            const Buf sinkb{k_cache + slice, v_cache + slice, sbytes};
+            if (sb0 < r1) {
+                if (segment(sinkb, r0, sa1, band, sb0)) ta = tb;
+            } else {
+                pre_b = segment(sinkb, r0, sa1, next, 0);
+            }
         }
-        if (sb0 < r1) segment(kr, vr, sb0, r1);
+        if (sb0 < r1) pre_b = segment(band, sb0, r1, next, 0);
+        have_pre = true;
 
         if constexpr (APPEND)
             if (ends) {
