@@ -10,18 +10,20 @@
 //    The pass also builds the first radix-select histogram (top 12 bits of
 //    the non-negative fp32 score) in LDS and flushes it with atomics.
 // 2. top-k selection by radix select over the fp32 score bits: the first
-//    12-bit digit comes from the indexer's histogram, the keys of the bin
-//    that holds the k-th score are gathered (4096-key chunk workgroups) and
-//    refined to the exact k-th key T by one workgroup per batch row (or by
-//    extra passes over the scores when that bin is huge); chunk workgroups
-//    then count and write, in ascending index order, every score above T
-//    plus the first equal-to-T scores until k are taken.
+//    12-bit digit comes from the indexer's histogram; per 4096-key chunk a
+//    workgroup writes the keys at or above the bin holding the k-th score
+//    (every selected key is one of them) in index order; one workgroup per
+//    batch row then finds the exact k-th key T from those entries (or by
+//    extra passes over the scores when that bin is huge) and writes, in
+//    ascending index order, every key above T plus the first equal-to-T
+//    keys until k are taken.
 // 3. sparse_attn_kernel: MQA attention of the H heads over the gathered
 //    latent rows (the indexed rows are read straight from the cache; no copy
 //    of the selection is made).  Same MFMA structure as the dense decode:
-//    S^T = C . Q^T over 576 dims, online softmax, O^T += C[:, :512]^T . P^T;
-//    a workgroup covers 32 heads and 128 selected rows staged through LDS and
-//    writes a partial (m, l, o) per head that combine_partials_kernel merges.
+//    S^T = C . Q^T over 576 dims, softmax, O^T += C[:, :512]^T . P^T; a
+//    workgroup covers 32 heads and 128 selected rows staged through LDS,
+//    eight waves each take 16 heads and 32 rows, their states are merged in
+//    LDS, and one partial (m, l, o) per head goes to combine_partials_kernel.
 // 4. mla_dense_kernel: the same attention over every row of the context
 //    (dense absorbed-MLA decode), 64 heads per workgroup, the rows streamed
 //    through a ring of LDS buffers.
@@ -598,17 +600,19 @@ __global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(
 // ---------------------------------------------------------------------------
 // 3. attention over the selected latent rows
 // ---------------------------------------------------------------------------
-// One workgroup per (128 selected rows, 32 heads, batch row), two waves of 16
-// heads.  The gathered latent rows are staged in LDS in four 32-row
-// sub-chunks, all requested at once and copied straight from global memory
-// by buffer loads into LDS, so each row is fetched once per 32 heads instead
-// of once per 16 and per operand, and the gather latency is paid once.  Per sub-chunk each wave computes
+// One workgroup per (128 selected rows, 32 heads, batch row), eight waves:
+// two head groups of 16 heads times four 32-row sub-chunks.  The gathered
+// latent rows are copied straight from global memory into LDS by buffer
+// loads (all four sub-chunks requested at once, so the gather latency is
+// paid once), each row fetched once per 32 heads.  Wave (group, sub-chunk)
+// computes
 //   S^T[32 rows][16 heads] = C . Q^T   (18 k-steps of 16x16x32 bf16 MFMA)
-// folds it into its running softmax state and accumulates
-//   O^T[512][16 heads] += C[:, :512]^T . P^T,
-// and at the end writes one partial per (chunk, head) for
-// combine_partials_kernel.
-constexpr int kAttnWaves = 2;                        // 16 heads each
+//   O^T[512][16 heads]     = C[:, :512]^T . P^T   (P as hi + lo bf16)
+// with its softmax state; the four states of a head group are merged in LDS
+// and one partial per (chunk, head) goes to combine_partials_kernel.
+// (Two waves walking the four sub-chunks one after the other: 1.5 us slower
+// per call; 64 or 128 heads per workgroup, fewer re-reads of each row but
+// fewer workgroups: 1.5 and 10 us slower.)
 constexpr int kSubRows = 32;                         // rows per LDS sub-chunk
 constexpr int kRowBytes = kDqk * 2;                  // 1152
 constexpr int kRowStride = kRowBytes + 16;           // padded: 8 consecutive rows hit distinct banks
@@ -676,22 +680,63 @@ __device__ __forceinline__ void sparse_sub_step(const uint8_t* rows, const u32x4
     }
 }
 
+// Eight-wave variant: one workgroup per (128 selected rows, 32 heads, batch
+// row) as above, but wave (hgw, sc) = (w & 1, w >> 1) takes only row
+// sub-chunk sc for head group hgw, so the four sub-chunks are processed at
+// once instead of one after the other.  The four states of a head group
+// are then merged through LDS (the row buffers, free by then) in two rounds
+// of log-sum-exp rescaling, and wave sc = 0 writes the chunk's partial.
+// q is requested together with the selected indices; the copies follow the
+// first barrier, and one wait covers both the copies and q.
+constexpr int kAttnWaves = 8;
+constexpr int kAttnGroups = 2;                                      // 16 heads each
+
+__device__ __forceinline__ void merge_state(f32x4 (&o)[4][8], float& m_run, float& l_run,
+                                            const f32x4* slot, const float* ml, int lane, int n) {
+    const float mb = ml[2 * n], lb = ml[2 * n + 1];
+    const float M = fmaxf(m_run, mb);
+    if (M == -INFINITY) return;                 // both halves empty
+    const float a = fast_exp2(m_run - M), c = fast_exp2(mb - M);
+    l_run = a * l_run + c * lb;
+    m_run = M;
+#pragma unroll
+    for (int dq = 0; dq < 4; ++dq)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 ob = slot[(dq * 8 + t) * 64 + lane];
+            o[dq][t] = a * o[dq][t] + c * ob;
+        }
+}
+
+__device__ __forceinline__ void put_state(const f32x4 (&o)[4][8], float m_run, float l_run,
+                                          f32x4* slot, float* ml, int lane, int G, int n) {
+#pragma unroll
+    for (int dq = 0; dq < 4; ++dq)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) slot[(dq * 8 + t) * 64 + lane] = o[dq][t];
+    if (G == 0) {
+        ml[2 * n] = m_run;
+        ml[2 * n + 1] = l_run;
+    }
+}
+
 __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ seq_lens, int H, int S_max,
     int top_k, float qscale, float* __restrict__ part_o, float* __restrict__ part_ml,
     int n_chunks) {
     constexpr int KU = kDqk / 32;
-    // one buffer per sub-chunk, as separate LDS objects (the compiler then
-    // knows a read does not alias the copies still in flight)
+    static_assert(kSubBytes >= 64 * 32 * 16, "a state slot fits a row buffer");
     __shared__ __attribute__((aligned(16))) uint8_t rows0[kSubBytes];
     __shared__ __attribute__((aligned(16))) uint8_t rows1[kSubBytes];
     __shared__ __attribute__((aligned(16))) uint8_t rows2[kSubBytes];
     __shared__ __attribute__((aligned(16))) uint8_t rows3[kSubBytes];
     __shared__ int32_t sel_s[kRowsPerChunk];
+    __shared__ float ml_s[kAttnGroups][2][32];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hgw = wave & 1, sc = wave >> 1;
     const int G = lane >> 4, n = lane & 15;
     const int chunk = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
     const int L = min(max(seq_lens[b], 1), S_max);
@@ -699,28 +744,24 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
     const int c0 = chunk * kRowsPerChunk;
     if (c0 >= k) return;                        // whole workgroup
     const int c1 = min(c0 + kRowsPerChunk, k);
-    const int nsub = (c1 - c0 + kSubRows - 1) / kSubRows;
-    const int h = hg * (16 * kAttnWaves) + 16 * wave + n;
-    const bool heads = hg * (16 * kAttnWaves) + 16 * wave < H;   // wave-uniform (H % 16 == 0)
+    const int h = hg * (16 * kAttnGroups) + 16 * hgw + n;
+    const bool heads = hg * (16 * kAttnGroups) + 16 * hgw < H;   // wave-uniform (H % 16 == 0)
 
-    // q and the selected indices are requested together; the barrier's
-    // wait covers both, so the copies below start after one load latency
-    // (a wave past the last head still copies its share and meets the barriers)
+    // the selected indices, then q (its latency overlaps the copies)
+    int32_t sel = -1;
+    if (tid < kRowsPerChunk && c0 + tid < c1) sel = topk_idx[(size_t)b * top_k + c0 + tid];
     u32x4 qf[KU];
     const uint16_t* qrow = q + ((size_t)b * H + (heads ? h : 0)) * kDqk;
 #pragma unroll
     for (int u = 0; u < KU; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + 32 * u + 8 * G);
-    for (int i = tid; i < kRowsPerChunk; i += 64 * kAttnWaves)
-        sel_s[i] = c0 + i < c1 ? topk_idx[(size_t)b * top_k + c0 + i] : -1;
+    if (tid < kRowsPerChunk) sel_s[tid] = sel;
     __syncthreads();
 
     const __amdgpu_buffer_rsrc_t cr =
         make_rsrc(latent + (size_t)b * S_max * kDqk, (uint32_t)S_max * kDqk * 2u);
-    // This wave's copies: copy j = kAttnWaves * i + wave fills LDS bytes
-    // [1024 j, +1024) of a sub-chunk buffer, lane l the 16 bytes at 1024 j + 16 l,
-    // i.e. row r = x / kRowStride, column x mod kRowStride.  The (row, column)
-    // of each of the lane's copies is the same for every sub-chunk; only the
-    // row index read from sel_s changes, and those reads are batched.
+    // copy j of sub-chunk s fills LDS bytes [1024 j, +1024) of its buffer,
+    // lane l the 16 bytes at 1024 j + 16 l (row x / kRowStride, column
+    // x mod kRowStride); wave w takes copies j = 8 i + w of every sub-chunk
     constexpr int kCopiesPerWave = (kSubCopies + kAttnWaves - 1) / kAttnWaves;
     int rr[kCopiesPerWave], cc[kCopiesPerWave];
 #pragma unroll
@@ -729,10 +770,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
         rr[i] = x / kRowStride;
         cc[i] = x - rr[i] * kRowStride;
     }
-    auto copy_sub = [&](int s, uint8_t* dst) {
+    auto copy_sub = [&](int s2, uint8_t* dst) {
         int idx[kCopiesPerWave];
 #pragma unroll
-        for (int i = 0; i < kCopiesPerWave; ++i) idx[i] = sel_s[kSubRows * s + min(rr[i], kSubRows - 1)];
+        for (int i = 0; i < kCopiesPerWave; ++i) idx[i] = sel_s[kSubRows * s2 + min(rr[i], kSubRows - 1)];
         int wv = wave;
         asm volatile("" : "+s"(wv));
 #pragma unroll
@@ -745,18 +786,14 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
             }
         }
     };
-
-    // q is complete before the copies are issued (the barrier waited for
-    // it): the compiler's wait counts do not include loads into LDS, so a
-    // wait for q placed after them would also wait for every copy
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_sched_barrier(0);
-    // all four sub-chunks are requested at once: one gather latency per chunk
-    // (rows past the selection read as zeros without traffic)
     copy_sub(0, rows0);
     copy_sub(1, rows1);
     copy_sub(2, rows2);
     copy_sub(3, rows3);
+    // every wave's copies and q are complete, then the barrier makes all
+    // copies visible (the asm memory clobber keeps the LDS reads below it)
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("s_barrier" ::: "memory");
 
     f32x4 o[4][8];
 #pragma unroll
@@ -764,35 +801,26 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
 #pragma unroll
         for (int t = 0; t < 8; ++t) o[dq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
+    const int p0 = c0 + kSubRows * sc;
+    if (heads && p0 < c1) {
+        const uint8_t* rows = sc == 0 ? rows0 : sc == 1 ? rows1 : sc == 2 ? rows2 : rows3;
+        sparse_sub_step(rows, qf, o, m_run, l_run, p0, c1, qscale, G, n);
+    }
+    __syncthreads();                            // the row buffers are free from here
 
-    // Sub-chunk s is complete once at most the copies of the later sub-chunks
-    // are outstanding (every wave issues at least kCopiesMin per sub-chunk;
-    // vmcnt counts in issue order); a plain s_barrier then makes every wave's
-    // copies visible.  (__syncthreads would add a vmcnt(0) for its fence and
-    // wait for all four sub-chunks.)  The asm memory clobber keeps the LDS
-    // reads below the barrier.
-    constexpr int kCopiesMin = kSubCopies / kAttnWaves;
-    static_assert(3 * kCopiesMin < 64, "vmcnt range");
-    auto wait_sub = [&](auto later) {   // later: copies of later sub-chunks allowed in flight
-        constexpr int v = decltype(later)::value;
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (v & 15) | ((v >> 4) << 14));
-        asm volatile("s_barrier" ::: "memory");
+    // merge round 1: sc 1 -> 0 and 3 -> 2 (slots in buffers 2 hgw + sc / 2)
+    auto slot = [&](int i) {
+        return reinterpret_cast<f32x4*>(i == 0 ? rows0 : i == 1 ? rows1 : i == 2 ? rows2 : rows3);
     };
-    wait_sub(std::integral_constant<int, 3 * kCopiesMin>{});
-    if (heads) sparse_sub_step(rows0, qf, o, m_run, l_run, c0, c1, qscale, G, n);
-    if (nsub > 1) {
-        wait_sub(std::integral_constant<int, 2 * kCopiesMin>{});
-        if (heads) sparse_sub_step(rows1, qf, o, m_run, l_run, c0 + kSubRows, c1, qscale, G, n);
-    }
-    if (nsub > 2) {
-        wait_sub(std::integral_constant<int, kCopiesMin>{});
-        if (heads) sparse_sub_step(rows2, qf, o, m_run, l_run, c0 + 2 * kSubRows, c1, qscale, G, n);
-    }
-    if (nsub > 3) {
-        wait_sub(std::integral_constant<int, 0>{});
-        if (heads) sparse_sub_step(rows3, qf, o, m_run, l_run, c0 + 3 * kSubRows, c1, qscale, G, n);
-    }
-    if (!heads) return;
+    if (sc & 1) put_state(o, m_run, l_run, slot(2 * hgw + (sc >> 1)), ml_s[hgw][sc >> 1], lane, G, n);
+    __syncthreads();
+    if (!(sc & 1)) merge_state(o, m_run, l_run, slot(2 * hgw + (sc >> 1)), ml_s[hgw][sc >> 1], lane, n);
+    __syncthreads();
+    // round 2: sc 2 -> 0
+    if (sc == 2) put_state(o, m_run, l_run, slot(2 * hgw), ml_s[hgw][0], lane, G, n);
+    __syncthreads();
+    if (sc != 0 || !heads) return;
+    merge_state(o, m_run, l_run, slot(2 * hgw), ml_s[hgw][0], lane, n);
 
     const size_t idx = ((size_t)b * H + h) * n_chunks + chunk;
     float* po = part_o + idx * kDv;
@@ -1746,7 +1774,8 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
                        topk_idx);
     hipLaunchKernelGGL(topk_finish_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, seq_lens, S_max,
                        S_stride, top_k, cand, cand_idx, cand_cnt, nkc, info, topk_idx);
-    hipLaunchKernelGGL(sparse_attn_kernel, dim3(lay.n_chunks, (H + 16 * kAttnWaves - 1) / (16 * kAttnWaves), B),
+    hipLaunchKernelGGL(sparse_attn_kernel,
+                       dim3(lay.n_chunks, (H + 16 * kAttnGroups - 1) / (16 * kAttnGroups), B),
                        dim3(64 * kAttnWaves), 0, s,
                        (const uint16_t*)q, (const uint16_t*)latent, topk_idx, seq_lens, H, S_max,
                        top_k, scale * kLog2e, po, pml, lay.n_chunks);
