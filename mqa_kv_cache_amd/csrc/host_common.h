@@ -79,6 +79,8 @@ struct SparseLayout {
                            // chunk, u32 [B][key chunks][4096] their indices, u32 [B][key chunks]
                            // their counts
     size_t info_bytes;     // per-batch threshold bin and the count above it
+    size_t refine_bytes;   // multi-head indexers' band re-scoring: u32 [B][8] state, u32 [B][256]
+                           // band, f64 [B][256] exact scores, u32 [B][4096] keys certainly in
     size_t o_bytes;        // fp32 attention partials
     size_t ml_bytes;
     size_t total;

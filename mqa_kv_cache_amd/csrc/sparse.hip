@@ -225,6 +225,8 @@ __global__ __launch_bounds__(256) void indexer_weighted_kernel(
             k_index + ((size_t)b * S_max + r_begin) * kDidx, (uint32_t)nrows * kDidx * 2u);
         const __amdgpu_buffer_rsrc_t sr =
             make_rsrc(keys + (size_t)b * S_stride + r_begin, (uint32_t)nrows * 4u);
+        // the largest squared key norm seen (rows past the block read as zero)
+        float kmax = 0.f;
         // A operand of 16-key group g: lane (G, n) holds key 16 g + n, dims
         // 32 u + 8 G .. +7 (each load covers 64 contiguous bytes of 16 rows)
         auto load = [&](u32x4 (&kk)[4], int g) {
@@ -233,6 +235,16 @@ __global__ __launch_bounds__(256) void indexer_weighted_kernel(
                 kk[u] = buf_load16_nt(kr, (uint32_t)(((16 * g + n) * kDidx + 32 * u + 8 * G) * 2));
         };
         auto score = [&](const u32x4 (&kk)[4], int g) {
+            // |k|^2 of key 16 g + n: this lane's 32 dims, then its four lane groups
+            float n2 = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float a = bf16_lo(kk[u][j]), c = bf16_hi(kk[u][j]);
+                    n2 = fmaf(a, a, fmaf(c, c, n2));
+                }
+            kmax = fmaxf(kmax, rows4_sum(n2));
             float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int hb = 0; hb < NHB; ++hb) {
@@ -268,10 +280,16 @@ __global__ __launch_bounds__(256) void indexer_weighted_kernel(
             g += 8;
         }
         if (n_steps & 1) score(ka, g);
+        // bin 0 of the first-digit histogram is implied by the row length, so
+        // its slot carries the row's largest squared key norm (fp32 bits of a
+        // non-negative value order like the value) for the exact re-scoring
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) kmax = fmaxf(kmax, wave_shfl_xor(kmax, o));
+        if (lane == 0) atomicMax(&hist[(size_t)b * kHistBins], __float_as_uint(kmax));
     }
     __syncthreads();
     for (int i = tid; i < kHistBins; i += 256)
-        if (lh[i]) atomicAdd(&hist[(size_t)b * kHistBins + i], lh[i]);
+        if (i && lh[i]) atomicAdd(&hist[(size_t)b * kHistBins + i], lh[i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -472,6 +490,187 @@ __device__ void lower_digits(uint32_t B1, uint32_t need, uint32_t n, KeyAt key_a
     __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// Exact selection for the multi-head indexers.  Their scores are fp32 sums
+// from the matrix cores, within eps of the exact value.  Let T be the k-th
+// largest fp32 score: a key whose fp32 score exceeds T + 2 eps is in the
+// exact top k (every key whose exact score is at least its exact score has
+// an fp32 score above T, and fewer than k do), and a key below T - 2 eps is
+// out.  So only the band [T - 2 eps, T + 2 eps] is re-scored, in fp64
+// (products of bf16 values are exact; the sums of 128 of them are exact in
+// fp64 for any realistic spread of exponents), and the band's places go to
+// its best keys by exact score, ties to the lower index.
+//   weighted (DSA ①):  e_s = sum_h w_h ReLU(q_h . k_s).  An fp32 sum of n
+//     terms errs by at most gamma_n = n 2^-24 (to first order) times the sum
+//     of their magnitudes: 130 for each head's dot (bounded by |q_h| |k_s|,
+//     Cauchy-Schwarz) and about 72 for the weighted sum over the heads
+//     (whose terms are again at most |w_h| |q_h| |k_s|), so
+//     |e - E| <= 202 2^-24 W |k_s| < 2^-16.3 W |k_s|, W = sum_h |w_h| |q_h|;
+//     eps = 2^-15 W max_s |k_s| (twice that), the row's largest key norm
+//     coming from the indexer pass;
+//   QSA blocks (①-②):  e_j = sum_h ReLU(q_h . bk_j), |bk_j| = 1: the dots err
+//     by gamma_130 |q_h| plus the fp32 block key's own error (a few units of
+//     2^-22 relative) and the hi + lo split's 2^-17, the head sum by
+//     gamma_72; eps = 2^-14 sum_h |q_h| + 2^-20 |T| (about twice that); the
+//     block key is recomputed in fp64 (mean of the four keys, L2 norm, RoPE
+//     at 4 j) for the exact score.
+// Three steps: the finish kernel finds T and the band and writes the band
+// and the keys certainly in (sorted by index) to the workspace; the band
+// kernel scores the band on up to 16 CUs per row (an fp64 contraction on the
+// matrix cores); the merge kernel ranks the band by exact score and merges.  A band
+// of more than kBandCap keys (long runs of near-equal scores), or one from a
+// row whose threshold bin overflowed LDS, keeps the fp32 selection, which is
+// then exact up to those near-ties only.
+constexpr int kBandCap = 256;
+constexpr int kSureCap = 4096;   // keys certainly in: fewer than k <= 4096
+
+struct RefineArgs {
+    int mode;                  // 0: none (exact one-head scores), 1: weighted, 2: QSA blocks
+    int H_I;                   // indexer heads (<= 64)
+    const uint16_t* q_index;   // [B][H_I][128] bf16
+    const float* w_index;      // [B][H_I] (weighted)
+    const uint16_t* k_index;   // [B][S_tok][128] bf16 indexer keys
+    int S_tok;                 // rows of k_index per batch row
+    const uint32_t* knorm;     // weighted: fp32 bits of the row's largest |k_s|^2, row stride kHistBins
+    RopeDev rope;              // QSA block-key RoPE (half 0: none)
+    // per-row band state in the workspace
+    uint32_t* state;           // [B][8]: active, band size nb, keys certainly in c_in, need
+    uint32_t* band_idx;        // [B][kBandCap]
+    double* band_score;        // [B][kBandCap]
+    uint32_t* sure_in;         // [B][kSureCap] ascending
+};
+
+// fp32 score of an order-preserving key
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key >> 31) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// The band for one batch row, after the fp32 radix select found the k-th
+// key T (lk/li: the E entries of keys in bins >= B1 in index order;
+// keys_row: the row's n_keys fp32 keys).  Writes the band, the keys
+// certainly in (ascending) and the row's state (active = 1) to the
+// workspace and returns true, or returns false when the band does not
+// qualify (nothing written; the caller finishes the row in fp32).  Every
+// thread of the block calls it.
+__device__ bool band_setup(const RefineArgs& ra, int b, int n_keys, int k, uint32_t T, uint32_t B1,
+                           const uint32_t* lk, const uint32_t* li, uint32_t E,
+                           const uint32_t* keys_row, uint32_t* wsum, uint32_t* res, double* qn_h,
+                           float* fshared) {
+    static_assert(kSelThreads == 16 * 64, "16 threads per indexer head");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint16_t* qrow0 = ra.q_index + (size_t)b * ra.H_I * kDidx;
+    // ---- eps: |q_h| (times |w_h|) by 16 threads per head, 8 dims each
+    {
+        const int hh = tid >> 4, part = tid & 15;
+        double sq = 0.0;
+        if (hh < ra.H_I) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(qrow0 + (size_t)hh * kDidx + 8 * part);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const double a = bf16_lo(v[i]), c = bf16_hi(v[i]);
+                sq = fma(a, a, fma(c, c, sq));
+            }
+        }
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 64);
+        if (part == 0) {
+            double qn = sqrt(sq);
+            if (hh < ra.H_I && ra.mode == 1) qn *= fabs((double)ra.w_index[(size_t)b * ra.H_I + hh]);
+            qn_h[hh] = hh < ra.H_I ? qn : 0.0;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const double qn = wave_sum_f64(qn_h[lane]);
+        if (lane == 0) {
+            const double fT = key_value(T);
+            double eps;
+            if (ra.mode == 1)
+                eps = 0x1p-15 * qn * sqrt((double)__uint_as_float(ra.knorm[(size_t)b * kHistBins]));
+            else
+                eps = 0x1p-14 * qn + 0x1p-20 * fabs(fT);
+            eps = 2.0 * eps + 0x1p-20 * fabs(fT) + 1e-30;   // the band's half width, rounding slack
+            fshared[0] = (float)(fT - eps);
+            fshared[1] = (float)(fT + eps);
+            res[0] = 0u;                                    // band members found
+        }
+    }
+    __syncthreads();
+    const float lo_v = fshared[0], hi_v = fshared[1];
+    // keys of lo_v (rounded down) and hi_v (rounded up) in key order
+    auto okey = [](float v) {
+        v = (v == 0.0f) ? 0.0f : v;
+        const uint32_t u = __float_as_uint(v);
+        return (u >> 31) ? ~u : (u | 0x80000000u);
+    };
+    const uint32_t K_lo = okey(lo_v) - 1u, K_hi = okey(hi_v) + 1u;
+    uint32_t* band = ra.band_idx + (size_t)b * kBandCap;
+    uint32_t* sure = ra.sure_in + (size_t)b * kSureCap;
+    // ---- sure-in entries (key > K_hi) in index order, band entries appended
+    const uint32_t per = (E + kSelThreads - 1) / kSelThreads;
+    const uint32_t e0 = min((uint32_t)tid * per, E), e1 = min(e0 + per, E);
+    uint32_t nin = 0;
+    for (uint32_t e = e0; e < e1; ++e) {
+        const uint32_t key = lk[e];
+        nin += key > K_hi;
+        if (key >= K_lo && key <= K_hi) {
+            const uint32_t at = atomicAdd(&res[0], 1u);
+            if (at < (uint32_t)kBandCap) band[at] = li[e];
+        }
+    }
+    uint32_t pos = block_inclusive_scan<kSelThreads>(nin, wsum) - nin;
+    for (uint32_t e = e0; e < e1; ++e)
+        if (lk[e] > K_hi && pos < (uint32_t)kSureCap) sure[pos++] = li[e];
+    if (tid == kSelThreads - 1) res[1] = pos;      // keys certainly selected
+    // the band may reach below the first-digit bin of the entries: those keys
+    // are found in the row itself (four keys per request, several in flight)
+    if (K_lo < (B1 << 20)) {
+        const int n4 = n_keys >> 2;
+        const u32x4* k4 = reinterpret_cast<const u32x4*>(keys_row);
+        auto test = [&](uint32_t key, int i) {
+            if (key >= K_lo && key < (B1 << 20)) {
+                const uint32_t at = atomicAdd(&res[0], 1u);
+                if (at < (uint32_t)kBandCap) band[at] = (uint32_t)i;
+            }
+        };
+        constexpr int kU = 4;
+        for (int i0 = tid; i0 < n4; i0 += kU * kSelThreads) {
+            u32x4 v[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int i = i0 + u * kSelThreads;
+                v[u] = i < n4 ? k4[i] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int i = i0 + u * kSelThreads;
+                if (i < n4)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) test(v[u][c], 4 * i + c);
+            }
+        }
+        for (int i = 4 * n4 + tid; i < n_keys; i += kSelThreads) test(keys_row[i], i);
+    }
+    __syncthreads();
+    const uint32_t nb = res[0], c_in = res[1];
+    const int need = k - (int)c_in;
+    if (nb > (uint32_t)kBandCap || need < 0 || need > (int)nb) return false;   // uniform
+    if (tid == 0) {
+        uint32_t* st = ra.state + (size_t)b * 8;
+        st[1] = nb;
+        st[2] = c_in;
+        st[3] = (uint32_t)need;
+        st[0] = 1u;
+    }
+    return true;
+}
+
 // One workgroup per batch row: the exact k-th key T from the entries, then
 // the selected indices in ascending order (keys > T, and the first `ties`
 // keys == T by index).  The entries (at most k - 1 above the threshold bin
@@ -484,15 +683,18 @@ __global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int S_max, int S_stride,
     int top_k, const uint32_t* __restrict__ ent_key, const uint32_t* __restrict__ ent_idx,
     const uint32_t* __restrict__ ent_cnt, int n_chunks, const SelInfo* __restrict__ info,
-    int32_t* __restrict__ topk_idx) {
+    int32_t* __restrict__ topk_idx, RefineArgs ra) {
     __shared__ uint32_t h[kHistBins];
     __shared__ uint32_t lk[kEntCap], li[kEntCap];
     __shared__ uint16_t emap[kEntCap];
     __shared__ uint32_t wsum[kSelThreads / 64];
     __shared__ uint32_t res[2];
+    __shared__ double qn_h[64];
+    __shared__ float fshared[2];
     __shared__ uint32_t cstart[kSelThreads];   // entry offset of each chunk
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x;
+    if (ra.mode != 0 && tid == 0) ra.state[(size_t)b * 8] = 0u;   // band kernels: nothing to do
     const int L = min(max(seq_lens[b], 1), S_max);
     const int k = min(top_k, L);
     if (k == L) return;                        // written by the compact kernel
@@ -542,6 +744,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(
         }
         __syncthreads();
         lower_digits(B1, need, E, [&](uint32_t i) { return lk[i]; }, h, wsum, res, T, ties);
+        if (ra.mode != 0 &&
+            band_setup(ra, b, L, k, T, B1, lk, li, E,
+                       reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride), wsum, res,
+                       qn_h, fshared))
+            return;                            // the band kernels finish the row
         // thread t takes entries [t per, (t + 1) per): ranks of ties and
         // output slots from two block scans
         const uint32_t per = (E + kSelThreads - 1) / kSelThreads;
@@ -596,6 +803,235 @@ __global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(
         __syncthreads();
     }
 }
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// Raw indexer-key words of band member m for lane `lane` (pair `lane` of
+// its key row, or of the four rows of its block); zero past the band.
+__device__ __forceinline__ void band_rows(const RefineArgs& ra, const uint32_t* krows, const uint32_t* band,
+                                          uint32_t m, uint32_t nb, int lane, uint32_t (&r)[4]) {
+    r[0] = r[1] = r[2] = r[3] = 0u;
+    if (m >= nb) return;
+    const size_t j = band[m];
+    if (ra.mode == 1) {
+        r[0] = krows[j * (kDidx / 2) + lane];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = krows[(4 * j + i) * (kDidx / 2) + lane];
+    }
+}
+
+// Band member m's 128-dim vector x in fp64 from its raw key words (lane l:
+// dims 2l, 2l+1): the key itself, or the block key (mean of the four keys,
+// L2 norm, RoPE at position 4 j).  A member past the band gives zeros.
+__device__ __forceinline__ void band_vector(const RefineArgs& ra, const uint32_t* band, uint32_t m,
+                                            uint32_t nb, const uint32_t (&r)[4], int lane, double& x0,
+                                            double& x1) {
+    if (ra.mode == 1) {
+        x0 = (double)bf16_lo(r[0]);
+        x1 = (double)bf16_hi(r[0]);
+        return;
+    }
+    x0 = x1 = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x0 += (double)bf16_lo(r[i]);
+        x1 += (double)bf16_hi(r[i]);
+    }
+    x0 *= 0.25;
+    x1 *= 0.25;
+    const double nrm = sqrt(wave_sum_f64(x0 * x0 + x1 * x1));
+    if (nrm > 0.0) {
+        x0 /= nrm;
+        x1 /= nrm;
+    } else {
+        x0 = x1 = 0.0;
+    }
+    if (m < nb && lane < ra.rope.half) {
+        const double a = (double)(4 * (int)band[m]) * ra.rope.pos_scale * ra.rope.theta[lane];
+        double sn, c;
+        sincos(a, &sn, &c);
+        c *= (double)ra.rope.amp;
+        sn *= (double)ra.rope.amp;
+        const double y0 = x0 * c - x1 * sn, y1 = x0 * sn + x1 * c;
+        x0 = y0;
+        x1 = y1;
+    }
+}
+
+// The band's best `need` keys (exact score, then lower index) merged with
+// the keys certainly in, ascending, into the row's output: one workgroup per
+// batch row.  Each lane holds band entries lane + 64 i; a wave counts for
+// one member at a time how many entries rank ahead of it (ballots), then how
+// many chosen entries have a lower index: its place among the chosen.  The
+// lists are requested whole, with the row's state, before it is known how
+// much of them the row uses (the workspace slices are always in bounds).
+__global__ __launch_bounds__(kSelThreads) void band_merge_kernel(RefineArgs ra, int top_k,
+                                                                 int32_t* __restrict__ topk_idx) {
+    static_assert(kBandCap == 4 * 64 && kSelThreads == 1024 && kSureCap == 4 * kSelThreads,
+                  "four band entries per lane, four sure entries per thread");
+    __shared__ uint32_t sure[kSureCap];
+    __shared__ uint32_t bidx[kBandCap], bsorted[kBandCap], bflag[kBandCap];
+    __shared__ double bscore[kBandCap];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.x;
+    const uint32_t* st = ra.state + (size_t)b * 8;
+    const uint32_t active = st[0], nb = st[1], c_in = st[2], need = st[3];
+    const u32x4 sv = reinterpret_cast<const u32x4*>(ra.sure_in + (size_t)b * kSureCap)[tid];
+    uint32_t bi = 0u;
+    double bs = 0.0;
+    if (tid < kBandCap) {
+        bi = ra.band_idx[(size_t)b * kBandCap + tid];
+        bs = ra.band_score[(size_t)b * kBandCap + tid];
+    }
+    if (active == 0u) return;            // uniform
+    reinterpret_cast<u32x4*>(sure)[tid] = sv;
+    if (tid < kBandCap) {
+        bidx[tid] = bi;
+        bscore[tid] = bs;
+    }
+    __syncthreads();
+    double su[4];
+    uint32_t iu[4];
+    bool vu[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t u = lane + 64 * i;
+        vu[i] = u < nb;
+        su[i] = vu[i] ? bscore[u] : 0.0;
+        iu[i] = vu[i] ? bidx[u] : 0u;
+    }
+    for (uint32_t m = wave; m < nb; m += kSelThreads / 64) {
+        const double sm = bscore[m];
+        const uint32_t my = bidx[m];
+        uint32_t ahead = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ahead += __popcll(__ballot(vu[i] && (su[i] > sm || (su[i] == sm && iu[i] < my))));
+        if (lane == 0) bflag[m] = ahead < need;
+    }
+    __syncthreads();
+    bool cu[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cu[i] = vu[i] && bflag[lane + 64 * i];
+    for (uint32_t m = wave; m < nb; m += kSelThreads / 64) {
+        if (!bflag[m]) continue;         // uniform over the wave
+        const uint32_t my = bidx[m];
+        uint32_t below = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) below += __popcll(__ballot(cu[i] && iu[i] < my));
+        if (lane == 0) bsorted[below] = my;
+    }
+    __syncthreads();
+    auto lower = [](const uint32_t* a, uint32_t n, uint32_t x) {   // # of a[0..n) below x
+        uint32_t lo = 0, hi = n;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (a[mid] < x) lo = mid + 1;
+            else hi = mid;
+        }
+        return lo;
+    };
+    int32_t* outp = topk_idx + (size_t)b * top_k;
+    for (uint32_t i = tid; i < c_in; i += kSelThreads) {
+        const uint32_t x = sure[i];
+        outp[i + lower(bsorted, need, x)] = (int32_t)x;
+    }
+    for (uint32_t i = tid; i < need; i += kSelThreads) {
+        const uint32_t x = bsorted[i];
+        outp[i + lower(sure, c_in, x)] = (int32_t)x;
+    }
+}
+
+// Exact fp64 scores of 16 band members (m0 = 16 blockIdx.x) of batch row
+// blockIdx.y: the products of the H_I query heads with the members' vectors
+// as an fp64 contraction on the matrix cores (16 x 16 x 4 tiles).  Wave w
+// builds member m0 + w's vector into the B operand tile xb (column w), then
+// multiplies head tile w % 4 with the tile over dim quarter w / 4 (8 steps
+// of four dims); the quarters' partial dots are summed in order, then ReLU,
+// weight, and the heads summed (four per wave, then the 16 waves in order).
+// Operand layouts of the 16 x 16 x 4 fp64 instruction: lane l gives
+// A[l % 16][l / 16] (head 16 ht + l % 16, dim 4 s + l / 16, from qs) and
+// B[l / 16][l % 16] (dim 4 s + l / 16 of column l % 16), and holds
+// D[l / 16 + 4 r][l % 16] in register r.  B element (s, l) sits at
+// s * 64 + (l ^ (s & 31)) in xb, which spreads the builders' stores (two
+// dims of one column per lane) over the banks.  The band entry and its key rows are requested before the row's state is
+// known, with the row index clamped into the key array, so those loads stay
+// in bounds whatever the workspace holds.
+__global__ __launch_bounds__(kSelThreads) void band_score_kernel(RefineArgs ra) {
+    __shared__ u32x4 qs[16 * 64];        // dims 8 p4 .. 8 p4 + 7 of head h at [p4][h]
+    __shared__ double xb[32 * 64];
+    __shared__ double pd[4][64][16];     // [dim quarter][head][member] partial dots
+    __shared__ double ws[16][16];        // [wave][member] sums of four heads
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.y;
+    const uint32_t m0 = 16u * blockIdx.x;
+    const uint32_t* st = ra.state + (size_t)b * 8;
+    const uint32_t active = st[0], nb = st[1];
+    const uint32_t* band = ra.band_idx + (size_t)b * kBandCap;
+    const uint32_t* krows = reinterpret_cast<const uint32_t*>(ra.k_index + (size_t)b * ra.S_tok * kDidx);
+    // requests first: this wave's member rows, the query slice, the weight
+    const uint32_t n_rows = ra.mode == 1 ? (uint32_t)ra.S_tok : (uint32_t)ra.S_tok / 4;   // keys or blocks
+    uint32_t r[4] = {0u, 0u, 0u, 0u};
+    if (n_rows > 0) {
+        const uint32_t j = min(band[m0 + wave], n_rows - 1);
+        if (ra.mode == 1) {
+            r[0] = krows[(size_t)j * (kDidx / 2) + lane];
+            r[1] = r[2] = r[3] = 0u;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[i] = krows[(4 * (size_t)j + i) * (kDidx / 2) + lane];
+        }
+    }
+    const int hh = tid >> 4, p4 = tid & 15;
+    const u32x4 qv = hh < ra.H_I
+        ? *reinterpret_cast<const u32x4*>(ra.q_index + ((size_t)b * ra.H_I + hh) * kDidx + 8 * p4)
+        : u32x4{0u, 0u, 0u, 0u};
+    const double wh = hh >= ra.H_I ? 0.0 : ra.mode == 1 ? (double)ra.w_index[(size_t)b * ra.H_I + hh] : 1.0;
+    if (active == 0u || m0 >= nb) return;   // the row was finished in fp32, or no members here (uniform)
+    if (m0 + wave >= nb) r[0] = r[1] = r[2] = r[3] = 0u;
+    qs[p4 * 64 + hh] = qv;
+    {
+        double x0, x1;
+        band_vector(ra, band, m0 + wave, nb, r, lane, x0, x1);
+        const int s0 = lane >> 1, l0 = wave + 32 * (lane & 1);   // B lanes c + 16 q, q = 2 (lane % 2), + 1
+        xb[s0 * 64 + (l0 ^ (s0 & 31))] = x0;
+        xb[s0 * 64 + ((l0 + 16) ^ (s0 & 31))] = x1;
+    }
+    __syncthreads();
+    {
+        const int ht = wave & 3, kq = wave >> 2, col = lane & 15, qd = lane >> 4;
+        const uint16_t* qh = reinterpret_cast<const uint16_t*>(qs);
+        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int s = 8 * kq; s < 8 * kq + 8; ++s) {
+            const int d = 4 * s + qd;
+            const uint32_t q16 = qh[((d >> 3) * 64 + 16 * ht + col) * 8 + (d & 7)];
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)__uint_as_float(q16 << 16),
+                                                       xb[s * 64 + (lane ^ (s & 31))], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pd[kq][16 * ht + qd + 4 * i][col] = acc[i];
+    }
+    __syncthreads();
+    {
+        // thread (head hh, member p4): the full dot, ReLU, weight; four heads
+        // per wave summed across lanes (xor 16, 32), then the waves in order
+        const double dot = ((pd[0][hh][p4] + pd[1][hh][p4]) + pd[2][hh][p4]) + pd[3][hh][p4];
+        double v = wh * fmax(dot, 0.0);
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        if (lane < 16) ws[wave][lane] = v;
+    }
+    __syncthreads();
+    if (tid < 16 && m0 + tid < nb) {
+        double sc = 0.0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) sc += ws[w][tid];
+        ra.band_score[(size_t)b * kBandCap + m0 + tid] = sc;
+    }
+}
+
 
 // ---------------------------------------------------------------------------
 // 3. attention over the selected latent rows
@@ -1579,6 +2015,18 @@ __global__ __launch_bounds__(256) void qsa_combine_kernel(const float* __restric
 
 }  // namespace
 
+// The band re-scoring's buffers in the workspace region of refine_bytes.
+static void refine_buffers(char* w, int32_t B, RefineArgs& ra) {
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    ra.state = reinterpret_cast<uint32_t*>(w);
+    w += al((size_t)B * 8 * sizeof(uint32_t));
+    ra.band_idx = reinterpret_cast<uint32_t*>(w);
+    w += al((size_t)B * kBandCap * sizeof(uint32_t));
+    ra.band_score = reinterpret_cast<double*>(w);
+    w += al((size_t)B * kBandCap * sizeof(double));
+    ra.sure_in = reinterpret_cast<uint32_t*>(w);
+}
+
 SparseLayout sparse_layout(int32_t B, int32_t H, int32_t S_max, int32_t top_k) {
     SparseLayout l{};
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -1590,9 +2038,11 @@ SparseLayout sparse_layout(int32_t B, int32_t H, int32_t S_max, int32_t top_k) {
     // [B][key chunks][4096], then their counts [B][key chunks]
     l.cand_bytes = al((size_t)B * l.n_key_chunks * (2 * kChunkKeys + 1) * sizeof(uint32_t));
     l.info_bytes = al((size_t)B * sizeof(SelInfo));
+    l.refine_bytes = al((size_t)B * 8 * sizeof(uint32_t)) + al((size_t)B * kBandCap * sizeof(uint32_t)) +
+                     al((size_t)B * kBandCap * sizeof(double)) + al((size_t)B * kSureCap * sizeof(uint32_t));
     l.o_bytes = al((size_t)B * H * l.n_chunks * kDv * sizeof(float));
     l.ml_bytes = al((size_t)B * H * l.n_chunks * 2 * sizeof(float));
-    l.total = l.scores_bytes + l.hist_bytes + l.cand_bytes + l.info_bytes +
+    l.total = l.scores_bytes + l.hist_bytes + l.cand_bytes + l.info_bytes + l.refine_bytes +
               l.o_bytes + l.ml_bytes;
     return l;
 }
@@ -1630,6 +2080,8 @@ hipError_t launch_qsa_sparse_decode(const void* q, const void* k_cache, const vo
     w += sl.cand_bytes;
     SelInfo* info = reinterpret_cast<SelInfo*>(w);
     w += sl.info_bytes;
+    char* refine = w;
+    w += sl.refine_bytes;
     w += sl.o_bytes + sl.ml_bytes;   // (empty)
     int32_t* cnt = reinterpret_cast<int32_t*>(w);
     w += lay.cnt_bytes;
@@ -1670,8 +2122,18 @@ hipError_t launch_qsa_sparse_decode(const void* q, const void* k_cache, const vo
     }
     hipLaunchKernelGGL(topk_compact_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, hist, cnt,
                        NB, KS, kQsaTopBlocks, cand, cand_idx, cand_cnt, nkc, info, blk);
+    RefineArgs ra{};   // the block scores are fp32: re-score the band at the 512th
+    ra.mode = 2;
+    ra.H_I = H_I;
+    ra.q_index = qi;
+    ra.k_index = ki;
+    ra.S_tok = S_max;
+    ra.rope = rope;
+    refine_buffers(refine, B, ra);
     hipLaunchKernelGGL(topk_finish_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, cnt, NB, KS,
-                       kQsaTopBlocks, cand, cand_idx, cand_cnt, nkc, info, blk);
+                       kQsaTopBlocks, cand, cand_idx, cand_cnt, nkc, info, blk, ra);
+    hipLaunchKernelGGL(band_score_kernel, dim3(kBandCap / 16, B), dim3(kSelThreads), 0, s, ra);
+    hipLaunchKernelGGL(band_merge_kernel, dim3(B), dim3(kSelThreads), 0, s, ra, kQsaTopBlocks, blk);
     hipLaunchKernelGGL(gqa_gather_attn_kernel, dim3(kGChunks, Hkv, B), dim3(64), 0, s,
                        (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, blk,
                        seq_lens, Hq, Hkv, S_max, scale * kLog2e, tok, po, pml, kGChunks);
@@ -1732,6 +2194,8 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
     w += lay.cand_bytes;
     SelInfo* info = reinterpret_cast<SelInfo*>(w);
     w += lay.info_bytes;
+    char* refine = w;
+    w += lay.refine_bytes;
     float* po = reinterpret_cast<float*>(w);
     w += lay.o_bytes;
     float* pml = reinterpret_cast<float*>(w);
@@ -1772,8 +2236,23 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
     hipLaunchKernelGGL(topk_compact_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, hist,
                        seq_lens, S_max, S_stride, top_k, cand, cand_idx, cand_cnt, nkc, info,
                        topk_idx);
+    RefineArgs ra{};
+    if (H_I > 0) {   // the weighted indexer's fp32 scores: re-score the band at the k-th
+        ra.mode = 1;
+        ra.H_I = H_I;
+        ra.q_index = qi;
+        ra.w_index = w_index;
+        ra.k_index = ki;
+        ra.S_tok = S_max;
+        ra.knorm = hist;
+        refine_buffers(refine, B, ra);
+    }
     hipLaunchKernelGGL(topk_finish_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, seq_lens, S_max,
-                       S_stride, top_k, cand, cand_idx, cand_cnt, nkc, info, topk_idx);
+                       S_stride, top_k, cand, cand_idx, cand_cnt, nkc, info, topk_idx, ra);
+    if (ra.mode != 0) {
+        hipLaunchKernelGGL(band_score_kernel, dim3(kBandCap / 16, B), dim3(kSelThreads), 0, s, ra);
+        hipLaunchKernelGGL(band_merge_kernel, dim3(B), dim3(kSelThreads), 0, s, ra, top_k, topk_idx);
+    }
     hipLaunchKernelGGL(sparse_attn_kernel,
                        dim3(lay.n_chunks, (H + 16 * kAttnGroups - 1) / (16 * kAttnGroups), B),
                        dim3(64 * kAttnWaves), 0, s,
