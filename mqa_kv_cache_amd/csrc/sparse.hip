@@ -1051,7 +1051,7 @@ __global__ __launch_bounds__(kSelThreads) void band_score_kernel(RefineArgs ra) 
 // fewer workgroups: 1.5 and 10 us slower.)
 constexpr int kSubRows = 32;                         // rows per LDS sub-chunk
 constexpr int kRowBytes = kDqk * 2;                  // 1152
-constexpr int kRowStride = kRowBytes + 16;           // padded: 8 consecutive rows hit distinct banks
+constexpr int kRowStride = kRowBytes + 32;           // padded to 296 dwords (8 mod 16): see below
 constexpr int kSubCopies = (kSubRows * kRowStride + 1023) / 1024;   // 1 KB copies per sub-chunk
 constexpr int kSubBytes = kSubCopies * 1024;         // the last copy spills into slack nothing reads
 
@@ -1367,13 +1367,17 @@ __device__ __forceinline__ float dense_rowmax(const f32x4 (&sc)[2]) {
 // group, lane 4a + c of a ds_read_b64_tr_b16 receives element c of the
 // 8-byte chunks addressed by lanes a, a+4, a+8 and a+12.  Lane r of group G
 // addresses row (4G + r/4) [second read: 16 + 4G + r/4] at dims
-// tb + dv(r mod 4)..+3, dv(a) = 4 (a mod 2) + 64 (a / 2), so lane n receives
-// dim tb + dv(n/4) + n mod 4 of the four rows: the tile's A operand, with
-// k = the rows slot_row(G, 0..7) that the P operand uses.  The output tile
-// o[dq][t] (tb = 128 dq + 8 t) then holds dims tb + dv(G) + i.  The split
-// dims keep a 32-lane read on 64 distinct banks: with the 292-dword row
-// stride the eight rows start on distinct 4-bank groups mod 32, and each
-// row's four chunks take its group and the group 32 banks on.
+// tb + 4 (r mod 4)..+3, so lane n receives dim tb + n of the four rows: the
+// tile's A operand, with k = the rows slot_row(G, 0..7) that the P operand
+// uses, and the output tile o[dq][t] (tb = 128 dq + 16 t) holds dims
+// tb + 4G + i.
+// Banks (measured with the LDS bank-conflict counter on gfx950): a
+// transposing 8-byte read serves 32 lanes at a time from 64 banks, a 16-byte
+// read 16 lanes (lanes 0-7 with 16-23, and so on).  With the row stride at
+// 8 mod 16 dwords, the eight rows of a transposing read start 8 dwords apart
+// mod 64 and each reads 8 consecutive dwords: all 64 banks once; the score
+// reads (row n, 16-byte column G) and the top-k path's row reads also cover
+// the banks once.
 __device__ __forceinline__ void dense_pv(const uint8_t* rows, const f32x4 (&sc)[2], float m,
                                          f32x4 (&o)[4][8], float& l_run, int G, int n) {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -1396,7 +1400,7 @@ __device__ __forceinline__ void dense_pv(const uint8_t* rows, const f32x4 (&sc)[
         ph[k] = hl[0];
         pl[k] = hl[1];
     }
-    const uint8_t* v0 = rows + (4 * G + (n >> 2)) * kRowStride + 8 * (n & 1) + 128 * ((n >> 1) & 1);
+    const uint8_t* v0 = rows + (4 * G + (n >> 2)) * kRowStride + 8 * (n & 3);
     const uint8_t* v1 = v0 + 16 * kRowStride;
     // per 128-dim quarter: 16 reads, then the hi products of its eight tiles,
     // then the lo products (no MFMA waits on the one just before it)
@@ -1405,7 +1409,7 @@ __device__ __forceinline__ void dense_pv(const uint8_t* rows, const f32x4 (&sc)[
         u32x4 col[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const int off = (128 * dq + 8 * t) * 2;
+            const int off = (128 * dq + 16 * t) * 2;
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v0 + off));
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(v1 + off));
             col[t] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -1588,11 +1592,11 @@ __global__ __launch_bounds__(64 * NW) void mla_dense_kernel(
     if (!heads) return;
 
     const size_t idx = ((size_t)b * H + h) * n_split + split;
-    float* po = part_o + idx * kDv + 4 * (G & 1) + 64 * (G >> 1);
+    float* po = part_o + idx * kDv + 4 * G;
 #pragma unroll
     for (int dq = 0; dq < 4; ++dq)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(po + 128 * dq + 8 * t) = o[dq][t];
+        for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(po + 128 * dq + 16 * t) = o[dq][t];
     if (G == 0) {
         part_ml[idx * 2] = m_run;
         part_ml[idx * 2 + 1] = l_run;
