@@ -398,10 +398,14 @@ gqa_status topk_sparse_decode(const void* q, const void* latent, const void* q_i
  * weighted indexer ([稀疏注意力] DSA ①, the Lightning Indexer formula):
  *     I_s = sum_{j < H_I} w_j * ReLU(q_index[j] . k_index[s])
  * H_I query heads share the single key row; w_j is a per-head weight of
- * either sign.  The indexer runs on the matrix cores: each head's dot
- * product and the weighted sum are accumulated in fp32 (not the exact dots
- * of topk_sparse_decode), and the top_k largest I_s (ties to the lower index)
- * are selected as in topk_sparse_decode; steps 3 and the outputs are the same.
+ * either sign.  The selection is the exact top_k of I_s (ties to the lower
+ * index; indices ascending, -1 padded), as if I_s were computed exactly: the
+ * indexer runs on the matrix cores with fp32 sums, and every key whose fp32
+ * score lies within a proven bound of the k-th one (2^-14 * sum_j |w_j|
+ * |q_index[j]| * max_s |k_index[s]|) is scored again in fp64 before the
+ * final choice.  A run of more than 256 keys within that bound (near-equal
+ * scores) keeps the fp32 order among them.  Step 3 and the outputs are
+ * those of topk_sparse_decode.
  *
  *   q_index     bf16 [B][H_I][D_idx]
  *   w_index     fp32 [B][H_I] (device, 4-byte aligned)
@@ -427,8 +431,13 @@ gqa_status topk_sparse_decode_weighted(const void* q, const void* latent, const 
  *      token_idx[b] holds at most 2051 ascending positions, -1 after;
  *   4. standard GQA attention of every query head over those tokens of its
  *      kv head's cache:  out = softmax(scale * q . K[t]) V[t].
- * The block keys are computed in fp32 and enter the score product as hi + lo
- * bf16 terms; scores are summed in fp32.
+ * The block set is the exact top 512 of these scores (as if computed in
+ * exact arithmetic): the blocks are scored on the matrix cores (block keys
+ * in fp32, entering as hi + lo bf16 terms, fp32 sums), and every block whose
+ * fp32 score lies within a proven bound of the 512th (about
+ * 2^-13 * sum_h |q_index[h]|) is scored again in fp64, its block key rebuilt
+ * in fp64, before the final choice.  A run of more than 256 blocks within
+ * that bound keeps the fp32 order among them.
  *
  *   q          bf16 [B][Hq][D], already rotated at its position (post-RoPE cache)
  *   k_cache    bf16 [B][Hkv][S_max][D], v_cache the same

@@ -1,4 +1,5 @@
-// Causal GQA prefill on gfx950 MFMA (32x32x16, fp16 operands, fp32 accumulation).
+// Causal GQA prefill on gfx950 MFMA (32x32x16; scores from hi + lo bf16 operands by
+// default or fp16; P.V in fp16; fp32 accumulation).
 //
 // Prefill is a dense contraction: K/V are reused by every later query
 // ([注意力变体与MoE] "生成时的瓶颈", last paragraph), so it runs on the matrix

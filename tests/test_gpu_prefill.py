@@ -126,6 +126,45 @@ def _prefill_full(m, window, k2=0):
     assert_close(got[:, :, rows], ref[:, :, rows], f"prefill full size w={window} x{2 ** k2}")
 
 
+def _exp_shift(bits, e):
+    """bf16 values times 2^e, exactly (the exponent field moved; zeros kept)."""
+    out = bits.astype(np.int32)
+    nz = (bits & 0x7FFF) != 0
+    out[nz] += e << 7
+    return out.astype(np.uint16)
+
+
+@pytest.mark.parametrize("fp16_scores", [False, True])
+def test_prefill_v_at_the_fp16_range_edges(m, fp16_scores):
+    """V enters the P.V product as fp16: values near the top of fp16's range
+    (|v| up to ~4e4 < 65504) stay exact, so in units of 2^13 the output meets
+    the usual tolerance; values near 2^-20 (fp16 subnormals) lose at most
+    2^-25 each, so the output errs by at most 2^-25 absolute: checked in
+    units of 2^-20 (a flush to zero would miss by ~1)."""
+    import torch
+    B, T, Hq, Hkv, D = 1, 260, 8, 2, 128
+    p = prefill_inputs_host(B, T, Hq, Hkv, D, seed=33)
+    rope = rope_settings(ROPE_NTK, base=1e6, factor=4.0)
+    scale = 1 / math.sqrt(D)
+    qf, kf = bf16_bits_to_f64(p["q"]), bf16_bits_to_f64(p["k"])
+    for e in (13, -20):
+        vb = _exp_shift(p["v"], e)
+        vf = bf16_bits_to_f64(vb)
+        assert np.max(np.abs(vf)) < 65504.0
+        print(f"[case] prefill V x 2^{e} fp16_scores={fp16_scores}", flush=True)
+        out = m.gqa_prefill_causal(to_dev(p["q"]), to_dev(p["k"]), to_dev(vb), scale, rope=rope,
+                                   fp16_scores=fp16_scores)
+        torch.cuda.synchronize()
+        ref = oatt.prefill_causal(qf, kf, vf, scale, rope)
+        got = from_dev(out)
+        if e > 0:   # the path is linear in V: in units of 2^e the usual tolerance holds
+            assert_close(got * 2.0 ** -e, ref * 2.0 ** -e, f"V x 2^{e} (in units of 2^{e})")
+        else:
+            err = np.abs(got - ref) * 2.0 ** 20
+            bound = 2.0 ** -5 + 1e-2 * np.abs(ref) * 2.0 ** 20
+            assert np.all(err <= bound), f"V x 2^{e}: max err/bound {np.max(err / bound):.3f}"
+
+
 def test_prefill_full_size_8k_whole_tiles(m):
     """T=8192, 32 q heads, 8 kv heads, NTK s=4 base 1e6: every head over five
     whole query tiles; guarded output and workspace; two calls bitwise equal."""
