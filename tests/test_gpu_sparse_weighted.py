@@ -21,7 +21,7 @@ import pytest
 from helpers import assert_close, from_dev, to_dev
 from oracle import sparse as osp
 from workloads import (SPARSE_128K, bf16_bits_to_f64, bf16_tensor_to_f64, device_randn_bf16,
-                       sparse_inputs_host)
+                       f32_to_bf16_bits, sparse_inputs_host)
 
 pytestmark = pytest.mark.gpu
 SCALE = 1 / math.sqrt(192)
@@ -130,6 +130,36 @@ def test_weighted_sparse_ties_take_lower_indices(m):
     qi = randn_bf16(rng, (1, 64, 128))
     gidx = _run(m, d, qi, _weights(rng, 1, 64), 700)
     assert list(gidx[0]) == list(range(700))
+
+
+def test_weighted_sparse_band_reaches_below_the_threshold_bin(m):
+    """16 heads all along dim 0 (q_h = e_0) with weights 1/16: key s scores
+    max(k_s[0], 0) exactly, in fp32 too.  k-1 keys score 4, the k-th score is
+    exactly 1.0 (the lowest value of its first-digit bin), 100 keys score
+    1 - 2^-8 (the bin below), the rest 0; one key with |k| = 256 (its dim 1)
+    widens the re-scored band to about +-2^-6, so the band reaches into the
+    bin below and its keys there come from the row itself.  Row 1 has two
+    keys at exactly 1.0: the lower index wins."""
+    rng = np.random.default_rng(96)
+    B, S, k = 2, 3000, 256
+    d = sparse_inputs_host(B, 16, S, 576, 128, 97, [S, S])
+    ki = np.zeros((B, S, 128), dtype=np.float32)
+    ki[:, :, 0] = -1.0
+    for b in range(B):
+        perm = rng.permutation(S)
+        n_t = 1 + b                                  # keys at exactly 1.0
+        ki[b, perm[:k - 1], 0] = 4.0
+        ki[b, perm[k - 1:k - 1 + n_t], 0] = 1.0
+        ki[b, perm[k - 1 + n_t:k - 1 + n_t + 100], 0] = 1.0 - 2.0 ** -8
+        ki[b, perm[-1], 1] = 256.0                   # score 0, largest norm
+    d["k_index"] = f32_to_bf16_bits(ki)
+    qi = np.zeros((B, 16, 128), dtype=np.float32)
+    qi[:, :, 0] = 1.0
+    w = np.full((B, 16), 1.0 / 16, dtype=np.float32)
+    gidx = _run(m, d, f32_to_bf16_bits(qi), w, k)
+    for b in range(B):
+        e = np.maximum(ki[b, :, 0].astype(np.float64), 0.0)
+        assert np.array_equal(gidx[b], osp.topk_select_exact(e, k))
 
 
 def test_weighted_sparse_full_size_128k(m):
