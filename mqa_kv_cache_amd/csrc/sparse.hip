@@ -384,8 +384,9 @@ __device__ void first_digit(const uint32_t* hist_g, int b, int L, int k, uint32_
 }
 
 // Per 4096-key chunk: the keys of the threshold bin and of the bins above it
-// (every selected key is one of them), as (key, index) entries in index
-// order, to the chunk's own slice (its index range of the entry arrays);
+// (every selected key is one of them), and with lower_bins = 1 those of the
+// bin below as well (where the re-scored band of the multi-head indexers can
+// reach), as (key, index) entries in index order, to the chunk's own slice (its index range of the entry arrays);
 // their number to ent_cnt[b][c]: no cross-workgroup atomics.  Wave w owns a
 // contiguous quarter of the chunk, its keys requested before the histogram
 // work so both latencies overlap; the order within a wave comes from
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_compact_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist_g,
     const int32_t* __restrict__ seq_lens, int S_max, int S_stride, int top_k,
     uint32_t* __restrict__ ent_key, uint32_t* __restrict__ ent_idx, uint32_t* __restrict__ ent_cnt,
-    int n_chunks, SelInfo* __restrict__ info, int32_t* __restrict__ topk_idx) {
+    int n_chunks, SelInfo* __restrict__ info, int32_t* __restrict__ topk_idx, int lower_bins) {
     constexpr int NW = kChunkThreads / 64;
     constexpr int span = kChunkKeys / NW;
     __shared__ uint32_t h[kHistBins];
@@ -429,10 +430,11 @@ __global__ __launch_bounds__(kChunkThreads) void topk_compact_kernel(
     first_digit<kChunkThreads>(hist_g, b, L, k, h, wsum, res);
     const uint32_t B1 = res[0];
     if (c == 0 && tid == 0) info[b] = SelInfo{B1, res[1]};
+    const uint32_t B0 = B1 > (uint32_t)lower_bins ? B1 - (uint32_t)lower_bins : 0u;   // lowest bin kept
     uint32_t n_w = 0;
 #pragma unroll
     for (int it = 0; it < kKeysPerLane; ++it)
-        n_w += (uint32_t)__popcll(__ballot(j0 + 64 * it + lane < j1 && (kv[it] >> 20) >= B1));
+        n_w += (uint32_t)__popcll(__ballot(j0 + 64 * it + lane < j1 && (kv[it] >> 20) >= B0));
     if (lane == 0) wcnt[wave] = n_w;
     __syncthreads();
     uint32_t pos = 0;
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_compact_kernel(
 #pragma unroll
     for (int it = 0; it < kKeysPerLane; ++it) {
         const int j = j0 + 64 * it + lane;
-        const bool keep = j < j1 && (kv[it] >> 20) >= B1;
+        const bool keep = j < j1 && (kv[it] >> 20) >= B0;
         const uint64_t mask = __ballot(keep);
         const uint32_t p = pos + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -517,10 +519,14 @@ __device__ void lower_digits(uint32_t B1, uint32_t need, uint32_t n, KeyAt key_a
 // Three steps: the finish kernel finds T and the band and writes the band
 // and the keys certainly in (sorted by index) to the workspace; the band
 // kernel scores the band on up to 16 CUs per row (an fp64 contraction on the
-// matrix cores); the merge kernel ranks the band by exact score and merges.  A band
-// of more than kBandCap keys (long runs of near-equal scores), or one from a
-// row whose threshold bin overflowed LDS, keeps the fp32 selection, which is
-// then exact up to those near-ties only.
+// matrix cores); the merge kernel ranks the band by exact score and merges.
+// For the weighted indexer (whose band is the wider) the entries include the
+// bin below the threshold bin as well, so the band is found among them
+// unless it reaches two bins down; otherwise the band's keys below the
+// threshold bin come from a scan of the row.  A band of more
+// than kBandCap keys (long runs of near-equal scores), or one from a row whose
+// entries overflowed LDS, keeps the fp32 selection, which is then exact up
+// to those near-ties only.
 constexpr int kBandCap = 256;
 constexpr int kSureCap = 4096;   // keys certainly in: fewer than k <= 4096
 
@@ -533,6 +539,7 @@ struct RefineArgs {
     int S_tok;                 // rows of k_index per batch row
     const uint32_t* knorm;     // weighted: fp32 bits of the row's largest |k_s|^2, row stride kHistBins
     RopeDev rope;              // QSA block-key RoPE (half 0: none)
+    int lower_bins;            // the entries hold bins >= B1 - lower_bins (0 or 1)
     // per-row band state in the workspace
     uint32_t* state;           // [B][8]: active, band size nb, keys certainly in c_in, need
     uint32_t* band_idx;        // [B][kBandCap]
@@ -628,13 +635,15 @@ __device__ bool band_setup(const RefineArgs& ra, int b, int n_keys, int k, uint3
     for (uint32_t e = e0; e < e1; ++e)
         if (lk[e] > K_hi && pos < (uint32_t)kSureCap) sure[pos++] = li[e];
     if (tid == kSelThreads - 1) res[1] = pos;      // keys certainly selected
-    // the band may reach below the first-digit bin of the entries: those keys
-    // are found in the row itself (four keys per request, several in flight)
-    if (K_lo < (B1 << 20)) {
+    // the band may reach below the lowest first-digit bin of the entries
+    // (the threshold bin, or the one below it): those keys are found in the
+    // row itself (four keys per request, several in flight)
+    const uint32_t B0 = B1 > (uint32_t)ra.lower_bins ? B1 - (uint32_t)ra.lower_bins : 0u;   // entries: bins >= B0
+    if (K_lo < (B0 << 20)) {
         const int n4 = n_keys >> 2;
         const u32x4* k4 = reinterpret_cast<const u32x4*>(keys_row);
         auto test = [&](uint32_t key, int i) {
-            if (key >= K_lo && key < (B1 << 20)) {
+            if (key >= K_lo && key < (B0 << 20)) {
                 const uint32_t at = atomicAdd(&res[0], 1u);
                 if (at < (uint32_t)kBandCap) band[at] = (uint32_t)i;
             }
@@ -2125,7 +2134,7 @@ hipError_t launch_qsa_sparse_decode(const void* q, const void* k_cache, const vo
             return hipErrorInvalidValue;
     }
     hipLaunchKernelGGL(topk_compact_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, hist, cnt,
-                       NB, KS, kQsaTopBlocks, cand, cand_idx, cand_cnt, nkc, info, blk);
+                       NB, KS, kQsaTopBlocks, cand, cand_idx, cand_cnt, nkc, info, blk, 0);
     RefineArgs ra{};   // the block scores are fp32: re-score the band at the 512th
     ra.mode = 2;
     ra.H_I = H_I;
@@ -2239,7 +2248,7 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
     }
     hipLaunchKernelGGL(topk_compact_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, hist,
                        seq_lens, S_max, S_stride, top_k, cand, cand_idx, cand_cnt, nkc, info,
-                       topk_idx);
+                       topk_idx, H_I > 0 ? 1 : 0);
     RefineArgs ra{};
     if (H_I > 0) {   // the weighted indexer's fp32 scores: re-score the band at the k-th
         ra.mode = 1;
@@ -2249,6 +2258,7 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
         ra.k_index = ki;
         ra.S_tok = S_max;
         ra.knorm = hist;
+        ra.lower_bins = 1;
         refine_buffers(refine, B, ra);
     }
     hipLaunchKernelGGL(topk_finish_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, seq_lens, S_max,
