@@ -680,6 +680,149 @@ __device__ bool band_setup(const RefineArgs& ra, int b, int n_keys, int k, uint3
     return true;
 }
 
+// One workgroup per batch row does the whole selection.  The first digit
+// (the bin B1 holding the k-th largest key, and the count above it) comes
+// from the indexer's histogram; the entries (keys in bins >= B1, and for the
+// weighted indexer the bin below too: every selected key and every band
+// member is one of them) are gathered from the row into LDS in index order:
+// each thread takes 16 consecutive keys per round (one round is 16384 keys,
+// the next round's keys requested before this round's are sorted out),
+// counts its entries, one block scan places them.  Their number is known
+// from the histogram before the row is read; when it exceeds the LDS
+// capacity the digit passes and the ordered pass run over the row's keys in
+// global memory instead (slow, and only for rows with huge runs of
+// near-equal scores).  Then the two lower digit passes give the exact k-th
+// key T, and the selected indices (keys > T, and the first `ties` keys == T
+// by index) are written in ascending order from two block scans.
+constexpr int kSelKeysPerThread = 16;
+constexpr int kSelRound = kSelThreads * kSelKeysPerThread;   // keys per round
+// Rows of at most this many keys take the one-kernel select; longer rows
+// the two-kernel one (the chunk workgroups read a row in parallel, where one
+// workgroup's reads of it run at ~20 GB/s: 32 us for 131072 keys against
+// 18 us for the two kernels, 16 us against 18.7 at 32768 keys).
+constexpr int kSelOneKernelMax = 32768;
+
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
+    const float* __restrict__ scores, const uint32_t* __restrict__ hist_g,
+    const int32_t* __restrict__ seq_lens, int S_max, int S_stride, int top_k,
+    int32_t* __restrict__ topk_idx, RefineArgs ra) {
+    __shared__ uint32_t h[kHistBins];
+    __shared__ uint32_t lk[kEntCap], li[kEntCap];
+    __shared__ uint32_t wsum[kSelThreads / 64];
+    __shared__ uint32_t res[2];
+    __shared__ double qn_h[64];
+    __shared__ float fshared[2];
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x;
+    if (ra.mode != 0 && tid == 0) ra.state[(size_t)b * 8] = 0u;   // band kernels: nothing to do
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int k = min(top_k, L);
+    int32_t* outp = topk_idx + (size_t)b * top_k;
+    for (int i = k + tid; i < top_k; i += kSelThreads) outp[i] = -1;
+    if (k == L) {                                  // everything is selected
+        for (int j = tid; j < L; j += kSelThreads) outp[j] = j;
+        return;
+    }
+    const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride);
+    // the first round's keys are requested before the histogram work
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    u32x4v kv[kSelKeysPerThread / 4], kn[kSelKeysPerThread / 4];
+    auto load_round = [&](int r0, u32x4v (&v)[kSelKeysPerThread / 4]) {
+        const int j0 = r0 + tid * kSelKeysPerThread;
+#pragma unroll
+        for (int u = 0; u < kSelKeysPerThread / 4; ++u) {
+            const int j = j0 + 4 * u;   // a multiple of 4; the row is padded to 4 keys
+            v[u] = j < L ? *reinterpret_cast<const u32x4v*>(keys + j) : u32x4v{0u, 0u, 0u, 0u};
+        }
+    };
+    load_round(0, kv);
+    first_digit<kSelThreads>(hist_g, b, L, k, h, wsum, res);
+    const uint32_t B1 = res[0], above = res[1];
+    const uint32_t need = (uint32_t)k - above;
+    const uint32_t B0 = B1 > (uint32_t)ra.lower_bins ? B1 - (uint32_t)ra.lower_bins : 0u;
+    uint32_t E = above + h[B1] + (B0 < B1 ? h[B0] : 0u);   // entries: keys in bins >= B0
+    uint32_t T, ties;
+    if (E <= (uint32_t)kEntCap) {                  // uniform
+        uint32_t base = 0;
+        for (int r0 = 0; r0 < L; r0 += kSelRound) {   // uniform trip count
+            const bool more = r0 + kSelRound < L;
+            if (more) load_round(r0 + kSelRound, kn);
+            const int j0 = r0 + tid * kSelKeysPerThread;
+            uint32_t c = 0;
+#pragma unroll
+            for (int u = 0; u < kSelKeysPerThread / 4; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) c += j0 + 4 * u + q < L && (kv[u][q] >> 20) >= B0;
+            uint32_t p = base + block_inclusive_scan<kSelThreads>(c, wsum) - c;
+            if (c)
+#pragma unroll
+                for (int u = 0; u < kSelKeysPerThread / 4; ++u)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int j = j0 + 4 * u + q;
+                        if (j < L && (kv[u][q] >> 20) >= B0 && p < (uint32_t)kEntCap) {
+                            lk[p] = kv[u][q];
+                            li[p] = (uint32_t)j;
+                            ++p;
+                        }
+                    }
+            if (tid == kSelThreads - 1) res[0] = p;
+            __syncthreads();
+            base = res[0];
+            __syncthreads();
+            if (more)
+#pragma unroll
+                for (int u = 0; u < kSelKeysPerThread / 4; ++u) kv[u] = kn[u];
+        }
+        E = base;                                  // equal to the histogram's count
+        lower_digits(B1, need, E, [&](uint32_t i) { return lk[i]; }, h, wsum, res, T, ties);
+        if (ra.mode != 0 &&
+            band_setup(ra, b, L, k, T, B1, lk, li, E, keys, wsum, res, qn_h, fshared))
+            return;                                // the band kernels finish the row
+        // thread t takes entries [t per, (t + 1) per): ranks of ties and
+        // output slots from two block scans
+        const uint32_t per = (E + kSelThreads - 1) / kSelThreads;
+        const uint32_t e0 = min((uint32_t)tid * per, E), e1 = min(e0 + per, E);
+        uint32_t eq = 0;
+        for (uint32_t e = e0; e < e1; ++e) eq += lk[e] == T;
+        uint32_t eq_seen = block_inclusive_scan<kSelThreads>(eq, wsum) - eq;
+        uint32_t take = 0;
+        for (uint32_t e = e0, r = eq_seen; e < e1; ++e) {
+            const uint32_t key = lk[e];
+            take += key > T || (key == T && r++ < ties);
+        }
+        uint32_t p = block_inclusive_scan<kSelThreads>(take, wsum) - take;
+        for (uint32_t e = e0; e < e1; ++e) {
+            const uint32_t key = lk[e];
+            bool tk = key > T;
+            if (key == T) tk = eq_seen++ < ties;
+            if (tk && p < (uint32_t)k) outp[p++] = (int32_t)li[e];   // p < k always holds
+        }
+        return;
+    }
+    // too many entries for LDS: digit passes over the row's keys, then the
+    // ordered pass in 1024-key tiles of the row
+    lower_digits(B1, need, (uint32_t)L, [&](uint32_t i) { return keys[i]; }, h, wsum, res, T, ties);
+    uint32_t eq_base = 0, sel_base = 0;
+    for (uint32_t t0 = 0; t0 < (uint32_t)L; t0 += kSelThreads) {
+        const uint32_t e = t0 + tid;
+        const uint32_t key = e < (uint32_t)L ? keys[e] : 0u;
+        const uint32_t eqf = e < (uint32_t)L && key == T;
+        const uint32_t eq_incl = block_inclusive_scan<kSelThreads>(eqf, wsum);
+        const uint32_t tk = e < (uint32_t)L && (key > T || (eqf && eq_base + eq_incl - eqf < ties));
+        const uint32_t t_incl = block_inclusive_scan<kSelThreads>(tk, wsum);
+        if (tk && sel_base + t_incl - tk < (uint32_t)k) outp[sel_base + t_incl - tk] = (int32_t)e;
+        if (tid == kSelThreads - 1) {
+            res[0] = eq_incl;
+            res[1] = t_incl;
+        }
+        __syncthreads();
+        eq_base += res[0];
+        sel_base += res[1];
+        __syncthreads();
+    }
+}
+
 // One workgroup per batch row: the exact k-th key T from the entries, then
 // the selected indices in ascending order (keys > T, and the first `ties`
 // keys == T by index).  The entries (at most k - 1 above the threshold bin
@@ -2133,8 +2276,7 @@ hipError_t launch_qsa_sparse_decode(const void* q, const void* k_cache, const vo
         default:
             return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(topk_compact_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, hist, cnt,
-                       NB, KS, kQsaTopBlocks, cand, cand_idx, cand_cnt, nkc, info, blk, 0);
+
     RefineArgs ra{};   // the block scores are fp32: re-score the band at the 512th
     ra.mode = 2;
     ra.H_I = H_I;
@@ -2143,8 +2285,16 @@ hipError_t launch_qsa_sparse_decode(const void* q, const void* k_cache, const vo
     ra.S_tok = S_max;
     ra.rope = rope;
     refine_buffers(refine, B, ra);
-    hipLaunchKernelGGL(topk_finish_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, cnt, NB, KS,
-                       kQsaTopBlocks, cand, cand_idx, cand_cnt, nkc, info, blk, ra);
+    if (NB <= kSelOneKernelMax) {
+        hipLaunchKernelGGL(topk_select_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, hist, cnt, NB,
+                           KS, kQsaTopBlocks, blk, ra);
+    } else {
+        hipLaunchKernelGGL(topk_compact_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, hist,
+                           cnt, NB, KS, kQsaTopBlocks, cand, cand_idx, cand_cnt, nkc, info, blk,
+                           ra.lower_bins);
+        hipLaunchKernelGGL(topk_finish_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, cnt, NB, KS,
+                           kQsaTopBlocks, cand, cand_idx, cand_cnt, nkc, info, blk, ra);
+    }
     hipLaunchKernelGGL(band_score_kernel, dim3(kBandCap / 16, B), dim3(kSelThreads), 0, s, ra);
     hipLaunchKernelGGL(band_merge_kernel, dim3(B), dim3(kSelThreads), 0, s, ra, kQsaTopBlocks, blk);
     hipLaunchKernelGGL(gqa_gather_attn_kernel, dim3(kGChunks, Hkv, B), dim3(64), 0, s,
@@ -2246,9 +2396,7 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
         default:
             return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(topk_compact_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, hist,
-                       seq_lens, S_max, S_stride, top_k, cand, cand_idx, cand_cnt, nkc, info,
-                       topk_idx, H_I > 0 ? 1 : 0);
+
     RefineArgs ra{};
     if (H_I > 0) {   // the weighted indexer's fp32 scores: re-score the band at the k-th
         ra.mode = 1;
@@ -2261,8 +2409,16 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
         ra.lower_bins = 1;
         refine_buffers(refine, B, ra);
     }
-    hipLaunchKernelGGL(topk_finish_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, seq_lens, S_max,
-                       S_stride, top_k, cand, cand_idx, cand_cnt, nkc, info, topk_idx, ra);
+    if (S_max <= kSelOneKernelMax) {
+        hipLaunchKernelGGL(topk_select_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, hist, seq_lens,
+                           S_max, S_stride, top_k, topk_idx, ra);
+    } else {
+        hipLaunchKernelGGL(topk_compact_kernel, dim3(nkc, B), dim3(kChunkThreads), 0, s, scores, hist,
+                           seq_lens, S_max, S_stride, top_k, cand, cand_idx, cand_cnt, nkc, info,
+                           topk_idx, ra.lower_bins);
+        hipLaunchKernelGGL(topk_finish_kernel, dim3(B), dim3(kSelThreads), 0, s, scores, seq_lens, S_max,
+                           S_stride, top_k, cand, cand_idx, cand_cnt, nkc, info, topk_idx, ra);
+    }
     if (ra.mode != 0) {
         hipLaunchKernelGGL(band_score_kernel, dim3(kBandCap / 16, B), dim3(kSelThreads), 0, s, ra);
         hipLaunchKernelGGL(band_merge_kernel, dim3(B), dim3(kSelThreads), 0, s, ra, top_k, topk_idx);

@@ -135,6 +135,12 @@ def test_qsa_gqa_groups(m):
     _run(m, 2, 10, 2, 3000, [3000, 1234], 16, 109, ROPE64)
 
 
+def test_qsa_long_rows_take_the_two_kernel_select(m):
+    """More than 32768 blocks per row (S_max = 132000): the chunk and row
+    select kernels with the band re-scoring."""
+    _run(m, 1, 8, 1, 132000, [132000], 64, 110, ROPE64)
+
+
 def test_qsa_full_size_128k(m):
     """B=4, L=128K, Hq=32, Hkv=4, 64 indexer heads: every row's block set
     equals the exact top 512, every head against the oracle."""

@@ -116,6 +116,18 @@ def test_sparse_overflow_and_lds_rows_in_one_call(m):
     assert list(idx[2][:1500]) == list(range(1500)) and np.all(idx[2][1500:] == -1)
 
 
+def test_sparse_long_rows_take_the_two_kernel_select(m):
+    """Rows longer than 32768 keys are selected by the chunk and row kernels
+    (shorter ones by one kernel per row): row 0 with 20000 equal top scores
+    (the row kernel's overflow path), row 1 ordinary, row 2 shorter than k."""
+    d = sparse_inputs_host(3, 16, 40000, 576, 128, 49, [40000, 39001, 1500])
+    d["k_index"][0, :20000] = d["k_index"][0, 0]
+    d["q_index"][0] = d["k_index"][0, 0]
+    idx = _run(m, d, 2048)
+    assert list(idx[0]) == list(range(2048))
+    assert list(idx[2][:1500]) == list(range(1500)) and np.all(idx[2][1500:] == -1)
+
+
 def test_sparse_full_size_128k(m):
     import torch
     cfg = SPARSE_128K
