@@ -69,6 +69,37 @@ def test_decode_yarn_and_split_independence(m):
         assert np.max(np.abs(o - outs[0])) <= 4e-3
 
 
+def test_decode_calls_on_two_streams_run_concurrently_and_agree(m):
+    """The library keeps no mutable state: two decodes with disjoint buffers
+    on two streams (default priority), issued back to back many times, give
+    the results of the same calls made one at a time on one stream."""
+    import torch
+    rope = rope_settings(ROPE_YARN, base=500000.0, factor=4.0, original_max_position=64)
+    cases = []
+    for seed, lens in ((21, [900, 17, 512]), (22, [64, 1000, 333])):
+        h = decode_inputs_host(3, 16, 2, 128, 1000, seed, lens)
+        d = [to_dev(h[key]) for key in ("q", "k", "v")]
+        cases.append((d, torch.tensor(lens, dtype=torch.int32).cuda()))
+    print("[case] decode on two streams", flush=True)
+    ref = []
+    for (q, k, v), lens in cases:
+        ref.append(m.gqa_decode(q, k, v, lens, 0.088, q_rope=rope))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(r) for r in ref]
+    ws = [torch.empty(m.gqa_decode_workspace_size(3, 16, 2, 128, 1000), dtype=torch.uint8,
+                      device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    for rep in range(20):
+        for i, (((q, k, v), lens), st) in enumerate(zip(cases, streams)):
+            with torch.cuda.stream(st):
+                m.gqa_decode(q, k, v, lens, 0.088, q_rope=rope, out=outs[i], workspace=ws[i],
+                             stream=st)
+    torch.cuda.synchronize()
+    for o, r in zip(outs, ref):
+        assert torch.equal(o, r)
+
+
 def test_decode_no_rope_and_gqa_equals_repeated_mha(m):
     """GQA on the GPU equals an MHA run over K/V materialised with each head
     repeated g times (repeat_interleave): bit for bit when every context is
