@@ -1396,7 +1396,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
     }
     __syncthreads();                            // the row buffers are free from here
 
-    // merge round 1: sc 1 -> 0 and 3 -> 2 (slots in buffers 2 hgw + sc / 2)
+    // merge step 1: sc 1 -> 0 and 3 -> 2 (slots in buffers 2 hgw + sc / 2)
     auto slot = [&](int i) {
         return reinterpret_cast<f32x4*>(i == 0 ? rows0 : i == 1 ? rows1 : i == 2 ? rows2 : rows3);
     };
@@ -1404,7 +1404,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
     __syncthreads();
     if (!(sc & 1)) merge_state(o, m_run, l_run, slot(2 * hgw + (sc >> 1)), ml_s[hgw][sc >> 1], lane, n);
     __syncthreads();
-    // round 2: sc 2 -> 0
+    // merge step 2: sc 2 -> 0
     if (sc == 2) put_state(o, m_run, l_run, slot(2 * hgw), ml_s[hgw][0], lane, G, n);
     __syncthreads();
     if (sc != 0 || !heads) return;
