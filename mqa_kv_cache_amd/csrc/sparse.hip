@@ -685,8 +685,8 @@ __device__ bool band_setup(const RefineArgs& ra, int b, int n_keys, int k, uint3
 // from the indexer's histogram; the entries (keys in bins >= B1, and for the
 // weighted indexer the bin below too: every selected key and every band
 // member is one of them) are gathered from the row into LDS in index order:
-// each thread takes 16 consecutive keys per round (one round is 16384 keys,
-// the next round's keys requested before this round's are sorted out),
+// each thread takes 16 consecutive keys per pass (one pass is 16384 keys,
+// the next pass's keys requested before this pass's are sorted out),
 // counts its entries, one block scan places them.  Their number is known
 // from the histogram before the row is read; when it exceeds the LDS
 // capacity the digit passes and the ordered pass run over the row's keys in
@@ -695,7 +695,7 @@ __device__ bool band_setup(const RefineArgs& ra, int b, int n_keys, int k, uint3
 // key T, and the selected indices (keys > T, and the first `ties` keys == T
 // by index) are written in ascending order from two block scans.
 constexpr int kSelKeysPerThread = 16;
-constexpr int kSelRound = kSelThreads * kSelKeysPerThread;   // keys per round
+constexpr int kSelPass = kSelThreads * kSelKeysPerThread;   // keys per pass
 // Rows of at most this many keys take the one-kernel select; longer rows
 // the two-kernel one (the chunk workgroups read a row in parallel, where one
 // workgroup's reads of it run at ~20 GB/s: 32 us for 131072 keys against
@@ -724,10 +724,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
         return;
     }
     const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores + (size_t)b * S_stride);
-    // the first round's keys are requested before the histogram work
+    // the first pass's keys are requested before the histogram work
     typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
     u32x4v kv[kSelKeysPerThread / 4], kn[kSelKeysPerThread / 4];
-    auto load_round = [&](int r0, u32x4v (&v)[kSelKeysPerThread / 4]) {
+    auto load_pass = [&](int r0, u32x4v (&v)[kSelKeysPerThread / 4]) {
         const int j0 = r0 + tid * kSelKeysPerThread;
 #pragma unroll
         for (int u = 0; u < kSelKeysPerThread / 4; ++u) {
@@ -735,7 +735,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
             v[u] = j < L ? *reinterpret_cast<const u32x4v*>(keys + j) : u32x4v{0u, 0u, 0u, 0u};
         }
     };
-    load_round(0, kv);
+    load_pass(0, kv);
     first_digit<kSelThreads>(hist_g, b, L, k, h, wsum, res);
     const uint32_t B1 = res[0], above = res[1];
     const uint32_t need = (uint32_t)k - above;
@@ -744,9 +744,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     uint32_t T, ties;
     if (E <= (uint32_t)kEntCap) {                  // uniform
         uint32_t base = 0;
-        for (int r0 = 0; r0 < L; r0 += kSelRound) {   // uniform trip count
-            const bool more = r0 + kSelRound < L;
-            if (more) load_round(r0 + kSelRound, kn);
+        for (int r0 = 0; r0 < L; r0 += kSelPass) {   // uniform trip count
+            const bool more = r0 + kSelPass < L;
+            if (more) load_pass(r0 + kSelPass, kn);
             const int j0 = r0 + tid * kSelKeysPerThread;
             uint32_t c = 0;
 #pragma unroll
@@ -1272,7 +1272,7 @@ __device__ __forceinline__ void sparse_sub_step(const uint8_t* rows, const u32x4
 // row) as above, but wave (hgw, sc) = (w & 1, w >> 1) takes only row
 // sub-chunk sc for head group hgw, so the four sub-chunks are processed at
 // once instead of one after the other.  The four states of a head group
-// are then merged through LDS (the row buffers, free by then) in two rounds
+// are then merged through LDS (the row buffers, free by then) in two steps
 // of log-sum-exp rescaling, and wave sc = 0 writes the chunk's partial.
 // q is requested together with the selected indices; the copies follow the
 // first barrier, and one wait covers both the copies and q.
