@@ -6,7 +6,9 @@
 // (token, frequency) once in LDS (fp64 angle, reduced, fp32 sincos, times
 // the YaRN amplitude), so the transcendental work is shared by all heads of
 // a token and hidden behind the loads.  The kernel is HBM-bound: each
-// element is read once and written once.
+// element is read once and written once, so both go with the nontemporal
+// policy (2% faster than the default on the 8K prefill's Q rows; 16 chunks
+// per thread instead of 8 ran 25% slower).
 #include "device_common.h"
 
 namespace gqa {
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_apply_kernel(
             cc[k] = rem - h * chunks;
             const bool ok = it < total && tok0 + tl[k] < n_tok;
             off[k] = ok ? (tok0 + tl[k]) * stride_tok + (int64_t)h * stride_head + 8 * cc[k] : -1;
-            if (ok) v[k] = *reinterpret_cast<const u32x4*>(in + off[k]);
+            if (ok) v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in + off[k]));
         }
         if (base == 0) {
             for (int e = tid; e < tok_per_block * half; e += kRopeThreads) {
@@ -68,9 +70,9 @@ __global__ __launch_bounds__(kRopeThreads) void rope_apply_kernel(
                     const float xe = bf16_lo(v[k][p]), xo = bf16_hi(v[k][p]);
                     v[k][p] = pack_bf16x2(xe * cp[p] - xo * sp[p], xe * sp[p] + xo * cp[p]);
                 }
-                *reinterpret_cast<u32x4*>(out + off[k]) = v[k];
+                __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4*>(out + off[k]));
             } else if (out != in) {
-                *reinterpret_cast<u32x4*>(out + off[k]) = v[k];
+                __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4*>(out + off[k]));
             }
         }
     }
