@@ -271,23 +271,30 @@ __device__ __forceinline__ bool first_piece(const int32_t* seq_lens, int B, int 
     return true;
 }
 
-// Per-lane RoPE frequencies of the q dims this lane holds (dims 32u + 8G ..
-// +7, pairs i = 16u + 4G + p), read once per wave: the table sits in the
-// kernel arguments and a lane-dependent index would otherwise cost a memory
-// round trip per pair.
+// RoPE frequencies for the q dims of a row group.  Lane (G, n) of a wave
+// holds q dims 32u + 8G .. +7, i.e. pairs 16u + 4G + p (p < 4), for every u:
+// the 16 lanes of a row group need the same 4 D/32 angles.  So lane (G, n)
+// keeps the frequency of one of them, pair 16 (n / 4) + 4G + n % 4, each
+// angle is evaluated once per row group and broadcast along the 16-lane row
+// (DPP row_newbcast).  The frequency is read from the kernel arguments once
+// per wave.
 template <int D>
 struct QFreq {
-    double th[D / 32][4];
+    double th;   // frequency of pair `pair` (0 for a lane past D/2 pairs or the rotary dims)
+    int pair;
 };
 template <int D>
-__device__ __forceinline__ void load_freq(const RopeDev& rope, int G, QFreq<D>& f) {
-#pragma unroll
-    for (int u = 0; u < D / 32; ++u)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int i = 16 * u + 4 * G + p;
-            f.th[u][p] = i < rope.half ? rope.theta[i] : 0.0;
-        }
+__device__ __forceinline__ void load_freq(const RopeDev& rope, int G, int n, QFreq<D>& f) {
+    f.pair = 16 * (n >> 2) + 4 * G + (n & 3);
+    f.th = ((n >> 2) < D / 32 && f.pair < rope.half) ? rope.theta[f.pair] : 0.0;
+}
+template <int J, int N>
+__device__ __forceinline__ void row_bcast(float v, float (&out)[N]) {
+    if constexpr (J < N) {
+        out[J] = __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + J, 0xF, 0xF, false));
+        row_bcast<J + 1, N>(v, out);
+    }
 }
 // cos/sin of angle pos * pos_scale * theta, reduced to [-pi, pi] in fp64,
 // then fp32 sincos, both scaled by amp (the same steps as rope_cos_sin).
@@ -315,6 +322,27 @@ __device__ __forceinline__ double dyn_log2s(const RopeDev& r, int L) {
 __device__ __forceinline__ double dyn_theta(double th, int i, double l2s, const RopeDev& r) {
     return l2s > 0.0 ? th * exp2(r.dyn_exp * (double)i * l2s) : th;
 }
+// cos and sin (amplitude included) at position L-1 of the pairs this lane's
+// q dims hold: cs[u][p], sn[u][p] for pair 16u + 4G + p.  Each lane
+// evaluates one angle; the row broadcast hands every lane the 4 D/32 of its
+// row group.  Wave-uniform control flow (all lanes active).
+template <int D>
+__device__ __forceinline__ void row_angles(const QFreq<D>& fq, int L, const RopeDev& rope,
+                                           float (&cs)[D / 32][4], float (&sn)[D / 32][4]) {
+    constexpr int KU = D / 32;
+    float c, s;
+    cos_sin_theta(dyn_theta(fq.th, fq.pair, dyn_log2s(rope, L), rope), (double)(L - 1), rope, c, s);
+    float cf[4 * KU], sf[4 * KU];
+    row_bcast<0, 4 * KU>(c, cf);
+    row_bcast<0, 4 * KU>(s, sf);
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            cs[u][p] = cf[4 * u + p];
+            sn[u][p] = sf[4 * u + p];
+        }
+}
 
 // Raw q rows of the group's heads (issued before the first tile loads, so
 // waiting for them does not wait for the tiles).
@@ -334,20 +362,11 @@ __device__ __forceinline__ void load_q_raw(const uint16_t* q, int b, int kv, int
 // Rotates q at position L-1, folds in scale*log2(e) and splits it into the
 // hi + lo bf16 pair the two MFMA passes use.
 template <int D, int NB>
-__device__ __forceinline__ void prep_q(const u32x4 (&raw)[NB][D / 32], const QFreq<D>& fq, int L,
-                                       float qscale, const RopeDev& rope, int G,
-                                       u32x4 (&qhi)[NB][D / 32], u32x4 (&qlo)[NB][D / 32]) {
+__device__ __forceinline__ void prep_q(const u32x4 (&raw)[NB][D / 32], const float (&cs)[D / 32][4],
+                                       const float (&sn)[D / 32][4], float qscale,
+                                       const RopeDev& rope, int G, u32x4 (&qhi)[NB][D / 32],
+                                       u32x4 (&qlo)[NB][D / 32]) {
     constexpr int KU = D / 32;
-    float cs[KU][4], sn[KU][4];
-    if (rope.half) {
-        const double l2s = dyn_log2s(rope, L);
-#pragma unroll
-        for (int u = 0; u < KU; ++u)
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-                cos_sin_theta(dyn_theta(fq.th[u][p], 16 * u + 4 * G + p, l2s, rope), (double)(L - 1),
-                              rope, cs[u][p], sn[u][p]);
-    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -410,9 +429,9 @@ __device__ __forceinline__ void load_new_row(NewRow<D>& nr, const AppendArgs& ap
 }
 
 template <int D>
-__device__ __forceinline__ void rotate_new_key(NewRow<D>& nr, int L, const QFreq<D>& fq,
-                                               const RopeDev& rope, int G) {
-    const double l2s = dyn_log2s(rope, L);
+__device__ __forceinline__ void rotate_new_key(NewRow<D>& nr, const float (&cs)[D / 32][4],
+                                               const float (&sn)[D / 32][4], const RopeDev& rope,
+                                               int G) {
 #pragma unroll
     for (int u = 0; u < D / 32; ++u) {
         u32x4 w;
@@ -420,10 +439,7 @@ __device__ __forceinline__ void rotate_new_key(NewRow<D>& nr, int L, const QFreq
         for (int p = 0; p < 4; ++p) {
             float xe = bf16_lo(nr.k[u][p]), xo = bf16_hi(nr.k[u][p]);
             if (16 * u + 4 * G + p < rope.half) {
-                float c, sn;
-                cos_sin_theta(dyn_theta(fq.th[u][p], 16 * u + 4 * G + p, l2s, rope), (double)(L - 1),
-                              rope, c, sn);
-                const float ye = xe * c - xo * sn, yo = xe * sn + xo * c;
+                const float ye = xe * cs[u][p] - xo * sn[u][p], yo = xe * sn[u][p] + xo * cs[u][p];
                 xe = ye;
                 xo = yo;
             }
@@ -486,12 +502,24 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
     CtxGeom geo = ctx_geom(seq_lens, b, S_max, cv);   // geo.n == L
     int kv = (int)((gs - base) / L);
     QFreq<D> fq;
-    load_freq<D>(rope, G, fq);
+    load_freq<D>(rope, G, n, fq);
     const RowSpace rs{total, R};
     // the first tile of the next segment or piece, requested with the last
     // tile of the current one (pre_b: it went into tb rather than ta)
     bool have_pre = false, pre_b = false;
     DecodeTile<D> ta, tb;
+    // the piece's q rows (and, with the cache write, its new key and value
+    // rows).  With one 16-head block the next piece's are requested at the
+    // start of this one, so a wave that crosses into another context does
+    // not wait a load latency for them (larger blocks lack the registers and
+    // request them at the start of their piece)
+    constexpr bool kAheadQ = NB == 1;
+    u32x4 qraw[NB][KU];
+    [[maybe_unused]] NewRow<D> nr;
+    if constexpr (kAheadQ) {
+        load_q_raw<D, NB>(q, b, kv, Hq, g, G, n, qraw);
+        if constexpr (APPEND) load_new_row<D>(nr, app, ((size_t)b * Hkv + kv) * D, G, n);
+    }
 
     while (gs < ge) {
         const int64_t ctx0 = base + (int64_t)kv * L;        // global row of this context's row 0
@@ -521,9 +549,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
         const uint16_t* nkp = k_cache;
         const uint16_t* nvp = v_cache;
         uint32_t nbytes_n = 0u;
+        u32x4 qraw_n[NB][KU];
+        [[maybe_unused]] NewRow<D> nr_n;
         if (gs_n < ge) {
             const int kv_n = kv + 1 == Hkv ? 0 : kv + 1;
             const int b_n = kv + 1 == Hkv ? b + 1 : b;
+            if constexpr (kAheadQ) {
+                load_q_raw<D, NB>(q, b_n, kv_n, Hq, g, G, n, qraw_n);
+                if constexpr (APPEND) load_new_row<D>(nr_n, app, ((size_t)b_n * Hkv + kv_n) * D, G, n);
+            }
             const CtxGeom geo_n = kv + 1 == Hkv ? ctx_geom(seq_lens, b_n, S_max, cv) : geo;
             const int r1_n = (int)min((int64_t)geo_n.n, ge - gs_n);
             const size_t slice_n = ((size_t)b_n * Hkv + kv_n) * (size_t)S_max * D;
@@ -538,12 +572,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
             }
         }
 
-        // q is requested first, then the first tiles; q is prepared while the
-        // tiles are in flight
-        u32x4 qraw[NB][KU];
-        load_q_raw<D, NB>(q, b, kv, Hq, g, G, n, qraw);
-        [[maybe_unused]] NewRow<D> nr;
-        if constexpr (APPEND) load_new_row<D>(nr, app, ((size_t)b * Hkv + kv) * D, G, n);
+        if constexpr (!kAheadQ) {
+            load_q_raw<D, NB>(q, b, kv, Hq, g, G, n, qraw);
+            if constexpr (APPEND) load_new_row<D>(nr, app, ((size_t)b * Hkv + kv) * D, G, n);
+        }
         if (!have_pre) {
             if (sink_seg) load_tile<D>(ta, ksr, vsr, r0, G, n);
             else load_tile<D>(ta, kr, vr, r0, G, n);
@@ -552,14 +584,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
         }
 
         u32x4 qhi[NB][KU], qlo[NB][KU];
-        prep_q<D, NB>(qraw, fq, geo.qpos + 1, qscale, rope, G, qhi, qlo);
+        float cs[KU][4], sn[KU][4];
+        row_angles<D>(fq, geo.qpos + 1, rope, cs, sn);
+        prep_q<D, NB>(qraw, cs, sn, qscale, rope, G, qhi, qlo);
         // the new token's row, as a row of this context's attended range (it
         // is always in the band segment)
         const int r_new = geo.newrow - geo.lo + geo.ns;
         const bool ends = APPEND && r0 <= r_new && r_new < r1;   // this piece holds it
         const int rr_new = (r_new - sb0) & 31;                    // its row in its tile
         if constexpr (APPEND)
-            if (ends) rotate_new_key<D>(nr, geo.qpos + 1, fq, rope, G);
+            if (ends) rotate_new_key<D>(nr, cs, sn, rope, G);
 
         f32x4 o[NB][8];
         float m_run[NB], l_run[NB];
@@ -653,6 +687,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
 
         // ---- next context
         gs = ctx0 + r1;
+        if (gs >= ge) break;
+        if constexpr (kAheadQ) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int u = 0; u < KU; ++u) qraw[nb][u] = qraw_n[nb][u];
+            if constexpr (APPEND) nr = nr_n;
+        }
         if (++kv == Hkv) {
             kv = 0;
             base += (int64_t)Hkv * L;
