@@ -1193,120 +1193,33 @@ __global__ __launch_bounds__(kSelThreads) void band_score_kernel(RefineArgs ra) 
 // latent rows are copied straight from global memory into LDS by buffer
 // loads (all four sub-chunks requested at once, so the gather latency is
 // paid once), each row fetched once per 32 heads.  Wave (group, sub-chunk)
-// computes
-//   S^T[32 rows][16 heads] = C . Q^T   (18 k-steps of 16x16x32 bf16 MFMA)
-//   O^T[512][16 heads]     = C[:, :512]^T . P^T   (P as hi + lo bf16)
-// with its softmax state; the four states of a head group are merged in LDS
-// and one partial per (chunk, head) goes to combine_partials_kernel.
+// computes the scores of its sub-chunk,
+//   S^T[32 rows][16 heads] = C . Q^T   (18 k-steps of 16x16x32 bf16 MFMA),
+// the four waves of a head group exchange their row maxima through LDS, so
+// each forms P = exp2(S - M) with the chunk's exact maximum M (no running
+// rescale), and hand P (hi + lo bf16, in the layout of the PV operand) and
+// its row sums to each other through LDS.  Then wave (group, sc) computes
+// output dims 128 sc .. +127 over all 128 rows,
+//   O^T[128 dims][16 heads] = C[:, dims]^T . P^T,
+// and writes them: no softmax states are merged inside the workgroup, and
+// the partial write is spread over all eight waves.  P is kept in the LDS
+// bytes of latent dims 512..575 (the rope part, read only by the scores),
+// which are free once every wave has its scores.  One partial per (chunk,
+// head) goes to combine_partials_kernel.
 // (Two waves walking the four sub-chunks one after the other: 1.5 us slower
 // per call; 64 or 128 heads per workgroup, fewer re-reads of each row but
-// fewer workgroups: 1.5 and 10 us slower.)
+// fewer workgroups: 1.5 and 10 us slower.  Merging the four waves' softmax
+// states through LDS instead of splitting the output dims took two more
+// barrier rounds and left the partial write to two waves.)
 constexpr int kSubRows = 32;                         // rows per LDS sub-chunk
 constexpr int kRowBytes = kDqk * 2;                  // 1152
 constexpr int kRowStride = kRowBytes + 32;           // padded to 296 dwords (8 mod 16): see below
 constexpr int kSubCopies = (kSubRows * kRowStride + 1023) / 1024;   // 1 KB copies per sub-chunk
 constexpr int kSubBytes = kSubCopies * 1024;         // the last copy spills into slack nothing reads
-
-__device__ __forceinline__ void sparse_sub_step(const uint8_t* rows, const u32x4 (&qf)[kDqk / 32],
-                                                f32x4 (&o)[4][8], float& m_run, float& l_run,
-                                                int p0, int c1, float qscale, int G, int n) {
-    constexpr int KU = kDqk / 32;
-    const uint8_t* kb = rows + n * kRowStride + 16 * G;
-    f32x4 sc[2];
-#pragma unroll
-    for (int th = 0; th < 2; ++th) {
-        sc[th] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < KU; ++u)
-            sc[th] = mfma16(*reinterpret_cast<const u32x4*>(kb + 16 * th * kRowStride + 64 * u), qf[u], sc[th]);
-    }
-#pragma unroll
-    for (int th = 0; th < 2; ++th)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sc[th][i] *= qscale;
-            if (p0 + 16 * th + 4 * G + i >= c1) sc[th][i] = -INFINITY;
-        }
-    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mx = rows4_max(mx);                   // finite: row p0 < c1 is visible
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f)) {   // lazy rescale (probabilities < 2^8)
-        asm volatile("" ::: "memory");
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int dq = 0; dq < 4; ++dq)
-#pragma unroll
-            for (int t = 0; t < 8; ++t) o[dq][t] *= alpha;
-        m_run = m_new;
-    }
-    float pr[2][4];
-    float ls = 0.f;
-#pragma unroll
-    for (int th = 0; th < 2; ++th)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pr[th][i] = fast_exp2(sc[th][i] - m_run);
-            ls += pr[th][i];
-        }
-    l_run += rows4_sum(ls);
-    u32x4 ph, pl;
-    pack_p_hilo(pr, ph, pl);
-#pragma unroll
-    for (int dq = 0; dq < 4; ++dq) {
-        u32x4 vr[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-            vr[r] = *reinterpret_cast<const u32x4*>(rows + slot_row(G, r) * kRowStride + (128 * dq + 8 * n) * 2);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const u32x4 vc = column_of(vr, t);
-            o[dq][t] = mfma16(vc, ph, o[dq][t]);
-            o[dq][t] = mfma16(vc, pl, o[dq][t]);
-        }
-    }
-}
-
-// Eight-wave variant: one workgroup per (128 selected rows, 32 heads, batch
-// row) as above, but wave (hgw, sc) = (w & 1, w >> 1) takes only row
-// sub-chunk sc for head group hgw, so the four sub-chunks are processed at
-// once instead of one after the other.  The four states of a head group
-// are then merged through LDS (the row buffers, free by then) in two steps
-// of log-sum-exp rescaling, and wave sc = 0 writes the chunk's partial.
-// q is requested together with the selected indices; the copies follow the
-// first barrier, and one wait covers both the copies and q.
 constexpr int kAttnWaves = 8;
-constexpr int kAttnGroups = 2;                                      // 16 heads each
-
-__device__ __forceinline__ void merge_state(f32x4 (&o)[4][8], float& m_run, float& l_run,
-                                            const f32x4* slot, const float* ml, int lane, int n) {
-    const float mb = ml[2 * n], lb = ml[2 * n + 1];
-    const float M = fmaxf(m_run, mb);
-    if (M == -INFINITY) return;                 // both halves empty
-    const float a = fast_exp2(m_run - M), c = fast_exp2(mb - M);
-    l_run = a * l_run + c * lb;
-    m_run = M;
-#pragma unroll
-    for (int dq = 0; dq < 4; ++dq)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const f32x4 ob = slot[(dq * 8 + t) * 64 + lane];
-            o[dq][t] = a * o[dq][t] + c * ob;
-        }
-}
-
-__device__ __forceinline__ void put_state(const f32x4 (&o)[4][8], float m_run, float l_run,
-                                          f32x4* slot, float* ml, int lane, int G, int n) {
-#pragma unroll
-    for (int dq = 0; dq < 4; ++dq)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) slot[(dq * 8 + t) * 64 + lane] = o[dq][t];
-    if (G == 0) {
-        ml[2 * n] = m_run;
-        ml[2 * n + 1] = l_run;
-    }
-}
+constexpr int kAttnGroups = 2;                       // 16 heads each
+constexpr int kPBytes = 2 * kDv;                     // byte offset of the P slot in a row (dim 512)
+static_assert(kDqk - kDv == 64 && kSubRows == 2 * 16, "P of a wave: 16 rows x 128 B of rope dims");
 
 __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
@@ -1314,13 +1227,13 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
     int top_k, float qscale, float* __restrict__ part_o, float* __restrict__ part_ml,
     int n_chunks) {
     constexpr int KU = kDqk / 32;
-    static_assert(kSubBytes >= 64 * 32 * 16, "a state slot fits a row buffer");
     __shared__ __attribute__((aligned(16))) uint8_t rows0[kSubBytes];
     __shared__ __attribute__((aligned(16))) uint8_t rows1[kSubBytes];
     __shared__ __attribute__((aligned(16))) uint8_t rows2[kSubBytes];
     __shared__ __attribute__((aligned(16))) uint8_t rows3[kSubBytes];
     __shared__ int32_t sel_s[kRowsPerChunk];
-    __shared__ float ml_s[kAttnGroups][2][32];
+    __shared__ float mx_s[kAttnGroups][4][16];
+    __shared__ float l_s[kAttnGroups][4][16];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1349,7 +1262,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
         make_rsrc(latent + (size_t)b * S_max * kDqk, (uint32_t)S_max * kDqk * 2u);
     // copy j of sub-chunk s fills LDS bytes [1024 j, +1024) of its buffer,
     // lane l the 16 bytes at 1024 j + 16 l (row x / kRowStride, column
-    // x mod kRowStride); wave w takes copies j = 8 i + w of every sub-chunk
+    // x mod kRowStride); wave w takes copies j = 8 i + w of every sub-chunk.
+    // Rows past the selection read zeros (no traffic), so P = 0 meets V = 0.
     constexpr int kCopiesPerWave = (kSubCopies + kAttnWaves - 1) / kAttnWaves;
     int rr[kCopiesPerWave], cc[kCopiesPerWave];
 #pragma unroll
@@ -1383,52 +1297,99 @@ __global__ __launch_bounds__(64 * kAttnWaves) void sparse_attn_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("s_barrier" ::: "memory");
 
-    f32x4 o[4][8];
-#pragma unroll
-    for (int dq = 0; dq < 4; ++dq)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) o[dq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+    uint8_t* const mine = sc == 0 ? rows0 : sc == 1 ? rows1 : sc == 2 ? rows2 : rows3;
     const int p0 = c0 + kSubRows * sc;
+    // scores of the sub-chunk: sc2[th][i] is row 16 th + 4G + i, head n
+    f32x4 sc2[2];
+    float mx = -INFINITY;
     if (heads && p0 < c1) {
-        const uint8_t* rows = sc == 0 ? rows0 : sc == 1 ? rows1 : sc == 2 ? rows2 : rows3;
-        sparse_sub_step(rows, qf, o, m_run, l_run, p0, c1, qscale, G, n);
+        const uint8_t* kb = mine + n * kRowStride + 16 * G;
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+            sc2[th] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < KU; ++u)
+                sc2[th] = mfma16(*reinterpret_cast<const u32x4*>(kb + 16 * th * kRowStride + 64 * u), qf[u], sc2[th]);
+        }
+#pragma unroll
+        for (int th = 0; th < 2; ++th)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sc2[th][i] *= qscale;
+                if (p0 + 16 * th + 4 * G + i >= c1) sc2[th][i] = -INFINITY;
+            }
+        mx = fmaxf(fmaxf(fmaxf(sc2[0][0], sc2[0][1]), fmaxf(sc2[0][2], sc2[0][3])),
+                   fmaxf(fmaxf(sc2[1][0], sc2[1][1]), fmaxf(sc2[1][2], sc2[1][3])));
+        mx = rows4_max(mx);
+    } else {
+        sc2[0] = sc2[1] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
-    __syncthreads();                            // the row buffers are free from here
+    if (G == 0) mx_s[hgw][sc][n] = mx;
+    // maxima visible; every wave is past its score reads, so the rope dims
+    // of the row buffers are free for P
+    __syncthreads();
 
-    // merge step 1: sc 1 -> 0 and 3 -> 2 (slots in buffers 2 hgw + sc / 2)
-    auto slot = [&](int i) {
-        return reinterpret_cast<f32x4*>(i == 0 ? rows0 : i == 1 ? rows1 : i == 2 ? rows2 : rows3);
-    };
-    if (sc & 1) put_state(o, m_run, l_run, slot(2 * hgw + (sc >> 1)), ml_s[hgw][sc >> 1], lane, G, n);
-    __syncthreads();
-    if (!(sc & 1)) merge_state(o, m_run, l_run, slot(2 * hgw + (sc >> 1)), ml_s[hgw][sc >> 1], lane, n);
-    __syncthreads();
-    // merge step 2: sc 2 -> 0
-    if (sc == 2) put_state(o, m_run, l_run, slot(2 * hgw), ml_s[hgw][0], lane, G, n);
-    __syncthreads();
-    if (sc != 0 || !heads) return;
-    merge_state(o, m_run, l_run, slot(2 * hgw), ml_s[hgw][0], lane, n);
+    // the chunk's maximum (finite for a head wave: row c0 < c1 is in
+    // sub-chunk 0), P and its row sums
+    const float M = fmaxf(fmaxf(mx_s[hgw][0][n], mx_s[hgw][1][n]), fmaxf(mx_s[hgw][2][n], mx_s[hgw][3][n]));
+    float pr[2][4];
+    float ls = 0.f;
+#pragma unroll
+    for (int th = 0; th < 2; ++th)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pr[th][i] = heads ? fast_exp2(sc2[th][i] - M) : 0.f;
+            ls += pr[th][i];
+        }
+    ls = rows4_sum(ls);
+    u32x4 ph, pl;
+    pack_p_hilo(pr, ph, pl);
+    // the wave's P: rows 16 hgw + lane / 4 of its buffer, bytes
+    // kPBytes + 32 (lane % 4) (hi) and + 16 (lo)
+    auto pslot = [&](uint8_t* buf) { return buf + (16 * hgw + (lane >> 2)) * kRowStride + kPBytes + 32 * (lane & 3); };
+    *reinterpret_cast<u32x4*>(pslot(mine)) = ph;
+    *reinterpret_cast<u32x4*>(pslot(mine) + 16) = pl;
+    if (G == 0) l_s[hgw][sc][n] = ls;
+    __syncthreads();                            // P and the row sums visible
+    if (!heads) return;
+
+    // O^T for dims 128 sc .. +127 over the chunk's sub-chunks:
+    // o[t][i] is dim 128 sc + 8 (4G + i) + t of head n
+    f32x4 o[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+        if (c0 + kSubRows * s2 >= c1) break;    // wave-uniform: the rest has P = 0
+        uint8_t* const buf = s2 == 0 ? rows0 : s2 == 1 ? rows1 : s2 == 2 ? rows2 : rows3;
+        const u32x4 qh = *reinterpret_cast<const u32x4*>(pslot(buf));
+        const u32x4 ql = *reinterpret_cast<const u32x4*>(pslot(buf) + 16);
+        u32x4 vr[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            vr[r] = *reinterpret_cast<const u32x4*>(buf + slot_row(G, r) * kRowStride + (128 * sc + 8 * n) * 2);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const u32x4 vc = column_of(vr, t);
+            o[t] = mfma16(vc, qh, o[t]);
+            o[t] = mfma16(vc, ql, o[t]);
+        }
+    }
 
     const size_t idx = ((size_t)b * H + h) * n_chunks + chunk;
     float* po = part_o + idx * kDv;
 #pragma unroll
-    for (int dq = 0; dq < 4; ++dq)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d0 = 128 * dq + 8 * (4 * G + i);   // this lane holds d = d0 + t
-            *reinterpret_cast<f32x4*>(po + d0) = f32x4{o[dq][0][i], o[dq][1][i], o[dq][2][i], o[dq][3][i]};
-            *reinterpret_cast<f32x4*>(po + d0 + 4) = f32x4{o[dq][4][i], o[dq][5][i], o[dq][6][i], o[dq][7][i]};
-        }
-    if (G == 0) {
-        part_ml[idx * 2] = m_run;
-        part_ml[idx * 2 + 1] = l_run;
+    for (int i = 0; i < 4; ++i) {
+        const int d0 = 128 * sc + 8 * (4 * G + i);
+        *reinterpret_cast<f32x4*>(po + d0) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
+        *reinterpret_cast<f32x4*>(po + d0 + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
+    }
+    if (sc == 0 && G == 0) {
+        part_ml[idx * 2] = M;
+        part_ml[idx * 2 + 1] = l_s[hgw][0][n] + l_s[hgw][1][n] + l_s[hgw][2][n] + l_s[hgw][3][n];
     }
 }
 
-// The sub-step of the dense kernel: sparse_sub_step with the key reads of the
-// score product issued in batches of six per row half ahead of their MFMAs
-// (one read in flight at a time otherwise: the register budget is tight).
 // ---------------------------------------------------------------------------
 // 4. dense absorbed-MLA decode (no selection: every row of the context).
 // The same MQA attention as sparse_attn_kernel over contiguous rows.  One
