@@ -138,9 +138,11 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
 
 /* As gqa_decode with the number of work ranges chosen by the caller:
  * the rows of all B*Hkv contexts, taken in (batch, kv head, row) order, are
- * cut into n_parts equal ranges, each streamed by one wavefront (n_parts in
- * [1, 2^20]; 0 = the library's default).  The workspace must then hold
- * gqa_decode_workspace_size_parts(...) bytes (it grows with n_parts). */
+ * cut into n_parts equal ranges (n_parts in [1, 2^20]; 0 = the library's
+ * default); each group of four consecutive ranges is streamed by the four
+ * wavefronts of one workgroup, which take its 32-row tiles in turn.  The
+ * workspace must then hold gqa_decode_workspace_size_parts(...) bytes (it
+ * grows with n_parts). */
 size_t gqa_decode_workspace_size_parts(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                        int32_t S_max, int32_t n_parts);
 

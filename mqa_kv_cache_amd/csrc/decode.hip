@@ -238,21 +238,22 @@ __device__ __forceinline__ void locate(const int32_t* seq_lens, int B, int Hkv, 
     L = 1;
 }
 
-// The wave's first piece: the row space total, the range length R, the
-// wave's first global row gs = w R and the context holding it (batch b, the
-// global row `base` of its (kv 0, row 0), its attended rows L).  With at
-// most 64 sequences one vector load of seq_lens and one wave-wide prefix sum
-// give all of them; more sequences take the chunked passes.  Returns false
-// when the wave's range is empty.
+// The first piece of group range w: the row space total, the group range
+// length R = grp ceil(total / n_parts) (grp consecutive ranges of the
+// n_parts), its first global row gs = w R and the context holding it
+// (batch b, the global row `base` of its (kv 0, row 0), its attended rows
+// L).  With at most 64 sequences one vector load of seq_lens and one
+// wave-wide prefix sum give all of them; more sequences take the chunked
+// passes.  Returns false when the group range is empty.
 __device__ __forceinline__ bool first_piece(const int32_t* seq_lens, int B, int Hkv, int S_max,
-                                            int n_parts, int w, int lane, const CacheView& cv,
+                                            int n_parts, int grp, int w, int lane, const CacheView& cv,
                                             int64_t& total, int64_t& R, int64_t& gs, int& b,
                                             int64_t& base, int& L) {
     if (B <= 64) {
         const int Lb = lane < B ? ctx_len(seq_lens, lane, S_max, cv) : 0;
         const int64_t incl = wave_scan_incl((int64_t)Hkv * Lb, lane);
         total = __shfl(incl, 63, 64);
-        R = (total + n_parts - 1) / n_parts;
+        R = grp * ((total + n_parts - 1) / n_parts);
         gs = (int64_t)w * R;
         if (gs >= total) return false;
         const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < B && gs < incl);
@@ -264,7 +265,7 @@ __device__ __forceinline__ bool first_piece(const int32_t* seq_lens, int B, int 
     }
     const RowSpace rs = row_space(seq_lens, B, Hkv, S_max, n_parts, lane, cv);
     total = rs.total;
-    R = rs.R;
+    R = grp * rs.R;
     gs = (int64_t)w * R;
     if (gs >= total) return false;
     locate(seq_lens, B, Hkv, S_max, gs, lane, cv, b, base, L);
@@ -478,6 +479,16 @@ __device__ __forceinline__ void store_new_row(const NewRow<D>& nr, uint16_t* kro
     if (G == Gs && n < D / 8) *reinterpret_cast<u32x4*>(vrow + 8 * n) = nr.v;
 }
 
+// The kWaves waves of a workgroup stream one group range of kWaves
+// consecutive ranges together: its 32-row tiles, counted across its pieces
+// and segments in order, go to the waves in turn (tile t to wave t mod
+// kWaves).  At any moment the group's waves then read neighbouring tiles; a
+// read probe of this step's size with no math ran 11% faster (268 MB) and
+// 1.6% faster (1.6 GB) that way than with a contiguous range per wave.  Each
+// wave keeps one softmax state per piece (context) of the group range and
+// writes it to slot kWaves (W + ctx) + wave, an empty one (m = -inf, l = 0,
+// o = 0) when none of the piece's tiles was its turn, so the states of a
+// context are contiguous and the combine needs no per-wave bookkeeping.
 template <int D, int NB, bool APPEND>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
@@ -485,17 +496,18 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
     int Hkv, int S_max, float qscale, RopeDev rope, float* __restrict__ part_o,
     float* __restrict__ part_ml, int n_parts, AppendArgs app, CacheView cv) {
     constexpr int KU = D / 32;
+    constexpr int kStep = 32 * kWaves;   // rows between two tiles of one wave
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4, n = lane & 15;
     const int g = Hq / Hkv;
     // wave-uniform by construction; readfirstlane lets the compiler keep every
     // derived address and buffer descriptor in scalar registers
-    const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
-    if (w >= n_parts) return;
-    int64_t total, R, gs, base;   // base: global row of (b, kv 0, row 0)
+    const int W = blockIdx.x;                                             // the group range
+    const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);       // this wave's turn
+    int64_t total, R, gs, base;   // base: global row of (b, kv 0, row 0); R: the group range
     int b, L;
-    if (!first_piece(seq_lens, B, Hkv, S_max, n_parts, w, lane, cv, total, R, gs, b, base, L))
-        return;
+    if (!first_piece(seq_lens, B, Hkv, S_max, n_parts, kWaves, W, lane, cv, total, R, gs, b, base, L))
+        return;                                                           // whole workgroup
     const int64_t ge = min(gs + R, total);
     b = __builtin_amdgcn_readfirstlane(b);
     L = __builtin_amdgcn_readfirstlane(L);
@@ -503,9 +515,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
     int kv = (int)((gs - base) / L);
     QFreq<D> fq;
     load_freq<D>(rope, G, n, fq);
-    const RowSpace rs{total, R};
-    // the first tile of the next segment or piece, requested with the last
-    // tile of the current one (pre_b: it went into tb rather than ta)
+    // tiles of the group range before the current piece (every wave counts them)
+    int tau = 0;
+    // the wave's first tile of the current piece was requested by the piece
+    // before (pre_b: into tb rather than ta)
     bool have_pre = false, pre_b = false;
     DecodeTile<D> ta, tb;
     // the piece's q rows (and, with the cache write, its new key and value
@@ -535,20 +548,27 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
         const int sb0 = max(r0, geo.ns);
         const size_t first = slice + (size_t)(geo.lo - geo.ns) * D;
         const uint32_t nbytes = (uint32_t)r1 * D * 2u;
-        const __amdgpu_buffer_rsrc_t kr = make_rsrc(k_cache + first, nbytes);
-        const __amdgpu_buffer_rsrc_t vr = make_rsrc(v_cache + first, nbytes);
         const uint32_t sbytes = (uint32_t)max(sa1, 0) * D * 2u;
-        const __amdgpu_buffer_rsrc_t ksr = make_rsrc(k_cache + slice, sbytes);
-        const __amdgpu_buffer_rsrc_t vsr = make_rsrc(v_cache + slice, sbytes);
         const bool sink_seg = r0 < sa1;
+        // the segments' tiles, and this wave's first one in each (valid when
+        // below the segment's count)
+        const int nta = sink_seg ? (sa1 - r0 + 31) >> 5 : 0;
+        const int ntb = sb0 < r1 ? (r1 - sb0 + 31) >> 5 : 0;
+        const int ka = (j - tau) & (kWaves - 1);
+        const int kb = (j - tau - nta) & (kWaves - 1);
+        const bool in_a = ka < nta, in_b = kb < ntb;
+        const int tau_n = tau + nta + ntb;
 
-        // The piece after this one starts at row 0 of the next context; its
-        // first segment's buffers (none when this is the wave's last piece:
-        // an empty buffer reads zeros without traffic).
+        // The piece after this one starts at row 0 of the next context; the
+        // buffers of its first segment and this wave's first tile there
+        // (none when that is not this wave's turn or this is the group's
+        // last piece: an empty buffer reads zeros without traffic).
         const int64_t gs_n = ctx0 + r1;
         const uint16_t* nkp = k_cache;
         const uint16_t* nvp = v_cache;
         uint32_t nbytes_n = 0u;
+        int x0_n = 0;
+        bool pre_n = false;   // that tile exists
         u32x4 qraw_n[NB][KU];
         [[maybe_unused]] NewRow<D> nr_n;
         if (gs_n < ge) {
@@ -561,39 +581,51 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
             const CtxGeom geo_n = kv + 1 == Hkv ? ctx_geom(seq_lens, b_n, S_max, cv) : geo;
             const int r1_n = (int)min((int64_t)geo_n.n, ge - gs_n);
             const size_t slice_n = ((size_t)b_n * Hkv + kv_n) * (size_t)S_max * D;
+            int rows_n;
             if (geo_n.ns > 0) {          // its sink segment comes first
                 nkp = k_cache + slice_n;
                 nvp = v_cache + slice_n;
-                nbytes_n = (uint32_t)min(r1_n, geo_n.ns) * D * 2u;
+                rows_n = min(r1_n, geo_n.ns);
             } else {
                 nkp = k_cache + slice_n + (size_t)geo_n.lo * D;
                 nvp = v_cache + slice_n + (size_t)geo_n.lo * D;
-                nbytes_n = (uint32_t)r1_n * D * 2u;
+                rows_n = r1_n;
             }
+            const int k_n = (j - tau_n) & (kWaves - 1);
+            pre_n = 32 * k_n < rows_n;
+            x0_n = 32 * k_n;
+            nbytes_n = pre_n ? (uint32_t)rows_n * D * 2u : 0u;
         }
 
         if constexpr (!kAheadQ) {
             load_q_raw<D, NB>(q, b, kv, Hq, g, G, n, qraw);
             if constexpr (APPEND) load_new_row<D>(nr, app, ((size_t)b * Hkv + kv) * D, G, n);
         }
+        // the wave's first tile of the piece, unless requested already
         if (!have_pre) {
-            if (sink_seg) load_tile<D>(ta, ksr, vsr, r0, G, n);
-            else load_tile<D>(ta, kr, vr, r0, G, n);
+            if (in_a) load_tile<D>(ta, make_rsrc(k_cache + slice, sbytes), make_rsrc(v_cache + slice, sbytes),
+                                   r0 + 32 * ka, G, n);
+            else if (in_b) load_tile<D>(ta, make_rsrc(k_cache + first, nbytes), make_rsrc(v_cache + first, nbytes),
+                                        sb0 + 32 * kb, G, n);
         } else if (pre_b) {
             ta = tb;
         }
 
-        u32x4 qhi[NB][KU], qlo[NB][KU];
-        float cs[KU][4], sn[KU][4];
-        row_angles<D>(fq, geo.qpos + 1, rope, cs, sn);
-        prep_q<D, NB>(qraw, cs, sn, qscale, rope, G, qhi, qlo);
         // the new token's row, as a row of this context's attended range (it
-        // is always in the band segment)
+        // is always in the band segment), and whether its tile is this wave's
         const int r_new = geo.newrow - geo.lo + geo.ns;
         const bool ends = APPEND && r0 <= r_new && r_new < r1;   // this piece holds it
+        const bool owns = ends && ((tau + nta + ((r_new - sb0) >> 5)) & (kWaves - 1)) == j;
         const int rr_new = (r_new - sb0) & 31;                    // its row in its tile
-        if constexpr (APPEND)
-            if (ends) rotate_new_key<D>(nr, cs, sn, rope, G);
+
+        u32x4 qhi[NB][KU], qlo[NB][KU];
+        if (in_a || in_b) {
+            float cs[KU][4], sn[KU][4];
+            row_angles<D>(fq, geo.qpos + 1, rope, cs, sn);
+            prep_q<D, NB>(qraw, cs, sn, qscale, rope, G, qhi, qlo);
+            if constexpr (APPEND)
+                if (owns) rotate_new_key<D>(nr, cs, sn, rope, G);
+        }
 
         f32x4 o[NB][8];
         float m_run[NB], l_run[NB];
@@ -607,14 +639,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
 
         auto fix = [&](DecodeTile<D>& t, int t0) {
             if constexpr (APPEND)
-                if (ends && t0 <= r_new && r_new < t0 + 32) swap_new_row<D>(t, nr, rr_new, G, n);
+                if (owns && t0 <= r_new && r_new < t0 + 32) swap_new_row<D>(t, nr, rr_new, G, n);
         };
-        // Tiles t0 = s0, s0 + 32, .. of rows [s0, s1), the first already in
-        // ta.  Each step requests the step after next's tile; the last step
-        // requests instead the first tile of what follows (row x0 of the
-        // buffers xk, xv), so the wave never waits a whole load latency
-        // between segments or pieces.  Returns true when that tile went into
-        // tb.
+        // This wave's tiles t0 = s0, s0 + kStep, .. of rows [s0, s1) (the
+        // segment's tiles that are its turn), the first already in ta.  Each
+        // step requests the wave's next tile; the last step requests instead
+        // the wave's first tile of what follows (row x0 of the buffers xb),
+        // so the wave never waits a whole load latency between segments or
+        // pieces.  Returns true when that tile went into tb.
         // (buffers are passed as base pointers and byte sizes, so the choice
         // is a scalar select and every step issues the same loads)
         struct Buf {
@@ -624,45 +656,48 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
         };
         auto segment = [&](Buf sb, int s0, int s1, Buf xb, int x0) {
             for (int t0 = s0;;) {
-                bool last = t0 + 32 >= s1;
+                bool last = t0 + kStep >= s1;
                 load_tile<D>(tb, make_rsrc(last ? xb.k : sb.k, last ? xb.bytes : sb.bytes),
                              make_rsrc(last ? xb.v : sb.v, last ? xb.bytes : sb.bytes),
-                             last ? x0 : t0 + 32, G, n);
+                             last ? x0 : t0 + kStep, G, n);
                 fix(ta, t0);
                 tile_math<D, NB>(ta, t0, s1, G, qhi, qlo, o, m_run, l_run);
-                t0 += 32;
+                t0 += kStep;
                 if (t0 >= s1) return true;
-                last = t0 + 32 >= s1;
+                last = t0 + kStep >= s1;
                 load_tile<D>(ta, make_rsrc(last ? xb.k : sb.k, last ? xb.bytes : sb.bytes),
                              make_rsrc(last ? xb.v : sb.v, last ? xb.bytes : sb.bytes),
-                             last ? x0 : t0 + 32, G, n);
+                             last ? x0 : t0 + kStep, G, n);
                 fix(tb, t0);
                 tile_math<D, NB>(tb, t0, s1, G, qhi, qlo, o, m_run, l_run);
-                t0 += 32;
+                t0 += kStep;
                 if (t0 >= s1) return false;
             }
         };
         const Buf band{k_cache + first, v_cache + first, nbytes};
         const Buf next{nkp, nvp, nbytes_n};
-        if (sink_seg) {
+        if (in_a) {
             const Buf sinkb{k_cache + slice, v_cache + slice, sbytes};
-            if (sb0 < r1) {
-                if (segment(sinkb, r0, sa1, band, sb0)) ta = tb;
+            if (in_b) {
+                if (segment(sinkb, r0 + 32 * ka, sa1, band, sb0 + 32 * kb)) ta = tb;
             } else {
-                pre_b = segment(sinkb, r0, sa1, next, 0);
+                pre_b = segment(sinkb, r0 + 32 * ka, sa1, next, x0_n);
             }
         }
-        if (sb0 < r1) pre_b = segment(band, sb0, r1, next, 0);
-        have_pre = true;
+        if (in_b) pre_b = segment(band, sb0 + 32 * kb, r1, next, x0_n);
+        // the wave's first tile of the next piece was requested by its last
+        // step here (when it had one), or is not its turn
+        have_pre = (in_a || in_b) && pre_n;
 
         if constexpr (APPEND)
-            if (ends) {
+            if (owns) {
                 const size_t row = slice + (size_t)geo.newrow * D;
                 store_new_row<D>(nr, app.k_cache + row, app.v_cache + row, rr_new, G, n);
             }
 
-        // ---- partial (m, l, o) of this piece
-        const int64_t slot = gs / rs.R + ((int64_t)b * Hkv + kv);
+        // ---- partial (m, l, o) of this wave's tiles of the piece (empty
+        // when it had none)
+        const int64_t slot = (int64_t)kWaves * (W + ((int64_t)b * Hkv + kv)) + j;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int hl = nb * 16 + n;
@@ -687,6 +722,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
 
         // ---- next context
         gs = ctx0 + r1;
+        tau = tau_n;
         if (gs >= ge) break;
         if constexpr (kAheadQ) {
 #pragma unroll
@@ -705,8 +741,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
     }
 }
 
-// One wave per (batch, q head): merges the states of the pieces of its
-// context, slots floor(x/R) + i for the global rows x of context i.  Lane j
+// One wave per (batch, q head): merges the states of its context, slots
+// kWaves (floor(x/R) + i) + wave for the global rows x of context i and the
+// group ranges of R rows (kWaves per range group, contiguous).  Lane j
 // reads the (m, l) of piece j, so the maximum and the weights take one
 // round trip, and the o rows of the first 16 pieces (lane: D/64 values) are
 // requested in the same round trip; further pieces are read eight at a time.
@@ -736,12 +773,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
         total += rows;
         base += before;
     }
-    const int64_t R = (total + n_parts - 1) / n_parts;
+    const int64_t R = kWaves * ((total + n_parts - 1) / n_parts);
     const int L = ctx_len(seq_lens, b, S_max, cv);
     const int64_t x0 = base + (int64_t)kv * L;
     const int64_t ctx = (int64_t)b * Hkv + kv;
-    const int64_t s0 = x0 / R + ctx;
-    const int np = (int)((x0 + L - 1) / R + ctx - s0 + 1);
+    const int64_t s0 = kWaves * (x0 / R + ctx);
+    const int np = (int)(kWaves * ((x0 + L - 1) / R - x0 / R + 1));
     const size_t pstride = (size_t)g * D;
     float acc[PER];
 #pragma unroll
@@ -767,7 +804,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
         float M = m;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, wave_shfl_xor(M, o));
-        const float M_new = fmaxf(M_run, M);       // finite: every piece has a row
+        // finite: each range group's kWaves states hold a row, and chunks of
+        // 64 states start at such groups
+        const float M_new = fmaxf(M_run, M);
         const float rescale = fast_exp2(M_run - M_new);
         den *= rescale;
 #pragma unroll
@@ -828,7 +867,7 @@ void launch_split(hipStream_t s, const void* q, const void* k, const void* v, co
 DecodeLayout decode_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t n_parts) {
     DecodeLayout l;
     l.n_parts = n_parts;
-    l.slots = (int64_t)n_parts + (int64_t)B * Hkv;
+    l.slots = (int64_t)kWaves * ((n_parts + kWaves - 1) / kWaves + (int64_t)B * Hkv);
     const size_t units = (size_t)l.slots * (Hq / Hkv);
     l.o_bytes = (units * D * sizeof(float) + 255) & ~(size_t)255;
     l.ml_bytes = (units * 2 * sizeof(float) + 255) & ~(size_t)255;

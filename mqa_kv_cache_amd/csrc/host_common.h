@@ -38,7 +38,7 @@ hipError_t launch_rope_apply(const void* in, void* out, const int32_t* positions
 
 struct DecodeLayout {
     int32_t n_parts;       // equal row ranges of the global row space (one wave each)
-    int64_t slots;         // n_parts + B*Hkv partial-state slots
+    int64_t slots;         // 4 (ceil(n_parts / 4) + B*Hkv) partial-state slots
     size_t o_bytes;        // partial outputs  fp32 [slots][g][D]
     size_t ml_bytes;       // partial (m, l)   fp32 [slots][g][2]
     size_t total;
