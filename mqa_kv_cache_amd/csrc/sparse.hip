@@ -21,9 +21,11 @@
 //    latent rows (the indexed rows are read straight from the cache; no copy
 //    of the selection is made).  Same MFMA structure as the dense decode:
 //    S^T = C . Q^T over 576 dims, softmax, O^T += C[:, :512]^T . P^T; a
-//    workgroup covers 32 heads and 128 selected rows staged through LDS,
-//    eight waves each take 16 heads and 32 rows, their states are merged in
-//    LDS, and one partial (m, l, o) per head goes to combine_partials_kernel.
+//    workgroup covers 32 heads and 128 selected rows staged through LDS;
+//    eight waves each score 16 heads over 32 rows, exchange maxima, P and
+//    row sums through LDS, and each writes 128 of the 512 output dims of
+//    its 16 heads over all 128 rows: one partial (m, l, o) per head goes to
+//    combine_partials_kernel.
 // 4. mla_dense_kernel: the same attention over every row of the context
 //    (dense absorbed-MLA decode), 64 heads per workgroup, the rows streamed
 //    through a ring of LDS buffers.
