@@ -44,6 +44,10 @@ DECODE_CASES = [
     (4, 16, 2, 128, 64, [5, 64, 65, 300], 4, 0, 1, False),   # rolling: short, full, wrapped
     (3, 16, 2, 128, 96, [96, 150, 1000], 4, 0, 1, True),     # rolling write skips the sink slots
     (2, 12, 4, 64, 50, [31, 77], 10, 0, 1, True),            # rolling, g=3, head dim 64
+    # ~128K attended rows: a workgroup's four waves share ranges of 16+ tiles,
+    # and context starts (two tiles of sinks, then the band) fall inside them
+    (4, 8, 4, 128, 10000, [10000, 9000, 8300, 9999], 40, 8192, 0, True),
+    (4, 8, 4, 128, 8192, [20000, 9000, 8192, 12345], 40, 0, 1, True),
 ]
 
 
