@@ -102,12 +102,15 @@ def test_decode_calls_on_two_streams_run_concurrently_and_agree(m):
 
 def test_decode_no_rope_and_gqa_equals_repeated_mha(m):
     """GQA on the GPU equals an MHA run over K/V materialised with each head
-    repeated g times (repeat_interleave): bit for bit when every context is
-    one piece (n_parts=1), within rounding for the default work split (whose
-    piece boundaries depend on the total row count)."""
+    repeated g times (repeat_interleave): bit for bit when the whole row
+    space is one group range (n_parts=1) and every context holds a multiple
+    of four 32-row tiles (250 and 100 rows: 8 and 4 tiles, the last ragged),
+    so each head's tiles go to the same waves and states in both runs;
+    within rounding for the default work split (whose range boundaries
+    depend on the total row count)."""
     import torch
     B, Hq, Hkv, D, S = 2, 16, 4, 128, 300
-    d = decode_inputs_host(B, Hq, Hkv, D, S, 13, [300, 123])
+    d = decode_inputs_host(B, Hq, Hkv, D, S, 13, [250, 100])
     sl = torch.from_numpy(d["seq_lens"]).cuda()
     q, k, v = to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"])
     g = Hq // Hkv
