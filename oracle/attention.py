@@ -14,12 +14,33 @@ Readings where the pages leave a step open:
   (the pages' decode concatenates the new key to the past keys before
   attending).
 * Cached keys are stored after RoPE, so decode rotates only q.
+* The cache holds bf16, so a decode step that writes its new key attends
+  over the key as cached: the rotated key rounded to the nearest bf16 value
+  (ties to even), not the unrounded rotation (the pages' decode attends
+  over the cache after the new row is concatenated to it).
 """
 from __future__ import annotations
 
 import numpy as np
 
 from . import rope as _rope
+
+
+def round_bf16(x) -> np.ndarray:
+    """The nearest bfloat16 value of each element, as float64.
+
+    bfloat16 keeps float32's sign and 8-bit exponent and 7 stored fraction
+    bits, i.e. 8 significant bits: in the binade [2^(e-1), 2^e) its values
+    are 2^(e-8) apart.  Round to nearest, ties to the even neighbour (the
+    one whose last significant bit is 0).  Below bfloat16's smallest normal
+    value 2^-126 the spacing stays 2^-133 (its subnormals).  Finite
+    results only (no overflow handling: the cached keys are far inside the
+    range).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                       # |x| in [2^(e-1), 2^e)
+    e = np.maximum(e, -125)                  # subnormal spacing 2^-133
+    return np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)   # rint: half to even
 
 
 def softmax(s: np.ndarray) -> np.ndarray:
@@ -175,8 +196,10 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, rope_p, pairs=None) -> n
 
 def append_rows(k_cache, v_cache, k_new, v_new, seq_lens, rope_p):
     """The decode step's cache write: the new token's key, rotated at its
-    position seq_lens[b]-1, and its value go into row seq_lens[b]-1 of every
-    kv head; returns new (float64) copies of the caches.
+    position seq_lens[b]-1 and rounded to bf16 as the cache stores it
+    (:func:`round_bf16`), and its value (bf16 already) go into row
+    seq_lens[b]-1 of every kv head; returns new (float64) copies of the
+    caches.
 
     [注意力机制进化史] "解码中的KV Cache" (the new key and value are
     concatenated to the past ones); [transformer架构] §1.1 (the key is
@@ -193,7 +216,7 @@ def append_rows(k_cache, v_cache, k_new, v_new, seq_lens, rope_p):
         if rope_p is not None:
             kr = _rope.rotate_rows(k_new[b][None], np.array([pos]),
                                    _rope.with_length(rope_p, pos + 1))[0]
-        kc[b, :, pos] = kr
+        kc[b, :, pos] = round_bf16(kr)
         vc[b, :, pos] = v_new[b]
     return kc, vc
 
@@ -280,7 +303,7 @@ def append_rows_window(k_cache, v_cache, k_new, v_new, seq_lens, rope_p, rolling
         kr = np.asarray(k_new[b], dtype=np.float64)
         if rope_p is not None:
             kr = _rope.rotate_rows(kr[None], np.array([pos]), _rope.with_length(rope_p, pos + 1))[0]
-        kc[b, :, row] = kr
+        kc[b, :, row] = round_bf16(kr)
         vc[b, :, row] = np.asarray(v_new[b], dtype=np.float64)
     return kc, vc
 
