@@ -44,6 +44,10 @@ CASES = [
     (1, 64, 1, 128, 96, [96]),                # g=64 (four head blocks)
     (2, 8, 2, 64, 333, [333, 65]),            # head dim 64
     (2, 12, 4, 128, 129, [129, 33]),          # g=3: partial head block
+    # more than 64 sequences: the row space and a range's first context are
+    # found by the chunked prefix passes (64 sequences per pass)
+    (100, 8, 2, 128, 200, [int(x) for x in np.random.default_rng(15).integers(1, 201, 100)]),
+    (130, 8, 1, 64, 96, [int(x) for x in np.random.default_rng(16).integers(1, 97, 130)]),
 ]
 
 
@@ -52,7 +56,12 @@ def test_decode_parity_small(m, case):
     B, Hq, Hkv, D, S, lens = case
     rope = rope_settings(ROPE_PLAIN, base=500000.0)
     got, ref = _run_case(m, B, Hq, Hkv, D, S, np.array(lens, dtype=np.int32), rope, seed=11)
-    assert_close(got, ref, f"decode {case}")
+    assert_close(got, ref, f"decode {case[:5]}")
+    if B > 64:   # and with few, long ranges (groups that span many sequences)
+        for parts in (1, 7):
+            got, ref = _run_case(m, B, Hq, Hkv, D, S, np.array(lens, dtype=np.int32), rope, seed=11,
+                                 n_parts=parts)
+            assert_close(got, ref, f"decode {case[:5]} parts={parts}")
 
 
 def test_decode_yarn_and_split_independence(m):

@@ -48,6 +48,8 @@ DECODE_CASES = [
     # and context starts (two tiles of sinks, then the band) fall inside them
     (4, 8, 4, 128, 10000, [10000, 9000, 8300, 9999], 40, 8192, 0, True),
     (4, 8, 4, 128, 8192, [20000, 9000, 8192, 12345], 40, 0, 1, True),
+    # more than 64 sequences (the chunked prefix passes), sinks, window and the write
+    (80, 8, 2, 128, 300, [int(x) for x in np.random.default_rng(17).integers(1, 301, 80)], 4, 100, 0, True),
 ]
 
 
