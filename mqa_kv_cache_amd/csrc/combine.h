@@ -46,19 +46,14 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(
         }
         const float m = lane < cn ? ml[2 * (s0 + lane)] : -INFINITY;
         const float l = lane < cn ? ml[2 * (s0 + lane) + 1] : 0.f;
-        float M = m;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, wave_shfl_xor(M, o));
+        const float M = wave_max(m);
         const float M_new = fmaxf(M_run, M);   // finite: every split holds a row
         const float rescale = fast_exp2(M_run - M_new);
         den *= rescale;
 #pragma unroll
         for (int j = 0; j < PER; ++j) acc[j] *= rescale;
         const float wl = lane < cn ? fast_exp2(m - M_new) : 0.f;
-        float dsum = wl * l;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) dsum += wave_shfl_xor(dsum, o);
-        den += dsum;
+        den += wave_sum(wl * l);
 #pragma unroll
         for (int jj = 0; jj < kFirst; ++jj) {
             const float wgt = jj < cn ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(

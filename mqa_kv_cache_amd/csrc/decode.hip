@@ -192,13 +192,34 @@ __device__ __forceinline__ int ctx_len(const int32_t* seq_lens, int b, int S_max
                                        const CacheView& cv) {
     return ctx_geom(seq_lens, b, S_max, cv).n;
 }
-// inclusive prefix sum over the 64 lanes
+// 64-bit value of lane (lane - n) within the lane's 16-lane row, 0 for the
+// first n lanes of a row (DPP row_shr:n on both halves)
+template <int N>
+__device__ __forceinline__ int64_t row_shr64(int64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x110 + N, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)((uint64_t)v >> 32), 0x110 + N, 0xF, 0xF, false);
+    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+// the 64-bit value of a (wave-uniform) lane
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), l);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+// inclusive prefix sum over the 64 lanes (every lane active): four DPP
+// shifts give each 16-lane row its own scan, then rows 1-3 add the totals
+// of the rows before them (lanes 15, 31, 47).  A scan through LDS
+// permutes took two dependent LDS round trips per step.
 __device__ __forceinline__ int64_t wave_scan_incl(int64_t x, int lane) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int64_t y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+    x += row_shr64<1>(x);
+    x += row_shr64<2>(x);
+    x += row_shr64<4>(x);
+    x += row_shr64<8>(x);
+    const int64_t t0 = readlane64(x, 15), t1 = readlane64(x, 31), t2 = readlane64(x, 47);
+    const int row = lane >> 4;
+    if (row >= 1) x += t0;
+    if (row >= 2) x += t1;
+    if (row >= 3) x += t2;
     return x;
 }
 __device__ __forceinline__ RowSpace row_space(const int32_t* seq_lens, int B, int Hkv, int S_max,
@@ -206,10 +227,8 @@ __device__ __forceinline__ RowSpace row_space(const int32_t* seq_lens, int B, in
     int64_t total = 0;
     for (int c0 = 0; c0 < B; c0 += 64) {
         const int bb = c0 + lane;
-        int64_t rows = bb < B ? (int64_t)Hkv * ctx_len(seq_lens, bb, S_max, cv) : 0;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) rows += __shfl_xor(rows, o, 64);
-        total += rows;
+        const int64_t rows = bb < B ? (int64_t)Hkv * ctx_len(seq_lens, bb, S_max, cv) : 0;
+        total += readlane64(wave_scan_incl(rows, lane), 63);
     }
     return RowSpace{total, (total + n_parts - 1) / n_parts};
 }
@@ -227,11 +246,11 @@ __device__ __forceinline__ void locate(const int32_t* seq_lens, int B, int Hkv, 
         if (hit) {
             const int f = __builtin_ctzll(hit);
             b = c0 + f;
-            L = __shfl(Lb, f, 64);
-            base = run + __shfl(incl, f, 64) - (int64_t)Hkv * L;
+            L = __builtin_amdgcn_readlane(Lb, f);
+            base = run + readlane64(incl, f) - (int64_t)Hkv * L;
             return;
         }
-        run += __shfl(incl, 63, 64);
+        run += readlane64(incl, 63);
     }
     b = B;   // not reached for x < total
     base = run;
@@ -252,15 +271,15 @@ __device__ __forceinline__ bool first_piece(const int32_t* seq_lens, int B, int 
     if (B <= 64) {
         const int Lb = lane < B ? ctx_len(seq_lens, lane, S_max, cv) : 0;
         const int64_t incl = wave_scan_incl((int64_t)Hkv * Lb, lane);
-        total = __shfl(incl, 63, 64);
+        total = readlane64(incl, 63);
         R = grp * ((total + n_parts - 1) / n_parts);
         gs = (int64_t)w * R;
         if (gs >= total) return false;
         const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < B && gs < incl);
         const int f = __builtin_ctzll(hit);
         b = f;
-        L = __shfl(Lb, f, 64);
-        base = __shfl(incl, f, 64) - (int64_t)Hkv * L;
+        L = __builtin_amdgcn_readlane(Lb, f);
+        base = readlane64(incl, f) - (int64_t)Hkv * L;
         return true;
     }
     const RowSpace rs = row_space(seq_lens, B, Hkv, S_max, n_parts, lane, cv);
@@ -759,19 +778,17 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     const int b = idx / Hq, h = idx - b * Hq;
     const int g = Hq / Hkv, kv = h / g, hl = h - kv * g;
     // one pass over seq_lens gives both the row space total and the global
-    // row of (b, kv 0, row 0) (the prefix over the batches before b)
+    // row of (b, kv 0, row 0) (the prefix over the batches before b): one
+    // scan per 64 batches, read at lane 63 and at the lane before b
     int64_t total = 0, base = 0;
     for (int c0 = 0; c0 < B; c0 += 64) {
         const int bb = c0 + lane;
-        int64_t rows = bb < B ? (int64_t)Hkv * ctx_len(seq_lens, bb, S_max, cv) : 0;
-        int64_t before = bb < b ? rows : 0;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            rows += __shfl_xor(rows, o, 64);
-            before += __shfl_xor(before, o, 64);
-        }
-        total += rows;
-        base += before;
+        const int64_t rows = bb < B ? (int64_t)Hkv * ctx_len(seq_lens, bb, S_max, cv) : 0;
+        const int64_t incl = wave_scan_incl(rows, lane);
+        const int64_t chunk = readlane64(incl, 63);
+        total += chunk;
+        if (b >= c0 + 64) base += chunk;
+        else if (b > c0) base += readlane64(incl, b - c0 - 1);
     }
     const int64_t R = kWaves * ((total + n_parts - 1) / n_parts);
     const int L = ctx_len(seq_lens, b, S_max, cv);
@@ -801,9 +818,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
             m = part_ml[i2 * 2];
             l = part_ml[i2 * 2 + 1];
         }
-        float M = m;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, wave_shfl_xor(M, o));
+        const float M = wave_max(m);
         // finite: each range group's kWaves states hold a row, and chunks of
         // 64 states start at such groups
         const float M_new = fmaxf(M_run, M);
@@ -812,10 +827,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 #pragma unroll
         for (int e = 0; e < PER; ++e) acc[e] *= rescale;
         const float wl = lane < cn ? fast_exp2(m - M_new) : 0.f;
-        float dsum = wl * l;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) dsum += wave_shfl_xor(dsum, o);
-        den += dsum;
+        den += wave_sum(wl * l);
 #pragma unroll
         for (int jj = 0; jj < kFirst; ++jj) {
             const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), jj));

@@ -136,9 +136,29 @@ __device__ __forceinline__ u32x4 column_of(const u32x4 (&rows)[8], int t) {
     return r;
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
-    return __shfl_xor(v, mask, 64);
+// max and sum over the 64 lanes (every lane active), wave-uniform result:
+// DPP swaps within quads, half rows and rows reduce each 16-lane row, and
+// the four row results are combined from lanes 0, 16, 32, 48.
+template <int Ctrl>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), Ctrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float rowlane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));    // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_f<0x4E>(x));    // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_f<0x141>(x));   // row_half_mirror
+    x = fmaxf(x, dpp_f<0x140>(x));   // row_mirror
+    return fmaxf(fmaxf(rowlane_f(x, 0), rowlane_f(x, 16)), fmaxf(rowlane_f(x, 32), rowlane_f(x, 48)));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    x += dpp_f<0x141>(x);
+    x += dpp_f<0x140>(x);
+    return (rowlane_f(x, 0) + rowlane_f(x, 16)) + (rowlane_f(x, 32) + rowlane_f(x, 48));
 }
 
 // Both halves of the wave's values of v, through the gfx950 lane-half swap

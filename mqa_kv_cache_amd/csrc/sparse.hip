@@ -285,8 +285,7 @@ __global__ __launch_bounds__(256) void indexer_weighted_kernel(
         // bin 0 of the first-digit histogram is implied by the row length, so
         // its slot carries the row's largest squared key norm (fp32 bits of a
         // non-negative value order like the value) for the exact re-scoring
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) kmax = fmaxf(kmax, wave_shfl_xor(kmax, o));
+        kmax = wave_max(kmax);
         if (lane == 0) atomicMax(&hist[(size_t)b * kHistBins], __float_as_uint(kmax));
     }
     __syncthreads();
