@@ -251,17 +251,25 @@ def window_rows(seq_len: int, S_max: int, window: int = 0, rolling: bool = False
     Linear cache: position p is row p (window 0 = no window).  Rolling
     buffer ([transformer架构] §2.5.2): position t lives in slot
     :func:`sink_slot`, so the buffer holds the sinks and the last
-    S_max - s positions, and the window is the buffer (window must be 0).
+    S_max - s positions (its ring).  Window 0 attends to all of them (the
+    buffer is the window); a window w of at most the ring's S_max - s slots
+    attends to the slots of the visible positions, all still in the buffer
+    (reading: §2.5.2 sizes the buffer to the window; a smaller window over
+    a larger buffer keeps the §2.5.1 band, whose slots may wrap around the
+    buffer's end).
     """
     L = int(seq_len)
     if rolling:
-        if window:
-            raise ValueError("a rolling buffer's window is its size")
         if not 0 <= sinks < S_max:
             raise ValueError("the sinks must leave a ring of at least one slot")
         ring = S_max - sinks
-        positions = np.concatenate([np.arange(min(sinks, L)),
-                                    np.arange(max(sinks, L - ring), L)]).astype(np.int64)
+        if not 0 <= window <= ring:
+            raise ValueError("a rolling buffer's window must fit its ring of S_max - sinks slots")
+        if window:
+            positions = visible_keys(L - 1, int(window), sinks)
+        else:
+            positions = np.concatenate([np.arange(min(sinks, L)),
+                                        np.arange(max(sinks, L - ring), L)]).astype(np.int64)
         return np.array([sink_slot(t, S_max, sinks) for t in positions], dtype=np.int64)
     return visible_keys(L - 1, int(window), sinks)
 

@@ -254,6 +254,16 @@ def test_rolling_buffer_equals_linear_cache_with_its_window():
     a = att.decode_window(q, roll_k, roll_v, lens, 0.25, p, rolling=True)
     lin = att.decode_window(q, kpos, vpos, lens, 0.25, p, window=S)
     assert np.allclose(a, lin, rtol=1e-13, atol=1e-14)
+    # a window shorter than the buffer: the band's slots wrap around the
+    # buffer's end for L = 53 (positions 44..52 of w = 9 sit in slots 12..15
+    # and 0..4), and the result is still the linear cache's window
+    for w in (1, 5, 9, S):
+        a = att.decode_window(q, roll_k, roll_v, lens, 0.25, p, window=w, rolling=True)
+        lin = att.decode_window(q, kpos, vpos, lens, 0.25, p, window=w)
+        assert np.allclose(a, lin, rtol=1e-13, atol=1e-14)
+    assert sorted(att.window_rows(53, S, 9, rolling=True)) == [0, 1, 2, 3, 4, 12, 13, 14, 15]
+    with pytest.raises(ValueError):
+        att.window_rows(53, S, S + 1, rolling=True)
     # the append step writes slot (L-1) mod S (rolling) or row L-1 (linear)
     kn, vn = _rand((B, Hkv, D), 66), _rand((B, Hkv, D), 67)
     kr, vr = att.append_rows_window(roll_k, roll_v, kn, vn, lens, p, rolling=True)
@@ -430,5 +440,12 @@ def test_sink_decode_equals_prefill_rows_and_rolling_sinks():
         dec_l = att.decode_window(q[:, :, t], kcb, v, np.array([t + 1]), 0.3, p, window=S_max - s,
                                   sinks=s)
         assert np.allclose(dec_r, dec_l, rtol=1e-12, atol=1e-13)
+        # windows shorter than the ring of 7 slots (wrapping around it as t grows)
+        for wr in (1, 4, 6):
+            dec_r = att.decode_window(q[:, :, t], rk, rv, np.array([t + 1]), 0.3, p, window=wr,
+                                      rolling=True, sinks=s)
+            dec_l = att.decode_window(q[:, :, t], kcb, v, np.array([t + 1]), 0.3, p, window=wr,
+                                      sinks=s)
+            assert np.allclose(dec_r, dec_l, rtol=1e-12, atol=1e-13)
     for j in range(s):   # the sink slots still hold positions 0..s-1
         assert np.array_equal(rk[:, :, j], kcb[:, :, j]) and np.array_equal(rv[:, :, j], v[:, :, j])
