@@ -8,10 +8,11 @@ the whole batch; inputs are resident in HBM before timing starts and two
 independent caches alternate so the 256 MB Infinity Cache cannot serve them.
 
 The same run also measures the other hot-path entry points (decode at 4K,
-with Dynamic NTK, with the cache write, over a window, a rolling buffer and
-StreamingLLM sinks; causal prefill at 8K on the matrix cores, also with its
-fp16-score option, a window and sinks; top-k sparse decode at 128K, the
-weighted indexer, QSA, dense MLA and rope_apply) and times the CPU fp64
+with Dynamic NTK, with the cache write, over a window, a rolling buffer
+(also with a shorter window) and StreamingLLM sinks; causal prefill at 8K
+on the matrix cores, also with its fp16-score option, a window and sinks;
+top-k sparse decode at 128K, the weighted indexer, QSA, dense MLA and
+rope_apply) and times the CPU fp64
 oracle on a bounded sample of the headline workload.  All data is synthetic
 and seeded.
 
@@ -201,17 +202,19 @@ def bench_decode_append(cfg, steps, warmup, nsets=2):
     return dict(ms=ms, kv_bytes=kv_bytes)
 
 
-def bench_decode_window(cfg, steps, warmup, window, rolling, nsets=4, sinks=0):
+def bench_decode_window(cfg, steps, warmup, window, rolling, nsets=4, sinks=0, buffer=0):
     """gqa_decode_window on the 32K workload's batch, q heads and lengths: a
     `window`-token sliding window over the linear cache, or a rolling buffer
-    of `window` slots (contexts longer than the buffer); with `sinks` > 0
-    (gqa_decode_sink_window) the first positions stay visible as well."""
+    of `window` slots (contexts longer than the buffer), or of `buffer` slots
+    with the `window`-token window (its slots wrap around the buffer's end
+    for some contexts); with `sinks` > 0 (gqa_decode_sink_window) the first
+    positions stay visible as well."""
     import torch
 
     import mqa_kv_cache_amd as m
     from workloads import device_randn_bf16
     B, Hq, Hkv, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.D
-    S = window if rolling else cfg.S_max
+    S = (buffer or window) if rolling else cfg.S_max
     lens_np = cfg.seq_lens()
     lens = torch.from_numpy(lens_np).cuda()
     sets = [(device_randn_bf16((B, Hq, D), cfg.seed * 100 + 10 * i + 1),
@@ -228,11 +231,13 @@ def bench_decode_window(cfg, steps, warmup, window, rolling, nsets=4, sinks=0):
 
     def step(i):
         q, k, v = sets[i % nsets]
-        m.gqa_decode_window(q, k, v, lens, cfg.scale, window=0 if rolling else window,
+        m.gqa_decode_window(q, k, v, lens, cfg.scale, window=window if not rolling or buffer else 0,
                             rolling=rolling, q_rope=rope, out=out, workspace=ws, sinks=sinks)
 
     ms = timed_loop(step, steps, warmup)
-    label = (f"sink{sinks}_" if sinks else "") + (f"rolling{window}" if rolling else f"window{window}")
+    label = (f"sink{sinks}_" if sinks else "") + (
+        f"rolling{buffer}_window{window}" if rolling and buffer else
+        f"rolling{window}" if rolling else f"window{window}")
     log(f"[bench] decode {label} (32K contexts): step {ms * 1e3:.1f} us, {kv_bytes / ms / 1e6:.0f} GB/s")
     del sets
     torch.cuda.empty_cache()
@@ -508,6 +513,7 @@ def main():
     if want("window"):
         res["dw"] = bench_decode_window(DECODE_32K_YARN, K, W, 4096, False)
         res["dr"] = bench_decode_window(DECODE_32K_YARN, K, W, 4096, True)
+        res["drw"] = bench_decode_window(DECODE_32K_YARN, K, W, 4096, True, buffer=8192)
     if want("sinks"):
         res["ds"] = bench_decode_window(DECODE_32K_YARN, K, W, 4096, False, sinks=4)
     if want("prefill"):
@@ -587,7 +593,7 @@ def main():
         line["decode_append_32k"] = {"GB/s": round(da["kv_bytes"] / da["ms"] / 1e6, 1),
                                      "pct_of_hbm_peak": round(100 * da["kv_bytes"] / da["ms"] / 1e6 / HBM_PEAK_GBS, 2),
                                      "ms_per_step": round(da["ms"], 5)}
-    for key in ("dw", "dr", "ds"):
+    for key in ("dw", "dr", "drw", "ds"):
         if key in res:
             r = res[key]
             line[f"decode_{r['label']}_32k"] = {

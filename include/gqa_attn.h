@@ -235,16 +235,19 @@ gqa_status gqa_decode_append(const void* q, const void* k_new, const void* v_new
  * keys i-w+1 .. i.  With a linear cache (rolling = 0, row = position,
  * seq_lens[b] in [1, S_max]) the new token (position L-1, L = seq_lens[b])
  * attends to rows max(0, L-window) .. L-1; window 0 means no window.
- * Rolling buffer ([transformer架构] §2.5.2, rolling = 1, window 0): position t
- * lives in slot t mod S_max, so the cache holds the last S_max positions and
- * the new token attends to every filled slot, min(L, S_max) of them; L may
- * exceed S_max.  q is rotated at its absolute position L-1 in both; keys are
- * cached after RoPE, so nothing is re-rotated.
+ * Rolling buffer ([transformer架构] §2.5.2, rolling = 1): position t lives in
+ * slot t mod S_max, so the cache holds the last S_max positions; L may exceed
+ * S_max.  With window 0 the new token attends to every filled slot,
+ * min(L, S_max) of them; with 0 < window <= S_max to the slots of positions
+ * max(0, L-window) .. L-1, which wrap around the buffer's end when
+ * (L-window) mod S_max > (L-1) mod S_max.  q is rotated at its absolute
+ * position L-1 in both caches; keys are cached after RoPE, so nothing is
+ * re-rotated.
  *
  *   k_new, v_new  NULL (no cache write) or, both, as in gqa_decode_append: the
  *                 new row goes to row L-1 (linear) or slot (L-1) mod S_max
  *                 (rolling) before the attention reads it
- *   window        >= 0; must be 0 when rolling = 1 (the buffer is the window)
+ *   window        >= 0; at most S_max when rolling = 1 (window 0: the buffer)
  *   rolling       0 or 1
  * Other arguments, limits and errors as gqa_decode / gqa_decode_append.
  */
@@ -263,12 +266,15 @@ gqa_status gqa_decode_window(const void* q, const void* k_new, const void* v_new
  * Linear cache (rolling = 0): the new token at position L-1 attends to rows
  * 0 .. min(sinks, lo)-1 and lo .. L-1, lo = max(0, L-window); window 0 means
  * no window (every row; sinks are then moot).  Rolling buffer (rolling = 1,
- * window 0, 0 <= sinks < S_max): slots 0 .. sinks-1 keep positions
- * 0 .. sinks-1 for good and position t >= sinks lives in slot
- * sinks + (t - sinks) mod (S_max - sinks); the new token attends to every
- * filled slot (min(L, S_max) of them) and the fused write (k_new, v_new)
- * goes to its position's slot.  sinks = 0 is exactly gqa_decode_window.
+ * 0 <= sinks < S_max): slots 0 .. sinks-1 keep positions 0 .. sinks-1 for
+ * good and position t >= sinks lives in slot sinks + (t - sinks) mod
+ * (S_max - sinks) (the ring); with window 0 the new token attends to every
+ * filled slot (min(L, S_max) of them), with 0 < window <= S_max - sinks to
+ * the sinks and the slots of positions max(0, L-window) .. L-1 (each once);
+ * the fused write (k_new, v_new) goes to its position's slot.  sinks = 0 is
+ * exactly gqa_decode_window.
  *   sinks  >= 0 (< S_max when rolling = 1)
+ *   window >= 0 (<= S_max - sinks when rolling = 1)
  * Other arguments, limits and errors as gqa_decode_window.
  */
 gqa_status gqa_decode_sink_window(const void* q, const void* k_new, const void* v_new,

@@ -325,12 +325,13 @@ def gqa_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale: float,
 def gqa_decode_window(q, k_cache, v_cache, seq_lens, scale: float, window: int = 0,
                       rolling: bool = False, k_new=None, v_new=None, q_rope=None, out=None,
                       workspace=None, stream=None, sinks: int = 0) -> torch.Tensor:
-    """gqa_decode over the last `window` positions of a linear cache, or over a
-    rolling buffer (rolling=True, window 0: position t in slot t mod S_max),
-    optionally writing the new token's k_new/v_new [B,Hkv,D] first.  sinks > 0
-    (gqa_decode_sink_window) also keeps the first `sinks` positions visible
-    (linear cache) or in the buffer's first slots (rolling).  Returns out
-    [B,Hq,D] bf16."""
+    """gqa_decode over the last `window` positions of a linear cache, or of a
+    rolling buffer (rolling=True: position t in slot t mod S_max; window 0
+    attends to every filled slot, 0 < window <= S_max - sinks to the last
+    `window` positions, whose slots may wrap), optionally writing the new
+    token's k_new/v_new [B,Hkv,D] first.  sinks > 0 (gqa_decode_sink_window)
+    also keeps the first `sinks` positions visible (linear cache) or in the
+    buffer's first slots (rolling).  Returns out [B,Hq,D] bf16."""
     B, Hq, D = q.shape
     _, Hkv, S_max, _ = k_cache.shape
     _shape(k_cache, (B, Hkv, S_max, D), "k_cache")

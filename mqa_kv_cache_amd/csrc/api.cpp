@@ -245,7 +245,7 @@ gqa_status gqa_decode_sink_window(const void* q, const void* k_new, const void* 
     if (st != GQA_OK) return st;
     if (!std::isfinite(scale) || window < 0 || sinks < 0 || (rolling != 0 && rolling != 1))
         return GQA_ERR_INVALID_ARGUMENT;
-    if (rolling && (window != 0 || sinks >= S_max)) return GQA_ERR_INVALID_ARGUMENT;
+    if (rolling && (sinks >= S_max || window > S_max - sinks)) return GQA_ERR_INVALID_ARGUMENT;
     if ((k_new == nullptr) != (v_new == nullptr)) return GQA_ERR_INVALID_ARGUMENT;
     if (!q || !k_cache || !v_cache || !seq_lens || !workspace || !out)
         return GQA_ERR_INVALID_ARGUMENT;

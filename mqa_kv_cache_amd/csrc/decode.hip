@@ -155,14 +155,18 @@ struct RowSpace {
 // "Slide Window Attention (SWA)" 修复方案 1: the first s tokens stay
 // visible beside the window).  Linear cache: positions max(0, L-window) ..
 // L-1 are rows of the same index (window 0: all L), preceded by the sink
-// rows 0 .. s-1 that lie below them; rolling buffer: every filled slot,
-// min(L, S_max) of them from row 0, where the first s slots keep positions
-// 0 .. s-1 and later positions cycle through the other S_max - s slots.  The
-// query's position is L-1 in all cases (keys are cached after RoPE).
+// rows 0 .. s-1 that lie below them.  Rolling buffer: the first s slots keep
+// positions 0 .. s-1 and later positions cycle through the other S_max - s
+// slots (the ring); window 0 attends to every filled slot, min(L, S_max) of
+// them from row 0, and a window w <= S_max - s to the sinks and the slots of
+// positions L-w .. L-1, which may wrap around the buffer's end: then the
+// slots from row 0 up to the new token's make the first segment and the
+// band runs from the slot of position L-w to the last slot.  The query's
+// position is L-1 in all cases (keys are cached after RoPE).
 // Attended row r of a context is cache row r (r < ns) or lo + r - ns.
 struct CacheView {
     int window;    // 0 = no window
-    int rolling;   // 1 = rolling buffer of S_max slots (window 0)
+    int rolling;   // 1 = rolling buffer of S_max slots (window 0 or <= its ring)
     int sinks;     // sink tokens kept beside the window / in the buffer's first slots
 };
 struct CtxGeom {
@@ -176,12 +180,15 @@ __device__ __forceinline__ CtxGeom ctx_geom(const int32_t* seq_lens, int b, int 
                                            const CacheView& cv) {
     const int raw = max(seq_lens[b], 1);
     if (cv.rolling) {
-        const int n = min(raw, S_max);
+        const int s = cv.sinks;
+        const unsigned ring = (unsigned)(S_max - s);
         const int t = raw - 1;
-        const int slot = t < cv.sinks ? t
-                                      : cv.sinks + (int)((unsigned)(t - cv.sinks) %
-                                                         (unsigned)(S_max - cv.sinks));
-        return CtxGeom{0, n, 0, t, slot};
+        const int slot = t < s ? t : s + (int)((unsigned)(t - s) % ring);
+        // every filled slot: no window, or a window reaching down to the
+        // sinks (then raw <= window + s <= S_max and slot p holds position p)
+        if (cv.window == 0 || raw - cv.window <= s) return CtxGeom{0, min(raw, S_max), 0, t, slot};
+        const int lo = s + (int)((unsigned)(raw - cv.window - s) % ring);   // slot of position L-w
+        return CtxGeom{lo, s + cv.window, lo <= slot ? s : slot + 1, t, slot};
     }
     const int L = min(raw, S_max);
     const int lo = cv.window > 0 ? max(0, L - cv.window) : 0;
@@ -630,12 +637,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_split_kernel(
             ta = tb;
         }
 
-        // the new token's row, as a row of this context's attended range (it
-        // is always in the band segment), and whether its tile is this wave's
-        const int r_new = geo.newrow - geo.lo + geo.ns;
+        // the new token's row, as a row of this context's attended range (in
+        // the first segment only when a rolling window wraps), and whether its
+        // tile is this wave's: the piece's tiles are counted from r0 in the
+        // first segment, then from sb0 in the band
+        const bool new_a = geo.newrow < geo.ns;
+        const int r_new = new_a ? geo.newrow : geo.newrow - geo.lo + geo.ns;
         const bool ends = APPEND && r0 <= r_new && r_new < r1;   // this piece holds it
-        const bool owns = ends && ((tau + nta + ((r_new - sb0) >> 5)) & (kWaves - 1)) == j;
-        const int rr_new = (r_new - sb0) & 31;                    // its row in its tile
+        const int t_new = new_a ? (r_new - r0) >> 5 : nta + ((r_new - sb0) >> 5);
+        const bool owns = ends && ((tau + t_new) & (kWaves - 1)) == j;
+        const int rr_new = (r_new - (new_a ? r0 : sb0)) & 31;     // its row in its tile
 
         u32x4 qhi[NB][KU], qlo[NB][KU];
         if (in_a || in_b) {

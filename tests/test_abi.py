@@ -137,12 +137,15 @@ def test_decode_window_validation(m):
                                      None, P, P, wsn, None)
     assert win(window=-1) == m.ERR_INVALID_ARGUMENT
     assert win(rolling=2) == m.ERR_INVALID_ARGUMENT
-    assert win(rolling=1, window=8) == m.ERR_INVALID_ARGUMENT    # the buffer is the window
+    assert win(rolling=1, window=65) == m.ERR_INVALID_ARGUMENT   # a window past the buffer
     assert win(kn=P) == m.ERR_INVALID_ARGUMENT                   # k_new without v_new
     assert win(kn=P, vn=MIS) == m.ERR_INVALID_ARGUMENT
     need = m.gqa_decode_workspace_size(2, 16, 2, 128, 64)
     assert win(window=5, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
     assert win(rolling=1, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+    # a window up to the buffer's size passes the argument checks
+    assert win(rolling=1, window=8, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+    assert win(rolling=1, window=64, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
 
 
 def test_prefill_validation(m):
@@ -200,10 +203,12 @@ def test_sink_window_validation(m):
     assert dec(sinks=-1) == m.ERR_INVALID_ARGUMENT
     assert dec(window=-1) == m.ERR_INVALID_ARGUMENT
     assert dec(rolling=1, window=0, sinks=64) == m.ERR_INVALID_ARGUMENT   # no ring slot left
-    assert dec(rolling=1, window=8) == m.ERR_INVALID_ARGUMENT
+    assert dec(rolling=1, window=61) == m.ERR_INVALID_ARGUMENT   # past the ring of 64 - 4 slots
     need = m.gqa_decode_workspace_size(2, 16, 2, 128, 64)
     assert dec(wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
     assert dec(rolling=1, window=0, sinks=63, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+    assert dec(rolling=1, window=60, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+    assert dec(rolling=1, window=1, sinks=63, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
     for fn in (lib.gqa_prefill_sink_window, lib.gqa_prefill_fp16):
         assert fn(P, P, P, 1, 64, 8, 2, 128, -1, 16, 0.1, None, P, P, 1 << 30,
                   None) == m.ERR_INVALID_ARGUMENT

@@ -341,6 +341,12 @@ WINDOW_CASES = [
     (4, 16, 2, 128, 64, [5, 64, 65, 300], 0, 1, False),    # rolling: short, exactly full, wrapped
     (3, 16, 2, 128, 96, [96, 150, 1000], 0, 1, True),      # rolling with the write (slot (L-1) mod S)
     (2, 12, 4, 64, 50, [31, 77], 0, 1, True),              # rolling, g=3, head dim 64
+    # rolling with a window shorter than the buffer: all filled slots (5),
+    # a band inside the buffer (30) and bands wrapping around its end (65, 70)
+    (4, 16, 2, 128, 64, [5, 30, 65, 70], 24, 1, False),
+    # ... with the write: the new token's slot is in the wrapped part (130, 100)
+    (4, 16, 2, 128, 96, [96, 130, 1010, 100], 40, 1, True),
+    (2, 12, 4, 64, 50, [31, 102], 10, 1, True),
 ]
 
 
@@ -382,17 +388,19 @@ def test_decode_window_parity(m, case):
     assert np.array_equal(kg, k0) and np.array_equal(vg, v0), "rows other than the new one changed"
 
 
-@pytest.mark.parametrize("mode", ["window4096", "rolling4096"])
+@pytest.mark.parametrize("mode", ["window4096", "rolling4096", "rolling8192w4096"])
 def test_decode_window_full_size_32k(m, mode):
     """The 32K workload (ragged 16K-32K contexts, YaRN) with a 4096-token
-    sliding window over its linear cache, and as a 4096-slot rolling buffer
-    (contexts far longer than the buffer), every head against the oracle."""
+    sliding window over its linear cache, as a 4096-slot rolling buffer
+    (contexts far longer than the buffer), and as an 8192-slot rolling buffer
+    with a 4096-token window (wrapping around the buffer's end for about half
+    of the contexts), every head against the oracle."""
     import torch
     cfg = DECODE_32K_YARN
     B, Hq, Hkv, D = cfg.B, cfg.Hq, cfg.Hkv, cfg.D
     lens = cfg.seq_lens()
-    S = cfg.S_max if mode == "window4096" else 4096
-    window, rolling = (4096, False) if mode == "window4096" else (0, True)
+    S, window, rolling = {"window4096": (cfg.S_max, 4096, False), "rolling4096": (4096, 0, True),
+                          "rolling8192w4096": (8192, 4096, True)}[mode]
     print(f"[case] window full size {mode}", flush=True)
     q = device_randn_bf16((B, Hq, D), cfg.seed * 10 + 1)
     k = device_randn_bf16((B, Hkv, S, D), cfg.seed * 10 + 2)

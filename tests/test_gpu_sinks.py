@@ -44,10 +44,19 @@ DECODE_CASES = [
     (4, 16, 2, 128, 64, [5, 64, 65, 300], 4, 0, 1, False),   # rolling: short, full, wrapped
     (3, 16, 2, 128, 96, [96, 150, 1000], 4, 0, 1, True),     # rolling write skips the sink slots
     (2, 12, 4, 64, 50, [31, 77], 10, 0, 1, True),            # rolling, g=3, head dim 64
+    # rolling with a window shorter than the ring: every filled slot (5), a
+    # band inside the ring (40, 300), a band wrapping around the buffer's end
+    # (65: the first segment is the sinks and slot 4)
+    (4, 16, 2, 128, 64, [5, 40, 65, 300], 4, 24, 1, False),
+    (3, 16, 2, 128, 96, [96, 130, 1000], 4, 40, 1, True),    # the write lands in the wrapped part (130)
+    (2, 12, 4, 64, 50, [31, 102], 10, 20, 1, True),
     # ~128K attended rows: a workgroup's four waves share ranges of 16+ tiles,
     # and context starts (two tiles of sinks, then the band) fall inside them
     (4, 8, 4, 128, 10000, [10000, 9000, 8300, 9999], 40, 8192, 0, True),
     (4, 8, 4, 128, 8192, [20000, 9000, 8192, 12345], 40, 0, 1, True),
+    # the same with a 4096-token window: 20000 and 9000 wrap (first segments
+    # of 3696 and 848 rows), 8192 and 12345 do not
+    (4, 8, 4, 128, 8192, [20000, 9000, 8192, 12345], 40, 4096, 1, True),
     # more than 64 sequences (the chunked prefix passes), sinks, window and the write
     (80, 8, 2, 128, 300, [int(x) for x in np.random.default_rng(17).integers(1, 301, 80)], 4, 100, 0, True),
 ]
