@@ -6,9 +6,10 @@
 // (token, frequency) once in LDS (fp64 angle, reduced, fp32 sincos, times
 // the YaRN amplitude), so the transcendental work is shared by all heads of
 // a token and hidden behind the loads.  The kernel is HBM-bound: each
-// element is read once and written once, so both go with the nontemporal
-// policy (2% faster than the default on the 8K prefill's Q rows; 16 chunks
-// per thread instead of 8 ran 25% slower).
+// element is read once and written once.  The stores take the nontemporal
+// policy and the loads the default one: on the 8K prefill's Q rows (67 MB
+// each way) that ran in 21.7 us against 27.9 us with both nontemporal and
+// 28.5 us with both default (16 chunks per thread instead of 8: slower).
 #include "device_common.h"
 
 namespace gqa {
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_apply_kernel(
             cc[k] = rem - h * chunks;
             const bool ok = it < total && tok0 + tl[k] < n_tok;
             off[k] = ok ? (tok0 + tl[k]) * stride_tok + (int64_t)h * stride_head + 8 * cc[k] : -1;
-            if (ok) v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in + off[k]));
+            if (ok) v[k] = *reinterpret_cast<const u32x4*>(in + off[k]);
         }
         if (base == 0) {
             for (int e = tid; e < tok_per_block * half; e += kRopeThreads) {
