@@ -84,14 +84,23 @@ class Guarded:
         assert torch.equal(self.raw[hi:], self.expect[hi:]), f"{what}: canary after the buffer changed"
 
 
+# The decode kernels' own precision: K and V are exact bf16 inputs, q and P
+# enter the products as hi + lo bf16 (~2^-17), sums are fp32, so the error is
+# the final bf16 rounding of the output (at most 2^-8 of it) plus fp32
+# rounding well under 5e-5.  Checked beside the contract tolerance so that an
+# error far below 2e-3 + 1e-2 |ref| (outputs of ~0.006 at 32K rows) still shows.
+KERNEL_ATOL, KERNEL_RTOL = 5e-5, 2.0 ** -7
+
+
 def check_every_head(got, q, k, v, lens, scale, rope, Hq, Hkv, what, qmul=1.0):
     """Every (b, h) output of a full-size decode against the oracle: per
-    (batch, kv head) the group's g heads at once over that context's rows."""
+    (batch, kv head) the group's g heads at once over that context's rows,
+    to the contract tolerance and to the kernels' own precision bound."""
     g = Hq // Hkv
     from oracle import attention as oatt
     from workloads import bf16_tensor_to_f64
     qf = bf16_tensor_to_f64(q) * qmul
-    worst = 0.0
+    worst = tight = 0.0
     for b in range(len(lens)):
         L = int(lens[b])
         for kv in range(Hkv):
@@ -100,4 +109,8 @@ def check_every_head(got, q, k, v, lens, scale, rope, Hq, Hkv, what, qmul=1.0):
             ref = oatt.decode_group(qf[b, kv * g:(kv + 1) * g], kb, vb, L, scale, rope)
             worst = max(worst, assert_close(got[b, kv * g:(kv + 1) * g], ref,
                                             f"{what} (b={b}, kv={kv}, L={L})"))
-    print(f"[parity] {what}: every head, worst err/bound {worst:.3f}", flush=True)
+            tight = max(tight, assert_close(got[b, kv * g:(kv + 1) * g], ref,
+                                            f"{what} (b={b}, kv={kv}, L={L}) kernel precision",
+                                            atol=KERNEL_ATOL, rtol=KERNEL_RTOL))
+    print(f"[parity] {what}: every head, worst err/bound {worst:.3f} (kernel precision bound "
+          f"{tight:.3f})", flush=True)

@@ -12,6 +12,18 @@ from workloads import (DECODE_4K, DECODE_32K_YARN, ROPE_PLAIN, ROPE_YARN, bf16_b
 pytestmark = pytest.mark.gpu
 
 
+def assert_split_agree(a, b, what):
+    """Two work splits of one decode agree to one bf16 rounding step of the
+    larger output (2^-7 of its magnitude) plus 2e-5 for the fp32 summation
+    order."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    bound = 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 2e-5
+    err = np.abs(a - b)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), (what, worst, float(err[worst]), float(bound[worst]))
+
+
 @pytest.fixture(scope="module")
 def m():
     import torch
@@ -74,8 +86,11 @@ def test_decode_yarn_and_split_independence(m):
         got, ref = _run_case(m, 4, 16, 2, 128, 1000, lens, rope, seed=12, n_parts=parts)
         assert_close(got, ref, f"yarn parts={parts}")
         outs.append(got)
-    for o in outs[1:]:
-        assert np.max(np.abs(o - outs[0])) <= 4e-3
+    # every split computes the same fp32 sums in another order (differences
+    # ~1e-6) and rounds them to bf16 once, so two splits differ by at most one
+    # bf16 step of the larger value (2^-7 of it) plus that order difference
+    for parts, o in zip((1, 2, 7, 64, 1000, 5000, 20000), outs[1:]):
+        assert_split_agree(o, outs[0], f"parts={parts}")
 
 
 def test_decode_calls_on_two_streams_run_concurrently_and_agree(m):
@@ -131,7 +146,7 @@ def test_decode_no_rope_and_gqa_equals_repeated_mha(m):
     assert torch.equal(o1, o2)
     o3 = m.gqa_decode(q, kr, vr, sl, 0.1)
     torch.cuda.synchronize()
-    assert np.max(np.abs(from_dev(o3) - from_dev(o1))) <= 4e-3
+    assert_split_agree(from_dev(o3), from_dev(o1), "default split vs one range")
     ref = oatt.decode(bf16_bits_to_f64(d["q"]), bf16_bits_to_f64(d["k"]), bf16_bits_to_f64(d["v"]),
                       d["seq_lens"], 0.1, None)
     assert_close(from_dev(o1), ref, "no-rope")
