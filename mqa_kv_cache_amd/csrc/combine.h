@@ -22,30 +22,48 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(
     const int idx = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     if (idx >= BH) return;
     const int b = idx / H;
-    const int L = min(min(max(seq_lens[b], 1), S_max), cap);
-    const int ns = (L + rows_per_split - 1) / rows_per_split;
     const float* ml = part_ml + (size_t)idx * n_split_max * 2;
     const float* po = part_o + (size_t)idx * n_split_max * D + lane * PER;
+    // The states of the first 64 splits are requested with seq_lens, in one
+    // round trip: their slots do not depend on the split count, which only
+    // says how many of them hold this call's values.  Slots past it hold
+    // stale bytes (possibly not finite): they are masked by selects and
+    // branches, never multiplied by a zero weight.  Lane s holds the (m, l)
+    // of split s; the o rows of the first 16 splits are loaded up front
+    // (they do not depend on the weights), further splits four at a time.
+    constexpr int kFirst = 16;
+    f32x4 v0[kFirst][PER / 4];
+#pragma unroll
+    for (int jj = 0; jj < kFirst; ++jj) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(po + (size_t)min(jj, n_split_max - 1) * D);
+#pragma unroll
+        for (int e = 0; e < PER / 4; ++e) v0[jj][e] = src[e];
+    }
+    float m0 = -INFINITY, l0 = 0.f;
+    if (lane < n_split_max) {
+        m0 = ml[2 * lane];
+        l0 = ml[2 * lane + 1];
+    }
+    const int L = min(min(max(seq_lens[b], 1), S_max), cap);
+    const int ns = (L + rows_per_split - 1) / rows_per_split;
     float acc[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] = 0.f;
     float den = 0.f, M_run = -INFINITY;
-    // lane s reads the (m, l) of split s (64 splits at a time); the o rows of
-    // the first 16 splits are requested in the same round trip (they do not
-    // depend on the weights), further splits four at a time
-    constexpr int kFirst = 16;
     for (int s0 = 0; s0 < ns; s0 += 64) {
         const int cn = min(64, ns - s0);
-        f32x4 v0[kFirst][PER / 4];
-#pragma unroll
-        for (int jj = 0; jj < kFirst; ++jj) {
-            const int sj = s0 + min(jj, cn - 1);   // past the end: a valid split, weight 0
-            const f32x4* src = reinterpret_cast<const f32x4*>(po + (size_t)sj * D);
-#pragma unroll
-            for (int e = 0; e < PER / 4; ++e) v0[jj][e] = src[e];
+        float m, l;
+        if (s0 == 0) {
+            m = m0;
+            l = l0;
+        } else {
+            m = lane < cn ? ml[2 * (s0 + lane)] : -INFINITY;
+            l = lane < cn ? ml[2 * (s0 + lane) + 1] : 0.f;
         }
-        const float m = lane < cn ? ml[2 * (s0 + lane)] : -INFINITY;
-        const float l = lane < cn ? ml[2 * (s0 + lane) + 1] : 0.f;
+        if (lane >= cn) {
+            m = -INFINITY;
+            l = 0.f;
+        }
         const float M = wave_max(m);
         const float M_new = fmaxf(M_run, M);   // finite: every split holds a row
         const float rescale = fast_exp2(M_run - M_new);
@@ -54,17 +72,22 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(
         for (int j = 0; j < PER; ++j) acc[j] *= rescale;
         const float wl = lane < cn ? fast_exp2(m - M_new) : 0.f;
         den += wave_sum(wl * l);
+        int j0 = 0;
+        if (s0 == 0) {
 #pragma unroll
-        for (int jj = 0; jj < kFirst; ++jj) {
-            const float wgt = jj < cn ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                            __builtin_bit_cast(int, wl), jj))
-                                      : 0.f;
+            for (int jj = 0; jj < kFirst; ++jj) {
+                if (jj < cn) {                          // wave-uniform
+                    const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                                __builtin_bit_cast(int, wl), jj));
 #pragma unroll
-            for (int e = 0; e < PER / 4; ++e)
+                    for (int e = 0; e < PER / 4; ++e)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) acc[4 * e + c] += wgt * v0[jj][e][c];
+                        for (int c = 0; c < 4; ++c) acc[4 * e + c] += wgt * v0[jj][e][c];
+                }
+            }
+            j0 = kFirst;
         }
-        for (int j0 = kFirst; j0 < cn; j0 += 4) {
+        for (; j0 < cn; j0 += 4) {
             f32x4 v[4][PER / 4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
