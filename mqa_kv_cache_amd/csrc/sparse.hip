@@ -2103,16 +2103,25 @@ __global__ __launch_bounds__(256) void qsa_combine_kernel(const float* __restric
     const int idx = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     if (idx >= BH) return;
     const int b = idx / Hq;
-    const int L = min(max(seq_lens[b], 1), S_max);
-    const int nc = (qsa_n_tokens(L) + kGChunk - 1) / kGChunk;   // 1 .. kGChunks
     const float* ml = part_ml + (size_t)idx * kGChunks * 2;
     const float* po = part_o + (size_t)idx * kGChunks * kGD + 2 * lane;
+    // every chunk's state is requested together with seq_lens (one round
+    // trip); the chunks past this row's count hold stale bytes, masked below
+    // by selects and branches, never multiplied by a zero weight
     float2 p[kGChunks];
 #pragma unroll
-    for (int c = 0; c < kGChunks; ++c)
-        p[c] = *reinterpret_cast<const float2*>(po + (size_t)min(c, nc - 1) * kGD);
-    const float mc = lane < nc ? ml[2 * lane] : -INFINITY;
-    const float lc = lane < nc ? ml[2 * lane + 1] : 0.f;
+    for (int c = 0; c < kGChunks; ++c) p[c] = *reinterpret_cast<const float2*>(po + (size_t)c * kGD);
+    float mc = -INFINITY, lc = 0.f;
+    if (lane < kGChunks) {
+        mc = ml[2 * lane];
+        lc = ml[2 * lane + 1];
+    }
+    const int L = min(max(seq_lens[b], 1), S_max);
+    const int nc = (qsa_n_tokens(L) + kGChunk - 1) / kGChunk;   // 1 .. kGChunks
+    if (lane >= nc) {
+        mc = -INFINITY;
+        lc = 0.f;
+    }
     float M = mc;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
@@ -2123,9 +2132,11 @@ __global__ __launch_bounds__(256) void qsa_combine_kernel(const float* __restric
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int c = 0; c < kGChunks; ++c) {
-        const float wc = __shfl(w, c, 64);
-        a0 += wc * p[c].x;
-        a1 += wc * p[c].y;
+        if (c < nc) {                              // wave-uniform
+            const float wc = __shfl(w, c, 64);
+            a0 += wc * p[c].x;
+            a1 += wc * p[c].y;
+        }
     }
     const float inv = 1.0f / den;
     *reinterpret_cast<uint32_t*>(out + (size_t)idx * kGD + 2 * lane) = pack_bf16x2(a0 * inv, a1 * inv);
