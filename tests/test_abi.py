@@ -97,6 +97,12 @@ def test_decode_validation(m):
         == m.ERR_UNSUPPORTED
     assert _decode(m, wsn=0, rope=_rope(m, scaling=9, base=1e4)) == m.ERR_INVALID_ARGUMENT
     assert m.gqa_decode_workspace_size(2, 15, 2, 128, 64) == 0
+    # a context's K or V rows must fit 32-bit byte offsets: 2^23 rows of 256 B
+    # are 2^31 bytes (rejected); one row fewer is the largest cache accepted
+    assert _decode(m, S=1 << 23, wsn=0) == m.ERR_UNSUPPORTED
+    assert _decode(m, S=(1 << 23) - 1, wsn=0) == m.ERR_WORKSPACE_TOO_SMALL
+    assert _decode(m, D=64, S=1 << 24, wsn=0) == m.ERR_UNSUPPORTED
+    assert _decode(m, D=64, S=(1 << 24) - 1, wsn=0) == m.ERR_WORKSPACE_TOO_SMALL
     lib = m.lib()
     assert lib.gqa_decode_parts(P, P, P, P, 2, 16, 2, 128, 64, 0.1, None, P, P, 1 << 30, -3,
                                 None) == m.ERR_INVALID_ARGUMENT   # negative part count
@@ -238,6 +244,9 @@ def test_sparse_validation(m):
     need = m.topk_sparse_decode_workspace_size(2, 128, 4096, 2048)
     assert need > 0
     assert call(wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
+    # a row's latent bytes (1152 per row) must fit 32-bit byte offsets
+    assert call(S=1864136) == m.ERR_UNSUPPORTED            # 2,147,484,672 bytes
+    assert call(S=1864135) == m.ERR_WORKSPACE_TOO_SMALL    # 2,147,483,520 bytes: the largest
 
 
 def test_sparse_weighted_validation(m):

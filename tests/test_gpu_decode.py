@@ -223,6 +223,26 @@ def test_decode_full_size_peaked(m, k2):
     _full_size(m, DECODE_32K_YARN, k2)
 
 
+def test_decode_largest_cache(m):
+    """The largest cache the ABI accepts for D = 128: 2^23 - 1 rows per kv
+    head (2^31 - 256 bytes of K and of V), every row attended (the last tile
+    holds 31 rows), q rotated at position 2^23 - 2.  Byte offsets of the last
+    tiles and of the prefetch past them sit at the 32-bit limit; every head
+    against the oracle."""
+    import torch
+    B, Hq, Hkv, D, S = 1, 8, 1, 128, (1 << 23) - 1
+    print(f"[case] largest cache B={B} Hq={Hq} Hkv={Hkv} D={D} S_max={S}", flush=True)
+    q = device_randn_bf16((B, Hq, D), 71)
+    k = device_randn_bf16((B, Hkv, S, D), 72)
+    v = device_randn_bf16((B, Hkv, S, D), 73)
+    lens = np.array([S], dtype=np.int32)
+    rope = rope_settings(ROPE_PLAIN, base=500000.0)
+    out = m.gqa_decode(q, k, v, torch.from_numpy(lens).cuda(), 1.0 / math.sqrt(D), q_rope=rope)
+    torch.cuda.synchronize()
+    check_every_head(from_dev(out), q, k, v, lens, 1.0 / math.sqrt(D), rope, Hq, Hkv,
+                     "largest cache")
+
+
 # ---------------------------------------------------------------------------
 # gqa_decode_append: the decode step with its cache write fused
 # ---------------------------------------------------------------------------

@@ -111,3 +111,21 @@ def test_mla_full_size_128k(m):
         assert_close(got[b], ref, f"full-size every head (b={b})")
         rel = np.linalg.norm(got[b] - ref) / np.linalg.norm(ref)
         assert rel < 1e-2, (b, rel)
+
+
+def test_mla_largest_cache(m):
+    """The largest latent cache the ABI accepts: 1,864,135 rows of 1152 bytes
+    (2^31 - 128 bytes), every row attended (the last 32-row step holds 7
+    rows); the copies of the last rows sit at the 32-bit offset limit.  Every
+    head against the oracle."""
+    import torch
+    B, H, S = 1, 16, 1864135
+    print(f"[case] mla largest cache B={B} H={H} S={S}", flush=True)
+    q = device_randn_bf16((B, H, 576), 91)
+    lat = device_randn_bf16((B, S, 576), 92)
+    out = m.mla_decode(q, lat, torch.tensor([S], dtype=torch.int32).cuda(), SCALE)
+    torch.cuda.synchronize()
+    ref = osp.sparse_attention_heads(bf16_tensor_to_f64(q)[0], bf16_tensor_to_f64(lat[0]),
+                                     np.arange(S), SCALE, 512)
+    assert_close(from_dev(out)[0], ref, "mla largest cache, every head")
+

@@ -162,3 +162,27 @@ def test_sparse_full_size_128k(m):
     out_g.check("out")
     idx_g.check("topk_idx")
     ws.check("workspace")
+
+
+def test_sparse_largest_cache(m):
+    """The largest latent cache the ABI accepts: 1,864,135 rows of 1152 bytes
+    (2^31 - 128 bytes), every row a candidate.  The gather's byte offsets of
+    the last rows sit at the 32-bit limit and the select runs over 456 key
+    chunks; index set bit-exact and every head against the oracle."""
+    import torch
+    B, H, S, k = 1, 16, 1864135, 2048
+    print(f"[case] sparse largest cache B={B} H={H} S={S} k={k}", flush=True)
+    q = device_randn_bf16((B, H, 576), 81)
+    lat = device_randn_bf16((B, S, 576), 82)
+    qi = device_randn_bf16((B, 128), 83)
+    ki = device_randn_bf16((B, S, 128), 84)
+    lens = torch.tensor([S], dtype=torch.int32).cuda()
+    idx, out = m.topk_sparse_decode(q, lat, qi, ki, lens, k, SCALE)
+    torch.cuda.synchronize()
+    gidx = idx.cpu().numpy()[0]
+    ridx = osp.topk_select(osp.indexer_scores(bf16_tensor_to_f64(qi)[0], bf16_tensor_to_f64(ki[0]), S), k)
+    assert np.array_equal(gidx, ridx), "index sets differ"
+    assert ridx.max() > S - 200000, "the selection reaches the last rows"
+    rows = bf16_tensor_to_f64(lat[0][torch.from_numpy(ridx.astype(np.int64)).cuda()])
+    ref = osp.sparse_attention_heads(bf16_tensor_to_f64(q)[0], rows, np.arange(k), SCALE, 512)
+    assert_close(from_dev(out)[0], ref, "largest cache, every head")
