@@ -170,6 +170,10 @@ def test_prefill_validation(m):
     assert call(rope=r, wsn=need - 1) == m.ERR_WORKSPACE_TOO_SMALL
     assert call(rope=r, ws=None, wsn=need) == m.ERR_INVALID_ARGUMENT
     assert m.gqa_prefill_workspace_size(1, 2, 16, 128, None) == need
+    # a head's rows must fit 32-bit byte offsets: 2^23 tokens of 256 B are
+    # rejected, one fewer is the longest prompt accepted
+    assert call(T=1 << 23) == m.ERR_UNSUPPORTED
+    assert call(T=(1 << 23) - 1) == m.ERR_WORKSPACE_TOO_SMALL
 
 
 def test_prefill_window_validation(m):

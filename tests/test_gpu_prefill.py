@@ -126,6 +126,35 @@ def _prefill_full(m, window, k2=0):
     assert_close(got[:, :, rows], ref[:, :, rows], f"prefill full size w={window} x{2 ** k2}")
 
 
+def test_prefill_window_largest_context(m):
+    """The longest prompt the ABI accepts for D = 128 (2^23 - 1 tokens: a kv
+    head's K rows are 2^31 - 256 bytes) through a 256-token window: the
+    first and last query tiles (the last holds 127 rows) and a tile at row
+    2^22 against the oracle.  The oracle rotates at positions 0 .. n-1 of
+    the slice it is given; with a window the outputs of a slice starting at
+    p0 depend only on position differences (the RoPE identity its CPU tests
+    pin), so a slice of the window's rows before the checked ones stands in
+    for the whole prompt."""
+    import torch
+    B, Hq, Hkv, D, T, w = 1, 2, 1, 128, (1 << 23) - 1, 256
+    rope = rope_settings(ROPE_NTK, base=1.0e6, factor=4.0)
+    scale = 1.0 / math.sqrt(D)
+    print(f"[case] prefill largest context T={T} window={w}", flush=True)
+    q = device_randn_bf16((B, Hq, T, D), 61)
+    k = device_randn_bf16((B, Hkv, T, D), 62)
+    v = device_randn_bf16((B, Hkv, T, D), 63)
+    out = m.gqa_prefill_causal(q, k, v, scale, rope=rope, window=w)
+    torch.cuda.synchronize()
+    for r0, r1 in ((0, 128), (1 << 22, (1 << 22) + 128), (T - 127, T)):
+        s0 = max(0, r0 - (w - 1))
+        sl = slice(s0, r1)
+        ref = oatt.prefill_causal(bf16_tensor_to_f64(q[:, :, sl]), bf16_tensor_to_f64(k[:, :, sl]),
+                                  bf16_tensor_to_f64(v[:, :, sl]), scale, rope,
+                                  rows=range(r0 - s0, r1 - s0), window=w)
+        got = from_dev(out[:, :, r0:r1])
+        assert_close(got, ref[:, :, r0 - s0:r1 - s0], f"largest context rows {r0}..{r1 - 1}")
+
+
 def _exp_shift(bits, e):
     """bf16 values times 2^e, exactly (the exponent field moved; zeros kept)."""
     out = bits.astype(np.int32)
