@@ -5,7 +5,7 @@ import math
 import numpy as np
 import pytest
 
-from helpers import assert_close, from_dev, to_dev
+from helpers import KERNEL_ATOL, KERNEL_RTOL, assert_close, from_dev, to_dev
 from oracle import sparse as osp
 from workloads import (SPARSE_128K, bf16_bits_to_f64, bf16_tensor_to_f64, device_randn_bf16,
                        sparse_inputs_host)
@@ -109,6 +109,8 @@ def test_mla_full_size_128k(m):
         latb = bf16_tensor_to_f64(lat[b, :lens_np[b]])
         ref = osp.sparse_attention_heads(qf[b], latb, np.arange(lens_np[b]), cfg.scale, cfg.Dv)
         assert_close(got[b], ref, f"full-size every head (b={b})")
+        assert_close(got[b], ref, f"full-size every head (b={b}) kernel precision",
+                     atol=KERNEL_ATOL, rtol=KERNEL_RTOL)
         rel = np.linalg.norm(got[b] - ref) / np.linalg.norm(ref)
         assert rel < 1e-2, (b, rel)
 
@@ -128,4 +130,6 @@ def test_mla_largest_cache(m):
     ref = osp.sparse_attention_heads(bf16_tensor_to_f64(q)[0], bf16_tensor_to_f64(lat[0]),
                                      np.arange(S), SCALE, 512)
     assert_close(from_dev(out)[0], ref, "mla largest cache, every head")
+    assert_close(from_dev(out)[0], ref, "mla largest cache, kernel precision", atol=KERNEL_ATOL,
+                 rtol=KERNEL_RTOL)
 

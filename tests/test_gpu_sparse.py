@@ -5,7 +5,7 @@ import math
 import numpy as np
 import pytest
 
-from helpers import Guarded, assert_close, from_dev, to_dev
+from helpers import KERNEL_ATOL, KERNEL_RTOL, Guarded, assert_close, from_dev, to_dev
 from oracle import sparse as osp
 from workloads import (SPARSE_128K, bf16_bits_to_f64, bf16_tensor_to_f64, device_randn_bf16,
                        f32_to_bf16_bits, sparse_inputs_host)
@@ -159,6 +159,8 @@ def test_sparse_full_size_128k(m):
         rows = bf16_tensor_to_f64(lat[b][torch.from_numpy(ridx.astype(np.int64)).cuda()])
         ref = osp.sparse_attention_heads(qf[b], rows, np.arange(k), cfg.scale, cfg.Dv)
         assert_close(got[b], ref, f"full-size every head (b={b})")
+        assert_close(got[b], ref, f"full-size every head (b={b}) kernel precision",
+                     atol=KERNEL_ATOL, rtol=KERNEL_RTOL)
     out_g.check("out")
     idx_g.check("topk_idx")
     ws.check("workspace")
@@ -186,3 +188,5 @@ def test_sparse_largest_cache(m):
     rows = bf16_tensor_to_f64(lat[0][torch.from_numpy(ridx.astype(np.int64)).cuda()])
     ref = osp.sparse_attention_heads(bf16_tensor_to_f64(q)[0], rows, np.arange(k), SCALE, 512)
     assert_close(from_dev(out)[0], ref, "largest cache, every head")
+    assert_close(from_dev(out)[0], ref, "largest cache, kernel precision", atol=KERNEL_ATOL,
+                 rtol=KERNEL_RTOL)
