@@ -10,7 +10,7 @@
 //    The pass also builds the first radix-select histogram (top 12 bits of
 //    the non-negative fp32 score) in LDS and flushes it with atomics.
 // 2. top-k selection by radix select over the fp32 score bits: the first
-//    12-bit digit comes from the indexer's histogram; per 4096-key chunk a
+//    12-bit digit comes from the indexer's histogram; per 2048-key chunk a
 //    workgroup writes the keys at or above the bin holding the k-th score
 //    (every selected key is one of them) in index order; one workgroup per
 //    batch row then finds the exact k-th key T from those entries (or by
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256) void indexer_weighted_kernel(
 
 // ---------------------------------------------------------------------------
 // 2. top-k selection (an exact radix select on 12 + 12 + 8 key bits):
-//    topk_compact_kernel  per (4096-key chunk, batch row): first digit B1
+//    topk_compact_kernel  per (2048-key chunk, batch row): first digit B1
 //                         from the histogram; the keys in bins >= B1 as
 //                         ordered (key, index) entries to the chunk's slice
 //    topk_finish_kernel   per batch row: exact k-th key T from the entries
@@ -306,7 +306,11 @@ __global__ __launch_bounds__(256) void indexer_weighted_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 1024;
 constexpr int kChunkThreads = 256;
-constexpr int kChunkKeys = 4096;          // keys per chunk workgroup
+// keys per chunk workgroup: 2048 gave the top-k call 69.8 us against 70.7
+// with 4096 and 72.4 with 8192 (more chunk workgroups fill more CUs); the
+// finish kernel gives each chunk a thread, so a row may span at most
+// kSelThreads chunks (2^21 keys), which the entry points' limits keep
+constexpr int kChunkKeys = 2048;
 
 struct SelInfo {
     uint32_t B1;       // first-digit bin of the k-th largest key
@@ -384,7 +388,7 @@ __device__ void first_digit(const uint32_t* hist_g, int b, int L, int k, uint32_
     find_crossing<NT>(h, kHistBins, (uint32_t)k, wsum, out);
 }
 
-// Per 4096-key chunk: the keys of the threshold bin and of the bins above it
+// Per 2048-key chunk: the keys of the threshold bin and of the bins above it
 // (every selected key is one of them), and with lower_bins = 1 those of the
 // bin below as well (where the re-scored band of the multi-head indexers can
 // reach), as (key, index) entries in index order, to the chunk's own slice (its index range of the entry arrays);
@@ -393,7 +397,7 @@ __device__ void first_digit(const uint32_t* hist_g, int b, int L, int k, uint32_
 // work so both latencies overlap; the order within a wave comes from
 // ballot/mbcnt.  With k = L every index is selected: the chunk writes its
 // indices straight to the output, and chunk 0 writes the -1 padding.
-constexpr int kKeysPerLane = kChunkKeys / kChunkThreads;     // 16
+constexpr int kKeysPerLane = kChunkKeys / kChunkThreads;     // 8
 
 __global__ __launch_bounds__(kChunkThreads) void topk_compact_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist_g,
@@ -2222,6 +2226,7 @@ hipError_t launch_qsa_sparse_decode(const void* q, const void* k_cache, const vo
     const int NB = lay.n_blk_max;
     const int KS = (NB + 3) & ~3;
     const int nkc = sl.n_key_chunks;
+    if (nkc > kSelThreads) return hipErrorInvalidValue;   // one finish thread per chunk
 
     const int nz = B * kHistBins;
     hipLaunchKernelGGL(qsa_prep_kernel, dim3((std::max(nz, (int)B) + 255) / 256), dim3(256), 0, s, hist, nz,
@@ -2337,6 +2342,7 @@ hipError_t launch_topk_sparse_decode(const void* q, const void* latent, const vo
     float* pml = reinterpret_cast<float*>(w);
     const int S_stride = (S_max + 3) & ~3;
     const int nkc = lay.n_key_chunks;
+    if (nkc > kSelThreads) return hipErrorInvalidValue;   // one finish thread per chunk
 
     const int nz = B * kHistBins;
     hipLaunchKernelGGL(zero_u32_kernel, dim3((nz + 255) / 256), dim3(256), 0, s, hist, nz);
