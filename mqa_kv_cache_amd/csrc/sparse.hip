@@ -305,7 +305,11 @@ __global__ __launch_bounds__(256) void indexer_weighted_kernel(
 // order is score order.
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 1024;
-constexpr int kChunkThreads = 256;
+// threads per chunk workgroup: its first-digit scan over the 4096 bins is
+// the latency the chunk kernel waits on; 512 threads (8 bins, 4 keys each)
+// gave the top-k call 66.3 us against 70.3 with 256 and 75.1 with 128, 66.5
+// with 1024
+constexpr int kChunkThreads = 512;
 // keys per chunk workgroup: 2048 gave the top-k call 69.8 us against 70.7
 // with 4096 and 72.4 with 8192 (more chunk workgroups fill more CUs); the
 // finish kernel gives each chunk a thread, so a row may span at most
@@ -397,7 +401,7 @@ __device__ void first_digit(const uint32_t* hist_g, int b, int L, int k, uint32_
 // work so both latencies overlap; the order within a wave comes from
 // ballot/mbcnt.  With k = L every index is selected: the chunk writes its
 // indices straight to the output, and chunk 0 writes the -1 padding.
-constexpr int kKeysPerLane = kChunkKeys / kChunkThreads;     // 8
+constexpr int kKeysPerLane = kChunkKeys / kChunkThreads;     // 4
 
 __global__ __launch_bounds__(kChunkThreads) void topk_compact_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist_g,
