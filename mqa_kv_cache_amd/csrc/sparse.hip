@@ -708,8 +708,11 @@ constexpr int kSelPass = kSelThreads * kSelKeysPerThread;   // keys per pass
 // Rows of at most this many keys take the one-kernel select; longer rows
 // the two-kernel one (the chunk workgroups read a row in parallel, where one
 // workgroup's reads of it run at ~20 GB/s: 32 us for 131072 keys against
-// 18 us for the two kernels, 16 us against 18.7 at 32768 keys).
-constexpr int kSelOneKernelMax = 32768;
+// 18 us for the two kernels; at 32768 keys the one kernel was faster, 16
+// against 18.7 us, until the chunk kernel's 512 threads: since then the QSA
+// call over 32768-block rows takes 74.1-74.3 us with the two kernels against
+// 76.0-76.4 with one).
+constexpr int kSelOneKernelMax = 16384;
 
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist_g,

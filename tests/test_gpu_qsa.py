@@ -136,7 +136,7 @@ def test_qsa_gqa_groups(m):
 
 
 def test_qsa_long_rows_take_the_two_kernel_select(m):
-    """More than 32768 blocks per row (S_max = 132000): the chunk and row
+    """More than 16384 blocks per row (S_max = 132000): the chunk and row
     select kernels with the band re-scoring."""
     _run(m, 1, 8, 1, 132000, [132000], 64, 110, ROPE64)
 

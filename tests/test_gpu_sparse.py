@@ -117,7 +117,7 @@ def test_sparse_overflow_and_lds_rows_in_one_call(m):
 
 
 def test_sparse_long_rows_take_the_two_kernel_select(m):
-    """Rows longer than 32768 keys are selected by the chunk and row kernels
+    """Rows longer than 16384 keys are selected by the chunk and row kernels
     (shorter ones by one kernel per row): row 0 with 20000 equal top scores
     (the row kernel's overflow path), row 1 ordinary, row 2 shorter than k."""
     d = sparse_inputs_host(3, 16, 40000, 576, 128, 49, [40000, 39001, 1500])
